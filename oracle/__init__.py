@@ -1,0 +1,208 @@
+"""Plain fp64 CPU oracle of the speculative-sampling verifier (ctypes wrapper).
+
+TEST INFRASTRUCTURE ONLY.  The product library never imports, links or calls
+anything in this directory; only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may.  The arithmetic lives in
+``spec_oracle.cpp``; this module only compiles it (with g++) and marshals
+numpy arrays.
+
+Pinned functions and their pins (see tests/test_oracle_pins.py):
+  philox4x32_10, uniform_accept, uniform_race -- Random123 known-answer
+      values and runs of ATen's independent Philox engine;
+  row_probs -- closed forms (temperature, top-k ties, -inf logits);
+  race -- chi-square against w / sum(w);
+  verify (prob / onehot / greedy / naive) -- the worked 5-token example and
+      Monte Carlo table of the vLLM rejection-resampling page, Eq. 1 of the
+      draft-model page, brute-force enumeration at V <= 4, and exact
+      reductions between the three modes.
+Parity unpinned by the pages (pinned only by this oracle's own definition):
+  the tie rules, the Philox keying and bit mapping, the zero-mass fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "spec_oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "libspec_oracle.so")
+
+MODE_PROB, MODE_ONEHOT, MODE_GREEDY, MODE_NAIVE = 0, 1, 2, 3
+DTYPE_F32, DTYPE_BF16 = 0, 1
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle into oracle/libspec_oracle.so (g++, fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["g++", "-std=c++17", "-O2", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = build()
+    lib = ctypes.CDLL(path)
+    c_u32p = ctypes.POINTER(ctypes.c_uint32)
+    lib.sv_ref_philox4x32_10.argtypes = [c_u32p, c_u32p, c_u32p]
+    lib.sv_ref_philox4x32_10.restype = None
+    lib.sv_ref_uniform_accept.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32]
+    lib.sv_ref_uniform_accept.restype = ctypes.c_double
+    lib.sv_ref_uniform_race.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32]
+    lib.sv_ref_uniform_race.restype = ctypes.c_double
+    lib.sv_ref_row_probs.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                     ctypes.c_int, ctypes.c_void_p]
+    lib.sv_ref_row_probs.restype = ctypes.c_int
+    lib.sv_ref_row_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    lib.sv_ref_row_argmax.restype = ctypes.c_int
+    lib.sv_ref_race.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
+                                ctypes.c_uint32, ctypes.POINTER(ctypes.c_double)]
+    lib.sv_ref_race.restype = ctypes.c_int
+    lib.sv_ref_verify.argtypes = ([ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_int, ctypes.c_uint64]
+                                  + [ctypes.c_void_p] * 13 + [ctypes.c_int])
+    lib.sv_ref_verify.restype = ctypes.c_int
+    lib.sv_ref_max_threads.argtypes = []
+    lib.sv_ref_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _logits_bytes(a) -> tuple[np.ndarray, int]:
+    """Accept float32 arrays or bfloat16 bit patterns held as uint16."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float32:
+        return a, DTYPE_F32
+    if a.dtype == np.uint16:
+        return a, DTYPE_BF16
+    raise TypeError(f"logits must be float32 or uint16 (bfloat16 bits), got {a.dtype}")
+
+
+def philox4x32_10(ctr, key) -> np.ndarray:
+    lib = _load()
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.zeros(4, dtype=np.uint32)
+    lib.sv_ref_philox4x32_10(c.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                             k.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)),
+                             out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32)))
+    return out
+
+
+def uniform_accept(seed: int, b: int, j: int) -> float:
+    return _load().sv_ref_uniform_accept(seed, b, j)
+
+
+def uniform_race(seed: int, b: int, j: int, y: int) -> float:
+    return _load().sv_ref_uniform_race(seed, b, j, y)
+
+
+def row_probs(row, temperature: float, top_k: int = 0) -> np.ndarray:
+    r, dt = _logits_bytes(row)
+    V = r.shape[-1]
+    out = np.zeros(V, dtype=np.float64)
+    _load().sv_ref_row_probs(_ptr(r), dt, V, float(temperature), int(top_k), _ptr(out))
+    return out
+
+
+def row_argmax(row) -> int:
+    r, dt = _logits_bytes(row)
+    return _load().sv_ref_row_argmax(_ptr(r), dt, r.shape[-1])
+
+
+def race(w, seed: int, b: int, j: int) -> tuple[int, float]:
+    wv = np.ascontiguousarray(w, dtype=np.float64)
+    m = ctypes.c_double(0.0)
+    tok = _load().sv_ref_race(_ptr(wv), wv.shape[0], seed, b, j, ctypes.byref(m))
+    return tok, m.value
+
+
+def max_threads() -> int:
+    return _load().sv_ref_max_threads()
+
+
+def verify(mode: int, target_logits, draft_logits, draft_tokens, *, temperature: float = 1.0,
+           top_k: int = 0, seed: int = 0, req_ids=None, diagnostics: bool = False,
+           nthreads: int = 0) -> dict:
+    """Run the oracle on host arrays.
+
+    target_logits: [n, G+1, V] float32 or uint16 (bfloat16 bits)
+    draft_logits:  [n, G, V] same dtype (prob / naive modes), else None
+    draft_tokens:  [n, G] int32
+    req_ids:       [n] request indices for the Philox streams (default 0..n-1)
+    """
+    lib = _load()
+    lt, dt = _logits_bytes(target_logits)
+    n, G1, V = lt.shape
+    G = G1 - 1
+    ld = None
+    if draft_logits is not None:
+        ld, dt2 = _logits_bytes(draft_logits)
+        if dt2 != dt or ld.shape != (n, G, V):
+            raise ValueError("draft logits must match target dtype and be [n, G, V]")
+    x = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    if x.shape != (n, G):
+        raise ValueError("draft tokens must be [n, G]")
+    rid = None if req_ids is None else np.ascontiguousarray(req_ids, dtype=np.int32)
+    out = np.empty((n, G + 1), dtype=np.int32)
+    nacc = np.empty(n, dtype=np.int32)
+    res = {"out_tokens": out, "num_accepted": nacc}
+    bad = np.zeros(n, dtype=np.int32)
+    res["bad_token"] = bad
+    pd = qd = targ = beta = am = rm = None
+    if mode == MODE_GREEDY:
+        targ = np.empty((n, G + 1), dtype=np.int32)
+        res["target_argmax"] = targ
+    else:
+        pd = np.empty((n, G), dtype=np.float64)
+        qd = np.empty((n, G), dtype=np.float64)
+        res["p_draft"], res["q_draft"] = pd, qd
+        if diagnostics:
+            beta = np.empty((n, G), dtype=np.float64)
+            am = np.empty((n, G), dtype=np.float64)
+            rm = np.empty(n, dtype=np.float64)
+            res["beta"], res["accept_margin"], res["race_margin"] = beta, am, rm
+    rc = lib.sv_ref_verify(mode, n, G, V, dt, float(temperature), int(top_k), int(seed),
+                           _ptr(lt), _ptr(ld), _ptr(x), _ptr(rid), _ptr(out), _ptr(nacc), _ptr(pd), _ptr(qd),
+                           _ptr(targ), _ptr(beta), _ptr(am), _ptr(rm), _ptr(bad), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return res
+
+
+def near_tie_position(res: dict, threshold: float = 1e-4) -> np.ndarray:
+    """First position whose decision had a margin <= threshold, else -1.
+
+    The accept decision at j (j <= n) and the race at n are the decisions of
+    a request; the greedy path takes none that can tie numerically.
+    """
+    nacc = res["num_accepted"]
+    n_req = nacc.shape[0]
+    pos = np.full(n_req, -1, dtype=np.int64)
+    if "accept_margin" not in res:
+        return pos
+    am, rm = res["accept_margin"], res["race_margin"]
+    G = am.shape[1]
+    for r in range(n_req):
+        n = int(nacc[r])
+        for j in range(min(n + 1, G)):
+            if am[r, j] <= threshold:
+                pos[r] = j
+                break
+        if pos[r] < 0 and rm[r] <= threshold:
+            pos[r] = n
+    return pos

@@ -1,0 +1,424 @@
+// Plain fp64 CPU oracle for the speculative-sampling verifier.
+//
+// TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+// load or call this file.  It is used by the test suite, by the smoke check
+// and by the CPU-baseline leg of the benchmark, and by nothing else.  It
+// shares no code, header, table or constant with the GPU library: it carries
+// its own Philox4x32-10 and its own decoding of the logit formats.
+//
+// Sources (the reference pages; titles as printed):
+//   [P1] "초안 모델로 생성 속도를 높이는 추측 디코딩" (cortexys.team),
+//        section "방법" (Algorithm 1 of Leviathan et al.) and section
+//        "수락률 α와 기대 속도 향상" (Eq. 1).
+//   [P3] "투기적 디코딩" (mlxcel.ai manual), sections "기본 라운드" and
+//        "정확성 기준".
+//   [P4] "vLLM speculative decoding이 기각 토큰을 다시 뽑는 이유" (velog),
+//        sections "드래프트가 제안하고 타깃이 판정한다" (the per-position test),
+//        "왜 하필 max(p − q, 0)인가" (the residual, Appendix A.1),
+//        "vLLM 커널은 이 규칙을 어떻게 옮겼나" (fp64 uniforms, the Exp(1)
+//        race, sampling constraints), "기본값 greedy 드래프트에서도 분포가
+//        지켜질까" (one-hot q and the greedy kernel).
+//
+// Readings where the pages are silent (each is listed with its reason in the
+// design notes of the repository):
+//   * temperature then top-k, the same T and k for p and q;
+//   * top-k keeps exactly k tokens ranked by (logit desc, index asc);
+//   * every argmax and every race tie goes to the lowest index;
+//   * uniforms are Philox4x32-10 words mapped to (k53 + 1) * 2^-53 in (0, 1];
+//     accept stream counter (0, j, b, 0), race stream counter
+//     (y >> 1, j, b, 1) with words (0,1) for even y and (2,3) for odd y;
+//   * accept iff q(x) > 0 and u <= p(x)/q(x) (equality accepts);
+//   * Exp(1) variate E = -ln(u); E == 0 gives an infinite race score;
+//   * a residual of zero total mass falls back to w = p;
+//   * an out-of-range draft token counts as rejected and raises a flag.
+//
+// Parity unpinned by the pages: the tie rules at exact equality (race ties,
+// accept at u == p/q) are events of probability ~2^-53 that no sampling test
+// can observe; they are this oracle's definition only.  The Philox keying and
+// bit mapping are pinned against themselves only through the documented
+// counter layout.
+//
+// Every loop is the definition written out, in fp64, in ascending index
+// order.  No blocking, no fusion, no reordering.  Requests are independent, so
+// the batch loop is an OpenMP parallel-for over requests; nothing inside a
+// request is parallel.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <numeric>
+#include <vector>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11).  One round maps counter (c0,c1,c2,c3) under key
+// (k0,k1) to (hi(M1*c2) ^ c1 ^ k0, lo(M1*c2), hi(M0*c0) ^ c3 ^ k1, lo(M0*c0));
+// the key is bumped by the Weyl constants before every round after the first.
+// ---------------------------------------------------------------------------
+const uint32_t kPhiloxM0 = 0xD2511F53u;
+const uint32_t kPhiloxM1 = 0xCD9E8D57u;
+const uint32_t kPhiloxW0 = 0x9E3779B9u;
+const uint32_t kPhiloxW1 = 0xBB67AE85u;
+
+void philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += kPhiloxW0;
+      k1 += kPhiloxW1;
+    }
+    uint64_t prod0 = (uint64_t)kPhiloxM0 * (uint64_t)c0;
+    uint64_t prod1 = (uint64_t)kPhiloxM1 * (uint64_t)c2;
+    uint32_t hi0 = (uint32_t)(prod0 >> 32), lo0 = (uint32_t)prod0;
+    uint32_t hi1 = (uint32_t)(prod1 >> 32), lo1 = (uint32_t)prod1;
+    uint32_t n0 = hi1 ^ c1 ^ k0;
+    uint32_t n1 = lo1;
+    uint32_t n2 = hi0 ^ c3 ^ k1;
+    uint32_t n3 = lo0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+// Two 32-bit words -> a double in (0, 1]: the top 53 bits of (hi:lo), plus
+// one, times 2^-53.  Exact in fp64; never 0, which the page on vLLM's kernel
+// gives as the reason for drawing the uniform in float64.
+double words_to_unit(uint32_t lo, uint32_t hi) {
+  uint64_t bits = ((uint64_t)hi << 32) | (uint64_t)lo;
+  uint64_t k53 = bits >> 11;
+  return (double)(k53 + 1) * std::ldexp(1.0, -53);
+}
+
+double uniform_accept(uint64_t seed, uint32_t b, uint32_t j) {
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t ctr[4] = {0u, j, b, 0u};
+  uint32_t w[4];
+  philox4x32_10(ctr, key, w);
+  return words_to_unit(w[0], w[1]);
+}
+
+double uniform_race(uint64_t seed, uint32_t b, uint32_t j, uint32_t y) {
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t ctr[4] = {y >> 1, j, b, 1u};
+  uint32_t w[4];
+  philox4x32_10(ctr, key, w);
+  if ((y & 1u) == 0u) return words_to_unit(w[0], w[1]);
+  return words_to_unit(w[2], w[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Logit decoding.  dtype 0: IEEE binary32.  dtype 1: bfloat16, i.e. the upper
+// 16 bits of a binary32.  Both embed exactly in fp64.
+// ---------------------------------------------------------------------------
+double decode_logit(const void* row, int dtype, int64_t y) {
+  if (dtype == 0) {
+    float f;
+    std::memcpy(&f, (const char*)row + 4 * y, 4);
+    return (double)f;
+  }
+  uint16_t h;
+  std::memcpy(&h, (const char*)row + 2 * y, 2);
+  uint32_t bits = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &bits, 4);
+  return (double)f;
+}
+
+size_t elem_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
+
+// The adjusted distribution of one position: temperature, then top-k, then
+// softmax ([P4] "vLLM 커널은 이 규칙을 어떻게 옮겼나": the sampling constraints
+// are applied to the logits before the test, so p is the adjusted law).
+std::vector<double> row_probs(const void* row, int dtype, int V, double T, int top_k) {
+  std::vector<double> l(V);
+  for (int y = 0; y < V; ++y) l[y] = decode_logit(row, dtype, y);
+
+  std::vector<char> keep(V, 1);
+  if (top_k > 0 && top_k < V) {
+    // Rank by (logit desc, index asc): a stable sort on descending logit keeps
+    // equal logits in ascending index order.  Ranking on l equals ranking on
+    // l / T for T > 0.
+    std::vector<int> order(V);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int c) { return l[a] > l[c]; });
+    std::fill(keep.begin(), keep.end(), 0);
+    for (int r = 0; r < top_k; ++r) keep[order[r]] = 1;
+  }
+
+  std::vector<double> z(V, 0.0);
+  double m = -std::numeric_limits<double>::infinity();
+  for (int y = 0; y < V; ++y) {
+    if (!keep[y]) continue;
+    z[y] = l[y] / T;
+    if (z[y] > m) m = z[y];
+  }
+  double Z = 0.0;
+  for (int y = 0; y < V; ++y)
+    if (keep[y]) Z += std::exp(z[y] - m);
+  std::vector<double> p(V, 0.0);
+  for (int y = 0; y < V; ++y)
+    if (keep[y]) p[y] = std::exp(z[y] - m) / Z;
+  return p;
+}
+
+// Greedy target token: the lowest index attaining the maximum raw logit.
+int row_argmax(const void* row, int dtype, int V) {
+  int best = 0;
+  double bv = decode_logit(row, dtype, 0);
+  for (int y = 1; y < V; ++y) {
+    double v = decode_logit(row, dtype, y);
+    if (v > bv) { bv = v; best = y; }
+  }
+  return best;
+}
+
+// Exp(1) race ([P4] "vLLM 커널은 이 규칙을 어떻게 옮겼나"): the argmax over
+// tokens with w_y > 0 of w_y / E_y, E_y = -ln u_y i.i.d. Exp(1), is a sample
+// from w / sum(w) with no normalisation.  Strict '>' keeps the lowest index on
+// ties.  *margin receives (s1 - s2) / s1 for the top two scores.
+int race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
+  const double inf = std::numeric_limits<double>::infinity();
+  int best = -1;
+  double s1 = -inf, s2 = -inf;
+  for (size_t y = 0; y < w.size(); ++y) {
+    if (!(w[y] > 0.0)) continue;
+    double u = uniform_race(seed, b, j, (uint32_t)y);
+    double E = -std::log(u);
+    double s = (E == 0.0) ? inf : w[y] / E;
+    if (s > s1) {
+      s2 = s1;
+      s1 = s;
+      best = (int)y;
+    } else if (s > s2) {
+      s2 = s;
+    }
+  }
+  if (margin) {
+    if (best < 0 || s2 == -inf) *margin = 1.0;          // one candidate: no decision to flip
+    else if (s1 == inf) *margin = (s2 == inf) ? 0.0 : 1.0;
+    else *margin = (s1 - s2) / s1;
+  }
+  return best;
+}
+
+enum { MODE_PROB = 0, MODE_ONEHOT = 1, MODE_GREEDY = 2, MODE_NAIVE = 3 };
+
+struct Problem {
+  int mode, B, G, V, dtype, top_k;
+  double T;
+  uint64_t seed;
+};
+
+// One request: Algorithm 1's verification part ([P1] "방법"; [P4]
+// "드래프트가 제안하고 타깃이 판정한다").  Positions j = 0..G-1 carry draft
+// tokens; row G of the target is the bonus position.  Returns 1 if a draft
+// token was out of range, else 0.
+int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, const int32_t* X,
+               int32_t* out, int32_t* n_out, double* p_draft, double* q_draft, int32_t* target_argmax,
+               double* beta, double* acc_margin, double* race_margin) {
+  const int G = P.G, V = P.V;
+  const size_t row_bytes = (size_t)V * elem_bytes(P.dtype);
+  const double nan = std::numeric_limits<double>::quiet_NaN();
+  int bad_token = 0;
+  std::vector<char> valid(G);
+  for (int j = 0; j < G; ++j) {
+    valid[j] = (X[j] >= 0 && X[j] < V);
+    if (!valid[j]) bad_token = 1;
+  }
+  if (acc_margin)
+    for (int j = 0; j < G; ++j) acc_margin[j] = nan;
+  if (race_margin) *race_margin = nan;
+
+  if (P.mode == MODE_GREEDY) {
+    // Temperature 0: accept iff the draft token is the target argmax ([P1]
+    // "방법"; [P4] "기본값 greedy 드래프트에서도 분포가 지켜질까"); the target
+    // argmax replaces the first mismatch, and is the bonus after G matches.
+    std::vector<int> a(G + 1);
+    for (int j = 0; j <= G; ++j) a[j] = row_argmax(Lt + (size_t)j * row_bytes, P.dtype, V);
+    int n = G;
+    for (int j = 0; j < G; ++j) {
+      if (!valid[j] || X[j] != a[j]) { n = j; break; }
+    }
+    for (int j = 0; j < n; ++j) out[j] = X[j];
+    out[n] = a[n];
+    for (int j = n + 1; j <= G; ++j) out[j] = -1;
+    *n_out = n;
+    if (target_argmax)
+      for (int j = 0; j <= G; ++j) target_argmax[j] = a[j];
+    return bad_token;
+  }
+
+  const bool has_q = (P.mode == MODE_PROB || P.mode == MODE_NAIVE);
+  std::vector<std::vector<double>> p(G + 1), q(has_q ? G : 0);
+  for (int j = 0; j <= G; ++j) p[j] = row_probs(Lt + (size_t)j * row_bytes, P.dtype, V, P.T, P.top_k);
+  for (int j = 0; j < (has_q ? G : 0); ++j)
+    q[j] = row_probs(Ld + (size_t)j * row_bytes, P.dtype, V, P.T, P.top_k);
+
+  // p(x_j) and q(x_j) for every draft position (q := 1 for a one-hot draft).
+  std::vector<double> px(G), qx(G);
+  for (int j = 0; j < G; ++j) {
+    px[j] = valid[j] ? p[j][X[j]] : 0.0;
+    if (has_q) qx[j] = valid[j] ? q[j][X[j]] : 0.0;
+    else qx[j] = valid[j] ? 1.0 : 0.0;
+    if (p_draft) p_draft[j] = px[j];
+    if (q_draft) q_draft[j] = qx[j];
+    if (beta) {
+      // Acceptance rate of position j: sum_y min(p, q) ([P4] "왜 하필
+      // max(p − q, 0)인가", Theorem 3.5).  For one-hot q it is p(x).
+      if (has_q) {
+        double s = 0.0;
+        for (int y = 0; y < V; ++y) s += std::min(p[j][y], q[j][y]);
+        beta[j] = s;
+      } else {
+        beta[j] = px[j];
+      }
+    }
+  }
+
+  // Front-to-back test with one independent uniform per position; the first
+  // rejection ends the scan ([P4] "드래프트가 제안하고 타깃이 판정한다").
+  int n = G;
+  for (int j = 0; j < G; ++j) {
+    double u = uniform_accept(P.seed, b, (uint32_t)j);
+    bool accept;
+    if (!valid[j]) {
+      accept = false;
+    } else if (has_q) {
+      accept = (qx[j] > 0.0) && (u <= px[j] / qx[j]);
+    } else {
+      accept = (u <= px[j]);
+    }
+    if (acc_margin) {
+      double lhs = u * qx[j], rhs = px[j];
+      double den = std::max(lhs, rhs);
+      acc_margin[j] = (!valid[j] || qx[j] == 0.0) ? 1.0 : (den > 0.0 ? std::fabs(lhs - rhs) / den : 0.0);
+    }
+    if (!accept) { n = j; break; }
+  }
+
+  std::vector<double> w(V, 0.0);
+  if (n < G) {
+    if (P.mode == MODE_PROB) {
+      // Residual norm(max(0, p - q)) ([P4] "왜 하필 max(p − q, 0)인가").
+      double mass = 0.0;
+      for (int y = 0; y < V; ++y) {
+        w[y] = std::max(p[n][y] - q[n][y], 0.0);
+        mass += w[y];
+      }
+      if (!(mass > 0.0)) w = p[n];  // unreachable in exact arithmetic
+    } else if (P.mode == MODE_ONEHOT) {
+      // One-hot q: the residual is p with the draft token masked ([P4]
+      // "기본값 greedy 드래프트에서도 분포가 지켜질까").
+      w = p[n];
+      if (valid[n]) w[X[n]] = 0.0;
+      double mass = 0.0;
+      for (int y = 0; y < V; ++y) mass += w[y];
+      if (!(mass > 0.0)) w = p[n];  // unreachable: p(x) = 1 always accepts
+    } else {
+      // MODE_NAIVE, test-only: resample from p after a rejection, the wrong
+      // rule that [P4] "Java로 규칙을 재현해 본 결과" shows to double count.
+      w = p[n];
+    }
+  } else {
+    // All G accepted: one more token from p at the bonus position.
+    w = p[G];
+  }
+  int tok = race(w, P.seed, b, (uint32_t)n, race_margin);
+
+  for (int j = 0; j < n; ++j) out[j] = X[j];
+  out[n] = tok;
+  for (int j = n + 1; j <= G; ++j) out[j] = -1;
+  *n_out = n;
+  return bad_token;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Philox4x32-10 on one counter block.
+void sv_ref_philox4x32_10(const uint32_t* ctr4, const uint32_t* key2, uint32_t* out4) {
+  philox4x32_10(ctr4, key2, out4);
+}
+
+double sv_ref_uniform_accept(uint64_t seed, uint32_t b, uint32_t j) { return uniform_accept(seed, b, j); }
+
+double sv_ref_uniform_race(uint64_t seed, uint32_t b, uint32_t j, uint32_t y) {
+  return uniform_race(seed, b, j, y);
+}
+
+// Adjusted distribution of one row (length V) into p_out.  Returns 0.
+int sv_ref_row_probs(const void* row, int dtype, int V, double T, int top_k, double* p_out) {
+  std::vector<double> p = row_probs(row, dtype, V, T, top_k);
+  std::copy(p.begin(), p.end(), p_out);
+  return 0;
+}
+
+int sv_ref_row_argmax(const void* row, int dtype, int V) { return row_argmax(row, dtype, V); }
+
+// Exp(1) race over weights w[0..V) on the race stream of (seed, b, j).
+int sv_ref_race(const double* w, int V, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
+  std::vector<double> wv(w, w + V);
+  return race(wv, seed, b, j, margin);
+}
+
+// Batched verifier.
+//   mode: 0 prob, 1 onehot, 2 greedy, 3 naive (test-only, deliberately wrong)
+//   Lt: [nreq][G+1][V] logits; Ld: [nreq][G][V] (prob and naive only)
+//   X: [nreq][G] int32 draft tokens
+//   req_ids: request index b of each request for the Philox streams
+//            (NULL: b = 0..nreq-1)
+//   outputs: out_tokens [nreq][G+1], num_accepted [nreq];
+//   optional (NULL to skip): p_draft, q_draft [nreq][G]; target_argmax
+//   [nreq][G+1] (greedy); beta, acc_margin [nreq][G]; race_margin [nreq];
+//   bad_token [nreq] (1 where a draft token is out of range).
+// Returns 0 on success, -1 on invalid arguments.
+int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top_k, uint64_t seed,
+                  const void* Lt, const void* Ld, const int32_t* X, const int32_t* req_ids,
+                  int32_t* out_tokens, int32_t* num_accepted, double* p_draft, double* q_draft,
+                  int32_t* target_argmax, double* beta, double* acc_margin, double* race_margin,
+                  int32_t* bad_token, int nthreads) {
+  if (nreq < 0 || G < 1 || V < 1 || (dtype != 0 && dtype != 1) || mode < 0 || mode > 3) return -1;
+  if (mode != MODE_GREEDY && !(T > 0.0)) return -1;
+  if (top_k < 0) return -1;
+  if (!Lt || !X || !out_tokens || !num_accepted) return -1;
+  if ((mode == MODE_PROB || mode == MODE_NAIVE) && !Ld) return -1;
+  Problem P{mode, nreq, G, V, dtype, top_k, T, seed};
+  const size_t row_bytes = (size_t)V * elem_bytes(dtype);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int r = 0; r < nreq; ++r) {
+    uint32_t b = req_ids ? (uint32_t)req_ids[r] : (uint32_t)r;
+    const char* lt = (const char*)Lt + (size_t)r * (G + 1) * row_bytes;
+    const char* ld = Ld ? (const char*)Ld + (size_t)r * G * row_bytes : nullptr;
+    int bad = verify_one(P, b, lt, ld, X + (size_t)r * G, out_tokens + (size_t)r * (G + 1), num_accepted + r,
+                         p_draft ? p_draft + (size_t)r * G : nullptr, q_draft ? q_draft + (size_t)r * G : nullptr,
+                         target_argmax ? target_argmax + (size_t)r * (G + 1) : nullptr,
+                         beta ? beta + (size_t)r * G : nullptr, acc_margin ? acc_margin + (size_t)r * G : nullptr,
+                         race_margin ? race_margin + r : nullptr);
+    if (bad_token) bad_token[r] = bad;
+  }
+  return 0;
+}
+
+// Number of threads the OpenMP runtime will use for the batch loop.
+int sv_ref_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+}  // extern "C"

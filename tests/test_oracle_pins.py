@@ -1,0 +1,567 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these tests compares the oracle with itself: each checks a printed
+value, a closed form, an exact identity, an independent implementation that
+is run (not copied), or a brute-force enumeration.  A plausible slip in the
+oracle (a dropped max(0, .), a swapped p and q, a resample from p instead of
+the residual, a wrong counter word, a flipped tie rule) fails at least one.
+"""
+
+import math
+import os
+import shutil
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+from scipy import stats
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+HELPERS = os.path.join(os.path.dirname(__file__), "helpers")
+
+
+def _read_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _f32_logits(probs):
+    with np.errstate(divide="ignore"):
+        return np.log(np.asarray(probs, dtype=np.float64)).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Philox4x32-10 and the uniform mapping
+# ---------------------------------------------------------------------------
+
+def test_philox_known_answers():
+    for r in _read_golden("philox4x32_10_kat.txt"):
+        vals = [int(v, 16) for v in r]
+        ctr, key, want = vals[0:4], vals[4:6], vals[6:10]
+        assert list(oracle.philox4x32_10(ctr, key)) == want
+
+
+def test_philox_matches_aten_engine_runs():
+    """Bit-equality with ATen's independent header-only Philox engine, run on
+    1000 random counter/key blocks."""
+    import torch
+    inc = os.path.join(os.path.dirname(torch.__file__), "include")
+    if not shutil.which("g++") or not os.path.isdir(inc):
+        pytest.skip("g++ or torch headers unavailable")
+    with tempfile.TemporaryDirectory() as td:
+        exe = os.path.join(td, "aten_philox")
+        subprocess.run(["g++", "-std=c++17", "-O1", "-I", inc, os.path.join(HELPERS, "aten_philox.cpp"),
+                        "-o", exe], check=True)
+        rng = np.random.default_rng(1234)
+        blocks = rng.integers(0, 2**32, size=(1000, 6), dtype=np.uint64)
+        blocks[:10, :4] = 0  # include tiny counters
+        stdin = "\n".join(" ".join(f"{int(v):08x}" for v in row) for row in blocks) + "\n"
+        out = subprocess.run([exe], input=stdin, capture_output=True, text=True, check=True).stdout.split("\n")
+    for row, line in zip(blocks, out):
+        want = [int(v, 16) for v in line.split()]
+        got = list(oracle.philox4x32_10(row[:4], row[4:6]))
+        assert got == want
+
+
+def _unit_from_words(lo, hi):
+    k53 = ((int(hi) << 32) | int(lo)) >> 11
+    return (k53 + 1) / 2.0**53
+
+
+def test_uniform_streams_use_documented_counters():
+    seed = 0x0123456789ABCDEF
+    key = [seed & 0xFFFFFFFF, seed >> 32]
+    for b, j in [(0, 0), (5, 3), (1023, 8), (2**31 - 1, 7)]:
+        w = oracle.philox4x32_10([0, j, b, 0], key)
+        assert oracle.uniform_accept(seed, b, j) == _unit_from_words(w[0], w[1])
+        for y in [0, 1, 2, 3, 255998, 255999]:
+            w = oracle.philox4x32_10([y >> 1, j, b, 1], key)
+            want = _unit_from_words(w[0], w[1]) if y % 2 == 0 else _unit_from_words(w[2], w[3])
+            assert oracle.uniform_race(seed, b, j, y) == want
+
+
+def test_uniforms_in_half_open_unit_interval_and_uniform():
+    u = np.array([oracle.uniform_accept(42, b, j) for b in range(2000) for j in range(8)])
+    assert np.all(u > 0.0) and np.all(u <= 1.0)
+    assert np.all(np.floor(u * 2.0**53) == u * 2.0**53)  # multiples of 2^-53
+    assert stats.kstest(u, "uniform").pvalue > 1e-4
+
+
+# ---------------------------------------------------------------------------
+# Adjusted distribution of one position: temperature, top-k, softmax
+# ---------------------------------------------------------------------------
+
+def test_temperature_closed_form():
+    # l = T * ln(w)  =>  softmax(l / T) = w / sum(w).
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    for T in [0.5, 0.7, 1.0, 2.0]:
+        l = (T * np.log(w)).astype(np.float32)
+        want = np.exp(l.astype(np.float64) / T)
+        want /= want.sum()
+        got = oracle.row_probs(l, T)
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
+        np.testing.assert_allclose(got, w / w.sum(), rtol=1e-6)
+
+
+def test_temperature_peaks_the_law():
+    rng = np.random.default_rng(0)
+    l = (rng.standard_normal(64) * 3).astype(np.float32)
+    p1, p07, p2 = (oracle.row_probs(l, T) for T in (1.0, 0.7, 2.0))
+    top = int(np.argmax(l))
+    assert p07[top] > p1[top] > p2[top]
+    for p in (p1, p07, p2):
+        assert abs(p.sum() - 1.0) < 1e-12
+
+
+def test_topk_keeps_k_largest_with_lowest_index_ties():
+    # All equal: the first k indices are kept.
+    l = np.zeros(10, dtype=np.float32)
+    p = oracle.row_probs(l, 1.0, top_k=3)
+    np.testing.assert_array_equal(p, [1 / 3, 1 / 3, 1 / 3] + [0.0] * 7)
+    # A tie straddling the k-th place: ranks by (value desc, index asc).
+    l = np.array([1, 5, 3, 5, 3, 3, 0], dtype=np.float32)
+    p = oracle.row_probs(l, 1.0, top_k=4)
+    kept = np.nonzero(p)[0].tolist()
+    assert kept == [1, 2, 3, 4]
+    r = np.exp(5.0 - 3.0)
+    np.testing.assert_allclose(p[[1, 3]], r / (2 * r + 2), rtol=1e-14)
+    np.testing.assert_allclose(p[[2, 4]], 1 / (2 * r + 2), rtol=1e-14)
+
+
+def test_topk_random_rows_against_sorted_reference():
+    rng = np.random.default_rng(7)
+    for V, k in [(50, 1), (50, 7), (300, 64), (1000, 64)]:
+        l = np.round(rng.standard_normal(V) * 4, 1).astype(np.float32)  # many ties
+        order = sorted(range(V), key=lambda y: (-float(l[y]), y))
+        kept = sorted(order[:k])
+        p = oracle.row_probs(l, 0.7, top_k=k)
+        assert np.nonzero(p)[0].tolist() == kept
+        # Ratios inside the kept set follow exp((l_a - l_b) / T).
+        a, c = kept[0], kept[-1]
+        assert math.isclose(p[a] / p[c], math.exp((float(l[a]) - float(l[c])) / 0.7), rel_tol=1e-12)
+        assert abs(p.sum() - 1.0) < 1e-12
+
+
+def test_topk_at_or_above_vocab_is_off():
+    l = np.random.default_rng(1).standard_normal(33).astype(np.float32)
+    base = oracle.row_probs(l, 0.8, 0)
+    for k in (33, 34, 1000):
+        np.testing.assert_array_equal(oracle.row_probs(l, 0.8, k), base)
+
+
+def test_neg_inf_logits_have_zero_mass_and_bf16_decoding():
+    # bf16 bit patterns: 0x3F80 = 1.0, 0x4000 = 2.0, 0xFF80 = -inf, 0x0000 = 0.
+    bits = np.array([0x3F80, 0x4000, 0xFF80, 0x0000], dtype=np.uint16)
+    p = oracle.row_probs(bits, 1.0)
+    e = np.exp([1.0, 2.0, 0.0])
+    np.testing.assert_allclose(p[[0, 1, 3]], e / e.sum(), rtol=1e-14)
+    assert p[2] == 0.0
+    assert oracle.row_argmax(bits) == 1
+    assert oracle.row_argmax(np.array([0xC000, 0x3F80, 0x3F80], dtype=np.uint16)) == 1  # tie -> lowest
+
+
+# ---------------------------------------------------------------------------
+# The Exp(1) race
+# ---------------------------------------------------------------------------
+
+def test_race_law_chi_square():
+    w = np.array([0.1, 0.0, 0.5, 0.2, 0.2, 0.0, 1e-3])
+    n = 200_000
+    counts = np.zeros(w.size)
+    for b in range(n):
+        tok, _ = oracle.race(w, 99, b, 3)
+        counts[tok] += 1
+    assert counts[1] == 0 and counts[5] == 0  # zero weight never wins
+    pos = w > 0
+    chi = stats.chisquare(counts[pos], n * w[pos] / w.sum())
+    assert chi.pvalue > 1e-6
+
+
+def test_race_wrong_law_is_detected():
+    """Power check: a plausible slip (racing on p instead of the residual)
+    is far outside the chi-square acceptance region used above."""
+    w = np.array([0.1, 0.5, 0.2, 0.2])
+    wrong = np.array([0.25, 0.25, 0.25, 0.25])
+    n = 50_000
+    counts = np.zeros(4)
+    for b in range(n):
+        counts[oracle.race(wrong, 5, b, 0)[0]] += 1
+    assert stats.chisquare(counts, n * w / w.sum()).pvalue < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# The worked 5-token example and its Monte Carlo table
+# ---------------------------------------------------------------------------
+
+def _worked():
+    g = {r[0]: r[1:] for r in _read_golden("worked_example_5tok.txt")}
+    p = np.array([float(v) for v in g["p"]])
+    q = np.array([float(v) for v in g["q"]])
+    return p, q, g
+
+
+def _single_position_batch(p, q, n, rng, onehot=False):
+    """n requests with gamma = 1: position 0 carries the draft, row 1 is the
+    bonus position.  Draft tokens are drawn from q (or argmax q)."""
+    lp, lq = _f32_logits(p), _f32_logits(q)
+    lt = np.broadcast_to(np.stack([lp, lp]), (n, 2, p.size)).copy()
+    ld = np.broadcast_to(lq[None], (n, 1, q.size)).copy()
+    if onehot:
+        x = np.full((n, 1), int(np.argmax(q)), dtype=np.int32)
+    else:
+        x = rng.choice(p.size, size=(n, 1), p=q).astype(np.int32)
+    return lt, ld, x
+
+
+def test_worked_example_acceptance_identities():
+    p, q, g = _worked()
+    lt, ld, x = _single_position_batch(p, q, 1, np.random.default_rng(0))
+    res = oracle.verify(oracle.MODE_PROB, lt, ld, x, temperature=1.0, diagnostics=True)
+    assert abs(res["beta"][0, 0] - float(g["sum_min_pq"][0])) < 1e-6
+    res = oracle.verify(oracle.MODE_ONEHOT, lt, None, np.array([[int(np.argmax(q))]], np.int32),
+                        diagnostics=True)
+    assert abs(res["p_draft"][0, 0] - float(g["p_at_argmax_q"][0])) < 1e-6
+    assert res["q_draft"][0, 0] == 1.0
+
+
+@pytest.mark.parametrize("method", ["prob", "greedy", "naive"])
+def test_worked_example_monte_carlo_table(method):
+    """Reruns the page's 2e6-trial table: acceptance rate, output law, L1."""
+    p, q, g = _worked()
+    n = int(g["trials"][0])
+    printed = {r[0]: [float(v) for v in r[1:]] for r in _read_golden("worked_example_5tok.txt")
+               if r[0] in ("prob", "greedy", "naive")}[method]
+    rng = np.random.default_rng({"prob": 11, "greedy": 12, "naive": 13}[method])
+    lt, ld, x = _single_position_batch(p, q, n, rng, onehot=(method == "greedy"))
+    mode = {"prob": oracle.MODE_PROB, "greedy": oracle.MODE_ONEHOT, "naive": oracle.MODE_NAIVE}[method]
+    res = oracle.verify(mode, lt, ld if method != "greedy" else None, x, temperature=1.0, seed=42)
+    acc = res["num_accepted"].mean()
+    freq = np.bincount(res["out_tokens"][:, 0], minlength=5) / n
+    l1 = np.abs(freq - p).sum()
+    sd_acc = math.sqrt(printed[0] * (1 - printed[0]) / n)
+    assert abs(acc - printed[0]) < 6 * sd_acc + 1e-4          # printed to 4 decimals
+    if method == "naive":
+        # Exact naive law min(p, q) + (1 - beta) p; first token 0.425.
+        beta = np.minimum(p, q).sum()
+        law = np.minimum(p, q) + (1 - beta) * p
+        assert abs(law[0] - float(g["naive_first_token"][0])) < 1e-12
+        assert abs(freq[0] - 0.425) < 5 * math.sqrt(0.425 * 0.575 / n)
+        assert abs(l1 - printed[6]) < 0.003
+        assert stats.chisquare(freq * n, law * n).pvalue > 1e-6
+    else:
+        assert l1 < 0.003
+        assert stats.chisquare(freq * n, p * n).pvalue > 1e-6
+    np.testing.assert_allclose(freq, printed[1:6], atol=6 * math.sqrt(0.25 / n) + 1e-4)
+
+
+# ---------------------------------------------------------------------------
+# Eq. 1 and the law of the accepted length
+# ---------------------------------------------------------------------------
+
+def _eq1(alpha, gamma):
+    return (1 - alpha ** (gamma + 1)) / (1 - alpha)
+
+
+def test_eq1_printed_values():
+    for r in _read_golden("eq1_expected_tokens.txt"):
+        if r[0] == "compute":
+            a, gm, val, dec = float(r[1]), int(r[2]), float(r[3]), int(r[4])
+            assert round((gm + 1) / _eq1(a, gm), dec) == val
+        else:
+            a, gm, val, dec = float(r[0]), int(r[1]), float(r[2]), int(r[3])
+            assert round(_eq1(a, gm), dec) == val
+
+
+def _iid_onehot_rows(alpha, gamma, n):
+    """One-hot rows whose draft token has target probability alpha at every
+    position: each position accepts independently with probability alpha."""
+    l = _f32_logits([alpha, 1 - alpha])
+    lt = np.broadcast_to(l[None, None], (n, gamma + 1, 2)).copy()
+    x = np.zeros((n, gamma), dtype=np.int32)
+    return lt, x
+
+
+@pytest.mark.parametrize("alpha,gamma", [(0.8, 5), (0.901, 3), (0.75, 7), (0.9, 7)])
+def test_mean_tokens_per_round_matches_eq1(alpha, gamma):
+    n = 200_000
+    lt, x = _iid_onehot_rows(alpha, gamma, n)
+    res = oracle.verify(oracle.MODE_ONEHOT, lt, None, x, temperature=1.0, seed=7, diagnostics=True)
+    a_eff = float(res["beta"][0, 0])  # p(x) after fp32 rounding of the logits
+    assert abs(a_eff - alpha) < 1e-6
+    tokens = res["num_accepted"] + 1
+    se = tokens.std() / math.sqrt(n)
+    assert abs(tokens.mean() - _eq1(a_eff, gamma)) < 5 * se
+    # Law of n: P(n = k) = alpha^k (1 - alpha) for k < gamma, alpha^gamma at gamma.
+    k = np.arange(gamma + 1)
+    law = np.where(k < gamma, a_eff ** k * (1 - a_eff), a_eff ** gamma)
+    counts = np.bincount(res["num_accepted"], minlength=gamma + 1)
+    assert stats.chisquare(counts, law * n).pvalue > 1e-6
+
+
+def test_greedy_iid_matches_and_invariants():
+    """Greedy rows where each draft equals the target argmax with prob 0.8."""
+    rng = np.random.default_rng(3)
+    n, G, V = 20_000, 5, 17
+    lt = rng.standard_normal((n, G + 1, V)).astype(np.float32)
+    amax = np.argmax(lt, axis=-1)
+    match = rng.random((n, G)) < 0.8
+    other = (amax[:, :G] + 1 + rng.integers(0, V - 1, (n, G))) % V
+    x = np.where(match, amax[:, :G], other).astype(np.int32)
+    res = oracle.verify(oracle.MODE_GREEDY, lt, None, x)
+    nacc, out = res["num_accepted"], res["out_tokens"]
+    np.testing.assert_array_equal(res["target_argmax"], amax)
+    for r in range(200):
+        k = nacc[r]
+        assert (out[r, :k] == x[r, :k]).all() and (x[r, :k] == amax[r, :k]).all()
+        assert out[r, k] == amax[r, k] and (k == G or x[r, k] != amax[r, k])
+        assert (out[r, k + 1:] == -1).all()
+    tokens = nacc + 1
+    assert abs(tokens.mean() - _eq1(0.8, G)) < 5 * tokens.std() / math.sqrt(n)
+
+
+# ---------------------------------------------------------------------------
+# Brute-force enumeration at V <= 4
+# ---------------------------------------------------------------------------
+
+def _exact_outcome_law(p, q, mode):
+    """Exact law of (n, emitted tokens) by enumerating every draft sequence.
+    p: [G+1][V], q: [G][V] (rows of the adjusted laws)."""
+    G, V = q.shape if mode == "prob" else (p.shape[0] - 1, p.shape[1])
+    law = {}
+    import itertools
+
+    if mode == "prob":
+        seqs = itertools.product(range(V), repeat=G)
+    else:  # onehot: the draft is the fixed q-argmax sequence
+        seqs = [tuple(int(np.argmax(q[j])) for j in range(G))]
+    for xs in seqs:
+        w = np.prod([q[j][xs[j]] for j in range(G)]) if mode == "prob" else 1.0
+        if w == 0:
+            continue
+        reach = w
+        for j in range(G + 1):
+            if j == G:
+                for y in range(V):
+                    if p[G][y] > 0:
+                        key = (G, xs + (y,))
+                        law[key] = law.get(key, 0.0) + reach * p[G][y]
+                break
+            x = xs[j]
+            qx = q[j][x] if mode == "prob" else 1.0
+            a = min(1.0, p[j][x] / qx) if qx > 0 else 0.0
+            rej = reach * (1 - a)
+            if rej > 0:
+                if mode == "prob":
+                    r = np.maximum(p[j] - q[j], 0)
+                else:
+                    r = p[j].copy()
+                    r[x] = 0
+                r = r / r.sum()
+                for y in range(V):
+                    if r[y] > 0:
+                        key = (j, xs[:j] + (y,))
+                        law[key] = law.get(key, 0.0) + rej * r[y]
+            reach *= a
+            if reach == 0:
+                break
+    return law
+
+
+def _check_brute_force(lt, ld, mode, n_runs, seed, top_k=0, T=1.0):
+    G = lt.shape[0] - 1
+    V = lt.shape[1]
+    p = np.stack([oracle.row_probs(lt[j], T, top_k) for j in range(G + 1)])
+    if mode == "prob":
+        q = np.stack([oracle.row_probs(ld[j], T, top_k) for j in range(G)])
+    else:
+        q = np.zeros((G, V))
+        q[np.arange(G), np.argmax(ld, axis=-1)] = 1.0
+    law = _exact_outcome_law(p, q, mode)
+    assert abs(sum(law.values()) - 1.0) < 1e-12
+    # Losslessness: the token emitted at each reached position follows p_j,
+    # and the accepted length follows prod(beta_i) (1 - beta_k).
+    beta = [np.minimum(p[j], q[j]).sum() for j in range(G)]
+    for j in range(G + 1):
+        reach = np.prod(beta[:j])
+        marg = np.zeros(V)
+        for (k, toks), pr in law.items():
+            if k >= j:
+                marg[toks[j]] += pr
+        np.testing.assert_allclose(marg, reach * p[j], atol=1e-12)
+    for k in range(G + 1):
+        pk = sum(pr for (kk, _), pr in law.items() if kk == k)
+        want = np.prod(beta[:k]) * ((1 - beta[k]) if k < G else 1.0)
+        assert abs(pk - want) < 1e-12
+    # Empirical law of the oracle over n_runs independent requests.
+    rng = np.random.default_rng(seed)
+    ltb = np.broadcast_to(lt[None], (n_runs,) + lt.shape).copy()
+    if mode == "prob":
+        ldb = np.broadcast_to(ld[None], (n_runs,) + ld.shape).copy()
+        x = np.stack([rng.choice(V, size=n_runs, p=q[j]) for j in range(G)], axis=1).astype(np.int32)
+        res = oracle.verify(oracle.MODE_PROB, ltb, ldb, x, temperature=T, top_k=top_k, seed=seed)
+    else:
+        x = np.broadcast_to(np.argmax(ld, axis=-1)[None].astype(np.int32), (n_runs, G)).copy()
+        res = oracle.verify(oracle.MODE_ONEHOT, ltb, None, x, temperature=T, top_k=top_k, seed=seed)
+    keys = list(law)
+    index = {k: i for i, k in enumerate(keys)}
+    counts = np.zeros(len(keys))
+    for r in range(n_runs):
+        k = int(res["num_accepted"][r])
+        toks = tuple(int(t) for t in res["out_tokens"][r, :k + 1])
+        assert (k, toks) in index, f"impossible outcome {(k, toks)}"
+        counts[index[(k, toks)]] += 1
+    expected = np.array([law[k] for k in keys]) * n_runs
+    big = expected >= 5
+    obs = np.append(counts[big], counts[~big].sum())
+    exp = np.append(expected[big], expected[~big].sum())
+    if exp[-1] == 0:
+        obs, exp = obs[:-1], exp[:-1]
+    if len(exp) > 1:
+        assert stats.chisquare(obs, exp).pvalue > 1e-6
+
+
+def _logits(rows):
+    return _f32_logits(rows)
+
+
+@pytest.mark.parametrize("case", ["generic", "zeros", "equal", "v1", "topk1"])
+def test_brute_force_prob(case):
+    rng = np.random.default_rng(hash(case) % 2**32)
+    if case == "generic":
+        lt = (rng.standard_normal((3, 3)) * 1.5).astype(np.float32)
+        ld = (rng.standard_normal((2, 3)) * 1.5).astype(np.float32)
+        _check_brute_force(lt, ld, "prob", 200_000, 1)
+    elif case == "zeros":  # zeros in p and in q
+        lt = _logits([[0.5, 0.0, 0.3, 0.2], [0.0, 0.6, 0.4, 0.0], [0.1, 0.2, 0.3, 0.4]])
+        ld = _logits([[0.2, 0.4, 0.0, 0.4], [0.3, 0.3, 0.4, 0.0]])
+        _check_brute_force(lt, ld, "prob", 200_000, 2)
+    elif case == "equal":  # q == p: never rejected, n = G always
+        lt = (rng.standard_normal((4, 4))).astype(np.float32)
+        _check_brute_force(lt, lt[:3].copy(), "prob", 100_000, 3)
+    elif case == "v1":
+        lt = np.zeros((3, 1), dtype=np.float32)
+        _check_brute_force(lt, np.zeros((2, 1), dtype=np.float32), "prob", 1000, 4)
+    elif case == "topk1":
+        lt = (rng.standard_normal((3, 4)) * 2).astype(np.float32)
+        ld = (rng.standard_normal((2, 4)) * 2).astype(np.float32)
+        _check_brute_force(lt, ld, "prob", 20_000, 5, top_k=1)
+
+
+def test_brute_force_onehot():
+    rng = np.random.default_rng(9)
+    lt = (rng.standard_normal((4, 4)) * 1.2).astype(np.float32)
+    ld = (rng.standard_normal((3, 4)) * 1.2).astype(np.float32)
+    _check_brute_force(lt, ld, "onehot", 200_000, 6, T=0.8)
+
+
+def test_brute_force_detects_naive_resampling():
+    """Power check: the deliberately wrong naive mode (resample from p after a
+    rejection) fails the same chi-square that the real rule passes."""
+    lt = _logits([[0.5, 0.25, 0.15, 0.1], [0.25, 0.25, 0.25, 0.25]])
+    ld = _logits([[0.3, 0.4, 0.1, 0.2]])
+    p = np.stack([oracle.row_probs(lt[j], 1.0) for j in range(2)])
+    q = oracle.row_probs(ld[0], 1.0)[None]
+    law = _exact_outcome_law(p, q, "prob")
+    n = 100_000
+    rng = np.random.default_rng(8)
+    x = rng.choice(4, size=(n, 1), p=q[0]).astype(np.int32)
+    res = oracle.verify(oracle.MODE_NAIVE, np.broadcast_to(lt[None], (n, 2, 4)).copy(),
+                        np.broadcast_to(ld[None], (n, 1, 4)).copy(), x, seed=1)
+    first = np.bincount(res["out_tokens"][:, 0], minlength=4)
+    want = np.zeros(4)
+    for (k, toks), pr in law.items():
+        want[toks[0]] += pr
+    assert stats.chisquare(first, want * n).pvalue < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Exact reductions between the modes, and special cases
+# ---------------------------------------------------------------------------
+
+def test_topk1_prob_equals_greedy():
+    rng = np.random.default_rng(21)
+    n, G, V = 300, 4, 50
+    lt = (rng.standard_normal((n, G + 1, V)) * 2).astype(np.float32)
+    ld = (lt[:, :G] + rng.standard_normal((n, G, V))).astype(np.float32)
+    x = np.argmax(ld, axis=-1).astype(np.int32)
+    a = oracle.verify(oracle.MODE_PROB, lt, ld, x, temperature=0.9, top_k=1, seed=5)
+    g = oracle.verify(oracle.MODE_GREEDY, lt, None, x)
+    np.testing.assert_array_equal(a["num_accepted"], g["num_accepted"])
+    np.testing.assert_array_equal(a["out_tokens"], g["out_tokens"])
+    assert 0 < g["num_accepted"].mean() < G  # both outcomes present
+
+
+def test_onehot_by_logits_prob_equals_onehot():
+    rng = np.random.default_rng(22)
+    n, G, V = 400, 3, 40
+    lt = (rng.standard_normal((n, G + 1, V)) * 2).astype(np.float32)
+    x = rng.integers(0, V, (n, G)).astype(np.int32)
+    ld = np.full((n, G, V), -np.inf, dtype=np.float32)
+    np.put_along_axis(ld, x[..., None], 0.0, axis=-1)
+    a = oracle.verify(oracle.MODE_PROB, lt, ld, x, temperature=1.3, seed=77)
+    o = oracle.verify(oracle.MODE_ONEHOT, lt, None, x, temperature=1.3, seed=77)
+    np.testing.assert_array_equal(a["out_tokens"], o["out_tokens"])
+    np.testing.assert_array_equal(a["num_accepted"], o["num_accepted"])
+    np.testing.assert_array_equal(a["p_draft"], o["p_draft"])
+
+
+def test_p_zero_always_rejected_and_q_equal_p_never():
+    rng = np.random.default_rng(23)
+    n, G, V = 500, 3, 30
+    lt = (rng.standard_normal((n, G + 1, V))).astype(np.float32)
+    # Draft tokens outside the target's top-5: p(x) = 0 after top-k.
+    order = np.argsort(-lt[:, :G], axis=-1, kind="stable")
+    x = order[..., 10].astype(np.int32)
+    ld = lt[:, :G].copy()
+    r = oracle.verify(oracle.MODE_PROB, lt, ld, x, temperature=1.0, top_k=5)
+    assert (r["num_accepted"] == 0).all()
+    assert (r["p_draft"][:, 0] == 0).all()
+    # q = p: every draft accepted, the bonus follows.
+    x2 = rng.integers(0, V, (n, G)).astype(np.int32)
+    r2 = oracle.verify(oracle.MODE_PROB, lt, ld, x2, temperature=1.0)
+    assert (r2["num_accepted"] == G).all()
+
+
+def test_accounting_and_padding():
+    rng = np.random.default_rng(24)
+    n, G, V = 1000, 6, 20
+    lt = (rng.standard_normal((n, G + 1, V)) * 2).astype(np.float32)
+    ld = (lt[:, :G] + rng.standard_normal((n, G, V))).astype(np.float32)
+    x = rng.integers(0, V, (n, G)).astype(np.int32)
+    r = oracle.verify(oracle.MODE_PROB, lt, ld, x, temperature=1.0, seed=3)
+    emitted = (r["out_tokens"] >= 0).sum(axis=1)
+    np.testing.assert_array_equal(emitted, r["num_accepted"] + 1)
+    for k in range(n):
+        m = r["num_accepted"][k]
+        assert (r["out_tokens"][k, :m] == x[k, :m]).all()
+
+
+def test_out_of_range_draft_token_is_rejected_and_flagged():
+    lt = np.zeros((2, 3, 4), dtype=np.float32)
+    ld = np.zeros((2, 2, 4), dtype=np.float32)
+    x = np.array([[1, 7], [-1, 0]], dtype=np.int32)
+    r = oracle.verify(oracle.MODE_PROB, lt, ld, x, temperature=1.0)
+    assert r["num_accepted"][0] == 1 and r["num_accepted"][1] == 0
+    assert r["bad_token"].tolist() == [1, 1]
+    assert r["p_draft"][0, 1] == 0.0 and r["q_draft"][1, 0] == 0.0
+    g = oracle.verify(oracle.MODE_GREEDY, lt, None, x)
+    assert g["num_accepted"].tolist() == [0, 0]  # argmax of all-zero rows is 0
+
+
+def test_argument_validation():
+    lt = np.zeros((1, 2, 4), dtype=np.float32)
+    x = np.zeros((1, 1), dtype=np.int32)
+    with pytest.raises(ValueError):
+        oracle.verify(oracle.MODE_ONEHOT, lt, None, x, temperature=0.0)
+    with pytest.raises(ValueError):
+        oracle.verify(oracle.MODE_PROB, lt, None, x, temperature=1.0)
+    with pytest.raises(ValueError):
+        oracle.verify(oracle.MODE_ONEHOT, lt, None, x, temperature=1.0, top_k=-1)

@@ -1,0 +1,189 @@
+"""Seeded synthetic inputs for the speculative-sampling verifier.
+
+This module is shared by the tests, the smoke check and the benchmark.  It
+holds no verifier arithmetic: it draws logits, draft-logit noise and draft
+tokens (the drafter's side of a speculative round), and nothing else.  The
+verifier's own random numbers (accept uniforms, race exponentials) are not
+drawn here; both the GPU library and the oracle derive them from the Philox
+key (seed) on their own.
+
+Recipe (all torch generators seeded with ``data_seed``; requests generated in
+fixed-size chunks so that the bytes do not depend on the device's memory):
+  target logits  Lt[b, j, :] ~ N(0, sigma_t^2) i.i.d., rounded to the dtype
+                 (bf16: round-to-nearest-even).
+  draft logits   Ld[b, j, :] = Lt[b, j, :] + sigma_b * N(0, 1), with sigma_b
+                 fixed or drawn per request from U[lo, hi], rounded to dtype.
+  draft tokens   prob:   x ~ softmax over the top-k set of Ld/T (Gumbel-max:
+                         argmax of Ld/T + Gumbel noise over the kept tokens;
+                         the kept set is the first k of a stable descending
+                         sort, i.e. ties to the lowest index);
+                 onehot: x = argmax(Lt + N(0, 1)) (greedy drafter);
+                 greedy: x = argmax Lt with probability ``greedy_match``,
+                         else a uniform draw from the other V - 1 ids.
+The five workloads mirror the shapes of the reference pages' setting scaled
+to a batch (gamma 3..8 as on the pages, temperatures 0 / 0.7 / 0.8 / 1,
+acceptance rates spanning the 0.5..0.9 range quoted for good drafter pairs).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    entry: str            # "prob" | "onehot" | "greedy"
+    B: int                # requests
+    G: int                # gamma: draft positions per request
+    V: int                # vocabulary size
+    dtype: str            # "f32" | "bf16"
+    temperature: float    # 0 for greedy
+    top_k: int            # 0 = off
+    target_sigma: float
+    draft_sigma: tuple    # (lo, hi); lo == hi for a fixed sigma
+    greedy_match: float = 0.8
+    data_seed: int = 0
+    verify_seed: int = 42
+    chunk: int = 8        # requests generated per generator call
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def target_rows(self) -> int:
+        return self.B * (self.G + 1)
+
+    @property
+    def draft_rows(self) -> int:
+        return self.B * self.G if self.entry == "prob" else 0
+
+    @property
+    def logit_bytes(self) -> int:
+        """Bytes of every logit row read once: the algorithmic traffic."""
+        return (self.target_rows + self.draft_rows) * self.V * self.elem_bytes
+
+    def scaled(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    # 8 requests, gamma 4, V 32000, fp32, T = 1, draft = target + N(0, 1).
+    "prob_f32_b8_g4_v32000": Workload("prob_f32_b8_g4_v32000", "prob", 8, 4, 32000, "f32", 1.0, 0,
+                                      3.0, (1.0, 1.0)),
+    # 64 requests, gamma 5, V 128256, bf16, greedy (T = 0), 0.8 argmax matches.
+    "greedy_bf16_b64_g5_v128256": Workload("greedy_bf16_b64_g5_v128256", "greedy", 64, 5, 128256, "bf16",
+                                           0.0, 0, 2.5, (0.0, 0.0), greedy_match=0.8),
+    # 256 requests, gamma 7, V 151936, fp32, T = 0.8, sigma_b ~ U[0.5, 2].
+    "prob_f32_b256_g7_v151936": Workload("prob_f32_b256_g7_v151936", "prob", 256, 7, 151936, "f32", 0.8, 0,
+                                         3.0, (0.5, 2.0)),
+    # 512 requests, gamma 3, V 262144, bf16, T = 1, greedy drafter, one-hot q.
+    "onehot_bf16_b512_g3_v262144": Workload("onehot_bf16_b512_g3_v262144", "onehot", 512, 3, 262144, "bf16",
+                                            1.0, 0, 3.0, (1.0, 1.0)),
+    # 1024 requests, gamma 8, V 256000, bf16, T = 0.7 then top-64 on p and q.
+    "prob_topk64_bf16_b1024_g8_v256000": Workload("prob_topk64_bf16_b1024_g8_v256000", "prob", 1024, 8, 256000,
+                                                  "bf16", 0.7, 64, 3.0, (0.3, 2.5)),
+}
+
+WORKLOAD_ORDER = list(WORKLOADS)
+HEADLINE = "prob_topk64_bf16_b1024_g8_v256000"
+
+
+def _gumbel_argmax(scores: torch.Tensor, gen: torch.Generator) -> torch.Tensor:
+    """argmax(scores + Gumbel) along the last axis (lowest index on ties)."""
+    u = torch.rand(scores.shape, generator=gen, device=scores.device, dtype=torch.float32)
+    g = -torch.log(-torch.log(u))
+    return torch.argmax(scores + g, dim=-1)
+
+
+def _draft_tokens_prob(ld: torch.Tensor, wl: Workload, gen: torch.Generator) -> torch.Tensor:
+    z = ld.float() / wl.temperature
+    if 0 < wl.top_k < wl.V:
+        vals, idx = torch.sort(z, dim=-1, descending=True, stable=True)
+        pick = _gumbel_argmax(vals[..., : wl.top_k], gen)
+        return torch.gather(idx[..., : wl.top_k], -1, pick.unsqueeze(-1)).squeeze(-1)
+    return _gumbel_argmax(z, gen)
+
+
+def generate(wl: Workload, device="cpu", requests: range | None = None) -> dict:
+    """Inputs of ``wl`` on ``device``: target_logits [B, G+1, V], draft_logits
+    [B, G, V] (prob only, else None), draft_tokens [B, G] int32.
+
+    ``requests`` restricts generation to whole chunks covering that range and
+    returns only those requests (same bytes as a full generation).
+    """
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(wl.data_seed)
+    B, G, V = wl.B, wl.G, wl.V
+    lo_req, hi_req = (0, B) if requests is None else (requests.start, requests.stop)
+    lt_all = torch.empty((hi_req - lo_req, G + 1, V), dtype=wl.torch_dtype, device=device)
+    ld_all = (torch.empty((hi_req - lo_req, G, V), dtype=wl.torch_dtype, device=device)
+              if wl.entry == "prob" else None)
+    x_all = torch.empty((hi_req - lo_req, G), dtype=torch.int32, device=device)
+    for c0 in range(0, B, wl.chunk):
+        c1 = min(B, c0 + wl.chunk)
+        if c1 <= lo_req:
+            # Draw and discard so that later chunks see the same stream.
+            _chunk(wl, c1 - c0, gen, device)
+            continue
+        if c0 >= hi_req:
+            break
+        lt, ld, x = _chunk(wl, c1 - c0, gen, device)
+        a, bnd = max(c0, lo_req), min(c1, hi_req)
+        lt_all[a - lo_req: bnd - lo_req] = lt[a - c0: bnd - c0]
+        if ld_all is not None:
+            ld_all[a - lo_req: bnd - lo_req] = ld[a - c0: bnd - c0]
+        x_all[a - lo_req: bnd - lo_req] = x[a - c0: bnd - c0]
+    return {"target_logits": lt_all, "draft_logits": ld_all, "draft_tokens": x_all}
+
+
+def _chunk(wl: Workload, c: int, gen: torch.Generator, device):
+    G, V = wl.G, wl.V
+    lt = (torch.randn((c, G + 1, V), generator=gen, device=device, dtype=torch.float32)
+          * wl.target_sigma).to(wl.torch_dtype)
+    ld = None
+    if wl.entry == "prob":
+        lo, hi = wl.draft_sigma
+        sig = lo + (hi - lo) * torch.rand((c, 1, 1), generator=gen, device=device, dtype=torch.float32)
+        noise = torch.randn((c, G, V), generator=gen, device=device, dtype=torch.float32)
+        ld = (lt[:, :G].float() + sig * noise).to(wl.torch_dtype)
+        x = _draft_tokens_prob(ld, wl, gen)
+    elif wl.entry == "onehot":
+        noise = torch.randn((c, G, V), generator=gen, device=device, dtype=torch.float32)
+        x = torch.argmax(lt[:, :G].float() + noise * wl.draft_sigma[0], dim=-1)
+    elif wl.entry == "greedy":
+        amax = torch.argmax(lt[:, :G].float(), dim=-1)
+        match = torch.rand((c, G), generator=gen, device=device) < wl.greedy_match
+        other = torch.randint(0, max(V - 1, 1), (c, G), generator=gen, device=device)
+        other = other + (other >= amax).to(other.dtype)
+        x = torch.where(match, amax, other) if V > 1 else amax
+    else:
+        raise ValueError(wl.entry)
+    return lt, ld, x.to(torch.int32)
+
+
+def to_host_arrays(t: torch.Tensor | None):
+    """float32 -> np.float32; bfloat16 -> np.uint16 bit patterns (for the oracle)."""
+    if t is None:
+        return None
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.int32:
+        return t.numpy()
+    raise TypeError(t.dtype)
+
+
+__all__ = ["Workload", "WORKLOADS", "WORKLOAD_ORDER", "HEADLINE", "generate", "to_host_arrays"]
