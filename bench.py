@@ -1,0 +1,212 @@
+"""Throughput of the speculative-sampling verifier on one MI355X.
+
+One step = one call of the verifier over the whole batch (every logit row
+read, every request verified).  Default workload: 1024 requests, gamma 8,
+vocabulary 256000, bf16 logits, temperature 0.7 then top-64 on p and q,
+probabilistic draft (spec_verify_prob).  Inputs are seeded synthetic logits
+generated on the GPU and resident in HBM before the timed region.
+
+Prints one JSON line: verified draft positions per second (value), plus
+rows/s, algorithmic GB/s, the roofline of the dominant kernel (the row pass,
+timed with HIP events on the launch stream) and the fp64 CPU oracle timed on
+a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "speculative_decoding_rejection_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, per_launch_alg: float):
+    """HBM bytes per launch of the row pass from committed rocprofv3 counter
+    runs, if they were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "rows_topk_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_hash") != kernel_source_hash() or t.get("workload") != workload:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, target_seconds: float) -> dict:
+    import oracle
+    import workloads
+
+    modes = {"prob": oracle.MODE_PROB, "onehot": oracle.MODE_ONEHOT, "greedy": oracle.MODE_GREEDY}
+
+    def run(n):
+        sub = slice(0, n)
+        lt = workloads.to_host_arrays(inp["target_logits"][sub])
+        ld = workloads.to_host_arrays(inp["draft_logits"][sub]) if wl.entry == "prob" else None
+        x = workloads.to_host_arrays(inp["draft_tokens"][sub])
+        t0 = time.perf_counter()
+        oracle.verify(modes[wl.entry], lt, ld, x, temperature=wl.temperature, top_k=wl.top_k,
+                      seed=wl.verify_seed)
+        return time.perf_counter() - t0
+
+    threads = oracle.max_threads()
+    n = min(wl.B, max(4, threads))
+    t = run(n)
+    if t < target_seconds / 3 and n < wl.B:
+        n = int(min(wl.B, max(n + 1, n * target_seconds / max(t, 1e-3))))
+        t = run(n)
+    return {
+        "value": n * wl.G / t,
+        "unit": "verified draft positions/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"first {n} of {wl.B} requests of the same workload (fp64 oracle, OpenMP over requests), "
+                  f"{t:.2f} s wall",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the verifier shards by request "
+              f"with no exchange; run one process per GPU on its share)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import speculative_decoding_rejection_amd as sv
+    import workloads
+
+    name = args.workload or workloads.HEADLINE
+    wl = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    sv.load_library()
+    log(f"[bench] {name}: generating inputs on {torch.cuda.get_device_name(0)}")
+    inp = workloads.generate(wl, device=dev)
+    torch.cuda.synchronize()
+
+    params = sv.make_params(wl.B, wl.G, wl.V, wl.torch_dtype, wl.temperature or 1.0, wl.top_k, wl.verify_seed)
+    ws = sv.alloc_workspace(params, dev)
+    B, G = wl.B, wl.G
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    pd = torch.empty((B, G), dtype=torch.float32, device=dev)
+    qd = torch.empty((B, G), dtype=torch.float32, device=dev)
+    ta = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    lt, ld, x = inp["target_logits"], inp["draft_logits"], inp["draft_tokens"]
+
+    def step():
+        if wl.entry == "prob":
+            sv.spec_verify_prob(params, lt, ld, x, out, nacc, pd, qd, ws, stream)
+        elif wl.entry == "onehot":
+            sv.spec_verify_onehot(params, lt, x, out, nacc, pd, ws, stream)
+        else:
+            sv.spec_verify_greedy(params, lt, x, out, nacc, ta, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+
+    sv.sv_kernel_timing_reset()
+    sv.sv_kernel_timing_enable(True)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    sv.sv_kernel_timing_enable(False)
+    dev_ms = ev0.elapsed_time(ev1)
+    rows_ms, rows_n = sv.sv_kernel_timing_read(sv.FAMILY_ROWS)
+    acc_ms, acc_n = sv.sv_kernel_timing_read(sv.FAMILY_ACCEPT)
+    race_ms, race_n = sv.sv_kernel_timing_read(sv.FAMILY_RACE)
+    log(f"[bench] timed: wall {wall * 1e3:.2f} ms, device {dev_ms:.2f} ms; rows {rows_ms:.2f} ms/{rows_n}, "
+        f"accept {acc_ms:.2f} ms/{acc_n}, race {race_ms:.2f} ms/{race_n}")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 copies of 1 GiB done")
+
+    sec = wall / args.steps
+    positions = B * G
+    rows = wl.target_rows + wl.draft_rows
+    bytes_alg = wl.logit_bytes
+    row_avg_s = rows_ms / max(rows_n, 1) / 1e3
+    achieved = bytes_alg / row_avg_s / 1e9
+    traffic = load_traffic(name, bytes_alg)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+    res = {
+        "metric": "verified draft positions/sec and HBM GB/s (% of peak) at B=1024,gamma=8,V=256k",
+        "value": positions / sec,
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded, generated on the GPU; no dataset)",
+        "config": {"workload": name, "entry": f"spec_verify_{wl.entry}", "batch": B, "gamma": G, "vocab": wl.V,
+                   "logits": wl.dtype, "temperature": wl.temperature, "top_k": wl.top_k,
+                   "parallelism": "single GPU"},
+        "rows_per_s": rows / sec,
+        "requests_per_s": B / sec,
+        "algorithmic_gbps": bytes_alg / sec / 1e9,
+        "hbm_fraction": bytes_alg / sec / 1e9 / HBM_PEAK_GBPS,
+        "kernels_ms_per_step": {"rows": rows_ms / max(rows_n, 1), "accept": acc_ms / max(acc_n, 1),
+                                "race": (race_ms / race_n) if race_n else 0.0},
+        "roofline": {"bound": "hbm", "kernel": "row pass (rows_topk_kernel)" if wl.top_k else "row pass",
+                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,141 @@
+/*
+ * libspecverify: batched speculative-sampling verifier for MI355X (gfx950).
+ *
+ * The operation is the verification half of one speculative-decoding round
+ * (page "초안 모델로 생성 속도를 높이는 추측 디코딩", section "방법",
+ * Algorithm 1; page "vLLM speculative decoding이 기각 토큰을 다시 뽑는 이유",
+ * section "드래프트가 제안하고 타깃이 판정한다").  For each request b the
+ * target model scored G+1 positions and the drafter proposed G tokens x_j:
+ *
+ *   p_j = softmax(topk(target_logits[b, j, :] / T))   j = 0..G
+ *   q_j = softmax(topk(draft_logits[b, j, :] / T))    j = 0..G-1
+ *   accept x_j iff u_j <= p_j(x_j) / q_j(x_j)          (q_j(x_j) > 0)
+ *   n   = first rejected position, or G
+ *   out[0..n-1] = x_0..x_{n-1}
+ *   out[n]      = a draw from norm(max(0, p_n - q_n))  if n < G (recovered)
+ *               = a draw from p_G                     if n = G (bonus)
+ *   out[n+1..G] = -1
+ *
+ * The recovered/bonus draw is the Exp(1) race argmax_y w_y / E_y (page on
+ * vLLM's kernel, section "vLLM 커널은 이 규칙을 어떻게 옮겼나"), so the
+ * residual is never normalised.  Temperature and top-k are applied to the
+ * logits first, to p and to q alike (same section: p is the adjusted law).
+ *
+ * Random numbers: a counter-based Philox4x32-10 keyed by sv_params.seed.
+ * The accept uniform of (b, j) comes from counter (0, j, b, 0), words 0 and
+ * 1; the race uniform of token y at position j from counter (y>>1, j, b, 1),
+ * words (0,1) for even y and (2,3) for odd y.  Two words (lo, hi) map to
+ * u = ((hi:lo >> 11) + 1) * 2^-53 in (0, 1], in fp64, so u is never 0.
+ * E = -ln(u).  Results are a pure function of the inputs and the seed.
+ *
+ * Ties: every argmax (greedy target token, race winner) goes to the lowest
+ * index; top-k keeps exactly k tokens ranked by (logit desc, index asc).
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller; the
+ *    library never allocates or frees device memory.  Rows are contiguous
+ *    (row stride = vocab); logits are fp32 or bf16 (sv_params.dtype), aligned
+ *    to their element size.
+ *  - workspace: caller-owned device scratch of at least
+ *    sv_workspace_bytes(params) bytes, 256-byte aligned.  Its contents on
+ *    entry are ignored; calls that share a workspace must not overlap.
+ *  - stream: a hipStream_t passed as void* (NULL = the default stream).  Calls
+ *    only enqueue work: there is no host synchronisation and no readback.
+ *  - Argument errors and launch errors are returned synchronously as an
+ *    sv_status; nothing is enqueued after an argument error.
+ *  - A draft token outside [0, vocab) is treated as rejected at its
+ *    position (q(x) := 0, a greedy mismatch) and sets a sticky code in the
+ *    workspace that sv_read_device_error reports.
+ *  - A row whose logits are all -inf, or that holds NaN or +inf, has no
+ *    defined law: results for it are unspecified (no fault).
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = 1,  /* bad size, temperature, top_k or null pointer */
+  SV_ERR_DTYPE = 2,        /* dtype not SV_F32 / SV_BF16, or misaligned logits */
+  SV_ERR_WORKSPACE = 3,    /* workspace null, misaligned or too small */
+  SV_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
+  SV_ERR_UNSUPPORTED = 5   /* top_k in (1024, vocab): not implemented */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef struct {
+  int32_t batch;       /* B >= 1 requests */
+  int32_t gamma;       /* G >= 1 draft positions per request */
+  int32_t vocab;       /* V >= 1 */
+  int32_t dtype;       /* sv_dtype of every logit array */
+  float temperature;   /* T > 0 (finite) for prob/onehot; ignored by greedy */
+  int32_t top_k;       /* 0 or >= vocab: off; else keep k <= 1024 tokens */
+  uint64_t seed;       /* Philox key */
+} sv_params;
+
+/* Bytes of workspace any entry point needs for these parameters (0 if the
+ * parameters are invalid). */
+size_t sv_workspace_bytes(const sv_params* params);
+
+/* Static, human-readable text of a status code. */
+const char* sv_status_string(sv_status status);
+
+/* Probabilistic draft ("probabilistic" draft sampling on the vLLM page,
+ * section "기본값 greedy 드래프트에서도 분포가 지켜질까"; the residual rule
+ * of section "왜 하필 max(p − q, 0)인가").
+ *   target_logits [B][G+1][V], draft_logits [B][G][V], draft_tokens [B][G]
+ *   out_tokens [B][G+1] (-1 after the emitted token), num_accepted [B] = n
+ *   p_draft, q_draft [B][G]: p_j(x_j), q_j(x_j) for every j (may be NULL). */
+sv_status spec_verify_prob(const sv_params* params, const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, int32_t* out_tokens, int32_t* num_accepted,
+                           float* p_draft, float* q_draft, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* One-hot draft (a greedy drafter, vLLM's default; same page, section
+ * "기본값 greedy 드래프트에서도 분포가 지켜질까"): q(x) = 1, accept iff
+ * u <= p(x), the residual is p with x masked.  Arguments as spec_verify_prob
+ * without draft logits; p_draft [B][G] may be NULL. */
+sv_status spec_verify_onehot(const sv_params* params, const void* target_logits, const int32_t* draft_tokens,
+                             int32_t* out_tokens, int32_t* num_accepted, float* p_draft, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Temperature 0 (page "초안 모델로 생성 속도를 높이는 추측 디코딩", section
+ * "방법": at T = 0 a draft token is accepted only if it is the target's
+ * argmax; the vLLM page's greedy kernel).  Accept iff x_j == argmax_y
+ * target_logits[b, j, y]; the target argmax replaces the first mismatch and
+ * is the bonus after G matches.  temperature and top_k are ignored; seed is
+ * unused.  target_argmax [B][G+1] may be NULL. */
+sv_status spec_verify_greedy(const sv_params* params, const void* target_logits, const int32_t* draft_tokens,
+                             int32_t* out_tokens, int32_t* num_accepted, int32_t* target_argmax,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream`, then copies the sticky device error word of the
+ * last call that used `workspace` to *host_code: 0 = none, 1 = a draft token
+ * was out of range. */
+sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream);
+
+/* Per-kernel timing for measurement.  While enabled, every launch of the
+ * library is bracketed by a pair of HIP events on the caller's stream;
+ * sv_kernel_timing_read synchronises on the recorded events and returns the
+ * summed device time (ms) and launch count of one kernel family:
+ *   0 = row pass (softmax / top-k / argmax over every logit row),
+ *   1 = per-request accept + scan (+ race over top-k candidates),
+ *   2 = residual / bonus race over a full row.
+ * Process-global; not thread-safe; at most 65536 launches per family are
+ * recorded between resets. */
+sv_status sv_kernel_timing_enable(int enable);
+sv_status sv_kernel_timing_reset(void);
+sv_status sv_kernel_timing_read(int family, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,61 @@
+"""Comparison of a verifier result with the oracle's (test infrastructure).
+
+The bar: p(x_j) and q(x_j) within an absolute tolerance; accepted lengths and
+every emitted token identical on every request whose decisions all had a
+relative margin above the near-tie threshold; on a request with a near-tie
+decision at position j0, identical before j0.  The greedy path compares
+exact input values and has no near-tie exemption.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import near_tie_position
+
+
+def compare(entry: str, got: dict, ref: dict, prob_tol: float = 1e-5, tie: float = 1e-4) -> dict:
+    out_g, out_r = np.asarray(got["out_tokens"]), ref["out_tokens"]
+    n_g, n_r = np.asarray(got["num_accepted"]), ref["num_accepted"]
+    nreq, G1 = out_r.shape
+    rep = {"requests": int(nreq), "rows": int(nreq * G1), "max_dp": 0.0, "max_dq": 0.0,
+           "near_tie_requests": 0, "mismatch_non_tie": 0, "mismatch_tie": 0, "bad": []}
+    if entry == "greedy":
+        diff = np.nonzero((out_g != out_r).any(axis=1) | (n_g != n_r))[0]
+        rep["mismatch_non_tie"] = int(diff.size)
+        rep["bad"] = diff[:10].tolist()
+        if "target_argmax" in got:
+            rep["argmax_mismatch"] = int((np.asarray(got["target_argmax"]) != ref["target_argmax"]).sum())
+        return rep
+    rep["max_dp"] = float(np.max(np.abs(np.asarray(got["p_draft"], np.float64) - ref["p_draft"])))
+    if "q_draft" in got and got["q_draft"] is not None:
+        rep["max_dq"] = float(np.max(np.abs(np.asarray(got["q_draft"], np.float64) - ref["q_draft"])))
+    pos = near_tie_position(ref, tie)
+    rep["near_tie_requests"] = int((pos >= 0).sum())
+    for r in range(nreq):
+        same = (n_g[r] == n_r[r]) and bool((out_g[r] == out_r[r]).all())
+        if same:
+            continue
+        if pos[r] >= 0:
+            j0 = int(pos[r])
+            if (out_g[r, :j0] == out_r[r, :j0]).all() and n_g[r] >= j0:
+                rep["mismatch_tie"] += 1
+                continue
+        rep["mismatch_non_tie"] += 1
+        if len(rep["bad"]) < 10:
+            rep["bad"].append(r)
+    return rep
+
+
+def assert_parity(entry: str, got: dict, ref: dict, prob_tol: float = 1e-5, tie: float = 1e-4,
+                  max_tie_fraction: float | None = None) -> dict:
+    rep = compare(entry, got, ref, prob_tol, tie)
+    assert rep["mismatch_non_tie"] == 0, f"token/length mismatch outside near-ties: {rep}"
+    if entry == "greedy":
+        assert rep.get("argmax_mismatch", 0) == 0, rep
+    else:
+        assert rep["max_dp"] <= prob_tol, rep
+        assert rep["max_dq"] <= prob_tol, rep
+    if max_tie_fraction is not None:
+        assert rep["near_tie_requests"] <= max_tie_fraction * rep["rows"], rep
+    return rep

@@ -1,0 +1,205 @@
+"""Python binding of libspecverify (ctypes): argument marshalling only.
+
+Every step of the verifier runs in the HIP kernels of libspecverify.so; this
+module passes device pointers, sizes and the current HIP stream through the C
+ABI declared in include/specverify.h, and uses PyTorch only to allocate device
+memory.  There is no fallback: if the library is not built, importing a
+function raises.
+
+Same names as the C ABI: sv_workspace_bytes, sv_status_string,
+spec_verify_prob, spec_verify_onehot, spec_verify_greedy,
+sv_read_device_error, sv_kernel_timing_enable / _reset / _read.  ``verify``
+is a convenience wrapper that allocates the outputs and the workspace.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED = range(6)
+SV_F32, SV_BF16 = 0, 1
+FAMILY_ROWS, FAMILY_ACCEPT, FAMILY_RACE = 0, 1, 2
+
+
+class SvParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("gamma", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("temperature", ctypes.c_float),
+        ("top_k", ctypes.c_int32),
+        ("seed", ctypes.c_uint64),
+    ]
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {sv_status_string(status)} (status {status})")
+
+
+_lib = None
+
+
+def load_library():
+    """Loads the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                           f"g.build()'` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    pp = ctypes.POINTER(SvParams)
+    lib.sv_workspace_bytes.argtypes = [pp]
+    lib.sv_workspace_bytes.restype = sz
+    lib.sv_status_string.argtypes = [ctypes.c_int]
+    lib.sv_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_prob.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_prob.restype = ctypes.c_int
+    lib.spec_verify_onehot.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_onehot.restype = ctypes.c_int
+    lib.spec_verify_greedy.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_greedy.restype = ctypes.c_int
+    lib.sv_read_device_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
+    lib.sv_read_device_error.restype = ctypes.c_int
+    lib.sv_kernel_timing_enable.argtypes = [ctypes.c_int]
+    lib.sv_kernel_timing_enable.restype = ctypes.c_int
+    lib.sv_kernel_timing_reset.argtypes = []
+    lib.sv_kernel_timing_reset.restype = ctypes.c_int
+    lib.sv_kernel_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
+                                          ctypes.POINTER(ctypes.c_int64)]
+    lib.sv_kernel_timing_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def make_params(batch, gamma, vocab, dtype, temperature=1.0, top_k=0, seed=0) -> SvParams:
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.float32: SV_F32, torch.bfloat16: SV_BF16}[dtype]
+    return SvParams(int(batch), int(gamma), int(vocab), int(dtype), float(temperature), int(top_k),
+                    int(seed) & 0xFFFFFFFFFFFFFFFF)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libspecverify takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status, where):
+    if status != SV_OK:
+        raise SpecVerifyError(status, where)
+
+
+def sv_status_string(status: int) -> str:
+    return load_library().sv_status_string(int(status)).decode()
+
+
+def sv_workspace_bytes(params: SvParams) -> int:
+    return int(load_library().sv_workspace_bytes(ctypes.byref(params)))
+
+
+def spec_verify_prob(params, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted, p_draft,
+                     q_draft, workspace, stream=None):
+    st = load_library().spec_verify_prob(ctypes.byref(params), _ptr(target_logits), _ptr(draft_logits),
+                                         _ptr(draft_tokens), _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft),
+                                         _ptr(q_draft), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "spec_verify_prob")
+
+
+def spec_verify_onehot(params, target_logits, draft_tokens, out_tokens, num_accepted, p_draft, workspace,
+                       stream=None):
+    st = load_library().spec_verify_onehot(ctypes.byref(params), _ptr(target_logits), _ptr(draft_tokens),
+                                           _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(workspace),
+                                           workspace.numel(), _stream(stream))
+    _check(st, "spec_verify_onehot")
+
+
+def spec_verify_greedy(params, target_logits, draft_tokens, out_tokens, num_accepted, target_argmax, workspace,
+                       stream=None):
+    st = load_library().spec_verify_greedy(ctypes.byref(params), _ptr(target_logits), _ptr(draft_tokens),
+                                           _ptr(out_tokens), _ptr(num_accepted), _ptr(target_argmax),
+                                           _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st, "spec_verify_greedy")
+
+
+def sv_read_device_error(workspace, stream=None) -> int:
+    code = ctypes.c_int32(0)
+    _check(load_library().sv_read_device_error(_ptr(workspace), ctypes.byref(code), _stream(stream)),
+           "sv_read_device_error")
+    return int(code.value)
+
+
+def sv_kernel_timing_enable(enable: bool) -> None:
+    _check(load_library().sv_kernel_timing_enable(1 if enable else 0), "sv_kernel_timing_enable")
+
+
+def sv_kernel_timing_reset() -> None:
+    _check(load_library().sv_kernel_timing_reset(), "sv_kernel_timing_reset")
+
+
+def sv_kernel_timing_read(family: int) -> tuple[float, int]:
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(load_library().sv_kernel_timing_read(int(family), ctypes.byref(ms), ctypes.byref(n)),
+           "sv_kernel_timing_read")
+    return float(ms.value), int(n.value)
+
+
+def alloc_workspace(params: SvParams, device) -> torch.Tensor:
+    nbytes = sv_workspace_bytes(params)
+    if nbytes == 0:
+        raise SpecVerifyError(SV_ERR_INVALID_ARG, "sv_workspace_bytes")
+    # torch's caching allocator returns 256-byte-aligned blocks.
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def verify(entry: str, target_logits, draft_tokens, draft_logits=None, *, temperature=1.0, top_k=0, seed=0,
+           workspace=None, stream=None) -> dict:
+    """Allocates outputs (and a workspace if none is given) and runs one entry
+    point.  target_logits [B, G+1, V] fp32/bf16 on the GPU; draft_tokens
+    [B, G] int32; draft_logits [B, G, V] for the "prob" entry."""
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    dev = target_logits.device
+    params = make_params(B, G, V, target_logits.dtype, temperature, top_k, seed)
+    ws = workspace if workspace is not None else alloc_workspace(params, dev)
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    res = {"out_tokens": out, "num_accepted": nacc, "workspace": ws}
+    if entry == "prob":
+        pd = torch.empty((B, G), dtype=torch.float32, device=dev)
+        qd = torch.empty((B, G), dtype=torch.float32, device=dev)
+        spec_verify_prob(params, target_logits, draft_logits, draft_tokens, out, nacc, pd, qd, ws, stream)
+        res.update(p_draft=pd, q_draft=qd)
+    elif entry == "onehot":
+        pd = torch.empty((B, G), dtype=torch.float32, device=dev)
+        spec_verify_onehot(params, target_logits, draft_tokens, out, nacc, pd, ws, stream)
+        res.update(p_draft=pd)
+    elif entry == "greedy":
+        ta = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+        spec_verify_greedy(params, target_logits, draft_tokens, out, nacc, ta, ws, stream)
+        res.update(target_argmax=ta)
+    else:
+        raise ValueError(entry)
+    return res

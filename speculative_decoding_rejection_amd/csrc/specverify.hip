@@ -1,0 +1,346 @@
+// libspecverify C ABI: argument validation, workspace plan, kernel launches.
+// Declarations and the contract of every entry point: include/specverify.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "specverify.h"
+#include "sv_kernels.hpp"
+
+namespace {
+
+using sv::RaceDesc;
+
+constexpr int kRowThreads = 256;
+constexpr int kRowUnroll = 4;
+constexpr int kTopkUnroll = 4;
+constexpr int kMaxTopK = 1024;
+constexpr size_t kWsAlign = 256;
+constexpr int kEntryProb = 0, kEntryOnehot = 1, kEntryGreedy = 2;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Everything a call needs, derived from the parameters alone.
+struct Plan {
+  int B, G, V, dtype, esize;
+  int K;          // active top-k (0 = off)
+  int kcap;       // candidate keys stored per row (K rounded to its kernel tier)
+  float c;        // log2(e) / T
+  int rows_t, rows_d;
+  int S, seg;     // row-pass splits of the vocabulary (softmax / argmax)
+  int Sr, segr;   // race-pass splits
+  size_t off_err, off_part, off_cand, off_desc, off_slots, total;
+};
+
+int splits_for(int rows, int V, int target_blocks, int min_seg) {
+  int s = (target_blocks + rows - 1) / rows;
+  int smax = V / min_seg;
+  if (smax < 1) smax = 1;
+  if (s > smax) s = smax;
+  if (s < 1) s = 1;
+  return s;
+}
+
+int seg_for(int V, int S) {
+  // Split boundaries on multiples of 64 elements keep 16-byte alignment
+  // relative to the row start.
+  int seg = (V + S - 1) / S;
+  seg = (seg + 63) / 64 * 64;
+  return seg;
+}
+
+sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
+  if (!p) return SV_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->gamma < 1 || p->vocab < 1) return SV_ERR_INVALID_ARG;
+  if (p->dtype != SV_F32 && p->dtype != SV_BF16) return SV_ERR_DTYPE;
+  if (p->top_k < 0) return SV_ERR_INVALID_ARG;
+  if (entry != kEntryGreedy && !(p->temperature > 0.f && std::isfinite(p->temperature))) return SV_ERR_INVALID_ARG;
+  const int64_t B = p->batch, G = p->gamma, V = p->vocab;
+  const int64_t rows = B * (2 * G + 1);
+  if (rows > (int64_t)INT32_MAX / 64 || V > (int64_t)INT32_MAX - 1024) return SV_ERR_INVALID_ARG;
+  Plan q{};
+  q.B = (int)B;
+  q.G = (int)G;
+  q.V = (int)V;
+  q.dtype = p->dtype;
+  q.esize = p->dtype == SV_F32 ? 4 : 2;
+  q.K = (entry != kEntryGreedy && p->top_k > 0 && p->top_k < p->vocab) ? p->top_k : 0;
+  if (q.K > kMaxTopK) return SV_ERR_UNSUPPORTED;
+  q.kcap = q.K;
+  q.c = entry == kEntryGreedy ? 0.f : (float)(1.4426950408889634 / (double)p->temperature);
+  q.rows_t = (int)(B * (G + 1));
+  q.rows_d = (int)(B * G);  // sized for the prob entry; unused by the others
+  q.S = splits_for(q.rows_t + q.rows_d, q.V, 2048, 8192);
+  q.seg = seg_for(q.V, q.S);
+  q.S = (q.V + q.seg - 1) / q.seg;
+  q.Sr = splits_for(q.B, q.V, 4096, 2048);
+  q.segr = seg_for(q.V, q.Sr);
+  q.Sr = (q.V + q.segr - 1) / q.segr;
+  const size_t nrows = (size_t)q.rows_t + (size_t)q.rows_d;
+  size_t off = 0;
+  q.off_err = off;
+  off = align_up(off + sizeof(int), kWsAlign);
+  q.off_part = off;
+  // Row-pass partials: float2 (softmax) or uint64 (argmax), both 8 bytes.
+  off = align_up(off + nrows * (size_t)q.S * 8, kWsAlign);
+  q.off_cand = off;
+  off = align_up(off + (q.K ? nrows * (size_t)q.kcap * 8 : 0), kWsAlign);
+  q.off_desc = off;
+  off = align_up(off + (size_t)q.B * sizeof(RaceDesc), kWsAlign);
+  q.off_slots = off;
+  off = align_up(off + (size_t)q.B * 3 * 8, kWsAlign);
+  q.total = off;
+  *pl = q;
+  return SV_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Per-kernel timing (measurement only).
+// ---------------------------------------------------------------------------
+constexpr int kFamilies = 3;
+constexpr size_t kMaxTimed = 65536;
+bool g_timing = false;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_events[kFamilies];
+size_t g_used[kFamilies] = {0, 0, 0};
+
+struct TimedLaunch {
+  int fam;
+  hipStream_t st;
+  hipEvent_t stop = nullptr;
+  TimedLaunch(int f, hipStream_t s) : fam(f), st(s) {
+    if (!g_timing || g_used[fam] >= kMaxTimed) return;
+    auto& ev = g_events[fam];
+    if (g_used[fam] == ev.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess) return;
+      if (hipEventCreate(&b) != hipSuccess) {
+        (void)hipEventDestroy(a);
+        return;
+      }
+      ev.emplace_back(a, b);
+    }
+    if (hipEventRecord(ev[g_used[fam]].first, st) != hipSuccess) return;
+    stop = ev[g_used[fam]].second;
+  }
+  void done() {
+    if (!stop) return;
+    if (hipEventRecord(stop, st) == hipSuccess) ++g_used[fam];
+    stop = nullptr;
+  }
+};
+
+sv_status check_launch() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; }
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+sv_status check_common(const Plan& pl, const void* target_logits, const int32_t* draft_tokens, int32_t* out_tokens,
+                       int32_t* num_accepted, void* workspace, size_t workspace_bytes) {
+  if (!target_logits || !draft_tokens || !out_tokens || !num_accepted) return SV_ERR_INVALID_ARG;
+  if (!aligned(target_logits, (size_t)pl.esize)) return SV_ERR_DTYPE;
+  if (!aligned(draft_tokens, 4) || !aligned(out_tokens, 4) || !aligned(num_accepted, 4)) return SV_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < pl.total) return SV_ERR_WORKSPACE;
+  return SV_OK;
+}
+
+template <typename ET>
+sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st) {
+  TimedLaunch t(0, st);
+  hipLaunchKernelGGL((sv::rows_softmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(nrows * pl.S),
+                     dim3(kRowThreads), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.S, pl.seg, pl.c,
+                     (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err));
+  t.done();
+  return check_launch();
+}
+
+template <typename ET>
+sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st) {
+  TimedLaunch t(0, st);
+  uint64_t* cand = (uint64_t*)(ws + pl.off_cand);
+  int* err = (int*)(ws + pl.off_err);
+  if (pl.K <= 64) {
+    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 256, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
+                       (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.K, cand, err);
+  } else if (pl.K <= 256) {
+    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 1024, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
+                       (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.K, cand, err);
+  } else {
+    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 4096, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
+                       (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.K, cand, err);
+  }
+  t.done();
+  return check_launch();
+}
+
+template <typename ET, int MODE>
+sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const void* ld, const int32_t* X,
+                         int32_t* out, int32_t* nacc, float* p_draft, float* q_draft, char* ws, hipStream_t st) {
+  const int nrows = pl.rows_t + (MODE == 0 ? pl.rows_d : 0);
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  int* err = (int*)(ws + pl.off_err);
+  sv_status s;
+  if (pl.K) {
+    s = run_rows_topk<ET>(pl, lt, ld, nrows, ws, st);
+    if (s != SV_OK) return s;
+    TimedLaunch t(1, st);
+    hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(64), 0, st,
+                       (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, pl.c, k0, k1, out,
+                       nacc, p_draft, q_draft, err);
+    t.done();
+    return check_launch();
+  }
+  s = run_rows_softmax<ET>(pl, lt, ld, nrows, ws, st);
+  if (s != SV_OK) return s;
+  RaceDesc* desc = (RaceDesc*)(ws + pl.off_desc);
+  unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
+  {
+    TimedLaunch t(1, st);
+    hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
+                       (const ET*)ld, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, pl.c, k0,
+                       k1, out, nacc, p_draft, q_draft, desc, slots, err);
+    t.done();
+    s = check_launch();
+    if (s != SV_OK) return s;
+  }
+  TimedLaunch t(2, st);
+  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256>), dim3(pl.B * pl.Sr), dim3(256), 0, st, (const ET*)lt,
+                     (const ET*)ld, pl.G, pl.V, pl.Sr, pl.segr, pl.c, k0, k1, (const RaceDesc*)desc, slots, out);
+  t.done();
+  return check_launch();
+}
+
+template <typename ET>
+sv_status verify_greedy(const Plan& pl, const void* lt, const int32_t* X, int32_t* out, int32_t* nacc,
+                        int32_t* targ, char* ws, hipStream_t st) {
+  int* err = (int*)(ws + pl.off_err);
+  uint64_t* part = (uint64_t*)(ws + pl.off_part);
+  {
+    TimedLaunch t(0, st);
+    hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
+                       dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part, err);
+    t.done();
+    sv_status s = check_launch();
+    if (s != SV_OK) return s;
+  }
+  TimedLaunch t(1, st);
+  hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part, X, pl.G, pl.V,
+                     pl.S, out, nacc, targ, err);
+  t.done();
+  return check_launch();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sv_workspace_bytes(const sv_params* params) {
+  Plan pl;
+  if (make_plan(params, kEntryProb, &pl) != SV_OK) {
+    // Greedy parameters may carry any temperature.
+    if (make_plan(params, kEntryGreedy, &pl) != SV_OK) return 0;
+  }
+  return pl.total;
+}
+
+const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument (size, temperature, top_k or null pointer)";
+    case SV_ERR_DTYPE: return "unsupported dtype or misaligned logits";
+    case SV_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or smaller than sv_workspace_bytes()";
+    case SV_ERR_HIP: return "HIP runtime or kernel launch failure";
+    case SV_ERR_UNSUPPORTED: return "top_k above 1024 (and below vocab) is not supported";
+  }
+  return "unknown status";
+}
+
+sv_status spec_verify_prob(const sv_params* params, const void* target_logits, const void* draft_logits,
+                           const int32_t* draft_tokens, int32_t* out_tokens, int32_t* num_accepted, float* p_draft,
+                           float* q_draft, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sv_status s = make_plan(params, kEntryProb, &pl);
+  if (s != SV_OK) return s;
+  s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
+  if (s != SV_OK) return s;
+  if (!draft_logits) return SV_ERR_INVALID_ARG;
+  if (!aligned(draft_logits, (size_t)pl.esize)) return SV_ERR_DTYPE;
+  if ((p_draft && !aligned(p_draft, 4)) || (q_draft && !aligned(q_draft, 4))) return SV_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (pl.dtype == SV_F32)
+    return verify_sampled<float, 0>(pl, params->seed, target_logits, draft_logits, draft_tokens, out_tokens,
+                                    num_accepted, p_draft, q_draft, ws, st);
+  return verify_sampled<uint16_t, 0>(pl, params->seed, target_logits, draft_logits, draft_tokens, out_tokens,
+                                     num_accepted, p_draft, q_draft, ws, st);
+}
+
+sv_status spec_verify_onehot(const sv_params* params, const void* target_logits, const int32_t* draft_tokens,
+                             int32_t* out_tokens, int32_t* num_accepted, float* p_draft, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sv_status s = make_plan(params, kEntryOnehot, &pl);
+  if (s != SV_OK) return s;
+  s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
+  if (s != SV_OK) return s;
+  if (p_draft && !aligned(p_draft, 4)) return SV_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (pl.dtype == SV_F32)
+    return verify_sampled<float, 1>(pl, params->seed, target_logits, nullptr, draft_tokens, out_tokens, num_accepted,
+                                    p_draft, nullptr, ws, st);
+  return verify_sampled<uint16_t, 1>(pl, params->seed, target_logits, nullptr, draft_tokens, out_tokens,
+                                     num_accepted, p_draft, nullptr, ws, st);
+}
+
+sv_status spec_verify_greedy(const sv_params* params, const void* target_logits, const int32_t* draft_tokens,
+                             int32_t* out_tokens, int32_t* num_accepted, int32_t* target_argmax, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sv_status s = make_plan(params, kEntryGreedy, &pl);
+  if (s != SV_OK) return s;
+  s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
+  if (s != SV_OK) return s;
+  if (target_argmax && !aligned(target_argmax, 4)) return SV_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (pl.dtype == SV_F32)
+    return verify_greedy<float>(pl, target_logits, draft_tokens, out_tokens, num_accepted, target_argmax, ws, st);
+  return verify_greedy<uint16_t>(pl, target_logits, draft_tokens, out_tokens, num_accepted, target_argmax, ws, st);
+}
+
+sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream) {
+  if (!workspace || !host_code) return SV_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return SV_ERR_HIP;
+  if (hipMemcpy(host_code, workspace, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return SV_ERR_HIP;
+  return SV_OK;
+}
+
+sv_status sv_kernel_timing_enable(int enable) {
+  g_timing = enable != 0;
+  return SV_OK;
+}
+
+sv_status sv_kernel_timing_reset(void) {
+  for (int f = 0; f < kFamilies; ++f) g_used[f] = 0;
+  return SV_OK;
+}
+
+sv_status sv_kernel_timing_read(int family, double* total_ms, int64_t* launches) {
+  if (family < 0 || family >= kFamilies || !total_ms || !launches) return SV_ERR_INVALID_ARG;
+  double tot = 0.0;
+  for (size_t i = 0; i < g_used[family]; ++i) {
+    const auto& ev = g_events[family][i];
+    if (hipEventSynchronize(ev.second) != hipSuccess) return SV_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev.first, ev.second) != hipSuccess) return SV_ERR_HIP;
+    tot += ms;
+  }
+  *total_ms = tot;
+  *launches = (int64_t)g_used[family];
+  return SV_OK;
+}
+
+}  // extern "C"

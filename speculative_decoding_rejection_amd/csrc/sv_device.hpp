@@ -1,0 +1,200 @@
+// Device-side building blocks of libspecverify (gfx950, wave64).
+//
+// Counter-based uniforms, the (value, index) order keys used by top-k and
+// argmax, logit unpacking, and wave-level reductions.  Everything here is
+// independent of the CPU oracle: the Philox below is written from the
+// definition in Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10.  Round: (c0,c1,c2,c3) -> (hi(B*c2)^c1^k0, lo(B*c2),
+// hi(A*c0)^c3^k1, lo(A*c0)) with A = 0xD2511F53, B = 0xCD9E8D57; the key
+// advances by the golden-ratio and sqrt(3)-1 Weyl increments between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t a_lo = c.x * 0xD2511F53u;
+    const uint32_t a_hi = __umulhi(c.x, 0xD2511F53u);
+    const uint32_t b_lo = c.z * 0xCD9E8D57u;
+    const uint32_t b_hi = __umulhi(c.z, 0xCD9E8D57u);
+    c = make_uint4(b_hi ^ c.y ^ k0, b_lo, a_hi ^ c.w ^ k1, a_lo);
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+// Stream layout: the accept uniform of (b, j) is counter (0, j, b, 0), words
+// 0/1; the race uniform of token y at position j is counter (y>>1, j, b, 1),
+// words 0/1 for even y, 2/3 for odd y.
+__device__ __forceinline__ uint4 accept_block(uint32_t k0, uint32_t k1, uint32_t b, uint32_t j) {
+  return philox10(make_uint4(0u, j, b, 0u), k0, k1);
+}
+__device__ __forceinline__ uint4 race_block(uint32_t k0, uint32_t k1, uint32_t b, uint32_t j, uint32_t y) {
+  return philox10(make_uint4(y >> 1, j, b, 1u), k0, k1);
+}
+
+// (lo, hi) -> u = (top 53 bits + 1) * 2^-53 in (0, 1], exact in fp64.
+__device__ __forceinline__ double unit_from_words(uint32_t lo, uint32_t hi) {
+  const uint64_t k53 = ((((uint64_t)hi) << 32) | lo) >> 11;
+  return (double)(k53 + 1ull) * 0x1.0p-53;
+}
+
+// E = -ln(u) for the same u, to fp32 relative accuracy.  For u >= 1/2 the
+// gap t = 1 - u = (2^53 - 1 - k53) * 2^-53 is exact in integers and
+// E = -log1p(-t) keeps full relative precision as u -> 1 (where u itself,
+// rounded to fp32, would collapse to 1).  E = 0 only for u == 1.
+__device__ __forceinline__ float exp1_from_words(uint32_t lo, uint32_t hi) {
+  const uint64_t k53 = ((((uint64_t)hi) << 32) | lo) >> 11;
+  if (k53 >= (1ull << 52)) {
+    const uint64_t t = (1ull << 53) - 1ull - k53;
+    const float tf = (float)t * 0x1.0p-53f;
+    return -log1pf(-tf);
+  }
+  const float uf = (float)(k53 + 1ull) * 0x1.0p-53f;
+  return -logf(uf);
+}
+
+// ---------------------------------------------------------------------------
+// Order keys.  key(v, i) = ord32(v) << 32 | ~i: larger key <=> larger value,
+// then smaller index.  ord32 maps IEEE bits to an unsigned order with -0
+// folded onto +0 (they compare equal as values).  Key 0 is below every real
+// key (it would be a NaN pattern) and marks "no element".
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ord32(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t make_key(float v, uint32_t idx) {
+  return (((uint64_t)ord32(v)) << 32) | (uint64_t)(~idx);
+}
+__device__ __forceinline__ float key_value(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  const uint32_t b = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(b);
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t key) { return ~(uint32_t)key; }
+
+// ---------------------------------------------------------------------------
+// Logit unpacking from 16-byte vectors.
+// ---------------------------------------------------------------------------
+template <typename ET> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kPerVec = 4;
+  static constexpr uint32_t kNegInfWord = 0xFF800000u;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* out) {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ float load1(const float* p) { return *p; }
+};
+// bfloat16 held as raw 16-bit patterns: the value is the upper half of a
+// binary32, so widening is a shift.
+template <> struct Elem<uint16_t> {
+  static constexpr int kPerVec = 8;
+  static constexpr uint32_t kNegInfWord = 0xFF80FF80u;
+  __device__ static __forceinline__ void unpack(const uint4& v, float* out) {
+    out[0] = __uint_as_float(v.x << 16);
+    out[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    out[2] = __uint_as_float(v.y << 16);
+    out[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    out[4] = __uint_as_float(v.z << 16);
+    out[5] = __uint_as_float(v.z & 0xFFFF0000u);
+    out[6] = __uint_as_float(v.w << 16);
+    out[7] = __uint_as_float(v.w & 0xFFFF0000u);
+  }
+  __device__ static __forceinline__ float load1(const uint16_t* p) {
+    return __uint_as_float(((uint32_t)*p) << 16);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Wave helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+// Orders this wave's LDS accesses: everything before completes before
+// anything after is issued (LDS is processed in order per wave).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint64_t shfl_u64(uint64_t v, int src) {
+  const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src);
+  const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
+  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint64_t o = shfl_xor_u64(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_or_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v |= shfl_xor_u64(v, m);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_and_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v &= shfl_xor_u64(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// Online softmax pair (m = max logit, s = sum exp2((l - m) * c)) merge.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2, float c) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) {
+    m = M;
+    s = 0.f;
+    return;
+  }
+  s = s * __builtin_amdgcn_exp2f((m - M) * c) + s2 * __builtin_amdgcn_exp2f((m2 - M) * c);
+  m = M;
+}
+__device__ __forceinline__ void wave_lse(float& m, float& s, float c) {
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) {
+    const float m2 = __shfl_xor(m, k);
+    const float s2 = __shfl_xor(s, k);
+    lse_merge(m, s, m2, s2, c);
+  }
+}
+
+}  // namespace sv

@@ -1,0 +1,90 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol that
+include/specverify.h declares, sizes workspaces, and rejects bad arguments
+before touching the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import speculative_decoding_rejection_amd as sv
+    from speculative_decoding_rejection_amd import build as b
+    if b.is_stale():
+        b.build()
+    sv.load_library()
+    return sv
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_exports_every_declared_symbol(sv):
+    names = _declared_functions()
+    assert "spec_verify_prob" in names and "spec_verify_greedy" in names and "sv_workspace_bytes" in names
+    lib = sv.load_library()
+    for n in names:
+        assert hasattr(lib, n), f"symbol {n} declared in include/ but not exported"
+
+
+def test_workspace_sizing(sv):
+    p = sv.make_params(1024, 8, 256000, sv.SV_BF16, 0.7, 64, 42)
+    n = sv.sv_workspace_bytes(p)
+    # Candidates: 17408 rows x 64 keys x 8 bytes, plus small per-request state.
+    assert 17408 * 64 * 8 <= n < 17408 * 64 * 8 + 4 * 2**20
+    assert sv.sv_workspace_bytes(sv.make_params(0, 8, 100, sv.SV_F32)) == 0
+    assert sv.sv_workspace_bytes(sv.make_params(4, 2, 100, sv.SV_F32, 0.0)) > 0  # greedy parameters
+
+
+def _call_prob(sv, params, ws_bytes=1 << 20, null=None):
+    lib = sv.load_library()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    args = [fake] * 5
+    if null is not None:
+        args[null] = None
+    return lib.spec_verify_prob(ctypes.byref(params), args[0], args[1], args[2], args[3], args[4], None, None,
+                                fake, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1), (dict(gamma=0), 1), (dict(vocab=0), 1), (dict(dtype=7), 2),
+    (dict(temperature=0.0), 1), (dict(temperature=-1.0), 1), (dict(temperature=float("inf")), 1),
+    (dict(top_k=-1), 1), (dict(top_k=2000), 5),
+])
+def test_argument_errors(sv, kw, status):
+    base = dict(batch=4, gamma=3, vocab=5000, dtype=sv.SV_BF16, temperature=1.0, top_k=0, seed=1)
+    base.update(kw)
+    assert _call_prob(sv, sv.make_params(**base)) == status
+
+
+def test_null_pointers_and_workspace(sv):
+    p = sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 0, 1)
+    for i in range(5):
+        assert _call_prob(sv, p, null=i) == sv.SV_ERR_INVALID_ARG
+    assert _call_prob(sv, p, ws_bytes=16) == sv.SV_ERR_WORKSPACE
+    lib = sv.load_library()
+    assert lib.sv_read_device_error(None, None, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_kernel_timing_read(9, None, None) == sv.SV_ERR_INVALID_ARG
+
+
+def test_top_k_at_or_above_vocab_is_accepted(sv):
+    # top_k >= V is "off", never unsupported.
+    p = sv.make_params(4, 3, 500, sv.SV_BF16, 1.0, 5000, 1)
+    assert _call_prob(sv, p, ws_bytes=16) == sv.SV_ERR_WORKSPACE  # reaches the workspace check
+
+
+def test_status_strings(sv):
+    for s in range(6):
+        assert sv.sv_status_string(s)
