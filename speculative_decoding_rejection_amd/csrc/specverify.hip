@@ -161,7 +161,7 @@ sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrow
   uint64_t* cand = (uint64_t*)(ws + pl.off_cand);
   int* err = (int*)(ws + pl.off_err);
   if (pl.K <= 64) {
-    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 256, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
+    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 768, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
                        (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.K, cand, err);
   } else if (pl.K <= 256) {
     hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 1024, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,

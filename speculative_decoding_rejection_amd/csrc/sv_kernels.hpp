@@ -291,64 +291,148 @@ __device__ int wave_keep_ge(uint64_t* buf, int n, uint64_t thr) {
   return out;
 }
 
-template <int CAPW>
-struct TopkWave {
-  uint64_t* buf;
-  uint32_t* hist;
-  uint64_t* tau_shared;
-  uint64_t tau;   // insert keys > tau
-  float tau_v;    // value part of tau (-inf when tau is at or below -inf keys)
-  int cnt;
-  int K;
+// Key bounds from the value bits only, in one histogram pass: for rank r
+// (r = r1, r2) returns q such that at least r of the n keys are >= q (q keeps
+// the bits above the highest bit where the keys' values differ, the next 8
+// bits of the bucket holding the r-th largest, and zeros below); 0 when
+// n < r.
+__device__ uint2 wave_coarse_select2(const uint64_t* buf, int n, int r1, int r2, uint32_t* hist) {
+  const int lane = lane_id();
+  uint32_t orv = 0u, andv = ~0u;
+  for (int i = lane; i < n; i += kWave) {
+    const uint32_t h = (uint32_t)(buf[i] >> 32);
+    orv |= h;
+    andv &= h;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    orv |= (uint32_t)__shfl_xor((int)orv, m);
+    andv &= (uint32_t)__shfl_xor((int)andv, m);
+  }
+  const uint32_t var = orv ^ andv;
+  if (var == 0u) return make_uint2(n >= r1 ? andv : 0u, n >= r2 ? andv : 0u);
+  const int hb = 31 - __builtin_clz(var);
+  const int shift = hb >= 7 ? hb - 7 : 0;
+  const uint32_t high = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
+  for (int bkt = lane; bkt < 256; bkt += kWave) hist[bkt] = 0u;
+  wave_lds_sync();
+  for (int i = lane; i < n; i += kWave) atomicAdd(&hist[((uint32_t)(buf[i] >> 32) >> shift) & 255u], 1u);
+  wave_lds_sync();
+  const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
+  const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
+  const uint32_t lsum = h0 + h1 + h2 + h3;
+  uint32_t incl = lsum;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t t = (uint32_t)__shfl_down((int)incl, o);
+    if (lane + o < kWave) incl += t;
+  }
+  const uint32_t above = incl - lsum;
+  uint32_t res[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int r = t == 0 ? r1 : r2;
+    res[t] = 0u;
+    if (n < r) continue;  // wave-uniform
+    const uint32_t need = (uint32_t)r;
+    const bool mine = above < need && need <= incl;
+    int dl = 0;
+    if (mine) {
+      if (above + h3 >= need) dl = 3;
+      else if (above + h3 + h2 >= need) dl = 2;
+      else if (above + h3 + h2 + h1 >= need) dl = 1;
+    }
+    const uint64_t owner = ballot(mine);
+    const int d = __shfl(4 * lane + dl, (int)__builtin_ctzll(owner));
+    res[t] = (andv & high) | ((uint32_t)d << shift);
+  }
+  wave_lds_sync();
+  return make_uint2(res[0], res[1]);
+}
 
-  __device__ __forceinline__ void set_tau(uint64_t t) {
-    tau = t;
-    const uint32_t o = (uint32_t)(t >> 32);
-    tau_v = (o <= 0x007FFFFFu) ? -INFINITY : key_value(t);
-  }
-  __device__ __forceinline__ void refresh() {
-    const uint64_t ts = __hip_atomic_load(tau_shared, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (ts > tau) set_tau(ts);
-  }
-  // Reduces the buffer to its K largest keys (and drops keys below tau).
-  __device__ void compact() {
-    wave_lds_sync();
-    if (cnt > K) {
-      const uint64_t thr = wave_select_kth(buf, cnt, K, hist);
-      if (thr > tau) {
-        set_tau(thr);
-        if (lane_id() == 0) atomicMax((unsigned long long*)tau_shared, (unsigned long long)thr);
-      }
-    }
-    cnt = wave_keep_ge(buf, cnt, tau);
-  }
-  // Offers up to EPV elements per lane (slot k valid if bit k of vmask).
-  template <int EPV>
-  __device__ __forceinline__ void offer(const float* f, uint32_t idx0, uint32_t vmask) {
-    float vm = -INFINITY;
+// Lower bound of the row's K-th largest key from what the waves published:
+// every wave w retains >= ceil(K/NW) keys >= q[w], so >= K keys are >= min_w
+// q[w]; the publisher of kth retains K keys >= kth.
+template <int NW>
+__device__ __forceinline__ uint64_t shared_bound(uint64_t* q_sh, uint64_t* kth_sh) {
+  uint64_t mn = ~0ull;
 #pragma unroll
-    for (int k = 0; k < EPV; ++k)
-      if (vmask & (1u << k)) vm = fmaxf(vm, f[k]);
-    const bool maybe = vmask != 0u && vm >= tau_v;
-    if (ballot(maybe) == 0ull) return;
-#pragma unroll
-    for (int k = 0; k < EPV; ++k) {
-      const uint64_t key = (vmask & (1u << k)) ? make_key(f[k], idx0 + (uint32_t)k) : 0ull;
-      bool hit = key > tau;
-      uint64_t m = ballot(hit);
-      if (m == 0ull) continue;
-      int nh = __builtin_popcountll(m);
-      if (cnt + nh > CAPW) {
-        compact();
-        hit = key > tau;
-        m = ballot(hit);
-        nh = __builtin_popcountll(m);
-      }
-      if (hit) buf[cnt + lanes_below(m)] = key;
-      cnt += nh;
+  for (int w = 0; w < NW; ++w) {
+    const uint64_t q = __hip_atomic_load(q_sh + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    mn = q < mn ? q : mn;
+  }
+  const uint64_t k = __hip_atomic_load(kth_sh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return k > mn ? k : mn;
+}
+
+// Shrinks one wave's candidate buffer and returns the wave's new threshold
+// (insert keys > tau).  Publishes a coarse ceil(K/NW)-th bound; if the buffer
+// is still above `guard` keys (or `exact` is set and it holds more than K),
+// the exact K-th largest is selected and published too.  Only keys below a
+// valid bound are ever dropped.
+template <int NW>
+__device__ __noinline__ uint64_t topk_compact(uint64_t* bw, uint32_t* hw, uint32_t* cntp, uint64_t* q_sh,
+                                              uint64_t* kth_sh, int w, uint64_t tau, int K, int guard,
+                                              bool exact) {
+  const int lane = lane_id();
+  const int K4 = (K + NW - 1) / NW;
+  wave_lds_sync();
+  int n = __builtin_amdgcn_readfirstlane(*cntp);
+  if (!exact && n >= K4) {
+    const uint2 q = wave_coarse_select2(bw, n, K4, K, hw);
+    if (lane == 0) {
+      atomicMax((unsigned long long*)(q_sh + w), (unsigned long long)q.x << 32);
+      if (q.y) atomicMax((unsigned long long*)kth_sh, (unsigned long long)q.y << 32);
     }
   }
-};
+  const uint64_t sb = shared_bound<NW>(q_sh, kth_sh);
+  tau = sb > tau ? sb : tau;
+  n = wave_keep_ge(bw, n, tau);
+  if (n > guard || (exact && n > K)) {
+    const uint64_t kth = wave_select_kth(bw, n, K, hw);
+    if (lane == 0) atomicMax((unsigned long long*)kth_sh, (unsigned long long)kth);
+    tau = kth > tau ? kth : tau;
+    n = wave_keep_ge(bw, n, tau);
+  }
+  if (lane == 0) *cntp = (uint32_t)n;
+  wave_lds_sync();
+  return tau;
+}
+
+// Float value below which no key can beat tau (-inf for keys at or below
+// the -inf keys).
+__device__ __forceinline__ float tau_value(uint64_t tau) {
+  const uint32_t o = (uint32_t)(tau >> 32);
+  return (o <= 0x007FFFFFu) ? -INFINITY : key_value(tau);
+}
+
+// Appends this lane's elements with key > tau to the wave buffer.
+template <int EPV>
+__device__ __forceinline__ void topk_append(const float* f, uint32_t idx0, uint32_t vmask, uint64_t tau, float tau_v,
+                                            uint64_t* bw, uint32_t* cntp) {
+#pragma unroll
+  for (int k = 0; k < EPV; ++k) {
+    if ((vmask & (1u << k)) && f[k] >= tau_v) {
+      const uint64_t key = make_key(f[k], idx0 + (uint32_t)k);
+      if (key > tau) {
+        const uint32_t pos = atomicAdd(cntp, 1u);
+        bw[pos] = key;
+      }
+    }
+  }
+}
+
+// Prefilter for bf16 vectors against a positive threshold: for positive
+// values the bf16 bit pattern orders like a signed 16-bit integer, and every
+// negative pattern is below every positive one.
+__device__ __forceinline__ bool bf16_vec_reaches(const uint4& v, short thr16) {
+  typedef short s2 __attribute__((ext_vector_type(2)));
+  const s2 a = __builtin_bit_cast(s2, v.x), b = __builtin_bit_cast(s2, v.y);
+  const s2 c = __builtin_bit_cast(s2, v.z), d = __builtin_bit_cast(s2, v.w);
+  const s2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  const short mm = m.x > m.y ? m.x : m.y;
+  return mm >= thr16;
+}
 
 template <typename ET, int CAPW, int U>
 __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
@@ -356,31 +440,43 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
                                                         int* __restrict__ err) {
   constexpr int NT = 256, NW = NT / kWave;
   constexpr int EPV = Elem<ET>::kPerVec;
+  constexpr int kGuard = CAPW - kWave * EPV;  // room for one more step's keys
   __shared__ uint64_t buf[NW][CAPW];
   __shared__ uint32_t hist[NW][256];
-  __shared__ uint64_t tau_shared;
-  __shared__ int counts[NW];
+  __shared__ uint64_t q_sh[NW];
+  __shared__ uint64_t kth_sh;
+  __shared__ uint32_t cnt_sh[NW];
   const int row = blockIdx.x;
   const int tid = threadIdx.x, w = tid / kWave;
   if (row == 0 && tid == 0) *err = 0;
-  if (tid == 0) tau_shared = 0ull;
+  if (tid < NW) {
+    q_sh[tid] = 0ull;
+    cnt_sh[tid] = 0u;
+  }
+  if (tid == 0) kth_sh = 0ull;
   __syncthreads();
   const ET* rp = row < rows_t ? lt + (size_t)row * V : ld + (size_t)(row - rows_t) * V;
   Slice<ET> sl(rp, 0, V);
-  TopkWave<CAPW> st{buf[w], hist[w], &tau_shared, 0ull, -INFINITY, 0, K};
+  uint64_t* bw = buf[w];
+  uint32_t* hw = hist[w];
+  uint32_t* cntp = &cnt_sh[w];
+  const int K4 = (K + NW - 1) / NW;
+  int trig = K4 + 32;
+  uint64_t tau = 0ull;
+  float tau_v = -INFINITY;
 
-  // Scalar head and tail (fewer than 2 * EPV elements): one slot per thread.
+  // Scalar head and tail (fewer than 2 * EPV elements): one per thread.
   {
     float f[EPV];
-    uint32_t idx = 0, vm = 0u;
 #pragma unroll
     for (int k = 0; k < EPV; ++k) f[k] = -INFINITY;
+    uint32_t idx = 0, vm = 0u;
     if (tid < sl.nscalar()) {
       idx = (uint32_t)sl.scalar_index(tid);
       f[0] = Elem<ET>::load1(rp + idx);
       vm = 1u;
     }
-    st.template offer<EPV>(f, idx, vm);
+    topk_append<EPV>(f, idx, vm, tau, tau_v, bw, cntp);
   }
   const uint4* vp = sl.vecs();
   const uint32_t full = (1u << EPV) - 1u;
@@ -391,37 +487,88 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
       const int i = i0 + u * NT + tid;
       v[u] = i < sl.nvec ? vp[i] : make_uint4(0u, 0u, 0u, 0u);
     }
-    st.refresh();
+    if (i0 == 0 && K <= kWave) {
+      // Every lane's largest element of the first batch beats the minimum of
+      // those maxima: 64 keys >= it, enough for K <= 64.
+      float lm = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (i0 + u * NT + tid < sl.nvec) {
+          float f[EPV];
+          Elem<ET>::unpack(v[u], f);
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) lm = fmaxf(lm, f[k]);
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) lm = fminf(lm, __shfl_xor(lm, m));
+      const uint64_t t0 = (((uint64_t)ord32(lm)) << 32) - 1ull;
+      if (t0 > tau) tau = t0;
+    }
+    {
+      const uint64_t sb = shared_bound<NW>(q_sh, &kth_sh);
+      if (sb > tau) tau = sb;
+      tau_v = tau_value(tau);
+    }
+    const bool packed = sizeof(ET) == 2 && tau_v > 0.f;
+    const short thr16 = (short)(__float_as_uint(tau_v) >> 16);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * NT + tid;
+      const bool valid = i < sl.nvec;
       float f[EPV];
       Elem<ET>::unpack(v[u], f);
-      st.template offer<EPV>(f, (uint32_t)sl.vec_index0(i), i < sl.nvec ? full : 0u);
+      bool maybe;
+      if (packed) {
+        maybe = valid && bf16_vec_reaches(v[u], thr16);
+      } else {
+        float vm = f[0];
+#pragma unroll
+        for (int k = 1; k < EPV; ++k) vm = fmaxf(vm, f[k]);
+        maybe = valid && vm >= tau_v;
+      }
+      if (ballot(maybe) == 0ull) continue;
+      if ((int)__builtin_amdgcn_readfirstlane(*cntp) > kGuard) {
+        tau = topk_compact<NW>(bw, hw, cntp, q_sh, &kth_sh, w, tau, K, kGuard, false);
+        tau_v = tau_value(tau);
+      }
+      topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cntp);
+      wave_lds_sync();
+      if ((int)__builtin_amdgcn_readfirstlane(*cntp) > trig) {
+        tau = topk_compact<NW>(bw, hw, cntp, q_sh, &kth_sh, w, tau, K, kGuard, false);
+        tau_v = tau_value(tau);
+        // Next compaction once 32 more keys arrived (or the buffer is above
+        // the first trigger again).
+        const int after = (int)__builtin_amdgcn_readfirstlane(*cntp);
+        trig = max(K4 + 32, after + 32);
+      }
     }
   }
   // Each wave reduces to at most K keys, then wave 0 merges the four.
-  st.refresh();
-  st.compact();
-  if (lane_id() == 0) counts[w] = st.cnt;
+  tau = topk_compact<NW>(bw, hw, cntp, q_sh, &kth_sh, w, tau, K, kGuard, true);
+  __syncthreads();
+  // A wave that compacted early may hold keys below the final bound: they
+  // are dropped here (valid: the bound has K retained keys at or above it).
+  const uint64_t fin = shared_bound<NW>(q_sh, &kth_sh);
+  int mine = wave_keep_ge(bw, (int)cnt_sh[w], fin > tau ? fin : tau);
+  __syncthreads();
+  if (lane_id() == 0) cnt_sh[w] = (uint32_t)mine;
   __syncthreads();
   if (w > 0) {
     int off = 0;
-    for (int k = 0; k < w; ++k) off += counts[k];
-    for (int i = lane_id(); i < st.cnt; i += kWave) buf[0][off + i] = st.buf[i];
+    for (int k = 0; k < w; ++k) off += (int)cnt_sh[k];
+    for (int i = lane_id(); i < mine; i += kWave) buf[0][off + i] = bw[i];
   }
   __syncthreads();
   if (w == 0) {
     int n = 0;
-    for (int k = 0; k < NW; ++k) n += counts[k];
-    st.cnt = n;
-    st.tau = 0ull;  // select among all merged keys
+    for (int k = 0; k < NW; ++k) n += (int)cnt_sh[k];
     if (n > K) {
-      const uint64_t thr = wave_select_kth(st.buf, n, K, st.hist);
-      n = wave_keep_ge(st.buf, n, thr);
+      const uint64_t thr = wave_select_kth(buf[0], n, K, hist[0]);
+      n = wave_keep_ge(buf[0], n, thr);
     }
     uint64_t* dst = cand + (size_t)row * K;
-    for (int i = lane_id(); i < K; i += kWave) dst[i] = i < n ? st.buf[i] : 0ull;
+    for (int i = lane_id(); i < K; i += kWave) dst[i] = i < n ? buf[0][i] : 0ull;
   }
 }
 
