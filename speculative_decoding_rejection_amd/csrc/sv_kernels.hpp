@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * NT;
-      v[u] = i < sl.nvec ? vp[i] : ninf;
+      v[u] = i < sl.nvec ? load_stream(vp + i) : ninf;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NT) void rows_argmax_kernel(const ET* __restrict__ 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * NT;
-      v[u] = i < sl.nvec ? vp[i] : make_uint4(0u, 0u, 0u, 0u);
+      v[u] = i < sl.nvec ? load_stream(vp + i) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u * NT + tid;
-      v[u] = i < sl.nvec ? vp[i] : make_uint4(0u, 0u, 0u, 0u);
+      v[u] = i < sl.nvec ? load_stream(vp + i) : make_uint4(0u, 0u, 0u, 0u);
     }
     if (i0 == 0 && K <= kWave) {
       // Every lane's largest element of the first batch beats the minimum of
@@ -831,10 +831,10 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   const uint4* vq = q_vec ? (const uint4*)(rq + a + sl.head) : nullptr;
   for (int i = tid; i < sl.nvec; i += NT) {
     float fp[EPV], fq[EPV];
-    Elem<ET>::unpack(vp[i], fp);
+    Elem<ET>::unpack(load_stream(vp + i), fp);
     const int y0 = sl.vec_index0(i);
     if (q_vec) {
-      Elem<ET>::unpack(vq[i], fq);
+      Elem<ET>::unpack(load_stream(vq + i), fq);
     } else {
 #pragma unroll
       for (int k = 0; k < EPV; ++k) fq[k] = rq ? Elem<ET>::load1(rq + y0 + k) : 0.f;
