@@ -20,7 +20,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+# SPECVERIFY_LIB may point at another build of the library (measurement of
+# build variants); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED = range(6)
 SV_F32, SV_BF16 = 0, 1

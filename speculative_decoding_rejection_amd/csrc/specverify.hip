@@ -16,7 +16,10 @@ using sv::RaceDesc;
 
 constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 4;
-constexpr int kTopkUnroll = 4;
+#ifndef SV_TOPK_UNROLL
+#define SV_TOPK_UNROLL 4
+#endif
+constexpr int kTopkUnroll = SV_TOPK_UNROLL;
 constexpr int kMaxTopK = 1024;
 constexpr size_t kWsAlign = 256;
 constexpr int kEntryProb = 0, kEntryOnehot = 1, kEntryGreedy = 2;
@@ -155,20 +158,34 @@ sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int n
   return check_launch();
 }
 
+#ifndef SV_TOPK_CAPW64
+#define SV_TOPK_CAPW64 768  // per-wave key buffer for k <= 64
+#endif
+#ifndef SV_TOPK_WPR
+#define SV_TOPK_WPR 2  // waves per row in the top-k row pass
+#endif
+
+template <typename ET, int CAPW>
+void launch_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, uint64_t* cand, int* err,
+                      hipStream_t st) {
+  constexpr int RPB = 4 / SV_TOPK_WPR;
+  hipLaunchKernelGGL((sv::rows_topk_kernel<ET, CAPW, kTopkUnroll, SV_TOPK_WPR>), dim3((nrows + RPB - 1) / RPB),
+                     dim3(256), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, nrows, pl.V, pl.K, cand, err);
+}
+
 template <typename ET>
 sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st) {
   TimedLaunch t(0, st);
   uint64_t* cand = (uint64_t*)(ws + pl.off_cand);
   int* err = (int*)(ws + pl.off_err);
+  // Buffer capacity per wave: >= K + 64 * (elements per vector) for one
+  // vector step after a compaction, and >= WPR * K for the final merge.
   if (pl.K <= 64) {
-    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 768, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
-                       (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.K, cand, err);
+    launch_rows_topk<ET, SV_TOPK_CAPW64>(pl, lt, ld, nrows, cand, err, st);
   } else if (pl.K <= 256) {
-    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 1024, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
-                       (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.K, cand, err);
+    launch_rows_topk<ET, 1024>(pl, lt, ld, nrows, cand, err, st);
   } else {
-    hipLaunchKernelGGL((sv::rows_topk_kernel<ET, 4096, kTopkUnroll>), dim3(nrows), dim3(256), 0, st,
-                       (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.K, cand, err);
+    launch_rows_topk<ET, 4096>(pl, lt, ld, nrows, cand, err, st);
   }
   t.done();
   return check_launch();

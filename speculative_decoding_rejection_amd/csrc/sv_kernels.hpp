@@ -394,10 +394,18 @@ __device__ __noinline__ uint64_t topk_compact(uint64_t* bw, uint32_t* hw, uint32
     tau = kth > tau ? kth : tau;
     n = wave_keep_ge(bw, n, tau);
   }
-  if (lane == 0) *cntp = (uint32_t)n;
+  // The combined bound goes to one word that the streaming loop reads.
+  if (lane == 0) {
+    *cntp = (uint32_t)n;
+    atomicMax((unsigned long long*)(kth_sh + 1), (unsigned long long)tau);
+  }
   wave_lds_sync();
   return tau;
 }
+
+#ifndef SV_TOPK_TRIG_STEP
+#define SV_TOPK_TRIG_STEP 32  // keys added between two compactions of a wave buffer
+#endif
 
 // Float value below which no key can beat tau (-inf for keys at or below
 // the -inf keys).
@@ -434,34 +442,45 @@ __device__ __forceinline__ bool bf16_vec_reaches(const uint4& v, short thr16) {
   return mm >= thr16;
 }
 
-template <typename ET, int CAPW, int U>
+// WPR waves share one row (4 / WPR rows per 256-thread workgroup).  Fewer
+// waves per row track the row's running k-th key more tightly (fewer keys
+// pass the filter); more waves per row shorten each row's latency.
+template <typename ET, int CAPW, int U, int WPR>
 __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
-                                                        int rows_t, int V, int K, uint64_t* __restrict__ cand,
-                                                        int* __restrict__ err) {
+                                                        int rows_t, int nrows, int V, int K,
+                                                        uint64_t* __restrict__ cand, int* __restrict__ err) {
   constexpr int NT = 256, NW = NT / kWave;
+  constexpr int RPB = NW / WPR;     // rows per workgroup
+  constexpr int GT = WPR * kWave;   // threads per row
   constexpr int EPV = Elem<ET>::kPerVec;
   constexpr int kGuard = CAPW - kWave * EPV;  // room for one more step's keys
   __shared__ uint64_t buf[NW][CAPW];
   __shared__ uint32_t hist[NW][256];
   __shared__ uint64_t q_sh[NW];
-  __shared__ uint64_t kth_sh;
+  __shared__ uint64_t kth_sh[RPB][2];  // per row: best k-th bound; best combined bound
   __shared__ uint32_t cnt_sh[NW];
-  const int row = blockIdx.x;
+  __shared__ uint32_t lm_sh[RPB][WPR * kWave];
   const int tid = threadIdx.x, w = tid / kWave;
-  if (row == 0 && tid == 0) *err = 0;
+  const int g = w / WPR, wg = w % WPR, gtid = tid % GT;
+  const int row = blockIdx.x * RPB + g;
+  const bool row_ok = row < nrows;
+  if (blockIdx.x == 0 && tid == 0) *err = 0;
   if (tid < NW) {
     q_sh[tid] = 0ull;
     cnt_sh[tid] = 0u;
   }
-  if (tid == 0) kth_sh = 0ull;
+  if (tid < 2 * RPB) kth_sh[tid / 2][tid % 2] = 0ull;
   __syncthreads();
-  const ET* rp = row < rows_t ? lt + (size_t)row * V : ld + (size_t)(row - rows_t) * V;
-  Slice<ET> sl(rp, 0, V);
+  const int rr = row_ok ? row : 0;
+  const ET* rp = rr < rows_t ? lt + (size_t)rr * V : ld + (size_t)(rr - rows_t) * V;
+  Slice<ET> sl(rp, 0, row_ok ? V : 0);
   uint64_t* bw = buf[w];
   uint32_t* hw = hist[w];
   uint32_t* cntp = &cnt_sh[w];
-  const int K4 = (K + NW - 1) / NW;
-  int trig = K4 + 32;
+  uint64_t* qg = q_sh + g * WPR;
+  uint64_t* kg = kth_sh[g];
+  const int K4 = (K + WPR - 1) / WPR;
+  int trig = K4 + SV_TOPK_TRIG_STEP;
   uint64_t tau = 0ull;
   float tau_v = -INFINITY;
 
@@ -471,8 +490,8 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
 #pragma unroll
     for (int k = 0; k < EPV; ++k) f[k] = -INFINITY;
     uint32_t idx = 0, vm = 0u;
-    if (tid < sl.nscalar()) {
-      idx = (uint32_t)sl.scalar_index(tid);
+    if (gtid < sl.nscalar()) {
+      idx = (uint32_t)sl.scalar_index(gtid);
       f[0] = Elem<ET>::load1(rp + idx);
       vm = 1u;
     }
@@ -480,95 +499,129 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
   }
   const uint4* vp = sl.vecs();
   const uint32_t full = (1u << EPV) - 1u;
-  for (int i0 = 0; i0 < sl.nvec; i0 += NT * U) {
-    uint4 v[U];
+
+  // Filters one vector of this lane: appends its keys > tau, compacts when
+  // the wave buffer passes the trigger.  Called with wave-uniform control.
+  auto filter = [&](const uint4& vv, int i, bool packed, short thr16) {
+    const bool valid = i < sl.nvec;
+    float f[EPV];
+    Elem<ET>::unpack(vv, f);
+    bool maybe;
+    if (packed) {
+      maybe = valid && bf16_vec_reaches(vv, thr16);
+    } else {
+      float vm = f[0];
+#pragma unroll
+      for (int k = 1; k < EPV; ++k) vm = fmaxf(vm, f[k]);
+      maybe = valid && vm >= tau_v;
+    }
+    if (ballot(maybe) == 0ull) return;
+    if ((int)__builtin_amdgcn_readfirstlane(*cntp) > kGuard) {
+      tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
+      tau_v = tau_value(tau);
+    }
+    topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cntp);
+    wave_lds_sync();
+    if ((int)__builtin_amdgcn_readfirstlane(*cntp) > trig) {
+      tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
+      tau_v = tau_value(tau);
+      // Next compaction once SV_TOPK_TRIG_STEP more keys arrived.
+      const int after = (int)__builtin_amdgcn_readfirstlane(*cntp);
+      trig = max(K4 + SV_TOPK_TRIG_STEP, after + SV_TOPK_TRIG_STEP);
+    }
+  };
+
+  // Warm start.  Every lane's largest element of the row's first batch is a
+  // distinct element, so the K-th largest of those WPR * 64 maxima has at
+  // least K elements at or above it: a valid threshold from the start, far
+  // above what one wave's first batch alone would give.
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = u * GT + gtid;
+    v[u] = sl.nvec > 0 ? load_stream(vp + (i < sl.nvec ? i : sl.nvec - 1)) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  {
+    float lm = -INFINITY;
+    bool has = false;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * NT + tid;
-      v[u] = i < sl.nvec ? load_stream(vp + i) : make_uint4(0u, 0u, 0u, 0u);
-    }
-    if (i0 == 0 && K <= kWave) {
-      // Every lane's largest element of the first batch beats the minimum of
-      // those maxima: 64 keys >= it, enough for K <= 64.
-      float lm = -INFINITY;
+      if (u * GT + gtid < sl.nvec) {
+        float f[EPV];
+        Elem<ET>::unpack(v[u], f);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (i0 + u * NT + tid < sl.nvec) {
-          float f[EPV];
-          Elem<ET>::unpack(v[u], f);
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) lm = fmaxf(lm, f[k]);
-        }
+        for (int k = 0; k < EPV; ++k) lm = fmaxf(lm, f[k]);
+        has = true;
       }
+    }
+    lm_sh[g][wg * kWave + lane_id()] = has ? ord32(lm) : 0u;
+    __syncthreads();
+    if (K <= WPR * kWave) {
+      uint32_t mine[WPR];
 #pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) lm = fminf(lm, __shfl_xor(lm, m));
-      const uint64_t t0 = (((uint64_t)ord32(lm)) << 32) - 1ull;
-      if (t0 > tau) tau = t0;
+      for (int r = 0; r < WPR; ++r) mine[r] = lm_sh[g][r * kWave + lane_id()];
+      // Largest t with at least K maxima >= t, i.e. the K-th largest.
+      uint32_t t = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t c = t | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int r = 0; r < WPR; ++r) cnt += __builtin_popcountll(ballot(mine[r] >= c));
+        if (cnt >= K) t = c;
+      }
+      if (t != 0u) {
+        const uint64_t t0 = ((uint64_t)t << 32) - 1ull;
+        if (t0 > tau) tau = t0;
+      }
+    }
+    tau_v = tau_value(tau);
+    const bool packed = sizeof(ET) == 2 && tau_v > 0.f;
+    const short thr16 = (short)(__float_as_uint(tau_v) >> 16);
+#pragma unroll
+    for (int u = 0; u < U; ++u) filter(v[u], u * GT + gtid, packed, thr16);
+  }
+  for (int i0 = GT * U; i0 < sl.nvec; i0 += GT * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * GT + gtid;
+      v[u] = load_stream(vp + (i < sl.nvec ? i : sl.nvec - 1));  // in range; masked below
     }
     {
-      const uint64_t sb = shared_bound<NW>(q_sh, &kth_sh);
+      const uint64_t sb = __hip_atomic_load(kg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (sb > tau) tau = sb;
       tau_v = tau_value(tau);
     }
     const bool packed = sizeof(ET) == 2 && tau_v > 0.f;
     const short thr16 = (short)(__float_as_uint(tau_v) >> 16);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * NT + tid;
-      const bool valid = i < sl.nvec;
-      float f[EPV];
-      Elem<ET>::unpack(v[u], f);
-      bool maybe;
-      if (packed) {
-        maybe = valid && bf16_vec_reaches(v[u], thr16);
-      } else {
-        float vm = f[0];
-#pragma unroll
-        for (int k = 1; k < EPV; ++k) vm = fmaxf(vm, f[k]);
-        maybe = valid && vm >= tau_v;
-      }
-      if (ballot(maybe) == 0ull) continue;
-      if ((int)__builtin_amdgcn_readfirstlane(*cntp) > kGuard) {
-        tau = topk_compact<NW>(bw, hw, cntp, q_sh, &kth_sh, w, tau, K, kGuard, false);
-        tau_v = tau_value(tau);
-      }
-      topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cntp);
-      wave_lds_sync();
-      if ((int)__builtin_amdgcn_readfirstlane(*cntp) > trig) {
-        tau = topk_compact<NW>(bw, hw, cntp, q_sh, &kth_sh, w, tau, K, kGuard, false);
-        tau_v = tau_value(tau);
-        // Next compaction once 32 more keys arrived (or the buffer is above
-        // the first trigger again).
-        const int after = (int)__builtin_amdgcn_readfirstlane(*cntp);
-        trig = max(K4 + 32, after + 32);
-      }
-    }
+    for (int u = 0; u < U; ++u) filter(v[u], i0 + u * GT + gtid, packed, thr16);
   }
-  // Each wave reduces to at most K keys, then wave 0 merges the four.
-  tau = topk_compact<NW>(bw, hw, cntp, q_sh, &kth_sh, w, tau, K, kGuard, true);
+  // Each wave reduces to at most K keys, then the row's first wave merges.
+  tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, true);
   __syncthreads();
   // A wave that compacted early may hold keys below the final bound: they
   // are dropped here (valid: the bound has K retained keys at or above it).
-  const uint64_t fin = shared_bound<NW>(q_sh, &kth_sh);
+  const uint64_t fin = shared_bound<WPR>(qg, kg);
   int mine = wave_keep_ge(bw, (int)cnt_sh[w], fin > tau ? fin : tau);
   __syncthreads();
   if (lane_id() == 0) cnt_sh[w] = (uint32_t)mine;
   __syncthreads();
-  if (w > 0) {
+  uint64_t* b0 = buf[g * WPR];
+  if (wg > 0) {
     int off = 0;
-    for (int k = 0; k < w; ++k) off += (int)cnt_sh[k];
-    for (int i = lane_id(); i < mine; i += kWave) buf[0][off + i] = bw[i];
+    for (int k = 0; k < wg; ++k) off += (int)cnt_sh[g * WPR + k];
+    for (int i = lane_id(); i < mine; i += kWave) b0[off + i] = bw[i];
   }
   __syncthreads();
-  if (w == 0) {
+  if (wg == 0 && row_ok) {
     int n = 0;
-    for (int k = 0; k < NW; ++k) n += (int)cnt_sh[k];
+    for (int k = 0; k < WPR; ++k) n += (int)cnt_sh[g * WPR + k];
     if (n > K) {
-      const uint64_t thr = wave_select_kth(buf[0], n, K, hist[0]);
-      n = wave_keep_ge(buf[0], n, thr);
+      const uint64_t thr = wave_select_kth(b0, n, K, hw);
+      n = wave_keep_ge(b0, n, thr);
     }
     uint64_t* dst = cand + (size_t)row * K;
-    for (int i = lane_id(); i < K; i += kWave) dst[i] = i < n ? buf[0][i] : 0ull;
+    for (int i = lane_id(); i < K; i += kWave) dst[i] = i < n ? b0[i] : 0ull;
   }
 }
 
