@@ -24,6 +24,15 @@
 
 #include "sv_device.hpp"
 
+// Build knobs of the top-k row pass (measured defaults).
+#ifndef SV_TOPK_PIPE
+#define SV_TOPK_PIPE 1  // 0: load a batch then filter it; 1: refill each slot after it is filtered;
+                        // 2: load the next batch before filtering this one
+#endif
+#ifndef SV_TOPK_COMPACT_INLINE
+#define SV_TOPK_COMPACT_INLINE __noinline__  // rare; kept out of the streaming loop's code
+#endif
+
 namespace sv {
 
 // Error word bits.
@@ -371,7 +380,7 @@ __device__ __forceinline__ uint64_t shared_bound(uint64_t* q_sh, uint64_t* kth_s
 // the exact K-th largest is selected and published too.  Only keys below a
 // valid bound are ever dropped.
 template <int NW>
-__device__ __noinline__ uint64_t topk_compact(uint64_t* bw, uint32_t* hw, uint32_t* cntp, uint64_t* q_sh,
+__device__ SV_TOPK_COMPACT_INLINE uint64_t topk_compact(uint64_t* bw, uint32_t* hw, uint32_t* cntp, uint64_t* q_sh,
                                               uint64_t* kth_sh, int w, uint64_t tau, int K, int guard,
                                               bool exact) {
   const int lane = lane_id();
@@ -414,20 +423,22 @@ __device__ __forceinline__ float tau_value(uint64_t tau) {
   return (o <= 0x007FFFFFu) ? -INFINITY : key_value(tau);
 }
 
-// Appends this lane's elements with key > tau to the wave buffer.
+// Appends this lane's elements with key > tau to the wave buffer at
+// positions from a ballot prefix count; returns the new (wave-uniform) count.
 template <int EPV>
-__device__ __forceinline__ void topk_append(const float* f, uint32_t idx0, uint32_t vmask, uint64_t tau, float tau_v,
-                                            uint64_t* bw, uint32_t* cntp) {
+__device__ __forceinline__ int topk_append(const float* f, uint32_t idx0, uint32_t vmask, uint64_t tau, float tau_v,
+                                           uint64_t* bw, int cnt) {
 #pragma unroll
   for (int k = 0; k < EPV; ++k) {
-    if ((vmask & (1u << k)) && f[k] >= tau_v) {
-      const uint64_t key = make_key(f[k], idx0 + (uint32_t)k);
-      if (key > tau) {
-        const uint32_t pos = atomicAdd(cntp, 1u);
-        bw[pos] = key;
-      }
-    }
+    const bool cand = (vmask & (1u << k)) && f[k] >= tau_v;
+    if (ballot(cand) == 0ull) continue;
+    const uint64_t key = cand ? make_key(f[k], idx0 + (uint32_t)k) : 0ull;
+    const bool hit = key > tau;
+    const uint64_t m = ballot(hit);
+    if (hit) bw[cnt + lanes_below(m)] = key;
+    cnt += __builtin_popcountll(m);
   }
+  return cnt;
 }
 
 // Prefilter for bf16 vectors against a positive threshold: for positive
@@ -483,6 +494,7 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
   int trig = K4 + SV_TOPK_TRIG_STEP;
   uint64_t tau = 0ull;
   float tau_v = -INFINITY;
+  int cnt = 0;  // keys in this wave's buffer (wave-uniform; in LDS only around compactions)
 
   // Scalar head and tail (fewer than 2 * EPV elements): one per thread.
   {
@@ -495,7 +507,7 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
       f[0] = Elem<ET>::load1(rp + idx);
       vm = 1u;
     }
-    topk_append<EPV>(f, idx, vm, tau, tau_v, bw, cntp);
+    cnt = topk_append<EPV>(f, idx, vm, tau, tau_v, bw, cnt);
   }
   const uint4* vp = sl.vecs();
   const uint32_t full = (1u << EPV) - 1u;
@@ -516,18 +528,20 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
       maybe = valid && vm >= tau_v;
     }
     if (ballot(maybe) == 0ull) return;
-    if ((int)__builtin_amdgcn_readfirstlane(*cntp) > kGuard) {
+    if (cnt > kGuard) {
+      if (lane_id() == 0) *cntp = (uint32_t)cnt;
       tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
       tau_v = tau_value(tau);
+      cnt = (int)__builtin_amdgcn_readfirstlane(*cntp);
     }
-    topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cntp);
-    wave_lds_sync();
-    if ((int)__builtin_amdgcn_readfirstlane(*cntp) > trig) {
+    cnt = topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cnt);
+    if (cnt > trig) {
+      if (lane_id() == 0) *cntp = (uint32_t)cnt;
       tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
       tau_v = tau_value(tau);
+      cnt = (int)__builtin_amdgcn_readfirstlane(*cntp);
       // Next compaction once SV_TOPK_TRIG_STEP more keys arrived.
-      const int after = (int)__builtin_amdgcn_readfirstlane(*cntp);
-      trig = max(K4 + SV_TOPK_TRIG_STEP, after + SV_TOPK_TRIG_STEP);
+      trig = max(K4 + SV_TOPK_TRIG_STEP, cnt + SV_TOPK_TRIG_STEP);
     }
   };
 
@@ -577,15 +591,32 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
     tau_v = tau_value(tau);
     const bool packed = sizeof(ET) == 2 && tau_v > 0.f;
     const short thr16 = (short)(__float_as_uint(tau_v) >> 16);
-#pragma unroll
-    for (int u = 0; u < U; ++u) filter(v[u], u * GT + gtid, packed, thr16);
-  }
-  for (int i0 = GT * U; i0 < sl.nvec; i0 += GT * U) {
+    // Rolling pipeline: once a slot is filtered its register is refilled
+    // with the slot's next vector, so U - 1 loads per lane stay in flight and
+    // no register is moved (a move would wait for every pending load).
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * GT + gtid;
-      v[u] = load_stream(vp + (i < sl.nvec ? i : sl.nvec - 1));  // in range; masked below
+      filter(v[u], u * GT + gtid, packed, thr16);
+#if SV_TOPK_PIPE == 1
+      if (sl.nvec > 0) v[u] = load_stream(vp + min(GT * U + u * GT + gtid, sl.nvec - 1));
+#endif
     }
+  }
+#if SV_TOPK_PIPE == 2
+  if (sl.nvec > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load_stream(vp + min(GT * U + u * GT + gtid, sl.nvec - 1));
+  }
+#endif
+  for (int i0 = GT * U; i0 < sl.nvec; i0 += GT * U) {
+#if SV_TOPK_PIPE == 0
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = load_stream(vp + min(i0 + u * GT + gtid, sl.nvec - 1));
+#elif SV_TOPK_PIPE == 2
+    uint4 nxt[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) nxt[u] = load_stream(vp + min(i0 + GT * U + u * GT + gtid, sl.nvec - 1));
+#endif
     {
       const uint64_t sb = __hip_atomic_load(kg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (sb > tau) tau = sb;
@@ -594,9 +625,18 @@ __global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ l
     const bool packed = sizeof(ET) == 2 && tau_v > 0.f;
     const short thr16 = (short)(__float_as_uint(tau_v) >> 16);
 #pragma unroll
-    for (int u = 0; u < U; ++u) filter(v[u], i0 + u * GT + gtid, packed, thr16);
+    for (int u = 0; u < U; ++u) {
+      filter(v[u], i0 + u * GT + gtid, packed, thr16);
+#if SV_TOPK_PIPE == 1
+      // Past the end the request repeats the last vector (one cache line).
+      v[u] = load_stream(vp + min(i0 + GT * U + u * GT + gtid, sl.nvec - 1));
+#elif SV_TOPK_PIPE == 2
+      v[u] = nxt[u];
+#endif
+    }
   }
   // Each wave reduces to at most K keys, then the row's first wave merges.
+  if (lane_id() == 0) *cntp = (uint32_t)cnt;
   tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, true);
   __syncthreads();
   // A wave that compacted early may hold keys below the final bound: they
