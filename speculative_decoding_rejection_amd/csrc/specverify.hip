@@ -224,6 +224,8 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
   TimedLaunch t(2, st);
   hipLaunchKernelGGL((sv::race_full_kernel<ET, 256>), dim3(pl.B * pl.Sr), dim3(256), 0, st, (const ET*)lt,
                      (const ET*)ld, pl.G, pl.V, pl.Sr, pl.segr, pl.c, k0, k1, (const RaceDesc*)desc, slots, out);
+  hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G, pl.V,
+                     pl.c, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
   t.done();
   return check_launch();
 }

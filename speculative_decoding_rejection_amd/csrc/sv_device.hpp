@@ -19,14 +19,24 @@ constexpr int kWave = 64;
 // hi(A*c0)^c3^k1, lo(A*c0)) with A = 0xD2511F53, B = 0xCD9E8D57; the key
 // advances by the golden-ratio and sqrt(3)-1 Weyl increments between rounds.
 // ---------------------------------------------------------------------------
+// a ^ b ^ k in one VALU instruction (gfx950's three-input bit operation,
+// truth table 0x96); k is wave-uniform (the key schedule) and sits in an SGPR.
+__device__ __forceinline__ uint32_t xor3_sk(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+// Requires a wave-uniform key (k0, k1).
 __device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t a_lo = c.x * 0xD2511F53u;
-    const uint32_t a_hi = __umulhi(c.x, 0xD2511F53u);
-    const uint32_t b_lo = c.z * 0xCD9E8D57u;
-    const uint32_t b_hi = __umulhi(c.z, 0xCD9E8D57u);
-    c = make_uint4(b_hi ^ c.y ^ k0, b_lo, a_hi ^ c.w ^ k1, a_lo);
+    // 32 x 32 -> 64-bit products: one v_mad_u64_u32 each on gfx950 (about
+    // 1.4x the throughput of separate low and high multiplies).
+    const uint64_t pa = (uint64_t)c.x * 0xD2511F53ull;
+    const uint64_t pb = (uint64_t)c.z * 0xCD9E8D57ull;
+    c = make_uint4(xor3_sk((uint32_t)(pb >> 32), c.y, k0), (uint32_t)pb, xor3_sk((uint32_t)(pa >> 32), c.w, k1),
+                   (uint32_t)pa);
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -49,19 +59,19 @@ __device__ __forceinline__ double unit_from_words(uint32_t lo, uint32_t hi) {
   return (double)(k53 + 1ull) * 0x1.0p-53;
 }
 
-// E = -ln(u) for the same u, to fp32 relative accuracy.  For u >= 1/2 the
-// gap t = 1 - u = (2^53 - 1 - k53) * 2^-53 is exact in integers and
-// E = -log1p(-t) keeps full relative precision as u -> 1 (where u itself,
-// rounded to fp32, would collapse to 1).  E = 0 only for u == 1.
+// E = -ln(u) for the same u, to about 7e-7 relative error in fp32.  The
+// gap t = 1 - u = (2^53 - 1 - k53) * 2^-53 is exact in integers (the
+// complement of the 53 bits); for t < 1/16, -ln(1 - t) = t + t^2/2 + ...
+// truncated after t^5/5 (next term below 2e-7 relative), so precision holds
+// as u -> 1 where u itself, rounded to fp32, would collapse to 1; otherwise
+// -ln(u) = -ln(2) log2(u) with the hardware log2 on u rounded to fp32
+// (|log2 u| >= 0.093 there).  E = 0 only for u == 1.
 __device__ __forceinline__ float exp1_from_words(uint32_t lo, uint32_t hi) {
-  const uint64_t k53 = ((((uint64_t)hi) << 32) | lo) >> 11;
-  if (k53 >= (1ull << 52)) {
-    const uint64_t t = (1ull << 53) - 1ull - k53;
-    const float tf = (float)t * 0x1.0p-53f;
-    return -log1pf(-tf);
-  }
-  const float uf = (float)(k53 + 1ull) * 0x1.0p-53f;
-  return -logf(uf);
+  const float t = fmaf((float)(~lo >> 11), 0x1.0p-53f, (float)(~hi) * 0x1.0p-32f);
+  const float u = fmaf((float)((lo >> 11) + 1u), 0x1.0p-53f, (float)hi * 0x1.0p-32f);
+  const float ser = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, 0.2f, 0.25f), 0.33333334f), 0.5f), 1.0f);
+  const float lg = -0.6931471805599453f * __builtin_amdgcn_logf(u);
+  return t < 0.0625f ? ser : lg;
 }
 
 // ---------------------------------------------------------------------------

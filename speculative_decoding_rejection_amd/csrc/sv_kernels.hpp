@@ -764,11 +764,11 @@ __global__ __launch_bounds__(64) void accept_topk_kernel(const uint64_t* __restr
     const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
     const float E = (y & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
     if (w > 0.f) {
-      const uint64_t kk = make_key(E > 0.f ? w / E : INFINITY, y);
+      const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), y);
       best_w = kk > best_w ? kk : best_w;
     }
     if (p > 0.f) {
-      const uint64_t kk = make_key(E > 0.f ? p / E : INFINITY, y);
+      const uint64_t kk = make_key(p * __builtin_amdgcn_rcpf(E), y);
       best_p = kk > best_p ? kk : best_p;
     }
   }
@@ -860,15 +860,18 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
   if (lane == 0) {
     nacc[b] = n;
     desc[b] = d;
-    slots[3 * b + 0] = 0ull;  // best residual key
-    slots[3 * b + 1] = 0ull;  // best p key (zero-mass fallback)
-    slots[3 * b + 2] = 0ull;  // finished workgroups
+    slots[3 * b] = 0ull;  // best race key
   }
 }
 
 // ===========================================================================
 // Race pass (no top-k): Exp(1) race over the full row n of each request.
 // ===========================================================================
+// Scores w / E with w = p - q (residual), p with the draft token masked
+// (one-hot), or p (bonus).  Each thread keeps its best (score, index) in
+// ascending index order (strict '>' keeps the lowest index); the workgroup
+// merges (value, index) keys; the request's workgroups merge with a 64-bit
+// atomic max, and race_finish_kernel writes the token.
 template <typename ET, int NT>
 __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld, int G,
                                                        int V, int S, int seg, float c, uint32_t k0, uint32_t k1,
@@ -883,29 +886,22 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   const ET* rq = d.resid ? ld + ((size_t)b * G + n) * V : nullptr;
   const int a = s * seg;
   const int e = min(V, a + seg);
-  uint64_t best_w = 0ull, best_p = 0ull;
-  auto score = [&](float lp, float lq, uint32_t y, uint4& blk, uint32_t& blk_id) {
-    const uint32_t pair = y >> 1;
-    if (pair != blk_id) {
-      blk = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
-      blk_id = pair;
-    }
-    const float E = (y & 1u) ? exp1_from_words(blk.z, blk.w) : exp1_from_words(blk.x, blk.y);
+  const int tid = threadIdx.x;
+  const uint32_t ub = (uint32_t)b, un = (uint32_t)n;
+  float best = -1.f;
+  int best_y = -1;
+  auto weight = [&](float lp, float lq, int y) -> float {
     const float p = __builtin_amdgcn_exp2f((lp - d.mp) * c) * d.inv_zp;
-    float w;
-    if (d.resid) {
-      const float q = __builtin_amdgcn_exp2f((lq - d.mq) * c) * d.inv_zq;
-      w = fmaxf(p - q, 0.f);
-      if (p > 0.f) {
-        const uint64_t kk = make_key(E > 0.f ? p / E : INFINITY, y);
-        best_p = kk > best_p ? kk : best_p;
-      }
-    } else {
-      w = ((int)y == d.mask_tok) ? 0.f : p;
-    }
+    if (d.resid) return fmaxf(p - __builtin_amdgcn_exp2f((lq - d.mq) * c) * d.inv_zq, 0.f);
+    return y == d.mask_tok ? 0.f : p;
+  };
+  auto consider = [&](float w, float E, int y) {
     if (w > 0.f) {
-      const uint64_t kk = make_key(E > 0.f ? w / E : INFINITY, y);
-      best_w = kk > best_w ? kk : best_w;
+      const float sc = w * __builtin_amdgcn_rcpf(E);  // E = 0 gives +inf
+      if (sc > best) {
+        best = sc;
+        best_y = y;
+      }
     }
   };
   Slice<ET> sl(rp, a, e);
@@ -913,56 +909,109 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   // row's alignment (rows start at different offsets when V * size is not a
   // multiple of 16); otherwise element by element.
   const bool q_vec = rq && ((((uintptr_t)(rp + a)) ^ ((uintptr_t)(rq + a))) & 15u) == 0u;
-  const int tid = threadIdx.x;
-  uint4 blk = make_uint4(0, 0, 0, 0);
-  uint32_t blk_id = 0xFFFFFFFFu;
-  if (tid < sl.nscalar()) {
-    const int y = sl.scalar_index(tid);
-    score(Elem<ET>::load1(rp + y), rq ? Elem<ET>::load1(rq + y) : 0.f, (uint32_t)y, blk, blk_id);
-  }
   const uint4* vp = sl.vecs();
   const uint4* vq = q_vec ? (const uint4*)(rq + a + sl.head) : nullptr;
-  for (int i = tid; i < sl.nvec; i += NT) {
+  // Vectors start on even tokens when the slice's first vector does: then
+  // tokens 2m and 2m+1 share one Philox block.
+  const bool even0 = ((a + sl.head) & 1) == 0;
+  auto race_vec = [&](const uint4& pv, const uint4& qv, int i) {
     float fp[EPV], fq[EPV];
-    Elem<ET>::unpack(load_stream(vp + i), fp);
+    Elem<ET>::unpack(pv, fp);
     const int y0 = sl.vec_index0(i);
     if (q_vec) {
-      Elem<ET>::unpack(load_stream(vq + i), fq);
+      Elem<ET>::unpack(qv, fq);
     } else {
 #pragma unroll
       for (int k = 0; k < EPV; ++k) fq[k] = rq ? Elem<ET>::load1(rq + y0 + k) : 0.f;
     }
+    if (even0) {
 #pragma unroll
-    for (int k = 0; k < EPV; ++k) score(fp[k], fq[k], (uint32_t)(y0 + k), blk, blk_id);
+      for (int m = 0; m < EPV / 2; ++m) {
+        const int y = y0 + 2 * m;
+        const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
+        consider(weight(fp[2 * m], fq[2 * m], y), exp1_from_words(r.x, r.y), y);
+        consider(weight(fp[2 * m + 1], fq[2 * m + 1], y + 1), exp1_from_words(r.z, r.w), y + 1);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) {
+        const int y = y0 + k;
+        const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
+        consider(weight(fp[k], fq[k], y), (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y), y);
+      }
+    }
+  };
+  const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
+  // Two vectors per iteration: more independent Philox chains in flight.
+  int i = tid;
+  for (; i + NT < sl.nvec; i += 2 * NT) {
+    const uint4 p0 = load_stream(vp + i), p1 = load_stream(vp + i + NT);
+    const uint4 q0 = q_vec ? load_stream(vq + i) : zero4;
+    const uint4 q1 = q_vec ? load_stream(vq + i + NT) : zero4;
+    race_vec(p0, q0, i);
+    race_vec(p1, q1, i + NT);
   }
-  best_w = wave_max_u64(best_w);
-  best_p = wave_max_u64(best_p);
-  __shared__ uint64_t red[2][NT / kWave];
-  const int w = tid / kWave;
-  if (lane_id() == 0) {
-    red[0][w] = best_w;
-    red[1][w] = best_p;
+  if (i < sl.nvec) race_vec(load_stream(vp + i), q_vec ? load_stream(vq + i) : zero4, i);
+  uint64_t key = best_y >= 0 ? make_key(best, (uint32_t)best_y) : 0ull;
+  // Scalar head and tail: keyed directly, so index order does not matter.
+  if (tid < sl.nscalar()) {
+    const int y = sl.scalar_index(tid);
+    const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
+    const float w = weight(Elem<ET>::load1(rp + y), rq ? Elem<ET>::load1(rq + y) : 0.f, y);
+    if (w > 0.f) {
+      const float E = (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
+      const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), (uint32_t)y);
+      key = kk > key ? kk : key;
+    }
   }
+  key = wave_max_u64(key);
+  __shared__ uint64_t red[NT / kWave];
+  if (lane_id() == 0) red[tid / kWave] = key;
   __syncthreads();
   if (tid == 0) {
-    uint64_t bw = red[0][0], bp = red[1][0];
-    for (int k = 1; k < NT / kWave; ++k) {
-      bw = red[0][k] > bw ? red[0][k] : bw;
-      bp = red[1][k] > bp ? red[1][k] : bp;
+    uint64_t bk = red[0];
+    for (int k = 1; k < NT / kWave; ++k) bk = red[k] > bk ? red[k] : bk;
+    // Device-scope atomic max: coherent across XCDs; read by the next launch.
+    if (bk) atomicMax(&slots[3 * b], (unsigned long long)bk);
+  }
+}
+
+// Writes each request's race winner.  If the residual had no positive weight
+// (possible only when p and q agree to rounding) the draw is taken from p_n
+// instead, by the whole workgroup over the row (rare).
+template <typename ET, int NT>
+__global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ lt, int G, int V, float c, uint32_t k0,
+                                                         uint32_t k1, const RaceDesc* __restrict__ desc,
+                                                         const unsigned long long* __restrict__ slots,
+                                                         int32_t* __restrict__ out) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const RaceDesc d = desc[b];
+  const int n = d.n;
+  const unsigned long long win = slots[3 * b];
+  if (win) {
+    if (tid == 0) out[(size_t)b * (G + 1) + n] = (int32_t)key_index(win);
+    return;
+  }
+  const ET* rp = lt + ((size_t)b * (G + 1) + n) * V;
+  const uint32_t ub = (uint32_t)b, un = (uint32_t)n;
+  uint64_t kp = 0ull;
+  for (int y = tid; y < V; y += NT) {
+    const float p = __builtin_amdgcn_exp2f((Elem<ET>::load1(rp + y) - d.mp) * c) * d.inv_zp;
+    if (p > 0.f) {
+      const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
+      const float E = (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
+      const uint64_t kk = make_key(p * __builtin_amdgcn_rcpf(E), (uint32_t)y);
+      kp = kk > kp ? kk : kp;
     }
-    unsigned long long* sl3 = slots + 3 * b;
-    if (bw) atomicMax(&sl3[0], (unsigned long long)bw);
-    if (bp) atomicMax(&sl3[1], (unsigned long long)bp);
-    __threadfence();
-    const unsigned long long done = atomicAdd(&sl3[2], 1ull);
-    if (done == (unsigned long long)(S - 1)) {
-      // Last workgroup of this request: every other one has published.
-      __threadfence();
-      const unsigned long long fw = atomicAdd(&sl3[0], 0ull);
-      const unsigned long long fp2 = atomicAdd(&sl3[1], 0ull);
-      const unsigned long long win = fw ? fw : fp2;
-      out[(size_t)b * (G + 1) + n] = win ? (int32_t)key_index(win) : -1;
-    }
+  }
+  kp = wave_max_u64(kp);
+  __shared__ uint64_t red[NT / kWave];
+  if (lane_id() == 0) red[tid / kWave] = kp;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t bk = red[0];
+    for (int k = 1; k < NT / kWave; ++k) bk = red[k] > bk ? red[k] : bk;
+    out[(size_t)b * (G + 1) + n] = bk ? (int32_t)key_index(bk) : -1;
   }
 }
 
