@@ -65,14 +65,14 @@ typedef enum {
   SV_ERR_DTYPE = 2,        /* dtype not SV_F32 / SV_BF16, or misaligned logits */
   SV_ERR_WORKSPACE = 3,    /* workspace null, misaligned or too small */
   SV_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
-  SV_ERR_UNSUPPORTED = 5   /* top_k in (1024, vocab): not implemented */
+  SV_ERR_UNSUPPORTED = 5   /* top_k in (1024, vocab) or gamma > 16384: not implemented */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
 typedef struct {
   int32_t batch;       /* B >= 1 requests */
-  int32_t gamma;       /* G >= 1 draft positions per request */
+  int32_t gamma;       /* 1 <= G <= 16384 draft positions per request */
   int32_t vocab;       /* V >= 1 */
   int32_t dtype;       /* sv_dtype of every logit array */
   float temperature;   /* T > 0 (finite) for prob/onehot; ignored by greedy */

@@ -21,6 +21,7 @@ constexpr int kRowUnroll = 4;
 #endif
 constexpr int kTopkUnroll = SV_TOPK_UNROLL;
 constexpr int kMaxTopK = 1024;
+constexpr int kMaxGamma = 16384;  // the top-k accept pass keeps one byte per position in LDS
 constexpr size_t kWsAlign = 256;
 constexpr int kEntryProb = 0, kEntryOnehot = 1, kEntryGreedy = 2;
 
@@ -62,6 +63,7 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   if (p->top_k < 0) return SV_ERR_INVALID_ARG;
   if (entry != kEntryGreedy && !(p->temperature > 0.f && std::isfinite(p->temperature))) return SV_ERR_INVALID_ARG;
   const int64_t B = p->batch, G = p->gamma, V = p->vocab;
+  if (G > kMaxGamma) return SV_ERR_UNSUPPORTED;
   const int64_t rows = B * (2 * G + 1);
   if (rows > (int64_t)INT32_MAX / 64 || V > (int64_t)INT32_MAX - 1024) return SV_ERR_INVALID_ARG;
   Plan q{};
@@ -202,7 +204,7 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     s = run_rows_topk<ET>(pl, lt, ld, nrows, ws, st);
     if (s != SV_OK) return s;
     TimedLaunch t(1, st);
-    hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(64), 0, st,
+    hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
                        (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, pl.c, k0, k1, out,
                        nacc, p_draft, q_draft, err);
     t.done();
@@ -270,7 +272,7 @@ const char* sv_status_string(sv_status s) {
     case SV_ERR_DTYPE: return "unsupported dtype or misaligned logits";
     case SV_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or smaller than sv_workspace_bytes()";
     case SV_ERR_HIP: return "HIP runtime or kernel launch failure";
-    case SV_ERR_UNSUPPORTED: return "top_k above 1024 (and below vocab) is not supported";
+    case SV_ERR_UNSUPPORTED: return "top_k above 1024 (and below vocab) or gamma above 16384 is not supported";
   }
   return "unknown status";
 }

@@ -701,20 +701,26 @@ __device__ __forceinline__ float cand_prob(const uint64_t* ck, int K, CandStats 
   return wave_sum_f(p);
 }
 
-// MODE 0: prob (q from draft candidates), 1: onehot.
+// MODE 0: prob (q from draft candidates), 1: onehot.  One 256-thread
+// workgroup per request: the four waves compute p(x_j), q(x_j) and the
+// accept test of different positions; wave 0 then finds the first rejection
+// and runs the race over the kept tokens of row n.  Dynamic LDS: G bytes.
 template <int MODE>
-__global__ __launch_bounds__(64) void accept_topk_kernel(const uint64_t* __restrict__ cand,
-                                                         const int32_t* __restrict__ X, int G, int V, int K,
-                                                         int rows_t, float c, uint32_t k0, uint32_t k1,
-                                                         int32_t* __restrict__ out, int32_t* __restrict__ nacc,
-                                                         float* __restrict__ p_draft, float* __restrict__ q_draft,
-                                                         int* __restrict__ err) {
+__global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __restrict__ cand,
+                                                          const int32_t* __restrict__ X, int G, int V, int K,
+                                                          int rows_t, float c, uint32_t k0, uint32_t k1,
+                                                          int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+                                                          float* __restrict__ p_draft, float* __restrict__ q_draft,
+                                                          int* __restrict__ err) {
+  extern __shared__ uint8_t rejected[];  // [G]
+  __shared__ uint64_t qkeys[1024];
+  __shared__ int n_sh;
   const int b = blockIdx.x;
-  const int lane = lane_id();
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  constexpr int NW = 4;
   const uint64_t* ct = cand + (size_t)b * (G + 1) * K;
   const uint64_t* cd = cand + ((size_t)rows_t + (size_t)b * G) * K;
-  int n = G;
-  for (int j = 0; j < G; ++j) {
+  for (int j = w; j < G; j += NW) {
     const int x = X[(size_t)b * G + j];
     const bool valid = x >= 0 && x < V;
     const CandStats sp = cand_stats(ct + (size_t)j * K, K, c);
@@ -723,24 +729,43 @@ __global__ __launch_bounds__(64) void accept_topk_kernel(const uint64_t* __restr
     if (MODE == 0) {
       const CandStats sq = cand_stats(cd + (size_t)j * K, K, c);
       qx = valid ? cand_prob(cd + (size_t)j * K, K, sq, c, x) : 0.f;
-      if (q_draft && lane == 0) q_draft[(size_t)b * G + j] = qx;
     }
-    if (p_draft && lane == 0) p_draft[(size_t)b * G + j] = px;
-    if (!valid && lane == 0) atomicOr(err, kErrBadToken);
-    if (n == G) {
+    if (lane == 0) {
+      if (p_draft) p_draft[(size_t)b * G + j] = px;
+      if (MODE == 0 && q_draft) q_draft[(size_t)b * G + j] = qx;
+      if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
       const bool acc = valid && (MODE == 0 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
-      if (!acc) n = j;
+      rejected[j] = acc ? 0 : 1;
     }
   }
+  __syncthreads();
+  if (w == 0) {
+    int n = G;
+    for (int j0 = 0; j0 < G; j0 += kWave) {
+      const uint64_t m = ballot(j0 + lane < G && rejected[j0 + lane] != 0);
+      if (m) {
+        n = j0 + (int)__builtin_ctzll(m);
+        break;
+      }
+    }
+    if (lane == 0) n_sh = n;
+  }
+  __syncthreads();
+  const int n = n_sh;
+  if (MODE == 0 && n < G) {
+    const uint64_t* cq = cd + (size_t)n * K;
+    for (int i = threadIdx.x; i < K; i += 256) qkeys[i] = cq[i];
+  }
+  __syncthreads();
+  if (w != 0) return;
   // Recovered (n < G) or bonus (n == G) token by the Exp(1) race over the
   // kept tokens of target row n.
   const uint64_t* cp = ct + (size_t)n * K;
   const CandStats sp = cand_stats(cp, K, c);
   CandStats sq{0.f, 0.f};
-  const uint64_t* cq = cd + (size_t)n * K;
-  if (MODE == 0 && n < G) sq = cand_stats(cq, K, c);
+  if (MODE == 0 && n < G) sq = cand_stats(qkeys, K, c);
   const int xn = n < G ? X[(size_t)b * G + n] : -1;
   uint64_t best_w = 0ull, best_p = 0ull;
   for (int i = lane; i < K; i += kWave) {
@@ -748,23 +773,23 @@ __global__ __launch_bounds__(64) void accept_topk_kernel(const uint64_t* __restr
     if (!k) continue;
     const uint32_t y = key_index(k);
     const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
-    float w = p;
+    float wgt = p;
     if (n < G) {
       if (MODE == 0) {
         float q = 0.f;
         for (int t = 0; t < K; ++t) {
-          const uint64_t kq = cq[t];
+          const uint64_t kq = qkeys[t];
           if (kq && key_index(kq) == y) q = __builtin_amdgcn_exp2f((key_value(kq) - sq.m) * c) * sq.inv_z;
         }
-        w = fmaxf(p - q, 0.f);
+        wgt = fmaxf(p - q, 0.f);
       } else if ((int)y == xn) {
-        w = 0.f;
+        wgt = 0.f;
       }
     }
     const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
     const float E = (y & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
-    if (w > 0.f) {
-      const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), y);
+    if (wgt > 0.f) {
+      const uint64_t kk = make_key(wgt * __builtin_amdgcn_rcpf(E), y);
       best_w = kk > best_w ? kk : best_w;
     }
     if (p > 0.f) {
@@ -800,6 +825,20 @@ __device__ __forceinline__ void merge_partials(const float2* part, int S, float 
   Z = s;
 }
 
+// Merge of one row's S partials by one lane.
+__device__ __forceinline__ void merge_row_lane(const float2* part, int S, float c, float& M, float& Z) {
+  float m = -INFINITY, s = 0.f;
+  for (int k = 0; k < S; ++k) {
+    const float2 v = part[k];
+    lse_merge(m, s, v.x, v.y, c);
+  }
+  M = m;
+  Z = s;
+}
+
+// One wave per request; lane j handles position j (chunks of 64 positions):
+// merged softmax stats, the gathered logit, p(x_j), q(x_j) and the accept
+// test all run in parallel, and the first rejection is one ballot.
 template <typename ET, int MODE>
 __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                          const float2* __restrict__ part,
@@ -813,30 +852,33 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
   const int b = blockIdx.x;
   const int lane = lane_id();
   int n = G;
-  for (int j = 0; j < G; ++j) {
-    const int x = X[(size_t)b * G + j];
-    const bool valid = x >= 0 && x < V;
-    const size_t rt = (size_t)b * (G + 1) + j;
-    float M, Z;
-    merge_partials(part + rt * S, S, c, M, Z);
-    float px = 0.f;
-    if (valid) px = __builtin_amdgcn_exp2f((Elem<ET>::load1(lt + rt * V + x) - M) * c) / Z;
-    float qx = valid ? 1.f : 0.f;
-    if (MODE == 0) {
-      const size_t rd = (size_t)b * G + j;
-      float Mq, Zq;
-      merge_partials(part + ((size_t)rows_t + rd) * S, S, c, Mq, Zq);
-      qx = valid ? __builtin_amdgcn_exp2f((Elem<ET>::load1(ld + rd * V + x) - Mq) * c) / Zq : 0.f;
-      if (q_draft && lane == 0) q_draft[rd] = qx;
-    }
-    if (p_draft && lane == 0) p_draft[(size_t)b * G + j] = px;
-    if (!valid && lane == 0) atomicOr(err, kErrBadToken);
-    if (n == G) {
+  for (int j0 = 0; j0 < G; j0 += kWave) {
+    const int j = j0 + lane;
+    bool rej = false;
+    if (j < G) {
+      const int x = X[(size_t)b * G + j];
+      const bool valid = x >= 0 && x < V;
+      const size_t rt = (size_t)b * (G + 1) + j;
+      float M, Z;
+      merge_row_lane(part + rt * S, S, c, M, Z);
+      const float px = valid ? __builtin_amdgcn_exp2f((Elem<ET>::load1(lt + rt * V + x) - M) * c) / Z : 0.f;
+      float qx = valid ? 1.f : 0.f;
+      if (MODE == 0) {
+        const size_t rd = (size_t)b * G + j;
+        float Mq, Zq;
+        merge_row_lane(part + ((size_t)rows_t + rd) * S, S, c, Mq, Zq);
+        qx = valid ? __builtin_amdgcn_exp2f((Elem<ET>::load1(ld + rd * V + x) - Mq) * c) / Zq : 0.f;
+        if (q_draft) q_draft[rd] = qx;
+      }
+      if (p_draft) p_draft[(size_t)b * G + j] = px;
+      if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
       const bool acc = valid && (MODE == 0 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
-      if (!acc) n = j;
+      rej = !acc;
     }
+    const uint64_t m = ballot(rej);
+    if (n == G && m) n = j0 + (int)__builtin_ctzll(m);
   }
   float Mp, Zp;
   merge_partials(part + ((size_t)b * (G + 1) + n) * S, S, c, Mp, Zp);
@@ -1022,38 +1064,38 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
                                                            const int32_t* __restrict__ X, int G, int V, int S,
                                                            int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                                            int32_t* __restrict__ targ, int* __restrict__ err) {
+  // Lane j handles position j (chunks of 64): the target argmax of row j
+  // (max over the row's partial keys), written to out[j] for now, and the
+  // match test; the first mismatch is one ballot.
   const int b = blockIdx.x;
   const int lane = lane_id();
-  int n = G;
   int32_t* o = out + (size_t)b * (G + 1);
-  for (int j = 0; j <= G; ++j) {
-    const uint64_t* pj = part + ((size_t)b * (G + 1) + j) * S;
-    uint64_t m = 0ull;
-    for (int k = lane; k < S; k += kWave) m = pj[k] > m ? pj[k] : m;
-    m = wave_max_u64(m);
-    const int a = (int)key_index(m);
-    if (targ && lane == 0) targ[(size_t)b * (G + 1) + j] = a;
-    if (n == G) {
+  int n = G;
+  for (int j0 = 0; j0 <= G; j0 += kWave) {
+    const int j = j0 + lane;
+    bool mis = false;
+    if (j <= G) {
+      const uint64_t* pj = part + ((size_t)b * (G + 1) + j) * S;
+      uint64_t m = 0ull;
+      for (int k = 0; k < S; ++k) m = pj[k] > m ? pj[k] : m;
+      const int a = (int)key_index(m);
+      o[j] = a;
+      if (targ) targ[(size_t)b * (G + 1) + j] = a;
       if (j < G) {
         const int x = X[(size_t)b * G + j];
         const bool valid = x >= 0 && x < V;
-        if (!valid && lane == 0) atomicOr(err, kErrBadToken);
-        if (!valid || x != a) {
-          n = j;
-          if (lane == 0) o[j] = a;
-        } else if (lane == 0) {
-          o[j] = x;
-        }
-      } else if (lane == 0) {
-        o[G] = a;  // bonus
+        if (!valid) atomicOr(err, kErrBadToken);
+        mis = !valid || x != a;
       }
-    } else {
-      if (j < G) {
-        const int x = X[(size_t)b * G + j];
-        if (!(x >= 0 && x < V) && lane == 0) atomicOr(err, kErrBadToken);
-      }
-      if (lane == 0) o[j] = -1;
     }
+    const uint64_t mm = ballot(mis);
+    if (n == G && mm) n = j0 + (int)__builtin_ctzll(mm);
+  }
+  // Accepted drafts before n, the target argmax (already in place) at n,
+  // padding after: each lane rewrites only the positions it wrote above.
+  for (int j = lane; j <= G; j += kWave) {
+    if (j < n) o[j] = X[(size_t)b * G + j];
+    else if (j > n) o[j] = -1;
   }
   if (lane == 0) nacc[b] = n;
 }

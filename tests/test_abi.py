@@ -61,7 +61,7 @@ def _call_prob(sv, params, ws_bytes=1 << 20, null=None):
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 1), (dict(gamma=0), 1), (dict(vocab=0), 1), (dict(dtype=7), 2),
     (dict(temperature=0.0), 1), (dict(temperature=-1.0), 1), (dict(temperature=float("inf")), 1),
-    (dict(top_k=-1), 1), (dict(top_k=2000), 5),
+    (dict(top_k=-1), 1), (dict(top_k=2000), 5), (dict(gamma=16385), 5),
 ])
 def test_argument_errors(sv, kw, status):
     base = dict(batch=4, gamma=3, vocab=5000, dtype=sv.SV_BF16, temperature=1.0, top_k=0, seed=1)
