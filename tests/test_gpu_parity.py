@@ -92,6 +92,27 @@ def test_small_parity(sv, name, over, k):
     check(sv, wl.entry, inp, T=wl.temperature, k=wl.top_k if k is None else k, seed=wl.verify_seed)
 
 
+@pytest.mark.parametrize("entry,G,k", [("prob", 70, 0), ("onehot", 130, 0), ("greedy", 129, 0),
+                                       ("prob", 100, 16), ("onehot", 65, 64)])
+def test_long_drafts(sv, entry, G, k):
+    # More than 64 positions: the accept passes walk positions in chunks.
+    base = {"prob": "prob_f32_b8_g4_v32000", "onehot": "onehot_bf16_b512_g3_v262144",
+            "greedy": "greedy_bf16_b64_g5_v128256"}[entry]
+    wl = W[base].scaled(B=3, G=G, V=777, chunk=3)
+    inp = workloads.generate(wl)
+    if entry != "greedy":
+        # Mostly-accepting drafts so that rejections land beyond position 64.
+        inp["draft_tokens"] = torch.argmax(inp["target_logits"][:, :G].float(), dim=-1).to(torch.int32)
+        if entry == "prob":
+            inp["draft_logits"] = inp["target_logits"][:, :G].clone()
+    got, _, _ = check(sv, entry, inp, T=0.9 if entry != "greedy" else 0.0, k=k, seed=21)
+    if entry == "greedy":
+        inp["draft_tokens"] = torch.argmax(inp["target_logits"][:, :G].float(), dim=-1).to(torch.int32)
+        inp["draft_tokens"][0, 100] = (inp["draft_tokens"][0, 100] + 1) % 777
+        got, _, _ = check(sv, entry, inp, T=0.0, k=0, seed=21)
+        assert got["num_accepted"][0] == 100 and got["num_accepted"][1] == G
+
+
 def test_topk1_matches_greedy_on_gpu(sv):
     wl = W["prob_f32_b256_g7_v151936"].scaled(B=16, V=4099, G=4)
     inp = workloads.generate(wl)
