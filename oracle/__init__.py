@@ -9,12 +9,16 @@ numpy arrays.
 Pinned functions and their pins (see tests/test_oracle_pins.py):
   philox4x32_10, uniform_accept, uniform_race -- Random123 known-answer
       values and runs of ATen's independent Philox engine;
-  row_probs -- closed forms (temperature, top-k ties, -inf logits);
+  row_probs -- closed forms (temperature, top-k ties, -inf logits; top-p
+      nucleus sets on hand-computed laws, index ties on flat rows, the
+      temperature-before-top-p and top-k-before-top-p orders);
   race -- chi-square against w / sum(w);
   verify (prob / onehot / greedy / naive) -- the worked 5-token example and
       Monte Carlo table of the vLLM rejection-resampling page, Eq. 1 of the
       draft-model page, brute-force enumeration at V <= 4, and exact
-      reductions between the three modes.
+      reductions between the three modes;
+  verify_batch -- per-request settings reduce exactly to single-setting
+      calls; temperature-0 requests follow numpy's argmax.
 Parity unpinned by the pages (pinned only by this oracle's own definition):
   the tie rules, the Philox keying and bit mapping, the zero-mass fallback.
 """
@@ -64,6 +68,13 @@ def _load():
     lib.sv_ref_row_probs.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                      ctypes.c_int, ctypes.c_void_p]
     lib.sv_ref_row_probs.restype = ctypes.c_int
+    lib.sv_ref_row_probs_p.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                       ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
+                                       ctypes.POINTER(ctypes.c_double)]
+    lib.sv_ref_row_probs_p.restype = ctypes.c_int
+    lib.sv_ref_verify_batch.argtypes = ([ctypes.c_int] * 5 + [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_uint64]
+                                        + [ctypes.c_void_p] * 14 + [ctypes.c_int])
+    lib.sv_ref_verify_batch.restype = ctypes.c_int
     lib.sv_ref_row_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
     lib.sv_ref_row_argmax.restype = ctypes.c_int
     lib.sv_ref_race.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
@@ -111,12 +122,18 @@ def uniform_race(seed: int, b: int, j: int, y: int) -> float:
     return _load().sv_ref_uniform_race(seed, b, j, y)
 
 
-def row_probs(row, temperature: float, top_k: int = 0) -> np.ndarray:
+def row_probs(row, temperature: float, top_k: int = 0, top_p: float = 1.0, return_margin: bool = False):
+    """Adjusted law of one row: temperature, top-k, top-p (>= 1: off)."""
     r, dt = _logits_bytes(row)
     V = r.shape[-1]
     out = np.zeros(V, dtype=np.float64)
-    _load().sv_ref_row_probs(_ptr(r), dt, V, float(temperature), int(top_k), _ptr(out))
-    return out
+    m = ctypes.c_double(1.0)
+    if top_p >= 1.0:
+        _load().sv_ref_row_probs(_ptr(r), dt, V, float(temperature), int(top_k), _ptr(out))
+    else:
+        _load().sv_ref_row_probs_p(_ptr(r), dt, V, float(temperature), int(top_k), float(top_p), _ptr(out),
+                                   ctypes.byref(m))
+    return (out, m.value) if return_margin else out
 
 
 def row_argmax(row) -> int:
@@ -179,6 +196,50 @@ def verify(mode: int, target_logits, draft_logits, draft_tokens, *, temperature:
     rc = lib.sv_ref_verify(mode, n, G, V, dt, float(temperature), int(top_k), int(seed),
                            _ptr(lt), _ptr(ld), _ptr(x), _ptr(rid), _ptr(out), _ptr(nacc), _ptr(pd), _ptr(qd),
                            _ptr(targ), _ptr(beta), _ptr(am), _ptr(rm), _ptr(bad), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected the arguments (rc={rc})")
+    return res
+
+
+def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, *, max_top_k: int = 1024,
+                 seed: int = 0, req_ids=None, diagnostics: bool = False, nthreads: int = 0) -> dict:
+    """Run the oracle with per-request settings.
+
+    draft_logits None: one-hot drafts.  temperature [n] float32 (0 = greedy
+    request), top_k [n] int32, top_p [n] float32; the values are taken at
+    the caller's fp32 / int32 precision.
+    """
+    lib = _load()
+    lt, dt = _logits_bytes(target_logits)
+    n, G1, V = lt.shape
+    G = G1 - 1
+    ld = None
+    if draft_logits is not None:
+        ld, dt2 = _logits_bytes(draft_logits)
+        if dt2 != dt or ld.shape != (n, G, V):
+            raise ValueError("draft logits must match target dtype and be [n, G, V]")
+    x = np.ascontiguousarray(draft_tokens, dtype=np.int32)
+    if x.shape != (n, G):
+        raise ValueError("draft tokens must be [n, G]")
+    t = np.ascontiguousarray(temperature, dtype=np.float32).reshape(n)
+    k = np.ascontiguousarray(top_k, dtype=np.int32).reshape(n)
+    p = np.ascontiguousarray(top_p, dtype=np.float32).reshape(n)
+    rid = None if req_ids is None else np.ascontiguousarray(req_ids, dtype=np.int32)
+    res = {"out_tokens": np.empty((n, G + 1), dtype=np.int32), "num_accepted": np.empty(n, dtype=np.int32),
+           "p_draft": np.empty((n, G), dtype=np.float64), "q_draft": np.empty((n, G), dtype=np.float64),
+           "bad_token": np.zeros(n, dtype=np.int32), "bad_param": np.zeros(n, dtype=np.int32),
+           "cut_margin": np.empty(n, dtype=np.float64), "greedy": t == 0.0}
+    beta = am = rm = None
+    if diagnostics:
+        beta = np.empty((n, G), dtype=np.float64)
+        am = np.empty((n, G), dtype=np.float64)
+        rm = np.empty(n, dtype=np.float64)
+        res["beta"], res["accept_margin"], res["race_margin"] = beta, am, rm
+    rc = lib.sv_ref_verify_batch(0 if ld is not None else 1, n, G, V, dt, _ptr(t), _ptr(k), _ptr(p),
+                                 int(max_top_k), int(seed), _ptr(lt), _ptr(ld), _ptr(x), _ptr(rid),
+                                 _ptr(res["out_tokens"]), _ptr(res["num_accepted"]), _ptr(res["p_draft"]),
+                                 _ptr(res["q_draft"]), _ptr(beta), _ptr(am), _ptr(rm), _ptr(res["cut_margin"]),
+                                 _ptr(res["bad_token"]), _ptr(res["bad_param"]), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
     return res

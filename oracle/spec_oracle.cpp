@@ -21,8 +21,13 @@
 //
 // Readings where the pages are silent (each is listed with its reason in the
 // design notes of the repository):
-//   * temperature then top-k, the same T and k for p and q;
+//   * temperature, then top-k, then top-p, the same settings for p and q;
 //   * top-k keeps exactly k tokens ranked by (logit desc, index asc);
+//   * top-p keeps the shortest prefix of the law left by top-k, in the same
+//     order, whose probability reaches top_p (at least one token), and
+//     renormalises over it;
+//   * a request with temperature 0 takes the greedy rule, and its p(x_j) is
+//     the temperature-0 law (1 on the target argmax, else 0) with q(x_j) = 1;
 //   * every argmax and every race tie goes to the lowest index;
 //   * uniforms are Philox4x32-10 words mapped to (k53 + 1) * 2^-53 in (0, 1];
 //     accept stream counter (0, j, b, 0), race stream counter
@@ -136,20 +141,26 @@ double decode_logit(const void* row, int dtype, int64_t y) {
 size_t elem_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
 
 // The adjusted distribution of one position: temperature, then top-k, then
-// softmax ([P4] "vLLM 커널은 이 규칙을 어떻게 옮겼나": the sampling constraints
-// are applied to the logits before the test, so p is the adjusted law).
-std::vector<double> row_probs(const void* row, int dtype, int V, double T, int top_k) {
+// top-p, then softmax ([P4] "vLLM 커널은 이 규칙을 어떻게 옮겼나": the sampling
+// constraints are applied to the logits before the test, so p is the adjusted
+// law; the page lists them as temperature, top_k, top_p).  top_p >= 1 is off.
+// *cut_margin (if not NULL) receives the distance of top_p from the nearest
+// cumulative mass of the nucleus decision, min(C_s - top_p, top_p - C_{s-1}),
+// or 1 when top-p is off.
+std::vector<double> row_probs(const void* row, int dtype, int V, double T, int top_k, double top_p = 1.0,
+                              double* cut_margin = nullptr) {
   std::vector<double> l(V);
   for (int y = 0; y < V; ++y) l[y] = decode_logit(row, dtype, y);
 
+  // Rank by (logit desc, index asc): a stable sort on descending logit keeps
+  // equal logits in ascending index order.  Ranking on l equals ranking on
+  // l / T for T > 0.
+  std::vector<int> order(V);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int a, int c) { return l[a] > l[c]; });
+
   std::vector<char> keep(V, 1);
   if (top_k > 0 && top_k < V) {
-    // Rank by (logit desc, index asc): a stable sort on descending logit keeps
-    // equal logits in ascending index order.  Ranking on l equals ranking on
-    // l / T for T > 0.
-    std::vector<int> order(V);
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int a, int c) { return l[a] > l[c]; });
     std::fill(keep.begin(), keep.end(), 0);
     for (int r = 0; r < top_k; ++r) keep[order[r]] = 1;
   }
@@ -167,6 +178,34 @@ std::vector<double> row_probs(const void* row, int dtype, int V, double T, int t
   std::vector<double> p(V, 0.0);
   for (int y = 0; y < V; ++y)
     if (keep[y]) p[y] = std::exp(z[y] - m) / Z;
+  if (cut_margin) *cut_margin = 1.0;
+  if (!(top_p < 1.0)) return p;
+
+  // Nucleus: walk the kept tokens in rank order, adding their probability
+  // under the top-k law, and stop at the first token where the running mass
+  // reaches top_p.
+  double C = 0.0, Cprev = 0.0;
+  int s = 0;
+  for (int r = 0; r < V; ++r) {
+    const int y = order[r];
+    if (!keep[y]) continue;
+    Cprev = C;
+    C += p[y];
+    ++s;
+    if (C >= top_p) break;
+  }
+  if (cut_margin) *cut_margin = std::min(C - top_p, top_p - Cprev);
+  std::vector<char> nucleus(V, 0);
+  for (int r = 0, taken = 0; r < V && taken < s; ++r) {
+    const int y = order[r];
+    if (!keep[y]) continue;
+    nucleus[y] = 1;
+    ++taken;
+  }
+  double Zn = 0.0;
+  for (int y = 0; y < V; ++y)
+    if (nucleus[y]) Zn += std::exp(z[y] - m);
+  for (int y = 0; y < V; ++y) p[y] = nucleus[y] ? std::exp(z[y] - m) / Zn : 0.0;
   return p;
 }
 
@@ -216,6 +255,7 @@ struct Problem {
   int mode, B, G, V, dtype, top_k;
   double T;
   uint64_t seed;
+  double top_p = 1.0;
 };
 
 // One request: Algorithm 1's verification part ([P1] "방법"; [P4]
@@ -224,7 +264,7 @@ struct Problem {
 // token was out of range, else 0.
 int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, const int32_t* X,
                int32_t* out, int32_t* n_out, double* p_draft, double* q_draft, int32_t* target_argmax,
-               double* beta, double* acc_margin, double* race_margin) {
+               double* beta, double* acc_margin, double* race_margin, double* cut_margin = nullptr) {
   const int G = P.G, V = P.V;
   const size_t row_bytes = (size_t)V * elem_bytes(P.dtype);
   const double nan = std::numeric_limits<double>::quiet_NaN();
@@ -237,6 +277,7 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
   if (acc_margin)
     for (int j = 0; j < G; ++j) acc_margin[j] = nan;
   if (race_margin) *race_margin = nan;
+  if (cut_margin) *cut_margin = 1.0;
 
   if (P.mode == MODE_GREEDY) {
     // Temperature 0: accept iff the draft token is the target argmax ([P1]
@@ -259,9 +300,16 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
 
   const bool has_q = (P.mode == MODE_PROB || P.mode == MODE_NAIVE);
   std::vector<std::vector<double>> p(G + 1), q(has_q ? G : 0);
-  for (int j = 0; j <= G; ++j) p[j] = row_probs(Lt + (size_t)j * row_bytes, P.dtype, V, P.T, P.top_k);
-  for (int j = 0; j < (has_q ? G : 0); ++j)
-    q[j] = row_probs(Ld + (size_t)j * row_bytes, P.dtype, V, P.T, P.top_k);
+  double cm = 1.0, cmj = 1.0;
+  for (int j = 0; j <= G; ++j) {
+    p[j] = row_probs(Lt + (size_t)j * row_bytes, P.dtype, V, P.T, P.top_k, P.top_p, &cmj);
+    cm = std::min(cm, cmj);
+  }
+  for (int j = 0; j < (has_q ? G : 0); ++j) {
+    q[j] = row_probs(Ld + (size_t)j * row_bytes, P.dtype, V, P.T, P.top_k, P.top_p, &cmj);
+    cm = std::min(cm, cmj);
+  }
+  if (cut_margin) *cut_margin = cm;
 
   // p(x_j) and q(x_j) for every draft position (q := 1 for a one-hot draft).
   std::vector<double> px(G), qx(G);
@@ -363,6 +411,15 @@ int sv_ref_row_probs(const void* row, int dtype, int V, double T, int top_k, dou
   return 0;
 }
 
+// Adjusted distribution with top-p (top_p >= 1: off); *cut_margin as in
+// row_probs.  Returns 0.
+int sv_ref_row_probs_p(const void* row, int dtype, int V, double T, int top_k, double top_p, double* p_out,
+                       double* cut_margin) {
+  std::vector<double> p = row_probs(row, dtype, V, T, top_k, top_p, cut_margin);
+  std::copy(p.begin(), p.end(), p_out);
+  return 0;
+}
+
 int sv_ref_row_argmax(const void* row, int dtype, int V) { return row_argmax(row, dtype, V); }
 
 // Exp(1) race over weights w[0..V) on the race stream of (seed, b, j).
@@ -407,6 +464,76 @@ int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top
                          target_argmax ? target_argmax + (size_t)r * (G + 1) : nullptr,
                          beta ? beta + (size_t)r * G : nullptr, acc_margin ? acc_margin + (size_t)r * G : nullptr,
                          race_margin ? race_margin + r : nullptr);
+    if (bad_token) bad_token[r] = bad;
+  }
+  return 0;
+}
+
+// Batched verifier with per-request sampling settings.
+//   draft_mode: 0 prob (Ld: [nreq][G][V]), 1 onehot (Ld unused)
+//   T[r]: temperature, 0 = greedy request; K[r]: top-k (0 or >= V: off);
+//   P[r]: top-p in (0, 1], 1 = off; all three as the caller's fp32 / int32.
+//   max_top_k: a top_k in (max_top_k, V) makes the request invalid.
+//   An invalid request (T negative, NaN or infinite; top_k negative or above
+//   max_top_k and below V; top_p NaN, <= 0 or > 1) emits nothing: out_tokens
+//   all -1, num_accepted 0, p_draft / q_draft 0, bad_param 1.
+//   Greedy requests: the argmax rule; p_draft[j] = 1 if x_j is the target
+//   argmax of row j else 0, q_draft[j] = 1.
+//   cut_margin [nreq]: the smallest top-p boundary margin over the request's
+//   rows (1 without top-p).  Other arguments as sv_ref_verify.
+int sv_ref_verify_batch(int draft_mode, int nreq, int G, int V, int dtype, const float* T, const int32_t* K,
+                        const float* Pp, int max_top_k, uint64_t seed, const void* Lt, const void* Ld,
+                        const int32_t* X, const int32_t* req_ids, int32_t* out_tokens, int32_t* num_accepted,
+                        double* p_draft, double* q_draft, double* beta, double* acc_margin, double* race_margin,
+                        double* cut_margin, int32_t* bad_token, int32_t* bad_param, int nthreads) {
+  if (nreq < 0 || G < 1 || V < 1 || (dtype != 0 && dtype != 1) || (draft_mode != 0 && draft_mode != 1)) return -1;
+  if (!Lt || !X || !out_tokens || !num_accepted || !T || !K || !Pp) return -1;
+  if (draft_mode == MODE_PROB && !Ld) return -1;
+  const size_t row_bytes = (size_t)V * elem_bytes(dtype);
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int r = 0; r < nreq; ++r) {
+    const uint32_t b = req_ids ? (uint32_t)req_ids[r] : (uint32_t)r;
+    const double t = (double)T[r], pp = (double)Pp[r];
+    const int k = K[r];
+    const bool ok = std::isfinite(t) && t >= 0.0 && k >= 0 && (k >= V || k <= max_top_k) && pp > 0.0 &&
+                    pp <= 1.0;
+    int32_t* o = out_tokens + (size_t)r * (G + 1);
+    double* pd = p_draft ? p_draft + (size_t)r * G : nullptr;
+    double* qd = q_draft ? q_draft + (size_t)r * G : nullptr;
+    if (bad_param) bad_param[r] = ok ? 0 : 1;
+    if (cut_margin) cut_margin[r] = 1.0;
+    if (race_margin) race_margin[r] = 1.0;
+    if (acc_margin)
+      for (int j = 0; j < G; ++j) acc_margin[(size_t)r * G + j] = 1.0;
+    if (!ok) {
+      for (int j = 0; j <= G; ++j) o[j] = -1;
+      num_accepted[r] = 0;
+      for (int j = 0; j < G; ++j) {
+        if (pd) pd[j] = 0.0;
+        if (qd) qd[j] = 0.0;
+      }
+      if (bad_token) bad_token[r] = 0;
+      continue;
+    }
+    const char* lt = (const char*)Lt + (size_t)r * (G + 1) * row_bytes;
+    const char* ld = (draft_mode == MODE_PROB) ? (const char*)Ld + (size_t)r * G * row_bytes : nullptr;
+    const int32_t* x = X + (size_t)r * G;
+    Problem P{t == 0.0 ? (int)MODE_GREEDY : draft_mode, nreq, G, V, dtype, k, t, seed, pp};
+    std::vector<int32_t> targ(G + 1);
+    int bad = verify_one(P, b, lt, ld, x, o, num_accepted + r, pd, qd, targ.data(),
+                         beta ? beta + (size_t)r * G : nullptr, acc_margin ? acc_margin + (size_t)r * G : nullptr,
+                         race_margin ? race_margin + r : nullptr, cut_margin ? cut_margin + r : nullptr);
+    if (P.mode == MODE_GREEDY) {
+      // The temperature-0 law is one-hot on the target argmax.
+      for (int j = 0; j < G; ++j) {
+        if (pd) pd[j] = (x[j] == targ[j]) ? 1.0 : 0.0;
+        if (qd) qd[j] = 1.0;
+        if (beta) beta[(size_t)r * G + j] = (x[j] == targ[j]) ? 1.0 : 0.0;
+      }
+    }
     if (bad_token) bad_token[r] = bad;
   }
   return 0;

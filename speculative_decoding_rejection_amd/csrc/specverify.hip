@@ -167,12 +167,17 @@ sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int n
 #define SV_TOPK_WPR 2  // waves per row in the top-k row pass
 #endif
 
+#ifndef SV_TOPK_RPB
+#define SV_TOPK_RPB 2  // rows per workgroup in the top-k row pass
+#endif
+
 template <typename ET, int CAPW>
 void launch_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, uint64_t* cand, int* err,
                       hipStream_t st) {
-  constexpr int RPB = 4 / SV_TOPK_WPR;
-  hipLaunchKernelGGL((sv::rows_topk_kernel<ET, CAPW, kTopkUnroll, SV_TOPK_WPR>), dim3((nrows + RPB - 1) / RPB),
-                     dim3(256), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, nrows, pl.V, pl.K, cand, err);
+  constexpr int RPB = SV_TOPK_RPB;
+  hipLaunchKernelGGL((sv::rows_topk_kernel<ET, CAPW, kTopkUnroll, SV_TOPK_WPR, RPB>), dim3((nrows + RPB - 1) / RPB),
+                     dim3(SV_TOPK_WPR * RPB * 64), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, nrows, pl.V, pl.K,
+                     cand, err);
 }
 
 template <typename ET>

@@ -453,15 +453,16 @@ __device__ __forceinline__ bool bf16_vec_reaches(const uint4& v, short thr16) {
   return mm >= thr16;
 }
 
-// WPR waves share one row (4 / WPR rows per 256-thread workgroup).  Fewer
-// waves per row track the row's running k-th key more tightly (fewer keys
-// pass the filter); more waves per row shorten each row's latency.
-template <typename ET, int CAPW, int U, int WPR>
-__global__ __launch_bounds__(256) void rows_topk_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
-                                                        int rows_t, int nrows, int V, int K,
-                                                        uint64_t* __restrict__ cand, int* __restrict__ err) {
-  constexpr int NT = 256, NW = NT / kWave;
-  constexpr int RPB = NW / WPR;     // rows per workgroup
+// WPR waves share one row; a workgroup holds RPB rows.  Fewer waves per row
+// track the row's running k-th key more tightly (fewer keys pass the
+// filter); more waves per row shorten each row's latency.
+template <typename ET, int CAPW, int U, int WPR, int RPB>
+__global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* __restrict__ lt,
+                                                                       const ET* __restrict__ ld, int rows_t,
+                                                                       int nrows, int V, int K,
+                                                                       uint64_t* __restrict__ cand,
+                                                                       int* __restrict__ err) {
+  constexpr int NT = WPR * RPB * kWave, NW = NT / kWave;
   constexpr int GT = WPR * kWave;   // threads per row
   constexpr int EPV = Elem<ET>::kPerVec;
   constexpr int kGuard = CAPW - kWave * EPV;  // room for one more step's keys

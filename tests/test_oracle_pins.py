@@ -565,3 +565,231 @@ def test_argument_validation():
         oracle.verify(oracle.MODE_PROB, lt, None, x, temperature=1.0)
     with pytest.raises(ValueError):
         oracle.verify(oracle.MODE_ONEHOT, lt, None, x, temperature=1.0, top_k=-1)
+
+
+# ---------------------------------------------------------------------------
+# Top-p (nucleus) after temperature and top-k; per-request settings
+# ---------------------------------------------------------------------------
+
+def test_top_p_closed_forms():
+    """Law (0.5, 0.3, 0.15, 0.05): the nucleus is the shortest rank prefix
+    whose mass reaches top_p, renormalised (hand-computed values)."""
+    lt = _f32_logits([0.5, 0.3, 0.15, 0.05])
+    cases = {
+        1e-30: [1.0, 0, 0, 0],
+        0.45: [1.0, 0, 0, 0],
+        0.5 - 1e-6: [1.0, 0, 0, 0],
+        0.55: [0.625, 0.375, 0, 0],
+        0.79: [0.625, 0.375, 0, 0],
+        0.81: [0.5 / 0.95, 0.3 / 0.95, 0.15 / 0.95, 0],
+        0.96: [0.5, 0.3, 0.15, 0.05],
+    }
+    for top_p, want in cases.items():
+        got, margin = oracle.row_probs(lt, 1.0, 0, top_p, return_margin=True)
+        np.testing.assert_allclose(got, want, atol=2e-7, err_msg=f"top_p={top_p}")
+    # Margins: distance of top_p to the nearest cumulative mass.
+    assert abs(oracle.row_probs(lt, 1.0, 0, 0.55, return_margin=True)[1] - 0.05) < 1e-7
+    assert abs(oracle.row_probs(lt, 1.0, 0, 0.79, return_margin=True)[1] - 0.01) < 1e-7
+    # top_p = 1 is off, identical to the law without it.
+    np.testing.assert_array_equal(oracle.row_probs(lt, 0.7, 0, 1.0), oracle.row_probs(lt, 0.7, 0))
+
+
+def test_top_p_ties_go_to_the_lowest_index():
+    # Flat row: every token 1/10; 0.45 needs five tokens, 0.55 six.
+    flat = np.zeros(10, dtype=np.float32)
+    np.testing.assert_allclose(oracle.row_probs(flat, 1.0, 0, 0.45), [0.2] * 5 + [0] * 5, atol=1e-15)
+    np.testing.assert_allclose(oracle.row_probs(flat, 1.0, 0, 0.55), [1 / 6] * 6 + [0] * 4, atol=1e-15)
+    # Three tied maxima at 1, 3, 5 (mass e^2 / (3 e^2 + 4) = 0.2823 each):
+    # top_p 0.5 takes two of them, the two lowest indices.
+    row = np.array([0, 2, 0, 2, 0, 2, 0], dtype=np.float32)
+    np.testing.assert_allclose(oracle.row_probs(row, 1.0, 0, 0.5), [0, 0.5, 0, 0.5, 0, 0, 0], atol=1e-15)
+    # Mass that equals top_p exactly reaches it: 0.25 + 0.25 = 0.5 keeps two.
+    np.testing.assert_allclose(oracle.row_probs(np.zeros(4, np.float32), 1.0, 0, 0.5), [0.5, 0.5, 0, 0],
+                               atol=1e-15)
+    # The largest fp32 below 1 keeps every token of a flat row.
+    top = float(np.nextafter(np.float32(1.0), np.float32(0.0)))
+    np.testing.assert_allclose(oracle.row_probs(flat, 1.0, 0, top), [0.1] * 10, atol=1e-15)
+
+
+def test_top_p_applies_after_temperature():
+    """Logits (2, 1, 0), top_p 0.8: at T = 1 the law (e^2, e, 1) / 11.107 needs
+    two tokens (0.665 < 0.8 <= 0.910); at T = 0.5 the law (e^4, e^2, 1) / 62.99
+    needs one (0.867).  Cutting at T = 1 and then sharpening would keep two."""
+    row = np.array([2, 1, 0], dtype=np.float32)
+    e = math.e
+    np.testing.assert_allclose(oracle.row_probs(row, 1.0, 0, 0.8), [e / (e + 1), 1 / (e + 1), 0], atol=1e-7)
+    np.testing.assert_allclose(oracle.row_probs(row, 0.5, 0, 0.8), [1, 0, 0], atol=1e-15)
+
+
+def test_top_p_applies_to_the_top_k_law():
+    """Logits (3, 2, 1, 0): after top-2 the law is (e^3, e^2) / (e^3 + e^2),
+    0.731 >= 0.72, so top_p 0.72 keeps one token; on the untruncated law
+    (0.644 < 0.72) it would keep two.  After top-3, top_p 0.9 keeps two
+    (0.6652 + 0.2447 = 0.9100)."""
+    row = np.array([3, 2, 1, 0], dtype=np.float32)
+    e = math.e
+    np.testing.assert_allclose(oracle.row_probs(row, 1.0, 2, 0.72), [1, 0, 0, 0], atol=1e-15)
+    np.testing.assert_allclose(oracle.row_probs(row, 1.0, 0, 0.72), [e / (e + 1), 1 / (e + 1), 0, 0], atol=1e-7)
+    np.testing.assert_allclose(oracle.row_probs(row, 1.0, 3, 0.9), [e / (e + 1), 1 / (e + 1), 0, 0], atol=1e-7)
+
+
+@pytest.mark.parametrize("top_k", [0, 7, 40])
+def test_top_p_invariants_on_random_rows(top_k):
+    """On random rows: the nucleus is a rank prefix of the top-k set; its mass
+    under the top-k law reaches top_p and falls short of it without its last
+    token; on it the law is proportional to exp(l / T) and sums to 1."""
+    rng = np.random.default_rng(17 + top_k)
+    for it in range(40):
+        V = int(rng.integers(2, 300))
+        row = (rng.standard_normal(V) * rng.uniform(0.3, 4)).astype(np.float32)
+        if it % 5 == 0:
+            row = np.round(row).astype(np.float32)  # many ties
+        T = float(rng.uniform(0.3, 2.0))
+        top_p = float(rng.uniform(0.05, 0.99))
+        p = oracle.row_probs(row, T, top_k, top_p)
+        base = oracle.row_probs(row, T, top_k)
+        rank = sorted(range(V), key=lambda y: (-float(row[y]), y))
+        kept = [y for y in rank if p[y] > 0]
+        assert kept == rank[:len(kept)], "nucleus is not a rank prefix"
+        mass = sum(base[y] for y in kept)
+        assert mass >= top_p - 1e-12
+        assert mass - base[kept[-1]] < top_p + 1e-12
+        z = row[kept].astype(np.float64) / T
+        w = np.exp(z - z.max())
+        np.testing.assert_allclose(p[kept], w / w.sum(), rtol=1e-12)
+        assert abs(p.sum() - 1.0) < 1e-12
+
+
+def test_brute_force_top_p():
+    """Losslessness with the nucleus law: the exact outcome law of the
+    verification, and the oracle's empirical one, with top-p on p and q."""
+    rng = np.random.default_rng(23)
+    lt = (rng.standard_normal((3, 4)) * 1.5).astype(np.float32)
+    ld = (rng.standard_normal((2, 4)) * 1.5).astype(np.float32)
+    G, V, n_runs, T, top_p = 2, 4, 100_000, 0.9, 0.8
+    p = np.stack([oracle.row_probs(lt[j], T, 0, top_p) for j in range(G + 1)])
+    q = np.stack([oracle.row_probs(ld[j], T, 0, top_p) for j in range(G)])
+    assert (p == 0).any() and (q == 0).any()  # the cut removes tokens here
+    law = _exact_outcome_law(p, q, "prob")
+    beta = [np.minimum(p[j], q[j]).sum() for j in range(G)]
+    for j in range(G + 1):
+        marg = np.zeros(V)
+        for (k, toks), pr in law.items():
+            if k >= j:
+                marg[toks[j]] += pr
+        np.testing.assert_allclose(marg, np.prod(beta[:j]) * p[j], atol=1e-12)
+    ltb = np.broadcast_to(lt[None], (n_runs,) + lt.shape).copy()
+    ldb = np.broadcast_to(ld[None], (n_runs,) + ld.shape).copy()
+    x = np.stack([rng.choice(V, size=n_runs, p=q[j]) for j in range(G)], axis=1).astype(np.int32)
+    res = oracle.verify_batch(ltb, ldb, x, np.full(n_runs, T, np.float32), np.zeros(n_runs, np.int32),
+                              np.full(n_runs, top_p, np.float32), seed=11)
+    keys = list(law)
+    index = {k: i for i, k in enumerate(keys)}
+    counts = np.zeros(len(keys))
+    for r in range(n_runs):
+        k = int(res["num_accepted"][r])
+        toks = tuple(int(t) for t in res["out_tokens"][r, :k + 1])
+        assert (k, toks) in index, f"impossible outcome {(k, toks)}"
+        counts[index[(k, toks)]] += 1
+    expected = np.array([law[k] for k in keys]) * n_runs
+    big = expected >= 5
+    assert stats.chisquare(counts[big], expected[big] * counts[big].sum() / expected[big].sum()).pvalue > 1e-6
+
+
+def _mixed_case(rng, n, G, V, dtype=np.float32):
+    lt = (rng.standard_normal((n, G + 1, V)) * 2).astype(np.float32)
+    ld = (lt[:, :G] + rng.standard_normal((n, G, V)).astype(np.float32)).astype(np.float32)
+    x = rng.integers(0, V, size=(n, G)).astype(np.int32)
+    # Make some drafts the target argmax so greedy requests accept some.
+    am = np.argmax(lt[:, :G], axis=-1).astype(np.int32)
+    sel = rng.random((n, G)) < 0.6
+    x[sel] = am[sel]
+    T = rng.choice(np.array([0.0, 0.5, 0.8, 1.0, 1.3], np.float32), size=n)
+    K = rng.choice(np.array([0, 1, 5, 20, V + 3], np.int32), size=n)
+    P = rng.choice(np.array([1.0, 0.3, 0.9, 0.95], np.float32), size=n)
+    return lt, ld, x, T, K, P
+
+
+@pytest.mark.parametrize("draft", ["prob", "onehot"])
+def test_batch_reduces_to_single_setting_calls(draft):
+    """Each request of a mixed batch gives exactly what a call with its own
+    settings alone gives: the sampled path of verify() (top-p off) or, at
+    temperature 0, the greedy rule."""
+    rng = np.random.default_rng(31 if draft == "prob" else 32)
+    n, G, V = 40, 4, 50
+    lt, ld, x, T, K, P = _mixed_case(rng, n, G, V)
+    P[:] = 1.0
+    res = oracle.verify_batch(lt, ld if draft == "prob" else None, x, T, K, P, seed=77)
+    mode = oracle.MODE_PROB if draft == "prob" else oracle.MODE_ONEHOT
+    for r in range(n):
+        if T[r] == 0:
+            one = oracle.verify(oracle.MODE_GREEDY, lt[r:r + 1], None, x[r:r + 1], seed=77, req_ids=[r])
+        else:
+            one = oracle.verify(mode, lt[r:r + 1], ld[r:r + 1] if draft == "prob" else None, x[r:r + 1],
+                                temperature=float(T[r]), top_k=int(K[r]), seed=77, req_ids=[r])
+            np.testing.assert_array_equal(res["p_draft"][r], one["p_draft"][0])
+        np.testing.assert_array_equal(res["out_tokens"][r], one["out_tokens"][0])
+        assert res["num_accepted"][r] == one["num_accepted"][0]
+
+
+def test_batch_greedy_requests_follow_numpy_argmax():
+    rng = np.random.default_rng(41)
+    n, G, V = 30, 5, 64
+    lt, ld, x, T, K, P = _mixed_case(rng, n, G, V)
+    T[:] = 0.0
+    res = oracle.verify_batch(lt, ld, x, T, K, P, seed=5)
+    a = np.argmax(lt, axis=-1)
+    for r in range(n):
+        mism = np.nonzero(x[r] != a[r, :G])[0]
+        nn = int(mism[0]) if mism.size else G
+        want = np.full(G + 1, -1)
+        want[:nn] = x[r, :nn]
+        want[nn] = a[r, nn]
+        np.testing.assert_array_equal(res["out_tokens"][r], want)
+        assert res["num_accepted"][r] == nn
+        np.testing.assert_array_equal(res["p_draft"][r], (x[r] == a[r, :G]).astype(np.float64))
+        np.testing.assert_array_equal(res["q_draft"][r], np.ones(G))
+
+
+def test_batch_top_p_tiny_is_greedy_acceptance_and_bonus():
+    """With top_p tiny every law is one-hot on its row's argmax: a draft that
+    is the argmax of both rows is always accepted, any other always rejected,
+    and the emitted token at n is the target argmax."""
+    rng = np.random.default_rng(43)
+    n, G, V = 30, 4, 40
+    lt, ld, x, T, K, P = _mixed_case(rng, n, G, V)
+    ld = lt[:, :G].copy()
+    T[:] = 0.9
+    K[:] = 0
+    P[:] = 1e-30
+    res = oracle.verify_batch(lt, ld, x, T, K, P, seed=6)
+    a = np.argmax(lt, axis=-1)
+    for r in range(n):
+        mism = np.nonzero(x[r] != a[r, :G])[0]
+        nn = int(mism[0]) if mism.size else G
+        assert res["num_accepted"][r] == nn
+        assert res["out_tokens"][r, nn] == a[r, nn]
+
+
+def test_batch_invalid_settings_emit_nothing():
+    rng = np.random.default_rng(47)
+    n, G, V = 6, 3, 30
+    lt, ld, x, T, K, P = _mixed_case(rng, n, G, V)
+    T[:] = 0.8
+    K[:] = 0
+    P[:] = 1.0
+    T[0] = -1.0
+    T[1] = np.inf
+    K[2] = -1
+    K[3] = 25  # above max_top_k = 20 and below V
+    P[4] = 0.0
+    P[5] = 1.5
+    res = oracle.verify_batch(lt, ld, x, T, K, P, max_top_k=20, seed=1)
+    assert res["bad_param"].tolist() == [1] * 6
+    assert (res["out_tokens"] == -1).all() and (res["num_accepted"] == 0).all()
+    K[3] = 20
+    T[:2] = 0.8
+    K[2] = 0
+    P[4:] = 1.0
+    res = oracle.verify_batch(lt, ld, x, T, K, P, max_top_k=20, seed=1)
+    assert res["bad_param"].tolist() == [0] * 6
