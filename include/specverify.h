@@ -116,9 +116,62 @@ sv_status spec_verify_greedy(const sv_params* params, const void* target_logits,
                              int32_t* out_tokens, int32_t* num_accepted, int32_t* target_argmax,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Per-request sampling settings of spec_verify_batch: DEVICE arrays of
+ * length batch, owned by the caller and read by the kernels (the host never
+ * reads them).  The adjusted laws are temperature, then top-k, then top-p,
+ * applied alike to p and q (page "vLLM speculative decoding이 기각 토큰을 다시
+ * 뽑는 이유", section "vLLM 커널은 이 규칙을 어떻게 옮겼나": temperature,
+ * top_k and top_p are applied before the test, in that order).
+ *   temperature[b]  T_b >= 0, finite.  T_b == 0: a greedy request, decided by
+ *                   argmax matching (section "기본값 greedy 드래프트에서도
+ *                   분포가 지켜질까"); its top_k and top_p are ignored.
+ *   top_k[b]        0 or >= vocab: off; else 1..max_top_k.  NULL: all off.
+ *   top_p[b]        in (0, 1]; 1: off.  The nucleus is the shortest prefix,
+ *                   in (logit desc, index asc) order, of the law left by
+ *                   top-k whose probability reaches top_p (at least one
+ *                   token); the law is renormalised over it.  NULL: all off.
+ *   max_top_k       host-side bound, 0..1024: every top_k[b] below vocab is
+ *                   at most this (it sizes the workspace and the kernels).
+ * A request whose settings break these rules (T negative, NaN or infinite;
+ * top_k negative or in (max_top_k, vocab); top_p NaN, <= 0 or > 1) emits
+ * nothing: out_tokens all -1, num_accepted 0, p_draft and q_draft 0; the
+ * sticky error word gets bit 2.  Other requests are unaffected. */
+typedef struct {
+  const float* temperature;
+  const int32_t* top_k;
+  const float* top_p;
+  int32_t max_top_k;
+  int32_t reserved; /* 0 */
+} sv_sampling;
+
+/* Workspace bytes of spec_verify_batch for these parameters (0 if invalid).
+ * params->temperature and params->top_k are not used. */
+size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* sampling);
+
+/* Verification with per-request settings: greedy, top-k, top-p and plain
+ * requests mixed in one call (vLLM's rejection sampler takes such a batch,
+ * same section).  Sampled requests follow spec_verify_prob (draft_logits not
+ * NULL) or spec_verify_onehot (draft_logits NULL) with their own T, top-k and
+ * top-p, and draw from the same Philox streams (keyed by params->seed): a
+ * batch whose requests all share one setting gives bit-identical results to
+ * the single-setting entry point.  Greedy requests follow spec_verify_greedy;
+ * for them p_draft[b][j] is the temperature-0 law (1 if x_j is the target
+ * argmax, else 0) and q_draft[b][j] = 1.  Draft rows of greedy requests are
+ * not read.  q_draft (may be NULL) is 1 for valid one-hot drafts.
+ *   params: batch, gamma, vocab, dtype, seed (temperature, top_k unused)
+ *   target_logits [B][G+1][V], draft_logits [B][G][V] or NULL,
+ *   draft_tokens [B][G], out_tokens [B][G+1], num_accepted [B],
+ *   p_draft, q_draft [B][G] (may be NULL).
+ * Workspace: sv_workspace_bytes_batch(params, sampling) bytes. */
+sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const void* target_logits,
+                            const void* draft_logits, const int32_t* draft_tokens, int32_t* out_tokens,
+                            int32_t* num_accepted, float* p_draft, float* q_draft, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Synchronises `stream`, then copies the sticky device error word of the
- * last call that used `workspace` to *host_code: 0 = none, 1 = a draft token
- * was out of range. */
+ * last call that used `workspace` to *host_code: bit 0 (1) = a draft token
+ * was out of range; bit 1 (2) = a request of spec_verify_batch had invalid
+ * settings. */
 sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream);
 
 /* Per-kernel timing for measurement.  While enabled, every launch of the

@@ -59,3 +59,67 @@ def assert_parity(entry: str, got: dict, ref: dict, prob_tol: float = 1e-5, tie:
     if max_tie_fraction is not None:
         assert rep["near_tie_requests"] <= max_tie_fraction * rep["rows"], rep
     return rep
+
+
+def compare_batch(got: dict, ref: dict, prob_tol: float = 1e-5, tie: float = 1e-4, cut_tol: float = 1e-9) -> dict:
+    """Per-request comparison of a batch call (per-request settings).
+
+    Invalid requests: nothing emitted (tokens -1, n 0, p = q = 0), exactly.
+    Temperature-0 requests: tokens, n and the 0/1 law p(x_j), q = 1, exactly.
+    Sampled requests: the bar of ``compare``.  A request whose oracle top-p
+    decision had a cumulative mass within ``cut_tol`` of top_p (both sides sum
+    fp64 masses, so only a tie to rounding can flip it) is counted in
+    ``near_cut_requests`` and not compared.
+    """
+    out_g, out_r = np.asarray(got["out_tokens"]), ref["out_tokens"]
+    n_g, n_r = np.asarray(got["num_accepted"]), ref["num_accepted"]
+    pd_g, qd_g = np.asarray(got["p_draft"], np.float64), np.asarray(got["q_draft"], np.float64)
+    nreq, G1 = out_r.shape
+    pos = near_tie_position(ref, tie)
+    rep = {"requests": int(nreq), "rows": int(nreq * G1), "max_dp": 0.0, "max_dq": 0.0, "near_tie_requests": 0,
+           "near_cut_requests": 0, "mismatch_non_tie": 0, "mismatch_tie": 0, "greedy_requests": 0,
+           "invalid_requests": 0, "bad": []}
+
+    def fail(r):
+        rep["mismatch_non_tie"] += 1
+        if len(rep["bad"]) < 10:
+            rep["bad"].append(r)
+
+    for r in range(nreq):
+        same = (n_g[r] == n_r[r]) and bool((out_g[r] == out_r[r]).all())
+        if ref["bad_param"][r]:
+            rep["invalid_requests"] += 1
+            if not same or (pd_g[r] != 0).any() or (qd_g[r] != 0).any():
+                fail(r)
+            continue
+        if ref["greedy"][r]:
+            rep["greedy_requests"] += 1
+            if not same or (pd_g[r] != ref["p_draft"][r]).any() or (qd_g[r] != ref["q_draft"][r]).any():
+                fail(r)
+            continue
+        if ref["cut_margin"][r] < cut_tol:
+            rep["near_cut_requests"] += 1
+            continue
+        rep["max_dp"] = max(rep["max_dp"], float(np.max(np.abs(pd_g[r] - ref["p_draft"][r]))))
+        rep["max_dq"] = max(rep["max_dq"], float(np.max(np.abs(qd_g[r] - ref["q_draft"][r]))))
+        if pos[r] >= 0:
+            rep["near_tie_requests"] += 1
+        if same:
+            continue
+        if pos[r] >= 0:
+            j0 = int(pos[r])
+            if (out_g[r, :j0] == out_r[r, :j0]).all() and n_g[r] >= j0:
+                rep["mismatch_tie"] += 1
+                continue
+        fail(r)
+    return rep
+
+
+def assert_parity_batch(got: dict, ref: dict, prob_tol: float = 1e-5, tie: float = 1e-4, cut_tol: float = 1e-9,
+                        max_exempt_fraction: float | None = None) -> dict:
+    rep = compare_batch(got, ref, prob_tol, tie, cut_tol)
+    assert rep["mismatch_non_tie"] == 0, f"mismatch outside near-ties: {rep}"
+    assert rep["max_dp"] <= prob_tol and rep["max_dq"] <= prob_tol, rep
+    if max_exempt_fraction is not None:
+        assert rep["near_tie_requests"] + rep["near_cut_requests"] <= max_exempt_fraction * rep["rows"], rep
+    return rep

@@ -6,10 +6,11 @@ ABI declared in include/specverify.h, and uses PyTorch only to allocate device
 memory.  There is no fallback: if the library is not built, importing a
 function raises.
 
-Same names as the C ABI: sv_workspace_bytes, sv_status_string,
-spec_verify_prob, spec_verify_onehot, spec_verify_greedy,
-sv_read_device_error, sv_kernel_timing_enable / _reset / _read.  ``verify``
-is a convenience wrapper that allocates the outputs and the workspace.
+Same names as the C ABI: sv_workspace_bytes, sv_workspace_bytes_batch,
+sv_status_string, spec_verify_prob, spec_verify_onehot, spec_verify_greedy,
+spec_verify_batch, sv_read_device_error, sv_kernel_timing_enable / _reset /
+_read.  ``verify`` and ``verify_batch`` are convenience wrappers that
+allocate the outputs and the workspace.
 """
 
 from __future__ import annotations
@@ -38,6 +39,16 @@ class SvParams(ctypes.Structure):
         ("temperature", ctypes.c_float),
         ("top_k", ctypes.c_int32),
         ("seed", ctypes.c_uint64),
+    ]
+
+
+class SvSampling(ctypes.Structure):
+    _fields_ = [
+        ("temperature", ctypes.c_void_p),
+        ("top_k", ctypes.c_void_p),
+        ("top_p", ctypes.c_void_p),
+        ("max_top_k", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -71,6 +82,11 @@ def load_library():
     lib.spec_verify_onehot.restype = ctypes.c_int
     lib.spec_verify_greedy.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_greedy.restype = ctypes.c_int
+    ps = ctypes.POINTER(SvSampling)
+    lib.sv_workspace_bytes_batch.argtypes = [pp, ps]
+    lib.sv_workspace_bytes_batch.restype = sz
+    lib.spec_verify_batch.argtypes = [pp, ps, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_batch.restype = ctypes.c_int
     lib.sv_read_device_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
     lib.sv_read_device_error.restype = ctypes.c_int
     lib.sv_kernel_timing_enable.argtypes = [ctypes.c_int]
@@ -146,6 +162,33 @@ def spec_verify_greedy(params, target_logits, draft_tokens, out_tokens, num_acce
     _check(st, "spec_verify_greedy")
 
 
+def make_sampling(temperature, top_k=None, top_p=None, max_top_k: int = 0) -> SvSampling:
+    """Per-request settings from device tensors: temperature [B] float32,
+    top_k [B] int32 or None, top_p [B] float32 or None.  The returned struct
+    holds raw pointers: keep the tensors alive while it is used."""
+    def chk(t, dt):
+        if t is None:
+            return None
+        if t.dtype != dt:
+            raise ValueError(f"expected {dt}, got {t.dtype}")
+        return _ptr(t)
+    return SvSampling(chk(temperature, torch.float32), chk(top_k, torch.int32), chk(top_p, torch.float32),
+                      int(max_top_k), 0)
+
+
+def sv_workspace_bytes_batch(params: SvParams, sampling: SvSampling) -> int:
+    return int(load_library().sv_workspace_bytes_batch(ctypes.byref(params), ctypes.byref(sampling)))
+
+
+def spec_verify_batch(params, sampling, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted,
+                      p_draft, q_draft, workspace, stream=None):
+    st = load_library().spec_verify_batch(ctypes.byref(params), ctypes.byref(sampling), _ptr(target_logits),
+                                          _ptr(draft_logits), _ptr(draft_tokens), _ptr(out_tokens),
+                                          _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft), _ptr(workspace),
+                                          workspace.numel(), _stream(stream))
+    _check(st, "spec_verify_batch")
+
+
 def sv_read_device_error(workspace, stream=None) -> int:
     code = ctypes.c_int32(0)
     _check(load_library().sv_read_device_error(_ptr(workspace), ctypes.byref(code), _stream(stream)),
@@ -205,3 +248,28 @@ def verify(entry: str, target_logits, draft_tokens, draft_logits=None, *, temper
     else:
         raise ValueError(entry)
     return res
+
+
+def verify_batch(target_logits, draft_tokens, draft_logits=None, *, temperature, top_k=None, top_p=None,
+                 max_top_k=None, seed=0, workspace=None, stream=None) -> dict:
+    """Allocates outputs (and a workspace if none is given) and runs
+    spec_verify_batch.  temperature [B] float32, top_k [B] int32 or None,
+    top_p [B] float32 or None, all on the GPU.  max_top_k defaults to 1024
+    when top_k is given (it only sizes the workspace and kernels)."""
+    B, G1, V = target_logits.shape
+    G = G1 - 1
+    dev = target_logits.device
+    if max_top_k is None:
+        max_top_k = 1024 if top_k is not None else 0
+    params = make_params(B, G, V, target_logits.dtype, 1.0, 0, seed)
+    sampling = make_sampling(temperature, top_k, top_p, max_top_k)
+    nbytes = sv_workspace_bytes_batch(params, sampling)
+    if nbytes == 0:
+        raise SpecVerifyError(SV_ERR_INVALID_ARG, "sv_workspace_bytes_batch")
+    ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
+    nacc = torch.empty((B,), dtype=torch.int32, device=dev)
+    pd = torch.empty((B, G), dtype=torch.float32, device=dev)
+    qd = torch.empty((B, G), dtype=torch.float32, device=dev)
+    spec_verify_batch(params, sampling, target_logits, draft_logits, draft_tokens, out, nacc, pd, qd, ws, stream)
+    return {"out_tokens": out, "num_accepted": nacc, "p_draft": pd, "q_draft": qd, "workspace": ws}

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspecverify.so")
 SOURCES = [os.path.join(CSRC, "specverify.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("sv_device.hpp", "sv_kernels.hpp")] + [
+DEPS = SOURCES + sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")) + [
     os.path.join(ROOT, "include", "specverify.h")]
 
 HIPCC_FLAGS = [

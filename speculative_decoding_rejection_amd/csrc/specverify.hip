@@ -8,11 +8,13 @@
 #include <vector>
 
 #include "specverify.h"
-#include "sv_kernels.hpp"
+#include "sv_batch.hpp"
 
 namespace {
 
 using sv::RaceDesc;
+using sv::ReqInfo;
+using sv::RowCut;
 
 constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 4;
@@ -36,7 +38,7 @@ struct Plan {
   int rows_t, rows_d;
   int S, seg;     // row-pass splits of the vocabulary (softmax / argmax)
   int Sr, segr;   // race-pass splits
-  size_t off_err, off_part, off_cand, off_desc, off_slots, total;
+  size_t off_err, off_part, off_cand, off_desc, off_slots, off_info, off_cut, total;
 };
 
 int splits_for(int rows, int V, int target_blocks, int min_seg) {
@@ -97,8 +99,30 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   off = align_up(off + (size_t)q.B * sizeof(RaceDesc), kWsAlign);
   q.off_slots = off;
   off = align_up(off + (size_t)q.B * 3 * 8, kWsAlign);
+  q.off_info = q.off_cut = off;
   q.total = off;
   *pl = q;
+  return SV_OK;
+}
+
+// Plan of a batch call: the scalar plan's layout sized for the largest top-k
+// any request may use, plus per-request settings and per-row nucleus cuts.
+sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
+  if (!p || !sm || !sm->temperature) return SV_ERR_INVALID_ARG;
+  if (sm->max_top_k < 0) return SV_ERR_INVALID_ARG;
+  if (sm->max_top_k > kMaxTopK) return SV_ERR_UNSUPPORTED;
+  sv_params q = *p;
+  q.temperature = 1.f;
+  q.top_k = p->vocab > 1 ? (sm->max_top_k < p->vocab - 1 ? sm->max_top_k : p->vocab - 1) : 0;
+  sv_status s = make_plan(&q, kEntryProb, pl);
+  if (s != SV_OK) return s;
+  pl->c = 0.f;
+  size_t off = pl->total;
+  pl->off_info = off;
+  off = align_up(off + (size_t)pl->B * sizeof(ReqInfo), kWsAlign);
+  pl->off_cut = off;
+  if (sm->top_p) off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
+  pl->total = off;
   return SV_OK;
 }
 
@@ -151,11 +175,12 @@ sv_status check_common(const Plan& pl, const void* target_logits, const int32_t*
 }
 
 template <typename ET>
-sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st) {
+sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st,
+                           const ReqInfo* info = nullptr) {
   TimedLaunch t(0, st);
   hipLaunchKernelGGL((sv::rows_softmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(nrows * pl.S),
                      dim3(kRowThreads), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.S, pl.seg, pl.c,
-                     (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err));
+                     (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err), info, pl.G);
   t.done();
   return check_launch();
 }
@@ -173,27 +198,42 @@ sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int n
 
 template <typename ET, int CAPW>
 void launch_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, uint64_t* cand, int* err,
-                      hipStream_t st) {
+                      hipStream_t st, const ReqInfo* info) {
   constexpr int RPB = SV_TOPK_RPB;
   hipLaunchKernelGGL((sv::rows_topk_kernel<ET, CAPW, kTopkUnroll, SV_TOPK_WPR, RPB>), dim3((nrows + RPB - 1) / RPB),
                      dim3(SV_TOPK_WPR * RPB * 64), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, nrows, pl.V, pl.K,
-                     cand, err);
+                     cand, err, info, pl.G, pl.kcap);
 }
 
+// pl.K: the top-k of every row, or (batch call) the largest one; rows are
+// stored pl.kcap keys apart.
 template <typename ET>
-sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st) {
+sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st,
+                        const ReqInfo* info = nullptr) {
   TimedLaunch t(0, st);
   uint64_t* cand = (uint64_t*)(ws + pl.off_cand);
   int* err = (int*)(ws + pl.off_err);
   // Buffer capacity per wave: >= K + 64 * (elements per vector) for one
   // vector step after a compaction, and >= WPR * K for the final merge.
   if (pl.K <= 64) {
-    launch_rows_topk<ET, SV_TOPK_CAPW64>(pl, lt, ld, nrows, cand, err, st);
+    launch_rows_topk<ET, SV_TOPK_CAPW64>(pl, lt, ld, nrows, cand, err, st, info);
   } else if (pl.K <= 256) {
-    launch_rows_topk<ET, 1024>(pl, lt, ld, nrows, cand, err, st);
+    launch_rows_topk<ET, 1024>(pl, lt, ld, nrows, cand, err, st, info);
   } else {
-    launch_rows_topk<ET, 4096>(pl, lt, ld, nrows, cand, err, st);
+    launch_rows_topk<ET, 4096>(pl, lt, ld, nrows, cand, err, st, info);
   }
+  t.done();
+  return check_launch();
+}
+
+template <typename ET, bool CUT>
+sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, uint32_t k1, RaceDesc* desc,
+                   unsigned long long* slots, int32_t* out, hipStream_t st) {
+  TimedLaunch t(2, st);
+  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256, CUT>), dim3(pl.B * pl.Sr), dim3(256), 0, st, (const ET*)lt,
+                     (const ET*)ld, pl.G, pl.V, pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots);
+  hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
+                     pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
   t.done();
   return check_launch();
 }
@@ -211,7 +251,7 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
                        (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, pl.c, k0, k1, out,
-                       nacc, p_draft, q_draft, err);
+                       nacc, p_draft, q_draft, err, (const ReqInfo*)nullptr, pl.kcap);
     t.done();
     return check_launch();
   }
@@ -223,18 +263,13 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const ET*)ld, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, pl.c, k0,
-                       k1, out, nacc, p_draft, q_draft, desc, slots, err);
+                       k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)nullptr,
+                       (const RowCut*)nullptr);
     t.done();
     s = check_launch();
     if (s != SV_OK) return s;
   }
-  TimedLaunch t(2, st);
-  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256>), dim3(pl.B * pl.Sr), dim3(256), 0, st, (const ET*)lt,
-                     (const ET*)ld, pl.G, pl.V, pl.Sr, pl.segr, pl.c, k0, k1, (const RaceDesc*)desc, slots, out);
-  hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G, pl.V,
-                     pl.c, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
-  t.done();
-  return check_launch();
+  return run_race<ET, false>(pl, lt, ld, k0, k1, desc, slots, out, st);
 }
 
 template <typename ET>
@@ -245,16 +280,76 @@ sv_status verify_greedy(const Plan& pl, const void* lt, const int32_t* X, int32_
   {
     TimedLaunch t(0, st);
     hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
-                       dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part, err);
+                       dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part, err,
+                       (const ReqInfo*)nullptr, pl.G);
     t.done();
     sv_status s = check_launch();
     if (s != SV_OK) return s;
   }
   TimedLaunch t(1, st);
   hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part, X, pl.G, pl.V,
-                     pl.S, out, nacc, targ, err);
+                     pl.S, out, nacc, targ, err, (const ReqInfo*)nullptr, (float*)nullptr, (float*)nullptr);
   t.done();
   return check_launch();
+}
+
+// A batch call: per-request settings (device arrays), greedy, top-k and
+// full-row requests in one launch sequence.  Every kernel of a kind runs over
+// every row or request and skips those of other kinds.
+template <typename ET, int MODE>
+sv_status verify_batch(const Plan& pl, const sv_sampling* sm, uint64_t seed, const void* lt, const void* ld,
+                       const int32_t* X, int32_t* out, int32_t* nacc, float* p_draft, float* q_draft, char* ws,
+                       hipStream_t st) {
+  const int nrows = pl.rows_t + (MODE == 0 ? pl.rows_d : 0);
+  const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
+  int* err = (int*)(ws + pl.off_err);
+  ReqInfo* info = (ReqInfo*)(ws + pl.off_info);
+  RowCut* cut = (RowCut*)(ws + pl.off_cut);
+  uint64_t* part64 = (uint64_t*)(ws + pl.off_part);
+  const bool nuc = sm->top_p != nullptr;
+  sv_status s;
+  {
+    TimedLaunch t(0, st);
+    hipLaunchKernelGGL(sv::classify_kernel, dim3(1), dim3(1024), 0, st, sm->temperature, sm->top_k, sm->top_p, pl.B,
+                       pl.G, pl.V, sm->max_top_k, info, err, out, nacc, p_draft, q_draft);
+    t.done();
+    if ((s = check_launch()) != SV_OK) return s;
+  }
+  if (pl.K > 0 && (s = run_rows_topk<ET>(pl, lt, ld, nrows, ws, st, info)) != SV_OK) return s;
+  if ((s = run_rows_softmax<ET>(pl, lt, ld, nrows, ws, st, info)) != SV_OK) return s;
+  {
+    TimedLaunch t(0, st);
+    hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
+                       dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part64, err,
+                       (const ReqInfo*)info, pl.G);
+    if (nuc && pl.K > 0)
+      hipLaunchKernelGGL(sv::nucleus_topk_kernel, dim3((nrows + 3) / 4), dim3(256), 0, st,
+                         (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info);
+    if (nuc)
+      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(256), 0, st, (const ET*)lt, (const ET*)ld,
+                         pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part), (const ReqInfo*)info, cut);
+    t.done();
+    if ((s = check_launch()) != SV_OK) return s;
+  }
+  RaceDesc* desc = (RaceDesc*)(ws + pl.off_desc);
+  unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
+  {
+    TimedLaunch t(1, st);
+    if (pl.K > 0)
+      hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
+                         (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, 0.f, k0, k1, out,
+                         nacc, p_draft, q_draft, err, (const ReqInfo*)info, pl.kcap);
+    hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
+                       (const ET*)ld, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0, k1,
+                       out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
+                       (const RowCut*)(nuc ? cut : nullptr));
+    hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part64, X, pl.G,
+                       pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft, q_draft);
+    t.done();
+    if ((s = check_launch()) != SV_OK) return s;
+  }
+  if (nuc) return run_race<ET, true>(pl, lt, ld, k0, k1, desc, slots, out, st);
+  return run_race<ET, false>(pl, lt, ld, k0, k1, desc, slots, out, st);
 }
 
 }  // namespace
@@ -334,6 +429,43 @@ sv_status spec_verify_greedy(const sv_params* params, const void* target_logits,
   if (pl.dtype == SV_F32)
     return verify_greedy<float>(pl, target_logits, draft_tokens, out_tokens, num_accepted, target_argmax, ws, st);
   return verify_greedy<uint16_t>(pl, target_logits, draft_tokens, out_tokens, num_accepted, target_argmax, ws, st);
+}
+
+size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* sampling) {
+  Plan pl;
+  if (make_batch_plan(params, sampling, &pl) != SV_OK) return 0;
+  return pl.total;
+}
+
+sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const void* target_logits,
+                            const void* draft_logits, const int32_t* draft_tokens, int32_t* out_tokens,
+                            int32_t* num_accepted, float* p_draft, float* q_draft, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  Plan pl;
+  sv_status s = make_batch_plan(params, sampling, &pl);
+  if (s != SV_OK) return s;
+  s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
+  if (s != SV_OK) return s;
+  if (draft_logits && !aligned(draft_logits, (size_t)pl.esize)) return SV_ERR_DTYPE;
+  if (!aligned(sampling->temperature, 4) || (sampling->top_k && !aligned(sampling->top_k, 4)) ||
+      (sampling->top_p && !aligned(sampling->top_p, 4)))
+    return SV_ERR_INVALID_ARG;
+  if ((p_draft && !aligned(p_draft, 4)) || (q_draft && !aligned(q_draft, 4))) return SV_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const uint64_t seed = params->seed;
+  if (pl.dtype == SV_F32) {
+    if (draft_logits)
+      return verify_batch<float, 0>(pl, sampling, seed, target_logits, draft_logits, draft_tokens, out_tokens,
+                                    num_accepted, p_draft, q_draft, ws, st);
+    return verify_batch<float, 1>(pl, sampling, seed, target_logits, nullptr, draft_tokens, out_tokens,
+                                  num_accepted, p_draft, q_draft, ws, st);
+  }
+  if (draft_logits)
+    return verify_batch<uint16_t, 0>(pl, sampling, seed, target_logits, draft_logits, draft_tokens, out_tokens,
+                                     num_accepted, p_draft, q_draft, ws, st);
+  return verify_batch<uint16_t, 1>(pl, sampling, seed, target_logits, nullptr, draft_tokens, out_tokens,
+                                   num_accepted, p_draft, q_draft, ws, st);
 }
 
 sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream) {

@@ -1,0 +1,463 @@
+// Kernels of batch calls: per-request settings (temperature, top-k, top-p,
+// temperature-0 requests mixed with sampled ones) and the nucleus (top-p)
+// cut.
+//
+// Method: page "vLLM speculative decoding이 기각 토큰을 다시 뽑는 이유"
+// (velog), section "vLLM 커널은 이 규칙을 어떻게 옮겼나": temperature, top_k
+// and top_p are applied to the logits before the test, so p (and q) are the
+// adjusted laws; section "기본값 greedy 드래프트에서도 분포가 지켜질까": a
+// temperature-0 request is decided by argmax matching.
+//
+// The nucleus of a row is the shortest prefix, in (logit desc, index asc)
+// order, of the law left by temperature and top-k whose mass reaches top_p.
+// It is a prefix in key order, so it is one cut key kappa: a token is kept iff
+// make_key(logit, index) >= kappa.  Whether a token is in the nucleus is an
+// integer decision taken on cumulative masses, so those masses are fp64:
+// exp((l - l_max) / T) in double precision for every token that can matter.
+#pragma once
+
+#include "sv_kernels.hpp"
+
+namespace sv {
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+// Inclusive prefix sum over the lanes of a wave, in lane order.
+__device__ __forceinline__ double wave_incl_scan_d(double v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const double o = __shfl_up(v, (unsigned)d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Mass of logit l relative to the row's largest logit lm, at 1/T = it: the
+// unnormalised probability exp(l / T - lm / T), in fp64.
+__device__ __forceinline__ double nucleus_mass(double lm, float l, double it) {
+  return exp(((double)l - lm) * it);
+}
+
+// ===========================================================================
+// Classify pass: one workgroup reads the per-request settings, validates
+// them, and writes one ReqInfo per request.  An invalid request emits
+// nothing (tokens -1, n = 0, p(x) = q(x) = 0) and sets kErrBadParam.  It also
+// clears the call's error word, before any other kernel of the call can set
+// a bit.
+// ===========================================================================
+__global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict__ T, const int32_t* __restrict__ K,
+                                                        const float* __restrict__ P, int B, int G, int V,
+                                                        int max_top_k, ReqInfo* __restrict__ info,
+                                                        int* __restrict__ err, int32_t* __restrict__ out,
+                                                        int32_t* __restrict__ nacc, float* __restrict__ p_draft,
+                                                        float* __restrict__ q_draft) {
+  if (threadIdx.x == 0) atomicExch(err, 0);
+  __syncthreads();
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const float t = T[b];
+    const int k = K ? K[b] : 0;
+    const float p = P ? P[b] : 1.f;
+    const bool ok = __builtin_isfinite(t) && t >= 0.f && k >= 0 && (k >= V || k <= max_top_k) && p > 0.f &&
+                    p <= 1.f;
+    ReqInfo r;
+    r.kind = kReqInvalid;
+    r.c = 0.f;
+    r.K = 0;
+    r.top_p = p;
+    r.T = t;
+    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    if (ok) {
+      if (t == 0.f) {
+        r.kind = kReqGreedy;
+      } else {
+        r.c = (float)(1.4426950408889634 / (double)t);
+        if (k > 0 && k < V) {
+          r.kind = kReqTopk;
+          r.K = k;
+        } else {
+          r.kind = kReqFull;
+        }
+      }
+    }
+    info[b] = r;
+    if (!ok) {
+      atomicOr(err, kErrBadParam);
+      for (int j = 0; j <= G; ++j) out[(size_t)b * (G + 1) + j] = -1;
+      nacc[b] = 0;
+      for (int j = 0; j < G; ++j) {
+        if (p_draft) p_draft[(size_t)b * G + j] = 0.f;
+        if (q_draft) q_draft[(size_t)b * G + j] = 0.f;
+      }
+    }
+  }
+}
+
+// Bitonic sort of a[0, n) into descending order by one wave (n a power of
+// two).
+__device__ __forceinline__ void wave_sort_desc(uint64_t* a, int n) {
+  const int lane = lane_id();
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = lane; i < n / 2; i += kWave) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = a[lo], y = a[hi];
+        if ((x < y) == desc) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
+// The same by a whole workgroup of NT threads.
+template <int NT>
+__device__ __forceinline__ void block_sort_desc(uint64_t* a, int n) {
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < n / 2; i += NT) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = a[lo], y = a[hi];
+        if ((x < y) == desc) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Walks sorted keys a[0, n) (descending) by one wave, starting from mass A:
+// returns the first index t whose running mass A + e_0 + ... + e_t reaches
+// target, and that running mass in *zk.  If rounding leaves the target
+// unreached, the last index and the total.
+__device__ __forceinline__ int wave_walk(const uint64_t* a, int n, double A, double target, double lm, double it,
+                                         double* zk) {
+  const int lane = lane_id();
+  double base = A;
+  for (int i0 = 0; i0 < n; i0 += kWave) {
+    const int i = i0 + lane;
+    const uint64_t k = i < n ? a[i] : 0ull;
+    const double e = k ? nucleus_mass(lm, key_value(k), it) : 0.0;
+    const double inc = base + wave_incl_scan_d(e);
+    const uint64_t hit = ballot(i < n && inc >= target);
+    if (hit) {
+      const int l = (int)__builtin_ctzll(hit);
+      *zk = __shfl(inc, l);
+      return i0 + l;
+    }
+    base = __shfl(inc, kWave - 1);
+  }
+  *zk = base;
+  return n - 1;
+}
+
+// ===========================================================================
+// Nucleus of a top-k row: one wave per row (four rows per workgroup).  The
+// row's k candidate keys are sorted (descending), their fp64 masses summed
+// and walked, and the candidates after the cut are zeroed in place.
+// ===========================================================================
+__global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict__ cand, int kstride, int rows_t,
+                                                           int nrows, int G, const ReqInfo* __restrict__ info) {
+  __shared__ uint64_t keys_sh[4][1024];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int row = blockIdx.x * 4 + w;
+  if (row >= nrows) return;
+  const ReqInfo ri = info[row_request(row, rows_t, G)];
+  if (ri.kind != kReqTopk || !(ri.top_p < 1.f)) return;
+  const int K = ri.K;  // 1 <= K <= 1024 (validated by the host bound)
+  int n2 = kWave;
+  while (n2 < K) n2 <<= 1;
+  uint64_t* ks = keys_sh[w];
+  uint64_t* src = cand + (size_t)row * kstride;
+  for (int i = lane; i < n2; i += kWave) ks[i] = i < K ? src[i] : 0ull;
+  wave_lds_sync();
+  wave_sort_desc(ks, n2);
+  const uint64_t top = ks[0];
+  if (top == 0ull) return;
+  const double lm = (double)key_value(top), it = 1.0 / (double)ri.T;
+  double z = 0.0;
+  for (int i = lane; i < K; i += kWave) {
+    const uint64_t k = ks[i];
+    if (k) z += nucleus_mass(lm, key_value(k), it);
+  }
+  z = wave_sum_d(z);
+  double zk;
+  const int t = wave_walk(ks, K, 0.0, (double)ri.top_p * z, lm, it, &zk);
+  for (int i = lane; i < K; i += kWave) src[i] = i <= t ? ks[i] : 0ull;
+}
+
+// ===========================================================================
+// Nucleus of a full row (no top-k): one workgroup per row, after the softmax
+// row pass (whose partials give the row's largest logit).
+//
+//   pass 1  fp64 mass of every token; the total Z; a histogram of mass and
+//           count over bins of the gap d = (l_max - l) / T, 64 bins per nat
+//           over [0, 48).  Tokens further below the maximum carry less than
+//           2^31 e^-48 < 1e-11 of Z in total, so the cut (top_p <= 1 - 2^-24)
+//           always falls inside the histogram.
+//   scan    the bin where the running mass reaches top_p * Z, and the mass A
+//           of the bins before it.
+//   pass 2  the bin's tokens are collected into LDS (at most kNucCap),
+//           sorted by key and walked from A: the first token that reaches
+//           top_p * Z is the cut.
+//   refine  (a bin with more than kNucCap tokens, e.g. many equal logits)
+//           radix passes over the keys of that bin, 8 bits at a time below
+//           their common prefix, each keeping the digit that holds the cut,
+//           until at most kNucCap tokens remain.
+// Each pass streams the row from HBM.
+// ===========================================================================
+constexpr int kNucBinsPerNat = 64;
+constexpr int kNucNats = 48;
+constexpr int kNucBins = kNucBinsPerNat * kNucNats;  // 3072
+constexpr int kNucCap = 2048;
+
+__device__ __forceinline__ int nucleus_bin(double lm, float l, double it) {
+  const double d = (lm - (double)l) * it;
+  return (d >= 0.0 && d < (double)kNucNats) ? (int)(d * (double)kNucBinsPerNat) : -1;
+}
+
+// Calls f(logit, index) for every element of the row this thread owns.
+template <typename ET, int NT, typename F>
+__device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
+  constexpr int EPV = Elem<ET>::kPerVec, U = 2;
+  Slice<ET> sl(rp, 0, V);
+  const int tid = threadIdx.x;
+  if (tid < sl.nscalar()) {
+    const int y = sl.scalar_index(tid);
+    f(Elem<ET>::load1(rp + y), y);
+  }
+  const uint4* vp = sl.vecs();
+  for (int i0 = tid; i0 < sl.nvec; i0 += NT * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NT;
+      v[u] = i < sl.nvec ? load_stream(vp + i) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u * NT;
+      if (i < sl.nvec) {
+        float fv[EPV];
+        Elem<ET>::unpack(v[u], fv);
+        const int y0 = sl.vec_index0(i);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) f(fv[k], y0 + k);
+      }
+    }
+  }
+}
+
+template <typename ET>
+__global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                           int rows_t, int G, int V, int S,
+                                                           const float2* __restrict__ part,
+                                                           const ReqInfo* __restrict__ info,
+                                                           RowCut* __restrict__ cut) {
+  constexpr int NT = 256, NW = NT / kWave, PER = kNucBins / NT;
+  static_assert(kNucBins % NT == 0, "bins per thread");
+  const int row = blockIdx.x;
+  const ReqInfo ri = info[row_request(row, rows_t, G)];
+  if (ri.kind != kReqFull || !(ri.top_p < 1.f)) return;  // uniform over the workgroup
+  __shared__ double hm[kNucBins];
+  __shared__ uint32_t hc[kNucBins];
+  __shared__ uint64_t keys[kNucCap];
+  __shared__ double red_d[NW], red_s[NW];
+  __shared__ double incl_sh[NT];
+  __shared__ uint64_t red_k[2][NW];
+  __shared__ double sh_A;
+  __shared__ int sh_bin, sh_n;
+  __shared__ uint32_t sh_cnt;
+  __shared__ uint64_t sh_prefix;
+  __shared__ int sh_plen;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const ET* rp = row < rows_t ? lt + (size_t)row * V : ld + (size_t)(row - rows_t) * V;
+
+  // Largest logit of the row, from the softmax partials.
+  float lmax = -INFINITY;
+  for (int k = lane; k < S; k += kWave) lmax = fmaxf(lmax, part[(size_t)row * S + k].x);
+  lmax = wave_max_f(lmax);
+  const double lm = (double)lmax, it = 1.0 / (double)ri.T;
+
+  for (int i = tid; i < kNucBins; i += NT) {
+    hm[i] = 0.0;
+    hc[i] = 0u;
+  }
+  if (tid == 0) {
+    sh_bin = -1;
+    sh_prefix = 0ull;  // fixed top bits of the cut key (refinement)
+    sh_plen = 0;
+  }
+  __syncthreads();
+
+  // Pass 1: masses, Z and the gap histogram.
+  double zt = 0.0;
+  row_foreach<ET, NT>(rp, V, [&](float l, int) {
+    const double e = nucleus_mass(lm, l, it);
+    zt += e;
+    const int bin = nucleus_bin(lm, l, it);
+    if (bin >= 0) {
+      atomicAdd(&hm[bin], e);
+      atomicAdd(&hc[bin], 1u);
+    }
+  });
+  zt = wave_sum_d(zt);
+  if (lane == 0) red_d[w] = zt;
+  __syncthreads();
+  double Z = 0.0;
+  for (int k = 0; k < NW; ++k) Z += red_d[k];
+  const double target = (double)ri.top_p * Z;
+
+  // Scan: thread t owns bins [t * PER, (t + 1) * PER).  Its interval of
+  // running mass is (incl[t - 1], incl[t]], so the intervals tile [0, total].
+  double loc = 0.0;
+  for (int k = 0; k < PER; ++k) loc += hm[tid * PER + k];
+  double inc = wave_incl_scan_d(loc);
+  if (lane == kWave - 1) red_s[w] = inc;
+  __syncthreads();
+  for (int k = 0; k < w; ++k) inc += red_s[k];
+  incl_sh[tid] = inc;
+  __syncthreads();
+  {
+    const double start = tid == 0 ? 0.0 : incl_sh[tid - 1];
+    if (start < target && target <= inc) {
+      double cum = start;
+      int pick = -1;
+      double pickA = start;
+      for (int k = 0; k < PER; ++k) {
+        const int bin = tid * PER + k;
+        if (hc[bin] == 0u) continue;
+        pick = bin;  // last non-empty bin so far: the choice if rounding leaves the target unreached
+        pickA = cum;
+        const double nxt = cum + hm[bin];
+        if (nxt >= target) break;
+        cum = nxt;
+      }
+      sh_bin = pick;
+      sh_A = pickA;
+      sh_cnt = pick >= 0 ? hc[pick] : 0u;
+    }
+  }
+  __syncthreads();
+  const int bstar = sh_bin;
+  if (bstar < 0) {
+    // No finite mass (degenerate row): no cut.
+    if (tid == 0) cut[row] = RowCut{0ull, lmax, (float)(1.0 / Z)};
+    return;
+  }
+
+  // Refinement of an over-full bin: radix over the keys below their common
+  // prefix.
+  if (sh_cnt > (uint32_t)kNucCap) {
+    uint64_t kmin = ~0ull, kmax = 0ull;
+    row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+      if (nucleus_bin(lm, l, it) == bstar) {
+        const uint64_t k = make_key(l, (uint32_t)y);
+        kmin = k < kmin ? k : kmin;
+        kmax = k > kmax ? k : kmax;
+      }
+    });
+    kmax = wave_max_u64(kmax);
+    kmin = ~wave_max_u64(~kmin);
+    if (lane == 0) {
+      red_k[0][w] = kmin;
+      red_k[1][w] = kmax;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      uint64_t a = red_k[0][0], z = red_k[1][0];
+      for (int k = 1; k < NW; ++k) {
+        a = red_k[0][k] < a ? red_k[0][k] : a;
+        z = red_k[1][k] > z ? red_k[1][k] : z;
+      }
+      const int plen = a == z ? 64 : __builtin_clzll(a ^ z);
+      sh_plen = plen;
+      sh_prefix = plen == 0 ? 0ull : (plen == 64 ? z : (z & (~0ull << (64 - plen))));
+    }
+    __syncthreads();
+    while (sh_cnt > (uint32_t)kNucCap && sh_plen < 64) {
+      const int plen = sh_plen;
+      const uint64_t prefix = sh_prefix;
+      const int nb = 64 - plen < 8 ? 64 - plen : 8;
+      const int shift = 64 - plen - nb;
+      for (int i = tid; i < 256; i += NT) {
+        hm[i] = 0.0;
+        hc[i] = 0u;
+      }
+      __syncthreads();
+      row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+        if (nucleus_bin(lm, l, it) != bstar) return;
+        const uint64_t k = make_key(l, (uint32_t)y);
+        if (plen > 0 && (k >> (64 - plen)) != (prefix >> (64 - plen))) return;
+        const int dig = (int)((k >> shift) & ((1ull << nb) - 1ull));
+        atomicAdd(&hm[dig], nucleus_mass(lm, l, it));
+        atomicAdd(&hc[dig], 1u);
+      });
+      __syncthreads();
+      if (tid == 0) {
+        double cum = sh_A;
+        int pick = -1;
+        double pickA = cum;
+        for (int dig = (1 << nb) - 1; dig >= 0; --dig) {  // descending keys first
+          if (hc[dig] == 0u) continue;
+          pick = dig;
+          pickA = cum;
+          const double nxt = cum + hm[dig];
+          if (nxt >= target) break;
+          cum = nxt;
+        }
+        if (pick >= 0) {  // always: the digits hold the sh_cnt > 0 tokens of the prefix
+          sh_prefix = prefix | ((uint64_t)pick << shift);
+          sh_plen = plen + nb;
+          sh_A = pickA;
+          sh_cnt = hc[pick];
+        } else {
+          sh_plen = 64;
+          sh_cnt = 0u;
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // Pass 2: collect the tokens of the bin (and prefix), sort, walk.
+  const int plen = sh_plen;
+  const uint64_t prefix = sh_prefix;
+  if (tid == 0) sh_n = 0;
+  __syncthreads();
+  row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+    if (nucleus_bin(lm, l, it) != bstar) return;
+    const uint64_t k = make_key(l, (uint32_t)y);
+    if (plen > 0 && (plen == 64 ? k != prefix : (k >> (64 - plen)) != (prefix >> (64 - plen)))) return;
+    const int pos = atomicAdd(&sh_n, 1);
+    if (pos < kNucCap) keys[pos] = k;
+  });
+  __syncthreads();
+  const int n = sh_n < kNucCap ? sh_n : kNucCap;
+  int n2 = 2;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + tid; i < n2; i += NT) keys[i] = 0ull;
+  __syncthreads();
+  block_sort_desc<NT>(keys, n2);
+  if (w == 0) {
+    double zk;
+    const int t = n > 0 ? wave_walk(keys, n, sh_A, target, lm, it, &zk) : -1;
+    if (lane == 0) {
+      if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / zk)};
+      else cut[row] = RowCut{0ull, lmax, (float)(1.0 / Z)};
+    }
+  }
+}
+
+}  // namespace sv

@@ -37,14 +37,44 @@ namespace sv {
 
 // Error word bits.
 constexpr int kErrBadToken = 1;
+constexpr int kErrBadParam = 2;
+
+// Per-request settings of a batch call (written by the classify pass).  In a
+// call with one setting for every request the kernels get a null pointer.
+enum : int32_t { kReqInvalid = 0, kReqGreedy = 1, kReqTopk = 2, kReqFull = 3 };
+struct __align__(16) ReqInfo {
+  int32_t kind;  // kReq*
+  float c;       // log2(e) / T (sampled requests)
+  int32_t K;     // top-k of a kReqTopk request
+  float top_p;   // < 1: nucleus cut
+  float T;       // temperature
+  int32_t pad[3];
+};
+
+// Request of a logit row: rows [0, rows_t) are target rows b * (G + 1) + j,
+// the rest draft rows b * G + j.
+__device__ __forceinline__ int row_request(int row, int rows_t, int G) {
+  return row < rows_t ? row / (G + 1) : (row - rows_t) / G;
+}
+
+// Nucleus cut of a full row: tokens with key >= kappa are kept (kappa 0: no
+// cut); m is the row's largest logit and inv_z the inverse kept mass in units
+// of exp2((l - m) * c).
+struct __align__(16) RowCut {
+  uint64_t kappa;
+  float m, inv_z;
+};
 
 // Per-request race descriptor written by the accept pass (no top-k).
 struct __align__(16) RaceDesc {
-  int32_t n;         // race position (first rejection or G)
+  int32_t n;         // race position (first rejection or G); -1: no race
   int32_t mask_tok;  // one-hot: token removed from the residual, else -1
   int32_t resid;     // 1: weights max(p - q, 0); 0: weights p
   int32_t pad;
   float mp, inv_zp, mq, inv_zq;  // softmax stats of target row n / draft row n
+  float c;                       // log2(e) / T of the request
+  int32_t pad2[3];
+  uint64_t kp, kq;               // nucleus cuts of target row n / draft row n (0: none)
 };
 
 // A contiguous slice [a, e) of one logit row split into a scalar head (until
@@ -76,11 +106,19 @@ struct Slice {
 template <typename ET, int NT, int U>
 __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                           int rows_t, int V, int S, int seg, float c,
-                                                          float2* __restrict__ part, int* __restrict__ err) {
+                                                          float2* __restrict__ part, int* __restrict__ err,
+                                                          const ReqInfo* __restrict__ info, int G) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int blk = blockIdx.x;
   const int row = blk / S, s = blk - row * S;
-  if (blk == 0 && threadIdx.x == 0) *err = 0;
+  if (info) {
+    // Batch call: only rows of requests without top-k; per-request T.
+    const ReqInfo ri = info[row_request(row, rows_t, G)];
+    if (ri.kind != kReqFull) return;
+    c = ri.c;
+  } else if (blk == 0 && threadIdx.x == 0) {
+    *err = 0;
+  }
   const ET* rp = row < rows_t ? lt + (size_t)row * V : ld + (size_t)(row - rows_t) * V;
   const int a = s * seg;
   const int e = min(V, a + seg);
@@ -136,11 +174,17 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
 // ===========================================================================
 template <typename ET, int NT, int U>
 __global__ __launch_bounds__(NT) void rows_argmax_kernel(const ET* __restrict__ lt, int V, int S, int seg,
-                                                         uint64_t* __restrict__ part, int* __restrict__ err) {
+                                                         uint64_t* __restrict__ part, int* __restrict__ err,
+                                                         const ReqInfo* __restrict__ info, int G) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int blk = blockIdx.x;
   const int row = blk / S, s = blk - row * S;
-  if (blk == 0 && threadIdx.x == 0) *err = 0;
+  if (info) {
+    // Batch call: target rows of temperature-0 requests only.
+    if (info[row / (G + 1)].kind != kReqGreedy) return;
+  } else if (blk == 0 && threadIdx.x == 0) {
+    *err = 0;
+  }
   const ET* rp = lt + (size_t)row * V;
   const int a = s * seg;
   const int e = min(V, a + seg);
@@ -461,7 +505,9 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
                                                                        const ET* __restrict__ ld, int rows_t,
                                                                        int nrows, int V, int K,
                                                                        uint64_t* __restrict__ cand,
-                                                                       int* __restrict__ err) {
+                                                                       int* __restrict__ err,
+                                                                       const ReqInfo* __restrict__ info, int G,
+                                                                       int kstride) {
   constexpr int NT = WPR * RPB * kWave, NW = NT / kWave;
   constexpr int GT = WPR * kWave;   // threads per row
   constexpr int EPV = Elem<ET>::kPerVec;
@@ -475,8 +521,16 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   const int tid = threadIdx.x, w = tid / kWave;
   const int g = w / WPR, wg = w % WPR, gtid = tid % GT;
   const int row = blockIdx.x * RPB + g;
-  const bool row_ok = row < nrows;
-  if (blockIdx.x == 0 && tid == 0) *err = 0;
+  bool row_ok = row < nrows;
+  if (info) {
+    // Batch call: rows of top-k requests only, each with its own k (<= the
+    // stride); a skipped row streams nothing but joins every barrier.
+    const ReqInfo ri = info[row_request(row_ok ? row : 0, rows_t, G)];
+    row_ok = row_ok && ri.kind == kReqTopk;
+    K = __builtin_amdgcn_readfirstlane(row_ok ? ri.K : 1);  // one row per wave: wave-uniform
+  } else if (blockIdx.x == 0 && tid == 0) {
+    *err = 0;
+  }
   if (tid < NW) {
     q_sh[tid] = 0ull;
     cnt_sh[tid] = 0u;
@@ -661,7 +715,7 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
       const uint64_t thr = wave_select_kth(b0, n, K, hw);
       n = wave_keep_ge(b0, n, thr);
     }
-    uint64_t* dst = cand + (size_t)row * K;
+    uint64_t* dst = cand + (size_t)row * kstride;
     for (int i = lane_id(); i < K; i += kWave) dst[i] = i < n ? b0[i] : 0ull;
   }
 }
@@ -712,28 +766,36 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
                                                           int rows_t, float c, uint32_t k0, uint32_t k1,
                                                           int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                                           float* __restrict__ p_draft, float* __restrict__ q_draft,
-                                                          int* __restrict__ err) {
+                                                          int* __restrict__ err, const ReqInfo* __restrict__ info,
+                                                          int kstride) {
   extern __shared__ uint8_t rejected[];  // [G]
   __shared__ uint64_t qkeys[1024];
   __shared__ int n_sh;
   const int b = blockIdx.x;
+  if (info) {
+    // Batch call: top-k requests only, with their own k and T.
+    const ReqInfo ri = info[b];
+    if (ri.kind != kReqTopk) return;
+    K = ri.K;
+    c = ri.c;
+  }
   const int lane = lane_id(), w = threadIdx.x / kWave;
   constexpr int NW = 4;
-  const uint64_t* ct = cand + (size_t)b * (G + 1) * K;
-  const uint64_t* cd = cand + ((size_t)rows_t + (size_t)b * G) * K;
+  const uint64_t* ct = cand + (size_t)b * (G + 1) * kstride;
+  const uint64_t* cd = cand + ((size_t)rows_t + (size_t)b * G) * kstride;
   for (int j = w; j < G; j += NW) {
     const int x = X[(size_t)b * G + j];
     const bool valid = x >= 0 && x < V;
-    const CandStats sp = cand_stats(ct + (size_t)j * K, K, c);
-    const float px = valid ? cand_prob(ct + (size_t)j * K, K, sp, c, x) : 0.f;
+    const CandStats sp = cand_stats(ct + (size_t)j * kstride, K, c);
+    const float px = valid ? cand_prob(ct + (size_t)j * kstride, K, sp, c, x) : 0.f;
     float qx = valid ? 1.f : 0.f;
     if (MODE == 0) {
-      const CandStats sq = cand_stats(cd + (size_t)j * K, K, c);
-      qx = valid ? cand_prob(cd + (size_t)j * K, K, sq, c, x) : 0.f;
+      const CandStats sq = cand_stats(cd + (size_t)j * kstride, K, c);
+      qx = valid ? cand_prob(cd + (size_t)j * kstride, K, sq, c, x) : 0.f;
     }
     if (lane == 0) {
       if (p_draft) p_draft[(size_t)b * G + j] = px;
-      if (MODE == 0 && q_draft) q_draft[(size_t)b * G + j] = qx;
+      if (q_draft) q_draft[(size_t)b * G + j] = qx;
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
@@ -756,14 +818,14 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
   __syncthreads();
   const int n = n_sh;
   if (MODE == 0 && n < G) {
-    const uint64_t* cq = cd + (size_t)n * K;
+    const uint64_t* cq = cd + (size_t)n * kstride;
     for (int i = threadIdx.x; i < K; i += 256) qkeys[i] = cq[i];
   }
   __syncthreads();
   if (w != 0) return;
   // Recovered (n < G) or bonus (n == G) token by the Exp(1) race over the
   // kept tokens of target row n.
-  const uint64_t* cp = ct + (size_t)n * K;
+  const uint64_t* cp = ct + (size_t)n * kstride;
   const CandStats sp = cand_stats(cp, K, c);
   CandStats sq{0.f, 0.f};
   if (MODE == 0 && n < G) sq = cand_stats(qkeys, K, c);
@@ -839,7 +901,9 @@ __device__ __forceinline__ void merge_row_lane(const float2* part, int S, float 
 
 // One wave per request; lane j handles position j (chunks of 64 positions):
 // merged softmax stats, the gathered logit, p(x_j), q(x_j) and the accept
-// test all run in parallel, and the first rejection is one ballot.
+// test all run in parallel, and the first rejection is one ballot.  In a batch
+// call (info not null) only requests without top-k are handled here, each
+// with its own T, and rows with a nucleus cut take their stats from `cut`.
 template <typename ET, int MODE>
 __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                          const float2* __restrict__ part,
@@ -849,9 +913,31 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
                                                          float* __restrict__ p_draft, float* __restrict__ q_draft,
                                                          RaceDesc* __restrict__ desc,
                                                          unsigned long long* __restrict__ slots,
-                                                         int* __restrict__ err) {
+                                                         int* __restrict__ err, const ReqInfo* __restrict__ info,
+                                                         const RowCut* __restrict__ cut) {
   const int b = blockIdx.x;
   const int lane = lane_id();
+  bool nuc = false;
+  if (info) {
+    const ReqInfo ri = info[b];
+    if (ri.kind != kReqFull) {
+      if (lane == 0) desc[b].n = -1;  // no full-row race for this request
+      return;
+    }
+    c = ri.c;
+    nuc = ri.top_p < 1.f;
+  }
+  // Probability of token x (logit l) in row r, merged by one lane.
+  auto prob_lane = [&](size_t r, float l, int x) -> float {
+    if (nuc) {
+      const RowCut rc = cut[r];
+      if (make_key(l, (uint32_t)x) < rc.kappa) return 0.f;
+      return __builtin_amdgcn_exp2f((l - rc.m) * c) * rc.inv_z;
+    }
+    float M, Z;
+    merge_row_lane(part + r * S, S, c, M, Z);
+    return __builtin_amdgcn_exp2f((l - M) * c) / Z;
+  };
   int n = G;
   for (int j0 = 0; j0 < G; j0 += kWave) {
     const int j = j0 + lane;
@@ -860,17 +946,13 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
       const int x = X[(size_t)b * G + j];
       const bool valid = x >= 0 && x < V;
       const size_t rt = (size_t)b * (G + 1) + j;
-      float M, Z;
-      merge_row_lane(part + rt * S, S, c, M, Z);
-      const float px = valid ? __builtin_amdgcn_exp2f((Elem<ET>::load1(lt + rt * V + x) - M) * c) / Z : 0.f;
+      const float px = valid ? prob_lane(rt, Elem<ET>::load1(lt + rt * V + x), x) : 0.f;
       float qx = valid ? 1.f : 0.f;
       if (MODE == 0) {
         const size_t rd = (size_t)b * G + j;
-        float Mq, Zq;
-        merge_row_lane(part + ((size_t)rows_t + rd) * S, S, c, Mq, Zq);
-        qx = valid ? __builtin_amdgcn_exp2f((Elem<ET>::load1(ld + rd * V + x) - Mq) * c) / Zq : 0.f;
-        if (q_draft) q_draft[rd] = qx;
+        qx = valid ? prob_lane((size_t)rows_t + rd, Elem<ET>::load1(ld + rd * V + x), x) : 0.f;
       }
+      if (q_draft) q_draft[(size_t)b * G + j] = qx;
       if (p_draft) p_draft[(size_t)b * G + j] = px;
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
@@ -881,23 +963,32 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
     const uint64_t m = ballot(rej);
     if (n == G && m) n = j0 + (int)__builtin_ctzll(m);
   }
-  float Mp, Zp;
-  merge_partials(part + ((size_t)b * (G + 1) + n) * S, S, c, Mp, Zp);
+  // Stats of row r for the race, merged by the whole wave.
+  auto race_stats = [&](size_t r, float& M, float& inv_z, uint64_t& kap) {
+    if (nuc) {
+      const RowCut rc = cut[r];
+      M = rc.m;
+      inv_z = rc.inv_z;
+      kap = rc.kappa;
+    } else {
+      float Z;
+      merge_partials(part + r * S, S, c, M, Z);
+      inv_z = 1.f / Z;
+      kap = 0ull;
+    }
+  };
   RaceDesc d;
   d.n = n;
   d.mask_tok = (MODE == 1 && n < G) ? X[(size_t)b * G + n] : -1;
   d.resid = (MODE == 0 && n < G) ? 1 : 0;
   d.pad = 0;
-  d.mp = Mp;
-  d.inv_zp = 1.f / Zp;
+  race_stats((size_t)b * (G + 1) + n, d.mp, d.inv_zp, d.kp);
   d.mq = 0.f;
   d.inv_zq = 0.f;
-  if (d.resid) {
-    float Mq, Zq;
-    merge_partials(part + ((size_t)rows_t + (size_t)b * G + n) * S, S, c, Mq, Zq);
-    d.mq = Mq;
-    d.inv_zq = 1.f / Zq;
-  }
+  d.kq = 0ull;
+  d.c = c;
+  d.pad2[0] = d.pad2[1] = d.pad2[2] = 0;
+  if (d.resid) race_stats((size_t)rows_t + (size_t)b * G + n, d.mq, d.inv_zq, d.kq);
   int32_t* o = out + (size_t)b * (G + 1);
   for (int j = lane; j <= G; j += kWave) o[j] = j < n ? X[(size_t)b * G + j] : -1;
   if (lane == 0) {
@@ -914,17 +1005,19 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
 // (one-hot), or p (bonus).  Each thread keeps its best (score, index) in
 // ascending index order (strict '>' keeps the lowest index); the workgroup
 // merges (value, index) keys; the request's workgroups merge with a 64-bit
-// atomic max, and race_finish_kernel writes the token.
-template <typename ET, int NT>
+// atomic max, and race_finish_kernel writes the token.  CUT: rows may carry a
+// nucleus cut (tokens with key < kp / kq have p = 0 / q = 0).
+template <typename ET, int NT, bool CUT>
 __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld, int G,
-                                                       int V, int S, int seg, float c, uint32_t k0, uint32_t k1,
+                                                       int V, int S, int seg, uint32_t k0, uint32_t k1,
                                                        const RaceDesc* __restrict__ desc,
-                                                       unsigned long long* __restrict__ slots,
-                                                       int32_t* __restrict__ out) {
+                                                       unsigned long long* __restrict__ slots) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int b = blockIdx.x / S, s = blockIdx.x - b * S;
   const RaceDesc d = desc[b];
   const int n = d.n;
+  if (n < 0) return;
+  const float c = d.c;
   const ET* rp = lt + ((size_t)b * (G + 1) + n) * V;
   const ET* rq = d.resid ? ld + ((size_t)b * G + n) * V : nullptr;
   const int a = s * seg;
@@ -934,8 +1027,13 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   float best = -1.f;
   int best_y = -1;
   auto weight = [&](float lp, float lq, int y) -> float {
-    const float p = __builtin_amdgcn_exp2f((lp - d.mp) * c) * d.inv_zp;
-    if (d.resid) return fmaxf(p - __builtin_amdgcn_exp2f((lq - d.mq) * c) * d.inv_zq, 0.f);
+    float p = __builtin_amdgcn_exp2f((lp - d.mp) * c) * d.inv_zp;
+    if (CUT && make_key(lp, (uint32_t)y) < d.kp) p = 0.f;
+    if (d.resid) {
+      float q = __builtin_amdgcn_exp2f((lq - d.mq) * c) * d.inv_zq;
+      if (CUT && make_key(lq, (uint32_t)y) < d.kq) q = 0.f;
+      return fmaxf(p - q, 0.f);
+    }
     return y == d.mask_tok ? 0.f : p;
   };
   auto consider = [&](float w, float E, int y) {
@@ -1022,14 +1120,16 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
 // Writes each request's race winner.  If the residual had no positive weight
 // (possible only when p and q agree to rounding) the draw is taken from p_n
 // instead, by the whole workgroup over the row (rare).
-template <typename ET, int NT>
-__global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ lt, int G, int V, float c, uint32_t k0,
+template <typename ET, int NT, bool CUT>
+__global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ lt, int G, int V, uint32_t k0,
                                                          uint32_t k1, const RaceDesc* __restrict__ desc,
                                                          const unsigned long long* __restrict__ slots,
                                                          int32_t* __restrict__ out) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const RaceDesc d = desc[b];
   const int n = d.n;
+  if (n < 0) return;
+  const float c = d.c;
   const unsigned long long win = slots[3 * b];
   if (win) {
     if (tid == 0) out[(size_t)b * (G + 1) + n] = (int32_t)key_index(win);
@@ -1039,7 +1139,9 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
   const uint32_t ub = (uint32_t)b, un = (uint32_t)n;
   uint64_t kp = 0ull;
   for (int y = tid; y < V; y += NT) {
-    const float p = __builtin_amdgcn_exp2f((Elem<ET>::load1(rp + y) - d.mp) * c) * d.inv_zp;
+    const float l = Elem<ET>::load1(rp + y);
+    float p = __builtin_amdgcn_exp2f((l - d.mp) * c) * d.inv_zp;
+    if (CUT && make_key(l, (uint32_t)y) < d.kp) p = 0.f;
     if (p > 0.f) {
       const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
       const float E = (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
@@ -1064,11 +1166,16 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
 __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __restrict__ part,
                                                            const int32_t* __restrict__ X, int G, int V, int S,
                                                            int32_t* __restrict__ out, int32_t* __restrict__ nacc,
-                                                           int32_t* __restrict__ targ, int* __restrict__ err) {
+                                                           int32_t* __restrict__ targ, int* __restrict__ err,
+                                                           const ReqInfo* __restrict__ info,
+                                                           float* __restrict__ p_draft, float* __restrict__ q_draft) {
   // Lane j handles position j (chunks of 64): the target argmax of row j
   // (max over the row's partial keys), written to out[j] for now, and the
-  // match test; the first mismatch is one ballot.
+  // match test; the first mismatch is one ballot.  In a batch call only
+  // temperature-0 requests are handled; their p(x_j) is the temperature-0
+  // law (1 on the argmax, else 0) and q(x_j) = 1.
   const int b = blockIdx.x;
+  if (info && info[b].kind != kReqGreedy) return;
   const int lane = lane_id();
   int32_t* o = out + (size_t)b * (G + 1);
   int n = G;
@@ -1087,6 +1194,8 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
         const bool valid = x >= 0 && x < V;
         if (!valid) atomicOr(err, kErrBadToken);
         mis = !valid || x != a;
+        if (p_draft) p_draft[(size_t)b * G + j] = mis ? 0.f : 1.f;
+        if (q_draft) q_draft[(size_t)b * G + j] = 1.f;
       }
     }
     const uint64_t mm = ballot(mis);

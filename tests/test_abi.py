@@ -88,3 +88,44 @@ def test_top_k_at_or_above_vocab_is_accepted(sv):
 def test_status_strings(sv):
     for s in range(6):
         assert sv.sv_status_string(s)
+
+
+def _call_batch(sv, params, sampling, ws_bytes=1 << 20, null=None):
+    lib = sv.load_library()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
+    args = [fake] * 5
+    if null is not None:
+        args[null] = None
+    sp = ctypes.byref(sampling) if sampling is not None else None
+    return lib.spec_verify_batch(ctypes.byref(params), sp, args[0], None, args[1], args[2], args[3], None, None,
+                                 args[4], ws_bytes, None)
+
+
+def test_batch_argument_errors(sv):
+    fake = 1 << 21
+    p = sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 0, 1)
+    ok = sv.SvSampling(fake, fake, fake, 64, 0)
+    assert _call_batch(sv, p, ok, ws_bytes=16) == sv.SV_ERR_WORKSPACE  # everything else valid
+    assert _call_batch(sv, p, None) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, sv.SvSampling(None, fake, fake, 64, 0)) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, sv.SvSampling(fake, fake, fake, -1, 0)) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, sv.SvSampling(fake, fake, fake, 1025, 0)) == sv.SV_ERR_UNSUPPORTED
+    for i in range(4):
+        assert _call_batch(sv, p, ok, null=i) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, ok, null=4) == sv.SV_ERR_WORKSPACE
+    # params->temperature and ->top_k are not used by the batch entry.
+    p2 = sv.make_params(4, 3, 5000, sv.SV_BF16, -5.0, 99999, 1)
+    assert _call_batch(sv, p2, ok, ws_bytes=16) == sv.SV_ERR_WORKSPACE
+
+
+def test_batch_workspace_sizing(sv):
+    fake = 1 << 21
+    p = sv.make_params(256, 7, 151936, sv.SV_F32, 1.0, 0, 1)
+    plain = sv.sv_workspace_bytes_batch(p, sv.SvSampling(fake, None, None, 0, 0))
+    topk = sv.sv_workspace_bytes_batch(p, sv.SvSampling(fake, fake, None, 64, 0))
+    nuc = sv.sv_workspace_bytes_batch(p, sv.SvSampling(fake, fake, fake, 64, 0))
+    rows = 256 * 15
+    assert topk - plain >= rows * 64 * 8           # candidate keys of every row
+    assert nuc - topk >= rows * 16                  # one nucleus cut per row
+    assert plain >= sv.sv_workspace_bytes(sv.make_params(256, 7, 151936, sv.SV_F32, 1.0, 0, 1))
+    assert sv.sv_workspace_bytes_batch(sv.make_params(0, 7, 100, sv.SV_F32), sv.SvSampling(fake, None, None, 0, 0)) == 0

@@ -20,9 +20,19 @@ fixed-size chunks so that the bytes do not depend on the device's memory):
                  onehot: x = argmax(Lt + N(0, 1)) (greedy drafter);
                  greedy: x = argmax Lt with probability ``greedy_match``,
                          else a uniform draw from the other V - 1 ids.
+                 batch:  per request, by its own settings: temperature 0 ->
+                         x = argmax Ld (a greedy drafter); else a draw from
+                         the draft's temperature / top-k law as for prob (the
+                         drafter does not apply top-p; a draft outside the
+                         nucleus is a valid input that the verifier rejects).
+  batch settings (entry "batch") each request takes one of the workload's
+                 ``mix`` classes (temperature, top_k, top_p), uniformly, from
+                 a generator seeded with data_seed + 1.
 The five workloads mirror the shapes of the reference pages' setting scaled
 to a batch (gamma 3..8 as on the pages, temperatures 0 / 0.7 / 0.8 / 1,
-acceptance rates spanning the 0.5..0.9 range quoted for good drafter pairs).
+acceptance rates spanning the 0.5..0.9 range quoted for good drafter pairs);
+the batch workload mixes greedy, top-k, top-p and top-k + top-p requests on
+the fp32 shape of the third.
 """
 
 from __future__ import annotations
@@ -50,6 +60,7 @@ class Workload:
     data_seed: int = 0
     verify_seed: int = 42
     chunk: int = 8        # requests generated per generator call
+    mix: tuple = ()       # entry "batch": ((temperature, top_k, top_p), ...) request classes
 
     @property
     def torch_dtype(self):
@@ -65,12 +76,20 @@ class Workload:
 
     @property
     def draft_rows(self) -> int:
-        return self.B * self.G if self.entry == "prob" else 0
+        return self.B * self.G if self.entry in ("prob", "batch") else 0
+
+    @property
+    def has_draft_logits(self) -> bool:
+        return self.entry in ("prob", "batch")
 
     @property
     def logit_bytes(self) -> int:
-        """Bytes of every logit row read once: the algorithmic traffic."""
-        return (self.target_rows + self.draft_rows) * self.V * self.elem_bytes
+        """Bytes of every logit row read once: the algorithmic traffic (for a
+        batch workload the expected draft rows of its sampled requests)."""
+        drafts = self.draft_rows
+        if self.entry == "batch" and self.mix:
+            drafts = drafts * sum(1 for t, _, _ in self.mix if t > 0) / len(self.mix)
+        return int((self.target_rows + drafts) * self.V * self.elem_bytes)
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -94,6 +113,16 @@ WORKLOADS = {
                                                   "bf16", 0.7, 64, 3.0, (0.3, 2.5)),
 }
 
+# Per-request settings in one call (spec_verify_batch): greedy, top-k 50,
+# top-p 0.9, top-k 40 then top-p 0.95, a quarter each, on the fp32 shape of
+# prob_f32_b256_g7_v151936.
+BATCH_WORKLOADS = {
+    "batch_mixed_f32_b256_g7_v151936": Workload(
+        "batch_mixed_f32_b256_g7_v151936", "batch", 256, 7, 151936, "f32", 1.0, 0, 3.0, (0.5, 2.0),
+        mix=((0.0, 0, 1.0), (0.7, 50, 1.0), (1.0, 0, 0.9), (0.8, 40, 0.95))),
+}
+ALL_WORKLOADS = {**WORKLOADS, **BATCH_WORKLOADS}
+
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "prob_topk64_bf16_b1024_g8_v256000"
 
@@ -105,13 +134,26 @@ def _gumbel_argmax(scores: torch.Tensor, gen: torch.Generator) -> torch.Tensor:
     return torch.argmax(scores + g, dim=-1)
 
 
-def _draft_tokens_prob(ld: torch.Tensor, wl: Workload, gen: torch.Generator) -> torch.Tensor:
-    z = ld.float() / wl.temperature
-    if 0 < wl.top_k < wl.V:
+def _draft_tokens_prob(ld: torch.Tensor, temperature: float, top_k: int, gen: torch.Generator) -> torch.Tensor:
+    V = ld.shape[-1]
+    z = ld.float() / temperature
+    if 0 < top_k < V:
         vals, idx = torch.sort(z, dim=-1, descending=True, stable=True)
-        pick = _gumbel_argmax(vals[..., : wl.top_k], gen)
-        return torch.gather(idx[..., : wl.top_k], -1, pick.unsqueeze(-1)).squeeze(-1)
+        pick = _gumbel_argmax(vals[..., :top_k], gen)
+        return torch.gather(idx[..., :top_k], -1, pick.unsqueeze(-1)).squeeze(-1)
     return _gumbel_argmax(z, gen)
+
+
+def batch_settings(wl: Workload, device="cpu") -> dict:
+    """Per-request settings of a batch workload: temperature [B] float32,
+    top_k [B] int32, top_p [B] float32 (one mix class per request)."""
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(wl.data_seed + 1)
+    cls = torch.randint(0, len(wl.mix), (wl.B,), generator=gen)
+    t = torch.tensor([wl.mix[c][0] for c in cls.tolist()], dtype=torch.float32)
+    k = torch.tensor([wl.mix[c][1] for c in cls.tolist()], dtype=torch.int32)
+    p = torch.tensor([wl.mix[c][2] for c in cls.tolist()], dtype=torch.float32)
+    return {"temperature": t.to(device), "top_k": k.to(device), "top_p": p.to(device)}
 
 
 def generate(wl: Workload, device="cpu", requests: range | None = None) -> dict:
@@ -128,36 +170,51 @@ def generate(wl: Workload, device="cpu", requests: range | None = None) -> dict:
     lo_req, hi_req = (0, B) if requests is None else (requests.start, requests.stop)
     lt_all = torch.empty((hi_req - lo_req, G + 1, V), dtype=wl.torch_dtype, device=device)
     ld_all = (torch.empty((hi_req - lo_req, G, V), dtype=wl.torch_dtype, device=device)
-              if wl.entry == "prob" else None)
+              if wl.has_draft_logits else None)
     x_all = torch.empty((hi_req - lo_req, G), dtype=torch.int32, device=device)
+    settings = batch_settings(wl) if wl.entry == "batch" else None
     for c0 in range(0, B, wl.chunk):
         c1 = min(B, c0 + wl.chunk)
+        sub = None if settings is None else {k: v[c0:c1] for k, v in settings.items()}
         if c1 <= lo_req:
             # Draw and discard so that later chunks see the same stream.
-            _chunk(wl, c1 - c0, gen, device)
+            _chunk(wl, c1 - c0, gen, device, sub)
             continue
         if c0 >= hi_req:
             break
-        lt, ld, x = _chunk(wl, c1 - c0, gen, device)
+        lt, ld, x = _chunk(wl, c1 - c0, gen, device, sub)
         a, bnd = max(c0, lo_req), min(c1, hi_req)
         lt_all[a - lo_req: bnd - lo_req] = lt[a - c0: bnd - c0]
         if ld_all is not None:
             ld_all[a - lo_req: bnd - lo_req] = ld[a - c0: bnd - c0]
         x_all[a - lo_req: bnd - lo_req] = x[a - c0: bnd - c0]
-    return {"target_logits": lt_all, "draft_logits": ld_all, "draft_tokens": x_all}
+    res = {"target_logits": lt_all, "draft_logits": ld_all, "draft_tokens": x_all}
+    if settings is not None:
+        res.update({k: v[lo_req:hi_req].to(device) for k, v in settings.items()})
+    return res
 
 
-def _chunk(wl: Workload, c: int, gen: torch.Generator, device):
+def _chunk(wl: Workload, c: int, gen: torch.Generator, device, settings=None):
     G, V = wl.G, wl.V
     lt = (torch.randn((c, G + 1, V), generator=gen, device=device, dtype=torch.float32)
           * wl.target_sigma).to(wl.torch_dtype)
     ld = None
-    if wl.entry == "prob":
+    if wl.has_draft_logits:
         lo, hi = wl.draft_sigma
         sig = lo + (hi - lo) * torch.rand((c, 1, 1), generator=gen, device=device, dtype=torch.float32)
         noise = torch.randn((c, G, V), generator=gen, device=device, dtype=torch.float32)
         ld = (lt[:, :G].float() + sig * noise).to(wl.torch_dtype)
-        x = _draft_tokens_prob(ld, wl, gen)
+    if wl.entry == "batch":
+        xs = []
+        for r in range(c):
+            t, k = float(settings["temperature"][r]), int(settings["top_k"][r])
+            if t == 0.0:
+                xs.append(torch.argmax(ld[r].float(), dim=-1))
+            else:
+                xs.append(_draft_tokens_prob(ld[r], t, k, gen))
+        x = torch.stack(xs)
+    elif wl.entry == "prob":
+        x = _draft_tokens_prob(ld, wl.temperature, wl.top_k, gen)
     elif wl.entry == "onehot":
         noise = torch.randn((c, G, V), generator=gen, device=device, dtype=torch.float32)
         x = torch.argmax(lt[:, :G].float() + noise * wl.draft_sigma[0], dim=-1)
@@ -186,4 +243,5 @@ def to_host_arrays(t: torch.Tensor | None):
     raise TypeError(t.dtype)
 
 
-__all__ = ["Workload", "WORKLOADS", "WORKLOAD_ORDER", "HEADLINE", "generate", "to_host_arrays"]
+__all__ = ["Workload", "WORKLOADS", "BATCH_WORKLOADS", "ALL_WORKLOADS", "WORKLOAD_ORDER", "HEADLINE",
+           "generate", "batch_settings", "to_host_arrays"]
