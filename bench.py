@@ -62,11 +62,16 @@ def cpu_baseline(wl, inp, target_seconds: float) -> dict:
     def run(n):
         sub = slice(0, n)
         lt = workloads.to_host_arrays(inp["target_logits"][sub])
-        ld = workloads.to_host_arrays(inp["draft_logits"][sub]) if wl.entry == "prob" else None
+        ld = workloads.to_host_arrays(inp["draft_logits"][sub]) if wl.has_draft_logits else None
         x = workloads.to_host_arrays(inp["draft_tokens"][sub])
         t0 = time.perf_counter()
-        oracle.verify(modes[wl.entry], lt, ld, x, temperature=wl.temperature, top_k=wl.top_k,
-                      seed=wl.verify_seed)
+        if wl.entry == "batch":
+            oracle.verify_batch(lt, ld, x, inp["temperature"][sub].cpu().numpy(), inp["top_k"][sub].cpu().numpy(),
+                                inp["top_p"][sub].cpu().numpy(), max_top_k=max(k for _, k, _ in wl.mix),
+                                seed=wl.verify_seed)
+        else:
+            oracle.verify(modes[wl.entry], lt, ld, x, temperature=wl.temperature, top_k=wl.top_k,
+                          seed=wl.verify_seed)
         return time.perf_counter() - t0
 
     threads = oracle.max_threads()
@@ -108,7 +113,7 @@ def main():
     import workloads
 
     name = args.workload or workloads.HEADLINE
-    wl = workloads.WORKLOADS[name]
+    wl = workloads.ALL_WORKLOADS[name]
     dev = torch.device("cuda:0")
     sv.load_library()
     log(f"[bench] {name}: generating inputs on {torch.cuda.get_device_name(0)}")
@@ -116,7 +121,12 @@ def main():
     torch.cuda.synchronize()
 
     params = sv.make_params(wl.B, wl.G, wl.V, wl.torch_dtype, wl.temperature or 1.0, wl.top_k, wl.verify_seed)
-    ws = sv.alloc_workspace(params, dev)
+    sampling = None
+    if wl.entry == "batch":
+        sampling = sv.make_sampling(inp["temperature"], inp["top_k"], inp["top_p"], max(k for _, k, _ in wl.mix))
+        ws = torch.empty(sv.sv_workspace_bytes_batch(params, sampling), dtype=torch.uint8, device=dev)
+    else:
+        ws = sv.alloc_workspace(params, dev)
     B, G = wl.B, wl.G
     out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
@@ -131,6 +141,8 @@ def main():
             sv.spec_verify_prob(params, lt, ld, x, out, nacc, pd, qd, ws, stream)
         elif wl.entry == "onehot":
             sv.spec_verify_onehot(params, lt, x, out, nacc, pd, ws, stream)
+        elif wl.entry == "batch":
+            sv.spec_verify_batch(params, sampling, lt, ld, x, out, nacc, pd, qd, ws, stream)
         else:
             sv.spec_verify_greedy(params, lt, x, out, nacc, ta, ws, stream)
 
@@ -171,8 +183,11 @@ def main():
     positions = B * G
     rows = wl.target_rows + wl.draft_rows
     bytes_alg = wl.logit_bytes
-    row_avg_s = rows_ms / max(rows_n, 1) / 1e3
-    achieved = bytes_alg / row_avg_s / 1e9
+    # Row-pass time per step: one launch for the single-setting entries; the
+    # batch entry's row family (classify, top-k, softmax, argmax, nucleus
+    # kernels) is taken as a whole.
+    row_step_s = rows_ms / args.steps / 1e3
+    achieved = bytes_alg / row_step_s / 1e9
     traffic = load_traffic(name, bytes_alg)
     cpu = None
     if not args.no_cpu_baseline:
@@ -193,14 +208,17 @@ def main():
         "data": "synthetic (seeded, generated on the GPU; no dataset)",
         "config": {"workload": name, "entry": f"spec_verify_{wl.entry}", "batch": B, "gamma": G, "vocab": wl.V,
                    "logits": wl.dtype, "temperature": wl.temperature, "top_k": wl.top_k,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"mix (T, top_k, top_p)": [list(m) for m in wl.mix]} if wl.entry == "batch" else {})},
         "rows_per_s": rows / sec,
         "requests_per_s": B / sec,
         "algorithmic_gbps": bytes_alg / sec / 1e9,
         "hbm_fraction": bytes_alg / sec / 1e9 / HBM_PEAK_GBPS,
-        "kernels_ms_per_step": {"rows": rows_ms / max(rows_n, 1), "accept": acc_ms / max(acc_n, 1),
-                                "race": (race_ms / race_n) if race_n else 0.0},
-        "roofline": {"bound": "hbm", "kernel": "row pass (rows_topk_kernel)" if wl.top_k else "row pass",
+        "kernels_ms_per_step": {"rows": rows_ms / args.steps, "accept": acc_ms / args.steps,
+                                "race": race_ms / args.steps},
+        "roofline": {"bound": "hbm", "kernel": ("row pass (rows_topk_kernel)" if wl.top_k else
+                                                "row family (all row kernels of a step)" if wl.entry == "batch"
+                                                else "row pass"),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic},
         "cpu_baseline": cpu,

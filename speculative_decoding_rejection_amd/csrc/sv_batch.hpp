@@ -42,6 +42,44 @@ __device__ __forceinline__ double nucleus_mass(double lm, float l, double it) {
   return exp(((double)l - lm) * it);
 }
 
+// exp(x) for x <= 0 in fp64, table-driven (P. T. P. Tang, "Table-driven
+// implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989): x = (64 m + j) ln2 / 64 + r with
+// |r| <= ln2 / 128, so exp(x) = 2^m * 2^(j/64) * exp(r).  k = 64 m + j is
+// x * 64 / ln2 rounded to the nearest integer by adding 1.5 * 2^52 (the
+// integer lands in the low mantissa bits); ln2 / 64 is split into a 32-bit
+// head (k times it is exact for |k| < 2^21) and a tail; exp(r) - 1 is its
+// Taylor polynomial of degree 6 (truncation below 1e-19); the factor 2^m is
+// an add to the exponent field (the result stays normal for x > -700, and
+// below that the mass, under 1e-304 of the row maximum's, is taken as 0).
+// tab[j] = 2^(j/64).  *k_out = k: -k is the token's gap bin (ln2 / 64 nats
+// per bin), a non-decreasing function of the gap -x.
+constexpr double kNucInvStep = 0x1.71547652b82fep+6;  // 64 / ln2
+constexpr double kNucRound = 0x1.8p52;
+__device__ __forceinline__ int nucleus_k(double x) {
+  return __double2loint(fma(x, kNucInvStep, kNucRound));
+}
+__device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, int* k_out) {
+  if (!(x > -700.0)) {
+    *k_out = 1;  // no bin
+    return 0.0;
+  }
+  const double t = fma(x, kNucInvStep, kNucRound);
+  const double kd = t - kNucRound;
+  const int k = __double2loint(t);
+  *k_out = k;
+  double r = fma(-kd, 0x1.62e42fee00000p-7, x);  // head of ln2 / 64
+  r = fma(-kd, 0x1.a39ef35793c76p-39, r);         // tail
+  double q = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+  q = fma(r, q, 1.0 / 24.0);
+  q = fma(r, q, 1.0 / 6.0);
+  q = fma(r, q, 0.5);
+  q = fma(r, q, 1.0);
+  const double tj = tab[k & 63];
+  const double v = fma(tj, q * r, tj);  // 2^(j/64) exp(r), in [0.99, 1.01]
+  return __hiloint2double(__double2hiint(v) + (k >> 6) * (1 << 20), __double2loint(v));
+}
+
 // ===========================================================================
 // Classify pass: one workgroup reads the per-request settings, validates
 // them, and writes one ReqInfo per request.  An invalid request emits
@@ -141,14 +179,14 @@ __device__ __forceinline__ void block_sort_desc(uint64_t* a, int n) {
 // returns the first index t whose running mass A + e_0 + ... + e_t reaches
 // target, and that running mass in *zk.  If rounding leaves the target
 // unreached, the last index and the total.
-__device__ __forceinline__ int wave_walk(const uint64_t* a, int n, double A, double target, double lm, double it,
-                                         double* zk) {
+template <typename M>
+__device__ __forceinline__ int wave_walk(const uint64_t* a, int n, double A, double target, M&& mass, double* zk) {
   const int lane = lane_id();
   double base = A;
   for (int i0 = 0; i0 < n; i0 += kWave) {
     const int i = i0 + lane;
     const uint64_t k = i < n ? a[i] : 0ull;
-    const double e = k ? nucleus_mass(lm, key_value(k), it) : 0.0;
+    const double e = k ? mass(key_value(k)) : 0.0;
     const double inc = base + wave_incl_scan_d(e);
     const uint64_t hit = ballot(i < n && inc >= target);
     if (hit) {
@@ -193,7 +231,7 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
   }
   z = wave_sum_d(z);
   double zk;
-  const int t = wave_walk(ks, K, 0.0, (double)ri.top_p * z, lm, it, &zk);
+  const int t = wave_walk(ks, K, 0.0, (double)ri.top_p * z, [&](float l) { return nucleus_mass(lm, l, it); }, &zk);
   for (int i = lane; i < K; i += kWave) src[i] = i <= t ? ks[i] : 0ull;
 }
 
@@ -201,36 +239,37 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 // Nucleus of a full row (no top-k): one workgroup per row, after the softmax
 // row pass (whose partials give the row's largest logit).
 //
-//   pass 1  fp64 mass of every token; the total Z; a histogram of mass and
-//           count over bins of the gap d = (l_max - l) / T, 64 bins per nat
-//           over [0, 48).  Tokens further below the maximum carry less than
-//           2^31 e^-48 < 1e-11 of Z in total, so the cut (top_p <= 1 - 2^-24)
+//   pass 1  fp64 mass of every token; the total Z; a histogram of mass over
+//           bins of the gap d = (l_max - l) / T, ln2 / 64 nats per bin over
+//           [0, 41.6).  Tokens further below the maximum carry less than
+//           2^31 e^-41 < 4e-9 of Z in total, so the cut (top_p <= 1 - 2^-24)
 //           always falls inside the histogram.
 //   scan    the bin where the running mass reaches top_p * Z, and the mass A
 //           of the bins before it.
-//   pass 2  the bin's tokens are collected into LDS (at most kNucCap),
-//           sorted by key and walked from A: the first token that reaches
-//           top_p * Z is the cut.
+//   pass 2  the bin's tokens are collected into LDS (at most kNucCap; the
+//           histogram's storage), sorted by key and walked from A: the first
+//           token that reaches top_p * Z is the cut.
 //   refine  (a bin with more than kNucCap tokens, e.g. many equal logits)
 //           radix passes over the keys of that bin, 8 bits at a time below
 //           their common prefix, each keeping the digit that holds the cut,
 //           until at most kNucCap tokens remain.
 // Each pass streams the row from HBM.
 // ===========================================================================
-constexpr int kNucBinsPerNat = 64;
-constexpr int kNucNats = 48;
-constexpr int kNucBins = kNucBinsPerNat * kNucNats;  // 3072
+constexpr int kNucBins = 3840;  // ln2 / 64 nats each: gaps below 41.6 nats
 constexpr int kNucCap = 2048;
 
+// Gap bin of logit l (-1: none), from the same rounding as the mass.
 __device__ __forceinline__ int nucleus_bin(double lm, float l, double it) {
-  const double d = (lm - (double)l) * it;
-  return (d >= 0.0 && d < (double)kNucNats) ? (int)(d * (double)kNucBinsPerNat) : -1;
+  const double x = ((double)l - lm) * it;
+  if (!(x > -700.0)) return -1;
+  const int b = -nucleus_k(x);
+  return b < kNucBins ? b : -1;
 }
 
 // Calls f(logit, index) for every element of the row this thread owns.
 template <typename ET, int NT, typename F>
 __device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
-  constexpr int EPV = Elem<ET>::kPerVec, U = 2;
+  constexpr int EPV = Elem<ET>::kPerVec, U = 4;
   Slice<ET> sl(rp, 0, V);
   const int tid = threadIdx.x;
   if (tid < sl.nscalar()) {
@@ -267,12 +306,17 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
                                                            RowCut* __restrict__ cut) {
   constexpr int NT = 256, NW = NT / kWave, PER = kNucBins / NT;
   static_assert(kNucBins % NT == 0, "bins per thread");
+  static_assert(kNucCap * sizeof(uint64_t) <= kNucBins * sizeof(double), "keys alias the histogram");
   const int row = blockIdx.x;
   const ReqInfo ri = info[row_request(row, rows_t, G)];
   if (ri.kind != kReqFull || !(ri.top_p < 1.f)) return;  // uniform over the workgroup
+  // The gap histogram is dead once its bin is chosen; the collected keys of
+  // that bin then take its storage.
   __shared__ double hm[kNucBins];
-  __shared__ uint32_t hc[kNucBins];
-  __shared__ uint64_t keys[kNucCap];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(hm);
+  __shared__ double tab[64];
+  __shared__ double dm[256];
+  __shared__ uint32_t dc[256];
   __shared__ double red_d[NW], red_s[NW];
   __shared__ double incl_sh[NT];
   __shared__ uint64_t red_k[2][NW];
@@ -290,10 +334,13 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
   lmax = wave_max_f(lmax);
   const double lm = (double)lmax, it = 1.0 / (double)ri.T;
 
-  for (int i = tid; i < kNucBins; i += NT) {
-    hm[i] = 0.0;
-    hc[i] = 0u;
-  }
+  for (int i = tid; i < kNucBins; i += NT) hm[i] = 0.0;
+  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  // Every mass of this kernel: exp((l - lm) / T) by the table-driven exp.
+  auto mass = [&](float l) {
+    int k;
+    return exp_nonpos_f64(((double)l - lm) * it, tab, &k);
+  };
   if (tid == 0) {
     sh_bin = -1;
     sh_prefix = 0ull;  // fixed top bits of the cut key (refinement)
@@ -301,16 +348,14 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
   }
   __syncthreads();
 
-  // Pass 1: masses, Z and the gap histogram.
+  // Pass 1: masses, Z and the mass histogram of the gap.  The gap is the
+  // negated exponent, so mass and bin come from one product.
   double zt = 0.0;
   row_foreach<ET, NT>(rp, V, [&](float l, int) {
-    const double e = nucleus_mass(lm, l, it);
+    int k;
+    const double e = exp_nonpos_f64(((double)l - lm) * it, tab, &k);
     zt += e;
-    const int bin = nucleus_bin(lm, l, it);
-    if (bin >= 0) {
-      atomicAdd(&hm[bin], e);
-      atomicAdd(&hc[bin], 1u);
-    }
+    if (k <= 0 && k > -kNucBins) atomicAdd(&hm[-k], e);
   });
   zt = wave_sum_d(zt);
   if (lane == 0) red_d[w] = zt;
@@ -337,7 +382,7 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
       double pickA = start;
       for (int k = 0; k < PER; ++k) {
         const int bin = tid * PER + k;
-        if (hc[bin] == 0u) continue;
+        if (!(hm[bin] > 0.0)) continue;
         pick = bin;  // last non-empty bin so far: the choice if rounding leaves the target unreached
         pickA = cum;
         const double nxt = cum + hm[bin];
@@ -346,8 +391,8 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
       }
       sh_bin = pick;
       sh_A = pickA;
-      sh_cnt = pick >= 0 ? hc[pick] : 0u;
     }
+    if (tid == 0) sh_n = 0;
   }
   __syncthreads();
   const int bstar = sh_bin;
@@ -357,9 +402,24 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
     return;
   }
 
+  // Pass 2: collect the keys of the bin (at most kNucCap are kept; the count
+  // tells whether the bin needs refining).  filter_key: bin and key prefix.
+  auto collect = [&](int plen, uint64_t prefix) {
+    row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+      if (nucleus_bin(lm, l, it) != bstar) return;
+      const uint64_t k = make_key(l, (uint32_t)y);
+      if (plen > 0 && (plen == 64 ? k != prefix : (k >> (64 - plen)) != (prefix >> (64 - plen)))) return;
+      const int pos = atomicAdd(&sh_n, 1);
+      if (pos < kNucCap) keys[pos] = k;
+    });
+  };
+  collect(0, 0ull);
+  __syncthreads();
+
   // Refinement of an over-full bin: radix over the keys below their common
-  // prefix.
-  if (sh_cnt > (uint32_t)kNucCap) {
+  // prefix, 8 bits at a time, keeping the digit that holds the cut.
+  if (sh_n > kNucCap) {
+    if (tid == 0) sh_cnt = (uint32_t)sh_n;
     uint64_t kmin = ~0ull, kmax = 0ull;
     row_foreach<ET, NT>(rp, V, [&](float l, int y) {
       if (nucleus_bin(lm, l, it) == bstar) {
@@ -392,8 +452,8 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
       const int nb = 64 - plen < 8 ? 64 - plen : 8;
       const int shift = 64 - plen - nb;
       for (int i = tid; i < 256; i += NT) {
-        hm[i] = 0.0;
-        hc[i] = 0u;
+        dm[i] = 0.0;
+        dc[i] = 0u;
       }
       __syncthreads();
       row_foreach<ET, NT>(rp, V, [&](float l, int y) {
@@ -401,8 +461,8 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
         const uint64_t k = make_key(l, (uint32_t)y);
         if (plen > 0 && (k >> (64 - plen)) != (prefix >> (64 - plen))) return;
         const int dig = (int)((k >> shift) & ((1ull << nb) - 1ull));
-        atomicAdd(&hm[dig], nucleus_mass(lm, l, it));
-        atomicAdd(&hc[dig], 1u);
+        atomicAdd(&dm[dig], mass(l));
+        atomicAdd(&dc[dig], 1u);
       });
       __syncthreads();
       if (tid == 0) {
@@ -410,10 +470,10 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
         int pick = -1;
         double pickA = cum;
         for (int dig = (1 << nb) - 1; dig >= 0; --dig) {  // descending keys first
-          if (hc[dig] == 0u) continue;
+          if (dc[dig] == 0u) continue;
           pick = dig;
           pickA = cum;
-          const double nxt = cum + hm[dig];
+          const double nxt = cum + dm[dig];
           if (nxt >= target) break;
           cum = nxt;
         }
@@ -421,7 +481,7 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
           sh_prefix = prefix | ((uint64_t)pick << shift);
           sh_plen = plen + nb;
           sh_A = pickA;
-          sh_cnt = hc[pick];
+          sh_cnt = dc[pick];
         } else {
           sh_plen = 64;
           sh_cnt = 0u;
@@ -429,21 +489,13 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
       }
       __syncthreads();
     }
+    if (tid == 0) sh_n = 0;
+    __syncthreads();
+    collect(sh_plen, sh_prefix);
+    __syncthreads();
   }
 
-  // Pass 2: collect the tokens of the bin (and prefix), sort, walk.
-  const int plen = sh_plen;
-  const uint64_t prefix = sh_prefix;
-  if (tid == 0) sh_n = 0;
-  __syncthreads();
-  row_foreach<ET, NT>(rp, V, [&](float l, int y) {
-    if (nucleus_bin(lm, l, it) != bstar) return;
-    const uint64_t k = make_key(l, (uint32_t)y);
-    if (plen > 0 && (plen == 64 ? k != prefix : (k >> (64 - plen)) != (prefix >> (64 - plen)))) return;
-    const int pos = atomicAdd(&sh_n, 1);
-    if (pos < kNucCap) keys[pos] = k;
-  });
-  __syncthreads();
+  // Sort the collected keys and walk them from the mass of the bins above.
   const int n = sh_n < kNucCap ? sh_n : kNucCap;
   int n2 = 2;
   while (n2 < n) n2 <<= 1;
@@ -452,7 +504,7 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
   block_sort_desc<NT>(keys, n2);
   if (w == 0) {
     double zk;
-    const int t = n > 0 ? wave_walk(keys, n, sh_A, target, lm, it, &zk) : -1;
+    const int t = n > 0 ? wave_walk(keys, n, sh_A, target, mass, &zk) : -1;
     if (lane == 0) {
       if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / zk)};
       else cut[row] = RowCut{0ull, lmax, (float)(1.0 / Z)};
