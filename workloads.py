@@ -85,11 +85,11 @@ class Workload:
     @property
     def logit_bytes(self) -> int:
         """Bytes of every logit row read once: the algorithmic traffic (for a
-        batch workload the expected draft rows of its sampled requests)."""
+        batch workload, the draft rows of its sampled requests only)."""
         drafts = self.draft_rows
         if self.entry == "batch" and self.mix:
-            drafts = drafts * sum(1 for t, _, _ in self.mix if t > 0) / len(self.mix)
-        return int((self.target_rows + drafts) * self.V * self.elem_bytes)
+            drafts = int((batch_settings(self)["temperature"] > 0).sum()) * self.G
+        return (self.target_rows + drafts) * self.V * self.elem_bytes
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
