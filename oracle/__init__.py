@@ -72,9 +72,9 @@ def _load():
                                        ctypes.c_int, ctypes.c_double, ctypes.c_void_p,
                                        ctypes.POINTER(ctypes.c_double)]
     lib.sv_ref_row_probs_p.restype = ctypes.c_int
-    lib.sv_ref_verify_batch.argtypes = ([ctypes.c_int] * 5 + [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_uint64]
-                                        + [ctypes.c_void_p] * 14 + [ctypes.c_int])
-    lib.sv_ref_verify_batch.restype = ctypes.c_int
+    lib.sv_ref_verify_ex.argtypes = ([ctypes.c_int] * 5 + [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_uint64]
+                                     + [ctypes.c_void_p] * 16 + [ctypes.c_int])
+    lib.sv_ref_verify_ex.restype = ctypes.c_int
     lib.sv_ref_row_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
     lib.sv_ref_row_argmax.restype = ctypes.c_int
     lib.sv_ref_race.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
@@ -202,46 +202,77 @@ def verify(mode: int, target_logits, draft_logits, draft_tokens, *, temperature:
 
 
 def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, *, max_top_k: int = 1024,
-                 seed: int = 0, req_ids=None, diagnostics: bool = False, nthreads: int = 0) -> dict:
+                 seed: int = 0, req_ids=None, diagnostics: bool = False, nthreads: int = 0, draft_probs=None,
+                 lengths=None) -> dict:
     """Run the oracle with per-request settings.
 
-    draft_logits None: one-hot drafts.  temperature [n] float32 (0 = greedy
-    request), top_k [n] int32, top_p [n] float32; the values are taken at
-    the caller's fp32 / int32 precision.
+    Arrays are padded: target_logits [n, G+1, V], draft_logits [n, G, V]
+    (None: one-hot drafts), draft_probs [n, G, V] float32 (the drafter's
+    probabilities, used as given; replaces draft_logits), draft_tokens
+    [n, G]; lengths [n] (draft positions per request, 0..G; None: all G)
+    selects the rows and positions that exist.  temperature [n] float32 (0 =
+    greedy request), top_k [n] int32, top_p [n] float32, taken at the
+    caller's fp32 / int32 precision.  Per-position outputs are [n, G], NaN
+    after a request's length.
     """
     lib = _load()
     lt, dt = _logits_bytes(target_logits)
     n, G1, V = lt.shape
     G = G1 - 1
-    ld = None
-    if draft_logits is not None:
+    kind = 1
+    ld = qp = None
+    if draft_probs is not None:
+        kind = 2
+        qp = np.ascontiguousarray(draft_probs, dtype=np.float32)
+        if qp.shape != (n, G, V):
+            raise ValueError("draft probabilities must be [n, G, V]")
+    elif draft_logits is not None:
+        kind = 0
         ld, dt2 = _logits_bytes(draft_logits)
         if dt2 != dt or ld.shape != (n, G, V):
             raise ValueError("draft logits must match target dtype and be [n, G, V]")
     x = np.ascontiguousarray(draft_tokens, dtype=np.int32)
     if x.shape != (n, G):
         raise ValueError("draft tokens must be [n, G]")
+    g = np.full(n, G, dtype=np.int32) if lengths is None else np.ascontiguousarray(lengths, dtype=np.int32)
+    if g.shape != (n,) or (g < 0).any() or (g > G).any():
+        raise ValueError("lengths must be [n] in 0..G")
+    # Pack: request r keeps target rows 0..g_r and draft rows / tokens 0..g_r-1.
+    lt_p = np.ascontiguousarray(np.concatenate([lt[r, :g[r] + 1] for r in range(n)])) if n else lt.reshape(0, V)
+    ld_p = (np.ascontiguousarray(np.concatenate([ld[r, :g[r]] for r in range(n)])) if ld is not None else None)
+    qp_p = (np.ascontiguousarray(np.concatenate([qp[r, :g[r]] for r in range(n)])) if qp is not None else None)
+    x_p = np.ascontiguousarray(np.concatenate([x[r, :g[r]] for r in range(n)])) if n else x.reshape(0)
+    tot = int(g.sum())
     t = np.ascontiguousarray(temperature, dtype=np.float32).reshape(n)
     k = np.ascontiguousarray(top_k, dtype=np.int32).reshape(n)
     p = np.ascontiguousarray(top_p, dtype=np.float32).reshape(n)
     rid = None if req_ids is None else np.ascontiguousarray(req_ids, dtype=np.int32)
-    res = {"out_tokens": np.empty((n, G + 1), dtype=np.int32), "num_accepted": np.empty(n, dtype=np.int32),
-           "p_draft": np.empty((n, G), dtype=np.float64), "q_draft": np.empty((n, G), dtype=np.float64),
-           "bad_token": np.zeros(n, dtype=np.int32), "bad_param": np.zeros(n, dtype=np.int32),
-           "cut_margin": np.empty(n, dtype=np.float64), "greedy": t == 0.0}
+    out = np.empty((n, G + 1), dtype=np.int32)
+    nacc = np.empty(n, dtype=np.int32)
+    pd, qd = np.empty(tot, np.float64), np.empty(tot, np.float64)
+    bad, badp, cm = np.zeros(n, np.int32), np.zeros(n, np.int32), np.empty(n, np.float64)
     beta = am = rm = None
     if diagnostics:
-        beta = np.empty((n, G), dtype=np.float64)
-        am = np.empty((n, G), dtype=np.float64)
-        rm = np.empty(n, dtype=np.float64)
-        res["beta"], res["accept_margin"], res["race_margin"] = beta, am, rm
-    rc = lib.sv_ref_verify_batch(0 if ld is not None else 1, n, G, V, dt, _ptr(t), _ptr(k), _ptr(p),
-                                 int(max_top_k), int(seed), _ptr(lt), _ptr(ld), _ptr(x), _ptr(rid),
-                                 _ptr(res["out_tokens"]), _ptr(res["num_accepted"]), _ptr(res["p_draft"]),
-                                 _ptr(res["q_draft"]), _ptr(beta), _ptr(am), _ptr(rm), _ptr(res["cut_margin"]),
-                                 _ptr(res["bad_token"]), _ptr(res["bad_param"]), int(nthreads))
+        beta, am, rm = np.empty(tot, np.float64), np.empty(tot, np.float64), np.empty(n, np.float64)
+    rc = lib.sv_ref_verify_ex(kind, n, G, V, dt, _ptr(t), _ptr(k), _ptr(p), int(max_top_k), int(seed), _ptr(lt_p),
+                              _ptr(ld_p), _ptr(qp_p), _ptr(x_p), _ptr(g), _ptr(rid), _ptr(out), _ptr(nacc), _ptr(pd),
+                              _ptr(qd), _ptr(beta), _ptr(am), _ptr(rm), _ptr(cm), _ptr(bad), _ptr(badp),
+                              int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
+
+    def pad(v):
+        o = np.full((n, G), np.nan)
+        off = 0
+        for r in range(n):
+            o[r, :g[r]] = v[off:off + g[r]]
+            off += g[r]
+        return o
+
+    res = {"out_tokens": out, "num_accepted": nacc, "p_draft": pad(pd), "q_draft": pad(qd), "bad_token": bad,
+           "bad_param": badp, "cut_margin": cm, "greedy": t == 0.0, "lengths": g}
+    if diagnostics:
+        res["beta"], res["accept_margin"], res["race_margin"] = pad(beta), pad(am), rm
     return res
 
 

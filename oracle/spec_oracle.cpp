@@ -28,6 +28,10 @@
 //     renormalises over it;
 //   * a request with temperature 0 takes the greedy rule, and its p(x_j) is
 //     the temperature-0 law (1 on the target argmax, else 0) with q(x_j) = 1;
+//   * a draft given as probabilities (vLLM's draft_probs) is q as given: no
+//     temperature, top-k, top-p or renormalisation is applied to it;
+//   * a request with g draft positions (0 <= g <= gamma) uses target rows
+//     0..g and positions 0..g-1; its uniforms are those of the same (b, j).
 //   * every argmax and every race tie goes to the lowest index;
 //   * uniforms are Philox4x32-10 words mapped to (k53 + 1) * 2^-53 in (0, 1];
 //     accept stream counter (0, j, b, 0), race stream counter
@@ -249,7 +253,7 @@ int race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, do
   return best;
 }
 
-enum { MODE_PROB = 0, MODE_ONEHOT = 1, MODE_GREEDY = 2, MODE_NAIVE = 3 };
+enum { MODE_PROB = 0, MODE_ONEHOT = 1, MODE_GREEDY = 2, MODE_NAIVE = 3, MODE_PROBS = 4 };
 
 struct Problem {
   int mode, B, G, V, dtype, top_k;
@@ -262,7 +266,7 @@ struct Problem {
 // "드래프트가 제안하고 타깃이 판정한다").  Positions j = 0..G-1 carry draft
 // tokens; row G of the target is the bonus position.  Returns 1 if a draft
 // token was out of range, else 0.
-int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, const int32_t* X,
+int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, const float* Qp, const int32_t* X,
                int32_t* out, int32_t* n_out, double* p_draft, double* q_draft, int32_t* target_argmax,
                double* beta, double* acc_margin, double* race_margin, double* cut_margin = nullptr) {
   const int G = P.G, V = P.V;
@@ -298,7 +302,7 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
     return bad_token;
   }
 
-  const bool has_q = (P.mode == MODE_PROB || P.mode == MODE_NAIVE);
+  const bool has_q = (P.mode == MODE_PROB || P.mode == MODE_NAIVE || P.mode == MODE_PROBS);
   std::vector<std::vector<double>> p(G + 1), q(has_q ? G : 0);
   double cm = 1.0, cmj = 1.0;
   for (int j = 0; j <= G; ++j) {
@@ -306,6 +310,12 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
     cm = std::min(cm, cmj);
   }
   for (int j = 0; j < (has_q ? G : 0); ++j) {
+    if (P.mode == MODE_PROBS) {
+      // The drafter's probabilities, as given.
+      q[j].assign(V, 0.0);
+      for (int y = 0; y < V; ++y) q[j][y] = (double)Qp[(size_t)j * V + y];
+      continue;
+    }
     q[j] = row_probs(Ld + (size_t)j * row_bytes, P.dtype, V, P.T, P.top_k, P.top_p, &cmj);
     cm = std::min(cm, cmj);
   }
@@ -355,7 +365,7 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
 
   std::vector<double> w(V, 0.0);
   if (n < G) {
-    if (P.mode == MODE_PROB) {
+    if (P.mode == MODE_PROB || P.mode == MODE_PROBS) {
       // Residual norm(max(0, p - q)) ([P4] "왜 하필 max(p − q, 0)인가").
       double mass = 0.0;
       for (int y = 0; y < V; ++y) {
@@ -459,7 +469,7 @@ int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top
     uint32_t b = req_ids ? (uint32_t)req_ids[r] : (uint32_t)r;
     const char* lt = (const char*)Lt + (size_t)r * (G + 1) * row_bytes;
     const char* ld = Ld ? (const char*)Ld + (size_t)r * G * row_bytes : nullptr;
-    int bad = verify_one(P, b, lt, ld, X + (size_t)r * G, out_tokens + (size_t)r * (G + 1), num_accepted + r,
+    int bad = verify_one(P, b, lt, ld, nullptr, X + (size_t)r * G, out_tokens + (size_t)r * (G + 1), num_accepted + r,
                          p_draft ? p_draft + (size_t)r * G : nullptr, q_draft ? q_draft + (size_t)r * G : nullptr,
                          target_argmax ? target_argmax + (size_t)r * (G + 1) : nullptr,
                          beta ? beta + (size_t)r * G : nullptr, acc_margin ? acc_margin + (size_t)r * G : nullptr,
@@ -469,8 +479,15 @@ int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top
   return 0;
 }
 
-// Batched verifier with per-request sampling settings.
-//   draft_mode: 0 prob (Ld: [nreq][G][V]), 1 onehot (Ld unused)
+// Batched verifier with per-request settings and ragged draft lengths.
+//   draft_kind: 0 draft logits (Ld, rows like Lt), 1 one-hot drafts (Ld
+//   unused), 2 draft probabilities (Qp: fp32 rows, q as given).
+//   lengths[r]: draft positions of request r, 0..G (NULL: all G).  Rows are
+//   packed request after request: request r's g_r + 1 target rows start at
+//   row sum_{r' < r} (g_r' + 1), its g_r draft rows (logits or
+//   probabilities), draft tokens and p_draft / q_draft / beta / acc_margin
+//   entries at sum_{r' < r} g_r'.  out_tokens is [nreq][G+1], -1 after the
+//   emitted token.
 //   T[r]: temperature, 0 = greedy request; K[r]: top-k (0 or >= V: off);
 //   P[r]: top-p in (0, 1], 1 = off; all three as the caller's fp32 / int32.
 //   max_top_k: a top_k in (max_top_k, V) makes the request invalid.
@@ -481,14 +498,23 @@ int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top
 //   argmax of row j else 0, q_draft[j] = 1.
 //   cut_margin [nreq]: the smallest top-p boundary margin over the request's
 //   rows (1 without top-p).  Other arguments as sv_ref_verify.
-int sv_ref_verify_batch(int draft_mode, int nreq, int G, int V, int dtype, const float* T, const int32_t* K,
-                        const float* Pp, int max_top_k, uint64_t seed, const void* Lt, const void* Ld,
-                        const int32_t* X, const int32_t* req_ids, int32_t* out_tokens, int32_t* num_accepted,
-                        double* p_draft, double* q_draft, double* beta, double* acc_margin, double* race_margin,
-                        double* cut_margin, int32_t* bad_token, int32_t* bad_param, int nthreads) {
-  if (nreq < 0 || G < 1 || V < 1 || (dtype != 0 && dtype != 1) || (draft_mode != 0 && draft_mode != 1)) return -1;
+int sv_ref_verify_ex(int draft_kind, int nreq, int G, int V, int dtype, const float* T, const int32_t* K,
+                     const float* Pp, int max_top_k, uint64_t seed, const void* Lt, const void* Ld, const float* Qp,
+                     const int32_t* X, const int32_t* lengths, const int32_t* req_ids, int32_t* out_tokens,
+                     int32_t* num_accepted, double* p_draft, double* q_draft, double* beta, double* acc_margin,
+                     double* race_margin, double* cut_margin, int32_t* bad_token, int32_t* bad_param,
+                     int nthreads) {
+  if (nreq < 0 || G < 0 || V < 1 || (dtype != 0 && dtype != 1) || draft_kind < 0 || draft_kind > 2) return -1;
   if (!Lt || !X || !out_tokens || !num_accepted || !T || !K || !Pp) return -1;
-  if (draft_mode == MODE_PROB && !Ld) return -1;
+  if (draft_kind == 0 && !Ld) return -1;
+  if (draft_kind == 2 && !Qp) return -1;
+  const int mode = draft_kind == 0 ? MODE_PROB : (draft_kind == 1 ? MODE_ONEHOT : MODE_PROBS);
+  std::vector<size_t> d0(nreq + 1, 0);  // packed draft offset of each request
+  for (int r = 0; r < nreq; ++r) {
+    const int g = lengths ? lengths[r] : G;
+    if (g < 0 || g > G) return -1;
+    d0[r + 1] = d0[r] + (size_t)g;
+  }
   const size_t row_bytes = (size_t)V * elem_bytes(dtype);
 #ifdef _OPENMP
   if (nthreads > 0) omp_set_num_threads(nthreads);
@@ -496,42 +522,45 @@ int sv_ref_verify_batch(int draft_mode, int nreq, int G, int V, int dtype, const
 #endif
   for (int r = 0; r < nreq; ++r) {
     const uint32_t b = req_ids ? (uint32_t)req_ids[r] : (uint32_t)r;
+    const int g = (int)(d0[r + 1] - d0[r]);
+    const size_t t0 = d0[r] + (size_t)r;  // first target row
     const double t = (double)T[r], pp = (double)Pp[r];
     const int k = K[r];
     const bool ok = std::isfinite(t) && t >= 0.0 && k >= 0 && (k >= V || k <= max_top_k) && pp > 0.0 &&
                     pp <= 1.0;
     int32_t* o = out_tokens + (size_t)r * (G + 1);
-    double* pd = p_draft ? p_draft + (size_t)r * G : nullptr;
-    double* qd = q_draft ? q_draft + (size_t)r * G : nullptr;
+    double* pd = p_draft ? p_draft + d0[r] : nullptr;
+    double* qd = q_draft ? q_draft + d0[r] : nullptr;
+    for (int j = 0; j <= G; ++j) o[j] = -1;
     if (bad_param) bad_param[r] = ok ? 0 : 1;
     if (cut_margin) cut_margin[r] = 1.0;
     if (race_margin) race_margin[r] = 1.0;
     if (acc_margin)
-      for (int j = 0; j < G; ++j) acc_margin[(size_t)r * G + j] = 1.0;
+      for (int j = 0; j < g; ++j) acc_margin[d0[r] + j] = 1.0;
     if (!ok) {
-      for (int j = 0; j <= G; ++j) o[j] = -1;
       num_accepted[r] = 0;
-      for (int j = 0; j < G; ++j) {
+      for (int j = 0; j < g; ++j) {
         if (pd) pd[j] = 0.0;
         if (qd) qd[j] = 0.0;
       }
       if (bad_token) bad_token[r] = 0;
       continue;
     }
-    const char* lt = (const char*)Lt + (size_t)r * (G + 1) * row_bytes;
-    const char* ld = (draft_mode == MODE_PROB) ? (const char*)Ld + (size_t)r * G * row_bytes : nullptr;
-    const int32_t* x = X + (size_t)r * G;
-    Problem P{t == 0.0 ? (int)MODE_GREEDY : draft_mode, nreq, G, V, dtype, k, t, seed, pp};
-    std::vector<int32_t> targ(G + 1);
-    int bad = verify_one(P, b, lt, ld, x, o, num_accepted + r, pd, qd, targ.data(),
-                         beta ? beta + (size_t)r * G : nullptr, acc_margin ? acc_margin + (size_t)r * G : nullptr,
+    const char* lt = (const char*)Lt + t0 * row_bytes;
+    const char* ld = (draft_kind == 0) ? (const char*)Ld + d0[r] * row_bytes : nullptr;
+    const float* qp = (draft_kind == 2) ? Qp + d0[r] * (size_t)V : nullptr;
+    const int32_t* x = X + d0[r];
+    Problem P{t == 0.0 ? (int)MODE_GREEDY : mode, nreq, g, V, dtype, k, t, seed, pp};
+    std::vector<int32_t> targ(g + 1);
+    int bad = verify_one(P, b, lt, ld, qp, x, o, num_accepted + r, pd, qd, targ.data(),
+                         beta ? beta + d0[r] : nullptr, acc_margin ? acc_margin + d0[r] : nullptr,
                          race_margin ? race_margin + r : nullptr, cut_margin ? cut_margin + r : nullptr);
     if (P.mode == MODE_GREEDY) {
       // The temperature-0 law is one-hot on the target argmax.
-      for (int j = 0; j < G; ++j) {
+      for (int j = 0; j < g; ++j) {
         if (pd) pd[j] = (x[j] == targ[j]) ? 1.0 : 0.0;
         if (qd) qd[j] = 1.0;
-        if (beta) beta[(size_t)r * G + j] = (x[j] == targ[j]) ? 1.0 : 0.0;
+        if (beta) beta[d0[r] + j] = (x[j] == targ[j]) ? 1.0 : 0.0;
       }
     }
     if (bad_token) bad_token[r] = bad;

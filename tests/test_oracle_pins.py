@@ -793,3 +793,88 @@ def test_batch_invalid_settings_emit_nothing():
     P[4:] = 1.0
     res = oracle.verify_batch(lt, ld, x, T, K, P, max_top_k=20, seed=1)
     assert res["bad_param"].tolist() == [0] * 6
+
+
+# ---------------------------------------------------------------------------
+# Draft given as probabilities; ragged draft lengths
+# ---------------------------------------------------------------------------
+
+def test_brute_force_draft_probabilities():
+    """q given as probabilities (zeros included, not a softmax of anything):
+    the exact outcome law, its losslessness identities, and the oracle's
+    empirical law."""
+    lt = _logits([[0.5, 0.0, 0.3, 0.2], [0.1, 0.6, 0.3, 0.0], [0.25, 0.25, 0.25, 0.25]])
+    q = np.array([[0.0, 0.5, 0.25, 0.25], [0.5, 0.25, 0.0, 0.25]], dtype=np.float32)
+    G, V, n_runs = 2, 4, 100_000
+    p = np.stack([oracle.row_probs(lt[j], 1.0) for j in range(G + 1)])
+    law = _exact_outcome_law(p, q.astype(np.float64), "prob")
+    beta = [np.minimum(p[j], q[j]).sum() for j in range(G)]
+    for j in range(G + 1):
+        marg = np.zeros(V)
+        for (k, toks), pr in law.items():
+            if k >= j:
+                marg[toks[j]] += pr
+        np.testing.assert_allclose(marg, np.prod(beta[:j]) * p[j], atol=1e-12)
+    rng = np.random.default_rng(29)
+    x = np.stack([rng.choice(V, size=n_runs, p=q[j].astype(np.float64)) for j in range(G)], axis=1).astype(np.int32)
+    res = oracle.verify_batch(np.broadcast_to(lt[None], (n_runs,) + lt.shape).copy(), None, x,
+                              np.ones(n_runs, np.float32), np.zeros(n_runs, np.int32), np.ones(n_runs, np.float32),
+                              draft_probs=np.broadcast_to(q[None], (n_runs, G, V)).copy(), seed=13)
+    np.testing.assert_array_equal(res["q_draft"], q[np.arange(G)[None, :], x])
+    keys = list(law)
+    index = {k: i for i, k in enumerate(keys)}
+    counts = np.zeros(len(keys))
+    for r in range(n_runs):
+        k = int(res["num_accepted"][r])
+        counts[index[(k, tuple(int(t) for t in res["out_tokens"][r, :k + 1]))]] += 1
+    expected = np.array([law[k] for k in keys]) * n_runs
+    big = expected >= 5
+    assert stats.chisquare(counts[big], expected[big] * counts[big].sum() / expected[big].sum()).pvalue > 1e-6
+
+
+def test_one_hot_probabilities_equal_onehot_drafts():
+    """q = 1 at the draft token, 0 elsewhere, given as probabilities, is the
+    one-hot rule exactly: accept iff u <= p(x), residual p with x masked."""
+    rng = np.random.default_rng(37)
+    n, G, V = 40, 4, 30
+    lt, ld, x, T, K, P = _mixed_case(rng, n, G, V)
+    T[T == 0] = 0.9
+    q = np.zeros((n, G, V), np.float32)
+    q[np.arange(n)[:, None], np.arange(G)[None, :], x] = 1.0
+    a = oracle.verify_batch(lt, None, x, T, K, P, draft_probs=q, seed=3)
+    b = oracle.verify_batch(lt, None, x, T, K, P, seed=3)
+    for key in ("out_tokens", "num_accepted", "p_draft", "q_draft"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_ragged_lengths_reduce_to_single_requests():
+    """A request with g of gamma draft positions gives exactly what a call
+    with gamma = g gives (its own uniforms); padding after it is -1."""
+    rng = np.random.default_rng(53)
+    n, G, V = 24, 5, 40
+    lt, ld, x, T, K, P = _mixed_case(rng, n, G, V)
+    g = rng.integers(0, G + 1, size=n).astype(np.int32)
+    g[:3] = [0, G, 1]
+    for draft in ("logits", "onehot"):
+        res = oracle.verify_batch(lt, ld if draft == "logits" else None, x, T, K, P, lengths=g, seed=21)
+        for r in range(n):
+            one = oracle.verify_batch(lt[r:r + 1, :g[r] + 1], ld[r:r + 1, :g[r]] if draft == "logits" else None,
+                                      x[r:r + 1, :g[r]], T[r:r + 1], K[r:r + 1], P[r:r + 1], seed=21, req_ids=[r])
+            assert res["num_accepted"][r] == one["num_accepted"][0]
+            np.testing.assert_array_equal(res["out_tokens"][r, :g[r] + 1], one["out_tokens"][0])
+            assert (res["out_tokens"][r, g[r] + 1:] == -1).all()
+            np.testing.assert_array_equal(res["p_draft"][r, :g[r]], one["p_draft"][0])
+            assert np.isnan(res["p_draft"][r, g[r]:]).all()
+
+
+def test_zero_draft_positions_emit_a_draw_from_p0():
+    """g = 0: nothing to verify, the one emitted token is the bonus draw from
+    p_0 (chi-square over many requests of one row)."""
+    lt = _logits([[0.5, 0.3, 0.15, 0.05], [0.25, 0.25, 0.25, 0.25]])
+    n = 50_000
+    res = oracle.verify_batch(np.broadcast_to(lt[None], (n, 2, 4)).copy(), None, np.zeros((n, 1), np.int32),
+                              np.ones(n, np.float32), np.zeros(n, np.int32), np.ones(n, np.float32),
+                              lengths=np.zeros(n, np.int32), seed=8)
+    assert (res["num_accepted"] == 0).all() and (res["out_tokens"][:, 1] == -1).all()
+    counts = np.bincount(res["out_tokens"][:, 0], minlength=4)
+    assert stats.chisquare(counts, np.array([0.5, 0.3, 0.15, 0.05]) * n).pvalue > 1e-6
