@@ -142,7 +142,7 @@ def main():
         elif wl.entry == "onehot":
             sv.spec_verify_onehot(params, lt, x, out, nacc, pd, ws, stream)
         elif wl.entry == "batch":
-            sv.spec_verify_batch(params, sampling, lt, ld, x, out, nacc, pd, qd, ws, stream)
+            sv.spec_verify_batch(params, sampling, None, lt, ld, x, out, nacc, pd, qd, ws, stream)
         else:
             sv.spec_verify_greedy(params, lt, x, out, nacc, ta, ws, stream)
 

@@ -116,6 +116,34 @@ sv_status spec_verify_greedy(const sv_params* params, const void* target_logits,
                              int32_t* out_tokens, int32_t* num_accepted, int32_t* target_argmax,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Form of the draft in spec_verify_batch. */
+typedef enum {
+  SV_DRAFT_LOGITS = 0, /* draft logits, same dtype and rules as the target's */
+  SV_DRAFT_ONEHOT = 1, /* no draft rows: a greedy drafter, q one-hot at x_j */
+  SV_DRAFT_PROBS = 2   /* fp32 draft probabilities q, used as given (vLLM's
+                          "probabilistic" draft_probs): no temperature, top-k,
+                          top-p or renormalisation is applied to them */
+} sv_draft_kind;
+
+/* Where the rows of a spec_verify_batch call live.  Strides are in elements
+ * (0 = vocab; otherwise >= vocab, e.g. a vocabulary padded for the LM head).
+ * cu_draft (DEVICE array [B+1], may be NULL): request b owns draft positions
+ * cu_draft[b] .. cu_draft[b+1]-1, g_b of them, 0 <= g_b <= gamma, with
+ * cu_draft[0] = 0 (vLLM's cu_num_draft_tokens).  Rows are then packed:
+ * request b's g_b + 1 target rows start at row cu_draft[b] + b; its g_b
+ * draft rows, draft tokens and p_draft / q_draft entries at cu_draft[b].
+ * out_tokens stays [B][gamma+1].  With cu_draft NULL every request has gamma
+ * positions, rows [B][gamma+1] and [B][gamma].  A cu_draft array that breaks
+ * these rules makes every request invalid: out_tokens -1, num_accepted 0,
+ * p_draft / q_draft not written, error bit 4. */
+typedef struct {
+  int32_t draft_kind;      /* sv_draft_kind */
+  int32_t reserved;        /* 0 */
+  int64_t target_stride;
+  int64_t draft_stride;
+  const int32_t* cu_draft;
+} sv_layout;
+
 /* Per-request sampling settings of spec_verify_batch: DEVICE arrays of
  * length batch, owned by the caller and read by the kernels (the host never
  * reads them).  The adjusted laws are temperature, then top-k, then top-p,
@@ -145,33 +173,41 @@ typedef struct {
 } sv_sampling;
 
 /* Workspace bytes of spec_verify_batch for these parameters (0 if invalid).
- * params->temperature and params->top_k are not used. */
+ * With sampling != NULL, params->temperature and params->top_k are not
+ * used. */
 size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* sampling);
 
 /* Verification with per-request settings: greedy, top-k, top-p and plain
  * requests mixed in one call (vLLM's rejection sampler takes such a batch,
- * same section).  Sampled requests follow spec_verify_prob (draft_logits not
- * NULL) or spec_verify_onehot (draft_logits NULL) with their own T, top-k and
- * top-p, and draw from the same Philox streams (keyed by params->seed): a
- * batch whose requests all share one setting gives bit-identical results to
- * the single-setting entry point.  Greedy requests follow spec_verify_greedy;
- * for them p_draft[b][j] is the temperature-0 law (1 if x_j is the target
- * argmax, else 0) and q_draft[b][j] = 1.  Draft rows of greedy requests are
- * not read.  q_draft (may be NULL) is 1 for valid one-hot drafts.
- *   params: batch, gamma, vocab, dtype, seed (temperature, top_k unused)
- *   target_logits [B][G+1][V], draft_logits [B][G][V] or NULL,
- *   draft_tokens [B][G], out_tokens [B][G+1], num_accepted [B],
- *   p_draft, q_draft [B][G] (may be NULL).
+ * same section), any draft form, dense or ragged rows.  Sampled requests
+ * follow spec_verify_prob (draft logits), spec_verify_onehot (no draft rows)
+ * or, with draft probabilities, the same test and residual with q as given,
+ * each with its own T, top-k and top-p on the target (and on draft logits);
+ * they draw from the same Philox streams (keyed by params->seed and the
+ * request's (b, j)): a dense batch whose requests all share one setting
+ * gives bit-identical results to the single-setting entry point.  Greedy
+ * requests follow spec_verify_greedy; for them p_draft is the temperature-0
+ * law (1 if x_j is the target argmax, else 0) and q_draft = 1.  Draft rows
+ * of greedy requests are not read.  q_draft is 1 for valid one-hot drafts.
+ *   params: batch, gamma (the largest draft length), vocab, dtype, seed;
+ *           with sampling == NULL also the one temperature (0: greedy) and
+ *           top_k of every request (top-p off)
+ *   sampling: per-request settings, or NULL
+ *   layout: draft form, strides, ragged offsets; NULL = dense rows with
+ *           draft logits if `draft` is not NULL, else one-hot drafts
+ *   target_logits, draft (logits or fp32 probabilities; NULL for one-hot),
+ *   draft_tokens, p_draft, q_draft (may be NULL): as described by layout;
+ *   out_tokens [B][G+1] (-1 after the emitted token), num_accepted [B].
  * Workspace: sv_workspace_bytes_batch(params, sampling) bytes. */
-sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const void* target_logits,
-                            const void* draft_logits, const int32_t* draft_tokens, int32_t* out_tokens,
-                            int32_t* num_accepted, float* p_draft, float* q_draft, void* workspace,
-                            size_t workspace_bytes, void* stream);
+sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const sv_layout* layout,
+                            const void* target_logits, const void* draft, const int32_t* draft_tokens,
+                            int32_t* out_tokens, int32_t* num_accepted, float* p_draft, float* q_draft,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronises `stream`, then copies the sticky device error word of the
  * last call that used `workspace` to *host_code: bit 0 (1) = a draft token
  * was out of range; bit 1 (2) = a request of spec_verify_batch had invalid
- * settings. */
+ * settings; bit 2 (4) = its cu_draft array broke the layout rules. */
 sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream);
 
 /* Per-kernel timing for measurement.  While enabled, every launch of the

@@ -89,19 +89,23 @@ def compare_batch(got: dict, ref: dict, prob_tol: float = 1e-5, tie: float = 1e-
         same = (n_g[r] == n_r[r]) and bool((out_g[r] == out_r[r]).all())
         if ref["bad_param"][r]:
             rep["invalid_requests"] += 1
-            if not same or (pd_g[r] != 0).any() or (qd_g[r] != 0).any():
+            g = int(ref["lengths"][r]) if "lengths" in ref else pd_g.shape[1]
+            if not same or (pd_g[r, :g] != 0).any() or (qd_g[r, :g] != 0).any():
                 fail(r)
             continue
         if ref["greedy"][r]:
             rep["greedy_requests"] += 1
-            if not same or (pd_g[r] != ref["p_draft"][r]).any() or (qd_g[r] != ref["q_draft"][r]).any():
+            g = int(ref["lengths"][r]) if "lengths" in ref else pd_g.shape[1]
+            if not same or (pd_g[r, :g] != ref["p_draft"][r, :g]).any() or (qd_g[r, :g] != ref["q_draft"][r, :g]).any():
                 fail(r)
             continue
         if ref["cut_margin"][r] < cut_tol:
             rep["near_cut_requests"] += 1
             continue
-        rep["max_dp"] = max(rep["max_dp"], float(np.max(np.abs(pd_g[r] - ref["p_draft"][r]))))
-        rep["max_dq"] = max(rep["max_dq"], float(np.max(np.abs(qd_g[r] - ref["q_draft"][r]))))
+        g = int(ref["lengths"][r]) if "lengths" in ref else pd_g.shape[1]
+        if g:
+            rep["max_dp"] = max(rep["max_dp"], float(np.max(np.abs(pd_g[r, :g] - ref["p_draft"][r, :g]))))
+            rep["max_dq"] = max(rep["max_dq"], float(np.max(np.abs(qd_g[r, :g] - ref["q_draft"][r, :g]))))
         if pos[r] >= 0:
             rep["near_tie_requests"] += 1
         if same:

@@ -27,6 +27,7 @@ LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_PKG, "libspecverify
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED = range(6)
 SV_F32, SV_BF16 = 0, 1
+SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT, SV_DRAFT_PROBS = 0, 1, 2
 FAMILY_ROWS, FAMILY_ACCEPT, FAMILY_RACE = 0, 1, 2
 
 
@@ -49,6 +50,16 @@ class SvSampling(ctypes.Structure):
         ("top_p", ctypes.c_void_p),
         ("max_top_k", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
+    ]
+
+
+class SvLayout(ctypes.Structure):
+    _fields_ = [
+        ("draft_kind", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("target_stride", ctypes.c_int64),
+        ("draft_stride", ctypes.c_int64),
+        ("cu_draft", ctypes.c_void_p),
     ]
 
 
@@ -85,7 +96,8 @@ def load_library():
     ps = ctypes.POINTER(SvSampling)
     lib.sv_workspace_bytes_batch.argtypes = [pp, ps]
     lib.sv_workspace_bytes_batch.restype = sz
-    lib.spec_verify_batch.argtypes = [pp, ps, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    pl_ = ctypes.POINTER(SvLayout)
+    lib.spec_verify_batch.argtypes = [pp, ps, pl_, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_batch.restype = ctypes.c_int
     lib.sv_read_device_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
     lib.sv_read_device_error.restype = ctypes.c_int
@@ -176,16 +188,19 @@ def make_sampling(temperature, top_k=None, top_p=None, max_top_k: int = 0) -> Sv
                       int(max_top_k), 0)
 
 
-def sv_workspace_bytes_batch(params: SvParams, sampling: SvSampling) -> int:
-    return int(load_library().sv_workspace_bytes_batch(ctypes.byref(params), ctypes.byref(sampling)))
+def sv_workspace_bytes_batch(params: SvParams, sampling) -> int:
+    return int(load_library().sv_workspace_bytes_batch(ctypes.byref(params),
+                                                       ctypes.byref(sampling) if sampling else None))
 
 
-def spec_verify_batch(params, sampling, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted,
+def spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, out_tokens, num_accepted,
                       p_draft, q_draft, workspace, stream=None):
-    st = load_library().spec_verify_batch(ctypes.byref(params), ctypes.byref(sampling), _ptr(target_logits),
-                                          _ptr(draft_logits), _ptr(draft_tokens), _ptr(out_tokens),
-                                          _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft), _ptr(workspace),
-                                          workspace.numel(), _stream(stream))
+    """sampling (SvSampling) and layout (SvLayout) may be None."""
+    st = load_library().spec_verify_batch(ctypes.byref(params), ctypes.byref(sampling) if sampling else None,
+                                          ctypes.byref(layout) if layout else None, _ptr(target_logits),
+                                          _ptr(draft), _ptr(draft_tokens), _ptr(out_tokens), _ptr(num_accepted),
+                                          _ptr(p_draft), _ptr(q_draft), _ptr(workspace), workspace.numel(),
+                                          _stream(stream))
     _check(st, "spec_verify_batch")
 
 
@@ -250,26 +265,49 @@ def verify(entry: str, target_logits, draft_tokens, draft_logits=None, *, temper
     return res
 
 
-def verify_batch(target_logits, draft_tokens, draft_logits=None, *, temperature, top_k=None, top_p=None,
-                 max_top_k=None, seed=0, workspace=None, stream=None) -> dict:
+def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, top_k=None, top_p=None,
+                 max_top_k=None, seed=0, draft_kind=None, cu_draft=None, gamma=None, vocab=None,
+                 single_temperature=1.0, single_top_k=0, workspace=None, stream=None) -> dict:
     """Allocates outputs (and a workspace if none is given) and runs
-    spec_verify_batch.  temperature [B] float32, top_k [B] int32 or None,
-    top_p [B] float32 or None, all on the GPU.  max_top_k defaults to 1024
-    when top_k is given (it only sizes the workspace and kernels)."""
-    B, G1, V = target_logits.shape
-    G = G1 - 1
+    spec_verify_batch.
+
+    Dense: target_logits [B, G+1, W], draft [B, G, W] (logits, or float32
+    probabilities with draft_kind SV_DRAFT_PROBS; None: one-hot drafts),
+    draft_tokens [B, G].  Ragged (cu_draft [B+1] int32 given, gamma = the
+    largest draft length): target_logits [sum(g_b + 1), W], draft
+    [sum(g_b), W], draft_tokens [sum(g_b)].  W is the row stride; vocab
+    (default W) the number of valid logits per row.  temperature / top_k /
+    top_p: [B] device tensors (float32 / int32 / float32), or temperature
+    None for one setting for every request (single_temperature,
+    single_top_k).  max_top_k defaults to 1024 when top_k is given."""
     dev = target_logits.device
-    if max_top_k is None:
-        max_top_k = 1024 if top_k is not None else 0
-    params = make_params(B, G, V, target_logits.dtype, 1.0, 0, seed)
-    sampling = make_sampling(temperature, top_k, top_p, max_top_k)
+    W = target_logits.shape[-1]
+    V = int(vocab) if vocab is not None else W
+    if cu_draft is not None:
+        B = cu_draft.shape[0] - 1
+        G = int(gamma)
+        tok_shape = draft_tokens.shape
+    else:
+        B, G1, _ = target_logits.shape
+        G = G1 - 1
+        tok_shape = (B, G)
+    if draft_kind is None:
+        draft_kind = SV_DRAFT_ONEHOT if draft is None else SV_DRAFT_LOGITS
+    dW = draft.shape[-1] if draft is not None else 0
+    layout = SvLayout(int(draft_kind), 0, W, dW, _ptr(cu_draft))
+    sampling = None
+    if temperature is not None:
+        if max_top_k is None:
+            max_top_k = 1024 if top_k is not None else 0
+        sampling = make_sampling(temperature, top_k, top_p, max_top_k)
+    params = make_params(B, G, V, target_logits.dtype, single_temperature, single_top_k, seed)
     nbytes = sv_workspace_bytes_batch(params, sampling)
     if nbytes == 0:
         raise SpecVerifyError(SV_ERR_INVALID_ARG, "sv_workspace_bytes_batch")
     ws = workspace if workspace is not None else torch.empty(nbytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    pd = torch.empty((B, G), dtype=torch.float32, device=dev)
-    qd = torch.empty((B, G), dtype=torch.float32, device=dev)
-    spec_verify_batch(params, sampling, target_logits, draft_logits, draft_tokens, out, nacc, pd, qd, ws, stream)
+    pd = torch.empty(tok_shape, dtype=torch.float32, device=dev)
+    qd = torch.empty(tok_shape, dtype=torch.float32, device=dev)
+    spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, out, nacc, pd, qd, ws, stream)
     return {"out_tokens": out, "num_accepted": nacc, "p_draft": pd, "q_draft": qd, "workspace": ws}

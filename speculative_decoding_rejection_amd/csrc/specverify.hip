@@ -39,6 +39,7 @@ struct Plan {
   int S, seg;     // row-pass splits of the vocabulary (softmax / argmax)
   int Sr, segr;   // race-pass splits
   size_t off_err, off_part, off_cand, off_desc, off_slots, off_info, off_cut, total;
+  sv::Layout L;   // rows, tokens, outputs (dense: rows V apart, every request G positions)
 };
 
 int splits_for(int rows, int V, int target_blocks, int min_seg) {
@@ -101,19 +102,30 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   off = align_up(off + (size_t)q.B * 3 * 8, kWsAlign);
   q.off_info = q.off_cut = off;
   q.total = off;
+  q.L = sv::Layout{nullptr, (int64_t)q.V, (int64_t)q.V};
   *pl = q;
   return SV_OK;
+}
+
+// The largest top-k a batch call may use: sampling->max_top_k, or the call's
+// single top_k when there are no per-request settings.
+int batch_max_top_k(const sv_params* p, const sv_sampling* sm) {
+  if (sm) return sm->max_top_k;
+  return (p->top_k > 0 && p->top_k < p->vocab) ? p->top_k : 0;
 }
 
 // Plan of a batch call: the scalar plan's layout sized for the largest top-k
 // any request may use, plus per-request settings and per-row nucleus cuts.
 sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
-  if (!p || !sm || !sm->temperature) return SV_ERR_INVALID_ARG;
-  if (sm->max_top_k < 0) return SV_ERR_INVALID_ARG;
-  if (sm->max_top_k > kMaxTopK) return SV_ERR_UNSUPPORTED;
+  if (!p) return SV_ERR_INVALID_ARG;
+  if (sm && !sm->temperature) return SV_ERR_INVALID_ARG;
+  if (!sm && !(std::isfinite(p->temperature) && p->temperature >= 0.f)) return SV_ERR_INVALID_ARG;
+  const int mk = batch_max_top_k(p, sm);
+  if (mk < 0 || p->top_k < 0) return SV_ERR_INVALID_ARG;
+  if (mk > kMaxTopK) return SV_ERR_UNSUPPORTED;
   sv_params q = *p;
   q.temperature = 1.f;
-  q.top_k = p->vocab > 1 ? (sm->max_top_k < p->vocab - 1 ? sm->max_top_k : p->vocab - 1) : 0;
+  q.top_k = p->vocab > 1 ? (mk < p->vocab - 1 ? mk : p->vocab - 1) : 0;
   sv_status s = make_plan(&q, kEntryProb, pl);
   if (s != SV_OK) return s;
   pl->c = 0.f;
@@ -121,7 +133,7 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   pl->off_info = off;
   off = align_up(off + (size_t)pl->B * sizeof(ReqInfo), kWsAlign);
   pl->off_cut = off;
-  if (sm->top_p) off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
+  if (sm && sm->top_p) off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
   pl->total = off;
   return SV_OK;
 }
@@ -180,7 +192,7 @@ sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int n
   TimedLaunch t(0, st);
   hipLaunchKernelGGL((sv::rows_softmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(nrows * pl.S),
                      dim3(kRowThreads), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.S, pl.seg, pl.c,
-                     (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err), info, pl.G);
+                     (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err), info, pl.G, pl.L);
   t.done();
   return check_launch();
 }
@@ -202,7 +214,7 @@ void launch_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows,
   constexpr int RPB = SV_TOPK_RPB;
   hipLaunchKernelGGL((sv::rows_topk_kernel<ET, CAPW, kTopkUnroll, SV_TOPK_WPR, RPB>), dim3((nrows + RPB - 1) / RPB),
                      dim3(SV_TOPK_WPR * RPB * 64), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, nrows, pl.V, pl.K,
-                     cand, err, info, pl.G, pl.kcap);
+                     cand, err, info, pl.G, pl.kcap, pl.L);
 }
 
 // pl.K: the top-k of every row, or (batch call) the largest one; rows are
@@ -226,12 +238,13 @@ sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrow
   return check_launch();
 }
 
-template <typename ET, bool CUT>
+template <typename ET, bool CUT, bool QP>
 sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, uint32_t k1, RaceDesc* desc,
                    unsigned long long* slots, int32_t* out, hipStream_t st) {
   TimedLaunch t(2, st);
-  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256, CUT>), dim3(pl.B * pl.Sr), dim3(256), 0, st, (const ET*)lt,
-                     (const ET*)ld, pl.G, pl.V, pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots);
+  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256, CUT, QP>), dim3(pl.B * pl.Sr), dim3(256), 0, st,
+                     (const ET*)lt, QP ? (const ET*)nullptr : (const ET*)ld, QP ? (const float*)ld : nullptr, pl.V,
+                     pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots);
   hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
                      pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
   t.done();
@@ -251,7 +264,8 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
                        (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, pl.c, k0, k1, out,
-                       nacc, p_draft, q_draft, err, (const ReqInfo*)nullptr, pl.kcap);
+                       nacc, p_draft, q_draft, err, (const ReqInfo*)nullptr, pl.kcap, pl.L,
+                       (const float*)nullptr);
     t.done();
     return check_launch();
   }
@@ -264,12 +278,12 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const ET*)ld, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, pl.c, k0,
                        k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)nullptr,
-                       (const RowCut*)nullptr);
+                       (const RowCut*)nullptr, pl.L, (const float*)nullptr);
     t.done();
     s = check_launch();
     if (s != SV_OK) return s;
   }
-  return run_race<ET, false>(pl, lt, ld, k0, k1, desc, slots, out, st);
+  return run_race<ET, false, false>(pl, lt, ld, k0, k1, desc, slots, out, st);
 }
 
 template <typename ET>
@@ -281,23 +295,33 @@ sv_status verify_greedy(const Plan& pl, const void* lt, const int32_t* X, int32_
     TimedLaunch t(0, st);
     hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
                        dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part, err,
-                       (const ReqInfo*)nullptr, pl.G);
+                       (const ReqInfo*)nullptr, pl.G, pl.L);
     t.done();
     sv_status s = check_launch();
     if (s != SV_OK) return s;
   }
   TimedLaunch t(1, st);
   hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part, X, pl.G, pl.V,
-                     pl.S, out, nacc, targ, err, (const ReqInfo*)nullptr, (float*)nullptr, (float*)nullptr);
+                     pl.S, out, nacc, targ, err, (const ReqInfo*)nullptr, (float*)nullptr, (float*)nullptr, pl.L);
   t.done();
   return check_launch();
 }
 
-// A batch call: per-request settings (device arrays), greedy, top-k and
-// full-row requests in one launch sequence.  Every kernel of a kind runs over
-// every row or request and skips those of other kinds.
+// A batch call: per-request settings (device arrays, or the call's single
+// setting), greedy, top-k and full-row requests, draft logits, one-hot drafts
+// or draft probabilities (MODE 0 / 1 / 2), dense or ragged rows.  Every
+// kernel of a kind runs over every (padded) row or request and skips those
+// of other kinds or beyond a request's draft length.
+struct BatchArgs {
+  const float* T;
+  const int32_t* K;
+  const float* P;
+  float T0;
+  int K0, max_top_k;
+};
+
 template <typename ET, int MODE>
-sv_status verify_batch(const Plan& pl, const sv_sampling* sm, uint64_t seed, const void* lt, const void* ld,
+sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const void* lt, const void* ld,
                        const int32_t* X, int32_t* out, int32_t* nacc, float* p_draft, float* q_draft, char* ws,
                        hipStream_t st) {
   const int nrows = pl.rows_t + (MODE == 0 ? pl.rows_d : 0);
@@ -306,28 +330,31 @@ sv_status verify_batch(const Plan& pl, const sv_sampling* sm, uint64_t seed, con
   ReqInfo* info = (ReqInfo*)(ws + pl.off_info);
   RowCut* cut = (RowCut*)(ws + pl.off_cut);
   uint64_t* part64 = (uint64_t*)(ws + pl.off_part);
-  const bool nuc = sm->top_p != nullptr;
+  const bool nuc = ba.P != nullptr;
+  const float* qp = MODE == 2 ? (const float*)ld : nullptr;
+  const void* ldl = MODE == 0 ? ld : nullptr;  // draft logits, if any
   sv_status s;
   {
     TimedLaunch t(0, st);
-    hipLaunchKernelGGL(sv::classify_kernel, dim3(1), dim3(1024), 0, st, sm->temperature, sm->top_k, sm->top_p, pl.B,
-                       pl.G, pl.V, sm->max_top_k, info, err, out, nacc, p_draft, q_draft);
+    hipLaunchKernelGGL(sv::classify_kernel, dim3(1), dim3(1024), 0, st, ba.T, ba.K, ba.P, ba.T0, ba.K0, pl.B, pl.G,
+                       pl.V, ba.max_top_k, pl.L, info, err, out, nacc, p_draft, q_draft);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
-  if (pl.K > 0 && (s = run_rows_topk<ET>(pl, lt, ld, nrows, ws, st, info)) != SV_OK) return s;
-  if ((s = run_rows_softmax<ET>(pl, lt, ld, nrows, ws, st, info)) != SV_OK) return s;
+  if (pl.K > 0 && (s = run_rows_topk<ET>(pl, lt, ldl, nrows, ws, st, info)) != SV_OK) return s;
+  if ((s = run_rows_softmax<ET>(pl, lt, ldl, nrows, ws, st, info)) != SV_OK) return s;
   {
     TimedLaunch t(0, st);
     hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
                        dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part64, err,
-                       (const ReqInfo*)info, pl.G);
+                       (const ReqInfo*)info, pl.G, pl.L);
     if (nuc && pl.K > 0)
       hipLaunchKernelGGL(sv::nucleus_topk_kernel, dim3((nrows + 3) / 4), dim3(256), 0, st,
-                         (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info);
+                         (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info, pl.L);
     if (nuc)
-      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(256), 0, st, (const ET*)lt, (const ET*)ld,
-                         pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part), (const ReqInfo*)info, cut);
+      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(256), 0, st, (const ET*)lt,
+                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
+                         (const ReqInfo*)info, cut, pl.L);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
@@ -338,18 +365,19 @@ sv_status verify_batch(const Plan& pl, const sv_sampling* sm, uint64_t seed, con
     if (pl.K > 0)
       hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
                          (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, 0.f, k0, k1, out,
-                         nacc, p_draft, q_draft, err, (const ReqInfo*)info, pl.kcap);
+                         nacc, p_draft, q_draft, err, (const ReqInfo*)info, pl.kcap, pl.L, qp);
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
-                       (const ET*)ld, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0, k1,
-                       out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
-                       (const RowCut*)(nuc ? cut : nullptr));
+                       (const ET*)ldl, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0,
+                       k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
+                       (const RowCut*)(nuc ? cut : nullptr), pl.L, qp);
     hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part64, X, pl.G,
-                       pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft, q_draft);
+                       pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft, q_draft, pl.L);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
-  if (nuc) return run_race<ET, true>(pl, lt, ld, k0, k1, desc, slots, out, st);
-  return run_race<ET, false>(pl, lt, ld, k0, k1, desc, slots, out, st);
+  constexpr bool QP = MODE == 2;
+  if (nuc) return run_race<ET, true, QP>(pl, lt, ld, k0, k1, desc, slots, out, st);
+  return run_race<ET, false, QP>(pl, lt, ld, k0, k1, desc, slots, out, st);
 }
 
 }  // namespace
@@ -437,35 +465,61 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
   return pl.total;
 }
 
-sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const void* target_logits,
-                            const void* draft_logits, const int32_t* draft_tokens, int32_t* out_tokens,
-                            int32_t* num_accepted, float* p_draft, float* q_draft, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const sv_layout* layout,
+                            const void* target_logits, const void* draft, const int32_t* draft_tokens,
+                            int32_t* out_tokens, int32_t* num_accepted, float* p_draft, float* q_draft,
+                            void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
   sv_status s = make_batch_plan(params, sampling, &pl);
   if (s != SV_OK) return s;
   s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
   if (s != SV_OK) return s;
-  if (draft_logits && !aligned(draft_logits, (size_t)pl.esize)) return SV_ERR_DTYPE;
-  if (!aligned(sampling->temperature, 4) || (sampling->top_k && !aligned(sampling->top_k, 4)) ||
-      (sampling->top_p && !aligned(sampling->top_p, 4)))
+  int kind = draft ? SV_DRAFT_LOGITS : SV_DRAFT_ONEHOT;
+  if (layout) {
+    kind = layout->draft_kind;
+    if (kind != SV_DRAFT_LOGITS && kind != SV_DRAFT_ONEHOT && kind != SV_DRAFT_PROBS) return SV_ERR_INVALID_ARG;
+    if (kind != SV_DRAFT_ONEHOT && !draft) return SV_ERR_INVALID_ARG;
+    const int64_t ts = layout->target_stride ? layout->target_stride : pl.V;
+    const int64_t ds = layout->draft_stride ? layout->draft_stride : pl.V;
+    if (ts < pl.V || ds < pl.V) return SV_ERR_INVALID_ARG;
+    pl.L = sv::Layout{layout->cu_draft, ts, ds};
+    if (layout->cu_draft && !aligned(layout->cu_draft, 4)) return SV_ERR_INVALID_ARG;
+  }
+  if (kind == SV_DRAFT_LOGITS && !aligned(draft, (size_t)pl.esize)) return SV_ERR_DTYPE;
+  if (kind == SV_DRAFT_PROBS && !aligned(draft, 4)) return SV_ERR_INVALID_ARG;
+  if (sampling && ((sampling->temperature && !aligned(sampling->temperature, 4)) ||
+                   (sampling->top_k && !aligned(sampling->top_k, 4)) || (sampling->top_p && !aligned(sampling->top_p, 4))))
     return SV_ERR_INVALID_ARG;
   if ((p_draft && !aligned(p_draft, 4)) || (q_draft && !aligned(q_draft, 4))) return SV_ERR_INVALID_ARG;
+  BatchArgs ba;
+  ba.T = sampling ? sampling->temperature : nullptr;
+  ba.K = sampling ? sampling->top_k : nullptr;
+  ba.P = sampling ? sampling->top_p : nullptr;
+  ba.T0 = params->temperature;
+  ba.K0 = params->top_k;
+  ba.max_top_k = batch_max_top_k(params, sampling);
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const uint64_t seed = params->seed;
+  const void* d = kind == SV_DRAFT_ONEHOT ? nullptr : draft;
   if (pl.dtype == SV_F32) {
-    if (draft_logits)
-      return verify_batch<float, 0>(pl, sampling, seed, target_logits, draft_logits, draft_tokens, out_tokens,
-                                    num_accepted, p_draft, q_draft, ws, st);
-    return verify_batch<float, 1>(pl, sampling, seed, target_logits, nullptr, draft_tokens, out_tokens,
-                                  num_accepted, p_draft, q_draft, ws, st);
+    if (kind == SV_DRAFT_LOGITS)
+      return verify_batch<float, 0>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted, p_draft,
+                                    q_draft, ws, st);
+    if (kind == SV_DRAFT_PROBS)
+      return verify_batch<float, 2>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted, p_draft,
+                                    q_draft, ws, st);
+    return verify_batch<float, 1>(pl, ba, seed, target_logits, nullptr, draft_tokens, out_tokens, num_accepted,
+                                  p_draft, q_draft, ws, st);
   }
-  if (draft_logits)
-    return verify_batch<uint16_t, 0>(pl, sampling, seed, target_logits, draft_logits, draft_tokens, out_tokens,
-                                     num_accepted, p_draft, q_draft, ws, st);
-  return verify_batch<uint16_t, 1>(pl, sampling, seed, target_logits, nullptr, draft_tokens, out_tokens,
-                                   num_accepted, p_draft, q_draft, ws, st);
+  if (kind == SV_DRAFT_LOGITS)
+    return verify_batch<uint16_t, 0>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted,
+                                     p_draft, q_draft, ws, st);
+  if (kind == SV_DRAFT_PROBS)
+    return verify_batch<uint16_t, 2>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted,
+                                     p_draft, q_draft, ws, st);
+  return verify_batch<uint16_t, 1>(pl, ba, seed, target_logits, nullptr, draft_tokens, out_tokens, num_accepted,
+                                   p_draft, q_draft, ws, st);
 }
 
 sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream) {

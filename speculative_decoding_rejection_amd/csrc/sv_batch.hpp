@@ -81,26 +81,42 @@ __device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, in
 }
 
 // ===========================================================================
-// Classify pass: one workgroup reads the per-request settings, validates
+// Classify pass: one workgroup reads the per-request settings (or, where an
+// array is null, the call's single setting T0 / K0 / top_p 1), validates
 // them, and writes one ReqInfo per request.  An invalid request emits
-// nothing (tokens -1, n = 0, p(x) = q(x) = 0) and sets kErrBadParam.  It also
-// clears the call's error word, before any other kernel of the call can set
-// a bit.
+// nothing (tokens -1, n = 0, p(x) = q(x) = 0) and sets kErrBadParam.  A
+// ragged layout is checked first (cu[0] = 0, 0 <= cu[b+1] - cu[b] <= G):
+// if it fails anywhere, every request is invalid, no per-position output is
+// written (their positions are unknown) and kErrBadLayout is set.  The pass
+// also clears the call's error word before any other kernel can set a bit.
 // ===========================================================================
 __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict__ T, const int32_t* __restrict__ K,
-                                                        const float* __restrict__ P, int B, int G, int V,
-                                                        int max_top_k, ReqInfo* __restrict__ info,
-                                                        int* __restrict__ err, int32_t* __restrict__ out,
-                                                        int32_t* __restrict__ nacc, float* __restrict__ p_draft,
-                                                        float* __restrict__ q_draft) {
-  if (threadIdx.x == 0) atomicExch(err, 0);
+                                                        const float* __restrict__ P, float T0, int K0, int B, int G,
+                                                        int V, int max_top_k, Layout L,
+                                                        ReqInfo* __restrict__ info, int* __restrict__ err,
+                                                        int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+                                                        float* __restrict__ p_draft, float* __restrict__ q_draft) {
+  __shared__ int bad_layout;
+  if (threadIdx.x == 0) {
+    atomicExch(err, 0);
+    bad_layout = 0;
+  }
   __syncthreads();
+  if (L.cu) {
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+      const int64_t c0 = L.cu[b], c1 = L.cu[b + 1];
+      if ((b == 0 && c0 != 0) || c1 - c0 < 0 || c1 - c0 > G) bad_layout = 1;
+    }
+  }
+  __syncthreads();
+  const bool all_bad = bad_layout != 0;
+  if (all_bad && threadIdx.x == 0) atomicOr(err, kErrBadLayout);
   for (int b = threadIdx.x; b < B; b += blockDim.x) {
-    const float t = T[b];
-    const int k = K ? K[b] : 0;
+    const float t = T ? T[b] : T0;
+    const int k = K ? K[b] : K0;
     const float p = P ? P[b] : 1.f;
-    const bool ok = __builtin_isfinite(t) && t >= 0.f && k >= 0 && (k >= V || k <= max_top_k) && p > 0.f &&
-                    p <= 1.f;
+    const bool ok = !all_bad && __builtin_isfinite(t) && t >= 0.f && k >= 0 && (k >= V || k <= max_top_k) &&
+                    p > 0.f && p <= 1.f;
     ReqInfo r;
     r.kind = kReqInvalid;
     r.c = 0.f;
@@ -123,15 +139,29 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
     }
     info[b] = r;
     if (!ok) {
-      atomicOr(err, kErrBadParam);
+      if (!all_bad) atomicOr(err, kErrBadParam);
       for (int j = 0; j <= G; ++j) out[(size_t)b * (G + 1) + j] = -1;
       nacc[b] = 0;
-      for (int j = 0; j < G; ++j) {
-        if (p_draft) p_draft[(size_t)b * G + j] = 0.f;
-        if (q_draft) q_draft[(size_t)b * G + j] = 0.f;
+      if (!all_bad) {
+        const int g = L.len(b, G);
+        for (int j = 0; j < g; ++j) {
+          if (p_draft) p_draft[L.tok(b, G, j)] = 0.f;
+          if (q_draft) q_draft[L.tok(b, G, j)] = 0.f;
+        }
       }
     }
   }
+}
+
+// Whether padded row `row` exists for its request (ragged calls).
+__device__ __forceinline__ bool row_exists(const Layout& L, int rows_t, int G, int row) {
+  if (!L.cu) return true;
+  if (row < rows_t) {
+    const int b = row / (G + 1);
+    return row - b * (G + 1) <= L.len(b, G);
+  }
+  const int r = row - rows_t, b = r / G;
+  return r - b * G < L.len(b, G);
 }
 
 // Bitonic sort of a[0, n) into descending order by one wave (n a power of
@@ -206,13 +236,15 @@ __device__ __forceinline__ int wave_walk(const uint64_t* a, int n, double A, dou
 // and walked, and the candidates after the cut are zeroed in place.
 // ===========================================================================
 __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict__ cand, int kstride, int rows_t,
-                                                           int nrows, int G, const ReqInfo* __restrict__ info) {
+                                                           int nrows, int G, const ReqInfo* __restrict__ info,
+                                                           Layout L) {
   __shared__ uint64_t keys_sh[4][1024];
   const int w = threadIdx.x / kWave, lane = lane_id();
   const int row = blockIdx.x * 4 + w;
   if (row >= nrows) return;
   const ReqInfo ri = info[row_request(row, rows_t, G)];
   if (ri.kind != kReqTopk || !(ri.top_p < 1.f)) return;
+  if (!row_exists(L, rows_t, G, row)) return;
   const int K = ri.K;  // 1 <= K <= 1024 (validated by the host bound)
   int n2 = kWave;
   while (n2 < K) n2 <<= 1;
@@ -303,13 +335,15 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
                                                            int rows_t, int G, int V, int S,
                                                            const float2* __restrict__ part,
                                                            const ReqInfo* __restrict__ info,
-                                                           RowCut* __restrict__ cut) {
+                                                           RowCut* __restrict__ cut, Layout L) {
   constexpr int NT = 256, NW = NT / kWave, PER = kNucBins / NT;
   static_assert(kNucBins % NT == 0, "bins per thread");
   static_assert(kNucCap * sizeof(uint64_t) <= kNucBins * sizeof(double), "keys alias the histogram");
   const int row = blockIdx.x;
   const ReqInfo ri = info[row_request(row, rows_t, G)];
   if (ri.kind != kReqFull || !(ri.top_p < 1.f)) return;  // uniform over the workgroup
+  const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
+  if (!rp) return;  // past the request's draft length
   // The gap histogram is dead once its bin is chosen; the collected keys of
   // that bin then take its storage.
   __shared__ double hm[kNucBins];
@@ -326,7 +360,6 @@ __global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict_
   __shared__ uint64_t sh_prefix;
   __shared__ int sh_plen;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const ET* rp = row < rows_t ? lt + (size_t)row * V : ld + (size_t)(row - rows_t) * V;
 
   // Largest logit of the row, from the softmax partials.
   float lmax = -INFINITY;

@@ -38,6 +38,42 @@ namespace sv {
 // Error word bits.
 constexpr int kErrBadToken = 1;
 constexpr int kErrBadParam = 2;
+constexpr int kErrBadLayout = 4;
+
+// Where rows, draft tokens and per-position outputs live.  Kernels index
+// their own workspace by the padded (request, position) pair: target row
+// b * (G + 1) + j, draft row b * G + j.  A ragged call (cu not null) gives
+// request b the draft positions cu[b] .. cu[b + 1] - 1 (g_b of them): its
+// target rows are packed at cu[b] + b + j (j <= g_b); its draft rows, draft
+// tokens and p / q outputs at cu[b] + j (j < g_b).  Strides are in elements.
+// The classify pass has checked cu (cu[0] = 0, 0 <= g_b <= G) before any
+// kernel reads it.
+struct Layout {
+  const int32_t* cu;
+  int64_t ts, ds;
+  __device__ __forceinline__ int len(int b, int G) const { return cu ? cu[b + 1] - cu[b] : G; }
+  __device__ __forceinline__ size_t tok(int b, int G, int j) const {
+    return cu ? (size_t)cu[b] + (size_t)j : (size_t)b * (size_t)G + (size_t)j;
+  }
+  __device__ __forceinline__ size_t trow(int b, int G, int j) const {
+    return cu ? (size_t)cu[b] + (size_t)b + (size_t)j : (size_t)b * (size_t)(G + 1) + (size_t)j;
+  }
+};
+
+// The logit row of padded row index `row` (target rows first), or null if
+// the request has no such row (ragged calls).
+template <typename ET>
+__device__ __forceinline__ const ET* row_ptr(const Layout& L, const ET* lt, const ET* ld, int rows_t, int G,
+                                             int row) {
+  if (row < rows_t) {
+    const int b = row / (G + 1), j = row - b * (G + 1);
+    if (L.cu && j > L.len(b, G)) return nullptr;
+    return lt + L.trow(b, G, j) * (size_t)L.ts;
+  }
+  const int r = row - rows_t, b = r / G, j = r - b * G;
+  if (L.cu && j >= L.len(b, G)) return nullptr;
+  return ld + L.tok(b, G, j) * (size_t)L.ds;
+}
 
 // Per-request settings of a batch call (written by the classify pass).  In a
 // call with one setting for every request the kernels get a null pointer.
@@ -69,12 +105,14 @@ struct __align__(16) RowCut {
 struct __align__(16) RaceDesc {
   int32_t n;         // race position (first rejection or G); -1: no race
   int32_t mask_tok;  // one-hot: token removed from the residual, else -1
-  int32_t resid;     // 1: weights max(p - q, 0); 0: weights p
+  int32_t resid;     // 1: weights max(p - q, 0), q from draft logits; 2: q given as
+                     // probabilities; 0: weights p
   int32_t pad;
   float mp, inv_zp, mq, inv_zq;  // softmax stats of target row n / draft row n
   float c;                       // log2(e) / T of the request
   int32_t pad2[3];
   uint64_t kp, kq;               // nucleus cuts of target row n / draft row n (0: none)
+  int64_t prow, qrow;            // element offsets of target row n and of draft row n
 };
 
 // A contiguous slice [a, e) of one logit row split into a scalar head (until
@@ -107,7 +145,7 @@ template <typename ET, int NT, int U>
 __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                           int rows_t, int V, int S, int seg, float c,
                                                           float2* __restrict__ part, int* __restrict__ err,
-                                                          const ReqInfo* __restrict__ info, int G) {
+                                                          const ReqInfo* __restrict__ info, int G, Layout L) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int blk = blockIdx.x;
   const int row = blk / S, s = blk - row * S;
@@ -119,7 +157,8 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
   } else if (blk == 0 && threadIdx.x == 0) {
     *err = 0;
   }
-  const ET* rp = row < rows_t ? lt + (size_t)row * V : ld + (size_t)(row - rows_t) * V;
+  const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
+  if (!rp) return;  // past the request's draft length
   const int a = s * seg;
   const int e = min(V, a + seg);
   Slice<ET> sl(rp, a, e);
@@ -175,7 +214,7 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
 template <typename ET, int NT, int U>
 __global__ __launch_bounds__(NT) void rows_argmax_kernel(const ET* __restrict__ lt, int V, int S, int seg,
                                                          uint64_t* __restrict__ part, int* __restrict__ err,
-                                                         const ReqInfo* __restrict__ info, int G) {
+                                                         const ReqInfo* __restrict__ info, int G, Layout L) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int blk = blockIdx.x;
   const int row = blk / S, s = blk - row * S;
@@ -185,7 +224,8 @@ __global__ __launch_bounds__(NT) void rows_argmax_kernel(const ET* __restrict__ 
   } else if (blk == 0 && threadIdx.x == 0) {
     *err = 0;
   }
-  const ET* rp = lt + (size_t)row * V;
+  const ET* rp = row_ptr(L, lt, lt, row + 1, G, row);
+  if (!rp) return;  // past the request's draft length
   const int a = s * seg;
   const int e = min(V, a + seg);
   Slice<ET> sl(rp, a, e);
@@ -507,7 +547,7 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
                                                                        uint64_t* __restrict__ cand,
                                                                        int* __restrict__ err,
                                                                        const ReqInfo* __restrict__ info, int G,
-                                                                       int kstride) {
+                                                                       int kstride, Layout L) {
   constexpr int NT = WPR * RPB * kWave, NW = NT / kWave;
   constexpr int GT = WPR * kWave;   // threads per row
   constexpr int EPV = Elem<ET>::kPerVec;
@@ -522,14 +562,18 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   const int g = w / WPR, wg = w % WPR, gtid = tid % GT;
   const int row = blockIdx.x * RPB + g;
   bool row_ok = row < nrows;
+  const ET* rp = nullptr;
   if (info) {
     // Batch call: rows of top-k requests only, each with its own k (<= the
     // stride); a skipped row streams nothing but joins every barrier.
     const ReqInfo ri = info[row_request(row_ok ? row : 0, rows_t, G)];
     row_ok = row_ok && ri.kind == kReqTopk;
+    if (row_ok) rp = row_ptr(L, lt, ld, rows_t, G, row);
+    row_ok = row_ok && rp != nullptr;
     K = __builtin_amdgcn_readfirstlane(row_ok ? ri.K : 1);  // one row per wave: wave-uniform
-  } else if (blockIdx.x == 0 && tid == 0) {
-    *err = 0;
+  } else {
+    if (blockIdx.x == 0 && tid == 0) *err = 0;
+    if (row_ok) rp = row_ptr(L, lt, ld, rows_t, G, row);
   }
   if (tid < NW) {
     q_sh[tid] = 0ull;
@@ -537,8 +581,7 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   }
   if (tid < 2 * RPB) kth_sh[tid / 2][tid % 2] = 0ull;
   __syncthreads();
-  const int rr = row_ok ? row : 0;
-  const ET* rp = rr < rows_t ? lt + (size_t)rr * V : ld + (size_t)(rr - rows_t) * V;
+  if (!row_ok) rp = lt;  // not read: the slice is empty
   Slice<ET> sl(rp, 0, row_ok ? V : 0);
   uint64_t* bw = buf[w];
   uint32_t* hw = hist[w];
@@ -756,10 +799,11 @@ __device__ __forceinline__ float cand_prob(const uint64_t* ck, int K, CandStats 
   return wave_sum_f(p);
 }
 
-// MODE 0: prob (q from draft candidates), 1: onehot.  One 256-thread
-// workgroup per request: the four waves compute p(x_j), q(x_j) and the
-// accept test of different positions; wave 0 then finds the first rejection
-// and runs the race over the kept tokens of row n.  Dynamic LDS: G bytes.
+// MODE 0: prob (q from draft candidates), 1: onehot, 2: q given as
+// probabilities (qp rows).  One 256-thread workgroup per request: the four
+// waves compute p(x_j), q(x_j) and the accept test of different positions;
+// wave 0 then finds the first rejection and runs the race over the kept
+// tokens of row n.  Dynamic LDS: G bytes.
 template <int MODE>
 __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __restrict__ cand,
                                                           const int32_t* __restrict__ X, int G, int V, int K,
@@ -767,7 +811,7 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
                                                           int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                                           float* __restrict__ p_draft, float* __restrict__ q_draft,
                                                           int* __restrict__ err, const ReqInfo* __restrict__ info,
-                                                          int kstride) {
+                                                          int kstride, Layout L, const float* __restrict__ qp) {
   extern __shared__ uint8_t rejected[];  // [G]
   __shared__ uint64_t qkeys[1024];
   __shared__ int n_sh;
@@ -779,12 +823,14 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     K = ri.K;
     c = ri.c;
   }
+  const int g = L.len(b, G);  // this request's draft positions
   const int lane = lane_id(), w = threadIdx.x / kWave;
   constexpr int NW = 4;
   const uint64_t* ct = cand + (size_t)b * (G + 1) * kstride;
   const uint64_t* cd = cand + ((size_t)rows_t + (size_t)b * G) * kstride;
-  for (int j = w; j < G; j += NW) {
-    const int x = X[(size_t)b * G + j];
+  for (int j = w; j < g; j += NW) {
+    const size_t xj = L.tok(b, G, j);
+    const int x = X[xj];
     const bool valid = x >= 0 && x < V;
     const CandStats sp = cand_stats(ct + (size_t)j * kstride, K, c);
     const float px = valid ? cand_prob(ct + (size_t)j * kstride, K, sp, c, x) : 0.f;
@@ -792,22 +838,24 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     if (MODE == 0) {
       const CandStats sq = cand_stats(cd + (size_t)j * kstride, K, c);
       qx = valid ? cand_prob(cd + (size_t)j * kstride, K, sq, c, x) : 0.f;
+    } else if (MODE == 2) {
+      qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
     }
     if (lane == 0) {
-      if (p_draft) p_draft[(size_t)b * G + j] = px;
-      if (q_draft) q_draft[(size_t)b * G + j] = qx;
+      if (p_draft) p_draft[xj] = px;
+      if (q_draft) q_draft[xj] = qx;
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
-      const bool acc = valid && (MODE == 0 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
       rejected[j] = acc ? 0 : 1;
     }
   }
   __syncthreads();
   if (w == 0) {
-    int n = G;
-    for (int j0 = 0; j0 < G; j0 += kWave) {
-      const uint64_t m = ballot(j0 + lane < G && rejected[j0 + lane] != 0);
+    int n = g;
+    for (int j0 = 0; j0 < g; j0 += kWave) {
+      const uint64_t m = ballot(j0 + lane < g && rejected[j0 + lane] != 0);
       if (m) {
         n = j0 + (int)__builtin_ctzll(m);
         break;
@@ -817,19 +865,20 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
   }
   __syncthreads();
   const int n = n_sh;
-  if (MODE == 0 && n < G) {
+  if (MODE == 0 && n < g) {
     const uint64_t* cq = cd + (size_t)n * kstride;
     for (int i = threadIdx.x; i < K; i += 256) qkeys[i] = cq[i];
   }
   __syncthreads();
   if (w != 0) return;
-  // Recovered (n < G) or bonus (n == G) token by the Exp(1) race over the
+  // Recovered (n < g) or bonus (n == g) token by the Exp(1) race over the
   // kept tokens of target row n.
   const uint64_t* cp = ct + (size_t)n * kstride;
   const CandStats sp = cand_stats(cp, K, c);
   CandStats sq{0.f, 0.f};
-  if (MODE == 0 && n < G) sq = cand_stats(qkeys, K, c);
-  const int xn = n < G ? X[(size_t)b * G + n] : -1;
+  if (MODE == 0 && n < g) sq = cand_stats(qkeys, K, c);
+  const int xn = n < g ? X[L.tok(b, G, n)] : -1;
+  const float* qrow = (MODE == 2 && n < g) ? qp + L.tok(b, G, n) * (size_t)L.ds : nullptr;
   uint64_t best_w = 0ull, best_p = 0ull;
   for (int i = lane; i < K; i += kWave) {
     const uint64_t k = cp[i];
@@ -837,7 +886,7 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     const uint32_t y = key_index(k);
     const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
     float wgt = p;
-    if (n < G) {
+    if (n < g) {
       if (MODE == 0) {
         float q = 0.f;
         for (int t = 0; t < K; ++t) {
@@ -845,6 +894,8 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
           if (kq && key_index(kq) == y) q = __builtin_amdgcn_exp2f((key_value(kq) - sq.m) * c) * sq.inv_z;
         }
         wgt = fmaxf(p - q, 0.f);
+      } else if (MODE == 2) {
+        wgt = fmaxf(p - qrow[y], 0.f);
       } else if ((int)y == xn) {
         wgt = 0.f;
       }
@@ -866,7 +917,7 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
   int32_t* o = out + (size_t)b * (G + 1);
   for (int j = lane; j <= G; j += kWave) {
     int32_t t = -1;
-    if (j < n) t = X[(size_t)b * G + j];
+    if (j < n) t = X[L.tok(b, G, j)];
     else if (j == n) t = win ? (int32_t)key_index(win) : -1;
     o[j] = t;
   }
@@ -904,6 +955,7 @@ __device__ __forceinline__ void merge_row_lane(const float2* part, int S, float 
 // test all run in parallel, and the first rejection is one ballot.  In a batch
 // call (info not null) only requests without top-k are handled here, each
 // with its own T, and rows with a nucleus cut take their stats from `cut`.
+// MODE 0: prob, 1: onehot, 2: q given as probabilities (qp rows).
 template <typename ET, int MODE>
 __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                          const float2* __restrict__ part,
@@ -914,7 +966,8 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
                                                          RaceDesc* __restrict__ desc,
                                                          unsigned long long* __restrict__ slots,
                                                          int* __restrict__ err, const ReqInfo* __restrict__ info,
-                                                         const RowCut* __restrict__ cut) {
+                                                         const RowCut* __restrict__ cut, Layout L,
+                                                         const float* __restrict__ qp) {
   const int b = blockIdx.x;
   const int lane = lane_id();
   bool nuc = false;
@@ -927,7 +980,8 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
     c = ri.c;
     nuc = ri.top_p < 1.f;
   }
-  // Probability of token x (logit l) in row r, merged by one lane.
+  const int g = L.len(b, G);  // this request's draft positions
+  // Probability of token x (logit l) in padded row r, merged by one lane.
   auto prob_lane = [&](size_t r, float l, int x) -> float {
     if (nuc) {
       const RowCut rc = cut[r];
@@ -938,32 +992,35 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
     merge_row_lane(part + r * S, S, c, M, Z);
     return __builtin_amdgcn_exp2f((l - M) * c) / Z;
   };
-  int n = G;
-  for (int j0 = 0; j0 < G; j0 += kWave) {
+  int n = g;
+  for (int j0 = 0; j0 < g; j0 += kWave) {
     const int j = j0 + lane;
     bool rej = false;
-    if (j < G) {
-      const int x = X[(size_t)b * G + j];
+    if (j < g) {
+      const size_t xj = L.tok(b, G, j);
+      const int x = X[xj];
       const bool valid = x >= 0 && x < V;
       const size_t rt = (size_t)b * (G + 1) + j;
-      const float px = valid ? prob_lane(rt, Elem<ET>::load1(lt + rt * V + x), x) : 0.f;
+      const float px = valid ? prob_lane(rt, Elem<ET>::load1(lt + L.trow(b, G, j) * (size_t)L.ts + x), x) : 0.f;
       float qx = valid ? 1.f : 0.f;
       if (MODE == 0) {
         const size_t rd = (size_t)b * G + j;
-        qx = valid ? prob_lane((size_t)rows_t + rd, Elem<ET>::load1(ld + rd * V + x), x) : 0.f;
+        qx = valid ? prob_lane((size_t)rows_t + rd, Elem<ET>::load1(ld + xj * (size_t)L.ds + x), x) : 0.f;
+      } else if (MODE == 2) {
+        qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
       }
-      if (q_draft) q_draft[(size_t)b * G + j] = qx;
-      if (p_draft) p_draft[(size_t)b * G + j] = px;
+      if (q_draft) q_draft[xj] = qx;
+      if (p_draft) p_draft[xj] = px;
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
-      const bool acc = valid && (MODE == 0 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
       rej = !acc;
     }
     const uint64_t m = ballot(rej);
-    if (n == G && m) n = j0 + (int)__builtin_ctzll(m);
+    if (n == g && m) n = j0 + (int)__builtin_ctzll(m);
   }
-  // Stats of row r for the race, merged by the whole wave.
+  // Stats of padded row r for the race, merged by the whole wave.
   auto race_stats = [&](size_t r, float& M, float& inv_z, uint64_t& kap) {
     if (nuc) {
       const RowCut rc = cut[r];
@@ -979,8 +1036,8 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
   };
   RaceDesc d;
   d.n = n;
-  d.mask_tok = (MODE == 1 && n < G) ? X[(size_t)b * G + n] : -1;
-  d.resid = (MODE == 0 && n < G) ? 1 : 0;
+  d.mask_tok = (MODE == 1 && n < g) ? X[L.tok(b, G, n)] : -1;
+  d.resid = n < g ? (MODE == 0 ? 1 : (MODE == 2 ? 2 : 0)) : 0;
   d.pad = 0;
   race_stats((size_t)b * (G + 1) + n, d.mp, d.inv_zp, d.kp);
   d.mq = 0.f;
@@ -988,9 +1045,11 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
   d.kq = 0ull;
   d.c = c;
   d.pad2[0] = d.pad2[1] = d.pad2[2] = 0;
-  if (d.resid) race_stats((size_t)rows_t + (size_t)b * G + n, d.mq, d.inv_zq, d.kq);
+  if (d.resid == 1) race_stats((size_t)rows_t + (size_t)b * G + n, d.mq, d.inv_zq, d.kq);
+  d.prow = (int64_t)(L.trow(b, G, n) * (size_t)L.ts);
+  d.qrow = d.resid ? (int64_t)(L.tok(b, G, n) * (size_t)L.ds) : 0;
   int32_t* o = out + (size_t)b * (G + 1);
-  for (int j = lane; j <= G; j += kWave) o[j] = j < n ? X[(size_t)b * G + j] : -1;
+  for (int j = lane; j <= G; j += kWave) o[j] = j < n ? X[L.tok(b, G, j)] : -1;
   if (lane == 0) {
     nacc[b] = n;
     desc[b] = d;
@@ -1006,11 +1065,12 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
 // ascending index order (strict '>' keeps the lowest index); the workgroup
 // merges (value, index) keys; the request's workgroups merge with a 64-bit
 // atomic max, and race_finish_kernel writes the token.  CUT: rows may carry a
-// nucleus cut (tokens with key < kp / kq have p = 0 / q = 0).
-template <typename ET, int NT, bool CUT>
-__global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld, int G,
-                                                       int V, int S, int seg, uint32_t k0, uint32_t k1,
-                                                       const RaceDesc* __restrict__ desc,
+// nucleus cut (tokens with key < kp / kq have p = 0 / q = 0).  QP: q is given
+// as fp32 probabilities (rows of qp).
+template <typename ET, int NT, bool CUT, bool QP>
+__global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                       const float* __restrict__ qp, int V, int S, int seg,
+                                                       uint32_t k0, uint32_t k1, const RaceDesc* __restrict__ desc,
                                                        unsigned long long* __restrict__ slots) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int b = blockIdx.x / S, s = blockIdx.x - b * S;
@@ -1018,8 +1078,9 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   const int n = d.n;
   if (n < 0) return;
   const float c = d.c;
-  const ET* rp = lt + ((size_t)b * (G + 1) + n) * V;
-  const ET* rq = d.resid ? ld + ((size_t)b * G + n) * V : nullptr;
+  const ET* rp = lt + d.prow;
+  const ET* rq = (!QP && d.resid) ? ld + d.qrow : nullptr;
+  const float* rqp = (QP && d.resid) ? qp + d.qrow : nullptr;
   const int a = s * seg;
   const int e = min(V, a + seg);
   const int tid = threadIdx.x;
@@ -1030,8 +1091,11 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
     float p = __builtin_amdgcn_exp2f((lp - d.mp) * c) * d.inv_zp;
     if (CUT && make_key(lp, (uint32_t)y) < d.kp) p = 0.f;
     if (d.resid) {
-      float q = __builtin_amdgcn_exp2f((lq - d.mq) * c) * d.inv_zq;
-      if (CUT && make_key(lq, (uint32_t)y) < d.kq) q = 0.f;
+      float q = lq;  // QP: the given probability
+      if (!QP) {
+        q = __builtin_amdgcn_exp2f((lq - d.mq) * c) * d.inv_zq;
+        if (CUT && make_key(lq, (uint32_t)y) < d.kq) q = 0.f;
+      }
       return fmaxf(p - q, 0.f);
     }
     return y == d.mask_tok ? 0.f : p;
@@ -1059,7 +1123,10 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
     float fp[EPV], fq[EPV];
     Elem<ET>::unpack(pv, fp);
     const int y0 = sl.vec_index0(i);
-    if (q_vec) {
+    if (QP) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) fq[k] = rqp ? rqp[y0 + k] : 0.f;
+    } else if (q_vec) {
       Elem<ET>::unpack(qv, fq);
     } else {
 #pragma unroll
@@ -1098,7 +1165,7 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   if (tid < sl.nscalar()) {
     const int y = sl.scalar_index(tid);
     const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
-    const float w = weight(Elem<ET>::load1(rp + y), rq ? Elem<ET>::load1(rq + y) : 0.f, y);
+    const float w = weight(Elem<ET>::load1(rp + y), QP ? (rqp ? rqp[y] : 0.f) : (rq ? Elem<ET>::load1(rq + y) : 0.f), y);
     if (w > 0.f) {
       const float E = (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
       const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), (uint32_t)y);
@@ -1135,7 +1202,7 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
     if (tid == 0) out[(size_t)b * (G + 1) + n] = (int32_t)key_index(win);
     return;
   }
-  const ET* rp = lt + ((size_t)b * (G + 1) + n) * V;
+  const ET* rp = lt + d.prow;
   const uint32_t ub = (uint32_t)b, un = (uint32_t)n;
   uint64_t kp = 0ull;
   for (int y = tid; y < V; y += NT) {
@@ -1168,7 +1235,8 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
                                                            int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                                            int32_t* __restrict__ targ, int* __restrict__ err,
                                                            const ReqInfo* __restrict__ info,
-                                                           float* __restrict__ p_draft, float* __restrict__ q_draft) {
+                                                           float* __restrict__ p_draft, float* __restrict__ q_draft,
+                                                           Layout L) {
   // Lane j handles position j (chunks of 64): the target argmax of row j
   // (max over the row's partial keys), written to out[j] for now, and the
   // match test; the first mismatch is one ballot.  In a batch call only
@@ -1176,35 +1244,37 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
   // law (1 on the argmax, else 0) and q(x_j) = 1.
   const int b = blockIdx.x;
   if (info && info[b].kind != kReqGreedy) return;
+  const int g = L.len(b, G);  // this request's draft positions
   const int lane = lane_id();
   int32_t* o = out + (size_t)b * (G + 1);
-  int n = G;
-  for (int j0 = 0; j0 <= G; j0 += kWave) {
+  int n = g;
+  for (int j0 = 0; j0 <= g; j0 += kWave) {
     const int j = j0 + lane;
     bool mis = false;
-    if (j <= G) {
+    if (j <= g) {
       const uint64_t* pj = part + ((size_t)b * (G + 1) + j) * S;
       uint64_t m = 0ull;
       for (int k = 0; k < S; ++k) m = pj[k] > m ? pj[k] : m;
       const int a = (int)key_index(m);
       o[j] = a;
       if (targ) targ[(size_t)b * (G + 1) + j] = a;
-      if (j < G) {
-        const int x = X[(size_t)b * G + j];
+      if (j < g) {
+        const size_t xj = L.tok(b, G, j);
+        const int x = X[xj];
         const bool valid = x >= 0 && x < V;
         if (!valid) atomicOr(err, kErrBadToken);
         mis = !valid || x != a;
-        if (p_draft) p_draft[(size_t)b * G + j] = mis ? 0.f : 1.f;
-        if (q_draft) q_draft[(size_t)b * G + j] = 1.f;
+        if (p_draft) p_draft[xj] = mis ? 0.f : 1.f;
+        if (q_draft) q_draft[xj] = 1.f;
       }
     }
     const uint64_t mm = ballot(mis);
-    if (n == G && mm) n = j0 + (int)__builtin_ctzll(mm);
+    if (n == g && mm) n = j0 + (int)__builtin_ctzll(mm);
   }
   // Accepted drafts before n, the target argmax (already in place) at n,
-  // padding after: each lane rewrites only the positions it wrote above.
+  // padding after: each lane rewrites only positions of its own lane.
   for (int j = lane; j <= G; j += kWave) {
-    if (j < n) o[j] = X[(size_t)b * G + j];
+    if (j < n) o[j] = X[L.tok(b, G, j)];
     else if (j > n) o[j] = -1;
   }
   if (lane == 0) nacc[b] = n;

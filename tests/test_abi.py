@@ -90,15 +90,16 @@ def test_status_strings(sv):
         assert sv.sv_status_string(s)
 
 
-def _call_batch(sv, params, sampling, ws_bytes=1 << 20, null=None):
+def _call_batch(sv, params, sampling, ws_bytes=1 << 20, null=None, layout=None, draft=None):
     lib = sv.load_library()
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first
     args = [fake] * 5
     if null is not None:
         args[null] = None
     sp = ctypes.byref(sampling) if sampling is not None else None
-    return lib.spec_verify_batch(ctypes.byref(params), sp, args[0], None, args[1], args[2], args[3], None, None,
-                                 args[4], ws_bytes, None)
+    lp = ctypes.byref(layout) if layout is not None else None
+    return lib.spec_verify_batch(ctypes.byref(params), sp, lp, args[0], draft, args[1], args[2], args[3], None,
+                                 None, args[4], ws_bytes, None)
 
 
 def test_batch_argument_errors(sv):
@@ -106,7 +107,6 @@ def test_batch_argument_errors(sv):
     p = sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 0, 1)
     ok = sv.SvSampling(fake, fake, fake, 64, 0)
     assert _call_batch(sv, p, ok, ws_bytes=16) == sv.SV_ERR_WORKSPACE  # everything else valid
-    assert _call_batch(sv, p, None) == sv.SV_ERR_INVALID_ARG
     assert _call_batch(sv, p, sv.SvSampling(None, fake, fake, 64, 0)) == sv.SV_ERR_INVALID_ARG
     assert _call_batch(sv, p, sv.SvSampling(fake, fake, fake, -1, 0)) == sv.SV_ERR_INVALID_ARG
     assert _call_batch(sv, p, sv.SvSampling(fake, fake, fake, 1025, 0)) == sv.SV_ERR_UNSUPPORTED
@@ -129,3 +129,25 @@ def test_batch_workspace_sizing(sv):
     assert nuc - topk >= rows * 16                  # one nucleus cut per row
     assert plain >= sv.sv_workspace_bytes(sv.make_params(256, 7, 151936, sv.SV_F32, 1.0, 0, 1))
     assert sv.sv_workspace_bytes_batch(sv.make_params(0, 7, 100, sv.SV_F32), sv.SvSampling(fake, None, None, 0, 0)) == 0
+
+
+def test_batch_single_setting_and_layout_errors(sv):
+    fake = 1 << 21
+    p = sv.make_params(4, 3, 5000, sv.SV_BF16, 0.7, 64, 1)
+    # No per-request settings: params' temperature / top_k apply to every request.
+    assert _call_batch(sv, p, None, ws_bytes=16) == sv.SV_ERR_WORKSPACE
+    assert _call_batch(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, 0.0, 0, 1), None, ws_bytes=16) == sv.SV_ERR_WORKSPACE
+    assert _call_batch(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, -1.0, 0, 1), None) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 2000, 1), None) == sv.SV_ERR_UNSUPPORTED
+    ok = sv.SvSampling(fake, None, None, 0, 0)
+    L = sv.SvLayout
+    d = ctypes.c_void_p(fake)
+    assert _call_batch(sv, p, ok, ws_bytes=16, layout=L(sv.SV_DRAFT_PROBS, 0, 0, 0, None), draft=d) == \
+        sv.SV_ERR_WORKSPACE
+    assert _call_batch(sv, p, ok, layout=L(7, 0, 0, 0, None), draft=d) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, ok, layout=L(sv.SV_DRAFT_PROBS, 0, 0, 0, None)) == sv.SV_ERR_INVALID_ARG  # no draft
+    assert _call_batch(sv, p, ok, layout=L(sv.SV_DRAFT_LOGITS, 0, 4999, 0, None), draft=d) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, ok, layout=L(sv.SV_DRAFT_LOGITS, 0, 0, 4000, None), draft=d) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, ok, ws_bytes=16, layout=L(sv.SV_DRAFT_LOGITS, 0, 5120, 5008, fake), draft=d) == \
+        sv.SV_ERR_WORKSPACE
+    assert _call_batch(sv, p, ok, layout=L(sv.SV_DRAFT_LOGITS, 0, 0, 0, fake + 2), draft=d) == sv.SV_ERR_INVALID_ARG

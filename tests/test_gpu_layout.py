@@ -1,0 +1,203 @@
+"""GPU parity of spec_verify_batch layouts against the fp64 oracle: draft
+probabilities as the draft input, ragged draft lengths (packed rows with
+cumulative offsets), row strides wider than the vocabulary, and the call's
+single setting without per-request arrays.
+
+Bar: as in test_gpu_batch.py (oracle/parity.py, compare_batch).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from oracle.parity import assert_parity_batch
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+MIX = ((0.0, 0, 1.0), (0.7, 50, 1.0), (1.0, 0, 0.9), (0.8, 40, 0.95), (1.2, 0, 1.0), (0.6, 1, 1.0))
+
+
+@pytest.fixture(scope="module")
+def sv():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import speculative_decoding_rejection_amd as sv
+    sv.load_library()
+    return sv
+
+
+def make(B, G, V, dtype, *, lengths=None, probs=False, seed=0, mix=MIX):
+    wl = workloads.BATCH_WORKLOADS["batch_mixed_f32_b256_g7_v151936"].scaled(
+        B=B, G=G, V=V, dtype=dtype, mix=mix, data_seed=seed, lengths=lengths or (), draft_probs=probs)
+    return workloads.generate(wl)
+
+
+def run_gpu(sv, inp, kind, *, ragged, pad_t=0, pad_d=0, seed=42, sampling=True):
+    """Lays the inputs out on the GPU (packed if ragged; rows padded by
+    pad_t / pad_d elements of +inf) and calls spec_verify_batch."""
+    B, G1, V = inp["target_logits"].shape
+    G = G1 - 1
+    draft = {"logits": inp.get("draft_logits"), "probs": inp.get("draft_probs"), "onehot": None}[kind]
+    lt, x = inp["target_logits"], inp["draft_tokens"]
+    cu = None
+    if ragged:
+        pk = workloads.pack_ragged(dict(inp, draft_logits=draft if kind == "logits" else None,
+                                        draft_probs=draft if kind == "probs" else None), inp["lengths"])
+        lt, x, cu = pk["target_logits"], pk["draft_tokens"], pk["cu_draft"]
+        draft = pk.get("draft_logits") if kind == "logits" else pk.get("draft_probs")
+    lt = workloads.with_stride(lt, V + pad_t, float("inf")) if pad_t else lt
+    if draft is not None and pad_d:
+        draft = workloads.with_stride(draft, V + pad_d, float("inf"))
+    kw = {}
+    if sampling:
+        kw = dict(temperature=inp["temperature"].to(DEV), top_k=inp["top_k"].to(DEV), top_p=inp["top_p"].to(DEV),
+                  max_top_k=max(1, int(inp["top_k"].max())))
+    kinds = {"logits": 0, "onehot": 1, "probs": 2}
+    res = sv.verify_batch(lt.to(DEV).contiguous(), x.to(DEV).contiguous(),
+                          None if draft is None else draft.to(DEV).contiguous(), draft_kind=kinds[kind],
+                          cu_draft=None if cu is None else cu.to(DEV), gamma=G, vocab=V, seed=seed, **kw)
+    torch.cuda.synchronize()
+    res["error_code"] = sv.sv_read_device_error(res["workspace"])
+    out = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in res.items()}
+    if ragged:  # per-position outputs back to [B, G]
+        g = inp["lengths"].numpy()
+        for key in ("p_draft", "q_draft"):
+            flat, padded, off = out[key], np.full((B, G), np.nan, np.float32), 0
+            for b in range(B):
+                padded[b, :g[b]] = flat[off:off + g[b]]
+                off += g[b]
+            out[key] = padded
+    return out
+
+
+def run_oracle(inp, kind, *, ragged, seed=42):
+    h = workloads.to_host_arrays
+    return oracle.verify_batch(h(inp["target_logits"]), h(inp["draft_logits"]) if kind == "logits" else None,
+                               h(inp["draft_tokens"]), inp["temperature"].numpy(), inp["top_k"].numpy(),
+                               inp["top_p"].numpy(), max_top_k=max(1, int(inp["top_k"].max())), seed=seed,
+                               diagnostics=True,
+                               draft_probs=inp["draft_probs"].numpy() if kind == "probs" else None,
+                               lengths=inp["lengths"].numpy() if ragged else None)
+
+
+def check(sv, inp, kind, ragged, **kw):
+    print(f"[layout] kind={kind} ragged={ragged} shape={tuple(inp['target_logits'].shape)} "
+          f"dtype={inp['target_logits'].dtype} {kw}", flush=True)
+    got = run_gpu(sv, inp, kind, ragged=ragged, **kw)
+    ref = run_oracle(inp, kind, ragged=ragged)
+    rep = assert_parity_batch(got, ref)
+    want = (1 if ref["bad_token"].any() else 0) | (2 if ref["bad_param"].any() else 0)
+    assert got["error_code"] == want
+    print(f"[layout] {rep}", flush=True)
+    return got, ref, rep
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 20011), ("bf16", 30001), ("bf16", 517)])
+def test_draft_probabilities(sv, dtype, V):
+    inp = make(24, 5, V, dtype, probs=True, seed=V % 11)
+    # Some drafts outside a top-k drafter's support (q(x) = 0: always rejected).
+    x, q = inp["draft_tokens"].clone(), inp["draft_probs"]
+    for b in range(0, 24, 3):
+        zeros = torch.nonzero(q[b, 0] == 0).flatten()
+        if zeros.numel():
+            x[b, 0] = zeros[b % zeros.numel()]
+    inp["draft_tokens"] = x
+    got, ref, rep = check(sv, inp, "probs", False)
+    assert (ref["q_draft"][~ref["greedy"]] == 0).any()
+
+
+@pytest.mark.parametrize("kind", ["logits", "onehot", "probs"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_ragged_lengths(sv, kind, dtype):
+    inp = make(30, 6, 7001, dtype, lengths=(0, 6), probs=True, seed=3)
+    assert (inp["lengths"] == 0).any() and (inp["lengths"] == 6).any()
+    check(sv, inp, kind, True)
+
+
+@pytest.mark.parametrize("kind", ["logits", "probs"])
+def test_row_strides(sv, kind):
+    """Rows wider than the vocabulary; the padding holds +inf, which would
+    take every top-k slot, argmax and race if it were read."""
+    inp = make(16, 4, 5003, "f32", probs=True, seed=5)
+    check(sv, inp, kind, False, pad_t=117, pad_d=61)
+    inp = make(16, 4, 5003, "bf16", probs=True, seed=6)
+    check(sv, inp, kind, False, pad_t=8, pad_d=3)
+
+
+def test_ragged_strides_probabilities(sv):
+    inp = make(20, 7, 9001, "bf16", lengths=(0, 7), probs=True, seed=7)
+    check(sv, inp, "probs", True, pad_t=5, pad_d=77)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_setting_equals_single_entries(sv, dtype):
+    """No per-request arrays: params' temperature and top_k apply to every
+    request, bit-identical to the single-setting entry points."""
+    wl = workloads.WORKLOADS["prob_topk64_bf16_b1024_g8_v256000"].scaled(B=12, V=20001, dtype=dtype)
+    inp = workloads.generate(wl)
+    lt, x, ld = inp["target_logits"].to(DEV), inp["draft_tokens"].to(DEV), inp["draft_logits"].to(DEV)
+    for T, k, entry in ((0.7, 64, "prob"), (0.9, 0, "prob"), (1.1, 0, "onehot"), (0.0, 0, "greedy")):
+        d = ld if entry == "prob" else None
+        a = sv.verify_batch(lt, x, d, single_temperature=T, single_top_k=k, seed=4)
+        b = sv.verify(entry, lt, x, d, temperature=T, top_k=k, seed=4)
+        torch.cuda.synchronize()
+        for key in ("out_tokens", "num_accepted"):
+            assert torch.equal(a[key], b[key]), (T, k, entry, key)
+        if entry != "greedy":
+            assert torch.equal(a["p_draft"], b["p_draft"])
+
+
+def test_bad_offsets_emit_nothing(sv):
+    """A cu_draft array that breaks the rules (a length above gamma) makes
+    every request invalid; no row is read."""
+    inp = make(6, 3, 1000, "f32", lengths=(1, 3), seed=8)
+    pk = workloads.pack_ragged(inp, inp["lengths"])
+    cu = pk["cu_draft"].clone()
+    cu[3] = cu[2] + 4  # g_2 = 4 > gamma
+    res = sv.verify_batch(pk["target_logits"].to(DEV), pk["draft_tokens"].to(DEV), pk["draft_logits"].to(DEV),
+                          temperature=inp["temperature"].to(DEV), cu_draft=cu.to(DEV), gamma=3, seed=1)
+    torch.cuda.synchronize()
+    assert sv.sv_read_device_error(res["workspace"]) & 4
+    assert (res["out_tokens"].cpu() == -1).all() and (res["num_accepted"].cpu() == 0).all()
+
+
+@pytest.mark.parametrize("name", ["batch_ragged_probs_f32_b256_g7_v151936"])
+def test_full_size_ragged_probs_sampled(sv, name):
+    wl = workloads.BATCH_WORKLOADS[name]
+    print(f"[full] {name}: generating on the GPU", flush=True)
+    inp = workloads.generate(wl, device=DEV)
+    pk = workloads.pack_ragged(inp, inp["lengths"].cpu())
+    mk = max(k for _, k, _ in wl.mix)
+    res = sv.verify_batch(pk["target_logits"], pk["draft_tokens"], pk["draft_probs"], draft_kind=2,
+                          cu_draft=pk["cu_draft"], gamma=wl.G, temperature=inp["temperature"], top_k=inp["top_k"],
+                          top_p=inp["top_p"], max_top_k=mk, seed=wl.verify_seed)
+    torch.cuda.synchronize()
+    assert sv.sv_read_device_error(res["workspace"]) == 0
+    g = inp["lengths"].cpu().numpy()
+    n, out = res["num_accepted"].cpu().numpy(), res["out_tokens"].cpu().numpy()
+    x = inp["draft_tokens"].cpu().numpy()
+    for b in range(wl.B):
+        assert 0 <= n[b] <= g[b]
+        assert (out[b, :n[b]] == x[b, :n[b]]).all() and 0 <= out[b, n[b]] < wl.V and (out[b, n[b] + 1:] == -1).all()
+    pd, qd = res["p_draft"].cpu().numpy(), res["q_draft"].cpu().numpy()
+    rng = np.random.default_rng(1)
+    ids = np.sort(rng.choice(wl.B, size=24, replace=False)).astype(np.int32)
+    sub = {k: v[ids.tolist()].cpu() for k, v in inp.items() if v is not None}
+    del inp, pk
+    torch.cuda.empty_cache()
+    h = workloads.to_host_arrays
+    ref = oracle.verify_batch(h(sub["target_logits"]), None, h(sub["draft_tokens"]), sub["temperature"].numpy(),
+                              sub["top_k"].numpy(), sub["top_p"].numpy(), max_top_k=mk, seed=wl.verify_seed,
+                              req_ids=ids, diagnostics=True, draft_probs=sub["draft_probs"].numpy(),
+                              lengths=sub["lengths"].numpy())
+    cu = np.concatenate([[0], np.cumsum(g)])
+    pd_pad = np.full((len(ids), wl.G), np.nan, np.float32)
+    qd_pad = np.full((len(ids), wl.G), np.nan, np.float32)
+    for i, b in enumerate(ids):
+        pd_pad[i, :g[b]] = pd[cu[b]:cu[b + 1]]
+        qd_pad[i, :g[b]] = qd[cu[b]:cu[b + 1]]
+    got = {"out_tokens": out[ids], "num_accepted": n[ids], "p_draft": pd_pad, "q_draft": qd_pad}
+    rep = assert_parity_batch(got, ref)
+    print(f"[full] {name}: {rep}", flush=True)

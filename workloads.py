@@ -61,6 +61,8 @@ class Workload:
     verify_seed: int = 42
     chunk: int = 8        # requests generated per generator call
     mix: tuple = ()       # entry "batch": ((temperature, top_k, top_p), ...) request classes
+    lengths: tuple = ()   # entry "batch": (lo, hi) draft positions per request, uniform (ragged rows)
+    draft_probs: bool = False  # entry "batch": the drafter hands over fp32 probabilities
 
     @property
     def torch_dtype(self):
@@ -79,6 +81,16 @@ class Workload:
         return self.B * self.G if self.entry in ("prob", "batch") else 0
 
     @property
+    def draft_lengths(self) -> np.ndarray:
+        """Draft positions per request (all G unless ragged)."""
+        if self.entry == "batch" and self.lengths:
+            gen = torch.Generator(device="cpu")
+            gen.manual_seed(self.data_seed + 2)
+            lo, hi = self.lengths
+            return torch.randint(lo, hi + 1, (self.B,), generator=gen, dtype=torch.int32).numpy()
+        return np.full(self.B, self.G, dtype=np.int32)
+
+    @property
     def has_draft_logits(self) -> bool:
         return self.entry in ("prob", "batch")
 
@@ -86,10 +98,13 @@ class Workload:
     def logit_bytes(self) -> int:
         """Bytes of every logit row read once: the algorithmic traffic (for a
         batch workload, the draft rows of its sampled requests only)."""
-        drafts = self.draft_rows
-        if self.entry == "batch" and self.mix:
-            drafts = int((batch_settings(self)["temperature"] > 0).sum()) * self.G
-        return (self.target_rows + drafts) * self.V * self.elem_bytes
+        if self.entry != "batch":
+            return (self.target_rows + self.draft_rows) * self.V * self.elem_bytes
+        g = self.draft_lengths
+        sampled = (batch_settings(self)["temperature"] > 0).numpy() if self.mix else np.ones(self.B, bool)
+        target = int((g + 1).sum()) * self.V * self.elem_bytes
+        draft = int(g[sampled].sum()) * self.V * (4 if self.draft_probs else self.elem_bytes)
+        return target + draft
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -115,11 +130,15 @@ WORKLOADS = {
 
 # Per-request settings in one call (spec_verify_batch): greedy, top-k 50,
 # top-p 0.9, top-k 40 then top-p 0.95, a quarter each, on the fp32 shape of
-# prob_f32_b256_g7_v151936.
+# prob_f32_b256_g7_v151936; the same with ragged draft lengths 1..7 and the
+# drafter's probabilities as the draft input.
+_MIX4 = ((0.0, 0, 1.0), (0.7, 50, 1.0), (1.0, 0, 0.9), (0.8, 40, 0.95))
 BATCH_WORKLOADS = {
     "batch_mixed_f32_b256_g7_v151936": Workload(
-        "batch_mixed_f32_b256_g7_v151936", "batch", 256, 7, 151936, "f32", 1.0, 0, 3.0, (0.5, 2.0),
-        mix=((0.0, 0, 1.0), (0.7, 50, 1.0), (1.0, 0, 0.9), (0.8, 40, 0.95))),
+        "batch_mixed_f32_b256_g7_v151936", "batch", 256, 7, 151936, "f32", 1.0, 0, 3.0, (0.5, 2.0), mix=_MIX4),
+    "batch_ragged_probs_f32_b256_g7_v151936": Workload(
+        "batch_ragged_probs_f32_b256_g7_v151936", "batch", 256, 7, 151936, "f32", 1.0, 0, 3.0, (0.5, 2.0),
+        mix=_MIX4, lengths=(1, 7), draft_probs=True),
 }
 ALL_WORKLOADS = {**WORKLOADS, **BATCH_WORKLOADS}
 
@@ -191,7 +210,55 @@ def generate(wl: Workload, device="cpu", requests: range | None = None) -> dict:
     res = {"target_logits": lt_all, "draft_logits": ld_all, "draft_tokens": x_all}
     if settings is not None:
         res.update({k: v[lo_req:hi_req].to(device) for k, v in settings.items()})
+    if wl.entry == "batch" and wl.draft_probs:
+        res["draft_probs"] = _drafter_probs(ld_all, res["temperature"], res["top_k"])
+    if wl.entry == "batch" and wl.lengths:
+        res["lengths"] = torch.from_numpy(wl.draft_lengths[lo_req:hi_req]).to(device)
     return res
+
+
+def _drafter_probs(ld: torch.Tensor, temperature: torch.Tensor, top_k: torch.Tensor) -> torch.Tensor:
+    """The drafter's own sampling law, handed over as fp32 probabilities:
+    softmax of its logits / T over its top-k set (the law its tokens were
+    drawn from); a temperature-0 drafter hands over a one-hot at its argmax."""
+    q = torch.zeros(ld.shape, dtype=torch.float32, device=ld.device)
+    for r in range(ld.shape[0]):
+        t, k = float(temperature[r]), int(top_k[r])
+        z = ld[r].float()
+        if t == 0.0:
+            q[r].scatter_(-1, torch.argmax(z, dim=-1, keepdim=True), 1.0)
+            continue
+        z = z / t
+        if 0 < k < z.shape[-1]:
+            vals, idx = torch.sort(z, dim=-1, descending=True, stable=True)
+            q[r].scatter_(-1, idx[..., :k], torch.softmax(vals[..., :k], dim=-1))
+        else:
+            q[r] = torch.softmax(z, dim=-1)
+    return q
+
+
+def pack_ragged(inp: dict, lengths) -> dict:
+    """Packed rows of a ragged batch (data layout only): request b keeps
+    target rows 0..g_b and draft rows / tokens 0..g_b-1, request after
+    request; cu [B+1] int32 holds the cumulative draft counts."""
+    g = [int(v) for v in lengths]
+    cu = np.zeros(len(g) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(g)
+    out = {"cu_draft": torch.from_numpy(cu).to(inp["target_logits"].device),
+           "target_logits": torch.cat([inp["target_logits"][b, :g[b] + 1] for b in range(len(g))]),
+           "draft_tokens": torch.cat([inp["draft_tokens"][b, :g[b]] for b in range(len(g))])}
+    for key in ("draft_logits", "draft_probs"):
+        if inp.get(key) is not None:
+            out[key] = torch.cat([inp[key][b, :g[b]] for b in range(len(g))])
+    return out
+
+
+def with_stride(rows: torch.Tensor, width: int, fill: float) -> torch.Tensor:
+    """Rows [..., V] copied into a [..., width] buffer whose padding holds
+    `fill` (a value that would change the results if it were ever read)."""
+    buf = torch.full(rows.shape[:-1] + (width,), fill, dtype=rows.dtype, device=rows.device)
+    buf[..., :rows.shape[-1]] = rows
+    return buf
 
 
 def _chunk(wl: Workload, c: int, gen: torch.Generator, device, settings=None):
@@ -244,4 +311,4 @@ def to_host_arrays(t: torch.Tensor | None):
 
 
 __all__ = ["Workload", "WORKLOADS", "BATCH_WORKLOADS", "ALL_WORKLOADS", "WORKLOAD_ORDER", "HEADLINE",
-           "generate", "batch_settings", "to_host_arrays"]
+           "generate", "batch_settings", "pack_ragged", "with_stride", "to_host_arrays"]
