@@ -66,9 +66,12 @@ def cpu_baseline(wl, inp, target_seconds: float) -> dict:
         x = workloads.to_host_arrays(inp["draft_tokens"][sub])
         t0 = time.perf_counter()
         if wl.entry == "batch":
-            oracle.verify_batch(lt, ld, x, inp["temperature"][sub].cpu().numpy(), inp["top_k"][sub].cpu().numpy(),
-                                inp["top_p"][sub].cpu().numpy(), max_top_k=max(k for _, k, _ in wl.mix),
-                                seed=wl.verify_seed)
+            probs = inp["draft_probs"][sub].cpu().numpy() if wl.draft_probs else None
+            lens = inp["lengths"][sub].cpu().numpy() if wl.lengths else None
+            oracle.verify_batch(lt, None if wl.draft_probs else ld, x, inp["temperature"][sub].cpu().numpy(),
+                                inp["top_k"][sub].cpu().numpy(), inp["top_p"][sub].cpu().numpy(),
+                                max_top_k=max(k for _, k, _ in wl.mix), seed=wl.verify_seed, draft_probs=probs,
+                                lengths=lens)
         else:
             oracle.verify(modes[wl.entry], lt, ld, x, temperature=wl.temperature, top_k=wl.top_k,
                           seed=wl.verify_seed)
@@ -81,7 +84,7 @@ def cpu_baseline(wl, inp, target_seconds: float) -> dict:
         n = int(min(wl.B, max(n + 1, n * target_seconds / max(t, 1e-3))))
         t = run(n)
     return {
-        "value": n * wl.G / t,
+        "value": int(wl.draft_lengths[:n].sum()) / t,
         "unit": "verified draft positions/s",
         "cores": threads,
         "kind": "oracle",
@@ -121,17 +124,31 @@ def main():
     torch.cuda.synchronize()
 
     params = sv.make_params(wl.B, wl.G, wl.V, wl.torch_dtype, wl.temperature or 1.0, wl.top_k, wl.verify_seed)
-    sampling = None
+    sampling = layout = None
+    padded = inp
     if wl.entry == "batch":
         sampling = sv.make_sampling(inp["temperature"], inp["top_k"], inp["top_p"], max(k for _, k, _ in wl.mix))
         ws = torch.empty(sv.sv_workspace_bytes_batch(params, sampling), dtype=torch.uint8, device=dev)
+        if wl.lengths or wl.draft_probs:
+            # Packed ragged rows and / or the drafter's probabilities, laid
+            # out before the timed region.
+            src = inp
+            if wl.lengths:
+                src = workloads.pack_ragged(inp, inp["lengths"].cpu())
+            draft = src["draft_probs"] if wl.draft_probs else src["draft_logits"]
+            layout = sv.SvLayout(sv.SV_DRAFT_PROBS if wl.draft_probs else sv.SV_DRAFT_LOGITS, 0, wl.V, wl.V,
+                                 sv._ptr(src["cu_draft"]) if wl.lengths else None)
+            padded = inp
+            inp = dict(inp, target_logits=src["target_logits"], draft_logits=draft,
+                       draft_tokens=src["draft_tokens"], cu_draft=src.get("cu_draft"))
+            torch.cuda.synchronize()
     else:
         ws = sv.alloc_workspace(params, dev)
     B, G = wl.B, wl.G
     out = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
-    pd = torch.empty((B, G), dtype=torch.float32, device=dev)
-    qd = torch.empty((B, G), dtype=torch.float32, device=dev)
+    pd = torch.empty(inp["draft_tokens"].shape, dtype=torch.float32, device=dev)
+    qd = torch.empty(inp["draft_tokens"].shape, dtype=torch.float32, device=dev)
     ta = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     lt, ld, x = inp["target_logits"], inp["draft_logits"], inp["draft_tokens"]
@@ -142,7 +159,7 @@ def main():
         elif wl.entry == "onehot":
             sv.spec_verify_onehot(params, lt, x, out, nacc, pd, ws, stream)
         elif wl.entry == "batch":
-            sv.spec_verify_batch(params, sampling, None, lt, ld, x, out, nacc, pd, qd, ws, stream)
+            sv.spec_verify_batch(params, sampling, layout, lt, ld, x, out, nacc, pd, qd, ws, stream)
         else:
             sv.spec_verify_greedy(params, lt, x, out, nacc, ta, ws, stream)
 
@@ -180,7 +197,7 @@ def main():
         log("[bench] copy calibration: 3 copies of 1 GiB done")
 
     sec = wall / args.steps
-    positions = B * G
+    positions = int(wl.draft_lengths.sum()) if wl.entry == "batch" else B * G
     rows = wl.target_rows + wl.draft_rows
     bytes_alg = wl.logit_bytes
     # Row-pass time per step: one launch for the single-setting entries; the
@@ -192,7 +209,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, inp, args.cpu_seconds)
+        cpu = cpu_baseline(wl, padded, args.cpu_seconds)
     res = {
         "metric": "verified draft positions/sec and HBM GB/s (% of peak) at B=1024,gamma=8,V=256k",
         "value": positions / sec,
@@ -209,7 +226,9 @@ def main():
         "config": {"workload": name, "entry": f"spec_verify_{wl.entry}", "batch": B, "gamma": G, "vocab": wl.V,
                    "logits": wl.dtype, "temperature": wl.temperature, "top_k": wl.top_k,
                    "parallelism": "single GPU",
-                   **({"mix (T, top_k, top_p)": [list(m) for m in wl.mix]} if wl.entry == "batch" else {})},
+                   **({"mix (T, top_k, top_p)": [list(m) for m in wl.mix]} if wl.entry == "batch" else {}),
+                   **({"draft lengths": list(wl.lengths)} if wl.lengths else {}),
+                   **({"draft": "fp32 probabilities"} if wl.draft_probs else {})},
         "rows_per_s": rows / sec,
         "requests_per_s": B / sec,
         "algorithmic_gbps": bytes_alg / sec / 1e9,

@@ -129,6 +129,21 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   sv_status s = make_plan(&q, kEntryProb, pl);
   if (s != SV_OK) return s;
   pl->c = 0.f;
+  // A kind of request may hold only part of the batch: the softmax and
+  // argmax passes split rows as if a quarter of them were theirs.
+  const int act = (pl->rows_t + pl->rows_d + 3) / 4;
+  const int S = splits_for(act, pl->V, 2048, 8192);
+  if (S > pl->S) {
+    pl->seg = seg_for(pl->V, S);
+    pl->S = (pl->V + pl->seg - 1) / pl->seg;
+    size_t off = pl->off_part;
+    off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * (size_t)pl->S * 8, kWsAlign);
+    const size_t shift = off - pl->off_cand;  // later sections move up
+    pl->off_cand += shift;
+    pl->off_desc += shift;
+    pl->off_slots += shift;
+    pl->total += shift;
+  }
   size_t off = pl->total;
   pl->off_info = off;
   off = align_up(off + (size_t)pl->B * sizeof(ReqInfo), kWsAlign);
@@ -352,7 +367,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       hipLaunchKernelGGL(sv::nucleus_topk_kernel, dim3((nrows + 3) / 4), dim3(256), 0, st,
                          (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info, pl.L);
     if (nuc)
-      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(256), 0, st, (const ET*)lt,
+      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(sv::kNucThreads), 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
     t.done();

@@ -268,13 +268,13 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 }
 
 // ===========================================================================
-// Nucleus of a full row (no top-k): one workgroup per row, after the softmax
+// Nucleus of a full row (no top-k): one 1024-thread workgroup per row, after the softmax
 // row pass (whose partials give the row's largest logit).
 //
 //   pass 1  fp64 mass of every token; the total Z; a histogram of mass over
 //           bins of the gap d = (l_max - l) / T, ln2 / 64 nats per bin over
-//           [0, 41.6).  Tokens further below the maximum carry less than
-//           2^31 e^-41 < 4e-9 of Z in total, so the cut (top_p <= 1 - 2^-24)
+//           [0, 44.4).  Tokens further below the maximum carry less than
+//           2^31 e^-44 < 2e-10 of Z in total, so the cut (top_p <= 1 - 2^-24)
 //           always falls inside the histogram.
 //   scan    the bin where the running mass reaches top_p * Z, and the mass A
 //           of the bins before it.
@@ -287,7 +287,8 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 //           until at most kNucCap tokens remain.
 // Each pass streams the row from HBM.
 // ===========================================================================
-constexpr int kNucBins = 3840;  // ln2 / 64 nats each: gaps below 41.6 nats
+constexpr int kNucBins = 4096;  // ln2 / 64 nats each: gaps below 44.4 nats
+constexpr int kNucThreads = 512;  // one workgroup per row
 constexpr int kNucCap = 2048;
 
 // Gap bin of logit l (-1: none), from the same rounding as the mass.
@@ -331,12 +332,12 @@ __device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
 }
 
 template <typename ET>
-__global__ __launch_bounds__(256) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+__global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                            int rows_t, int G, int V, int S,
                                                            const float2* __restrict__ part,
                                                            const ReqInfo* __restrict__ info,
                                                            RowCut* __restrict__ cut, Layout L) {
-  constexpr int NT = 256, NW = NT / kWave, PER = kNucBins / NT;
+  constexpr int NT = kNucThreads, NW = NT / kWave, PER = kNucBins / NT;
   static_assert(kNucBins % NT == 0, "bins per thread");
   static_assert(kNucCap * sizeof(uint64_t) <= kNucBins * sizeof(double), "keys alias the histogram");
   const int row = blockIdx.x;

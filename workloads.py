@@ -103,7 +103,9 @@ class Workload:
         g = self.draft_lengths
         sampled = (batch_settings(self)["temperature"] > 0).numpy() if self.mix else np.ones(self.B, bool)
         target = int((g + 1).sum()) * self.V * self.elem_bytes
-        draft = int(g[sampled].sum()) * self.V * (4 if self.draft_probs else self.elem_bytes)
+        # Draft probabilities are gathered (q(x_j)) and one residual row per
+        # rejected request is raced, not streamed by the row pass.
+        draft = 0 if self.draft_probs else int(g[sampled].sum()) * self.V * self.elem_bytes
         return target + draft
 
     def scaled(self, **kw) -> "Workload":
