@@ -93,6 +93,47 @@ def cpu_baseline(wl, inp, target_seconds: float) -> dict:
     }
 
 
+def rounds_driver(sv, wl, rounds: int, device, seed_offset: int = 1000) -> dict:
+    """Multi-round synthetic driver: `rounds` verification rounds of the
+    workload, each on fresh seeded rows, with the per-position acceptance
+    probability beta and the per-request counters (+= draft positions,
+    accepted drafts, 1 per round) kept on the GPU.  Returns the method's
+    statistics: tokens per round, the acceptance rate of each position
+    measured from n (P(n > j | n >= j)), the mean beta of each position, the
+    expected tokens per round from those betas by Eq. 1 of the draft-model
+    page generalised to per-position rates (sum over i of the product of the
+    first i rates), and the counters' totals."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    G, B = wl.G, wl.B
+    counters = torch.zeros((B, 3), dtype=torch.int64, device=device)
+    ns, betas = [], []
+    for r in range(rounds):
+        inp = workloads.generate(wl.scaled(data_seed=wl.data_seed + seed_offset + r), device=device)
+        ld = inp["draft_logits"] if wl.entry == "prob" else None
+        res = sv.verify_batch(inp["target_logits"], inp["draft_tokens"], ld, single_temperature=wl.temperature,
+                              single_top_k=wl.top_k, seed=wl.verify_seed + r, beta=True, counters=counters)
+        torch.cuda.synchronize()
+        ns.append(res["num_accepted"].cpu().numpy())
+        betas.append(res["beta"].cpu().numpy())
+    n = np.concatenate(ns)
+    beta = np.concatenate(betas)
+    reach = np.array([(n >= j).sum() for j in range(G + 1)], dtype=np.float64)
+    acc = [float((n > j).sum() / reach[j]) if reach[j] else float("nan") for j in range(G)]
+    bmean = beta.mean(axis=0)
+    eq1 = float(sum(np.prod(bmean[:i]) for i in range(G + 1)))
+    c = counters.cpu().numpy().sum(axis=0)
+    return {"rounds": rounds, "requests": B, "gamma": G, "tokens_per_round": float((n + 1).mean()),
+            "tokens_per_round_eq1": eq1, "acceptance_by_position": acc,
+            "beta_by_position": [float(v) for v in bmean],
+            "counters": {"draft_n": int(c[0]), "draft_n_accepted": int(c[1]), "draft_rounds": int(c[2])},
+            "mean_accepted_per_round": float(c[1] / c[2]) if c[2] else 0.0,
+            "_n": n, "_counters": counters.cpu().numpy()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +142,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--rounds", type=int, default=0,
+                    help="also run the multi-round driver for this many rounds and report its statistics")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -151,6 +194,7 @@ def main():
     qd = torch.empty(inp["draft_tokens"].shape, dtype=torch.float32, device=dev)
     ta = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
+    outputs = sv.make_outputs(out, nacc, pd, qd)
     lt, ld, x = inp["target_logits"], inp["draft_logits"], inp["draft_tokens"]
 
     def step():
@@ -159,7 +203,7 @@ def main():
         elif wl.entry == "onehot":
             sv.spec_verify_onehot(params, lt, x, out, nacc, pd, ws, stream)
         elif wl.entry == "batch":
-            sv.spec_verify_batch(params, sampling, layout, lt, ld, x, out, nacc, pd, qd, ws, stream)
+            sv.spec_verify_batch(params, sampling, layout, lt, ld, x, outputs, ws, stream)
         else:
             sv.spec_verify_greedy(params, lt, x, out, nacc, ta, ws, stream)
 
@@ -242,6 +286,10 @@ def main():
                      "traffic": traffic},
         "cpu_baseline": cpu,
     }
+    if args.rounds:
+        log(f"[bench] multi-round driver: {args.rounds} rounds")
+        st = rounds_driver(sv, wl, args.rounds, dev)
+        res["rounds"] = {k: v for k, v in st.items() if not k.startswith("_")}
     print(json.dumps(res), flush=True)
 
 

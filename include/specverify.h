@@ -172,6 +172,31 @@ typedef struct {
   int32_t reserved; /* 0 */
 } sv_sampling;
 
+/* Outputs of spec_verify_batch (DEVICE arrays owned by the caller).
+ *   out_tokens [B][G+1], num_accepted [B]: required, as spec_verify_prob.
+ *   p_draft, q_draft: p_j(x_j), q_j(x_j) per draft position (laid out like
+ *     draft_tokens); may be NULL.
+ *   beta: per draft position, sum_y min(p_j(y), q_j(y)), the probability
+ *     that position j's draft is accepted (page "초안 모델로 생성 속도를
+ *     높이는 추측 디코딩", section "수락률 α와 기대 속도 향상": alpha is its
+ *     expectation, Theorem 3.5); p_j(x_j) for one-hot drafts, 1 or 0 (argmax
+ *     match) for greedy requests; laid out like draft_tokens; may be NULL.
+ *     For requests without top-k and with draft logits or probabilities it
+ *     costs one more read of their target and draft rows.
+ *   counters [B][3] int64: per request, += (draft positions verified, drafts
+ *     accepted, 1) on every call that verifies it (the manual page's
+ *     draft_n, draft_n_accepted, draft_rounds: the mean accepted length is
+ *     counters[b][1] / counters[b][2]); never cleared by the library; may be
+ *     NULL.  Requests that are not verified (invalid) are not counted. */
+typedef struct {
+  int32_t* out_tokens;
+  int32_t* num_accepted;
+  float* p_draft;
+  float* q_draft;
+  float* beta;
+  int64_t* counters;
+} sv_outputs;
+
 /* Workspace bytes of spec_verify_batch for these parameters (0 if invalid).
  * With sampling != NULL, params->temperature and params->top_k are not
  * used. */
@@ -196,13 +221,12 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  *   layout: draft form, strides, ragged offsets; NULL = dense rows with
  *           draft logits if `draft` is not NULL, else one-hot drafts
  *   target_logits, draft (logits or fp32 probabilities; NULL for one-hot),
- *   draft_tokens, p_draft, q_draft (may be NULL): as described by layout;
- *   out_tokens [B][G+1] (-1 after the emitted token), num_accepted [B].
+ *   draft_tokens: as described by layout;
+ *   outputs: see sv_outputs.
  * Workspace: sv_workspace_bytes_batch(params, sampling) bytes. */
 sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const sv_layout* layout,
                             const void* target_logits, const void* draft, const int32_t* draft_tokens,
-                            int32_t* out_tokens, int32_t* num_accepted, float* p_draft, float* q_draft,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            const sv_outputs* outputs, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronises `stream`, then copies the sticky device error word of the
  * last call that used `workspace` to *host_code: bit 0 (1) = a draft token

@@ -63,6 +63,17 @@ class SvLayout(ctypes.Structure):
     ]
 
 
+class SvOutputs(ctypes.Structure):
+    _fields_ = [
+        ("out_tokens", ctypes.c_void_p),
+        ("num_accepted", ctypes.c_void_p),
+        ("p_draft", ctypes.c_void_p),
+        ("q_draft", ctypes.c_void_p),
+        ("beta", ctypes.c_void_p),
+        ("counters", ctypes.c_void_p),
+    ]
+
+
 class SpecVerifyError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -97,7 +108,8 @@ def load_library():
     lib.sv_workspace_bytes_batch.argtypes = [pp, ps]
     lib.sv_workspace_bytes_batch.restype = sz
     pl_ = ctypes.POINTER(SvLayout)
-    lib.spec_verify_batch.argtypes = [pp, ps, pl_, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    po = ctypes.POINTER(SvOutputs)
+    lib.spec_verify_batch.argtypes = [pp, ps, pl_, vp, vp, vp, po, vp, sz, vp]
     lib.spec_verify_batch.restype = ctypes.c_int
     lib.sv_read_device_error.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
     lib.sv_read_device_error.restype = ctypes.c_int
@@ -193,14 +205,24 @@ def sv_workspace_bytes_batch(params: SvParams, sampling) -> int:
                                                        ctypes.byref(sampling) if sampling else None))
 
 
-def spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, out_tokens, num_accepted,
-                      p_draft, q_draft, workspace, stream=None):
-    """sampling (SvSampling) and layout (SvLayout) may be None."""
+def make_outputs(out_tokens, num_accepted, p_draft=None, q_draft=None, beta=None, counters=None) -> SvOutputs:
+    """Output pointers of spec_verify_batch (device tensors; counters int64
+    [B, 3], accumulated across calls).  Keep the tensors alive while the
+    struct is used."""
+    if counters is not None and counters.dtype != torch.int64:
+        raise ValueError("counters must be int64")
+    return SvOutputs(_ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft), _ptr(beta),
+                     _ptr(counters))
+
+
+def spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, outputs, workspace,
+                      stream=None):
+    """sampling (SvSampling) and layout (SvLayout) may be None; outputs is an
+    SvOutputs (make_outputs)."""
     st = load_library().spec_verify_batch(ctypes.byref(params), ctypes.byref(sampling) if sampling else None,
                                           ctypes.byref(layout) if layout else None, _ptr(target_logits),
-                                          _ptr(draft), _ptr(draft_tokens), _ptr(out_tokens), _ptr(num_accepted),
-                                          _ptr(p_draft), _ptr(q_draft), _ptr(workspace), workspace.numel(),
-                                          _stream(stream))
+                                          _ptr(draft), _ptr(draft_tokens), ctypes.byref(outputs), _ptr(workspace),
+                                          workspace.numel(), _stream(stream))
     _check(st, "spec_verify_batch")
 
 
@@ -267,7 +289,8 @@ def verify(entry: str, target_logits, draft_tokens, draft_logits=None, *, temper
 
 def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, top_k=None, top_p=None,
                  max_top_k=None, seed=0, draft_kind=None, cu_draft=None, gamma=None, vocab=None,
-                 single_temperature=1.0, single_top_k=0, workspace=None, stream=None) -> dict:
+                 single_temperature=1.0, single_top_k=0, beta=False, counters=None, workspace=None,
+                 stream=None) -> dict:
     """Allocates outputs (and a workspace if none is given) and runs
     spec_verify_batch.
 
@@ -279,7 +302,9 @@ def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, t
     (default W) the number of valid logits per row.  temperature / top_k /
     top_p: [B] device tensors (float32 / int32 / float32), or temperature
     None for one setting for every request (single_temperature,
-    single_top_k).  max_top_k defaults to 1024 when top_k is given."""
+    single_top_k).  max_top_k defaults to 1024 when top_k is given.  beta:
+    also return the per-position acceptance probability; counters: an int64
+    [B, 3] device tensor the call adds its round to."""
     dev = target_logits.device
     W = target_logits.shape[-1]
     V = int(vocab) if vocab is not None else W
@@ -309,5 +334,10 @@ def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, t
     nacc = torch.empty((B,), dtype=torch.int32, device=dev)
     pd = torch.empty(tok_shape, dtype=torch.float32, device=dev)
     qd = torch.empty(tok_shape, dtype=torch.float32, device=dev)
-    spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, out, nacc, pd, qd, ws, stream)
-    return {"out_tokens": out, "num_accepted": nacc, "p_draft": pd, "q_draft": qd, "workspace": ws}
+    bt = torch.empty(tok_shape, dtype=torch.float32, device=dev) if beta else None
+    outputs = make_outputs(out, nacc, pd, qd, bt, counters)
+    spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, outputs, ws, stream)
+    res = {"out_tokens": out, "num_accepted": nacc, "p_draft": pd, "q_draft": qd, "workspace": ws}
+    if beta:
+        res["beta"] = bt
+    return res

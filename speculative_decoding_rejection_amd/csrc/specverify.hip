@@ -280,7 +280,7 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
                        (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, pl.c, k0, k1, out,
                        nacc, p_draft, q_draft, err, (const ReqInfo*)nullptr, pl.kcap, pl.L,
-                       (const float*)nullptr);
+                       (const float*)nullptr, sv::Stats{nullptr, nullptr});
     t.done();
     return check_launch();
   }
@@ -293,7 +293,7 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const ET*)ld, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, pl.c, k0,
                        k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)nullptr,
-                       (const RowCut*)nullptr, pl.L, (const float*)nullptr);
+                       (const RowCut*)nullptr, pl.L, (const float*)nullptr, sv::Stats{nullptr, nullptr});
     t.done();
     s = check_launch();
     if (s != SV_OK) return s;
@@ -317,7 +317,8 @@ sv_status verify_greedy(const Plan& pl, const void* lt, const int32_t* X, int32_
   }
   TimedLaunch t(1, st);
   hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part, X, pl.G, pl.V,
-                     pl.S, out, nacc, targ, err, (const ReqInfo*)nullptr, (float*)nullptr, (float*)nullptr, pl.L);
+                     pl.S, out, nacc, targ, err, (const ReqInfo*)nullptr, (float*)nullptr, (float*)nullptr, pl.L,
+                     sv::Stats{nullptr, nullptr});
   t.done();
   return check_launch();
 }
@@ -337,8 +338,13 @@ struct BatchArgs {
 
 template <typename ET, int MODE>
 sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const void* lt, const void* ld,
-                       const int32_t* X, int32_t* out, int32_t* nacc, float* p_draft, float* q_draft, char* ws,
-                       hipStream_t st) {
+                       const int32_t* X, const sv_outputs& o, char* ws, hipStream_t st) {
+  int32_t* out = o.out_tokens;
+  int32_t* nacc = o.num_accepted;
+  float* p_draft = o.p_draft;
+  float* q_draft = o.q_draft;
+  float* beta = o.beta;
+  int64_t* counters = o.counters;
   const int nrows = pl.rows_t + (MODE == 0 ? pl.rows_d : 0);
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   int* err = (int*)(ws + pl.off_err);
@@ -377,16 +383,28 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
   unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
   {
     TimedLaunch t(1, st);
+    const sv::Stats stats{beta, counters};
     if (pl.K > 0)
       hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
                          (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, 0.f, k0, k1, out,
-                         nacc, p_draft, q_draft, err, (const ReqInfo*)info, pl.kcap, pl.L, qp);
+                         nacc, p_draft, q_draft, err, (const ReqInfo*)info, pl.kcap, pl.L, qp, stats);
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const ET*)ldl, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0,
                        k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
-                       (const RowCut*)(nuc ? cut : nullptr), pl.L, qp);
+                       (const RowCut*)(nuc ? cut : nullptr), pl.L, qp, stats);
     hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part64, X, pl.G,
-                       pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft, q_draft, pl.L);
+                       pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft, q_draft, pl.L,
+                       stats);
+    t.done();
+    if ((s = check_launch()) != SV_OK) return s;
+  }
+  if (beta && MODE != 1) {
+    // Acceptance probability of every position of requests without top-k:
+    // one more read of their target and draft rows.
+    TimedLaunch t(1, st);
+    hipLaunchKernelGGL((sv::beta_full_kernel<ET, MODE == 2>), dim3(pl.B * pl.G), dim3(256), 0, st, (const ET*)lt,
+                       (const ET*)ldl, qp, (const float2*)(ws + pl.off_part), pl.G, pl.V, pl.S, pl.rows_t,
+                       (const ReqInfo*)info, (const RowCut*)(nuc ? cut : nullptr), pl.L, beta);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
@@ -482,12 +500,13 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
 
 sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const sv_layout* layout,
                             const void* target_logits, const void* draft, const int32_t* draft_tokens,
-                            int32_t* out_tokens, int32_t* num_accepted, float* p_draft, float* q_draft,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            const sv_outputs* outputs, void* workspace, size_t workspace_bytes, void* stream) {
   Plan pl;
   sv_status s = make_batch_plan(params, sampling, &pl);
   if (s != SV_OK) return s;
-  s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
+  if (!outputs) return SV_ERR_INVALID_ARG;
+  const sv_outputs o = *outputs;
+  s = check_common(pl, target_logits, draft_tokens, o.out_tokens, o.num_accepted, workspace, workspace_bytes);
   if (s != SV_OK) return s;
   int kind = draft ? SV_DRAFT_LOGITS : SV_DRAFT_ONEHOT;
   if (layout) {
@@ -505,7 +524,9 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
   if (sampling && ((sampling->temperature && !aligned(sampling->temperature, 4)) ||
                    (sampling->top_k && !aligned(sampling->top_k, 4)) || (sampling->top_p && !aligned(sampling->top_p, 4))))
     return SV_ERR_INVALID_ARG;
-  if ((p_draft && !aligned(p_draft, 4)) || (q_draft && !aligned(q_draft, 4))) return SV_ERR_INVALID_ARG;
+  if ((o.p_draft && !aligned(o.p_draft, 4)) || (o.q_draft && !aligned(o.q_draft, 4)) ||
+      (o.beta && !aligned(o.beta, 4)) || (o.counters && !aligned(o.counters, 8)))
+    return SV_ERR_INVALID_ARG;
   BatchArgs ba;
   ba.T = sampling ? sampling->temperature : nullptr;
   ba.K = sampling ? sampling->top_k : nullptr;
@@ -519,22 +540,16 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
   const void* d = kind == SV_DRAFT_ONEHOT ? nullptr : draft;
   if (pl.dtype == SV_F32) {
     if (kind == SV_DRAFT_LOGITS)
-      return verify_batch<float, 0>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted, p_draft,
-                                    q_draft, ws, st);
+      return verify_batch<float, 0>(pl, ba, seed, target_logits, d, draft_tokens, o, ws, st);
     if (kind == SV_DRAFT_PROBS)
-      return verify_batch<float, 2>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted, p_draft,
-                                    q_draft, ws, st);
-    return verify_batch<float, 1>(pl, ba, seed, target_logits, nullptr, draft_tokens, out_tokens, num_accepted,
-                                  p_draft, q_draft, ws, st);
+      return verify_batch<float, 2>(pl, ba, seed, target_logits, d, draft_tokens, o, ws, st);
+    return verify_batch<float, 1>(pl, ba, seed, target_logits, nullptr, draft_tokens, o, ws, st);
   }
   if (kind == SV_DRAFT_LOGITS)
-    return verify_batch<uint16_t, 0>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted,
-                                     p_draft, q_draft, ws, st);
+    return verify_batch<uint16_t, 0>(pl, ba, seed, target_logits, d, draft_tokens, o, ws, st);
   if (kind == SV_DRAFT_PROBS)
-    return verify_batch<uint16_t, 2>(pl, ba, seed, target_logits, d, draft_tokens, out_tokens, num_accepted,
-                                     p_draft, q_draft, ws, st);
-  return verify_batch<uint16_t, 1>(pl, ba, seed, target_logits, nullptr, draft_tokens, out_tokens, num_accepted,
-                                   p_draft, q_draft, ws, st);
+    return verify_batch<uint16_t, 2>(pl, ba, seed, target_logits, d, draft_tokens, o, ws, st);
+  return verify_batch<uint16_t, 1>(pl, ba, seed, target_logits, nullptr, draft_tokens, o, ws, st);
 }
 
 sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream) {

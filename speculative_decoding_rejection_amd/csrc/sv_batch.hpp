@@ -164,27 +164,6 @@ __device__ __forceinline__ bool row_exists(const Layout& L, int rows_t, int G, i
   return r - b * G < L.len(b, G);
 }
 
-// Bitonic sort of a[0, n) into descending order by one wave (n a power of
-// two).
-__device__ __forceinline__ void wave_sort_desc(uint64_t* a, int n) {
-  const int lane = lane_id();
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = lane; i < n / 2; i += kWave) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const uint64_t x = a[lo], y = a[hi];
-        if ((x < y) == desc) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      wave_lds_sync();
-    }
-  }
-}
-
 // The same by a whole workgroup of NT threads.
 template <int NT>
 __device__ __forceinline__ void block_sort_desc(uint64_t* a, int n) {
@@ -543,6 +522,79 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
       if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / zk)};
       else cut[row] = RowCut{0ull, lmax, (float)(1.0 / Z)};
     }
+  }
+}
+
+// ===========================================================================
+// Acceptance probability of every draft position of requests without top-k
+// (draft logits or probabilities): beta_j = sum_y min(p_j(y), q_j(y)) (page
+// "초안 모델로 생성 속도를 높이는 추측 디코딩", section "수락률 α와 기대 속도
+// 향상": alpha is its expectation).  One workgroup per (request, position);
+// both rows are read once more, with the stats (or nucleus cuts) of the row
+// pass.  QP: q given as fp32 probabilities.
+// ===========================================================================
+template <typename ET, bool QP>
+__global__ __launch_bounds__(256) void beta_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                        const float* __restrict__ qp,
+                                                        const float2* __restrict__ part, int G, int V, int S,
+                                                        int rows_t, const ReqInfo* __restrict__ info,
+                                                        const RowCut* __restrict__ cut, Layout L,
+                                                        float* __restrict__ beta) {
+  constexpr int NT = 256, NW = NT / kWave;
+  const int b = blockIdx.x / G, j = blockIdx.x - b * G;
+  const ReqInfo ri = info[b];
+  if (ri.kind != kReqFull || j >= L.len(b, G)) return;  // uniform over the workgroup
+  const float c = ri.c;
+  const bool nuc = ri.top_p < 1.f;
+  const size_t rt = (size_t)b * (G + 1) + j, rd = (size_t)rows_t + (size_t)b * G + j;
+  // Row stats: the nucleus cut, or the merged softmax partials.
+  float mp, izp, mq = 0.f, izq = 0.f;
+  uint64_t kp = 0ull, kq = 0ull;
+  if (nuc) {
+    const RowCut a = cut[rt];
+    mp = a.m;
+    izp = a.inv_z;
+    kp = a.kappa;
+    if (!QP) {
+      const RowCut d = cut[rd];
+      mq = d.m;
+      izq = d.inv_z;
+      kq = d.kappa;
+    }
+  } else {
+    float Z;
+    merge_row_lane(part + rt * S, S, c, mp, Z);
+    izp = 1.f / Z;
+    if (!QP) {
+      merge_row_lane(part + rd * S, S, c, mq, Z);
+      izq = 1.f / Z;
+    }
+  }
+  const ET* rp = lt + L.trow(b, G, j) * (size_t)L.ts;
+  const size_t dq = L.tok(b, G, j) * (size_t)L.ds;
+  float acc = 0.f;
+  for (int y = threadIdx.x; y < V; y += NT) {
+    const float l = Elem<ET>::load1(rp + y);
+    float p = __builtin_amdgcn_exp2f((l - mp) * c) * izp;
+    if (nuc && make_key(l, (uint32_t)y) < kp) p = 0.f;
+    float q;
+    if (QP) {
+      q = qp[dq + y];
+    } else {
+      const float lq = Elem<ET>::load1(ld + dq + y);
+      q = __builtin_amdgcn_exp2f((lq - mq) * c) * izq;
+      if (nuc && make_key(lq, (uint32_t)y) < kq) q = 0.f;
+    }
+    acc += fminf(p, q);
+  }
+  acc = wave_sum_f(acc);
+  __shared__ float red[NW];
+  if (lane_id() == 0) red[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int k = 0; k < NW; ++k) t += red[k];
+    beta[L.tok(b, G, j)] = t;
   }
 }
 

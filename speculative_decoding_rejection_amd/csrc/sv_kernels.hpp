@@ -60,6 +60,44 @@ struct Layout {
   }
 };
 
+// Optional statistics of a call: per-position acceptance probability beta
+// (laid out like the draft tokens) and per-request counters [B][3] (+=
+// draft positions, accepted drafts, 1).
+struct Stats {
+  float* beta;
+  int64_t* counters;
+};
+
+// Adds this call's round to request b's counters (one writer per request).
+__device__ __forceinline__ void count_round(const Stats& st, int b, int g, int n) {
+  if (!st.counters) return;
+  int64_t* c = st.counters + 3 * (size_t)b;
+  c[0] += g;
+  c[1] += n;
+  c[2] += 1;
+}
+
+// Bitonic sort of a[0, n) into descending order by one wave (n a power of
+// two; LDS).
+__device__ __forceinline__ void wave_sort_desc(uint64_t* a, int n) {
+  const int lane = lane_id();
+  for (int size = 2; size <= n; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = lane; i < n / 2; i += kWave) {
+        const int lo = 2 * i - (i & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const uint64_t x = a[lo], y = a[hi];
+        if ((x < y) == desc) {
+          a[lo] = y;
+          a[hi] = x;
+        }
+      }
+      wave_lds_sync();
+    }
+  }
+}
+
 // The logit row of padded row index `row` (target rows first), or null if
 // the request has no such row (ragged calls).
 template <typename ET>
@@ -811,9 +849,12 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
                                                           int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                                           float* __restrict__ p_draft, float* __restrict__ q_draft,
                                                           int* __restrict__ err, const ReqInfo* __restrict__ info,
-                                                          int kstride, Layout L, const float* __restrict__ qp) {
+                                                          int kstride, Layout L, const float* __restrict__ qp,
+                                                          Stats stats) {
   extern __shared__ uint8_t rejected[];  // [G]
   __shared__ uint64_t qkeys[1024];
+  // beta with draft logits: each wave's q candidates sorted by token index.
+  __shared__ uint64_t qidx_sh[MODE == 0 ? 4 : 1][MODE == 0 ? 1024 : 1];
   __shared__ int n_sh;
   const int b = blockIdx.x;
   if (info) {
@@ -835,11 +876,68 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     const CandStats sp = cand_stats(ct + (size_t)j * kstride, K, c);
     const float px = valid ? cand_prob(ct + (size_t)j * kstride, K, sp, c, x) : 0.f;
     float qx = valid ? 1.f : 0.f;
+    CandStats sq{0.f, 0.f};
     if (MODE == 0) {
-      const CandStats sq = cand_stats(cd + (size_t)j * kstride, K, c);
+      sq = cand_stats(cd + (size_t)j * kstride, K, c);
       qx = valid ? cand_prob(cd + (size_t)j * kstride, K, sq, c, x) : 0.f;
     } else if (MODE == 2) {
       qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
+    }
+    if (stats.beta) {
+      // beta_j = sum over p's kept tokens of min(p(y), q(y)).
+      float bj = px;  // one-hot q
+      if (MODE != 1) {
+        const uint64_t* pk = ct + (size_t)j * kstride;
+        float part = 0.f;
+        if (MODE == 0) {
+          // q's kept tokens as ((index + 1) << 32 | value bits), sorted
+          // descending, searched by index.
+          uint64_t* qs = qidx_sh[MODE == 0 ? w : 0];
+          int n2 = kWave;
+          while (n2 < K) n2 <<= 1;
+          const uint64_t* qk = cd + (size_t)j * kstride;
+          for (int i = lane; i < n2; i += kWave) {
+            uint64_t e = 0ull;
+            if (i < K) {
+              const uint64_t k = qk[i];
+              if (k) e = ((uint64_t)(key_index(k) + 1u) << 32) | (uint64_t)__float_as_uint(key_value(k));
+            }
+            qs[i] = e;
+          }
+          wave_lds_sync();
+          wave_sort_desc(qs, n2);
+          for (int i = lane; i < K; i += kWave) {
+            const uint64_t k = pk[i];
+            if (!k) continue;
+            const uint32_t y1 = key_index(k) + 1u;
+            const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
+            float q = 0.f;
+            int lo = 0, hi = n2 - 1;
+            while (lo <= hi) {
+              const int mid = (lo + hi) >> 1;
+              const uint32_t idx = (uint32_t)(qs[mid] >> 32);
+              if (idx == y1) {
+                q = __builtin_amdgcn_exp2f((__uint_as_float((uint32_t)qs[mid]) - sq.m) * c) * sq.inv_z;
+                break;
+              }
+              if (idx > y1) lo = mid + 1;
+              else hi = mid - 1;
+            }
+            part += fminf(p, q);
+          }
+          wave_lds_sync();  // qs is rewritten for this wave's next position
+        } else {
+          const float* qrow = qp + xj * (size_t)L.ds;
+          for (int i = lane; i < K; i += kWave) {
+            const uint64_t k = pk[i];
+            if (!k) continue;
+            const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
+            part += fminf(p, qrow[key_index(k)]);
+          }
+        }
+        bj = wave_sum_f(part);
+      }
+      if (lane == 0) stats.beta[xj] = bj;
     }
     if (lane == 0) {
       if (p_draft) p_draft[xj] = px;
@@ -921,7 +1019,10 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     else if (j == n) t = win ? (int32_t)key_index(win) : -1;
     o[j] = t;
   }
-  if (lane == 0) nacc[b] = n;
+  if (lane == 0) {
+    nacc[b] = n;
+    count_round(stats, b, g, n);
+  }
 }
 
 // ===========================================================================
@@ -967,7 +1068,7 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
                                                          unsigned long long* __restrict__ slots,
                                                          int* __restrict__ err, const ReqInfo* __restrict__ info,
                                                          const RowCut* __restrict__ cut, Layout L,
-                                                         const float* __restrict__ qp) {
+                                                         const float* __restrict__ qp, Stats stats) {
   const int b = blockIdx.x;
   const int lane = lane_id();
   bool nuc = false;
@@ -1011,6 +1112,7 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
       }
       if (q_draft) q_draft[xj] = qx;
       if (p_draft) p_draft[xj] = px;
+      if (MODE == 1 && stats.beta) stats.beta[xj] = px;  // one-hot q: beta = p(x)
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
@@ -1054,6 +1156,7 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
     nacc[b] = n;
     desc[b] = d;
     slots[3 * b] = 0ull;  // best race key
+    count_round(stats, b, g, n);
   }
 }
 
@@ -1236,7 +1339,7 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
                                                            int32_t* __restrict__ targ, int* __restrict__ err,
                                                            const ReqInfo* __restrict__ info,
                                                            float* __restrict__ p_draft, float* __restrict__ q_draft,
-                                                           Layout L) {
+                                                           Layout L, Stats stats) {
   // Lane j handles position j (chunks of 64): the target argmax of row j
   // (max over the row's partial keys), written to out[j] for now, and the
   // match test; the first mismatch is one ballot.  In a batch call only
@@ -1266,6 +1369,7 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
         mis = !valid || x != a;
         if (p_draft) p_draft[xj] = mis ? 0.f : 1.f;
         if (q_draft) q_draft[xj] = 1.f;
+        if (stats.beta) stats.beta[xj] = mis ? 0.f : 1.f;
       }
     }
     const uint64_t mm = ballot(mis);
@@ -1277,7 +1381,10 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
     if (j < n) o[j] = X[L.tok(b, G, j)];
     else if (j > n) o[j] = -1;
   }
-  if (lane == 0) nacc[b] = n;
+  if (lane == 0) {
+    nacc[b] = n;
+    count_round(stats, b, g, n);
+  }
 }
 
 }  // namespace sv

@@ -98,8 +98,9 @@ def _call_batch(sv, params, sampling, ws_bytes=1 << 20, null=None, layout=None, 
         args[null] = None
     sp = ctypes.byref(sampling) if sampling is not None else None
     lp = ctypes.byref(layout) if layout is not None else None
-    return lib.spec_verify_batch(ctypes.byref(params), sp, lp, args[0], draft, args[1], args[2], args[3], None,
-                                 None, args[4], ws_bytes, None)
+    outs = sv.SvOutputs(args[2], args[3], None, None, None, None)
+    return lib.spec_verify_batch(ctypes.byref(params), sp, lp, args[0], draft, args[1], ctypes.byref(outs), args[4],
+                                 ws_bytes, None)
 
 
 def test_batch_argument_errors(sv):
@@ -151,3 +152,14 @@ def test_batch_single_setting_and_layout_errors(sv):
     assert _call_batch(sv, p, ok, ws_bytes=16, layout=L(sv.SV_DRAFT_LOGITS, 0, 5120, 5008, fake), draft=d) == \
         sv.SV_ERR_WORKSPACE
     assert _call_batch(sv, p, ok, layout=L(sv.SV_DRAFT_LOGITS, 0, 0, 0, fake + 2), draft=d) == sv.SV_ERR_INVALID_ARG
+
+
+def test_batch_outputs_checks(sv):
+    lib = sv.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    p = sv.make_params(4, 3, 5000, sv.SV_BF16, 0.7, 0, 1)
+    assert lib.spec_verify_batch(ctypes.byref(p), None, None, fake, None, fake, None, fake, 1 << 20, None) == \
+        sv.SV_ERR_INVALID_ARG
+    outs = sv.SvOutputs(1 << 20, 1 << 20, None, None, None, (1 << 20) + 4)  # counters must be 8-byte aligned
+    assert lib.spec_verify_batch(ctypes.byref(p), None, None, fake, None, fake, ctypes.byref(outs), fake, 1 << 20,
+                                 None) == sv.SV_ERR_INVALID_ARG

@@ -878,3 +878,59 @@ def test_zero_draft_positions_emit_a_draw_from_p0():
     assert (res["num_accepted"] == 0).all() and (res["out_tokens"][:, 1] == -1).all()
     counts = np.bincount(res["out_tokens"][:, 0], minlength=4)
     assert stats.chisquare(counts, np.array([0.5, 0.3, 0.15, 0.05]) * n).pvalue > 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Per-position acceptance probability beta through the batch path
+# ---------------------------------------------------------------------------
+
+def test_beta_worked_example_with_draft_probabilities():
+    """The 5-token example with q handed over as probabilities: beta =
+    sum min(p, q) = 0.75 as printed; with one-hot drafts beta = p(x)."""
+    p, q, g = _worked()
+    lt = _f32_logits(p)[None, None, :].repeat(2, axis=1)
+    one = np.ones(1, np.float32)
+    res = oracle.verify_batch(lt, None, np.zeros((1, 1), np.int32), one, np.zeros(1, np.int32), one,
+                              draft_probs=np.asarray(q, np.float32)[None, None, :], diagnostics=True)
+    assert abs(res["beta"][0, 0] - float(g["sum_min_pq"][0])) < 1e-6
+    res = oracle.verify_batch(lt, None, np.array([[int(np.argmax(q))]], np.int32), one, np.zeros(1, np.int32), one,
+                              diagnostics=True)
+    assert abs(res["beta"][0, 0] - float(g["p_at_argmax_q"][0])) < 1e-6
+
+
+def test_beta_closed_forms():
+    rng = np.random.default_rng(61)
+    n, G, V = 12, 3, 50
+    lt = (rng.standard_normal((n, G + 1, V)) * 2).astype(np.float32)
+    x = rng.integers(0, V, (n, G)).astype(np.int32)
+    T = np.full(n, 0.8, np.float32)
+    K = np.zeros(n, np.int32)
+    P = np.ones(n, np.float32)
+    p = np.stack([np.stack([oracle.row_probs(lt[r, j], 0.8) for j in range(G)]) for r in range(n)])
+    # q = p (up to fp32 rounding): beta = 1.
+    res = oracle.verify_batch(lt, None, x, T, K, P, draft_probs=p.astype(np.float32), diagnostics=True)
+    np.testing.assert_allclose(res["beta"], 1.0, atol=1e-6)
+    # q only where a top-5 target has no mass: beta = 0.
+    K5 = np.full(n, 5, np.int32)
+    p5 = np.stack([np.stack([oracle.row_probs(lt[r, j], 0.8, 5) for j in range(G)]) for r in range(n)])
+    q0 = (p5 == 0).astype(np.float32)
+    q0 /= q0.sum(-1, keepdims=True)
+    res = oracle.verify_batch(lt, None, x, T, K5, P, draft_probs=q0, diagnostics=True, max_top_k=5)
+    np.testing.assert_array_equal(res["beta"], 0.0)
+    # Temperature 0: beta is the argmax indicator.
+    res = oracle.verify_batch(lt, None, x, np.zeros(n, np.float32), K, P, diagnostics=True)
+    np.testing.assert_array_equal(res["beta"], (x == np.argmax(lt[:, :G], axis=-1)).astype(np.float64))
+
+
+def test_decay_sigmas_give_the_pages_rates():
+    """The draft-noise levels of the decaying-acceptance workload give mean
+    beta = sum min(p, q) of 0.951, 0.889, 0.852 at positions 0, 1, 2 (the
+    Gemma run's per-position rates on the draft-model page), on rows other
+    than the ones they were solved on."""
+    import workloads
+    wl = workloads.ROUNDS_WORKLOADS["rounds_decay_bf16_b512_g3_v128256"].scaled(B=32, data_seed=11)
+    inp = workloads.generate(wl)
+    h = workloads.to_host_arrays
+    res = oracle.verify(oracle.MODE_PROB, h(inp["target_logits"]), h(inp["draft_logits"]), h(inp["draft_tokens"]),
+                        temperature=wl.temperature, seed=1, diagnostics=True)
+    np.testing.assert_allclose(res["beta"].mean(axis=0), workloads.DECAY_ALPHAS, atol=0.01)

@@ -62,6 +62,7 @@ class Workload:
     chunk: int = 8        # requests generated per generator call
     mix: tuple = ()       # entry "batch": ((temperature, top_k, top_p), ...) request classes
     lengths: tuple = ()   # entry "batch": (lo, hi) draft positions per request, uniform (ragged rows)
+    sigma_pos: tuple = ()  # draft noise per position (G values), replacing draft_sigma
     draft_probs: bool = False  # entry "batch": the drafter hands over fp32 probabilities
 
     @property
@@ -143,6 +144,21 @@ BATCH_WORKLOADS = {
         mix=_MIX4, lengths=(1, 7), draft_probs=True),
 }
 ALL_WORKLOADS = {**WORKLOADS, **BATCH_WORKLOADS}
+
+# Multi-round workload with acceptance decaying along the draft: the draft
+# noise of position j is chosen so that sum_y min(p, q) averages 0.951, 0.889
+# and 0.852 at gamma = 3, the per-position rates of the Gemma run on the
+# draft-model page (section "맥북 실측: Gemma 4 12B").  The noise levels come
+# from tests/golden/make_decay_sigmas.py (the oracle's beta, bisection); a CPU
+# test re-checks them.
+DECAY_ALPHAS = (0.951, 0.889, 0.852)
+DECAY_SIGMAS = (0.1210, 0.2765, 0.3707)
+ROUNDS_WORKLOADS = {
+    "rounds_decay_bf16_b512_g3_v128256": Workload(
+        "rounds_decay_bf16_b512_g3_v128256", "prob", 512, 3, 128256, "bf16", 1.0, 0, 3.0, (0.0, 0.0),
+        sigma_pos=DECAY_SIGMAS),
+}
+ALL_WORKLOADS.update(ROUNDS_WORKLOADS)
 
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "prob_topk64_bf16_b1024_g8_v256000"
@@ -271,6 +287,8 @@ def _chunk(wl: Workload, c: int, gen: torch.Generator, device, settings=None):
     if wl.has_draft_logits:
         lo, hi = wl.draft_sigma
         sig = lo + (hi - lo) * torch.rand((c, 1, 1), generator=gen, device=device, dtype=torch.float32)
+        if wl.sigma_pos:
+            sig = torch.tensor(wl.sigma_pos, dtype=torch.float32, device=device).reshape(1, G, 1)
         noise = torch.randn((c, G, V), generator=gen, device=device, dtype=torch.float32)
         ld = (lt[:, :G].float() + sig * noise).to(wl.torch_dtype)
     if wl.entry == "batch":
@@ -313,4 +331,5 @@ def to_host_arrays(t: torch.Tensor | None):
 
 
 __all__ = ["Workload", "WORKLOADS", "BATCH_WORKLOADS", "ALL_WORKLOADS", "WORKLOAD_ORDER", "HEADLINE",
+           "ROUNDS_WORKLOADS", "DECAY_ALPHAS",
            "generate", "batch_settings", "pack_ragged", "with_stride", "to_host_arrays"]
