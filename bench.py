@@ -110,13 +110,23 @@ def rounds_driver(sv, wl, rounds: int, device, seed_offset: int = 1000) -> dict:
 
     G, B = wl.G, wl.B
     counters = torch.zeros((B, 3), dtype=torch.int64, device=device)
-    ns, betas = [], []
+    ns, betas, ms_stats, ms_plain = [], [], [], []
+    stream = torch.cuda.current_stream()
     for r in range(rounds):
         inp = workloads.generate(wl.scaled(data_seed=wl.data_seed + seed_offset + r), device=device)
         ld = inp["draft_logits"] if wl.entry == "prob" else None
-        res = sv.verify_batch(inp["target_logits"], inp["draft_tokens"], ld, single_temperature=wl.temperature,
-                              single_top_k=wl.top_k, seed=wl.verify_seed + r, beta=True, counters=counters)
+        kw = dict(single_temperature=wl.temperature, single_top_k=wl.top_k, seed=wl.verify_seed + r)
+        # The same call without statistics, timed for comparison.
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record(stream)
+        sv.verify_batch(inp["target_logits"], inp["draft_tokens"], ld, **kw)
+        e1.record(stream)
+        res = sv.verify_batch(inp["target_logits"], inp["draft_tokens"], ld, beta=True, counters=counters, **kw)
+        e2.record(stream)
         torch.cuda.synchronize()
+        if r > 0:  # the first round warms up
+            ms_plain.append(e0.elapsed_time(e1))
+            ms_stats.append(e1.elapsed_time(e2))
         ns.append(res["num_accepted"].cpu().numpy())
         betas.append(res["beta"].cpu().numpy())
     n = np.concatenate(ns)
@@ -131,6 +141,8 @@ def rounds_driver(sv, wl, rounds: int, device, seed_offset: int = 1000) -> dict:
             "beta_by_position": [float(v) for v in bmean],
             "counters": {"draft_n": int(c[0]), "draft_n_accepted": int(c[1]), "draft_rounds": int(c[2])},
             "mean_accepted_per_round": float(c[1] / c[2]) if c[2] else 0.0,
+            "ms_per_call": float(np.mean(ms_plain)) if ms_plain else None,
+            "ms_per_call_with_beta_and_counters": float(np.mean(ms_stats)) if ms_stats else None,
             "_n": n, "_counters": counters.cpu().numpy()}
 
 

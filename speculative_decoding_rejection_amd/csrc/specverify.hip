@@ -398,6 +398,14 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
+  if (beta && MODE != 1 && pl.K > 0) {
+    TimedLaunch t(1, st);
+    hipLaunchKernelGGL((sv::beta_topk_kernel<MODE>), dim3((pl.B * pl.G + 3) / 4), dim3(256), 0, st,
+                       (const uint64_t*)(ws + pl.off_cand), qp, pl.B, pl.G, pl.kcap, pl.rows_t, (const ReqInfo*)info,
+                       pl.L, beta);
+    t.done();
+    if ((s = check_launch()) != SV_OK) return s;
+  }
   if (beta && MODE != 1) {
     // Acceptance probability of every position of requests without top-k:
     // one more read of their target and draft rows.

@@ -526,13 +526,85 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
 }
 
 // ===========================================================================
-// Acceptance probability of every draft position of requests without top-k
-// (draft logits or probabilities): beta_j = sum_y min(p_j(y), q_j(y)) (page
-// "초안 모델로 생성 속도를 높이는 추측 디코딩", section "수락률 α와 기대 속도
-// 향상": alpha is its expectation).  One workgroup per (request, position);
-// both rows are read once more, with the stats (or nucleus cuts) of the row
-// pass.  QP: q given as fp32 probabilities.
+// Acceptance probability of every draft position: beta_j = sum_y
+// min(p_j(y), q_j(y)) (page "초안 모델로 생성 속도를 높이는 추측 디코딩",
+// section "수락률 α와 기대 속도 향상": alpha is its expectation).  Launched
+// only when a caller asks for beta.
 // ===========================================================================
+
+// Top-k requests with draft logits (MODE 0) or probabilities (MODE 2): one
+// wave per (request, position), over the kept tokens of p.  MODE 0 sorts q's
+// kept tokens by token index in the wave's LDS and searches them.
+template <int MODE>
+__global__ __launch_bounds__(256) void beta_topk_kernel(const uint64_t* __restrict__ cand,
+                                                        const float* __restrict__ qp, int B, int G, int kstride,
+                                                        int rows_t, const ReqInfo* __restrict__ info, Layout L,
+                                                        float* __restrict__ beta) {
+  __shared__ uint64_t qs_sh[MODE == 0 ? 4 : 1][MODE == 0 ? 1024 : 1];
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int pos = blockIdx.x * 4 + w;
+  if (pos >= B * G) return;  // wave-uniform; no workgroup barrier below
+  const int b = pos / G, j = pos - b * G;
+  const ReqInfo ri = info[b];
+  if (ri.kind != kReqTopk || j >= L.len(b, G)) return;
+  const int K = ri.K;
+  const float c = ri.c;
+  const uint64_t* pk = cand + ((size_t)b * (G + 1) + j) * kstride;
+  const CandStats sp = cand_stats(pk, K, c);
+  float part = 0.f;
+  if (MODE == 0) {
+    const uint64_t* qk = cand + ((size_t)rows_t + (size_t)b * G + j) * kstride;
+    const CandStats sq = cand_stats(qk, K, c);
+    // q's kept tokens as ((index + 1) << 32 | value bits), sorted descending.
+    uint64_t* qs = qs_sh[MODE == 0 ? w : 0];
+    int n2 = kWave;
+    while (n2 < K) n2 <<= 1;
+    for (int i = lane; i < n2; i += kWave) {
+      uint64_t e = 0ull;
+      if (i < K) {
+        const uint64_t k = qk[i];
+        if (k) e = ((uint64_t)(key_index(k) + 1u) << 32) | (uint64_t)__float_as_uint(key_value(k));
+      }
+      qs[i] = e;
+    }
+    wave_lds_sync();
+    wave_sort_desc(qs, n2);
+    for (int i = lane; i < K; i += kWave) {
+      const uint64_t k = pk[i];
+      if (!k) continue;
+      const uint32_t y1 = key_index(k) + 1u;
+      const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
+      float q = 0.f;
+      int lo = 0, hi = n2 - 1;
+      while (lo <= hi) {
+        const int mid = (lo + hi) >> 1;
+        const uint32_t idx = (uint32_t)(qs[mid] >> 32);
+        if (idx == y1) {
+          q = __builtin_amdgcn_exp2f((__uint_as_float((uint32_t)qs[mid]) - sq.m) * c) * sq.inv_z;
+          break;
+        }
+        if (idx > y1) lo = mid + 1;
+        else hi = mid - 1;
+      }
+      part += fminf(p, q);
+    }
+  } else {
+    const float* qrow = qp + L.tok(b, G, j) * (size_t)L.ds;
+    for (int i = lane; i < K; i += kWave) {
+      const uint64_t k = pk[i];
+      if (!k) continue;
+      const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
+      part += fminf(p, qrow[key_index(k)]);
+    }
+  }
+  part = wave_sum_f(part);
+  if (lane == 0) beta[L.tok(b, G, j)] = part;
+}
+
+// Requests without top-k (draft logits or probabilities): one workgroup per
+// (request, position) reads both rows once more (16-byte vectors), with the
+// stats (or nucleus cuts) of the row pass.  QP: q given as fp32
+// probabilities.
 template <typename ET, bool QP>
 __global__ __launch_bounds__(256) void beta_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                         const float* __restrict__ qp,
@@ -540,7 +612,7 @@ __global__ __launch_bounds__(256) void beta_full_kernel(const ET* __restrict__ l
                                                         int rows_t, const ReqInfo* __restrict__ info,
                                                         const RowCut* __restrict__ cut, Layout L,
                                                         float* __restrict__ beta) {
-  constexpr int NT = 256, NW = NT / kWave;
+  constexpr int NT = 256, NW = NT / kWave, EPV = Elem<ET>::kPerVec;
   const int b = blockIdx.x / G, j = blockIdx.x - b * G;
   const ReqInfo ri = info[b];
   if (ri.kind != kReqFull || j >= L.len(b, G)) return;  // uniform over the workgroup
@@ -572,26 +644,46 @@ __global__ __launch_bounds__(256) void beta_full_kernel(const ET* __restrict__ l
   }
   const ET* rp = lt + L.trow(b, G, j) * (size_t)L.ts;
   const size_t dq = L.tok(b, G, j) * (size_t)L.ds;
-  float acc = 0.f;
-  for (int y = threadIdx.x; y < V; y += NT) {
-    const float l = Elem<ET>::load1(rp + y);
+  const ET* rq = QP ? nullptr : ld + dq;
+  const float* rqp = QP ? qp + dq : nullptr;
+  auto term = [&](float l, float lq, int y) -> float {
     float p = __builtin_amdgcn_exp2f((l - mp) * c) * izp;
     if (nuc && make_key(l, (uint32_t)y) < kp) p = 0.f;
-    float q;
-    if (QP) {
-      q = qp[dq + y];
-    } else {
-      const float lq = Elem<ET>::load1(ld + dq + y);
+    float q = lq;  // QP: the given probability
+    if (!QP) {
       q = __builtin_amdgcn_exp2f((lq - mq) * c) * izq;
       if (nuc && make_key(lq, (uint32_t)y) < kq) q = 0.f;
     }
-    acc += fminf(p, q);
+    return fminf(p, q);
+  };
+  Slice<ET> sl(rp, 0, V);
+  const bool q_vec = !QP && ((((uintptr_t)rp) ^ ((uintptr_t)rq)) & 15u) == 0u;
+  const uint4* vp = sl.vecs();
+  const uint4* vq = q_vec ? (const uint4*)(rq + sl.head) : nullptr;
+  float acc = 0.f;
+  const int tid = threadIdx.x;
+  if (tid < sl.nscalar()) {
+    const int y = sl.scalar_index(tid);
+    acc += term(Elem<ET>::load1(rp + y), QP ? rqp[y] : Elem<ET>::load1(rq + y), y);
+  }
+  for (int i = tid; i < sl.nvec; i += NT) {
+    float fp[EPV], fq[EPV];
+    Elem<ET>::unpack(load_stream(vp + i), fp);
+    const int y0 = sl.vec_index0(i);
+    if (q_vec) {
+      Elem<ET>::unpack(load_stream(vq + i), fq);
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) fq[k] = QP ? rqp[y0 + k] : Elem<ET>::load1(rq + y0 + k);
+    }
+#pragma unroll
+    for (int k = 0; k < EPV; ++k) acc += term(fp[k], fq[k], y0 + k);
   }
   acc = wave_sum_f(acc);
   __shared__ float red[NW];
-  if (lane_id() == 0) red[threadIdx.x / kWave] = acc;
+  if (lane_id() == 0) red[tid / kWave] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     float t = 0.f;
     for (int k = 0; k < NW; ++k) t += red[k];
     beta[L.tok(b, G, j)] = t;

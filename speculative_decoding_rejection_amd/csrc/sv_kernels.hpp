@@ -853,8 +853,6 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
                                                           Stats stats) {
   extern __shared__ uint8_t rejected[];  // [G]
   __shared__ uint64_t qkeys[1024];
-  // beta with draft logits: each wave's q candidates sorted by token index.
-  __shared__ uint64_t qidx_sh[MODE == 0 ? 4 : 1][MODE == 0 ? 1024 : 1];
   __shared__ int n_sh;
   const int b = blockIdx.x;
   if (info) {
@@ -876,72 +874,16 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     const CandStats sp = cand_stats(ct + (size_t)j * kstride, K, c);
     const float px = valid ? cand_prob(ct + (size_t)j * kstride, K, sp, c, x) : 0.f;
     float qx = valid ? 1.f : 0.f;
-    CandStats sq{0.f, 0.f};
     if (MODE == 0) {
-      sq = cand_stats(cd + (size_t)j * kstride, K, c);
+      const CandStats sq = cand_stats(cd + (size_t)j * kstride, K, c);
       qx = valid ? cand_prob(cd + (size_t)j * kstride, K, sq, c, x) : 0.f;
     } else if (MODE == 2) {
       qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
     }
-    if (stats.beta) {
-      // beta_j = sum over p's kept tokens of min(p(y), q(y)).
-      float bj = px;  // one-hot q
-      if (MODE != 1) {
-        const uint64_t* pk = ct + (size_t)j * kstride;
-        float part = 0.f;
-        if (MODE == 0) {
-          // q's kept tokens as ((index + 1) << 32 | value bits), sorted
-          // descending, searched by index.
-          uint64_t* qs = qidx_sh[MODE == 0 ? w : 0];
-          int n2 = kWave;
-          while (n2 < K) n2 <<= 1;
-          const uint64_t* qk = cd + (size_t)j * kstride;
-          for (int i = lane; i < n2; i += kWave) {
-            uint64_t e = 0ull;
-            if (i < K) {
-              const uint64_t k = qk[i];
-              if (k) e = ((uint64_t)(key_index(k) + 1u) << 32) | (uint64_t)__float_as_uint(key_value(k));
-            }
-            qs[i] = e;
-          }
-          wave_lds_sync();
-          wave_sort_desc(qs, n2);
-          for (int i = lane; i < K; i += kWave) {
-            const uint64_t k = pk[i];
-            if (!k) continue;
-            const uint32_t y1 = key_index(k) + 1u;
-            const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
-            float q = 0.f;
-            int lo = 0, hi = n2 - 1;
-            while (lo <= hi) {
-              const int mid = (lo + hi) >> 1;
-              const uint32_t idx = (uint32_t)(qs[mid] >> 32);
-              if (idx == y1) {
-                q = __builtin_amdgcn_exp2f((__uint_as_float((uint32_t)qs[mid]) - sq.m) * c) * sq.inv_z;
-                break;
-              }
-              if (idx > y1) lo = mid + 1;
-              else hi = mid - 1;
-            }
-            part += fminf(p, q);
-          }
-          wave_lds_sync();  // qs is rewritten for this wave's next position
-        } else {
-          const float* qrow = qp + xj * (size_t)L.ds;
-          for (int i = lane; i < K; i += kWave) {
-            const uint64_t k = pk[i];
-            if (!k) continue;
-            const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
-            part += fminf(p, qrow[key_index(k)]);
-          }
-        }
-        bj = wave_sum_f(part);
-      }
-      if (lane == 0) stats.beta[xj] = bj;
-    }
     if (lane == 0) {
       if (p_draft) p_draft[xj] = px;
       if (q_draft) q_draft[xj] = qx;
+      if (MODE == 1 && stats.beta) stats.beta[xj] = px;  // one-hot q: beta = p(x)
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
