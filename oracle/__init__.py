@@ -73,7 +73,7 @@ def _load():
                                        ctypes.POINTER(ctypes.c_double)]
     lib.sv_ref_row_probs_p.restype = ctypes.c_int
     lib.sv_ref_verify_ex.argtypes = ([ctypes.c_int] * 5 + [ctypes.c_void_p] * 3 + [ctypes.c_int, ctypes.c_uint64]
-                                     + [ctypes.c_void_p] * 16 + [ctypes.c_int])
+                                     + [ctypes.c_void_p] * 18 + [ctypes.c_int])
     lib.sv_ref_verify_ex.restype = ctypes.c_int
     lib.sv_ref_row_argmax.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
     lib.sv_ref_row_argmax.restype = ctypes.c_int
@@ -203,7 +203,7 @@ def verify(mode: int, target_logits, draft_logits, draft_tokens, *, temperature:
 
 def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, top_p, *, max_top_k: int = 1024,
                  seed: int = 0, req_ids=None, diagnostics: bool = False, nthreads: int = 0, draft_probs=None,
-                 lengths=None) -> dict:
+                 lengths=None, match: bool = False, parents=None) -> dict:
     """Run the oracle with per-request settings.
 
     Arrays are padded: target_logits [n, G+1, V], draft_logits [n, G, V]
@@ -214,6 +214,11 @@ def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, 
     greedy request), top_k [n] int32, top_p [n] float32, taken at the
     caller's fp32 / int32 precision.  Per-position outputs are [n, G], NaN
     after a request's length.
+
+    match: token-only drafts verified by sampler-match; draft position j is
+    node j + 1 of a tree whose root (node 0) has target row 0; parents [n, G]
+    gives each draft node's parent node (0..j), None for chains.  Returns
+    path_nodes [n, G+1] (accepted nodes in order, -1 after).
     """
     lib = _load()
     lt, dt = _logits_bytes(target_logits)
@@ -221,7 +226,9 @@ def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, 
     G = G1 - 1
     kind = 1
     ld = qp = None
-    if draft_probs is not None:
+    if match:
+        kind = 3
+    elif draft_probs is not None:
         kind = 2
         qp = np.ascontiguousarray(draft_probs, dtype=np.float32)
         if qp.shape != (n, G, V):
@@ -242,6 +249,11 @@ def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, 
     ld_p = (np.ascontiguousarray(np.concatenate([ld[r, :g[r]] for r in range(n)])) if ld is not None else None)
     qp_p = (np.ascontiguousarray(np.concatenate([qp[r, :g[r]] for r in range(n)])) if qp is not None else None)
     x_p = np.ascontiguousarray(np.concatenate([x[r, :g[r]] for r in range(n)])) if n else x.reshape(0)
+    par_p = None
+    if parents is not None:
+        par = np.ascontiguousarray(parents, dtype=np.int32)
+        par_p = np.ascontiguousarray(np.concatenate([par[r, :g[r]] for r in range(n)])) if n else par.reshape(0)
+    path = np.empty((n, G + 1), dtype=np.int32)
     tot = int(g.sum())
     t = np.ascontiguousarray(temperature, dtype=np.float32).reshape(n)
     k = np.ascontiguousarray(top_k, dtype=np.int32).reshape(n)
@@ -257,7 +269,7 @@ def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, 
     rc = lib.sv_ref_verify_ex(kind, n, G, V, dt, _ptr(t), _ptr(k), _ptr(p), int(max_top_k), int(seed), _ptr(lt_p),
                               _ptr(ld_p), _ptr(qp_p), _ptr(x_p), _ptr(g), _ptr(rid), _ptr(out), _ptr(nacc), _ptr(pd),
                               _ptr(qd), _ptr(beta), _ptr(am), _ptr(rm), _ptr(cm), _ptr(bad), _ptr(badp),
-                              int(nthreads))
+                              _ptr(par_p), _ptr(path), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected the arguments (rc={rc})")
 
@@ -270,7 +282,7 @@ def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, 
         return o
 
     res = {"out_tokens": out, "num_accepted": nacc, "p_draft": pad(pd), "q_draft": pad(qd), "bad_token": bad,
-           "bad_param": badp, "cut_margin": cm, "greedy": t == 0.0, "lengths": g}
+           "bad_param": badp, "cut_margin": cm, "greedy": t == 0.0, "lengths": g, "path_nodes": path}
     if diagnostics:
         res["beta"], res["accept_margin"], res["race_margin"] = pad(beta), pad(am), rm
     return res

@@ -31,7 +31,13 @@
 //   * a draft given as probabilities (vLLM's draft_probs) is q as given: no
 //     temperature, top-k, top-p or renormalisation is applied to it;
 //   * a request with g draft positions (0 <= g <= gamma) uses target rows
-//     0..g and positions 0..g-1; its uniforms are those of the same (b, j).
+//     0..g and positions 0..g-1; its uniforms are those of the same (b, j);
+//   * sampler-match ([P3] "mlxcel의 프롬프트 조회"): every node of the draft
+//     (a chain, or a tree given by parent indices) gets a fresh sample from
+//     its row's adjusted law, drawn by the Exp(1) race on the stream of
+//     (b, node); from the root, the walk follows the child whose token equals
+//     the sample (the lowest-indexed child if several do) and emits the
+//     sample where no child matches.
 //   * every argmax and every race tie goes to the lowest index;
 //   * uniforms are Philox4x32-10 words mapped to (k53 + 1) * 2^-53 in (0, 1];
 //     accept stream counter (0, j, b, 0), race stream counter
@@ -399,6 +405,67 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
   return bad_token;
 }
 
+// Sampler-match verification of one request ([P3] "mlxcel의 프롬프트 조회":
+// a proposal is accepted only if it equals the token the target's sampler
+// draws at that position; lossless for one-hot proposals).  Nodes 0..g: node
+// 0 is the root (the last context token), node i >= 1 carries the draft
+// token X[i-1] and has parent par[i-1] in 0..i-1 (NULL: i-1, a chain).  Row
+// i of Lt is the target's law after node i's path.  Outputs: out[0..d] the
+// d accepted tokens and the sample that ends the walk, *n_out = d, nodes[k]
+// the k-th accepted node; p_draft[i-1] = p_parent(X[i-1]), the probability
+// that node i is accepted once its parent is reached.  Returns 1 if a draft
+// token is out of range.
+int verify_match(const Problem& P, uint32_t b, const char* Lt, const int32_t* X, const int32_t* par, int32_t* out,
+                 int32_t* n_out, int32_t* nodes, double* p_draft, double* race_margin) {
+  const int g = P.G, V = P.V;
+  const size_t row_bytes = (size_t)V * elem_bytes(P.dtype);
+  int bad = 0;
+  std::vector<std::vector<double>> p(g + 1);
+  std::vector<int> s(g + 1);
+  double rm = 1.0;
+  for (int i = 0; i <= g; ++i) {
+    const char* row = Lt + (size_t)i * row_bytes;
+    if (P.mode == MODE_GREEDY) {
+      s[i] = row_argmax(row, P.dtype, V);  // the temperature-0 sampler
+    } else {
+      p[i] = row_probs(row, P.dtype, V, P.T, P.top_k, P.top_p);
+      double m = 1.0;
+      s[i] = race(p[i], P.seed, b, (uint32_t)i, &m);
+      rm = std::min(rm, m);
+    }
+  }
+  for (int i = 1; i <= g; ++i) {
+    const int x = X[i - 1];
+    const int pa = par ? par[i - 1] : i - 1;
+    const bool valid = x >= 0 && x < V;
+    if (!valid) bad = 1;
+    if (p_draft) {
+      if (P.mode == MODE_GREEDY) p_draft[i - 1] = (valid && x == s[pa]) ? 1.0 : 0.0;
+      else p_draft[i - 1] = valid ? p[pa][x] : 0.0;
+    }
+  }
+  int cur = 0, d = 0;
+  for (;;) {
+    const int t = s[cur];
+    int child = -1;
+    for (int i = 1; i <= g; ++i) {
+      const int pa = par ? par[i - 1] : i - 1;
+      if (pa == cur && X[i - 1] == t) {
+        child = i;
+        break;
+      }
+    }
+    out[d] = t;
+    if (child < 0) break;
+    if (nodes) nodes[d] = child;
+    ++d;
+    cur = child;
+  }
+  *n_out = d;
+  if (race_margin) *race_margin = rm;
+  return bad;
+}
+
 }  // namespace
 
 extern "C" {
@@ -481,7 +548,11 @@ int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top
 
 // Batched verifier with per-request settings and ragged draft lengths.
 //   draft_kind: 0 draft logits (Ld, rows like Lt), 1 one-hot drafts (Ld
-//   unused), 2 draft probabilities (Qp: fp32 rows, q as given).
+//   unused), 2 draft probabilities (Qp: fp32 rows, q as given), 3 token-only
+//   drafts verified by sampler-match (parents: [sum g_r] parent node of each
+//   draft node, in 0..i-1, packed like the tokens; NULL: chains; path_nodes
+//   [nreq][G+1]: accepted nodes in order, -1 after; a request whose parents
+//   break that rule emits nothing and gets bad_param).
 //   lengths[r]: draft positions of request r, 0..G (NULL: all G).  Rows are
 //   packed request after request: request r's g_r + 1 target rows start at
 //   row sum_{r' < r} (g_r' + 1), its g_r draft rows (logits or
@@ -503,12 +574,12 @@ int sv_ref_verify_ex(int draft_kind, int nreq, int G, int V, int dtype, const fl
                      const int32_t* X, const int32_t* lengths, const int32_t* req_ids, int32_t* out_tokens,
                      int32_t* num_accepted, double* p_draft, double* q_draft, double* beta, double* acc_margin,
                      double* race_margin, double* cut_margin, int32_t* bad_token, int32_t* bad_param,
-                     int nthreads) {
-  if (nreq < 0 || G < 0 || V < 1 || (dtype != 0 && dtype != 1) || draft_kind < 0 || draft_kind > 2) return -1;
+                     const int32_t* parents, int32_t* path_nodes, int nthreads) {
+  if (nreq < 0 || G < 0 || V < 1 || (dtype != 0 && dtype != 1) || draft_kind < 0 || draft_kind > 3) return -1;
   if (!Lt || !X || !out_tokens || !num_accepted || !T || !K || !Pp) return -1;
   if (draft_kind == 0 && !Ld) return -1;
   if (draft_kind == 2 && !Qp) return -1;
-  const int mode = draft_kind == 0 ? MODE_PROB : (draft_kind == 1 ? MODE_ONEHOT : MODE_PROBS);
+  const int mode = draft_kind == 0 ? MODE_PROB : (draft_kind == 2 ? MODE_PROBS : MODE_ONEHOT);
   std::vector<size_t> d0(nreq + 1, 0);  // packed draft offset of each request
   for (int r = 0; r < nreq; ++r) {
     const int g = lengths ? lengths[r] : G;
@@ -550,6 +621,35 @@ int sv_ref_verify_ex(int draft_kind, int nreq, int G, int V, int dtype, const fl
     const char* ld = (draft_kind == 0) ? (const char*)Ld + d0[r] * row_bytes : nullptr;
     const float* qp = (draft_kind == 2) ? Qp + d0[r] * (size_t)V : nullptr;
     const int32_t* x = X + d0[r];
+    if (path_nodes)
+      for (int j = 0; j <= G; ++j) path_nodes[(size_t)r * (G + 1) + j] = -1;
+    if (draft_kind == 3) {
+      // Sampler-match over a chain or a tree; q is one-hot (1 for a valid
+      // draft token) and beta = p_draft.
+      const int32_t* par = parents ? parents + d0[r] : nullptr;
+      bool tree_ok = true;
+      for (int i = 1; par && i <= g; ++i) tree_ok = tree_ok && par[i - 1] >= 0 && par[i - 1] < i;
+      if (!tree_ok) {
+        if (bad_param) bad_param[r] = 1;
+        num_accepted[r] = 0;
+        for (int j = 0; j < g; ++j) {
+          if (pd) pd[j] = 0.0;
+          if (qd) qd[j] = 0.0;
+        }
+        if (bad_token) bad_token[r] = 0;
+        continue;
+      }
+      Problem P{t == 0.0 ? (int)MODE_GREEDY : (int)MODE_ONEHOT, nreq, g, V, dtype, k, t, seed, pp};
+      int bad = verify_match(P, b, lt, x, par, o, num_accepted + r,
+                             path_nodes ? path_nodes + (size_t)r * (G + 1) : nullptr, pd,
+                             race_margin ? race_margin + r : nullptr);
+      for (int j = 0; j < g; ++j) {
+        if (qd) qd[j] = (x[j] >= 0 && x[j] < V) ? 1.0 : 0.0;
+        if (beta) beta[d0[r] + j] = pd ? pd[j] : 0.0;
+      }
+      if (bad_token) bad_token[r] = bad;
+      continue;
+    }
     Problem P{t == 0.0 ? (int)MODE_GREEDY : mode, nreq, g, V, dtype, k, t, seed, pp};
     std::vector<int32_t> targ(g + 1);
     int bad = verify_one(P, b, lt, ld, qp, x, o, num_accepted + r, pd, qd, targ.data(),

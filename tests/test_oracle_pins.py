@@ -934,3 +934,95 @@ def test_decay_sigmas_give_the_pages_rates():
     res = oracle.verify(oracle.MODE_PROB, h(inp["target_logits"]), h(inp["draft_logits"]), h(inp["draft_tokens"]),
                         temperature=wl.temperature, seed=1, diagnostics=True)
     np.testing.assert_allclose(res["beta"].mean(axis=0), workloads.DECAY_ALPHAS, atol=0.01)
+
+
+# ---------------------------------------------------------------------------
+# Sampler-match acceptance over chains and trees
+# ---------------------------------------------------------------------------
+
+def _match_runs(lt, x, parents, n_runs, seed, T=1.0):
+    G = x.shape[-1]
+    ltb = np.broadcast_to(lt[None], (n_runs,) + lt.shape).copy()
+    xb = np.broadcast_to(x[None], (n_runs, G)).copy()
+    pb = None if parents is None else np.broadcast_to(np.asarray(parents, np.int32)[None], (n_runs, G)).copy()
+    one = np.full(n_runs, T, np.float32)
+    return oracle.verify_batch(ltb, None, xb, one, np.zeros(n_runs, np.int32), np.ones(n_runs, np.float32),
+                               seed=seed, match=True, parents=pb, diagnostics=True)
+
+
+def test_sampler_match_chain_law():
+    """Chain x_0, x_1: the walk accepts x_j iff the fresh sample equals it;
+    P(n = d, out) = prod_{j<d} p_j(x_j) * p_d(out_d) with out_d != x_d for
+    d < G.  Checked exactly and against the oracle's empirical law."""
+    lt = _logits([[0.5, 0.25, 0.15, 0.1], [0.3, 0.3, 0.2, 0.2], [0.1, 0.2, 0.3, 0.4]])
+    x = np.array([0, 2], np.int32)
+    p = np.stack([oracle.row_probs(lt[j], 1.0) for j in range(3)])
+    law = {}
+    for d in range(3):
+        pre = np.prod([p[j][x[j]] for j in range(d)])
+        for y in range(4):
+            if d < 2 and y == x[d]:
+                continue
+            law[(d, tuple(x[:d]) + (y,))] = pre * p[d][y]
+    assert abs(sum(law.values()) - 1.0) < 1e-12
+    n_runs = 60_000
+    res = _match_runs(lt, x, None, n_runs, 3)
+    np.testing.assert_allclose(res["p_draft"][0], [p[0][0], p[1][2]], rtol=1e-12)
+    keys = list(law)
+    idx = {k: i for i, k in enumerate(keys)}
+    counts = np.zeros(len(keys))
+    for r in range(n_runs):
+        d = int(res["num_accepted"][r])
+        counts[idx[(d, tuple(int(t) for t in res["out_tokens"][r, :d + 1]))]] += 1
+        assert list(res["path_nodes"][r, :d]) == list(range(1, d + 1))
+    expected = np.array([law[k] for k in keys]) * n_runs
+    assert stats.chisquare(counts, expected).pvalue > 1e-6
+
+
+def test_sampler_match_tree_branches():
+    """Root with children a = 1 (node 1) and b = 2 (node 2), node 3 a child of
+    node 1 with token 0: the walk follows a with probability p_0(a), b with
+    p_0(b), stops at the root otherwise; the root's emitted token is ~p_0."""
+    lt = _logits([[0.4, 0.3, 0.2, 0.1], [0.6, 0.1, 0.1, 0.2], [0.25, 0.25, 0.25, 0.25], [0.1, 0.1, 0.1, 0.7]])
+    x = np.array([1, 2, 0], np.int32)
+    parents = np.array([0, 0, 1], np.int32)
+    n_runs = 60_000
+    res = _match_runs(lt, x, parents, n_runs, 9)
+    p0, p1 = oracle.row_probs(lt[0], 1.0), oracle.row_probs(lt[1], 1.0)
+    np.testing.assert_allclose(res["p_draft"][0], [p0[1], p0[2], p1[0]], rtol=1e-12)
+    first = res["out_tokens"][:, 0]
+    assert stats.chisquare(np.bincount(first, minlength=4), p0 * n_runs).pvalue > 1e-6
+    path1 = res["path_nodes"][:, 0]
+    via = np.array([(path1 == -1).sum(), (path1 == 1).sum(), (path1 == 2).sum()])
+    assert stats.chisquare(via, np.array([1 - p0[1] - p0[2], p0[1], p0[2]]) * n_runs).pvalue > 1e-6
+    # Through node 1, node 3 (token 0) is accepted with probability p_1(0).
+    thru = path1 == 1
+    deep = (res["path_nodes"][thru, 1] == 3).mean()
+    assert abs(deep - p1[0]) < 4 * np.sqrt(p1[0] * (1 - p1[0]) / thru.sum())
+
+
+def test_sampler_match_reductions():
+    rng = np.random.default_rng(71)
+    n, G, V = 30, 4, 40
+    lt, ld, x, T, K, P = _mixed_case(rng, n, G, V)
+    chain = np.tile(np.arange(G, dtype=np.int32), (n, 1))  # node j + 1's parent is node j
+    a = oracle.verify_batch(lt, None, x, T, K, P, seed=4, match=True)
+    b = oracle.verify_batch(lt, None, x, T, K, P, seed=4, match=True, parents=chain)
+    for key in ("out_tokens", "num_accepted", "p_draft", "path_nodes"):
+        np.testing.assert_array_equal(a[key], b[key])
+    # Temperature 0: the sampler is the argmax, and a chain is the greedy rule.
+    T0 = np.zeros(n, np.float32)
+    m = oracle.verify_batch(lt, None, x, T0, K, P, seed=4, match=True)
+    gr = oracle.verify_batch(lt, None, x, T0, K, P, seed=4)
+    np.testing.assert_array_equal(m["out_tokens"], gr["out_tokens"])
+    np.testing.assert_array_equal(m["num_accepted"], gr["num_accepted"])
+    np.testing.assert_array_equal(m["p_draft"], gr["p_draft"])
+    # Two children with the same token: the lower-indexed one is followed.
+    lt2 = _logits([[0.0, 1.0, 0.0, 0.0], [0.25] * 4, [0.25] * 4])
+    r = _match_runs(lt2, np.array([1, 1], np.int32), np.array([0, 0], np.int32), 20, 5)
+    assert (r["path_nodes"][:, 0] == 1).all()
+    # A parent that is not an earlier node makes the request invalid.
+    bad = chain.copy()
+    bad[2, 1] = 2
+    c = oracle.verify_batch(lt, None, x, T, K, P, seed=4, match=True, parents=bad)
+    assert c["bad_param"][2] == 1 and (c["out_tokens"][2] == -1).all() and c["bad_param"].sum() == 1
