@@ -65,13 +65,14 @@ def cpu_baseline(wl, inp, target_seconds: float) -> dict:
         ld = workloads.to_host_arrays(inp["draft_logits"][sub]) if wl.has_draft_logits else None
         x = workloads.to_host_arrays(inp["draft_tokens"][sub])
         t0 = time.perf_counter()
-        if wl.entry == "batch":
+        if wl.has_settings:
             probs = inp["draft_probs"][sub].cpu().numpy() if wl.draft_probs else None
             lens = inp["lengths"][sub].cpu().numpy() if wl.lengths else None
+            par = inp["parents"][sub].cpu().numpy() if inp.get("parents") is not None else None
             oracle.verify_batch(lt, None if wl.draft_probs else ld, x, inp["temperature"][sub].cpu().numpy(),
                                 inp["top_k"][sub].cpu().numpy(), inp["top_p"][sub].cpu().numpy(),
                                 max_top_k=max(k for _, k, _ in wl.mix), seed=wl.verify_seed, draft_probs=probs,
-                                lengths=lens)
+                                lengths=lens, match=wl.entry == "match", parents=par)
         else:
             oracle.verify(modes[wl.entry], lt, ld, x, temperature=wl.temperature, top_k=wl.top_k,
                           seed=wl.verify_seed)
@@ -181,10 +182,19 @@ def main():
     params = sv.make_params(wl.B, wl.G, wl.V, wl.torch_dtype, wl.temperature or 1.0, wl.top_k, wl.verify_seed)
     sampling = layout = None
     padded = inp
-    if wl.entry == "batch":
+    if wl.has_settings:
         sampling = sv.make_sampling(inp["temperature"], inp["top_k"], inp["top_p"], max(k for _, k, _ in wl.mix))
         ws = torch.empty(sv.sv_workspace_bytes_batch(params, sampling), dtype=torch.uint8, device=dev)
-        if wl.lengths or wl.draft_probs:
+        if wl.entry == "match":
+            # Token-only drafts (chains or trees), packed before the timed
+            # region if ragged.
+            src = workloads.pack_ragged(inp, inp["lengths"].cpu()) if wl.lengths else inp
+            layout = sv.SvLayout(sv.SV_DRAFT_MATCH, 0, wl.V, 0, sv._ptr(src.get("cu_draft")),
+                                 sv._ptr(src.get("parents")))
+            inp = dict(inp, target_logits=src["target_logits"], draft_tokens=src["draft_tokens"],
+                       cu_draft=src.get("cu_draft"), parents=src.get("parents"))
+            torch.cuda.synchronize()
+        elif wl.lengths or wl.draft_probs:
             # Packed ragged rows and / or the drafter's probabilities, laid
             # out before the timed region.
             src = inp
@@ -206,7 +216,8 @@ def main():
     qd = torch.empty(inp["draft_tokens"].shape, dtype=torch.float32, device=dev)
     ta = torch.empty((B, G + 1), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
-    outputs = sv.make_outputs(out, nacc, pd, qd)
+    pn = torch.empty((B, G + 1), dtype=torch.int32, device=dev) if wl.entry == "match" else None
+    outputs = sv.make_outputs(out, nacc, pd, qd, path_nodes=pn)
     lt, ld, x = inp["target_logits"], inp["draft_logits"], inp["draft_tokens"]
 
     def step():
@@ -214,7 +225,7 @@ def main():
             sv.spec_verify_prob(params, lt, ld, x, out, nacc, pd, qd, ws, stream)
         elif wl.entry == "onehot":
             sv.spec_verify_onehot(params, lt, x, out, nacc, pd, ws, stream)
-        elif wl.entry == "batch":
+        elif wl.has_settings:
             sv.spec_verify_batch(params, sampling, layout, lt, ld, x, outputs, ws, stream)
         else:
             sv.spec_verify_greedy(params, lt, x, out, nacc, ta, ws, stream)
@@ -253,7 +264,7 @@ def main():
         log("[bench] copy calibration: 3 copies of 1 GiB done")
 
     sec = wall / args.steps
-    positions = int(wl.draft_lengths.sum()) if wl.entry == "batch" else B * G
+    positions = int(wl.draft_lengths.sum()) if wl.has_settings else B * G
     rows = wl.target_rows + wl.draft_rows
     bytes_alg = wl.logit_bytes
     # Row-pass time per step: one launch for the single-setting entries; the
@@ -282,7 +293,9 @@ def main():
         "config": {"workload": name, "entry": f"spec_verify_{wl.entry}", "batch": B, "gamma": G, "vocab": wl.V,
                    "logits": wl.dtype, "temperature": wl.temperature, "top_k": wl.top_k,
                    "parallelism": "single GPU",
-                   **({"mix (T, top_k, top_p)": [list(m) for m in wl.mix]} if wl.entry == "batch" else {}),
+                   **({"mix (T, top_k, top_p)": [list(m) for m in wl.mix]} if wl.has_settings else {}),
+                   **({"draft": "tokens only (sampler-match)"} if wl.entry == "match" else {}),
+                   **({"tree parents": list(wl.parents)} if wl.parents else {}),
                    **({"draft lengths": list(wl.lengths)} if wl.lengths else {}),
                    **({"draft": "fp32 probabilities"} if wl.draft_probs else {})},
         "rows_per_s": rows / sec,
@@ -292,7 +305,7 @@ def main():
         "kernels_ms_per_step": {"rows": rows_ms / args.steps, "accept": acc_ms / args.steps,
                                 "race": race_ms / args.steps},
         "roofline": {"bound": "hbm", "kernel": ("row pass (rows_topk_kernel)" if wl.top_k else
-                                                "row family (all row kernels of a step)" if wl.entry == "batch"
+                                                "row family (all row kernels of a step)" if wl.has_settings
                                                 else "row pass"),
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic},

@@ -120,9 +120,13 @@ sv_status spec_verify_greedy(const sv_params* params, const void* target_logits,
 typedef enum {
   SV_DRAFT_LOGITS = 0, /* draft logits, same dtype and rules as the target's */
   SV_DRAFT_ONEHOT = 1, /* no draft rows: a greedy drafter, q one-hot at x_j */
-  SV_DRAFT_PROBS = 2   /* fp32 draft probabilities q, used as given (vLLM's
+  SV_DRAFT_PROBS = 2,  /* fp32 draft probabilities q, used as given (vLLM's
                           "probabilistic" draft_probs): no temperature, top-k,
                           top-p or renormalisation is applied to them */
+  SV_DRAFT_MATCH = 3   /* token-only drafts (prompt lookup, n-grams, tree
+                          drafts) verified by sampler-match (page "투기적
+                          디코딩" (mlxcel manual), section "mlxcel의 프롬프트
+                          조회"): see spec_verify_batch */
 } sv_draft_kind;
 
 /* Where the rows of a spec_verify_batch call live.  Strides are in elements
@@ -142,6 +146,14 @@ typedef struct {
   int64_t target_stride;
   int64_t draft_stride;
   const int32_t* cu_draft;
+  const int32_t* parents;  /* SV_DRAFT_MATCH only (may be NULL: chains): DEVICE
+                              array laid out like draft_tokens; the draft token
+                              of position j is node j + 1 of a tree whose root
+                              (node 0) is the last context token, and
+                              parents[.] of node i is its parent node, in
+                              0..i-1.  Target row i is the law after node i's
+                              path.  A request whose parents break this rule
+                              emits nothing (error bit 2). */
 } sv_layout;
 
 /* Per-request sampling settings of spec_verify_batch: DEVICE arrays of
@@ -181,8 +193,9 @@ typedef struct {
  *     높이는 추측 디코딩", section "수락률 α와 기대 속도 향상": alpha is its
  *     expectation, Theorem 3.5); p_j(x_j) for one-hot drafts, 1 or 0 (argmax
  *     match) for greedy requests; laid out like draft_tokens; may be NULL.
- *     For requests without top-k and with draft logits or probabilities it
- *     costs one more read of their target and draft rows.
+ *     0 for requests that are not verified.  For requests without top-k and
+ *     with draft logits or probabilities it costs one more read of their
+ *     target and draft rows.
  *   counters [B][3] int64: per request, += (draft positions verified, drafts
  *     accepted, 1) on every call that verifies it (the manual page's
  *     draft_n, draft_n_accepted, draft_rounds: the mean accepted length is
@@ -195,6 +208,8 @@ typedef struct {
   float* q_draft;
   float* beta;
   int64_t* counters;
+  int32_t* path_nodes;  /* SV_DRAFT_MATCH: [B][G+1], the accepted nodes in order,
+                           -1 after; may be NULL */
 } sv_outputs;
 
 /* Workspace bytes of spec_verify_batch for these parameters (0 if invalid).
@@ -223,6 +238,15 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  *   target_logits, draft (logits or fp32 probabilities; NULL for one-hot),
  *   draft_tokens: as described by layout;
  *   outputs: see sv_outputs.
+ * Sampler-match (layout->draft_kind SV_DRAFT_MATCH): every node gets a fresh
+ * sample from its row's adjusted law (the Exp(1) race on the stream of
+ * (request, node); temperature 0: the argmax); from the root the walk follows
+ * the child whose token equals the sample (the lowest-indexed one if several
+ * do) and emits the sample where no child matches: out_tokens holds the
+ * accepted tokens and that sample, num_accepted the accepted depth.  Lossless
+ * for token-only proposals.  p_draft of node i is p_parent(x_i), its
+ * acceptance probability once its parent is reached (also beta); q_draft is
+ * 1 for valid tokens.
  * Workspace: sv_workspace_bytes_batch(params, sampling) bytes. */
 sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const sv_layout* layout,
                             const void* target_logits, const void* draft, const int32_t* draft_tokens,

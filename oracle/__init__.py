@@ -253,7 +253,7 @@ def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, 
     if parents is not None:
         par = np.ascontiguousarray(parents, dtype=np.int32)
         par_p = np.ascontiguousarray(np.concatenate([par[r, :g[r]] for r in range(n)])) if n else par.reshape(0)
-    path = np.empty((n, G + 1), dtype=np.int32)
+    path = np.full((n, G + 1), -1, dtype=np.int32)
     tot = int(g.sum())
     t = np.ascontiguousarray(temperature, dtype=np.float32).reshape(n)
     k = np.ascontiguousarray(top_k, dtype=np.int32).reshape(n)
@@ -282,7 +282,8 @@ def verify_batch(target_logits, draft_logits, draft_tokens, temperature, top_k, 
         return o
 
     res = {"out_tokens": out, "num_accepted": nacc, "p_draft": pad(pd), "q_draft": pad(qd), "bad_token": bad,
-           "bad_param": badp, "cut_margin": cm, "greedy": t == 0.0, "lengths": g, "path_nodes": path}
+           "bad_param": badp, "cut_margin": cm, "greedy": t == 0.0, "lengths": g, "path_nodes": path,
+           "match": bool(match)}
     if diagnostics:
         res["beta"], res["accept_margin"], res["race_margin"] = pad(beta), pad(am), rm
     return res
@@ -292,7 +293,9 @@ def near_tie_position(res: dict, threshold: float = 1e-4) -> np.ndarray:
     """First position whose decision had a margin <= threshold, else -1.
 
     The accept decision at j (j <= n) and the race at n are the decisions of
-    a request; the greedy path takes none that can tie numerically.
+    a request; the greedy path takes none that can tie numerically.  Under
+    sampler-match the races of every node the walk visited decide the path:
+    a near-tie among them leaves no position fixed (0).
     """
     nacc = res["num_accepted"]
     n_req = nacc.shape[0]
@@ -308,5 +311,5 @@ def near_tie_position(res: dict, threshold: float = 1e-4) -> np.ndarray:
                 pos[r] = j
                 break
         if pos[r] < 0 and rm[r] <= threshold:
-            pos[r] = n
+            pos[r] = 0 if res.get("match") else n
     return pos

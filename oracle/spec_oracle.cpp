@@ -416,22 +416,23 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
 // that node i is accepted once its parent is reached.  Returns 1 if a draft
 // token is out of range.
 int verify_match(const Problem& P, uint32_t b, const char* Lt, const int32_t* X, const int32_t* par, int32_t* out,
-                 int32_t* n_out, int32_t* nodes, double* p_draft, double* race_margin) {
+                 int32_t* n_out, int32_t* nodes, double* p_draft, double* race_margin, double* cut_margin) {
   const int g = P.G, V = P.V;
   const size_t row_bytes = (size_t)V * elem_bytes(P.dtype);
   int bad = 0;
   std::vector<std::vector<double>> p(g + 1);
   std::vector<int> s(g + 1);
-  double rm = 1.0;
+  std::vector<double> margin(g + 1, 1.0);  // each node's race margin
+  double cm = 1.0;
   for (int i = 0; i <= g; ++i) {
     const char* row = Lt + (size_t)i * row_bytes;
     if (P.mode == MODE_GREEDY) {
       s[i] = row_argmax(row, P.dtype, V);  // the temperature-0 sampler
     } else {
-      p[i] = row_probs(row, P.dtype, V, P.T, P.top_k, P.top_p);
-      double m = 1.0;
-      s[i] = race(p[i], P.seed, b, (uint32_t)i, &m);
-      rm = std::min(rm, m);
+      double c = 1.0;
+      p[i] = row_probs(row, P.dtype, V, P.T, P.top_k, P.top_p, &c);
+      cm = std::min(cm, c);
+      s[i] = race(p[i], P.seed, b, (uint32_t)i, &margin[i]);
     }
   }
   for (int i = 1; i <= g; ++i) {
@@ -445,8 +446,10 @@ int verify_match(const Problem& P, uint32_t b, const char* Lt, const int32_t* X,
     }
   }
   int cur = 0, d = 0;
+  double rm = 1.0;  // over the nodes the walk visits: only their samples are used
   for (;;) {
     const int t = s[cur];
+    rm = std::min(rm, margin[cur]);
     int child = -1;
     for (int i = 1; i <= g; ++i) {
       const int pa = par ? par[i - 1] : i - 1;
@@ -463,6 +466,7 @@ int verify_match(const Problem& P, uint32_t b, const char* Lt, const int32_t* X,
   }
   *n_out = d;
   if (race_margin) *race_margin = rm;
+  if (cut_margin) *cut_margin = cm;
   return bad;
 }
 
@@ -564,7 +568,7 @@ int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top
 //   max_top_k: a top_k in (max_top_k, V) makes the request invalid.
 //   An invalid request (T negative, NaN or infinite; top_k negative or above
 //   max_top_k and below V; top_p NaN, <= 0 or > 1) emits nothing: out_tokens
-//   all -1, num_accepted 0, p_draft / q_draft 0, bad_param 1.
+//   all -1, num_accepted 0, p_draft / q_draft / beta 0, bad_param 1.
 //   Greedy requests: the argmax rule; p_draft[j] = 1 if x_j is the target
 //   argmax of row j else 0, q_draft[j] = 1.
 //   cut_margin [nreq]: the smallest top-p boundary margin over the request's
@@ -613,6 +617,7 @@ int sv_ref_verify_ex(int draft_kind, int nreq, int G, int V, int dtype, const fl
       for (int j = 0; j < g; ++j) {
         if (pd) pd[j] = 0.0;
         if (qd) qd[j] = 0.0;
+        if (beta) beta[d0[r] + j] = 0.0;
       }
       if (bad_token) bad_token[r] = 0;
       continue;
@@ -635,6 +640,7 @@ int sv_ref_verify_ex(int draft_kind, int nreq, int G, int V, int dtype, const fl
         for (int j = 0; j < g; ++j) {
           if (pd) pd[j] = 0.0;
           if (qd) qd[j] = 0.0;
+          if (beta) beta[d0[r] + j] = 0.0;
         }
         if (bad_token) bad_token[r] = 0;
         continue;
@@ -642,7 +648,7 @@ int sv_ref_verify_ex(int draft_kind, int nreq, int G, int V, int dtype, const fl
       Problem P{t == 0.0 ? (int)MODE_GREEDY : (int)MODE_ONEHOT, nreq, g, V, dtype, k, t, seed, pp};
       int bad = verify_match(P, b, lt, x, par, o, num_accepted + r,
                              path_nodes ? path_nodes + (size_t)r * (G + 1) : nullptr, pd,
-                             race_margin ? race_margin + r : nullptr);
+                             race_margin ? race_margin + r : nullptr, cut_margin ? cut_margin + r : nullptr);
       for (int j = 0; j < g; ++j) {
         if (qd) qd[j] = (x[j] >= 0 && x[j] < V) ? 1.0 : 0.0;
         if (beta) beta[d0[r] + j] = pd ? pd[j] : 0.0;

@@ -27,7 +27,7 @@ LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_PKG, "libspecverify
 
 SV_OK, SV_ERR_INVALID_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED = range(6)
 SV_F32, SV_BF16 = 0, 1
-SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT, SV_DRAFT_PROBS = 0, 1, 2
+SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT, SV_DRAFT_PROBS, SV_DRAFT_MATCH = 0, 1, 2, 3
 FAMILY_ROWS, FAMILY_ACCEPT, FAMILY_RACE = 0, 1, 2
 
 
@@ -60,6 +60,7 @@ class SvLayout(ctypes.Structure):
         ("target_stride", ctypes.c_int64),
         ("draft_stride", ctypes.c_int64),
         ("cu_draft", ctypes.c_void_p),
+        ("parents", ctypes.c_void_p),
     ]
 
 
@@ -71,6 +72,7 @@ class SvOutputs(ctypes.Structure):
         ("q_draft", ctypes.c_void_p),
         ("beta", ctypes.c_void_p),
         ("counters", ctypes.c_void_p),
+        ("path_nodes", ctypes.c_void_p),
     ]
 
 
@@ -205,14 +207,17 @@ def sv_workspace_bytes_batch(params: SvParams, sampling) -> int:
                                                        ctypes.byref(sampling) if sampling else None))
 
 
-def make_outputs(out_tokens, num_accepted, p_draft=None, q_draft=None, beta=None, counters=None) -> SvOutputs:
+def make_outputs(out_tokens, num_accepted, p_draft=None, q_draft=None, beta=None, counters=None,
+                 path_nodes=None) -> SvOutputs:
     """Output pointers of spec_verify_batch (device tensors; counters int64
-    [B, 3], accumulated across calls).  Keep the tensors alive while the
-    struct is used."""
+    [B, 3], accumulated across calls; path_nodes int32 [B, G+1] for
+    sampler-match).  Keep the tensors alive while the struct is used."""
     if counters is not None and counters.dtype != torch.int64:
         raise ValueError("counters must be int64")
+    if path_nodes is not None and path_nodes.dtype != torch.int32:
+        raise ValueError("path_nodes must be int32")
     return SvOutputs(_ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft), _ptr(q_draft), _ptr(beta),
-                     _ptr(counters))
+                     _ptr(counters), _ptr(path_nodes))
 
 
 def spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, outputs, workspace,
@@ -289,7 +294,7 @@ def verify(entry: str, target_logits, draft_tokens, draft_logits=None, *, temper
 
 def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, top_k=None, top_p=None,
                  max_top_k=None, seed=0, draft_kind=None, cu_draft=None, gamma=None, vocab=None,
-                 single_temperature=1.0, single_top_k=0, beta=False, counters=None, workspace=None,
+                 single_temperature=1.0, single_top_k=0, beta=False, counters=None, parents=None, workspace=None,
                  stream=None) -> dict:
     """Allocates outputs (and a workspace if none is given) and runs
     spec_verify_batch.
@@ -304,7 +309,9 @@ def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, t
     None for one setting for every request (single_temperature,
     single_top_k).  max_top_k defaults to 1024 when top_k is given.  beta:
     also return the per-position acceptance probability; counters: an int64
-    [B, 3] device tensor the call adds its round to."""
+    [B, 3] device tensor the call adds its round to.  draft_kind
+    SV_DRAFT_MATCH: sampler-match over chains, or over trees with parents
+    (int32, laid out like draft_tokens); also returns path_nodes [B, G+1]."""
     dev = target_logits.device
     W = target_logits.shape[-1]
     V = int(vocab) if vocab is not None else W
@@ -319,7 +326,7 @@ def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, t
     if draft_kind is None:
         draft_kind = SV_DRAFT_ONEHOT if draft is None else SV_DRAFT_LOGITS
     dW = draft.shape[-1] if draft is not None else 0
-    layout = SvLayout(int(draft_kind), 0, W, dW, _ptr(cu_draft))
+    layout = SvLayout(int(draft_kind), 0, W, dW, _ptr(cu_draft), _ptr(parents))
     sampling = None
     if temperature is not None:
         if max_top_k is None:
@@ -335,9 +342,12 @@ def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, t
     pd = torch.empty(tok_shape, dtype=torch.float32, device=dev)
     qd = torch.empty(tok_shape, dtype=torch.float32, device=dev)
     bt = torch.empty(tok_shape, dtype=torch.float32, device=dev) if beta else None
-    outputs = make_outputs(out, nacc, pd, qd, bt, counters)
+    pn = torch.empty((B, G + 1), dtype=torch.int32, device=dev) if draft_kind == SV_DRAFT_MATCH else None
+    outputs = make_outputs(out, nacc, pd, qd, bt, counters, pn)
     spec_verify_batch(params, sampling, layout, target_logits, draft, draft_tokens, outputs, ws, stream)
     res = {"out_tokens": out, "num_accepted": nacc, "p_draft": pd, "q_draft": qd, "workspace": ws}
+    if pn is not None:
+        res["path_nodes"] = pn
     if beta:
         res["beta"] = bt
     return res

@@ -39,6 +39,8 @@ struct Plan {
   int S, seg;     // row-pass splits of the vocabulary (softmax / argmax)
   int Sr, segr;   // race-pass splits
   size_t off_err, off_part, off_cand, off_desc, off_slots, off_info, off_cut, total;
+  int Srr, segrr;                           // row-race splits (sampler-match)
+  size_t off_rdesc, off_rslots, off_samples;  // per-row race descriptors, slots, samples
   sv::Layout L;   // rows, tokens, outputs (dense: rows V apart, every request G positions)
 };
 
@@ -149,6 +151,16 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   off = align_up(off + (size_t)pl->B * sizeof(ReqInfo), kWsAlign);
   pl->off_cut = off;
   if (sm && sm->top_p) off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
+  // Sampler-match: one race per target row.
+  pl->Srr = splits_for(pl->rows_t, pl->V, 4096, 2048);
+  pl->segrr = seg_for(pl->V, pl->Srr);
+  pl->Srr = (pl->V + pl->segrr - 1) / pl->segrr;
+  pl->off_rdesc = off;
+  off = align_up(off + (size_t)pl->rows_t * sizeof(RaceDesc), kWsAlign);
+  pl->off_rslots = off;
+  off = align_up(off + (size_t)pl->rows_t * 3 * 8, kWsAlign);
+  pl->off_samples = off;
+  off = align_up(off + (size_t)pl->rows_t * 4, kWsAlign);
   pl->total = off;
   return SV_OK;
 }
@@ -261,7 +273,24 @@ sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, 
                      (const ET*)lt, QP ? (const ET*)nullptr : (const ET*)ld, QP ? (const float*)ld : nullptr, pl.V,
                      pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots);
   hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
-                     pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
+                     pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out, (int32_t*)nullptr);
+  t.done();
+  return check_launch();
+}
+
+// One Exp(1) race per target row (sampler-match): descriptors and slots per
+// row, winners to `samples`.
+template <typename ET, bool CUT>
+sv_status run_row_race(const Plan& pl, const void* lt, uint32_t k0, uint32_t k1, char* ws, hipStream_t st) {
+  TimedLaunch t(2, st);
+  const RaceDesc* rdesc = (const RaceDesc*)(ws + pl.off_rdesc);
+  unsigned long long* rslots = (unsigned long long*)(ws + pl.off_rslots);
+  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256, CUT, false>), dim3(pl.rows_t * pl.Srr), dim3(256), 0, st,
+                     (const ET*)lt, (const ET*)nullptr, (const float*)nullptr, pl.V, pl.Srr, pl.segrr, k0, k1, rdesc,
+                     rslots);
+  hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.rows_t), dim3(256), 0, st, (const ET*)lt,
+                     pl.G, pl.V, k0, k1, rdesc, (const unsigned long long*)rslots, (int32_t*)nullptr,
+                     (int32_t*)(ws + pl.off_samples));
   t.done();
   return check_launch();
 }
@@ -334,6 +363,7 @@ struct BatchArgs {
   const float* P;
   float T0;
   int K0, max_top_k;
+  const int32_t* parents;  // sampler-match trees (null: chains)
 };
 
 template <typename ET, int MODE>
@@ -345,7 +375,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
   float* q_draft = o.q_draft;
   float* beta = o.beta;
   int64_t* counters = o.counters;
-  const int nrows = pl.rows_t + (MODE == 0 ? pl.rows_d : 0);
+  const int nrows = pl.rows_t + (MODE == 0 ? pl.rows_d : 0);  // MODE 3 (sampler-match): target rows only
   const uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)(seed >> 32);
   int* err = (int*)(ws + pl.off_err);
   ReqInfo* info = (ReqInfo*)(ws + pl.off_info);
@@ -358,7 +388,8 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
   {
     TimedLaunch t(0, st);
     hipLaunchKernelGGL(sv::classify_kernel, dim3(1), dim3(1024), 0, st, ba.T, ba.K, ba.P, ba.T0, ba.K0, pl.B, pl.G,
-                       pl.V, ba.max_top_k, pl.L, info, err, out, nacc, p_draft, q_draft);
+                       pl.V, ba.max_top_k, pl.L, MODE == 3 ? ba.parents : (const int32_t*)nullptr, info, err, out,
+                       nacc, p_draft, q_draft, beta);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
@@ -378,6 +409,33 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
                          (const ReqInfo*)info, cut, pl.L);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
+  }
+  if (MODE == 3) {
+    // Sampler-match: a sample for every node's row, then the walk.
+    {
+      TimedLaunch t(1, st);
+      hipLaunchKernelGGL(sv::match_prep_kernel, dim3((pl.rows_t + 255) / 256), dim3(256), 0, st,
+                         (const float2*)(ws + pl.off_part), pl.S, pl.rows_t, pl.G, (const ReqInfo*)info,
+                         (const RowCut*)(nuc ? cut : nullptr), pl.L, (RaceDesc*)(ws + pl.off_rdesc),
+                         (unsigned long long*)(ws + pl.off_rslots));
+      if (pl.K > 0)
+        hipLaunchKernelGGL(sv::sample_topk_kernel, dim3((pl.rows_t + 3) / 4), dim3(256), 0, st,
+                           (const uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, pl.G, (const ReqInfo*)info, pl.L,
+                           k0, k1, (int32_t*)(ws + pl.off_samples));
+      t.done();
+      if ((s = check_launch()) != SV_OK) return s;
+    }
+    s = nuc ? run_row_race<ET, true>(pl, lt, k0, k1, ws, st) : run_row_race<ET, false>(pl, lt, k0, k1, ws, st);
+    if (s != SV_OK) return s;
+    TimedLaunch t(1, st);
+    hipLaunchKernelGGL((sv::match_walk_kernel<ET>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
+                       (const float2*)(ws + pl.off_part), (const uint64_t*)part64,
+                       (const uint64_t*)(ws + pl.off_cand), pl.kcap, pl.S, pl.G, pl.V, (const ReqInfo*)info,
+                       (const RowCut*)(nuc ? cut : nullptr), pl.L, X, ba.parents,
+                       (const int32_t*)(ws + pl.off_samples), out, nacc, o.path_nodes, p_draft, q_draft,
+                       sv::Stats{beta, counters}, err);
+    t.done();
+    return check_launch();
   }
   RaceDesc* desc = (RaceDesc*)(ws + pl.off_desc);
   unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
@@ -519,8 +577,10 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
   int kind = draft ? SV_DRAFT_LOGITS : SV_DRAFT_ONEHOT;
   if (layout) {
     kind = layout->draft_kind;
-    if (kind != SV_DRAFT_LOGITS && kind != SV_DRAFT_ONEHOT && kind != SV_DRAFT_PROBS) return SV_ERR_INVALID_ARG;
-    if (kind != SV_DRAFT_ONEHOT && !draft) return SV_ERR_INVALID_ARG;
+    if (kind != SV_DRAFT_LOGITS && kind != SV_DRAFT_ONEHOT && kind != SV_DRAFT_PROBS && kind != SV_DRAFT_MATCH)
+      return SV_ERR_INVALID_ARG;
+    if ((kind == SV_DRAFT_LOGITS || kind == SV_DRAFT_PROBS) && !draft) return SV_ERR_INVALID_ARG;
+    if (layout->parents && (kind != SV_DRAFT_MATCH || !aligned(layout->parents, 4))) return SV_ERR_INVALID_ARG;
     const int64_t ts = layout->target_stride ? layout->target_stride : pl.V;
     const int64_t ds = layout->draft_stride ? layout->draft_stride : pl.V;
     if (ts < pl.V || ds < pl.V) return SV_ERR_INVALID_ARG;
@@ -542,10 +602,16 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
   ba.T0 = params->temperature;
   ba.K0 = params->top_k;
   ba.max_top_k = batch_max_top_k(params, sampling);
+  ba.parents = layout ? layout->parents : nullptr;
+  if (o.path_nodes && !aligned(o.path_nodes, 4)) return SV_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const uint64_t seed = params->seed;
-  const void* d = kind == SV_DRAFT_ONEHOT ? nullptr : draft;
+  const void* d = (kind == SV_DRAFT_ONEHOT || kind == SV_DRAFT_MATCH) ? nullptr : draft;
+  if (kind == SV_DRAFT_MATCH) {
+    if (pl.dtype == SV_F32) return verify_batch<float, 3>(pl, ba, seed, target_logits, nullptr, draft_tokens, o, ws, st);
+    return verify_batch<uint16_t, 3>(pl, ba, seed, target_logits, nullptr, draft_tokens, o, ws, st);
+  }
   if (pl.dtype == SV_F32) {
     if (kind == SV_DRAFT_LOGITS)
       return verify_batch<float, 0>(pl, ba, seed, target_logits, d, draft_tokens, o, ws, st);

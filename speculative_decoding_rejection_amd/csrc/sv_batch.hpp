@@ -93,9 +93,11 @@ __device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, in
 __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict__ T, const int32_t* __restrict__ K,
                                                         const float* __restrict__ P, float T0, int K0, int B, int G,
                                                         int V, int max_top_k, Layout L,
+                                                        const int32_t* __restrict__ parents,
                                                         ReqInfo* __restrict__ info, int* __restrict__ err,
                                                         int32_t* __restrict__ out, int32_t* __restrict__ nacc,
-                                                        float* __restrict__ p_draft, float* __restrict__ q_draft) {
+                                                        float* __restrict__ p_draft, float* __restrict__ q_draft,
+                                                        float* __restrict__ beta) {
   __shared__ int bad_layout;
   if (threadIdx.x == 0) {
     atomicExch(err, 0);
@@ -115,8 +117,16 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
     const float t = T ? T[b] : T0;
     const int k = K ? K[b] : K0;
     const float p = P ? P[b] : 1.f;
-    const bool ok = !all_bad && __builtin_isfinite(t) && t >= 0.f && k >= 0 && (k >= V || k <= max_top_k) &&
-                    p > 0.f && p <= 1.f;
+    bool ok = !all_bad && __builtin_isfinite(t) && t >= 0.f && k >= 0 && (k >= V || k <= max_top_k) &&
+              p > 0.f && p <= 1.f;
+    if (ok && parents) {
+      // Tree drafts: node i's parent is an earlier node.
+      const int g = L.len(b, G);
+      for (int i = 1; i <= g && ok; ++i) {
+        const int pa = parents[L.tok(b, G, i - 1)];
+        ok = pa >= 0 && pa < i;
+      }
+    }
     ReqInfo r;
     r.kind = kReqInvalid;
     r.c = 0.f;
@@ -147,6 +157,7 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
         for (int j = 0; j < g; ++j) {
           if (p_draft) p_draft[L.tok(b, G, j)] = 0.f;
           if (q_draft) q_draft[L.tok(b, G, j)] = 0.f;
+          if (beta) beta[L.tok(b, G, j)] = 0.f;
         }
       }
     }
@@ -687,6 +698,204 @@ __global__ __launch_bounds__(256) void beta_full_kernel(const ET* __restrict__ l
     float t = 0.f;
     for (int k = 0; k < NW; ++k) t += red[k];
     beta[L.tok(b, G, j)] = t;
+  }
+}
+
+// ===========================================================================
+// Sampler-match verification ([P3] "mlxcel의 프롬프트 조회" on the manual
+// page: a proposal is accepted only if it equals the token the target's
+// sampler draws at that position).  Node i of request b (0 = the root, i >= 1
+// the draft token X[i-1], parent given or i - 1) has target row (b, i); every
+// node gets a fresh sample from its row's adjusted law by the Exp(1) race on
+// the stream of (b, i) (temperature 0: the row's argmax); the walk from the
+// root follows the child whose token equals the sample (the lowest-indexed
+// one) and emits the sample where no child matches.
+// ===========================================================================
+
+// One race descriptor per target row of a request without top-k (n: the
+// node, rb: the request); other rows get n = -1.  One thread per row.
+__global__ __launch_bounds__(256) void match_prep_kernel(const float2* __restrict__ part, int S, int rows_t, int G,
+                                                         const ReqInfo* __restrict__ info,
+                                                         const RowCut* __restrict__ cut, Layout L,
+                                                         RaceDesc* __restrict__ rdesc,
+                                                         unsigned long long* __restrict__ rslots) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows_t) return;
+  const int b = row / (G + 1), j = row - b * (G + 1);
+  RaceDesc d;
+  d.n = -1;
+  d.mask_tok = -1;
+  d.resid = 0;
+  d.rb = b;
+  d.mp = d.inv_zp = d.mq = d.inv_zq = 0.f;
+  d.c = 0.f;
+  d.pad2[0] = d.pad2[1] = d.pad2[2] = 0;
+  d.kp = d.kq = 0ull;
+  d.prow = d.qrow = 0;
+  const ReqInfo ri = info[b];
+  if (ri.kind == kReqFull && j <= L.len(b, G)) {
+    d.n = j;
+    d.c = ri.c;
+    if (ri.top_p < 1.f) {
+      const RowCut rc = cut[row];
+      d.mp = rc.m;
+      d.inv_zp = rc.inv_z;
+      d.kp = rc.kappa;
+    } else {
+      float M, Z;
+      merge_row_lane(part + (size_t)row * S, S, ri.c, M, Z);
+      d.mp = M;
+      d.inv_zp = 1.f / Z;
+    }
+    d.prow = (int64_t)(L.trow(b, G, j) * (size_t)L.ts);
+  }
+  rdesc[row] = d;
+  rslots[3 * (size_t)row] = 0ull;
+}
+
+// Samples of the rows of top-k requests: the Exp(1) race over the kept
+// tokens.  One wave per row.
+__global__ __launch_bounds__(256) void sample_topk_kernel(const uint64_t* __restrict__ cand, int kstride, int rows_t,
+                                                          int G, const ReqInfo* __restrict__ info, Layout L,
+                                                          uint32_t k0, uint32_t k1, int32_t* __restrict__ samples) {
+  const int w = threadIdx.x / kWave, lane = lane_id();
+  const int row = blockIdx.x * 4 + w;
+  if (row >= rows_t) return;
+  const int b = row / (G + 1), j = row - b * (G + 1);
+  const ReqInfo ri = info[b];
+  if (ri.kind != kReqTopk || j > L.len(b, G)) return;
+  const uint64_t* pk = cand + (size_t)row * kstride;
+  const CandStats sp = cand_stats(pk, ri.K, ri.c);
+  uint64_t best = 0ull;
+  for (int i = lane; i < ri.K; i += kWave) {
+    const uint64_t k = pk[i];
+    if (!k) continue;
+    const uint32_t y = key_index(k);
+    const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * ri.c) * sp.inv_z;
+    if (p > 0.f) {
+      const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)j, y);
+      const float E = (y & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
+      const uint64_t kk = make_key(p * __builtin_amdgcn_rcpf(E), y);
+      best = kk > best ? kk : best;
+    }
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) samples[row] = best ? (int32_t)key_index(best) : -1;
+}
+
+// The walk, one wave per request: p_parent(x) of every node (its acceptance
+// probability once the parent is reached; also beta), then the path.
+template <typename ET>
+__global__ __launch_bounds__(64) void match_walk_kernel(const ET* __restrict__ lt, const float2* __restrict__ part,
+                                                        const uint64_t* __restrict__ part64,
+                                                        const uint64_t* __restrict__ cand, int kstride, int S, int G,
+                                                        int V, const ReqInfo* __restrict__ info,
+                                                        const RowCut* __restrict__ cut, Layout L,
+                                                        const int32_t* __restrict__ X,
+                                                        const int32_t* __restrict__ parents,
+                                                        const int32_t* __restrict__ samples,
+                                                        int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+                                                        int32_t* __restrict__ path_nodes,
+                                                        float* __restrict__ p_draft, float* __restrict__ q_draft,
+                                                        Stats stats, int* __restrict__ err) {
+  const int b = blockIdx.x, lane = lane_id();
+  const ReqInfo ri = info[b];
+  const size_t r0 = (size_t)b * (G + 1);
+  if (ri.kind == kReqInvalid) {  // outputs other than the path cleared by classify_kernel
+    if (path_nodes)
+      for (int j = lane; j <= G; j += kWave) path_nodes[r0 + j] = -1;
+    return;
+  }
+  const int g = L.len(b, G);
+  auto sample_of = [&](int i) -> int {
+    if (ri.kind == kReqGreedy) {
+      uint64_t m = 0ull;
+      for (int k = 0; k < S; ++k) {
+        const uint64_t v = part64[(r0 + i) * S + k];
+        m = v > m ? v : m;
+      }
+      return (int)key_index(m);
+    }
+    return samples[r0 + i];
+  };
+  auto parent_of = [&](int i) -> int { return parents ? parents[L.tok(b, G, i - 1)] : i - 1; };
+  // Acceptance probability of node i (>= 1): p_parent(x_i).
+  auto write_node = [&](int i, float pd, bool valid) {
+    const size_t t = L.tok(b, G, i - 1);
+    if (p_draft) p_draft[t] = pd;
+    if (q_draft) q_draft[t] = valid ? 1.f : 0.f;
+    if (stats.beta) stats.beta[t] = pd;
+  };
+  if (ri.kind == kReqTopk) {
+    for (int i = 1; i <= g; ++i) {  // wave-cooperative per node
+      const int x = X[L.tok(b, G, i - 1)];
+      const bool valid = x >= 0 && x < V;
+      const uint64_t* pk = cand + (r0 + parent_of(i)) * kstride;
+      const CandStats sp = cand_stats(pk, ri.K, ri.c);
+      const float pd = valid ? cand_prob(pk, ri.K, sp, ri.c, x) : 0.f;
+      if (lane == 0) {
+        write_node(i, pd, valid);
+        if (!valid) atomicOr(err, kErrBadToken);
+      }
+    }
+  } else {
+    for (int i0 = 1; i0 <= g; i0 += kWave) {
+      const int i = i0 + lane;
+      if (i > g) continue;
+      const int x = X[L.tok(b, G, i - 1)];
+      const bool valid = x >= 0 && x < V;
+      const int pa = parent_of(i);
+      float pd = 0.f;
+      if (valid) {
+        if (ri.kind == kReqGreedy) {
+          pd = x == sample_of(pa) ? 1.f : 0.f;
+        } else {
+          const size_t rp = r0 + pa;
+          const float l = Elem<ET>::load1(lt + L.trow(b, G, pa) * (size_t)L.ts + x);
+          if (ri.top_p < 1.f) {
+            const RowCut rc = cut[rp];
+            pd = make_key(l, (uint32_t)x) < rc.kappa ? 0.f : __builtin_amdgcn_exp2f((l - rc.m) * ri.c) * rc.inv_z;
+          } else {
+            float M, Z;
+            merge_row_lane(part + rp * S, S, ri.c, M, Z);
+            pd = __builtin_amdgcn_exp2f((l - M) * ri.c) / Z;
+          }
+        }
+      }
+      write_node(i, pd, valid);
+      if (!valid) atomicOr(err, kErrBadToken);
+    }
+  }
+  // Walk from the root.
+  int cur = 0, d = 0;
+  for (;;) {
+    const int t = sample_of(cur);
+    int child = -1;
+    if (t < 0) {
+      // no sample (cannot happen: a row's law always has positive mass)
+    } else if (!parents) {
+      if (cur < g && X[L.tok(b, G, cur)] == t) child = cur + 1;
+    } else {
+      for (int i0 = 1; i0 <= g && child < 0; i0 += kWave) {
+        const int i = i0 + lane;
+        const bool m = i <= g && parents[L.tok(b, G, i - 1)] == cur && X[L.tok(b, G, i - 1)] == t;
+        const uint64_t mask = ballot(m);
+        if (mask) child = i0 + (int)__builtin_ctzll(mask);
+      }
+    }
+    if (lane == 0) out[r0 + d] = t;
+    if (child < 0) break;
+    if (lane == 0 && path_nodes) path_nodes[r0 + d] = child;
+    ++d;
+    cur = child;
+  }
+  for (int j = lane; j <= G; j += kWave) {
+    if (j > d) out[r0 + j] = -1;
+    if (path_nodes && j >= d) path_nodes[r0 + j] = -1;
+  }
+  if (lane == 0) {
+    nacc[b] = d;
+    count_round(stats, b, g, d);
   }
 }
 

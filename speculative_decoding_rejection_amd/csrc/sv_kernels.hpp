@@ -145,7 +145,7 @@ struct __align__(16) RaceDesc {
   int32_t mask_tok;  // one-hot: token removed from the residual, else -1
   int32_t resid;     // 1: weights max(p - q, 0), q from draft logits; 2: q given as
                      // probabilities; 0: weights p
-  int32_t pad;
+  int32_t rb;        // request of the race stream (counter (y >> 1, n, rb, 1))
   float mp, inv_zp, mq, inv_zq;  // softmax stats of target row n / draft row n
   float c;                       // log2(e) / T of the request
   int32_t pad2[3];
@@ -1082,7 +1082,7 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
   d.n = n;
   d.mask_tok = (MODE == 1 && n < g) ? X[L.tok(b, G, n)] : -1;
   d.resid = n < g ? (MODE == 0 ? 1 : (MODE == 2 ? 2 : 0)) : 0;
-  d.pad = 0;
+  d.rb = b;
   race_stats((size_t)b * (G + 1) + n, d.mp, d.inv_zp, d.kp);
   d.mq = 0.f;
   d.inv_zq = 0.f;
@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   const int a = s * seg;
   const int e = min(V, a + seg);
   const int tid = threadIdx.x;
-  const uint32_t ub = (uint32_t)b, un = (uint32_t)n;
+  const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)n;
   float best = -1.f;
   int best_y = -1;
   auto weight = [&](float lp, float lq, int y) -> float {
@@ -1232,23 +1232,26 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
 // Writes each request's race winner.  If the residual had no positive weight
 // (possible only when p and q agree to rounding) the draw is taken from p_n
 // instead, by the whole workgroup over the row (rare).
+// With `samples` (one race per row) the token goes to samples[desc index];
+// otherwise to out[request][n].
 template <typename ET, int NT, bool CUT>
 __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ lt, int G, int V, uint32_t k0,
                                                          uint32_t k1, const RaceDesc* __restrict__ desc,
                                                          const unsigned long long* __restrict__ slots,
-                                                         int32_t* __restrict__ out) {
+                                                         int32_t* __restrict__ out, int32_t* __restrict__ samples) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const RaceDesc d = desc[b];
   const int n = d.n;
   if (n < 0) return;
   const float c = d.c;
+  int32_t* dst = samples ? samples + b : out + (size_t)b * (G + 1) + n;
   const unsigned long long win = slots[3 * b];
   if (win) {
-    if (tid == 0) out[(size_t)b * (G + 1) + n] = (int32_t)key_index(win);
+    if (tid == 0) *dst = (int32_t)key_index(win);
     return;
   }
   const ET* rp = lt + d.prow;
-  const uint32_t ub = (uint32_t)b, un = (uint32_t)n;
+  const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)n;
   uint64_t kp = 0ull;
   for (int y = tid; y < V; y += NT) {
     const float l = Elem<ET>::load1(rp + y);
@@ -1268,7 +1271,7 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
   if (tid == 0) {
     uint64_t bk = red[0];
     for (int k = 1; k < NT / kWave; ++k) bk = red[k] > bk ? red[k] : bk;
-    out[(size_t)b * (G + 1) + n] = bk ? (int32_t)key_index(bk) : -1;
+    *dst = bk ? (int32_t)key_index(bk) : -1;
   }
 }
 

@@ -163,3 +163,24 @@ def test_batch_outputs_checks(sv):
     outs = sv.SvOutputs(1 << 20, 1 << 20, None, None, None, (1 << 20) + 4)  # counters must be 8-byte aligned
     assert lib.spec_verify_batch(ctypes.byref(p), None, None, fake, None, fake, ctypes.byref(outs), fake, 1 << 20,
                                  None) == sv.SV_ERR_INVALID_ARG
+
+
+def test_batch_match_layout_errors(sv):
+    """Sampler-match: no draft rows are read; parents only with this kind and
+    4-byte aligned; path_nodes 4-byte aligned."""
+    fake = 1 << 21
+    p = sv.make_params(4, 3, 5000, sv.SV_BF16, 0.7, 0, 1)
+    ok = sv.SvSampling(fake, None, None, 0, 0)
+    L = sv.SvLayout
+    d = ctypes.c_void_p(fake)
+    M = sv.SV_DRAFT_MATCH
+    assert _call_batch(sv, p, ok, ws_bytes=16, layout=L(M, 0, 0, 0, None, None)) == sv.SV_ERR_WORKSPACE
+    assert _call_batch(sv, p, ok, ws_bytes=16, layout=L(M, 0, 0, 0, None, fake)) == sv.SV_ERR_WORKSPACE
+    assert _call_batch(sv, p, ok, layout=L(M, 0, 0, 0, None, fake + 2)) == sv.SV_ERR_INVALID_ARG
+    assert _call_batch(sv, p, ok, layout=L(sv.SV_DRAFT_LOGITS, 0, 0, 0, None, fake), draft=d) == \
+        sv.SV_ERR_INVALID_ARG  # parents with another kind
+    assert _call_batch(sv, p, ok, layout=L(4, 0, 0, 0, None, None)) == sv.SV_ERR_INVALID_ARG
+    lib = sv.load_library()
+    outs = sv.SvOutputs(1 << 20, 1 << 20, None, None, None, None, (1 << 20) + 2)
+    assert lib.spec_verify_batch(ctypes.byref(p), ctypes.byref(ok), ctypes.byref(L(M, 0, 0, 0, None, None)),
+                                 d, None, d, ctypes.byref(outs), d, 1 << 20, None) == sv.SV_ERR_INVALID_ARG

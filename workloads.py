@@ -25,9 +25,20 @@ fixed-size chunks so that the bytes do not depend on the device's memory):
                          the draft's temperature / top-k law as for prob (the
                          drafter does not apply top-p; a draft outside the
                          nucleus is a valid input that the verifier rejects).
-  batch settings (entry "batch") each request takes one of the workload's
-                 ``mix`` classes (temperature, top_k, top_p), uniformly, from
-                 a generator seeded with data_seed + 1.
+                 match:  token-only drafts for sampler-match (entry "match",
+                         settings as for batch).  The drafter's noisy row of
+                         node i (Lt of that row + sigma_b N(0, 1)) proposes
+                         its children: the k-th child of a node (by index)
+                         takes the k-th token of a draw without replacement
+                         (Gumbel top-k of that row / T over its top-k set;
+                         temperature 0: the k-th largest logit).  A chain
+                         (no ``parents``) is the batch recipe with one child
+                         per node.  With ``peak`` > 0 every target row gets
+                         +peak on one uniformly drawn token (a confident
+                         target, as where a reply copies its prompt).
+  batch settings (entry "batch" / "match") each request takes one of the
+                 workload's ``mix`` classes (temperature, top_k, top_p),
+                 uniformly, from a generator seeded with data_seed + 1.
 The five workloads mirror the shapes of the reference pages' setting scaled
 to a batch (gamma 3..8 as on the pages, temperatures 0 / 0.7 / 0.8 / 1,
 acceptance rates spanning the 0.5..0.9 range quoted for good drafter pairs);
@@ -64,6 +75,8 @@ class Workload:
     lengths: tuple = ()   # entry "batch": (lo, hi) draft positions per request, uniform (ragged rows)
     sigma_pos: tuple = ()  # draft noise per position (G values), replacing draft_sigma
     draft_probs: bool = False  # entry "batch": the drafter hands over fp32 probabilities
+    parents: tuple = ()   # entry "match": parent node of draft nodes 1..G (empty: a chain)
+    peak: float = 0.0     # logit bonus of one token per target row (0: none)
 
     @property
     def torch_dtype(self):
@@ -82,9 +95,18 @@ class Workload:
         return self.B * self.G if self.entry in ("prob", "batch") else 0
 
     @property
+    def ragged(self) -> bool:
+        return self.entry in ("batch", "match") and bool(self.lengths)
+
+    @property
+    def has_settings(self) -> bool:
+        """Per-request settings (spec_verify_batch)."""
+        return self.entry in ("batch", "match")
+
+    @property
     def draft_lengths(self) -> np.ndarray:
         """Draft positions per request (all G unless ragged)."""
-        if self.entry == "batch" and self.lengths:
+        if self.ragged:
             gen = torch.Generator(device="cpu")
             gen.manual_seed(self.data_seed + 2)
             lo, hi = self.lengths
@@ -99,6 +121,8 @@ class Workload:
     def logit_bytes(self) -> int:
         """Bytes of every logit row read once: the algorithmic traffic (for a
         batch workload, the draft rows of its sampled requests only)."""
+        if self.entry == "match":
+            return int((self.draft_lengths + 1).sum()) * self.V * self.elem_bytes
         if self.entry != "batch":
             return (self.target_rows + self.draft_rows) * self.V * self.elem_bytes
         g = self.draft_lengths
@@ -160,6 +184,24 @@ ROUNDS_WORKLOADS = {
 }
 ALL_WORKLOADS.update(ROUNDS_WORKLOADS)
 
+# Sampler-match over token-only drafts: prompt lookup's chains (at most 7
+# proposals per round, a verify block of 8) and a tree with second choices at
+# depths 1 and 2, on a 151936-token vocabulary in bf16.  Requests mix
+# temperature 0, top-k 20 then top-p 0.8, top-p 0.9 alone and plain sampling;
+# target rows carry a confident token (+18 logits over N(0, 9)), as where a
+# reply copies its prompt.
+_MIX_MATCH = ((0.0, 0, 1.0), (0.7, 20, 0.8), (1.0, 0, 0.9), (0.8, 0, 1.0))
+TREE7 = (0, 0, 1, 1, 3, 5, 6)
+MATCH_WORKLOADS = {
+    "match_lookup_bf16_b256_g7_v151936": Workload(
+        "match_lookup_bf16_b256_g7_v151936", "match", 256, 7, 151936, "bf16", 1.0, 0, 3.0, (0.5, 2.0),
+        mix=_MIX_MATCH, peak=18.0),
+    "match_tree_bf16_b256_g7_v151936": Workload(
+        "match_tree_bf16_b256_g7_v151936", "match", 256, 7, 151936, "bf16", 1.0, 0, 3.0, (0.5, 2.0),
+        mix=_MIX_MATCH, peak=18.0, parents=TREE7),
+}
+ALL_WORKLOADS.update(MATCH_WORKLOADS)
+
 WORKLOAD_ORDER = list(WORKLOADS)
 HEADLINE = "prob_topk64_bf16_b1024_g8_v256000"
 
@@ -209,7 +251,7 @@ def generate(wl: Workload, device="cpu", requests: range | None = None) -> dict:
     ld_all = (torch.empty((hi_req - lo_req, G, V), dtype=wl.torch_dtype, device=device)
               if wl.has_draft_logits else None)
     x_all = torch.empty((hi_req - lo_req, G), dtype=torch.int32, device=device)
-    settings = batch_settings(wl) if wl.entry == "batch" else None
+    settings = batch_settings(wl) if wl.has_settings else None
     for c0 in range(0, B, wl.chunk):
         c1 = min(B, c0 + wl.chunk)
         sub = None if settings is None else {k: v[c0:c1] for k, v in settings.items()}
@@ -230,8 +272,10 @@ def generate(wl: Workload, device="cpu", requests: range | None = None) -> dict:
         res.update({k: v[lo_req:hi_req].to(device) for k, v in settings.items()})
     if wl.entry == "batch" and wl.draft_probs:
         res["draft_probs"] = _drafter_probs(ld_all, res["temperature"], res["top_k"])
-    if wl.entry == "batch" and wl.lengths:
+    if wl.ragged:
         res["lengths"] = torch.from_numpy(wl.draft_lengths[lo_req:hi_req]).to(device)
+    if wl.entry == "match" and wl.parents:
+        res["parents"] = torch.tensor(wl.parents, dtype=torch.int32, device=device).repeat(hi_req - lo_req, 1)
     return res
 
 
@@ -265,7 +309,7 @@ def pack_ragged(inp: dict, lengths) -> dict:
     out = {"cu_draft": torch.from_numpy(cu).to(inp["target_logits"].device),
            "target_logits": torch.cat([inp["target_logits"][b, :g[b] + 1] for b in range(len(g))]),
            "draft_tokens": torch.cat([inp["draft_tokens"][b, :g[b]] for b in range(len(g))])}
-    for key in ("draft_logits", "draft_probs"):
+    for key in ("draft_logits", "draft_probs", "parents"):
         if inp.get(key) is not None:
             out[key] = torch.cat([inp[key][b, :g[b]] for b in range(len(g))])
     return out
@@ -281,9 +325,14 @@ def with_stride(rows: torch.Tensor, width: int, fill: float) -> torch.Tensor:
 
 def _chunk(wl: Workload, c: int, gen: torch.Generator, device, settings=None):
     G, V = wl.G, wl.V
-    lt = (torch.randn((c, G + 1, V), generator=gen, device=device, dtype=torch.float32)
-          * wl.target_sigma).to(wl.torch_dtype)
+    lt = torch.randn((c, G + 1, V), generator=gen, device=device, dtype=torch.float32) * wl.target_sigma
+    if wl.peak > 0.0:
+        at = torch.randint(0, V, (c, G + 1, 1), generator=gen, device=device)
+        lt.scatter_add_(-1, at, torch.full((c, G + 1, 1), wl.peak, device=device))
+    lt = lt.to(wl.torch_dtype)
     ld = None
+    if wl.entry == "match":
+        return lt, None, _match_tokens(wl, lt, c, gen, device, settings)
     if wl.has_draft_logits:
         lo, hi = wl.draft_sigma
         sig = lo + (hi - lo) * torch.rand((c, 1, 1), generator=gen, device=device, dtype=torch.float32)
@@ -314,6 +363,40 @@ def _chunk(wl: Workload, c: int, gen: torch.Generator, device, settings=None):
     else:
         raise ValueError(wl.entry)
     return lt, ld, x.to(torch.int32)
+
+
+def _match_tokens(wl: Workload, lt: torch.Tensor, c: int, gen: torch.Generator, device, settings) -> torch.Tensor:
+    """Token-only drafts of a chain or tree (the drafter's rows are noisy
+    copies of the parents' target rows; see the module recipe)."""
+    G, V = wl.G, wl.V
+    par = list(wl.parents) if wl.parents else list(range(G))
+    lo, hi = wl.draft_sigma
+    sig = lo + (hi - lo) * torch.rand((c, 1, 1), generator=gen, device=device, dtype=torch.float32)
+    noise = torch.randn((c, G, V), generator=gen, device=device, dtype=torch.float32)
+    ld = lt[:, :G].float() + sig * noise  # drafter row of node j, j < G (the nodes that can be parents)
+    nchild = [par.count(j) for j in range(G)]
+    rank = [par[:i].count(par[i]) for i in range(G)]  # child order under its parent
+    x = torch.empty((c, G), dtype=torch.int64, device=device)
+    for r in range(c):
+        t, k = float(settings["temperature"][r]), int(settings["top_k"][r])
+        for j in range(G):
+            if not nchild[j]:
+                continue
+            z = ld[r, j]
+            if t == 0.0:
+                order = torch.argsort(z, descending=True, stable=True)[:nchild[j]]
+            else:
+                z = z / t
+                keep = torch.argsort(z, descending=True, stable=True)
+                if 0 < k < V:
+                    keep = keep[:k]
+                u = torch.rand(keep.shape, generator=gen, device=device, dtype=torch.float32)
+                gz = z[keep] - torch.log(-torch.log(u))
+                order = keep[torch.argsort(gz, descending=True, stable=True)[:nchild[j]]]
+            for i in range(G):
+                if par[i] == j:
+                    x[r, i] = order[min(rank[i], order.numel() - 1)]
+    return x
 
 
 def to_host_arrays(t: torch.Tensor | None):
