@@ -80,6 +80,8 @@ def _load():
     lib.sv_ref_race.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
                                 ctypes.c_uint32, ctypes.POINTER(ctypes.c_double)]
     lib.sv_ref_race.restype = ctypes.c_int
+    lib.sv_ref_block_race.argtypes = lib.sv_ref_race.argtypes
+    lib.sv_ref_block_race.restype = ctypes.c_int
     lib.sv_ref_verify.argtypes = ([ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_int, ctypes.c_uint64]
                                   + [ctypes.c_void_p] * 13 + [ctypes.c_int])
     lib.sv_ref_verify.restype = ctypes.c_int
@@ -145,6 +147,15 @@ def race(w, seed: int, b: int, j: int) -> tuple[int, float]:
     wv = np.ascontiguousarray(w, dtype=np.float64)
     m = ctypes.c_double(0.0)
     tok = _load().sv_ref_race(_ptr(wv), wv.shape[0], seed, b, j, ctypes.byref(m))
+    return tok, m.value
+
+
+def block_race(w, seed: int, b: int, j: int) -> tuple[int, float]:
+    """The two-stage race (blocks of 64 tokens, then tokens): the sampler of
+    full-vocabulary laws under sampler-match."""
+    wv = np.ascontiguousarray(w, dtype=np.float64)
+    m = ctypes.c_double(0.0)
+    tok = _load().sv_ref_block_race(_ptr(wv), wv.shape[0], seed, b, j, ctypes.byref(m))
     return tok, m.value
 
 

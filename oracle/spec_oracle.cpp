@@ -259,6 +259,64 @@ int race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, do
   return best;
 }
 
+// The uniform of block k of a block race at (b, j): counter (k >> 1, j, b, 2),
+// words 0/1 for even k, 2/3 for odd k.
+double uniform_block(uint64_t seed, uint32_t b, uint32_t j, uint32_t k) {
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t ctr[4] = {k >> 1, j, b, 2u};
+  uint32_t w[4];
+  philox4x32_10(ctr, key, w);
+  if ((k & 1u) == 0u) return words_to_unit(w[0], w[1]);
+  return words_to_unit(w[2], w[3]);
+}
+
+// A draw from the law w (unnormalised) in two Exp(1) races: first over
+// blocks of kBlockRace consecutive tokens (block k holds tokens
+// [64k, 64k + 64)) weighted by their total mass W_k, one exponential per
+// block; then over the tokens of the winning block, with the token
+// exponentials of `race`.  The minimum of independent exponentials E_y / w_y
+// over a block is itself exponential with rate W_k, and which token attains
+// it is independent of its value with P(y) = w_y / W_k; so the block winner
+// has law W_k / W and the token law w_y / W: the same law as the one-stage
+// race, with one random number per block instead of one per token.
+// *margin: the smaller relative gap of the two stages.
+constexpr int kBlockRace = 64;
+int block_race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
+  const double inf = std::numeric_limits<double>::infinity();
+  const size_t V = w.size();
+  const size_t nblk = (V + kBlockRace - 1) / kBlockRace;
+  int kbest = -1;
+  double s1 = -inf, s2 = -inf;
+  for (size_t k = 0; k < nblk; ++k) {
+    double W = 0.0;
+    for (size_t y = k * kBlockRace; y < std::min(V, (k + 1) * kBlockRace); ++y)
+      if (w[y] > 0.0) W += w[y];
+    if (!(W > 0.0)) continue;
+    const double E = -std::log(uniform_block(seed, b, j, (uint32_t)k));
+    const double s = (E == 0.0) ? inf : W / E;
+    if (s > s1) {
+      s2 = s1;
+      s1 = s;
+      kbest = (int)k;
+    } else if (s > s2) {
+      s2 = s;
+    }
+  }
+  double m1 = 1.0;
+  if (kbest >= 0 && s2 != -inf) m1 = (s1 == inf) ? ((s2 == inf) ? 0.0 : 1.0) : (s1 - s2) / s1;
+  if (kbest < 0) {
+    if (margin) *margin = 1.0;
+    return -1;
+  }
+  // Stage two: the one-stage race restricted to the block (same streams).
+  std::vector<double> wb(w.size(), 0.0);
+  for (size_t y = (size_t)kbest * kBlockRace; y < std::min(V, ((size_t)kbest + 1) * kBlockRace); ++y) wb[y] = w[y];
+  double m2 = 1.0;
+  const int y = race(wb, seed, b, j, &m2);
+  if (margin) *margin = std::min(m1, m2);
+  return y;
+}
+
 enum { MODE_PROB = 0, MODE_ONEHOT = 1, MODE_GREEDY = 2, MODE_NAIVE = 3, MODE_PROBS = 4 };
 
 struct Problem {
@@ -432,7 +490,11 @@ int verify_match(const Problem& P, uint32_t b, const char* Lt, const int32_t* X,
       double c = 1.0;
       p[i] = row_probs(row, P.dtype, V, P.T, P.top_k, P.top_p, &c);
       cm = std::min(cm, c);
-      s[i] = race(p[i], P.seed, b, (uint32_t)i, &margin[i]);
+      // A top-k law (at most top_k tokens) is drawn by the one-stage race;
+      // a law over the whole vocabulary by the block race.
+      const bool topk = P.top_k > 0 && P.top_k < V;
+      s[i] = topk ? race(p[i], P.seed, b, (uint32_t)i, &margin[i])
+                  : block_race(p[i], P.seed, b, (uint32_t)i, &margin[i]);
     }
   }
   for (int i = 1; i <= g; ++i) {
@@ -507,6 +569,12 @@ int sv_ref_row_argmax(const void* row, int dtype, int V) { return row_argmax(row
 int sv_ref_race(const double* w, int V, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
   std::vector<double> wv(w, w + V);
   return race(wv, seed, b, j, margin);
+}
+
+// The two-stage (block) race over w[0..V) at (seed, b, j).
+int sv_ref_block_race(const double* w, int V, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
+  std::vector<double> wv(w, w + V);
+  return block_race(wv, seed, b, j, margin);
 }
 
 // Batched verifier.

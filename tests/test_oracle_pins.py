@@ -1026,3 +1026,60 @@ def test_sampler_match_reductions():
     bad[2, 1] = 2
     c = oracle.verify_batch(lt, None, x, T, K, P, seed=4, match=True, parents=bad)
     assert c["bad_param"][2] == 1 and (c["out_tokens"][2] == -1).all() and c["bad_param"].sum() == 1
+
+
+# ---------------------------------------------------------------------------
+# The two-stage (block) race that draws full-vocabulary laws under
+# sampler-match
+# ---------------------------------------------------------------------------
+
+def test_block_race_law():
+    """Blocks of 64 tokens race by total mass, then tokens within the
+    winner: the token law is w / sum(w) and the block law W_k / W (chi-square
+    over 120k independent draws; V = 300 leaves a last block of 44 tokens)."""
+    rng = np.random.default_rng(5)
+    V = 300
+    w = rng.exponential(1.0, V) ** 3
+    w[rng.random(V) < 0.2] = 0.0      # tokens without mass are never drawn
+    w[[0, 10, 70, 299]] = [30.0, 40.0, 25.0, 30.0]  # heavy tokens in the first, second and last blocks
+    w[128:192] = 0.0                  # a block without mass
+    n = 120_000
+    toks = np.array([oracle.block_race(w, 17, b, 3)[0] for b in range(n)])
+    assert (w[toks] > 0).all()
+    p = w / w.sum()
+    counts = np.bincount(toks, minlength=V)
+    big = p * n >= 5
+    obs = np.append(counts[big], counts[~big].sum())
+    exp = np.append(p[big] * n, p[~big].sum() * n)
+    assert stats.chisquare(obs, exp).pvalue > 1e-6
+    blk = np.add.reduceat(counts, np.arange(0, V, 64))
+    W = np.add.reduceat(p, np.arange(0, V, 64))
+    assert blk[2] == 0
+    keep = W > 0
+    assert stats.chisquare(blk[keep], W[keep] * n).pvalue > 1e-6
+
+
+def test_block_race_reduces_to_the_token_race():
+    """Within one block the first stage has one contestant, so the draw is
+    the one-stage race on the same token stream, draw for draw: for V <= 64,
+    and for a law whose mass lies in one block of a larger row."""
+    rng = np.random.default_rng(9)
+    for b in range(300):
+        w = rng.random(rng.integers(1, 65))
+        assert oracle.block_race(w, 5, b, 1)[0] == oracle.race(w, 5, b, 1)[0]
+        big = np.zeros(1000)
+        k = int(rng.integers(0, 16))  # block 15 is the last, partial one (tokens 960..999)
+        big[64 * k: 64 * k + 64] = rng.random(min(64, 1000 - 64 * k))
+        assert oracle.block_race(big, 5, b, 2)[0] == oracle.race(big, 5, b, 2)[0]
+
+
+def test_block_race_streams_are_distinct():
+    """Block uniforms come from their own stream (counter word 3 = 2): two
+    blocks of equal mass are each drawn about half the time, and the same
+    (seed, b, j) gives the same draw."""
+    w = np.zeros(128)
+    w[5] = w[100] = 1.0
+    toks = np.array([oracle.block_race(w, 23, b, 0)[0] for b in range(4000)])
+    assert set(toks.tolist()) == {5, 100}
+    assert abs((toks == 5).mean() - 0.5) < 4 * np.sqrt(0.25 / 4000)
+    assert all(oracle.block_race(w, 23, b, 0)[0] == t for b, t in zip(range(50), toks))
