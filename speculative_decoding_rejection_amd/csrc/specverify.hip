@@ -273,23 +273,22 @@ sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, 
                      (const ET*)lt, QP ? (const ET*)nullptr : (const ET*)ld, QP ? (const float*)ld : nullptr, pl.V,
                      pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots);
   hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
-                     pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out, (int32_t*)nullptr);
+                     pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
   t.done();
   return check_launch();
 }
 
-// One Exp(1) race per target row (sampler-match): descriptors and slots per
-// row, winners to `samples`.
+// One sample per target row of a full-row request (sampler-match): the
+// two-stage block race, descriptors and slots per row, winners to `samples`.
 template <typename ET, bool CUT>
-sv_status run_row_race(const Plan& pl, const void* lt, uint32_t k0, uint32_t k1, char* ws, hipStream_t st) {
+sv_status run_block_race(const Plan& pl, const void* lt, uint32_t k0, uint32_t k1, char* ws, hipStream_t st) {
   TimedLaunch t(2, st);
   const RaceDesc* rdesc = (const RaceDesc*)(ws + pl.off_rdesc);
   unsigned long long* rslots = (unsigned long long*)(ws + pl.off_rslots);
-  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256, CUT, false>), dim3(pl.rows_t * pl.Srr), dim3(256), 0, st,
-                     (const ET*)lt, (const ET*)nullptr, (const float*)nullptr, pl.V, pl.Srr, pl.segrr, k0, k1, rdesc,
-                     rslots);
-  hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.rows_t), dim3(256), 0, st, (const ET*)lt,
-                     pl.G, pl.V, k0, k1, rdesc, (const unsigned long long*)rslots, (int32_t*)nullptr,
+  hipLaunchKernelGGL((sv::block_race_kernel<ET, 256, CUT>), dim3(pl.rows_t * pl.Srr), dim3(256), 0, st,
+                     (const ET*)lt, pl.V, pl.Srr, pl.segrr, k0, k1, rdesc, rslots);
+  hipLaunchKernelGGL((sv::block_finish_kernel<ET, CUT>), dim3((pl.rows_t + 3) / 4), dim3(256), 0, st, (const ET*)lt,
+                     pl.rows_t, pl.V, k0, k1, rdesc, (const unsigned long long*)rslots,
                      (int32_t*)(ws + pl.off_samples));
   t.done();
   return check_launch();
@@ -425,7 +424,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       t.done();
       if ((s = check_launch()) != SV_OK) return s;
     }
-    s = nuc ? run_row_race<ET, true>(pl, lt, k0, k1, ws, st) : run_row_race<ET, false>(pl, lt, k0, k1, ws, st);
+    s = nuc ? run_block_race<ET, true>(pl, lt, k0, k1, ws, st) : run_block_race<ET, false>(pl, lt, k0, k1, ws, st);
     if (s != SV_OK) return s;
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::match_walk_kernel<ET>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,

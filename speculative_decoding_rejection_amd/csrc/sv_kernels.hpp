@@ -1229,22 +1229,20 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   }
 }
 
-// Writes each request's race winner.  If the residual had no positive weight
-// (possible only when p and q agree to rounding) the draw is taken from p_n
-// instead, by the whole workgroup over the row (rare).
-// With `samples` (one race per row) the token goes to samples[desc index];
-// otherwise to out[request][n].
+// Writes each request's race winner to out[request][n].  If the residual had
+// no positive weight (possible only when p and q agree to rounding) the draw
+// is taken from p_n instead, by the whole workgroup over the row (rare).
 template <typename ET, int NT, bool CUT>
 __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ lt, int G, int V, uint32_t k0,
                                                          uint32_t k1, const RaceDesc* __restrict__ desc,
                                                          const unsigned long long* __restrict__ slots,
-                                                         int32_t* __restrict__ out, int32_t* __restrict__ samples) {
+                                                         int32_t* __restrict__ out) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const RaceDesc d = desc[b];
   const int n = d.n;
   if (n < 0) return;
   const float c = d.c;
-  int32_t* dst = samples ? samples + b : out + (size_t)b * (G + 1) + n;
+  int32_t* dst = out + (size_t)b * (G + 1) + n;
   const unsigned long long win = slots[3 * b];
   if (win) {
     if (tid == 0) *dst = (int32_t)key_index(win);
