@@ -239,8 +239,13 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  *   draft_tokens: as described by layout;
  *   outputs: see sv_outputs.
  * Sampler-match (layout->draft_kind SV_DRAFT_MATCH): every node gets a fresh
- * sample from its row's adjusted law (the Exp(1) race on the stream of
- * (request, node); temperature 0: the argmax); from the root the walk follows
+ * sample from its row's adjusted law (temperature 0: the argmax).  A top-k
+ * law is drawn by the Exp(1) race over its kept tokens on the stream of
+ * (request, node); a law over the whole vocabulary by two races: over the
+ * blocks of 64 consecutive tokens weighted by their mass (block k's variate
+ * from counter (k >> 1, node, request, 2), words 0/1 for even k, 2/3 for odd
+ * k), then over the tokens of the winning block (the token streams of the
+ * one-stage race).  Both give the law exactly.  From the root the walk follows
  * the child whose token equals the sample (the lowest-indexed one if several
  * do) and emits the sample where no child matches: out_tokens holds the
  * accepted tokens and that sample, num_accepted the accepted depth.  Lossless

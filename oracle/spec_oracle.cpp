@@ -35,7 +35,9 @@
 //   * sampler-match ([P3] "mlxcel의 프롬프트 조회"): every node of the draft
 //     (a chain, or a tree given by parent indices) gets a fresh sample from
 //     its row's adjusted law, drawn by the Exp(1) race on the stream of
-//     (b, node); from the root, the walk follows the child whose token equals
+//     (b, node) (a law over the whole vocabulary: first over blocks of 64
+//     tokens by their mass, then within the winning block; the same law);
+//     from the root, the walk follows the child whose token equals
 //     the sample (the lowest-indexed child if several do) and emits the
 //     sample where no child matches.
 //   * every argmax and every race tie goes to the lowest index;
