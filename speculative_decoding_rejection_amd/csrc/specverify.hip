@@ -151,8 +151,9 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   off = align_up(off + (size_t)pl->B * sizeof(ReqInfo), kWsAlign);
   pl->off_cut = off;
   if (sm && sm->top_p) off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
-  // Sampler-match: one race per target row.
-  pl->Srr = splits_for(pl->rows_t, pl->V, 4096, 2048);
+  // Sampler-match: one sample per target row; the block race splits rows
+  // like the softmax pass (a quarter of the rows taken as its own).
+  pl->Srr = splits_for((pl->rows_t + 3) / 4, pl->V, 2048, 8192);
   pl->segrr = seg_for(pl->V, pl->Srr);
   pl->Srr = (pl->V + pl->segrr - 1) / pl->segrr;
   pl->off_rdesc = off;

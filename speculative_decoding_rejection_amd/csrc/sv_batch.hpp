@@ -823,6 +823,10 @@ __global__ __launch_bounds__(NT) void block_race_kernel(const ET* __restrict__ l
   const int kb0 = a / kRaceBlock, nblk = (e - a + kRaceBlock - 1) / kRaceBlock;
   const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)d.n;
   const float mpc = d.mp * d.c;
+  // The nucleus cut as a float compare (see race_full_kernel).
+  const bool cut = CUT && d.kp != 0ull;
+  const float kv = cut ? key_value(d.kp) : 0.f;
+  const int ki = cut ? (int)key_index(d.kp) : 0;
   uint64_t best = 0ull;
   for (int q0 = tid / LPB; q0 < nblk; q0 += U * BPS) {
     float f[U][EPV];
@@ -844,9 +848,8 @@ __global__ __launch_bounds__(NT) void block_race_kernel(const ET* __restrict__ l
       float w = 0.f;
 #pragma unroll
       for (int k = 0; k < EPV; ++k) {
-        float p = __builtin_amdgcn_exp2f(fmaf(f[u][k], d.c, -mpc));
-        if (CUT && make_key(f[u][k], (uint32_t)(y0 + k)) < d.kp) p = 0.f;
-        w += p;
+        const float p = __builtin_amdgcn_exp2f(fmaf(f[u][k], d.c, -mpc));
+        w += (!cut || f[u][k] > kv || (f[u][k] == kv && y0 + k <= ki)) ? p : 0.f;
       }
 #pragma unroll
       for (int m = LPB / 2; m >= 1; m >>= 1) w += __shfl_xor(w, m);

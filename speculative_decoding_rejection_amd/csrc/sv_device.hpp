@@ -20,11 +20,10 @@ constexpr int kWave = 64;
 // advances by the golden-ratio and sqrt(3)-1 Weyl increments between rounds.
 // ---------------------------------------------------------------------------
 // a ^ b ^ k in one VALU instruction (gfx950's three-input bit operation,
-// truth table 0x96); k is wave-uniform (the key schedule) and sits in an SGPR.
+// truth table 0x96); k is wave-uniform (the key schedule).  The builtin, not
+// inline assembly, so the scheduler can interleave independent Philox blocks.
 __device__ __forceinline__ uint32_t xor3_sk(uint32_t a, uint32_t b, uint32_t k) {
-  uint32_t r;
-  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
-  return r;
+  return __builtin_amdgcn_bitop3_b32(a, b, k, 0x96);
 }
 
 // Requires a wave-uniform key (k0, k1).
@@ -41,6 +40,24 @@ __device__ __forceinline__ uint4 philox10(uint4 c, uint32_t k0, uint32_t k1) {
     k1 += 0xBB67AE85u;
   }
   return c;
+}
+
+// N independent blocks advanced round by round together, so that N
+// multiply-xor chains are in flight at once (bit-identical to philox10).
+template <int N>
+__device__ __forceinline__ void philox10_multi(uint4 (&c)[N], uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint64_t pa = (uint64_t)c[i].x * 0xD2511F53ull;
+      const uint64_t pb = (uint64_t)c[i].z * 0xCD9E8D57ull;
+      c[i] = make_uint4(xor3_sk((uint32_t)(pb >> 32), c[i].y, k0), (uint32_t)pb,
+                        xor3_sk((uint32_t)(pa >> 32), c[i].w, k1), (uint32_t)pa);
+    }
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
 }
 
 // Stream layout: the accept uniform of (b, j) is counter (0, j, b, 0), words
@@ -73,6 +90,17 @@ __device__ __forceinline__ float exp1_from_words(uint32_t lo, uint32_t hi) {
   const float lg = -0.6931471805599453f * __builtin_amdgcn_logf(u);
   return t < 0.0625f ? ser : lg;
 }
+
+// The exact gap t = 1 - u of the same u, rounded to fp32.  -ln(1 - t) >= t,
+// so a race score w / E never exceeds w / t: a token with w <= s t cannot
+// beat a score s, and its logarithm need not be taken.
+__device__ __forceinline__ float unit_gap_from_words(uint32_t lo, uint32_t hi) {
+  return fmaf((float)(~lo >> 11), 0x1.0p-53f, (float)(~hi) * 0x1.0p-32f);
+}
+// Factor that keeps the skip test exact under fp32 rounding: E is computed
+// within 1e-6 relative of -ln(u) and t within 2^-24 of the gap, so a token
+// with w <= s t (1 - 2^-16) scores below s as computed.
+constexpr float kRaceSkip = 1.0f - 0x1.0p-16f;
 
 // ---------------------------------------------------------------------------
 // Order keys.  key(v, i) = ord32(v) << 32 | ~i: larger key <=> larger value,

@@ -1112,110 +1112,172 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
 // atomic max, and race_finish_kernel writes the token.  CUT: rows may carry a
 // nucleus cut (tokens with key < kp / kq have p = 0 / q = 0).  QP: q is given
 // as fp32 probabilities (rows of qp).
-template <typename ET, int NT, bool CUT, bool QP>
-__global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
-                                                       const float* __restrict__ qp, int V, int S, int seg,
-                                                       uint32_t k0, uint32_t k1, const RaceDesc* __restrict__ desc,
-                                                       unsigned long long* __restrict__ slots) {
+//
+// race_scan is one thread's pass over its part of the slice for one kind of
+// weight, chosen per workgroup outside the streaming loop: RES 0 (p, with
+// the one-hot draft token masked), 1 (max(p - q, 0), q from draft logits; QV:
+// the draft row shares the target row's 16-byte alignment and is read in
+// vectors), 2 (q given as fp32 probabilities); EVEN: vectors start on even
+// tokens, so tokens 2m and 2m + 1 share one Philox block.
+struct RaceRow {
+  float mp, inv_zp, mq, inv_zq, c, kvp, kvq;
+  int kip, kiq, mask_tok;
+  bool cut_p, cut_q;
+};
+
+template <typename ET, int NT, int RES, bool QV, bool EVEN>
+__device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq, const float* rqp, const RaceRow& r,
+                                              uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un) {
   constexpr int EPV = Elem<ET>::kPerVec;
-  const int b = blockIdx.x / S, s = blockIdx.x - b * S;
-  const RaceDesc d = desc[b];
-  const int n = d.n;
-  if (n < 0) return;
-  const float c = d.c;
-  const ET* rp = lt + d.prow;
-  const ET* rq = (!QP && d.resid) ? ld + d.qrow : nullptr;
-  const float* rqp = (QP && d.resid) ? qp + d.qrow : nullptr;
-  const int a = s * seg;
-  const int e = min(V, a + seg);
   const int tid = threadIdx.x;
-  const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)n;
   float best = -1.f;
   int best_y = -1;
+  // Nucleus cuts as float compares: key(l, y) >= kappa iff l > value(kappa),
+  // or l equals it and y <= index(kappa); kappa = 0 keeps every token.
   auto weight = [&](float lp, float lq, int y) -> float {
-    float p = __builtin_amdgcn_exp2f((lp - d.mp) * c) * d.inv_zp;
-    if (CUT && make_key(lp, (uint32_t)y) < d.kp) p = 0.f;
-    if (d.resid) {
-      float q = lq;  // QP: the given probability
-      if (!QP) {
-        q = __builtin_amdgcn_exp2f((lq - d.mq) * c) * d.inv_zq;
-        if (CUT && make_key(lq, (uint32_t)y) < d.kq) q = 0.f;
-      }
-      return fmaxf(p - q, 0.f);
+    float p = __builtin_amdgcn_exp2f((lp - r.mp) * r.c) * r.inv_zp;
+    if (r.cut_p && !(lp > r.kvp || (lp == r.kvp && y <= r.kip))) p = 0.f;
+    if (RES == 0) return y == r.mask_tok ? 0.f : p;
+    float q = lq;  // RES 2: the given probability
+    if (RES == 1) {
+      q = __builtin_amdgcn_exp2f((lq - r.mq) * r.c) * r.inv_zq;
+      if (r.cut_q && !(lq > r.kvq || (lq == r.kvq && y <= r.kiq))) q = 0.f;
     }
-    return y == d.mask_tok ? 0.f : p;
+    return fmaxf(p - q, 0.f);
   };
-  auto consider = [&](float w, float E, int y) {
-    if (w > 0.f) {
-      const float sc = w * __builtin_amdgcn_rcpf(E);  // E = 0 gives +inf
+  // A score equal to the thread's best loses (ties go to the lowest index,
+  // and a thread visits its tokens in ascending order).  A token that cannot
+  // reach the wave's best score (w <= bar t, bar the largest best of any lane
+  // at the last exchange) cannot win the row, so it skips the logarithm; a
+  // bar shared by the wave keeps whole waves on the short path.
+  float bar = -1.f;
+  auto consider = [&](float w, uint32_t lo, uint32_t hi, int y) {
+    if (w > 0.f && !(w <= fmaxf(best, bar) * unit_gap_from_words(lo, hi) * kRaceSkip)) {
+      const float sc = w * __builtin_amdgcn_rcpf(exp1_from_words(lo, hi));  // E = 0 gives +inf
       if (sc > best) {
         best = sc;
         best_y = y;
       }
     }
   };
-  Slice<ET> sl(rp, a, e);
-  // The draft row is read with 16-byte vectors only if it shares the target
-  // row's alignment (rows start at different offsets when V * size is not a
-  // multiple of 16); otherwise element by element.
-  const bool q_vec = rq && ((((uintptr_t)(rp + a)) ^ ((uintptr_t)(rq + a))) & 15u) == 0u;
   const uint4* vp = sl.vecs();
-  const uint4* vq = q_vec ? (const uint4*)(rq + a + sl.head) : nullptr;
-  // Vectors start on even tokens when the slice's first vector does: then
-  // tokens 2m and 2m+1 share one Philox block.
-  const bool even0 = ((a + sl.head) & 1) == 0;
+  const uint4* vq = QV ? (const uint4*)(rq + sl.a + sl.head) : nullptr;
   auto race_vec = [&](const uint4& pv, const uint4& qv, int i) {
     float fp[EPV], fq[EPV];
     Elem<ET>::unpack(pv, fp);
     const int y0 = sl.vec_index0(i);
-    if (QP) {
+    if (RES == 2) {
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) fq[k] = rqp ? rqp[y0 + k] : 0.f;
-    } else if (q_vec) {
+      for (int k = 0; k < EPV; ++k) fq[k] = rqp[y0 + k];
+    } else if (RES == 1 && QV) {
       Elem<ET>::unpack(qv, fq);
+    } else if (RES == 1) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) fq[k] = Elem<ET>::load1(rq + y0 + k);
     } else {
 #pragma unroll
-      for (int k = 0; k < EPV; ++k) fq[k] = rq ? Elem<ET>::load1(rq + y0 + k) : 0.f;
+      for (int k = 0; k < EPV; ++k) fq[k] = 0.f;
     }
-    if (even0) {
+    if (EVEN) {
+      // The vector's EPV / 2 race blocks (counter (y >> 1, n, b, 1)) at once.
+      uint4 rr[EPV / 2];
+#pragma unroll
+      for (int m = 0; m < EPV / 2; ++m) rr[m] = make_uint4((uint32_t)(y0 >> 1) + (uint32_t)m, un, ub, 1u);
+      philox10_multi<EPV / 2>(rr, k0, k1);
 #pragma unroll
       for (int m = 0; m < EPV / 2; ++m) {
         const int y = y0 + 2 * m;
-        const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
-        consider(weight(fp[2 * m], fq[2 * m], y), exp1_from_words(r.x, r.y), y);
-        consider(weight(fp[2 * m + 1], fq[2 * m + 1], y + 1), exp1_from_words(r.z, r.w), y + 1);
+        consider(weight(fp[2 * m], fq[2 * m], y), rr[m].x, rr[m].y, y);
+        consider(weight(fp[2 * m + 1], fq[2 * m + 1], y + 1), rr[m].z, rr[m].w, y + 1);
       }
     } else {
 #pragma unroll
       for (int k = 0; k < EPV; ++k) {
         const int y = y0 + k;
-        const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
-        consider(weight(fp[k], fq[k], y), (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y), y);
+        const uint4 rr = race_block(k0, k1, ub, un, (uint32_t)y);
+        if (y & 1) consider(weight(fp[k], fq[k], y), rr.z, rr.w, y);
+        else consider(weight(fp[k], fq[k], y), rr.x, rr.y, y);
       }
     }
   };
   const uint4 zero4 = make_uint4(0u, 0u, 0u, 0u);
-  // Two vectors per iteration: more independent Philox chains in flight.
-  int i = tid;
-  for (; i + NT < sl.nvec; i += 2 * NT) {
-    const uint4 p0 = load_stream(vp + i), p1 = load_stream(vp + i + NT);
-    const uint4 q0 = q_vec ? load_stream(vq + i) : zero4;
-    const uint4 q1 = q_vec ? load_stream(vq + i + NT) : zero4;
-    race_vec(p0, q0, i);
-    race_vec(p1, q1, i + NT);
+  // Two vectors per iteration (more independent Philox chains in flight);
+  // the trip count is the same for every lane, so the whole wave takes part
+  // in the exchange of the bar.
+  for (int base = 0; base < sl.nvec; base += 2 * NT) {
+    const int i0 = base + tid, i1 = i0 + NT;
+    const bool h0 = i0 < sl.nvec, h1 = i1 < sl.nvec;
+    const uint4 p0 = h0 ? load_stream(vp + i0) : zero4, p1 = h1 ? load_stream(vp + i1) : zero4;
+    const uint4 q0 = (QV && h0) ? load_stream(vq + i0) : zero4;
+    const uint4 q1 = (QV && h1) ? load_stream(vq + i1) : zero4;
+    if (h0) race_vec(p0, q0, i0);
+    if (h1) race_vec(p1, q1, i1);
+    bar = wave_max_f(best);
   }
-  if (i < sl.nvec) race_vec(load_stream(vp + i), q_vec ? load_stream(vq + i) : zero4, i);
   uint64_t key = best_y >= 0 ? make_key(best, (uint32_t)best_y) : 0ull;
   // Scalar head and tail: keyed directly, so index order does not matter.
   if (tid < sl.nscalar()) {
     const int y = sl.scalar_index(tid);
-    const uint4 r = race_block(k0, k1, ub, un, (uint32_t)y);
-    const float w = weight(Elem<ET>::load1(rp + y), QP ? (rqp ? rqp[y] : 0.f) : (rq ? Elem<ET>::load1(rq + y) : 0.f), y);
+    const uint4 rr = race_block(k0, k1, ub, un, (uint32_t)y);
+    const float lq = RES == 2 ? rqp[y] : (RES == 1 ? Elem<ET>::load1(rq + y) : 0.f);
+    const float w = weight(Elem<ET>::load1(sl.row + y), lq, y);
     if (w > 0.f) {
-      const float E = (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
+      const float E = (y & 1) ? exp1_from_words(rr.z, rr.w) : exp1_from_words(rr.x, rr.y);
       const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), (uint32_t)y);
       key = kk > key ? kk : key;
     }
+  }
+  return key;
+}
+
+template <typename ET, int NT, bool CUT, bool QP>
+__global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                       const float* __restrict__ qp, int V, int S, int seg,
+                                                       uint32_t k0, uint32_t k1, const RaceDesc* __restrict__ desc,
+                                                       unsigned long long* __restrict__ slots) {
+  const int b = blockIdx.x / S, s = blockIdx.x - b * S;
+  const RaceDesc d = desc[b];
+  const int n = d.n;
+  if (n < 0) return;
+  const ET* rp = lt + d.prow;
+  const ET* rq = (!QP && d.resid) ? ld + d.qrow : nullptr;
+  const float* rqp = (QP && d.resid) ? qp + d.qrow : nullptr;
+  const int a = s * seg;
+  const int e = min(V, a + seg);
+  const int tid = threadIdx.x;
+  RaceRow r;
+  r.mp = d.mp;
+  r.inv_zp = d.inv_zp;
+  r.mq = d.mq;
+  r.inv_zq = d.inv_zq;
+  r.c = d.c;
+  r.mask_tok = d.mask_tok;
+  r.cut_p = CUT && d.kp != 0ull;
+  r.cut_q = CUT && d.kq != 0ull;
+  r.kvp = r.cut_p ? key_value(d.kp) : 0.f;
+  r.kvq = r.cut_q ? key_value(d.kq) : 0.f;
+  r.kip = r.cut_p ? (int)key_index(d.kp) : 0;
+  r.kiq = r.cut_q ? (int)key_index(d.kq) : 0;
+  const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)n;
+  Slice<ET> sl(rp, a, e);
+  // The draft row is read with 16-byte vectors only if it shares the target
+  // row's alignment (rows start at different offsets when V * size is not a
+  // multiple of 16); otherwise element by element.
+  const bool q_vec = rq && ((((uintptr_t)(rp + a)) ^ ((uintptr_t)(rq + a))) & 15u) == 0u;
+  const bool even = ((a + sl.head) & 1) == 0;
+  uint64_t key;
+  if (!d.resid) {
+    key = even ? race_scan<ET, NT, 0, false, true>(sl, rq, rqp, r, k0, k1, ub, un)
+               : race_scan<ET, NT, 0, false, false>(sl, rq, rqp, r, k0, k1, ub, un);
+  } else if (QP) {
+    key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, k0, k1, ub, un)
+               : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, k0, k1, ub, un);
+  } else if (q_vec) {
+    key = even ? race_scan<ET, NT, 1, true, true>(sl, rq, rqp, r, k0, k1, ub, un)
+               : race_scan<ET, NT, 1, true, false>(sl, rq, rqp, r, k0, k1, ub, un);
+  } else {
+    key = even ? race_scan<ET, NT, 1, false, true>(sl, rq, rqp, r, k0, k1, ub, un)
+               : race_scan<ET, NT, 1, false, false>(sl, rq, rqp, r, k0, k1, ub, un);
   }
   key = wave_max_u64(key);
   __shared__ uint64_t red[NT / kWave];
