@@ -1119,44 +1119,53 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
 // the draft row shares the target row's 16-byte alignment and is read in
 // vectors), 2 (q given as fp32 probabilities); EVEN: vectors start on even
 // tokens, so tokens 2m and 2m + 1 share one Philox block.
+//
+// Weights are kept in the row's own units, w / inv_zp (the exponentials
+// exp2((l - m) c) of the target row, the draft's scaled by inv_zq / inv_zp):
+// one factor for every token of the row, so the race's winner is unchanged.
 struct RaceRow {
-  float mp, inv_zp, mq, inv_zq, c, kvp, kvq;
+  float mpc, mqc, ratio, c, kvp, kvq;  // mpc = m_p c, mqc = m_q c, ratio = inv_zq / inv_zp
   int kip, kiq, mask_tok;
   bool cut_p, cut_q;
 };
 
 template <typename ET, int NT, int RES, bool QV, bool EVEN>
 __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq, const float* rqp, const RaceRow& r,
-                                              uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un) {
+                                              float inv_zp, uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int tid = threadIdx.x;
-  float best = -1.f;
+  float best = 0.f;  // scores are positive; best_y < 0 until a token scores
   int best_y = -1;
   // Nucleus cuts as float compares: key(l, y) >= kappa iff l > value(kappa),
   // or l equals it and y <= index(kappa); kappa = 0 keeps every token.
   auto weight = [&](float lp, float lq, int y) -> float {
-    float p = __builtin_amdgcn_exp2f((lp - r.mp) * r.c) * r.inv_zp;
+    float p = __builtin_amdgcn_exp2f(fmaf(lp, r.c, -r.mpc));
     if (r.cut_p && !(lp > r.kvp || (lp == r.kvp && y <= r.kip))) p = 0.f;
-    if (RES == 0) return y == r.mask_tok ? 0.f : p;
-    float q = lq;  // RES 2: the given probability
+    if (RES == 0) return p;  // the one-hot draft token is masked per vector
+    float q;
     if (RES == 1) {
-      q = __builtin_amdgcn_exp2f((lq - r.mq) * r.c) * r.inv_zq;
+      q = __builtin_amdgcn_exp2f(fmaf(lq, r.c, -r.mqc));
       if (r.cut_q && !(lq > r.kvq || (lq == r.kvq && y <= r.kiq))) q = 0.f;
+      return fmaxf(fmaf(-q, r.ratio, p), 0.f);
     }
-    return fmaxf(p - q, 0.f);
+    return fmaxf(fmaf(-lq, 1.f / inv_zp, p), 0.f);  // RES 2: q given as a probability
   };
   // A score equal to the thread's best loses (ties go to the lowest index,
-  // and a thread visits its tokens in ascending order).  A token that cannot
-  // reach the wave's best score (w <= bar t, bar the largest best of any lane
-  // at the last exchange) cannot win the row, so it skips the logarithm; a
-  // bar shared by the wave keeps whole waves on the short path.
-  float bar = -1.f;
+  // and a thread visits its tokens in ascending order).  A token cannot win
+  // the row if w <= S t, with t = 1 - u (the race variate E = -ln(1 - t) >=
+  // t) and S the largest best score of any lane at the last exchange: such
+  // tokens skip the logarithm.  The test uses t's lower bound ~hi 2^-32
+  // (hi: the high Philox word) and folds 2^-32 and the rounding margin into
+  // `bar`; a bar shared by the wave keeps whole waves on the short path.
+  constexpr float kBarScale = kRaceSkip * 0x1.0p-32f;
+  float bar = 0.f;
   auto consider = [&](float w, uint32_t lo, uint32_t hi, int y) {
-    if (w > 0.f && !(w <= fmaxf(best, bar) * unit_gap_from_words(lo, hi) * kRaceSkip)) {
+    if (!(w <= bar * (float)(~hi))) {
       const float sc = w * __builtin_amdgcn_rcpf(exp1_from_words(lo, hi));  // E = 0 gives +inf
       if (sc > best) {
         best = sc;
         best_y = y;
+        bar = fmaxf(bar, sc * kBarScale);
       }
     }
   };
@@ -1166,6 +1175,11 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
     float fp[EPV], fq[EPV];
     Elem<ET>::unpack(pv, fp);
     const int y0 = sl.vec_index0(i);
+    if (RES == 0 && (uint32_t)(r.mask_tok - y0) < (uint32_t)EPV) {
+#pragma unroll
+      for (int k = 0; k < EPV; ++k)
+        if (k == r.mask_tok - y0) fp[k] = -INFINITY;
+    }
     if (RES == 2) {
 #pragma unroll
       for (int k = 0; k < EPV; ++k) fq[k] = rqp[y0 + k];
@@ -1212,7 +1226,7 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
     const uint4 q1 = (QV && h1) ? load_stream(vq + i1) : zero4;
     if (h0) race_vec(p0, q0, i0);
     if (h1) race_vec(p1, q1, i1);
-    bar = wave_max_f(best);
+    bar = wave_max_f(bar);
   }
   uint64_t key = best_y >= 0 ? make_key(best, (uint32_t)best_y) : 0ull;
   // Scalar head and tail: keyed directly, so index order does not matter.
@@ -1220,7 +1234,8 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
     const int y = sl.scalar_index(tid);
     const uint4 rr = race_block(k0, k1, ub, un, (uint32_t)y);
     const float lq = RES == 2 ? rqp[y] : (RES == 1 ? Elem<ET>::load1(rq + y) : 0.f);
-    const float w = weight(Elem<ET>::load1(sl.row + y), lq, y);
+    float w = weight(Elem<ET>::load1(sl.row + y), lq, y);
+    if (RES == 0 && y == r.mask_tok) w = 0.f;
     if (w > 0.f) {
       const float E = (y & 1) ? exp1_from_words(rr.z, rr.w) : exp1_from_words(rr.x, rr.y);
       const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), (uint32_t)y);
@@ -1246,11 +1261,10 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   const int e = min(V, a + seg);
   const int tid = threadIdx.x;
   RaceRow r;
-  r.mp = d.mp;
-  r.inv_zp = d.inv_zp;
-  r.mq = d.mq;
-  r.inv_zq = d.inv_zq;
   r.c = d.c;
+  r.mpc = d.mp * d.c;
+  r.mqc = d.mq * d.c;
+  r.ratio = d.inv_zq / d.inv_zp;
   r.mask_tok = d.mask_tok;
   r.cut_p = CUT && d.kp != 0ull;
   r.cut_q = CUT && d.kq != 0ull;
@@ -1267,17 +1281,17 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   const bool even = ((a + sl.head) & 1) == 0;
   uint64_t key;
   if (!d.resid) {
-    key = even ? race_scan<ET, NT, 0, false, true>(sl, rq, rqp, r, k0, k1, ub, un)
-               : race_scan<ET, NT, 0, false, false>(sl, rq, rqp, r, k0, k1, ub, un);
+    key = even ? race_scan<ET, NT, 0, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
+               : race_scan<ET, NT, 0, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   } else if (QP) {
-    key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, k0, k1, ub, un)
-               : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, k0, k1, ub, un);
+    key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
+               : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   } else if (q_vec) {
-    key = even ? race_scan<ET, NT, 1, true, true>(sl, rq, rqp, r, k0, k1, ub, un)
-               : race_scan<ET, NT, 1, true, false>(sl, rq, rqp, r, k0, k1, ub, un);
+    key = even ? race_scan<ET, NT, 1, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
+               : race_scan<ET, NT, 1, true, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   } else {
-    key = even ? race_scan<ET, NT, 1, false, true>(sl, rq, rqp, r, k0, k1, ub, un)
-               : race_scan<ET, NT, 1, false, false>(sl, rq, rqp, r, k0, k1, ub, un);
+    key = even ? race_scan<ET, NT, 1, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
+               : race_scan<ET, NT, 1, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   }
   key = wave_max_u64(key);
   __shared__ uint64_t red[NT / kWave];
