@@ -563,6 +563,46 @@ __device__ __forceinline__ int topk_append(const float* f, uint32_t idx0, uint32
   return cnt;
 }
 
+// The same for a few lanes: each lane L of `lanes` (a wave-uniform mask) in
+// turn broadcasts its 16-byte vector, and lanes 0 .. EPV-1 take its elements
+// (element j: word j / 2, low half first, for bf16; word j for fp32).  About
+// a third of the per-element walk when one or two lanes hold candidates.
+// yb: token index of element 0 of lane 0's vector.
+template <typename ET>
+__device__ __forceinline__ int topk_append_lanes(const uint4& vv, uint64_t lanes, int yb, uint64_t tau, float tau_v,
+                                                 uint64_t* bw, int cnt) {
+  constexpr int EPV = Elem<ET>::kPerVec;
+  const int lane = lane_id();
+  while (lanes) {
+    const int L = __builtin_ctzll(lanes);
+    lanes &= lanes - 1ull;
+    const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)vv.x, L);
+    const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)vv.y, L);
+    const uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)vv.z, L);
+    const uint32_t w3 = (uint32_t)__builtin_amdgcn_readlane((int)vv.w, L);
+    uint32_t bits;
+    if (EPV == 8) {
+      const int q = lane >> 1;
+      const uint32_t wd = q == 0 ? w0 : (q == 1 ? w1 : (q == 2 ? w2 : w3));
+      bits = (lane & 1) ? (wd & 0xFFFF0000u) : (wd << 16);
+    } else {
+      bits = lane == 0 ? w0 : (lane == 1 ? w1 : (lane == 2 ? w2 : w3));
+    }
+    const float f = __uint_as_float(bits);
+    const bool cand = lane < EPV && f >= tau_v;
+    const uint64_t key = cand ? make_key(f, (uint32_t)(yb + L * EPV + lane)) : 0ull;
+    const bool hit = key > tau;
+    const uint64_t m = ballot(hit);
+    if (hit) bw[cnt + lanes_below(m)] = key;
+    cnt += __builtin_popcountll(m);
+  }
+  return cnt;
+}
+
+#ifndef SV_TOPK_LANE_APPEND
+#define SV_TOPK_LANE_APPEND 2  // at most this many candidate lanes: the per-lane walk
+#endif
+
 // Prefilter for bf16 vectors against a positive threshold: for positive
 // values the bf16 bit pattern orders like a signed 16-bit integer, and every
 // negative pattern is below every positive one.
@@ -663,14 +703,20 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
       for (int k = 1; k < EPV; ++k) vm = fmaxf(vm, f[k]);
       maybe = valid && vm >= tau_v;
     }
-    if (ballot(maybe) == 0ull) return;
+    const uint64_t mm = ballot(maybe);
+    if (mm == 0ull) return;
     if (cnt > kGuard) {
       if (lane_id() == 0) *cntp = (uint32_t)cnt;
       tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
       tau_v = tau_value(tau);
       cnt = (int)__builtin_amdgcn_readfirstlane(*cntp);
     }
-    cnt = topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cnt);
+    if (__builtin_popcountll(mm) <= SV_TOPK_LANE_APPEND) {
+      // Lanes outside mm hold no element >= tau_v (maybe covers validity).
+      cnt = topk_append_lanes<ET>(vv, mm, sl.vec_index0(i - lane_id()), tau, tau_v, bw, cnt);
+    } else {
+      cnt = topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cnt);
+    }
     if (cnt > trig) {
       if (lane_id() == 0) *cntp = (uint32_t)cnt;
       tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
@@ -796,8 +842,33 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
       const uint64_t thr = wave_select_kth(b0, n, K, hw);
       n = wave_keep_ge(b0, n, thr);
     }
+    // The kept set is exact, but the order in which its keys were appended
+    // depends on when each wave saw which bound; the row's candidates are
+    // written in descending key order so that every later sum over them runs
+    // in the same order on every call.
     uint64_t* dst = cand + (size_t)row * kstride;
-    for (int i = lane_id(); i < K; i += kWave) dst[i] = i < n ? b0[i] : 0ull;
+    if (K <= kWave) {
+      const int lane = lane_id();
+      uint64_t v = lane < n ? b0[lane] : 0ull;
+      // Bitonic sort across the wave's lanes (one key each), descending.
+#pragma unroll
+      for (int size = 2; size <= kWave; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+          const uint64_t o = shfl_xor_u64(v, stride);
+          const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+          v = keep_max ? (o > v ? o : v) : (o < v ? o : v);
+        }
+      }
+      if (lane < K) dst[lane] = v;
+    } else {
+      int n2 = kWave;
+      while (n2 < n) n2 <<= 1;
+      for (int i = n + lane_id(); i < n2; i += kWave) b0[i] = 0ull;
+      wave_lds_sync();
+      wave_sort_desc(b0, n2);
+      for (int i = lane_id(); i < K; i += kWave) dst[i] = i < n ? b0[i] : 0ull;
+    }
   }
 }
 
