@@ -295,6 +295,23 @@ sv_status run_block_race(const Plan& pl, const void* lt, uint32_t k0, uint32_t k
   return check_launch();
 }
 
+// Accept pass over top-k candidates: the staged small kernel when every
+// request keeps at most 64 tokens and has at most 16 positions, else the
+// general one.  K: the call's top-k, or its largest (the candidate stride).
+template <int MODE>
+void launch_accept_topk(const Plan& pl, const uint64_t* cand, const int32_t* X, int K, float c, uint32_t k0,
+                        uint32_t k1, int32_t* out, int32_t* nacc, float* p_draft, float* q_draft, int* err,
+                        const ReqInfo* info, const float* qp, sv::Stats stats, hipStream_t st) {
+  if (pl.kcap <= sv::kSmallK && pl.G <= sv::kSmallG) {
+    hipLaunchKernelGGL((sv::accept_topk_small_kernel<MODE>), dim3(pl.B), dim3(512), 0, st, cand, X, pl.G, pl.V, K,
+                       pl.rows_t, c, k0, k1, out, nacc, p_draft, q_draft, err, info, pl.kcap, pl.L, qp, stats);
+  } else {
+    hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st, cand, X, pl.G,
+                       pl.V, K, pl.rows_t, c, k0, k1, out, nacc, p_draft, q_draft, err, info, pl.kcap, pl.L, qp,
+                       stats);
+  }
+}
+
 template <typename ET, int MODE>
 sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const void* ld, const int32_t* X,
                          int32_t* out, int32_t* nacc, float* p_draft, float* q_draft, char* ws, hipStream_t st) {
@@ -306,10 +323,9 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     s = run_rows_topk<ET>(pl, lt, ld, nrows, ws, st);
     if (s != SV_OK) return s;
     TimedLaunch t(1, st);
-    hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
-                       (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, pl.c, k0, k1, out,
-                       nacc, p_draft, q_draft, err, (const ReqInfo*)nullptr, pl.kcap, pl.L,
-                       (const float*)nullptr, sv::Stats{nullptr, nullptr});
+    launch_accept_topk<MODE>(pl, (const uint64_t*)(ws + pl.off_cand), X, pl.kcap, pl.c, k0, k1, out, nacc, p_draft,
+                             q_draft, err, (const ReqInfo*)nullptr, (const float*)nullptr,
+                             sv::Stats{nullptr, nullptr}, st);
     t.done();
     return check_launch();
   }
@@ -443,9 +459,8 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     TimedLaunch t(1, st);
     const sv::Stats stats{beta, counters};
     if (pl.K > 0)
-      hipLaunchKernelGGL((sv::accept_topk_kernel<MODE>), dim3(pl.B), dim3(256), (size_t)pl.G, st,
-                         (const uint64_t*)(ws + pl.off_cand), X, pl.G, pl.V, pl.kcap, pl.rows_t, 0.f, k0, k1, out,
-                         nacc, p_draft, q_draft, err, (const ReqInfo*)info, pl.kcap, pl.L, qp, stats);
+      launch_accept_topk<MODE>(pl, (const uint64_t*)(ws + pl.off_cand), X, pl.kcap, 0.f, k0, k1, out, nacc,
+                               p_draft, q_draft, err, (const ReqInfo*)info, qp, stats, st);
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const ET*)ldl, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0,
                        k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,

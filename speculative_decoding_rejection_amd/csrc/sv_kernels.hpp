@@ -1038,6 +1038,136 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
   }
 }
 
+// The same for K <= 64 and gamma <= 16 (every top-k call of the measured
+// shapes): one 512-thread workgroup per request stages all of its candidate
+// rows in LDS with one coalesced load (lane i of a row's wave holds key i),
+// then each of the eight waves takes a position; wave 0 races over row n.
+// The arithmetic is that of accept_topk_kernel key for key (the same
+// reductions over the same lanes), so both kernels give the same bits.
+constexpr int kSmallK = 64, kSmallG = 16;
+
+template <int MODE>
+__global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* __restrict__ cand,
+                                                                const int32_t* __restrict__ X, int G, int V, int K,
+                                                                int rows_t, float c, uint32_t k0, uint32_t k1,
+                                                                int32_t* __restrict__ out, int32_t* __restrict__ nacc,
+                                                                float* __restrict__ p_draft,
+                                                                float* __restrict__ q_draft, int* __restrict__ err,
+                                                                const ReqInfo* __restrict__ info, int kstride,
+                                                                Layout L, const float* __restrict__ qp,
+                                                                Stats stats) {
+  __shared__ uint64_t keys[2 * kSmallG + 1][kSmallK];
+  __shared__ uint8_t rejected[kSmallG];
+  const int b = blockIdx.x;
+  if (info) {
+    const ReqInfo ri = info[b];
+    if (ri.kind != kReqTopk) return;  // uniform over the workgroup
+    K = ri.K;
+    c = ri.c;
+  }
+  const int g = L.len(b, G);
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  constexpr int NW = 8;
+  const int nt = g + 1, nrow = nt + (MODE == 0 ? g : 0);
+  const uint64_t* ct = cand + (size_t)b * (G + 1) * kstride;
+  const uint64_t* cd = cand + ((size_t)rows_t + (size_t)b * G) * kstride;
+  for (int e = threadIdx.x; e < nrow * kSmallK; e += NW * kWave) {
+    const int r = e / kSmallK, i = e - r * kSmallK;
+    const uint64_t* src = r < nt ? ct + (size_t)r * kstride : cd + (size_t)(r - nt) * kstride;
+    keys[r][i] = i < K ? src[i] : 0ull;
+  }
+  __syncthreads();
+  // Softmax over a kept set held one key per lane: (m, 1 / z) as cand_stats.
+  auto stats_of = [&](uint64_t k) -> CandStats {
+    const float m = wave_max_f(k ? key_value(k) : -INFINITY);
+    const float z = wave_sum_f(k ? __builtin_amdgcn_exp2f((key_value(k) - m) * c) : 0.f);
+    return CandStats{m, 1.f / z};
+  };
+  auto prob_of = [&](uint64_t k, CandStats st, int x) -> float {
+    return wave_sum_f((k && (int)key_index(k) == x) ? __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z
+                                                   : 0.f);
+  };
+  for (int j = w; j < g; j += NW) {
+    const size_t xj = L.tok(b, G, j);
+    const int x = X[xj];
+    const bool valid = x >= 0 && x < V;
+    const uint64_t kp = keys[j][lane];
+    const float px = valid ? prob_of(kp, stats_of(kp), x) : 0.f;
+    float qx = valid ? 1.f : 0.f;
+    if (MODE == 0) {
+      const uint64_t kq = keys[nt + j][lane];
+      qx = valid ? prob_of(kq, stats_of(kq), x) : 0.f;
+    } else if (MODE == 2) {
+      qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
+    }
+    if (lane == 0) {
+      if (p_draft) p_draft[xj] = px;
+      if (q_draft) q_draft[xj] = qx;
+      if (MODE == 1 && stats.beta) stats.beta[xj] = px;  // one-hot q: beta = p(x)
+      if (!valid) atomicOr(err, kErrBadToken);
+      const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
+      const double u = unit_from_words(r.x, r.y);
+      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      rejected[j] = acc ? 0 : 1;
+    }
+  }
+  __syncthreads();
+  if (w != 0) return;
+  const int n = [&] {
+    const uint64_t m = ballot(lane < g && rejected[lane] != 0);
+    return m ? (int)__builtin_ctzll(m) : g;
+  }();
+  // Recovered (n < g) or bonus (n == g) token: the Exp(1) race over the kept
+  // tokens of target row n; the residual's q(y) is looked up among draft row
+  // n's keys by broadcasting them one lane at a time.
+  const uint64_t kp = keys[n][lane];
+  const CandStats sp = stats_of(kp);
+  const int xn = n < g ? X[L.tok(b, G, n)] : -1;
+  float q = 0.f;
+  if (MODE == 0 && n < g) {
+    const uint64_t kq = keys[nt + n][lane];
+    const CandStats sq = stats_of(kq);
+    const float myq = kq ? __builtin_amdgcn_exp2f((key_value(kq) - sq.m) * c) * sq.inv_z : 0.f;
+    const uint32_t myqi = kq ? key_index(kq) : 0xFFFFFFFFu;
+    const uint32_t y = key_index(kp);
+    for (int t = 0; t < K; ++t) {
+      const uint32_t yt = (uint32_t)__builtin_amdgcn_readlane((int)myqi, t);
+      const float qt = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(myq), t));
+      if (kp && yt == y) q = qt;
+    }
+  } else if (MODE == 2 && n < g && kp) {
+    q = qp[L.tok(b, G, n) * (size_t)L.ds + key_index(kp)];
+  }
+  uint64_t best_w = 0ull, best_p = 0ull;
+  if (kp) {
+    const uint32_t y = key_index(kp);
+    const float p = __builtin_amdgcn_exp2f((key_value(kp) - sp.m) * c) * sp.inv_z;
+    float wgt = p;
+    if (n < g) {
+      if (MODE == 0 || MODE == 2) wgt = fmaxf(p - q, 0.f);
+      else if ((int)y == xn) wgt = 0.f;
+    }
+    const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
+    const float E = (y & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
+    if (wgt > 0.f) best_w = make_key(wgt * __builtin_amdgcn_rcpf(E), y);
+    if (p > 0.f) best_p = make_key(p * __builtin_amdgcn_rcpf(E), y);
+  }
+  best_w = wave_max_u64(best_w);
+  best_p = wave_max_u64(best_p);
+  const uint64_t win = best_w ? best_w : best_p;  // zero residual mass: race on p
+  int32_t* o = out + (size_t)b * (G + 1);
+  for (int j = lane; j <= G; j += kWave) {
+    int32_t t = -1;
+    if (j < n) t = X[L.tok(b, G, j)];
+    else if (j == n) t = win ? (int32_t)key_index(win) : -1;
+    o[j] = t;
+  }
+  if (lane == 0) {
+    nacc[b] = n;
+    count_round(stats, b, g, n);
+  }
+}
+
 // ===========================================================================
 // Accept pass, full rows (no top-k): one wave per request.
 // ===========================================================================
