@@ -794,11 +794,14 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const uint64_t* __rest
 // 64 tokens: the pass is a plain re-read of each row.
 //
 // Stage one, (row, vocabulary split): splits start on multiples of 64
-// tokens, so a block never straddles two workgroups.  A group of 64 / EPV
-// lanes holds one block (one 16-byte vector per lane); the group's lanes sum
-// their masses with shuffles and its first lane scores the block.  The
-// row's workgroups merge (score, block) keys with a 64-bit atomic max.
+// tokens, so a block never straddles two workgroups.  The split is taken in
+// chunks of kBlockChunk blocks: a group of 64 / EPV lanes holds one block
+// (one 16-byte vector per lane) and sums its masses with shuffles into LDS;
+// then every thread scores whole blocks (one Philox block each), so the
+// random numbers are drawn with all lanes busy.  The row's workgroups merge
+// (score, block) keys with a 64-bit atomic max.
 constexpr int kRaceBlock = 64;
+constexpr int kBlockChunk = 1024;
 
 __device__ __forceinline__ uint4 block_race_words(uint32_t k0, uint32_t k1, uint32_t b, uint32_t j, uint32_t k) {
   return philox10(make_uint4(k >> 1, j, b, 2u), k0, k1);
@@ -812,6 +815,8 @@ __global__ __launch_bounds__(NT) void block_race_kernel(const ET* __restrict__ l
   constexpr int LPB = kRaceBlock / EPV;  // lanes per block
   constexpr int BPS = NT / LPB;           // blocks per workgroup step
   constexpr int U = 4;                    // steps in flight
+  __shared__ float wsh[kBlockChunk];
+  __shared__ uint64_t red[NT / kWave];
   const int row = blockIdx.x / S, s = blockIdx.x - row * S;
   const RaceDesc d = desc[row];
   if (d.n < 0) return;
@@ -828,42 +833,50 @@ __global__ __launch_bounds__(NT) void block_race_kernel(const ET* __restrict__ l
   const float kv = cut ? key_value(d.kp) : 0.f;
   const int ki = cut ? (int)key_index(d.kp) : 0;
   uint64_t best = 0ull;
-  for (int q0 = tid / LPB; q0 < nblk; q0 += U * BPS) {
-    float f[U][EPV];
+  for (int c0 = 0; c0 < nblk; c0 += kBlockChunk) {
+    const int cn = min(kBlockChunk, nblk - c0);
+    for (int q0 = tid / LPB; q0 < cn; q0 += U * BPS) {
+      float f[U][EPV];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + u * BPS;
-      const int y0 = (kb0 + q) * kRaceBlock + li * EPV;
-      if (q < nblk && vec_ok && y0 + EPV <= e) {
-        Elem<ET>::unpack(load_stream((const uint4*)(rp + y0)), f[u]);
-      } else {
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * BPS;
+        const int y0 = (kb0 + c0 + q) * kRaceBlock + li * EPV;
+        if (q < cn && vec_ok && y0 + EPV <= e) {
+          Elem<ET>::unpack(load_stream((const uint4*)(rp + y0)), f[u]);
+        } else {
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) f[u][k] = (q < nblk && y0 + k < e) ? Elem<ET>::load1(rp + y0 + k) : -INFINITY;
+          for (int k = 0; k < EPV; ++k) f[u][k] = (q < cn && y0 + k < e) ? Elem<ET>::load1(rp + y0 + k) : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + u * BPS;
+        const int y0 = (kb0 + c0 + q) * kRaceBlock + li * EPV;
+        float w = 0.f;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(f[u][k], d.c, -mpc));
+          w += (!cut || f[u][k] > kv || (f[u][k] == kv && y0 + k <= ki)) ? p : 0.f;
+        }
+#pragma unroll
+        for (int m = LPB / 2; m >= 1; m >>= 1) w += __shfl_xor(w, m);
+        if (li == 0 && q < cn) wsh[q] = w;
       }
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = q0 + u * BPS;
-      const int y0 = (kb0 + q) * kRaceBlock + li * EPV;
-      float w = 0.f;
-#pragma unroll
-      for (int k = 0; k < EPV; ++k) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(f[u][k], d.c, -mpc));
-        w += (!cut || f[u][k] > kv || (f[u][k] == kv && y0 + k <= ki)) ? p : 0.f;
-      }
-#pragma unroll
-      for (int m = LPB / 2; m >= 1; m >>= 1) w += __shfl_xor(w, m);
-      if (li == 0 && q < nblk && w > 0.f) {
-        const uint32_t kb = (uint32_t)(kb0 + q);
+    __syncthreads();
+    for (int q = tid; q < cn; q += NT) {
+      const float w = wsh[q];
+      if (w > 0.f) {
+        const uint32_t kb = (uint32_t)(kb0 + c0 + q);
         const uint4 r = block_race_words(k0, k1, ub, un, kb);
         const float E = (kb & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
         const uint64_t key = make_key(w * d.inv_zp * __builtin_amdgcn_rcpf(E), kb);
         best = key > best ? key : best;
       }
     }
+    __syncthreads();  // wsh is refilled by the next chunk
   }
   best = wave_max_u64(best);
-  __shared__ uint64_t red[NT / kWave];
   if (lane_id() == 0) red[tid / kWave] = best;
   __syncthreads();
   if (tid == 0) {
