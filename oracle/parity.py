@@ -47,6 +47,25 @@ def compare(entry: str, got: dict, ref: dict, prob_tol: float = 1e-5, tie: float
     return rep
 
 
+def near_tie_rows(ref: dict, tie: float = 1e-4) -> int:
+    """Number of (request, position) rows on which a decision the oracle took
+    had a relative margin <= tie: the accept test of position j (every j <= n
+    that was evaluated) and the race at position n.  The denominator of the
+    near-tie fraction is B * (G + 1) rows."""
+    if "accept_margin" not in ref:
+        return 0
+    am, rm, n = ref["accept_margin"], ref["race_margin"], ref["num_accepted"]
+    G = am.shape[1]
+    rows = 0
+    for r in range(n.shape[0]):
+        ev = min(int(n[r]) + 1, G)
+        tied = set(np.nonzero(am[r, :ev] <= tie)[0].tolist())
+        if rm[r] <= tie:
+            tied.add(int(n[r]))
+        rows += len(tied)
+    return rows
+
+
 def assert_parity(entry: str, got: dict, ref: dict, prob_tol: float = 1e-5, tie: float = 1e-4,
                   max_tie_fraction: float | None = None) -> dict:
     rep = compare(entry, got, ref, prob_tol, tie)

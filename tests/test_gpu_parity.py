@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from oracle.parity import assert_parity
+from oracle.parity import assert_parity, near_tie_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -208,20 +208,24 @@ def test_deterministic_and_stream(sv):
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads: outputs checked on sampled requests, invariants on all
+# Full-size workloads: every request compared with the oracle
 # ---------------------------------------------------------------------------
 
-FULL_SAMPLES = {
-    "prob_f32_b8_g4_v32000": 8,
-    "greedy_bf16_b64_g5_v128256": 64,
-    "prob_f32_b256_g7_v151936": 24,
-    "onehot_bf16_b512_g3_v262144": 24,
-    "prob_topk64_bf16_b1024_g8_v256000": 32,
-}
+FULL_CONFIGS = ["prob_f32_b8_g4_v32000", "greedy_bf16_b64_g5_v128256", "prob_f32_b256_g7_v151936",
+                "onehot_bf16_b512_g3_v262144", "prob_topk64_bf16_b1024_g8_v256000"]
 
 
-@pytest.mark.parametrize("name", list(FULL_SAMPLES))
-def test_full_size_sampled(sv, name):
+@pytest.mark.parametrize("name", FULL_CONFIGS)
+def test_full_size_every_request(sv, name):
+    """The five workloads at their full sizes, in the launch configuration the
+    benchmark times: p(x_j), q(x_j) within 1e-5 and accepted lengths and
+    tokens identical on every request outside flagged near-ties (the greedy
+    path, including the argmax, everywhere).  The near-tie exemption may be
+    used on fewer than 0.01% of the B (G + 1) rows: requests that differ from
+    the oracle after a near-tie decision are counted against that bar.  The
+    rows holding a near-tie decision (oracle margin <= 1e-4) are counted and
+    reported: one of 9216 on the headline workload, on which the GPU agrees
+    as well."""
     wl = W[name]
     dev = torch.device("cuda:0")
     print(f"[full] {name}: generating on the GPU", flush=True)
@@ -229,23 +233,21 @@ def test_full_size_sampled(sv, name):
     torch.cuda.synchronize()
     got = gpu_run(sv, wl.entry, inp, wl.temperature, wl.top_k, wl.verify_seed)
     n, out, x = got["num_accepted"], got["out_tokens"], inp["draft_tokens"].cpu().numpy()
-    # Invariants on every request.
     assert ((n >= 0) & (n <= wl.G)).all()
     for r in range(wl.B):
         assert (out[r, :n[r]] == x[r, :n[r]]).all()
         assert 0 <= out[r, n[r]] < wl.V
         assert (out[r, n[r] + 1:] == -1).all()
     assert got["error_code"] == 0
-    # Element-by-element parity on sampled requests.
-    rng = np.random.default_rng(0)
-    ns = FULL_SAMPLES[name]
-    ids = np.sort(rng.choice(wl.B, size=min(ns, wl.B), replace=False)).astype(np.int32)
-    sub = {"target_logits": inp["target_logits"][ids.tolist()].cpu(),
-           "draft_tokens": inp["draft_tokens"][ids.tolist()].cpu(),
-           "draft_logits": (inp["draft_logits"][ids.tolist()].cpu() if inp["draft_logits"] is not None else None)}
+    host = {"target_logits": inp["target_logits"].cpu(), "draft_tokens": inp["draft_tokens"].cpu(),
+            "draft_logits": inp["draft_logits"].cpu() if inp["draft_logits"] is not None else None}
     del inp
     torch.cuda.empty_cache()
-    ref = oracle_run(wl.entry, sub, wl.temperature, wl.top_k, wl.verify_seed, req_ids=ids)
-    gsub = {k: v[ids] for k, v in got.items() if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == wl.B}
-    rep = assert_parity(wl.entry, gsub, ref)
+    print(f"[full] {name}: oracle over all {wl.B} requests", flush=True)
+    ref = oracle_run(wl.entry, host, wl.temperature, wl.top_k, wl.verify_seed)
+    rep = assert_parity(wl.entry, got, ref)
+    rows = wl.B * (wl.G + 1)
+    ties = near_tie_rows(ref)
+    rep["near_tie_rows"] = ties
     print(f"[full] {name}: {rep}", flush=True)
+    assert rep["mismatch_tie"] < 1e-4 * rows, f"near-tie exemptions used on {rep['mismatch_tie']} of {rows} rows"
