@@ -65,7 +65,7 @@ typedef enum {
   SV_ERR_DTYPE = 2,        /* dtype not SV_F32 / SV_BF16, or misaligned logits */
   SV_ERR_WORKSPACE = 3,    /* workspace null, misaligned or too small */
   SV_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
-  SV_ERR_UNSUPPORTED = 5   /* top_k in (1024, vocab) or gamma > 16384: not implemented */
+  SV_ERR_UNSUPPORTED = 5   /* gamma > 16384: not implemented */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -76,7 +76,10 @@ typedef struct {
   int32_t vocab;       /* V >= 1 */
   int32_t dtype;       /* sv_dtype of every logit array */
   float temperature;   /* T > 0 (finite) for prob/onehot; ignored by greedy */
-  int32_t top_k;       /* 0 or >= vocab: off; else keep k <= 1024 tokens */
+  int32_t top_k;       /* 0 or >= vocab: off; else keep exactly k tokens.  k <= 1024:
+                          kept as candidates in one read of each row; larger k:
+                          a cut at the k-th key of each full row (a radix select,
+                          two to six more reads of the rows of such requests) */
   uint64_t seed;       /* Philox key */
 } sv_params;
 
@@ -170,8 +173,10 @@ typedef struct {
  *                   in (logit desc, index asc) order, of the law left by
  *                   top-k whose probability reaches top_p (at least one
  *                   token); the law is renormalised over it.  NULL: all off.
- *   max_top_k       host-side bound, 0..1024: every top_k[b] below vocab is
- *                   at most this (it sizes the workspace and the kernels).
+ *   max_top_k       host-side bound, >= 0: every top_k[b] below vocab is at
+ *                   most this (it sizes the workspace and the kernels).  A
+ *                   top_k[b] up to min(max_top_k, 1024) is kept as candidates;
+ *                   a larger one is a cut at the k-th key of each full row.
  * A request whose settings break these rules (T negative, NaN or infinite;
  * top_k negative or in (max_top_k, vocab); top_p NaN, <= 0 or > 1) emits
  * nothing: out_tokens all -1, num_accepted 0, p_draft and q_draft 0; the
@@ -240,8 +245,8 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  *   outputs: see sv_outputs.
  * Sampler-match (layout->draft_kind SV_DRAFT_MATCH): every node gets a fresh
  * sample from its row's adjusted law (temperature 0: the argmax).  A top-k
- * law is drawn by the Exp(1) race over its kept tokens on the stream of
- * (request, node); a law over the whole vocabulary by two races: over the
+ * law keeping at most 1024 tokens is drawn by the Exp(1) race over its kept
+ * tokens on the stream of (request, node); any other law by two races: over the
  * blocks of 64 consecutive tokens weighted by their mass (block k's variate
  * from counter (k >> 1, node, request, 2), words 0/1 for even k, 2/3 for odd
  * k), then over the tokens of the winning block (the token streams of the

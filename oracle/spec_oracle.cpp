@@ -35,8 +35,9 @@
 //   * sampler-match ([P3] "mlxcel의 프롬프트 조회"): every node of the draft
 //     (a chain, or a tree given by parent indices) gets a fresh sample from
 //     its row's adjusted law, drawn by the Exp(1) race on the stream of
-//     (b, node) (a law over the whole vocabulary: first over blocks of 64
-//     tokens by their mass, then within the winning block; the same law);
+//     (b, node) (a law over the whole vocabulary or a top-k above 1024
+//     tokens: first over blocks of 64 tokens by their mass, then within the
+//     winning block; the same law);
 //     from the root, the walk follows the child whose token equals
 //     the sample (the lowest-indexed child if several do) and emits the
 //     sample where no child matches.
@@ -283,6 +284,8 @@ double uniform_block(uint64_t seed, uint32_t b, uint32_t j, uint32_t k) {
 // race, with one random number per block instead of one per token.
 // *margin: the smaller relative gap of the two stages.
 constexpr int kBlockRace = 64;
+// Largest top-k whose law sampler-match draws token by token.
+constexpr int kTokenRaceMaxK = 1024;
 int block_race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
   const double inf = std::numeric_limits<double>::infinity();
   const size_t V = w.size();
@@ -492,9 +495,10 @@ int verify_match(const Problem& P, uint32_t b, const char* Lt, const int32_t* X,
       double c = 1.0;
       p[i] = row_probs(row, P.dtype, V, P.T, P.top_k, P.top_p, &c);
       cm = std::min(cm, c);
-      // A top-k law (at most top_k tokens) is drawn by the one-stage race;
-      // a law over the whole vocabulary by the block race.
-      const bool topk = P.top_k > 0 && P.top_k < V;
+      // A top-k law keeping at most kTokenRaceMaxK tokens is drawn by the
+      // one-stage race over its tokens; any other law (the whole vocabulary,
+      // or a larger top-k) by the block race.  Both draw the law exactly.
+      const bool topk = P.top_k > 0 && P.top_k < V && P.top_k <= kTokenRaceMaxK;
       s[i] = topk ? race(p[i], P.seed, b, (uint32_t)i, &margin[i])
                   : block_race(p[i], P.seed, b, (uint32_t)i, &margin[i]);
     }

@@ -42,6 +42,7 @@ struct Plan {
   int Srr, segrr;                           // row-race splits (sampler-match)
   size_t off_rdesc, off_rslots, off_samples;  // per-row race descriptors, slots, samples
   sv::Layout L;   // rows, tokens, outputs (dense: rows V apart, every request G positions)
+  bool big_k;     // batch plans: a top-k above kcap is possible (full-row cut)
 };
 
 int splits_for(int rows, int V, int target_blocks, int min_seg) {
@@ -117,17 +118,19 @@ int batch_max_top_k(const sv_params* p, const sv_sampling* sm) {
 }
 
 // Plan of a batch call: the scalar plan's layout sized for the largest top-k
-// any request may use, plus per-request settings and per-row nucleus cuts.
+// kept as candidates (at most kMaxTopK: a larger top-k is a cut over the full
+// row), plus per-request settings and per-row cuts (top-p, large top-k).
 sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   if (!p) return SV_ERR_INVALID_ARG;
   if (sm && !sm->temperature) return SV_ERR_INVALID_ARG;
   if (!sm && !(std::isfinite(p->temperature) && p->temperature >= 0.f)) return SV_ERR_INVALID_ARG;
   const int mk = batch_max_top_k(p, sm);
   if (mk < 0 || p->top_k < 0) return SV_ERR_INVALID_ARG;
-  if (mk > kMaxTopK) return SV_ERR_UNSUPPORTED;
+  // Candidates per row; none when the call's one setting is a large top-k.
+  const int cap = (!sm && mk > kMaxTopK) ? 0 : (mk < kMaxTopK ? mk : kMaxTopK);
   sv_params q = *p;
   q.temperature = 1.f;
-  q.top_k = p->vocab > 1 ? (mk < p->vocab - 1 ? mk : p->vocab - 1) : 0;
+  q.top_k = p->vocab > 1 ? (cap < p->vocab - 1 ? cap : p->vocab - 1) : 0;
   sv_status s = make_plan(&q, kEntryProb, pl);
   if (s != SV_OK) return s;
   pl->c = 0.f;
@@ -150,7 +153,9 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   pl->off_info = off;
   off = align_up(off + (size_t)pl->B * sizeof(ReqInfo), kWsAlign);
   pl->off_cut = off;
-  if (sm && sm->top_p) off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
+  pl->big_k = mk > pl->kcap && pl->V > 1;  // some request may take a full-row top-k cut
+  if ((sm && sm->top_p) || pl->big_k)
+    off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
   // Sampler-match: one sample per target row; the block race splits rows
   // like the softmax pass (a quarter of the rows taken as its own).
   pl->Srr = splits_for((pl->rows_t + 3) / 4, pl->V, 2048, 8192);
@@ -397,14 +402,16 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
   ReqInfo* info = (ReqInfo*)(ws + pl.off_info);
   RowCut* cut = (RowCut*)(ws + pl.off_cut);
   uint64_t* part64 = (uint64_t*)(ws + pl.off_part);
-  const bool nuc = ba.P != nullptr;
+  const bool nuc = ba.P != nullptr;        // top-p settings given: nucleus passes
+  const bool use_cut = nuc || pl.big_k;    // full rows may carry a RowCut
   const float* qp = MODE == 2 ? (const float*)ld : nullptr;
   const void* ldl = MODE == 0 ? ld : nullptr;  // draft logits, if any
   sv_status s;
   {
     TimedLaunch t(0, st);
     hipLaunchKernelGGL(sv::classify_kernel, dim3(1), dim3(1024), 0, st, ba.T, ba.K, ba.P, ba.T0, ba.K0, pl.B, pl.G,
-                       pl.V, ba.max_top_k, pl.L, MODE == 3 ? ba.parents : (const int32_t*)nullptr, info, err, out,
+                       pl.V, ba.max_top_k, pl.kcap, pl.L, MODE == 3 ? ba.parents : (const int32_t*)nullptr, info,
+                       err, out,
                        nacc, p_draft, q_draft, beta);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
@@ -416,6 +423,10 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
                        dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part64, err,
                        (const ReqInfo*)info, pl.G, pl.L);
+    if (pl.big_k)  // top-k above the candidate capacity: the k-th key of the full row, before any nucleus
+      hipLaunchKernelGGL((sv::kcut_full_kernel<ET>), dim3(nrows), dim3(sv::kNucThreads), 0, st, (const ET*)lt,
+                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
+                         (const ReqInfo*)info, cut, pl.L);
     if (nuc && pl.K > 0)
       hipLaunchKernelGGL(sv::nucleus_topk_kernel, dim3((nrows + 3) / 4), dim3(256), 0, st,
                          (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info, pl.L);
@@ -432,7 +443,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       TimedLaunch t(1, st);
       hipLaunchKernelGGL(sv::match_prep_kernel, dim3((pl.rows_t + 255) / 256), dim3(256), 0, st,
                          (const float2*)(ws + pl.off_part), pl.S, pl.rows_t, pl.G, (const ReqInfo*)info,
-                         (const RowCut*)(nuc ? cut : nullptr), pl.L, (RaceDesc*)(ws + pl.off_rdesc),
+                         (const RowCut*)(use_cut ? cut : nullptr), pl.L, (RaceDesc*)(ws + pl.off_rdesc),
                          (unsigned long long*)(ws + pl.off_rslots));
       if (pl.K > 0)
         hipLaunchKernelGGL(sv::sample_topk_kernel, dim3((pl.rows_t + 3) / 4), dim3(256), 0, st,
@@ -441,13 +452,13 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       t.done();
       if ((s = check_launch()) != SV_OK) return s;
     }
-    s = nuc ? run_block_race<ET, true>(pl, lt, k0, k1, ws, st) : run_block_race<ET, false>(pl, lt, k0, k1, ws, st);
+    s = use_cut ? run_block_race<ET, true>(pl, lt, k0, k1, ws, st) : run_block_race<ET, false>(pl, lt, k0, k1, ws, st);
     if (s != SV_OK) return s;
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::match_walk_kernel<ET>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const float2*)(ws + pl.off_part), (const uint64_t*)part64,
                        (const uint64_t*)(ws + pl.off_cand), pl.kcap, pl.S, pl.G, pl.V, (const ReqInfo*)info,
-                       (const RowCut*)(nuc ? cut : nullptr), pl.L, X, ba.parents,
+                       (const RowCut*)(use_cut ? cut : nullptr), pl.L, X, ba.parents,
                        (const int32_t*)(ws + pl.off_samples), out, nacc, o.path_nodes, p_draft, q_draft,
                        sv::Stats{beta, counters}, err);
     t.done();
@@ -464,7 +475,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const ET*)ldl, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0,
                        k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
-                       (const RowCut*)(nuc ? cut : nullptr), pl.L, qp, stats);
+                       (const RowCut*)(use_cut ? cut : nullptr), pl.L, qp, stats);
     hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part64, X, pl.G,
                        pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft, q_draft, pl.L,
                        stats);
@@ -485,20 +496,26 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::beta_full_kernel<ET, MODE == 2>), dim3(pl.B * pl.G), dim3(256), 0, st, (const ET*)lt,
                        (const ET*)ldl, qp, (const float2*)(ws + pl.off_part), pl.G, pl.V, pl.S, pl.rows_t,
-                       (const ReqInfo*)info, (const RowCut*)(nuc ? cut : nullptr), pl.L, beta);
+                       (const ReqInfo*)info, (const RowCut*)(use_cut ? cut : nullptr), pl.L, beta);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
   constexpr bool QP = MODE == 2;
-  if (nuc) return run_race<ET, true, QP>(pl, lt, ld, k0, k1, desc, slots, out, st);
+  if (use_cut) return run_race<ET, true, QP>(pl, lt, ld, k0, k1, desc, slots, out, st);
   return run_race<ET, false, QP>(pl, lt, ld, k0, k1, desc, slots, out, st);
 }
+
+// A single-setting call whose top-k exceeds the candidate capacity (and is
+// below the vocabulary) runs as a batch call with that one setting: the
+// top-k is a cut over each full row.
+bool large_top_k(const sv_params* p) { return p && p->top_k > kMaxTopK && p->top_k < p->vocab; }
 
 }  // namespace
 
 extern "C" {
 
 size_t sv_workspace_bytes(const sv_params* params) {
+  if (large_top_k(params)) return sv_workspace_bytes_batch(params, nullptr);
   Plan pl;
   if (make_plan(params, kEntryProb, &pl) != SV_OK) {
     // Greedy parameters may carry any temperature.
@@ -514,7 +531,7 @@ const char* sv_status_string(sv_status s) {
     case SV_ERR_DTYPE: return "unsupported dtype or misaligned logits";
     case SV_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or smaller than sv_workspace_bytes()";
     case SV_ERR_HIP: return "HIP runtime or kernel launch failure";
-    case SV_ERR_UNSUPPORTED: return "top_k above 1024 (and below vocab) or gamma above 16384 is not supported";
+    case SV_ERR_UNSUPPORTED: return "gamma above 16384 is not supported";
   }
   return "unknown status";
 }
@@ -522,6 +539,13 @@ const char* sv_status_string(sv_status s) {
 sv_status spec_verify_prob(const sv_params* params, const void* target_logits, const void* draft_logits,
                            const int32_t* draft_tokens, int32_t* out_tokens, int32_t* num_accepted, float* p_draft,
                            float* q_draft, void* workspace, size_t workspace_bytes, void* stream) {
+  if (large_top_k(params)) {
+    if (!(params->temperature > 0.f && std::isfinite(params->temperature))) return SV_ERR_INVALID_ARG;
+    if (!draft_logits) return SV_ERR_INVALID_ARG;
+    const sv_outputs o{out_tokens, num_accepted, p_draft, q_draft, nullptr, nullptr, nullptr};
+    return spec_verify_batch(params, nullptr, nullptr, target_logits, draft_logits, draft_tokens, &o, workspace,
+                             workspace_bytes, stream);
+  }
   Plan pl;
   sv_status s = make_plan(params, kEntryProb, &pl);
   if (s != SV_OK) return s;
@@ -542,6 +566,12 @@ sv_status spec_verify_prob(const sv_params* params, const void* target_logits, c
 sv_status spec_verify_onehot(const sv_params* params, const void* target_logits, const int32_t* draft_tokens,
                              int32_t* out_tokens, int32_t* num_accepted, float* p_draft, void* workspace,
                              size_t workspace_bytes, void* stream) {
+  if (large_top_k(params)) {
+    if (!(params->temperature > 0.f && std::isfinite(params->temperature))) return SV_ERR_INVALID_ARG;
+    const sv_outputs o{out_tokens, num_accepted, p_draft, nullptr, nullptr, nullptr, nullptr};
+    return spec_verify_batch(params, nullptr, nullptr, target_logits, nullptr, draft_tokens, &o, workspace,
+                             workspace_bytes, stream);
+  }
   Plan pl;
   sv_status s = make_plan(params, kEntryOnehot, &pl);
   if (s != SV_OK) return s;

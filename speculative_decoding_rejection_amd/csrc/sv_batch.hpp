@@ -92,7 +92,7 @@ __device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, in
 // ===========================================================================
 __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict__ T, const int32_t* __restrict__ K,
                                                         const float* __restrict__ P, float T0, int K0, int B, int G,
-                                                        int V, int max_top_k, Layout L,
+                                                        int V, int max_top_k, int cand_cap, Layout L,
                                                         const int32_t* __restrict__ parents,
                                                         ReqInfo* __restrict__ info, int* __restrict__ err,
                                                         int32_t* __restrict__ out, int32_t* __restrict__ nacc,
@@ -133,17 +133,20 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
     r.K = 0;
     r.top_p = p;
     r.T = t;
-    r.pad[0] = r.pad[1] = r.pad[2] = 0;
+    r.cut = 0;
+    r.pad[0] = r.pad[1] = 0;
     if (ok) {
       if (t == 0.f) {
         r.kind = kReqGreedy;
       } else {
         r.c = (float)(1.4426950408889634 / (double)t);
-        if (k > 0 && k < V) {
-          r.kind = kReqTopk;
+        if (k > 0 && k < V && k <= cand_cap) {
+          r.kind = kReqTopk;  // exact top-k by candidates
           r.K = k;
         } else {
           r.kind = kReqFull;
+          if (k > 0 && k < V) r.K = k;  // a cut at the k-th key of the full row
+          r.cut = (p < 1.f || r.K > 0) ? 1 : 0;
         }
       }
     }
@@ -335,6 +338,10 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   if (ri.kind != kReqFull || !(ri.top_p < 1.f)) return;  // uniform over the workgroup
   const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
   if (!rp) return;  // past the request's draft length
+  // Under a large top-k the nucleus is taken over the top-k law: tokens below
+  // the k-cut (written by kcut_full_kernel) have no mass here.
+  const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
+  auto below = [&](float l, int y) { return kfloor != 0ull && make_key(l, (uint32_t)y) < kfloor; };
   // The gap histogram is dead once its bin is chosen; the collected keys of
   // that bin then take its storage.
   __shared__ double hm[kNucBins];
@@ -375,7 +382,8 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   // Pass 1: masses, Z and the mass histogram of the gap.  The gap is the
   // negated exponent, so mass and bin come from one product.
   double zt = 0.0;
-  row_foreach<ET, NT>(rp, V, [&](float l, int) {
+  row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+    if (below(l, y)) return;
     int k;
     const double e = exp_nonpos_f64(((double)l - lm) * it, tab, &k);
     zt += e;
@@ -422,7 +430,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   const int bstar = sh_bin;
   if (bstar < 0) {
     // No finite mass (degenerate row): no cut.
-    if (tid == 0) cut[row] = RowCut{0ull, lmax, (float)(1.0 / Z)};
+    if (tid == 0) cut[row] = RowCut{kfloor, lmax, (float)(1.0 / Z)};
     return;
   }
 
@@ -430,7 +438,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   // tells whether the bin needs refining).  filter_key: bin and key prefix.
   auto collect = [&](int plen, uint64_t prefix) {
     row_foreach<ET, NT>(rp, V, [&](float l, int y) {
-      if (nucleus_bin(lm, l, it) != bstar) return;
+      if (nucleus_bin(lm, l, it) != bstar || below(l, y)) return;
       const uint64_t k = make_key(l, (uint32_t)y);
       if (plen > 0 && (plen == 64 ? k != prefix : (k >> (64 - plen)) != (prefix >> (64 - plen)))) return;
       const int pos = atomicAdd(&sh_n, 1);
@@ -446,7 +454,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
     if (tid == 0) sh_cnt = (uint32_t)sh_n;
     uint64_t kmin = ~0ull, kmax = 0ull;
     row_foreach<ET, NT>(rp, V, [&](float l, int y) {
-      if (nucleus_bin(lm, l, it) == bstar) {
+      if (nucleus_bin(lm, l, it) == bstar && !below(l, y)) {
         const uint64_t k = make_key(l, (uint32_t)y);
         kmin = k < kmin ? k : kmin;
         kmax = k > kmax ? k : kmax;
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
       }
       __syncthreads();
       row_foreach<ET, NT>(rp, V, [&](float l, int y) {
-        if (nucleus_bin(lm, l, it) != bstar) return;
+        if (nucleus_bin(lm, l, it) != bstar || below(l, y)) return;
         const uint64_t k = make_key(l, (uint32_t)y);
         if (plen > 0 && (k >> (64 - plen)) != (prefix >> (64 - plen))) return;
         const int dig = (int)((k >> shift) & ((1ull << nb) - 1ull));
@@ -531,7 +539,150 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
     const int t = n > 0 ? wave_walk(keys, n, sh_A, target, mass, &zk) : -1;
     if (lane == 0) {
       if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / zk)};
-      else cut[row] = RowCut{0ull, lmax, (float)(1.0 / Z)};
+      else cut[row] = RowCut{kfloor, lmax, (float)(1.0 / Z)};
+    }
+  }
+}
+
+// ===========================================================================
+// Top-k above the candidate capacity, over a full row: the kept set is the k
+// largest keys (logit desc, index asc), so it is one cut key kappa, the k-th
+// largest key.  kappa is found by radix select over the 64-bit key, 12 bits
+// per pass from the top (the row's tokens counted into an LDS histogram of
+// the next digit among those sharing the prefix found so far), until the
+// bucket holding the k-th key has at most kNucCap keys; the bucket's keys are
+// then collected, sorted and the k-th taken.  The same collect pass sums the
+// mass of every key above the bucket; the kept mass Z_k adds the bucket's
+// kept keys.  Writes cut[row] = {kappa, row maximum, 1 / Z_k} (masses
+// exp2((l - max) c), fp32 terms summed in fp64).  Keys are distinct, so at
+// most six passes (12, 24, ..., 60, 64 bits) reach a bucket of one key; rows
+// of N(0, 9) logits need two.  A nucleus over this law is cut afterwards by
+// nucleus_full_kernel, which reads kappa as its floor.
+// ===========================================================================
+constexpr int kCutBits = 12, kCutBins = 1 << kCutBits;
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const uint32_t o = (uint32_t)__shfl_up((int)v, (unsigned)d);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+template <typename ET>
+__global__ __launch_bounds__(kNucThreads) void kcut_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                                int rows_t, int G, int V, int S,
+                                                                const float2* __restrict__ part,
+                                                                const ReqInfo* __restrict__ info,
+                                                                RowCut* __restrict__ cut, Layout L) {
+  constexpr int NT = kNucThreads, NW = NT / kWave, PER = kCutBins / NT;
+  static_assert(kCutBins % NT == 0, "digits per thread");
+  const int row = blockIdx.x;
+  const ReqInfo ri = info[row_request(row, rows_t, G)];
+  if (ri.kind != kReqFull || ri.K <= 0) return;  // uniform over the workgroup
+  const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
+  if (!rp) return;  // past the request's draft length
+  __shared__ uint32_t hist[kCutBins];
+  __shared__ uint64_t keys[kNucCap];
+  __shared__ uint32_t red_u[NW];
+  __shared__ double red_d[NW];
+  __shared__ int sh_digit;
+  __shared__ uint32_t sh_need, sh_cnt, sh_n;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+
+  float lmax = -INFINITY;
+  for (int k = lane; k < S; k += kWave) lmax = fmaxf(lmax, part[(size_t)row * S + k].x);
+  lmax = wave_max_f(lmax);
+  const float c = ri.c, mc = lmax * c;
+  auto in_prefix = [](uint64_t k, uint64_t prefix, int plen) {
+    return plen == 0 || (k >> (64 - plen)) == (prefix >> (64 - plen));
+  };
+
+  uint64_t prefix = 0ull;
+  int plen = 0;
+  uint32_t need = (uint32_t)ri.K;  // rank of the cut key among the keys with the prefix (1-based)
+  uint32_t cnt = (uint32_t)V;      // keys with the prefix
+  while (cnt > (uint32_t)kNucCap && plen < 64) {
+    const int nb = 64 - plen < kCutBits ? 64 - plen : kCutBits;
+    const int shift = 64 - plen - nb;
+    const int nbins = 1 << nb;
+    for (int i = tid; i < kCutBins; i += NT) hist[i] = 0u;
+    __syncthreads();
+    row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+      const uint64_t k = make_key(l, (uint32_t)y);
+      if (in_prefix(k, prefix, plen)) atomicAdd(&hist[(uint32_t)(k >> shift) & (uint32_t)(nbins - 1)], 1u);
+    });
+    __syncthreads();
+    // Thread t owns positions [PER t, PER t + PER) of the digits in
+    // descending order (digit nbins - 1 - position): running counts then
+    // rank keys from the largest.
+    uint32_t loc = 0u;
+    for (int q = 0; q < PER; ++q) {
+      const int pos = PER * tid + q;
+      if (pos < nbins) loc += hist[nbins - 1 - pos];
+    }
+    uint32_t inc = wave_incl_scan_u32(loc);
+    if (lane == kWave - 1) red_u[w] = inc;
+    __syncthreads();
+    for (int k = 0; k < w; ++k) inc += red_u[k];
+    const uint32_t start = inc - loc;
+    if (start < need && need <= inc) {  // exactly one thread
+      uint32_t cum = start;
+      for (int q = 0; q < PER; ++q) {
+        const int d = nbins - 1 - (PER * tid + q);
+        const uint32_t h = hist[d];
+        if (cum + h >= need) {
+          sh_digit = d;
+          sh_need = need - cum;
+          sh_cnt = h;
+          break;
+        }
+        cum += h;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint64_t)(uint32_t)sh_digit << shift;
+    plen += nb;
+    need = sh_need;
+    cnt = sh_cnt;
+    __syncthreads();  // every thread has read the choice before the next clear
+  }
+
+  // Collect the bucket (at most kNucCap keys) and sum the mass above it.
+  if (tid == 0) sh_n = 0u;
+  __syncthreads();
+  double za = 0.0;
+  row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+    const uint64_t k = make_key(l, (uint32_t)y);
+    if (in_prefix(k, prefix, plen)) {
+      const uint32_t pos = atomicAdd(&sh_n, 1u);
+      if (pos < (uint32_t)kNucCap) keys[pos] = k;
+    } else if (plen > 0 && (k >> (64 - plen)) > (prefix >> (64 - plen))) {
+      za += (double)__builtin_amdgcn_exp2f(fmaf(l, c, -mc));
+    }
+  });
+  za = wave_sum_d(za);
+  if (lane == 0) red_d[w] = za;
+  __syncthreads();
+  double zabove = 0.0;
+  for (int k = 0; k < NW; ++k) zabove += red_d[k];
+  const int n = sh_n < (uint32_t)kNucCap ? (int)sh_n : kNucCap;
+  int n2 = 2;
+  while (n2 < n) n2 <<= 1;
+  for (int i = n + tid; i < n2; i += NT) keys[i] = 0ull;
+  __syncthreads();
+  block_sort_desc<NT>(keys, n2);
+  if (w == 0) {
+    // The kept part of the bucket: its `need` largest keys.
+    double zb = 0.0;
+    for (int i = lane; i < (int)need && i < n; i += kWave)
+      zb += (double)__builtin_amdgcn_exp2f(fmaf(key_value(keys[i]), c, -mc));
+    zb = wave_sum_d(zb);
+    if (lane == 0) {
+      const uint64_t kappa = need >= 1u && (int)need <= n ? keys[need - 1] : 0ull;
+      cut[row] = RowCut{kappa, lmax, (float)(1.0 / (zabove + zb))};
     }
   }
 }
@@ -628,7 +779,7 @@ __global__ __launch_bounds__(256) void beta_full_kernel(const ET* __restrict__ l
   const ReqInfo ri = info[b];
   if (ri.kind != kReqFull || j >= L.len(b, G)) return;  // uniform over the workgroup
   const float c = ri.c;
-  const bool nuc = ri.top_p < 1.f;
+  const bool nuc = ri.cut != 0;
   const size_t rt = (size_t)b * (G + 1) + j, rd = (size_t)rows_t + (size_t)b * G + j;
   // Row stats: the nucleus cut, or the merged softmax partials.
   float mp, izp, mq = 0.f, izq = 0.f;
@@ -736,7 +887,7 @@ __global__ __launch_bounds__(256) void match_prep_kernel(const float2* __restric
   if (ri.kind == kReqFull && j <= L.len(b, G)) {
     d.n = j;
     d.c = ri.c;
-    if (ri.top_p < 1.f) {
+    if (ri.cut) {
       const RowCut rc = cut[row];
       d.mp = rc.m;
       d.inv_zp = rc.inv_z;
@@ -986,7 +1137,7 @@ __global__ __launch_bounds__(64) void match_walk_kernel(const ET* __restrict__ l
         } else {
           const size_t rp = r0 + pa;
           const float l = Elem<ET>::load1(lt + L.trow(b, G, pa) * (size_t)L.ts + x);
-          if (ri.top_p < 1.f) {
+          if (ri.cut) {
             const RowCut rc = cut[rp];
             pd = make_key(l, (uint32_t)x) < rc.kappa ? 0.f : __builtin_amdgcn_exp2f((l - rc.m) * ri.c) * rc.inv_z;
           } else {

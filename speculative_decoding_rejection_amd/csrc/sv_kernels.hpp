@@ -119,10 +119,13 @@ enum : int32_t { kReqInvalid = 0, kReqGreedy = 1, kReqTopk = 2, kReqFull = 3 };
 struct __align__(16) ReqInfo {
   int32_t kind;  // kReq*
   float c;       // log2(e) / T (sampled requests)
-  int32_t K;     // top-k of a kReqTopk request
+  int32_t K;     // top-k: of a kReqTopk request (its candidates), or of a
+                 // kReqFull request whose k exceeds the candidate capacity
+                 // (a cut over the full row); 0 otherwise
   float top_p;   // < 1: nucleus cut
   float T;       // temperature
-  int32_t pad[3];
+  int32_t cut;   // kReqFull: 1 if its rows carry a RowCut (top-p or large k)
+  int32_t pad[2];
 };
 
 // Request of a logit row: rows [0, rows_t) are target rows b * (G + 1) + j,
@@ -1222,7 +1225,7 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
       return;
     }
     c = ri.c;
-    nuc = ri.top_p < 1.f;
+    nuc = ri.cut != 0;
   }
   const int g = L.len(b, G);  // this request's draft positions
   // Probability of token x (logit l) in padded row r, merged by one lane.

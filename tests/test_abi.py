@@ -61,7 +61,7 @@ def _call_prob(sv, params, ws_bytes=1 << 20, null=None):
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=0), 1), (dict(gamma=0), 1), (dict(vocab=0), 1), (dict(dtype=7), 2),
     (dict(temperature=0.0), 1), (dict(temperature=-1.0), 1), (dict(temperature=float("inf")), 1),
-    (dict(top_k=-1), 1), (dict(top_k=2000), 5), (dict(gamma=16385), 5),
+    (dict(top_k=-1), 1), (dict(gamma=16385), 5),
 ])
 def test_argument_errors(sv, kw, status):
     base = dict(batch=4, gamma=3, vocab=5000, dtype=sv.SV_BF16, temperature=1.0, top_k=0, seed=1)
@@ -83,6 +83,19 @@ def test_top_k_at_or_above_vocab_is_accepted(sv):
     # top_k >= V is "off", never unsupported.
     p = sv.make_params(4, 3, 500, sv.SV_BF16, 1.0, 5000, 1)
     assert _call_prob(sv, p, ws_bytes=16) == sv.SV_ERR_WORKSPACE  # reaches the workspace check
+
+
+def test_large_top_k_is_accepted(sv):
+    # 1024 < top_k < V: a cut over each full row (one RowCut per row).
+    p = sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 2000, 1)
+    assert _call_prob(sv, p, ws_bytes=16) == sv.SV_ERR_WORKSPACE  # reaches the workspace check
+    assert _call_prob(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, 0.0, 2000, 1), ws_bytes=16) == \
+        sv.SV_ERR_INVALID_ARG  # temperature 0 is the greedy entry's
+    rows = 4 * 7
+    small = sv.sv_workspace_bytes(sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 1000, 1))
+    large = sv.sv_workspace_bytes(p)
+    assert small >= rows * 1000 * 8                  # 1000 candidate keys per row
+    assert rows * 16 <= large < small                # one cut per row, no candidates
 
 
 def test_status_strings(sv):
@@ -110,7 +123,7 @@ def test_batch_argument_errors(sv):
     assert _call_batch(sv, p, ok, ws_bytes=16) == sv.SV_ERR_WORKSPACE  # everything else valid
     assert _call_batch(sv, p, sv.SvSampling(None, fake, fake, 64, 0)) == sv.SV_ERR_INVALID_ARG
     assert _call_batch(sv, p, sv.SvSampling(fake, fake, fake, -1, 0)) == sv.SV_ERR_INVALID_ARG
-    assert _call_batch(sv, p, sv.SvSampling(fake, fake, fake, 1025, 0)) == sv.SV_ERR_UNSUPPORTED
+    assert _call_batch(sv, p, sv.SvSampling(fake, fake, fake, 1025, 0), ws_bytes=16) == sv.SV_ERR_WORKSPACE
     for i in range(4):
         assert _call_batch(sv, p, ok, null=i) == sv.SV_ERR_INVALID_ARG
     assert _call_batch(sv, p, ok, null=4) == sv.SV_ERR_WORKSPACE
@@ -139,7 +152,8 @@ def test_batch_single_setting_and_layout_errors(sv):
     assert _call_batch(sv, p, None, ws_bytes=16) == sv.SV_ERR_WORKSPACE
     assert _call_batch(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, 0.0, 0, 1), None, ws_bytes=16) == sv.SV_ERR_WORKSPACE
     assert _call_batch(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, -1.0, 0, 1), None) == sv.SV_ERR_INVALID_ARG
-    assert _call_batch(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 2000, 1), None) == sv.SV_ERR_UNSUPPORTED
+    assert _call_batch(sv, sv.make_params(4, 3, 5000, sv.SV_BF16, 1.0, 2000, 1), None, ws_bytes=16) == \
+        sv.SV_ERR_WORKSPACE
     ok = sv.SvSampling(fake, None, None, 0, 0)
     L = sv.SvLayout
     d = ctypes.c_void_p(fake)

@@ -1083,3 +1083,20 @@ def test_block_race_streams_are_distinct():
     assert set(toks.tolist()) == {5, 100}
     assert abs((toks == 5).mean() - 0.5) < 4 * np.sqrt(0.25 / 4000)
     assert all(oracle.block_race(w, 23, b, 0)[0] == t for b, t in zip(range(50), toks))
+
+
+def test_sampler_match_race_by_law_size():
+    """The fresh sample of a node is the one-stage token race for a top-k law
+    keeping at most 1024 tokens and the block race for any larger law (a
+    top-k of 1025, or no top-k): the node's emitted token equals that race
+    on the row's adjusted law, stream for stream."""
+    rng = np.random.default_rng(13)
+    V = 3000
+    for trial in range(6):
+        lt = rng.normal(0.0, 2.0, size=(1, 2, V)).astype(np.float32)
+        x = np.array([[int(rng.integers(V))]], np.int32)
+        for k, racer in ((1024, oracle.race), (1025, oracle.block_race), (0, oracle.block_race)):
+            p = oracle.row_probs(lt[0, 0], 1.0, k)
+            res = oracle.verify_batch(lt, None, x, np.ones(1, np.float32), np.full(1, k, np.int32),
+                                      np.ones(1, np.float32), max_top_k=max(k, 1), seed=17 + trial, match=True)
+            assert int(res["out_tokens"][0, 0]) == racer(p, 17 + trial, 0, 0)[0]
