@@ -307,7 +307,9 @@ def verify_batch(target_logits, draft_tokens, draft=None, *, temperature=None, t
     (default W) the number of valid logits per row.  temperature / top_k /
     top_p: [B] device tensors (float32 / int32 / float32), or temperature
     None for one setting for every request (single_temperature,
-    single_top_k).  max_top_k defaults to 1024 when top_k is given.  beta:
+    single_top_k).  max_top_k (the bound on every top_k below vocab) defaults
+    to 1024 when top_k is given; pass it for top_k above 1024 (a request whose
+    top_k exceeds max_top_k and is below vocab is invalid).  beta:
     also return the per-position acceptance probability; counters: an int64
     [B, 3] device tensor the call adds its round to.  draft_kind
     SV_DRAFT_MATCH: sampler-match over chains, or over trees with parents
