@@ -595,7 +595,7 @@ __global__ __launch_bounds__(kNucThreads) void kcut_full_kernel(const ET* __rest
   float lmax = -INFINITY;
   for (int k = lane; k < S; k += kWave) lmax = fmaxf(lmax, part[(size_t)row * S + k].x);
   lmax = wave_max_f(lmax);
-  const float c = ri.c, mc = lmax * c;
+  const float c = ri.c;
   auto in_prefix = [](uint64_t k, uint64_t prefix, int plen) {
     return plen == 0 || (k >> (64 - plen)) == (prefix >> (64 - plen));
   };
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(kNucThreads) void kcut_full_kernel(const ET* __rest
       const uint32_t pos = atomicAdd(&sh_n, 1u);
       if (pos < (uint32_t)kNucCap) keys[pos] = k;
     } else if (plen > 0 && (k >> (64 - plen)) > (prefix >> (64 - plen))) {
-      za += (double)__builtin_amdgcn_exp2f(fmaf(l, c, -mc));
+      za += (double)__builtin_amdgcn_exp2f((l - lmax) * c);
     }
   });
   za = wave_sum_d(za);
@@ -678,7 +678,7 @@ __global__ __launch_bounds__(kNucThreads) void kcut_full_kernel(const ET* __rest
     // The kept part of the bucket: its `need` largest keys.
     double zb = 0.0;
     for (int i = lane; i < (int)need && i < n; i += kWave)
-      zb += (double)__builtin_amdgcn_exp2f(fmaf(key_value(keys[i]), c, -mc));
+      zb += (double)__builtin_amdgcn_exp2f((key_value(keys[i]) - lmax) * c);
     zb = wave_sum_d(zb);
     if (lane == 0) {
       const uint64_t kappa = need >= 1u && (int)need <= n ? keys[need - 1] : 0ull;
@@ -978,7 +978,6 @@ __global__ __launch_bounds__(NT) void block_race_kernel(const ET* __restrict__ l
   const bool vec_ok = (((uintptr_t)rp) & 15u) == 0u;  // a is a multiple of 64 elements
   const int kb0 = a / kRaceBlock, nblk = (e - a + kRaceBlock - 1) / kRaceBlock;
   const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)d.n;
-  const float mpc = d.mp * d.c;
   // The nucleus cut as a float compare (see race_full_kernel).
   const bool cut = CUT && d.kp != 0ull;
   const float kv = cut ? key_value(d.kp) : 0.f;
@@ -1006,7 +1005,7 @@ __global__ __launch_bounds__(NT) void block_race_kernel(const ET* __restrict__ l
         float w = 0.f;
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(f[u][k], d.c, -mpc));
+          const float p = __builtin_amdgcn_exp2f((f[u][k] - d.mp) * d.c);
           w += (!cut || f[u][k] > kv || (f[u][k] == kv && y0 + k <= ki)) ? p : 0.f;
         }
 #pragma unroll
@@ -1055,7 +1054,7 @@ __global__ __launch_bounds__(256) void block_finish_kernel(const ET* __restrict_
     if (y < V) {
       // The same mass expression as stage one (a block with mass keeps it).
       const float l = Elem<ET>::load1(lt + d.prow + y);
-      float p = __builtin_amdgcn_exp2f(fmaf(l, d.c, -(d.mp * d.c))) * d.inv_zp;
+      float p = __builtin_amdgcn_exp2f((l - d.mp) * d.c) * d.inv_zp;
       if (CUT && make_key(l, (uint32_t)y) < d.kp) p = 0.f;
       if (p > 0.f) {
         const uint4 r = race_block(k0, k1, (uint32_t)d.rb, (uint32_t)d.n, (uint32_t)y);

@@ -231,9 +231,10 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
         m = vm;
       }
       if (m != -INFINITY) {
-        const float mc = m * c;
+        // (l - m) c, not fma(l, c, -m c): the rounding of m c (up to |m c|
+        // 2^-24, large at low temperature) would shift every exponent.
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) sum += __builtin_amdgcn_exp2f(fmaf(f[k], c, -mc));
+        for (int k = 0; k < EPV; ++k) sum += __builtin_amdgcn_exp2f((f[k] - m) * c);
       }
     }
   }
@@ -1328,7 +1329,7 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
 // exp2((l - m) c) of the target row, the draft's scaled by inv_zq / inv_zp):
 // one factor for every token of the row, so the race's winner is unchanged.
 struct RaceRow {
-  float mpc, mqc, ratio, c, kvp, kvq;  // mpc = m_p c, mqc = m_q c, ratio = inv_zq / inv_zp
+  float mp, mq, ratio, c, kvp, kvq;  // row maxima of p and q; ratio = inv_zq / inv_zp
   int kip, kiq, mask_tok;
   bool cut_p, cut_q;
 };
@@ -1343,12 +1344,12 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   // Nucleus cuts as float compares: key(l, y) >= kappa iff l > value(kappa),
   // or l equals it and y <= index(kappa); kappa = 0 keeps every token.
   auto weight = [&](float lp, float lq, int y) -> float {
-    float p = __builtin_amdgcn_exp2f(fmaf(lp, r.c, -r.mpc));
+    float p = __builtin_amdgcn_exp2f((lp - r.mp) * r.c);
     if (r.cut_p && !(lp > r.kvp || (lp == r.kvp && y <= r.kip))) p = 0.f;
     if (RES == 0) return p;  // the one-hot draft token is masked per vector
     float q;
     if (RES == 1) {
-      q = __builtin_amdgcn_exp2f(fmaf(lq, r.c, -r.mqc));
+      q = __builtin_amdgcn_exp2f((lq - r.mq) * r.c);
       if (r.cut_q && !(lq > r.kvq || (lq == r.kvq && y <= r.kiq))) q = 0.f;
       return fmaxf(fmaf(-q, r.ratio, p), 0.f);
     }
@@ -1466,8 +1467,8 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   const int tid = threadIdx.x;
   RaceRow r;
   r.c = d.c;
-  r.mpc = d.mp * d.c;
-  r.mqc = d.mq * d.c;
+  r.mp = d.mp;
+  r.mq = d.mq;
   r.ratio = d.inv_zq / d.inv_zp;
   r.mask_tok = d.mask_tok;
   r.cut_p = CUT && d.kp != 0ull;

@@ -82,6 +82,12 @@ SMALL = [
     ("prob_f32_b256_g7_v151936", dict(B=8, V=3001, temperature=2.0, dtype="bf16"), None),
     ("onehot_bf16_b512_g3_v262144", dict(B=8, V=40000, temperature=0.5), 64),
     ("prob_f32_b8_g4_v32000", dict(B=4, V=70001), None),
+    # Extreme temperatures: at T 0.05 most masses underflow in fp32 (the law
+    # is nearly one-hot); at T 20 and 50 it is nearly flat.
+    ("prob_f32_b256_g7_v151936", dict(B=8, V=20011, temperature=0.05), None),
+    ("prob_topk64_bf16_b1024_g8_v256000", dict(B=8, V=30001, temperature=0.05), None),
+    ("onehot_bf16_b512_g3_v262144", dict(B=8, V=20011, temperature=20.0), None),
+    ("prob_f32_b256_g7_v151936", dict(B=8, V=20011, temperature=50.0, dtype="bf16"), None),
 ]
 
 
