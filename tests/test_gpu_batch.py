@@ -162,6 +162,14 @@ def test_large_top_k_with_top_p(sv, k):
     check_batch(sv, inp)
 
 
+@pytest.mark.parametrize("onehot", [False, True])
+def test_extreme_temperatures(sv, onehot):
+    """Nearly one-hot laws (T 0.03 and 0.05: most masses underflow in fp32)
+    and nearly flat ones (T 25), alone, under top-k and under top-p."""
+    mix = ((0.05, 0, 0.9), (0.05, 40, 1.0), (25.0, 0, 0.5), (0.03, 0, 1.0), (25.0, 300, 0.95), (0.0, 0, 1.0))
+    check_batch(sv, mixed(24, 5, 20011, "bf16", mix=mix, seed=9), onehot=onehot, max_top_k=300)
+
+
 def test_invalid_settings_emit_nothing(sv):
     inp = mixed(8, 3, 1000, "f32", mix=((0.8, 10, 0.9),), seed=2)
     t, k, p = inp["temperature"].clone(), inp["top_k"].clone(), inp["top_p"].clone()
