@@ -424,14 +424,14 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
                        dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part64, err,
                        (const ReqInfo*)info, pl.G, pl.L);
     if (pl.big_k)  // top-k above the candidate capacity: the k-th key of the full row, before any nucleus
-      hipLaunchKernelGGL((sv::kcut_full_kernel<ET>), dim3(nrows), dim3(sv::kNucThreads), 0, st, (const ET*)lt,
+      hipLaunchKernelGGL((sv::kcut_full_kernel<ET>), dim3(nrows), dim3(sv::kCutThreads), 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
     if (nuc && pl.K > 0)
       hipLaunchKernelGGL(sv::nucleus_topk_kernel, dim3((nrows + 3) / 4), dim3(256), 0, st,
                          (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info, pl.L);
     if (nuc)
-      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(sv::kNucThreads), 0, st, (const ET*)lt,
+      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(sv::NucShape<ET>::NT), 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
     t.done();

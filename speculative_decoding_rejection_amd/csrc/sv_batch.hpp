@@ -16,6 +16,8 @@
 // exp((l - l_max) / T) in double precision for every token that can matter.
 #pragma once
 
+#include <type_traits>
+
 #include "sv_kernels.hpp"
 
 namespace sv {
@@ -60,16 +62,15 @@ __device__ __forceinline__ int nucleus_k(double x) {
   return __double2loint(fma(x, kNucInvStep, kNucRound));
 }
 __device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, int* k_out) {
-  if (!(x > -700.0)) {
-    *k_out = 1;  // no bin
-    return 0.0;
-  }
-  const double t = fma(x, kNucInvStep, kNucRound);
+  // Branch-free, so that the masses of a vector's tokens are computed side by
+  // side: x <= -700 (and -inf) is evaluated at -700 and the result replaced.
+  const bool ok = x > -700.0;
+  const double xc = fmax(x, -700.0);
+  const double t = fma(xc, kNucInvStep, kNucRound);
   const double kd = t - kNucRound;
   const int k = __double2loint(t);
-  *k_out = k;
-  double r = fma(-kd, 0x1.62e42fee00000p-7, x);  // head of ln2 / 64
-  r = fma(-kd, 0x1.a39ef35793c76p-39, r);         // tail
+  double r = fma(-kd, 0x1.62e42fee00000p-7, xc);  // head of ln2 / 64
+  r = fma(-kd, 0x1.a39ef35793c76p-39, r);          // tail
   double q = fma(r, 1.0 / 720.0, 1.0 / 120.0);
   q = fma(r, q, 1.0 / 24.0);
   q = fma(r, q, 1.0 / 6.0);
@@ -77,7 +78,9 @@ __device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, in
   q = fma(r, q, 1.0);
   const double tj = tab[k & 63];
   const double v = fma(tj, q * r, tj);  // 2^(j/64) exp(r), in [0.99, 1.01]
-  return __hiloint2double(__double2hiint(v) + (k >> 6) * (1 << 20), __double2loint(v));
+  const double e = __hiloint2double(__double2hiint(v) + (k >> 6) * (1 << 20), __double2loint(v));
+  *k_out = k;  // of max(x, -700): -k is past every gap bin when x <= -700
+  return ok ? e : 0.0;
 }
 
 // ===========================================================================
@@ -281,56 +284,105 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 // Each pass streams the row from HBM.
 // ===========================================================================
 constexpr int kNucBins = 4096;  // ln2 / 64 nats each: gaps below 44.4 nats
-constexpr int kNucThreads = 512;  // one workgroup per row
+// One workgroup per row.  Workgroup size and vectors per thread and chunk,
+// by logit type (measured on MI355X): bf16 rows carry twice the tokens per
+// vector, and their pass is bound by the per-token work, so more, lighter
+// waves; fp32 rows take deeper chunks.
+template <typename ET>
+struct NucShape;
+template <>
+struct NucShape<float> {
+  static constexpr int NT = 256, U = 4;
+};
+template <>
+struct NucShape<uint16_t> {
+  static constexpr int NT = 512, U = 1;
+};
+constexpr int kCutThreads = 512;  // kcut_full_kernel
 constexpr int kNucCap = 2048;
 
 // Gap bin of logit l (-1: none), from the same rounding as the mass.
+// Branch-free: a gap beyond 700 nats (or an infinite one) rounds at 700,
+// which lies far past the last bin.
 __device__ __forceinline__ int nucleus_bin(double lm, float l, double it) {
-  const double x = ((double)l - lm) * it;
-  if (!(x > -700.0)) return -1;
-  const int b = -nucleus_k(x);
+  const int b = -nucleus_k(fmax(((double)l - lm) * it, -700.0));
   return b < kNucBins ? b : -1;
 }
 
-// Calls f(logit, index) for every element of the row this thread owns.
-template <typename ET, int NT, typename F>
-__device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
-  constexpr int EPV = Elem<ET>::kPerVec, U = 4;
+// Streams the row through the workgroup: fv(values, y0) for each 16-byte
+// vector this thread owns (elements y0 .. y0 + EPV - 1), fs(value, y) for the
+// scalar head and tail.  Chunks of U vectors per thread; the next chunk's
+// loads are issued before the current one is processed, so a wave's memory
+// requests stay in flight while it computes.
+template <typename ET, int NT, int U, typename FV, typename FS>
+__device__ __forceinline__ void row_stream(const ET* rp, int V, FV&& fv, FS&& fs) {
+  constexpr int EPV = Elem<ET>::kPerVec, STEP = NT * U;
   Slice<ET> sl(rp, 0, V);
   const int tid = threadIdx.x;
   if (tid < sl.nscalar()) {
     const int y = sl.scalar_index(tid);
-    f(Elem<ET>::load1(rp + y), y);
+    fs(Elem<ET>::load1(rp + y), y);
   }
   const uint4* vp = sl.vecs();
-  for (int i0 = tid; i0 < sl.nvec; i0 += NT * U) {
-    uint4 v[U];
+  const int nv = sl.nvec, nfull = nv / STEP;
+  auto proc = [&](const uint4& v, int i) {
+    float f[EPV];
+    Elem<ET>::unpack(v, f);
+    fv(f, sl.vec_index0(i));
+  };
+  if (nfull > 0) {
+    uint4 cur[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * NT;
-      v[u] = i < sl.nvec ? load_stream(vp + i) : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int u = 0; u < U; ++u) cur[u] = load_stream(vp + tid + u * NT);
+    for (int c = 0; c < nfull; ++c) {
+      const int i0 = c * STEP + tid;
+      uint4 nxt[U];
+      if (c + 1 < nfull) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int i = i0 + u * NT;
-      if (i < sl.nvec) {
-        float fv[EPV];
-        Elem<ET>::unpack(v[u], fv);
-        const int y0 = sl.vec_index0(i);
+        for (int u = 0; u < U; ++u) nxt[u] = load_stream(vp + i0 + STEP + u * NT);
+      } else {
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) f(fv[k], y0 + k);
+        for (int u = 0; u < U; ++u) nxt[u] = cur[u];
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u) proc(cur[u], i0 + u * NT);
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
   }
+  // The last partial chunk: fewer than U vectors for some threads.
+  const int i0 = nfull * STEP + tid;
+  uint4 v[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int i = i0 + u * NT;
+    v[u] = i < nv ? load_stream(vp + i) : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (i0 + u * NT < nv) proc(v[u], i0 + u * NT);
+}
+
+// Calls f(logit, index) for every element of the row this thread owns.
+template <typename ET, int NT, int U, typename F>
+__device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
+  constexpr int EPV = Elem<ET>::kPerVec;
+  row_stream<ET, NT, U>(
+      rp, V,
+      [&](const float (&fv)[EPV], int y0) {
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) f(fv[k], y0 + k);
+      },
+      f);
 }
 
 template <typename ET>
-__global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+__global__ __launch_bounds__(NucShape<ET>::NT) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                            int rows_t, int G, int V, int S,
                                                            const float2* __restrict__ part,
                                                            const ReqInfo* __restrict__ info,
                                                            RowCut* __restrict__ cut, Layout L) {
-  constexpr int NT = kNucThreads, NW = NT / kWave, PER = kNucBins / NT;
+  constexpr int NT = NucShape<ET>::NT, U = NucShape<ET>::U, NW = NT / kWave, PER = kNucBins / NT;
   static_assert(kNucBins % NT == 0, "bins per thread");
   static_assert(kNucCap * sizeof(uint64_t) <= kNucBins * sizeof(double), "keys alias the histogram");
   const int row = blockIdx.x;
@@ -344,13 +396,22 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   auto below = [&](float l, int y) { return kfloor != 0ull && make_key(l, (uint32_t)y) < kfloor; };
   // The gap histogram is dead once its bin is chosen; the collected keys of
   // that bin then take its storage.
-  __shared__ double hm[kNucBins];
+  __shared__ double hm[kNucBins + 1];  // + the spare slot of tokens without a bin
   uint64_t* keys = reinterpret_cast<uint64_t*>(hm);
   __shared__ double tab[64];
-  __shared__ double dm[256];
-  __shared__ uint32_t dc[256];
   __shared__ double red_d[NW], red_s[NW];
-  __shared__ double incl_sh[NT];
+  // The scan's running sums and the refinement's digit counts live at
+  // different times.
+  __shared__ union {
+    double incl[NT];
+    struct {
+      double m[256];
+      uint32_t c[256];
+    } dig;
+  } scr;
+  double* incl_sh = scr.incl;
+  double* dm = scr.dig.m;
+  uint32_t* dc = scr.dig.c;
   __shared__ uint64_t red_k[2][NW];
   __shared__ double sh_A;
   __shared__ int sh_bin, sh_n;
@@ -365,7 +426,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   lmax = wave_max_f(lmax);
   const double lm = (double)lmax, it = 1.0 / (double)ri.T;
 
-  for (int i = tid; i < kNucBins; i += NT) hm[i] = 0.0;
+  for (int i = tid; i <= kNucBins; i += NT) hm[i] = 0.0;
   if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
   // Every mass of this kernel: exp((l - lm) / T) by the table-driven exp.
   auto mass = [&](float l) {
@@ -377,18 +438,50 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
     sh_prefix = 0ull;  // fixed top bits of the cut key (refinement)
     sh_plen = 0;
   }
+
   __syncthreads();
 
   // Pass 1: masses, Z and the mass histogram of the gap.  The gap is the
-  // negated exponent, so mass and bin come from one product.
+  // negated exponent, so mass and bin come from one product.  Branch-free:
+  // a token without a bin adds to the spare slot hm[kNucBins], a token below
+  // the k-floor adds 0.
   double zt = 0.0;
-  row_foreach<ET, NT>(rp, V, [&](float l, int y) {
-    if (below(l, y)) return;
-    int k;
-    const double e = exp_nonpos_f64(((double)l - lm) * it, tab, &k);
-    zt += e;
-    if (k <= 0 && k > -kNucBins) atomicAdd(&hm[-k], e);
-  });
+  auto pass1 = [&](auto floor_tag) {
+    constexpr bool FLOOR = decltype(floor_tag)::value;
+    auto mass_bin = [&](float l, int y, uint32_t& bin) -> double {
+      int k;
+      double e = exp_nonpos_f64(((double)l - lm) * it, tab, &k);
+      if (FLOOR) e = make_key(l, (uint32_t)y) < kfloor ? 0.0 : e;
+      bin = min((uint32_t)(-k), (uint32_t)kNucBins);
+      return e;
+    };
+    row_stream<ET, NT, U>(
+        rp, V,
+        [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
+          // Masses and bins of the vector's tokens first (independent
+          // chains the scheduler interleaves), then the histogram adds.
+          constexpr int EPV = Elem<ET>::kPerVec;
+          double e[EPV];
+          uint32_t bin[EPV];
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) e[k] = mass_bin(fv[k], y0 + k, bin[k]);
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) atomicAdd(&hm[bin[k]], e[k]);
+#pragma unroll
+          for (int w2 = 1; w2 < EPV; w2 *= 2)
+#pragma unroll
+            for (int k = 0; k + w2 < EPV; k += 2 * w2) e[k] += e[k + w2];
+          zt += e[0];
+        },
+        [&](float l, int y) {
+          uint32_t bin;
+          const double e = mass_bin(l, y, bin);
+          atomicAdd(&hm[bin], e);
+          zt += e;
+        });
+  };
+  if (kfloor != 0ull) pass1(std::true_type{});
+  else pass1(std::false_type{});
   zt = wave_sum_d(zt);
   if (lane == 0) red_d[w] = zt;
   __syncthreads();
@@ -437,13 +530,35 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   // Pass 2: collect the keys of the bin (at most kNucCap are kept; the count
   // tells whether the bin needs refining).  filter_key: bin and key prefix.
   auto collect = [&](int plen, uint64_t prefix) {
-    row_foreach<ET, NT>(rp, V, [&](float l, int y) {
-      if (nucleus_bin(lm, l, it) != bstar || below(l, y)) return;
+    auto push = [&](float l, int y) {
+      if (below(l, y)) return;
       const uint64_t k = make_key(l, (uint32_t)y);
       if (plen > 0 && (plen == 64 ? k != prefix : (k >> (64 - plen)) != (prefix >> (64 - plen)))) return;
       const int pos = atomicAdd(&sh_n, 1);
       if (pos < kNucCap) keys[pos] = k;
-    });
+    };
+    // The bins of a vector's tokens first (branch-free), then the rare
+    // tokens of the chosen bin.
+    row_stream<ET, NT, U>(
+        rp, V,
+        [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
+          constexpr int EPV = Elem<ET>::kPerVec;
+          bool m[EPV];
+          bool any = false;
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) {
+            m[k] = nucleus_bin(lm, fv[k], it) == bstar;
+            any |= m[k];
+          }
+          if (any) {
+#pragma unroll
+            for (int k = 0; k < EPV; ++k)
+              if (m[k]) push(fv[k], y0 + k);
+          }
+        },
+        [&](float l, int y) {
+          if (nucleus_bin(lm, l, it) == bstar) push(l, y);
+        });
   };
   collect(0, 0ull);
   __syncthreads();
@@ -453,7 +568,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
   if (sh_n > kNucCap) {
     if (tid == 0) sh_cnt = (uint32_t)sh_n;
     uint64_t kmin = ~0ull, kmax = 0ull;
-    row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+    row_foreach<ET, NT, U>(rp, V, [&](float l, int y) {
       if (nucleus_bin(lm, l, it) == bstar && !below(l, y)) {
         const uint64_t k = make_key(l, (uint32_t)y);
         kmin = k < kmin ? k : kmin;
@@ -488,7 +603,7 @@ __global__ __launch_bounds__(kNucThreads) void nucleus_full_kernel(const ET* __r
         dc[i] = 0u;
       }
       __syncthreads();
-      row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+      row_foreach<ET, NT, U>(rp, V, [&](float l, int y) {
         if (nucleus_bin(lm, l, it) != bstar || below(l, y)) return;
         const uint64_t k = make_key(l, (uint32_t)y);
         if (plen > 0 && (k >> (64 - plen)) != (prefix >> (64 - plen))) return;
@@ -572,12 +687,12 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
 }
 
 template <typename ET>
-__global__ __launch_bounds__(kNucThreads) void kcut_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+__global__ __launch_bounds__(kCutThreads) void kcut_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                                 int rows_t, int G, int V, int S,
                                                                 const float2* __restrict__ part,
                                                                 const ReqInfo* __restrict__ info,
                                                                 RowCut* __restrict__ cut, Layout L) {
-  constexpr int NT = kNucThreads, NW = NT / kWave, PER = kCutBins / NT;
+  constexpr int NT = kCutThreads, NW = NT / kWave, PER = kCutBins / NT;
   static_assert(kCutBins % NT == 0, "digits per thread");
   const int row = blockIdx.x;
   const ReqInfo ri = info[row_request(row, rows_t, G)];
@@ -610,7 +725,7 @@ __global__ __launch_bounds__(kNucThreads) void kcut_full_kernel(const ET* __rest
     const int nbins = 1 << nb;
     for (int i = tid; i < kCutBins; i += NT) hist[i] = 0u;
     __syncthreads();
-    row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+    row_foreach<ET, NT, 2>(rp, V, [&](float l, int y) {
       const uint64_t k = make_key(l, (uint32_t)y);
       if (in_prefix(k, prefix, plen)) atomicAdd(&hist[(uint32_t)(k >> shift) & (uint32_t)(nbins - 1)], 1u);
     });
@@ -654,7 +769,7 @@ __global__ __launch_bounds__(kNucThreads) void kcut_full_kernel(const ET* __rest
   if (tid == 0) sh_n = 0u;
   __syncthreads();
   double za = 0.0;
-  row_foreach<ET, NT>(rp, V, [&](float l, int y) {
+  row_foreach<ET, NT, 2>(rp, V, [&](float l, int y) {
     const uint64_t k = make_key(l, (uint32_t)y);
     if (in_prefix(k, prefix, plen)) {
       const uint32_t pos = atomicAdd(&sh_n, 1u);
