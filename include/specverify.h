@@ -257,7 +257,15 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  * for token-only proposals.  p_draft of node i is p_parent(x_i), its
  * acceptance probability once its parent is reached (also beta); q_draft is
  * 1 for valid tokens.
- * Workspace: sv_workspace_bytes_batch(params, sampling) bytes. */
+ * Workspace: sv_workspace_bytes_batch(params, sampling) bytes.
+ * Streams: the row passes of the different kinds of request run side by
+ * side.  The call records an event on `stream`, the top-k rows and the
+ * temperature-0 rows are streamed on two library-owned streams of the current
+ * device that wait for it (created on the first batch call on that device,
+ * non-blocking, default priority, kept until the process ends), and `stream`
+ * waits for both before the accept passes: stream order is unchanged, and a
+ * capture of `stream` takes the two streams in.  Calls from several host
+ * threads are serialised while they enqueue this fork and join. */
 sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const sv_layout* layout,
                             const void* target_logits, const void* draft, const int32_t* draft_tokens,
                             const sv_outputs* outputs, void* workspace, size_t workspace_bytes, void* stream);

@@ -5,6 +5,8 @@
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "specverify.h"
@@ -184,8 +186,9 @@ struct TimedLaunch {
   int fam;
   hipStream_t st;
   hipEvent_t stop = nullptr;
+  // f < 0: not timed (a launch inside a span timed as a whole).
   TimedLaunch(int f, hipStream_t s) : fam(f), st(s) {
-    if (!g_timing || g_used[fam] >= kMaxTimed) return;
+    if (fam < 0 || !g_timing || g_used[fam] >= kMaxTimed) return;
     auto& ev = g_events[fam];
     if (g_used[fam] == ev.size()) {
       hipEvent_t a, b;
@@ -208,6 +211,43 @@ struct TimedLaunch {
 
 sv_status check_launch() { return hipGetLastError() == hipSuccess ? SV_OK : SV_ERR_HIP; }
 
+// ---------------------------------------------------------------------------
+// Side streams of a batch call's row phase.  The rows of different kinds of
+// request are disjoint and each kind has its own row kernels, so the top-k
+// rows and the temperature-0 rows are streamed on two side streams while the
+// full rows take the caller's stream: a kind that holds few rows no longer
+// runs alone on the chip.  Fork and join are events recorded on the caller's
+// stream and the side streams (stream order is kept; a capture of the
+// caller's stream takes the side streams in).  Created once per device
+// (non-blocking, default priority); the lock covers the enqueue of a fork and
+// its join, so concurrent host threads do not interleave the shared events.
+// ---------------------------------------------------------------------------
+struct SideStreams {
+  hipStream_t s[2] = {nullptr, nullptr};
+  hipEvent_t fork = nullptr, join[2] = {nullptr, nullptr};
+  bool ok = false;
+};
+std::mutex g_side_mu;
+std::map<int, SideStreams> g_side;
+
+// With g_side_mu held.  Null if the streams cannot be made (then the row
+// phase runs on the caller's stream alone).
+SideStreams* side_streams() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  auto it = g_side.find(dev);
+  if (it == g_side.end()) {
+    SideStreams ss;
+    bool ok = true;
+    for (int i = 0; i < 2 && ok; ++i) ok = hipStreamCreateWithFlags(&ss.s[i], hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+    for (int i = 0; i < 2 && ok; ++i) ok = hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming) == hipSuccess;
+    ss.ok = ok;
+    it = g_side.emplace(dev, ss).first;
+  }
+  return it->second.ok ? &it->second : nullptr;
+}
+
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 sv_status check_common(const Plan& pl, const void* target_logits, const int32_t* draft_tokens, int32_t* out_tokens,
@@ -221,8 +261,8 @@ sv_status check_common(const Plan& pl, const void* target_logits, const int32_t*
 
 template <typename ET>
 sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st,
-                           const ReqInfo* info = nullptr) {
-  TimedLaunch t(0, st);
+                           const ReqInfo* info = nullptr, int fam = 0) {
+  TimedLaunch t(fam, st);
   hipLaunchKernelGGL((sv::rows_softmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(nrows * pl.S),
                      dim3(kRowThreads), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.S, pl.seg, pl.c,
                      (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err), info, pl.G, pl.L);
@@ -254,8 +294,8 @@ void launch_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows,
 // stored pl.kcap keys apart.
 template <typename ET>
 sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st,
-                        const ReqInfo* info = nullptr) {
-  TimedLaunch t(0, st);
+                        const ReqInfo* info = nullptr, int fam = 0) {
+  TimedLaunch t(fam, st);
   uint64_t* cand = (uint64_t*)(ws + pl.off_cand);
   int* err = (int*)(ws + pl.off_err);
   // Buffer capacity per wave: >= K + 64 * (elements per vector) for one
@@ -416,26 +456,54 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
-  if (pl.K > 0 && (s = run_rows_topk<ET>(pl, lt, ldl, nrows, ws, st, info)) != SV_OK) return s;
-  if ((s = run_rows_softmax<ET>(pl, lt, ldl, nrows, ws, st, info)) != SV_OK) return s;
   {
+    // Row phase: top-k rows (candidates, then their nucleus) on side stream
+    // 0, temperature-0 rows (argmax) on side stream 1, full rows (softmax
+    // partials, then a large top-k's cut and the nucleus) on the caller's
+    // stream.  The three write disjoint parts of the workspace.
     TimedLaunch t(0, st);
-    hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
-                       dim3(kRowThreads), 0, st, (const ET*)lt, pl.V, pl.S, pl.seg, part64, err,
-                       (const ReqInfo*)info, pl.G, pl.L);
-    if (pl.big_k)  // top-k above the candidate capacity: the k-th key of the full row, before any nucleus
+    std::unique_lock<std::mutex> lock(g_side_mu);
+    SideStreams* side = side_streams();
+    hipStream_t s_topk = st, s_arg = st;
+    if (side && hipEventRecord(side->fork, st) == hipSuccess &&
+        hipStreamWaitEvent(side->s[0], side->fork, 0) == hipSuccess &&
+        hipStreamWaitEvent(side->s[1], side->fork, 0) == hipSuccess) {
+      s_topk = side->s[0];
+      s_arg = side->s[1];
+    }
+    sv_status rs = SV_OK;
+    if (pl.K > 0) {
+      rs = run_rows_topk<ET>(pl, lt, ldl, nrows, ws, s_topk, info, -1);
+      if (rs == SV_OK && nuc)
+        hipLaunchKernelGGL(sv::nucleus_topk_kernel, dim3((nrows + 3) / 4), dim3(256), 0, s_topk,
+                           (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info,
+                           pl.L);
+    }
+    if (rs == SV_OK)
+      hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
+                         dim3(kRowThreads), 0, s_arg, (const ET*)lt, pl.V, pl.S, pl.seg, part64, err,
+                         (const ReqInfo*)info, pl.G, pl.L);
+    if (rs == SV_OK) rs = run_rows_softmax<ET>(pl, lt, ldl, nrows, ws, st, info, -1);
+    if (rs == SV_OK && pl.big_k)  // top-k above the candidate capacity: the k-th key of the full row, before any nucleus
       hipLaunchKernelGGL((sv::kcut_full_kernel<ET>), dim3(nrows), dim3(sv::kCutThreads), 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
-    if (nuc && pl.K > 0)
-      hipLaunchKernelGGL(sv::nucleus_topk_kernel, dim3((nrows + 3) / 4), dim3(256), 0, st,
-                         (uint64_t*)(ws + pl.off_cand), pl.kcap, pl.rows_t, nrows, pl.G, (const ReqInfo*)info, pl.L);
-    if (nuc)
+    if (rs == SV_OK && nuc)
       hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(sv::NucShape<ET>::NT), 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
+    if (rs == SV_OK) rs = check_launch();
+    if (s_topk != st) {
+      // Join (also after a failed launch): the caller's stream waits for
+      // both side streams.
+      if (hipEventRecord(side->join[0], s_topk) != hipSuccess || hipEventRecord(side->join[1], s_arg) != hipSuccess ||
+          hipStreamWaitEvent(st, side->join[0], 0) != hipSuccess ||
+          hipStreamWaitEvent(st, side->join[1], 0) != hipSuccess)
+        rs = SV_ERR_HIP;
+    }
+    if (rs != SV_OK) return rs;
+    lock.unlock();
     t.done();
-    if ((s = check_launch()) != SV_OK) return s;
   }
   if (MODE == 3) {
     // Sampler-match: a sample for every node's row, then the walk.
