@@ -225,27 +225,31 @@ sv_status check_launch() { return hipGetLastError() == hipSuccess ? SV_OK : SV_E
 struct SideStreams {
   hipStream_t s[2] = {nullptr, nullptr};
   hipEvent_t fork = nullptr, join[2] = {nullptr, nullptr};
-  bool ok = false;
 };
 std::mutex g_side_mu;
 std::map<int, SideStreams> g_side;
 
 // With g_side_mu held.  Null if the streams cannot be made (then the row
-// phase runs on the caller's stream alone).
+// phase runs on the caller's stream alone, and a later call tries again).
 SideStreams* side_streams() {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   auto it = g_side.find(dev);
-  if (it == g_side.end()) {
-    SideStreams ss;
-    bool ok = true;
-    for (int i = 0; i < 2 && ok; ++i) ok = hipStreamCreateWithFlags(&ss.s[i], hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
-    for (int i = 0; i < 2 && ok; ++i) ok = hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming) == hipSuccess;
-    ss.ok = ok;
-    it = g_side.emplace(dev, ss).first;
+  if (it != g_side.end()) return &it->second;
+  SideStreams ss;
+  bool ok = true;
+  for (int i = 0; i < 2 && ok; ++i) ok = hipStreamCreateWithFlags(&ss.s[i], hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) == hipSuccess;
+  for (int i = 0; i < 2 && ok; ++i) ok = hipEventCreateWithFlags(&ss.join[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    for (hipStream_t h : ss.s)
+      if (h) (void)hipStreamDestroy(h);
+    for (hipEvent_t e : {ss.fork, ss.join[0], ss.join[1]})
+      if (e) (void)hipEventDestroy(e);
+    (void)hipGetLastError();  // the failure is not the caller's launch error
+    return nullptr;
   }
-  return it->second.ok ? &it->second : nullptr;
+  return &g_side.emplace(dev, ss).first->second;
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
