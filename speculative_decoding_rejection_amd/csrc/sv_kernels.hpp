@@ -567,45 +567,11 @@ __device__ __forceinline__ int topk_append(const float* f, uint32_t idx0, uint32
   return cnt;
 }
 
-// The same for a few lanes: each lane L of `lanes` (a wave-uniform mask) in
-// turn broadcasts its 16-byte vector, and lanes 0 .. EPV-1 take its elements
-// (element j: word j / 2, low half first, for bf16; word j for fp32).  About
-// a third of the per-element walk when one or two lanes hold candidates.
-// yb: token index of element 0 of lane 0's vector.
-template <typename ET>
-__device__ __forceinline__ int topk_append_lanes(const uint4& vv, uint64_t lanes, int yb, uint64_t tau, float tau_v,
-                                                 uint64_t* bw, int cnt) {
-  constexpr int EPV = Elem<ET>::kPerVec;
-  const int lane = lane_id();
-  while (lanes) {
-    const int L = __builtin_ctzll(lanes);
-    lanes &= lanes - 1ull;
-    const uint32_t w0 = (uint32_t)__builtin_amdgcn_readlane((int)vv.x, L);
-    const uint32_t w1 = (uint32_t)__builtin_amdgcn_readlane((int)vv.y, L);
-    const uint32_t w2 = (uint32_t)__builtin_amdgcn_readlane((int)vv.z, L);
-    const uint32_t w3 = (uint32_t)__builtin_amdgcn_readlane((int)vv.w, L);
-    uint32_t bits;
-    if (EPV == 8) {
-      const int q = lane >> 1;
-      const uint32_t wd = q == 0 ? w0 : (q == 1 ? w1 : (q == 2 ? w2 : w3));
-      bits = (lane & 1) ? (wd & 0xFFFF0000u) : (wd << 16);
-    } else {
-      bits = lane == 0 ? w0 : (lane == 1 ? w1 : (lane == 2 ? w2 : w3));
-    }
-    const float f = __uint_as_float(bits);
-    const bool cand = lane < EPV && f >= tau_v;
-    const uint64_t key = cand ? make_key(f, (uint32_t)(yb + L * EPV + lane)) : 0ull;
-    const bool hit = key > tau;
-    const uint64_t m = ballot(hit);
-    if (hit) bw[cnt + lanes_below(m)] = key;
-    cnt += __builtin_popcountll(m);
-  }
-  return cnt;
-}
-
-#ifndef SV_TOPK_LANE_APPEND
-#define SV_TOPK_LANE_APPEND 2  // at most this many candidate lanes: the per-lane walk
+#ifndef SV_TOPK_STASH_FLUSH
+#define SV_TOPK_STASH_FLUSH 64  // stashed vectors that trigger the bulk append
 #endif
+constexpr int kTopkStashFlush = SV_TOPK_STASH_FLUSH;
+constexpr int kTopkStash = kTopkStashFlush + kWave;  // a step adds at most one wave's worth
 
 // Prefilter for bf16 vectors against a positive threshold: for positive
 // values the bf16 bit pattern orders like a signed 16-bit integer, and every
@@ -640,6 +606,8 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   __shared__ uint64_t kth_sh[RPB][2];  // per row: best k-th bound; best combined bound
   __shared__ uint32_t cnt_sh[NW];
   __shared__ uint32_t lm_sh[RPB][WPR * kWave];
+  __shared__ uint4 stash_v[NW][kTopkStash];
+  __shared__ uint32_t stash_i[NW][kTopkStash];
   const int tid = threadIdx.x, w = tid / kWave;
   const int g = w / WPR, wg = w % WPR, gtid = tid % GT;
   const int row = blockIdx.x * RPB + g;
@@ -692,16 +660,56 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   const uint4* vp = sl.vecs();
   const uint32_t full = (1u << EPV) - 1u;
 
-  // Filters one vector of this lane: appends its keys > tau, compacts when
-  // the wave buffer passes the trigger.  Called with wave-uniform control.
+  // Candidate vectors are stashed, not walked: a step where some lane's
+  // vector may hold a key >= tau writes those lanes' vectors (and their first
+  // token index) to the wave's LDS stash with one masked store, so a step
+  // costs a few instructions however many lanes it stops.  Once the stash
+  // holds a wave's worth of vectors, every lane takes one of them and the
+  // wave appends their keys > tau (the current tau: tau only rises, so every
+  // key that beats the row's final bound was stashed and is appended).
+  int sc = 0;  // stashed vectors (wave-uniform)
+  uint4* sv_w = stash_v[w];
+  uint32_t* si_w = stash_i[w];
+  auto flush = [&]() {
+    wave_lds_sync();
+    for (int e0 = 0; e0 < sc; e0 += kWave) {
+      const int e = e0 + lane_id();
+      float f[EPV];
+      uint32_t idx0 = 0u, vm = 0u;
+      if (e < sc) {
+        Elem<ET>::unpack(sv_w[e], f);
+        idx0 = si_w[e];
+        vm = full;
+      } else {
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) f[k] = -INFINITY;
+      }
+      if (cnt > kGuard) {
+        if (lane_id() == 0) *cntp = (uint32_t)cnt;
+        tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
+        tau_v = tau_value(tau);
+        cnt = (int)__builtin_amdgcn_readfirstlane(*cntp);
+      }
+      cnt = topk_append<EPV>(f, idx0, vm, tau, tau_v, bw, cnt);
+      if (cnt > trig) {
+        if (lane_id() == 0) *cntp = (uint32_t)cnt;
+        tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
+        tau_v = tau_value(tau);
+        cnt = (int)__builtin_amdgcn_readfirstlane(*cntp);
+        trig = max(K4 + SV_TOPK_TRIG_STEP, cnt + SV_TOPK_TRIG_STEP);
+      }
+    }
+    sc = 0;
+    wave_lds_sync();
+  };
   auto filter = [&](const uint4& vv, int i, bool packed, short thr16) {
     const bool valid = i < sl.nvec;
-    float f[EPV];
-    Elem<ET>::unpack(vv, f);
     bool maybe;
     if (packed) {
       maybe = valid && bf16_vec_reaches(vv, thr16);
     } else {
+      float f[EPV];
+      Elem<ET>::unpack(vv, f);
       float vm = f[0];
 #pragma unroll
       for (int k = 1; k < EPV; ++k) vm = fmaxf(vm, f[k]);
@@ -709,26 +717,13 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
     }
     const uint64_t mm = ballot(maybe);
     if (mm == 0ull) return;
-    if (cnt > kGuard) {
-      if (lane_id() == 0) *cntp = (uint32_t)cnt;
-      tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
-      tau_v = tau_value(tau);
-      cnt = (int)__builtin_amdgcn_readfirstlane(*cntp);
+    if (maybe) {
+      const int slot = sc + lanes_below(mm);
+      sv_w[slot] = vv;
+      si_w[slot] = (uint32_t)sl.vec_index0(i);
     }
-    if (__builtin_popcountll(mm) <= SV_TOPK_LANE_APPEND) {
-      // Lanes outside mm hold no element >= tau_v (maybe covers validity).
-      cnt = topk_append_lanes<ET>(vv, mm, sl.vec_index0(i - lane_id()), tau, tau_v, bw, cnt);
-    } else {
-      cnt = topk_append<EPV>(f, (uint32_t)sl.vec_index0(i), valid ? full : 0u, tau, tau_v, bw, cnt);
-    }
-    if (cnt > trig) {
-      if (lane_id() == 0) *cntp = (uint32_t)cnt;
-      tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, false);
-      tau_v = tau_value(tau);
-      cnt = (int)__builtin_amdgcn_readfirstlane(*cntp);
-      // Next compaction once SV_TOPK_TRIG_STEP more keys arrived.
-      trig = max(K4 + SV_TOPK_TRIG_STEP, cnt + SV_TOPK_TRIG_STEP);
-    }
+    sc += __builtin_popcountll(mm);
+    if (sc >= kTopkStashFlush) flush();
   };
 
   // Warm start.  Every lane's largest element of the row's first batch is a
@@ -821,6 +816,7 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
 #endif
     }
   }
+  if (sc > 0) flush();
   // Each wave reduces to at most K keys, then the row's first wave merges.
   if (lane_id() == 0) *cntp = (uint32_t)cnt;
   tau = topk_compact<WPR>(bw, hw, cntp, qg, kg, wg, tau, K, kGuard, true);
