@@ -257,3 +257,16 @@ def test_full_size_every_request(sv, name):
     rep["near_tie_rows"] = ties
     print(f"[full] {name}: {rep}", flush=True)
     assert rep["mismatch_tie"] < 1e-4 * rows, f"near-tie exemptions used on {rep['mismatch_tie']} of {rows} rows"
+
+
+@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("entry,k,dtype", [("prob", 0, "f32"), ("prob", 64, "bf16"), ("prob", 300, "f32"),
+                                           ("onehot", 0, "bf16"), ("onehot", 64, "f32"), ("greedy", 0, "bf16")])
+def test_single_request(sv, entry, k, dtype, G):
+    """B = 1 (one workgroup's worth of rows, or fewer) and gamma = 1, at a
+    full-size vocabulary."""
+    name = {"prob": "prob_topk64_bf16_b1024_g8_v256000", "onehot": "onehot_bf16_b512_g3_v262144",
+            "greedy": "greedy_bf16_b64_g5_v128256"}[entry]
+    wl = W[name].scaled(B=1, G=G, dtype=dtype)
+    inp = workloads.generate(wl)
+    check(sv, entry, inp, T=wl.temperature if entry != "greedy" else 0.0, k=k, seed=13)
