@@ -183,6 +183,14 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 }
 // Orders this wave's LDS accesses: everything before completes before
 // anything after is issued (LDS is processed in order per wave).
+// LDS-qualified element types.  Helpers that take pointers to these compile
+// their accesses to ds_* instructions even when they are not inlined; through
+// a generic pointer they would be FLAT accesses, which also count as vector
+// memory operations, so every wait on them would wait for the row's pending
+// loads as well.
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+
 __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();

@@ -79,7 +79,8 @@ __device__ __forceinline__ void count_round(const Stats& st, int b, int g, int n
 
 // Bitonic sort of a[0, n) into descending order by one wave (n a power of
 // two; LDS).
-__device__ __forceinline__ void wave_sort_desc(uint64_t* a, int n) {
+template <typename PK>
+__device__ __forceinline__ void wave_sort_desc(PK a, int n) {
   const int lane = lane_id();
   for (int size = 2; size <= n; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -337,7 +338,8 @@ __global__ __launch_bounds__(NT) void rows_argmax_kernel(const ET* __restrict__ 
 // Returns a threshold t such that exactly K keys are >= t: the K-th largest
 // key itself, or (when the last examined digit bucket is taken whole) that
 // bucket's prefix with zero low bits.
-__device__ uint64_t wave_select_kth(const uint64_t* buf, int n, int K, uint32_t* hist) {
+template <typename PK, typename PH>
+__device__ uint64_t wave_select_kth(PK buf, int n, int K, PH hist) {
   const int lane = lane_id();
   uint64_t orv = 0, andv = ~0ull;
   for (int i = lane; i < n; i += kWave) {
@@ -361,7 +363,8 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int n, int K, uint32_t*
     wave_lds_sync();
     for (int i = lane; i < n; i += kWave) {
       const uint64_t k = buf[i];
-      if ((k & pmask) == prefix) atomicAdd(&hist[(uint32_t)(k >> shift) & 255u], 1u);
+      if ((k & pmask) == prefix)
+        __hip_atomic_fetch_add(&hist[(uint32_t)(k >> shift) & 255u], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
     wave_lds_sync();
     const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
@@ -411,7 +414,8 @@ __device__ uint64_t wave_select_kth(const uint64_t* buf, int n, int K, uint32_t*
 }
 
 // Keeps the keys >= thr, in order, in place; returns how many.
-__device__ int wave_keep_ge(uint64_t* buf, int n, uint64_t thr) {
+template <typename PK>
+__device__ int wave_keep_ge(PK buf, int n, uint64_t thr) {
   const int lane = lane_id();
   int out = 0;
   for (int base = 0; base < n; base += kWave) {
@@ -431,7 +435,8 @@ __device__ int wave_keep_ge(uint64_t* buf, int n, uint64_t thr) {
 // the bits above the highest bit where the keys' values differ, the next 8
 // bits of the bucket holding the r-th largest, and zeros below); 0 when
 // n < r.
-__device__ uint2 wave_coarse_select2(const uint64_t* buf, int n, int r1, int r2, uint32_t* hist) {
+template <typename PK, typename PH>
+__device__ uint2 wave_coarse_select2(PK buf, int n, int r1, int r2, PH hist) {
   const int lane = lane_id();
   uint32_t orv = 0u, andv = ~0u;
   for (int i = lane; i < n; i += kWave) {
@@ -451,7 +456,9 @@ __device__ uint2 wave_coarse_select2(const uint64_t* buf, int n, int r1, int r2,
   const uint32_t high = (shift + 8 >= 32) ? 0u : (~0u << (shift + 8));
   for (int bkt = lane; bkt < 256; bkt += kWave) hist[bkt] = 0u;
   wave_lds_sync();
-  for (int i = lane; i < n; i += kWave) atomicAdd(&hist[((uint32_t)(buf[i] >> 32) >> shift) & 255u], 1u);
+  for (int i = lane; i < n; i += kWave)
+    __hip_atomic_fetch_add(&hist[((uint32_t)(buf[i] >> 32) >> shift) & 255u], 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
   wave_lds_sync();
   const uint32_t h0 = hist[4 * lane + 0], h1 = hist[4 * lane + 1];
   const uint32_t h2 = hist[4 * lane + 2], h3 = hist[4 * lane + 3];
@@ -488,8 +495,8 @@ __device__ uint2 wave_coarse_select2(const uint64_t* buf, int n, int r1, int r2,
 // Lower bound of the row's K-th largest key from what the waves published:
 // every wave w retains >= ceil(K/NW) keys >= q[w], so >= K keys are >= min_w
 // q[w]; the publisher of kth retains K keys >= kth.
-template <int NW>
-__device__ __forceinline__ uint64_t shared_bound(uint64_t* q_sh, uint64_t* kth_sh) {
+template <int NW, typename PK>
+__device__ __forceinline__ uint64_t shared_bound(PK q_sh, PK kth_sh) {
   uint64_t mn = ~0ull;
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
@@ -505,10 +512,9 @@ __device__ __forceinline__ uint64_t shared_bound(uint64_t* q_sh, uint64_t* kth_s
 // is still above `guard` keys (or `exact` is set and it holds more than K),
 // the exact K-th largest is selected and published too.  Only keys below a
 // valid bound are ever dropped.
-template <int NW>
-__device__ SV_TOPK_COMPACT_INLINE uint64_t topk_compact(uint64_t* bw, uint32_t* hw, uint32_t* cntp, uint64_t* q_sh,
-                                              uint64_t* kth_sh, int w, uint64_t tau, int K, int guard,
-                                              bool exact) {
+template <int NW, typename PK, typename PH>
+__device__ SV_TOPK_COMPACT_INLINE uint64_t topk_compact(PK bw, PH hw, PH cntp, PK q_sh, PK kth_sh, int w, uint64_t tau,
+                                                       int K, int guard, bool exact) {
   const int lane = lane_id();
   const int K4 = (K + NW - 1) / NW;
   wave_lds_sync();
@@ -516,8 +522,8 @@ __device__ SV_TOPK_COMPACT_INLINE uint64_t topk_compact(uint64_t* bw, uint32_t* 
   if (!exact && n >= K4) {
     const uint2 q = wave_coarse_select2(bw, n, K4, K, hw);
     if (lane == 0) {
-      atomicMax((unsigned long long*)(q_sh + w), (unsigned long long)q.x << 32);
-      if (q.y) atomicMax((unsigned long long*)kth_sh, (unsigned long long)q.y << 32);
+      __hip_atomic_fetch_max(q_sh + w, (uint64_t)q.x << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (q.y) __hip_atomic_fetch_max(kth_sh, (uint64_t)q.y << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
   const uint64_t sb = shared_bound<NW>(q_sh, kth_sh);
@@ -525,14 +531,14 @@ __device__ SV_TOPK_COMPACT_INLINE uint64_t topk_compact(uint64_t* bw, uint32_t* 
   n = wave_keep_ge(bw, n, tau);
   if (n > guard || (exact && n > K)) {
     const uint64_t kth = wave_select_kth(bw, n, K, hw);
-    if (lane == 0) atomicMax((unsigned long long*)kth_sh, (unsigned long long)kth);
+    if (lane == 0) __hip_atomic_fetch_max(kth_sh, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     tau = kth > tau ? kth : tau;
     n = wave_keep_ge(bw, n, tau);
   }
   // The combined bound goes to one word that the streaming loop reads.
   if (lane == 0) {
     *cntp = (uint32_t)n;
-    atomicMax((unsigned long long*)(kth_sh + 1), (unsigned long long)tau);
+    __hip_atomic_fetch_max(kth_sh + 1, tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   wave_lds_sync();
   return tau;
@@ -551,9 +557,9 @@ __device__ __forceinline__ float tau_value(uint64_t tau) {
 
 // Appends this lane's elements with key > tau to the wave buffer at
 // positions from a ballot prefix count; returns the new (wave-uniform) count.
-template <int EPV>
+template <int EPV, typename PK>
 __device__ __forceinline__ int topk_append(const float* f, uint32_t idx0, uint32_t vmask, uint64_t tau, float tau_v,
-                                           uint64_t* bw, int cnt) {
+                                           PK bw, int cnt) {
 #pragma unroll
   for (int k = 0; k < EPV; ++k) {
     const bool cand = (vmask & (1u << k)) && f[k] >= tau_v;
@@ -606,7 +612,7 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   __shared__ uint64_t kth_sh[RPB][2];  // per row: best k-th bound; best combined bound
   __shared__ uint32_t cnt_sh[NW];
   __shared__ uint32_t lm_sh[RPB][WPR * kWave];
-  __shared__ uint4 stash_v[NW][kTopkStash];
+  __shared__ uint64_t stash_v[NW][2 * kTopkStash];  // 16-byte vectors as two words
   __shared__ uint32_t stash_i[NW][kTopkStash];
   const int tid = threadIdx.x, w = tid / kWave;
   const int g = w / WPR, wg = w % WPR, gtid = tid % GT;
@@ -633,11 +639,11 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   __syncthreads();
   if (!row_ok) rp = lt;  // not read: the slice is empty
   Slice<ET> sl(rp, 0, row_ok ? V : 0);
-  uint64_t* bw = buf[w];
-  uint32_t* hw = hist[w];
-  uint32_t* cntp = &cnt_sh[w];
-  uint64_t* qg = q_sh + g * WPR;
-  uint64_t* kg = kth_sh[g];
+  lds_u64* bw = (lds_u64*)buf[w];
+  lds_u32* hw = (lds_u32*)hist[w];
+  lds_u32* cntp = (lds_u32*)&cnt_sh[w];
+  lds_u64* qg = (lds_u64*)(q_sh + g * WPR);
+  lds_u64* kg = (lds_u64*)kth_sh[g];
   const int K4 = (K + WPR - 1) / WPR;
   int trig = K4 + SV_TOPK_TRIG_STEP;
   uint64_t tau = 0ull;
@@ -668,8 +674,8 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   // wave appends their keys > tau (the current tau: tau only rises, so every
   // key that beats the row's final bound was stashed and is appended).
   int sc = 0;  // stashed vectors (wave-uniform)
-  uint4* sv_w = stash_v[w];
-  uint32_t* si_w = stash_i[w];
+  lds_u64* sv_w = (lds_u64*)stash_v[w];
+  lds_u32* si_w = (lds_u32*)stash_i[w];
   auto flush = [&]() {
     wave_lds_sync();
     for (int e0 = 0; e0 < sc; e0 += kWave) {
@@ -677,7 +683,8 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
       float f[EPV];
       uint32_t idx0 = 0u, vm = 0u;
       if (e < sc) {
-        Elem<ET>::unpack(sv_w[e], f);
+        const uint64_t lo = sv_w[2 * e], hi = sv_w[2 * e + 1];
+        Elem<ET>::unpack(make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)), f);
         idx0 = si_w[e];
         vm = full;
       } else {
@@ -719,7 +726,8 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
     if (mm == 0ull) return;
     if (maybe) {
       const int slot = sc + lanes_below(mm);
-      sv_w[slot] = vv;
+      sv_w[2 * slot] = (uint64_t)vv.x | ((uint64_t)vv.y << 32);
+      sv_w[2 * slot + 1] = (uint64_t)vv.z | ((uint64_t)vv.w << 32);
       si_w[slot] = (uint32_t)sl.vec_index0(i);
     }
     sc += __builtin_popcountll(mm);
@@ -828,7 +836,7 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
   __syncthreads();
   if (lane_id() == 0) cnt_sh[w] = (uint32_t)mine;
   __syncthreads();
-  uint64_t* b0 = buf[g * WPR];
+  lds_u64* b0 = (lds_u64*)buf[g * WPR];
   if (wg > 0) {
     int off = 0;
     for (int k = 0; k < wg; ++k) off += (int)cnt_sh[g * WPR + k];
