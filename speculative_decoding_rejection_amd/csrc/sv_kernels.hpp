@@ -25,10 +25,6 @@
 #include "sv_device.hpp"
 
 // Build knobs of the top-k row pass (measured defaults).
-#ifndef SV_TOPK_PIPE
-#define SV_TOPK_PIPE 1  // 0: load a batch then filter it; 1: refill each slot after it is filtered;
-                        // 2: load the next batch before filtering this one
-#endif
 #ifndef SV_TOPK_COMPACT_INLINE
 #define SV_TOPK_COMPACT_INLINE __noinline__  // rare; kept out of the streaming loop's code
 #endif
@@ -323,14 +319,16 @@ __global__ __launch_bounds__(NT) void rows_argmax_kernel(const ET* __restrict__ 
 // ===========================================================================
 // Row pass 3: exact top-k in one read of the row.
 //
-// One workgroup (4 waves) per row; the waves stream interleaved 16-byte
-// vectors.  Each wave keeps the keys that beat a running threshold tau in its
-// own LDS buffer.  When the buffer would overflow, an exact radix select over
-// the buffer finds its K-th largest key, the buffer keeps exactly those K, and
-// tau rises to it.  tau is shared through LDS: every published value is the
-// K-th largest of K keys some wave retains, hence a lower bound of the row's
-// K-th largest key, so any wave may skip elements at or below it.  At the end
-// the surviving keys of the four waves are merged and selected once more.
+// WPR waves per row (RPB rows per workgroup) stream interleaved 16-byte
+// vectors.  A vector that may hold a key above the running threshold tau is
+// stashed in the wave's LDS; stashed vectors are appended in bulk to the
+// wave's key buffer, keeping only keys above the current tau.  Compactions
+// (a coarse histogram bound, or an exact radix select when the buffer is
+// nearly full) raise tau and publish bounds through LDS: every published
+// value has at least K retained keys at or above it, so it is a lower bound
+// of the row's K-th largest key and any wave may skip elements at or below
+// it.  At the end the surviving keys of the row's waves are merged, selected
+// once more and written in descending key order.
 // ===========================================================================
 
 // K-th largest of the n (> K) distinct keys in buf, by radix select over the
@@ -786,26 +784,10 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       filter(v[u], u * GT + gtid, packed, thr16);
-#if SV_TOPK_PIPE == 1
       if (sl.nvec > 0) v[u] = load_stream(vp + min(GT * U + u * GT + gtid, sl.nvec - 1));
-#endif
     }
   }
-#if SV_TOPK_PIPE == 2
-  if (sl.nvec > 0) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = load_stream(vp + min(GT * U + u * GT + gtid, sl.nvec - 1));
-  }
-#endif
   for (int i0 = GT * U; i0 < sl.nvec; i0 += GT * U) {
-#if SV_TOPK_PIPE == 0
-#pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = load_stream(vp + min(i0 + u * GT + gtid, sl.nvec - 1));
-#elif SV_TOPK_PIPE == 2
-    uint4 nxt[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) nxt[u] = load_stream(vp + min(i0 + GT * U + u * GT + gtid, sl.nvec - 1));
-#endif
     {
       const uint64_t sb = __hip_atomic_load(kg + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
       if (sb > tau) tau = sb;
@@ -816,12 +798,8 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       filter(v[u], i0 + u * GT + gtid, packed, thr16);
-#if SV_TOPK_PIPE == 1
       // Past the end the request repeats the last vector (one cache line).
       v[u] = load_stream(vp + min(i0 + GT * U + u * GT + gtid, sl.nvec - 1));
-#elif SV_TOPK_PIPE == 2
-      v[u] = nxt[u];
-#endif
     }
   }
   if (sc > 0) flush();
