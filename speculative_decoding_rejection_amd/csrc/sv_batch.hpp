@@ -264,8 +264,8 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 }
 
 // ===========================================================================
-// Nucleus of a full row (no top-k): one 1024-thread workgroup per row, after the softmax
-// row pass (whose partials give the row's largest logit).
+// Nucleus of a full row (no top-k): one workgroup per row (NucShape below),
+// after the softmax row pass (whose partials give the row's largest logit).
 //
 //   pass 1  fp64 mass of every token; the total Z; a histogram of mass over
 //           bins of the gap d = (l_max - l) / T, ln2 / 64 nats per bin over
