@@ -261,8 +261,10 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  * Streams: the row passes of the different kinds of request run side by
  * side.  The call records an event on `stream`, the top-k rows and the
  * temperature-0 rows are streamed on two library-owned streams of the current
- * device that wait for it (created on the first batch call on that device,
- * non-blocking, default priority, kept until the process ends), and `stream`
+ * device that wait for it (created on the first batch call on that device
+ * that is not being captured into a graph, non-blocking, default priority,
+ * kept until the process ends; until then the row passes run on `stream`
+ * one after another), and `stream`
  * waits for both before the accept passes: stream order is unchanged, and a
  * capture of `stream` takes the two streams in.  Calls from several host
  * threads are serialised while they enqueue this fork and join. */

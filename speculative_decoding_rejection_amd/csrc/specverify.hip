@@ -229,13 +229,20 @@ struct SideStreams {
 std::mutex g_side_mu;
 std::map<int, SideStreams> g_side;
 
-// With g_side_mu held.  Null if the streams cannot be made (then the row
-// phase runs on the caller's stream alone, and a later call tries again).
-SideStreams* side_streams() {
+// With g_side_mu held.  Null if the streams do not exist and cannot be made
+// now (then the row phase runs on the caller's stream alone, and a later call
+// tries again): they are not created while `st` is being captured into a
+// graph, so that a capture is never disturbed by their creation.
+SideStreams* side_streams(hipStream_t st) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   auto it = g_side.find(dev);
   if (it != g_side.end()) return &it->second;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
   SideStreams ss;
   bool ok = true;
   for (int i = 0; i < 2 && ok; ++i) ok = hipStreamCreateWithFlags(&ss.s[i], hipStreamNonBlocking) == hipSuccess;
@@ -467,7 +474,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     // stream.  The three write disjoint parts of the workspace.
     TimedLaunch t(0, st);
     std::unique_lock<std::mutex> lock(g_side_mu);
-    SideStreams* side = side_streams();
+    SideStreams* side = side_streams(st);
     hipStream_t s_topk = st, s_arg = st;
     if (side && hipEventRecord(side->fork, st) == hipSuccess &&
         hipStreamWaitEvent(side->s[0], side->fork, 0) == hipSuccess &&

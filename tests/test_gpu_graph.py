@@ -5,6 +5,8 @@ replayed several times, with other eager calls and synchronisations between
 the replays.  The draws are counter-based (seed, request, position, token),
 so every replay must reproduce the eager result bit for bit."""
 
+import os
+
 import pytest
 import torch
 
@@ -79,3 +81,46 @@ def test_single_setting_call_in_graph(sv):
 
     print(f"[graph] prob B={wl.B} V={wl.V} top_k={wl.top_k}", flush=True)
     _capture_and_replay(call, ("out_tokens", "num_accepted", "p_draft", "q_draft"))
+
+
+def test_first_batch_call_under_capture():
+    """A process whose first batch call is captured: the library does not
+    create its side streams during the capture (the row passes then run on
+    the captured stream), the capture succeeds, and its replays equal an
+    eager call made afterwards (which creates the streams).  Runs in a child
+    process so that no earlier call has created the streams."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = r'''
+import sys, torch
+sys.path.insert(0, sys.argv[1])
+import speculative_decoding_rejection_amd as sv, workloads
+sv.load_library()
+dev = torch.device("cuda:0")
+wl = workloads.BATCH_WORKLOADS["batch_mixed_f32_b256_g7_v151936"].scaled(B=16, V=20011)
+inp = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in workloads.generate(wl).items()}
+mk = max(k for _, k, _ in wl.mix)
+nbytes = sv.sv_workspace_bytes_batch(sv.make_params(16, wl.G, wl.V, torch.float32, 1.0, 0, 3),
+                                     sv.make_sampling(inp["temperature"], inp["top_k"], inp["top_p"], mk))
+ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+def call(w):
+    return sv.verify_batch(inp["target_logits"], inp["draft_tokens"], inp["draft_logits"],
+                           temperature=inp["temperature"], top_k=inp["top_k"], top_p=inp["top_p"],
+                           max_top_k=mk, seed=3, beta=True, workspace=w)
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):
+    res = call(ws)
+eager = call(torch.empty_like(ws))
+torch.cuda.synchronize()
+for rep in range(3):
+    g.replay()
+    torch.cuda.synchronize()
+    for k in ("out_tokens", "num_accepted", "p_draft", "q_draft", "beta"):
+        assert torch.equal(res[k], eager[k]), (rep, k)
+print("first-capture ok", flush=True)
+'''
+    r = subprocess.run([sys.executable, "-c", code, root], capture_output=True, text=True, timeout=240)
+    print(r.stdout[-2000:], r.stderr[-2000:], flush=True)
+    assert r.returncode == 0 and "first-capture ok" in r.stdout
