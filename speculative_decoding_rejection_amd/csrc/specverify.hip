@@ -21,7 +21,7 @@ using sv::RowCut;
 constexpr int kRowThreads = 256;
 constexpr int kRowUnroll = 4;
 #ifndef SV_TOPK_UNROLL
-#define SV_TOPK_UNROLL 8
+#define SV_TOPK_UNROLL 12
 #endif
 constexpr int kTopkUnroll = SV_TOPK_UNROLL;
 constexpr int kMaxTopK = 1024;
