@@ -500,7 +500,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
     if (rs == SV_OK && nuc)
-      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(sv::NucShape<ET>::NT), 0, st, (const ET*)lt,
+      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(sv::NucShape::NT), 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
     if (rs == SV_OK) rs = check_launch();

@@ -284,19 +284,13 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 // Each pass streams the row from HBM.
 // ===========================================================================
 constexpr int kNucBins = 4096;  // ln2 / 64 nats each: gaps below 44.4 nats
-// One workgroup per row.  Workgroup size and vectors per thread and chunk,
-// by logit type (measured on MI355X): bf16 rows carry twice the tokens per
-// vector, and their pass is bound by the per-token work, so more, lighter
-// waves; fp32 rows take deeper chunks.
-template <typename ET>
-struct NucShape;
-template <>
-struct NucShape<float> {
-  static constexpr int NT = 256, U = 4;
-};
-template <>
-struct NucShape<uint16_t> {
-  static constexpr int NT = 512, U = 1;
+// One workgroup per row: 512 threads, two vectors per thread and chunk.
+// Measured on MI355X with the row passes of the kinds running side by side:
+// against 256 / 512 / 1024 threads and 1 / 2 / 4 vectors (by logit type, and
+// with a larger shape for calls with few rows), this one shape was the
+// fastest or within 1% on the mixed, ragged and sampler-match workloads.
+struct NucShape {
+  static constexpr int NT = 512, U = 2;
 };
 constexpr int kCutThreads = 512;  // kcut_full_kernel
 constexpr int kNucCap = 2048;
@@ -377,12 +371,12 @@ __device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
 }
 
 template <typename ET>
-__global__ __launch_bounds__(NucShape<ET>::NT) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+__global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                            int rows_t, int G, int V, int S,
                                                            const float2* __restrict__ part,
                                                            const ReqInfo* __restrict__ info,
                                                            RowCut* __restrict__ cut, Layout L) {
-  constexpr int NT = NucShape<ET>::NT, U = NucShape<ET>::U, NW = NT / kWave, PER = kNucBins / NT;
+  constexpr int NT = NucShape::NT, U = NucShape::U, NW = NT / kWave, PER = kNucBins / NT;
   static_assert(kNucBins % NT == 0, "bins per thread");
   static_assert(kNucCap * sizeof(uint64_t) <= kNucBins * sizeof(double), "keys alias the histogram");
   const int row = blockIdx.x;
