@@ -279,7 +279,9 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
 sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream);
 
 /* Per-kernel timing for measurement.  While enabled, every launch of the
- * library is bracketed by a pair of HIP events on the caller's stream;
+ * library is bracketed by a pair of HIP events on the caller's stream (in a
+ * spec_verify_batch call the row passes are bracketed as one span, from the
+ * fork to the join);
  * sv_kernel_timing_read synchronises on the recorded events and returns the
  * summed device time (ms) and launch count of one kernel family:
  *   0 = row pass (softmax / top-k / argmax over every logit row),
