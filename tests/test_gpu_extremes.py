@@ -3,7 +3,7 @@ million tokens (1,000,003: a ragged tail after every split, key indices
 above 2^19) and many tiny requests (40,000 requests over a vocabulary of 37:
 request-level grids far larger than any workload's, and rows shorter than a
 wave), for every entry point and, for the batch call, per-request settings
-with top-k and top-p."""
+with top-k and top-p; and the largest draft length the library takes."""
 
 import numpy as np
 import pytest
@@ -80,3 +80,19 @@ def test_many_tiny_requests_batch(sv):
     print(f"[extreme]   {assert_parity_batch(got, ref)}", flush=True)
     both = ~np.isnan(ref["beta"])
     assert float(np.abs(got["beta"][both] - ref["beta"][both]).max()) <= 1e-5
+
+
+@pytest.mark.parametrize("entry,k", [("prob", 0), ("prob", 16), ("onehot", 16), ("greedy", 0)])
+def test_largest_gamma(sv, entry, k):
+    """gamma = 16384, the largest supported (the top-k accept pass keeps one
+    flag per position in LDS), over a short vocabulary; draft rows equal to
+    the target's so that long accepted runs occur."""
+    name = {"prob": "prob_f32_b8_g4_v32000", "onehot": "onehot_bf16_b512_g3_v262144",
+            "greedy": "greedy_bf16_b64_g5_v128256"}[entry]
+    wl = W[name].scaled(B=2, G=16384, V=41)
+    inp = workloads.generate(wl)
+    if entry == "prob":
+        inp["draft_logits"] = inp["target_logits"][:, :-1].clone()
+    T = wl.temperature if entry != "greedy" else 0.0
+    print(f"[extreme] {entry} k={k} gamma=16384 V=41", flush=True)
+    print(f"[extreme]   {single(sv, entry, inp, T, k, 24)}", flush=True)
