@@ -9,7 +9,10 @@ generated on the GPU and resident in HBM before the timed region.
 Prints one JSON line: verified draft positions per second (value), plus
 rows/s, algorithmic GB/s, the roofline of the dominant kernel (the row pass,
 timed with HIP events on the launch stream) and the fp64 CPU oracle timed on
-a bounded sample of the same workload on the host cores.
+a bounded sample of the same workload on the host cores, with the oracle's
+check of the GPU's outputs on the first requests, and the method's outcome on
+the batch (law of the accepted length, tokens per round, beta per position
+and Eq. 1's prediction from it).
 """
 
 from __future__ import annotations
@@ -53,13 +56,20 @@ def load_traffic(workload: str, per_launch_alg: float):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, target_seconds: float) -> dict:
+def cpu_baseline(wl, inp, target_seconds: float, got: dict | None = None, check_requests: int = 32) -> dict:
+    """The fp64 oracle timed on the first requests of the workload (sized to
+    about target_seconds of host time).  With got (the GPU's outputs of the
+    same call, per request, host arrays), an untimed diagnostics pass over
+    the first check_requests of them compares the two: largest |dp| and |dq|
+    of the gathered probabilities, near-tie rows, and requests that differ
+    (outside near-ties, and within them)."""
     import oracle
     import workloads
+    from oracle.parity import compare, compare_batch, near_tie_rows
 
     modes = {"prob": oracle.MODE_PROB, "onehot": oracle.MODE_ONEHOT, "greedy": oracle.MODE_GREEDY}
 
-    def run(n):
+    def run(n, diagnostics=False):
         sub = slice(0, n)
         lt = workloads.to_host_arrays(inp["target_logits"][sub])
         ld = workloads.to_host_arrays(inp["draft_logits"][sub]) if wl.has_draft_logits else None
@@ -69,21 +79,33 @@ def cpu_baseline(wl, inp, target_seconds: float) -> dict:
             probs = inp["draft_probs"][sub].cpu().numpy() if wl.draft_probs else None
             lens = inp["lengths"][sub].cpu().numpy() if wl.lengths else None
             par = inp["parents"][sub].cpu().numpy() if inp.get("parents") is not None else None
-            oracle.verify_batch(lt, None if wl.draft_probs else ld, x, inp["temperature"][sub].cpu().numpy(),
-                                inp["top_k"][sub].cpu().numpy(), inp["top_p"][sub].cpu().numpy(),
-                                max_top_k=max(k for _, k, _ in wl.mix), seed=wl.verify_seed, draft_probs=probs,
-                                lengths=lens, match=wl.entry == "match", parents=par)
+            ref = oracle.verify_batch(lt, None if wl.draft_probs else ld, x, inp["temperature"][sub].cpu().numpy(),
+                                      inp["top_k"][sub].cpu().numpy(), inp["top_p"][sub].cpu().numpy(),
+                                      max_top_k=max(k for _, k, _ in wl.mix), seed=wl.verify_seed,
+                                      draft_probs=probs, lengths=lens, match=wl.entry == "match", parents=par,
+                                      diagnostics=diagnostics)
         else:
-            oracle.verify(modes[wl.entry], lt, ld, x, temperature=wl.temperature, top_k=wl.top_k,
-                          seed=wl.verify_seed)
-        return time.perf_counter() - t0
+            ref = oracle.verify(modes[wl.entry], lt, ld, x, temperature=wl.temperature, top_k=wl.top_k,
+                                seed=wl.verify_seed, diagnostics=diagnostics and wl.entry != "greedy")
+        return time.perf_counter() - t0, ref
 
     threads = oracle.max_threads()
     n = min(wl.B, max(4, threads))
-    t = run(n)
+    t, _ = run(n)
     if t < target_seconds / 3 and n < wl.B:
         n = int(min(wl.B, max(n + 1, n * target_seconds / max(t, 1e-3))))
-        t = run(n)
+        t, _ = run(n)
+    check = None
+    if got is not None:
+        m = min(wl.B, check_requests)
+        _, ref = run(m, diagnostics=True)
+        sub = {k: v[:m] for k, v in got.items()}
+        rep = compare_batch(sub, ref) if wl.has_settings else compare(wl.entry, sub, ref)
+        check = {"requests": m, "rows": rep["rows"], "max_dp": rep["max_dp"], "max_dq": rep["max_dq"],
+                 "near_tie_rows": near_tie_rows(ref), "near_tie_requests": rep["near_tie_requests"],
+                 "mismatch_non_tie": rep["mismatch_non_tie"], "mismatch_tie": rep["mismatch_tie"]}
+        if "near_cut_requests" in rep:
+            check["near_cut_requests"] = rep["near_cut_requests"]
     return {
         "value": int(wl.draft_lengths[:n].sum()) / t,
         "unit": "verified draft positions/s",
@@ -91,6 +113,7 @@ def cpu_baseline(wl, inp, target_seconds: float) -> dict:
         "kind": "oracle",
         "sample": f"first {n} of {wl.B} requests of the same workload (fp64 oracle, OpenMP over requests), "
                   f"{t:.2f} s wall",
+        "check": check,
     }
 
 
@@ -181,7 +204,7 @@ def main():
 
     params = sv.make_params(wl.B, wl.G, wl.V, wl.torch_dtype, wl.temperature or 1.0, wl.top_k, wl.verify_seed)
     sampling = layout = None
-    padded = inp
+    dense_inp = inp
     if wl.has_settings:
         sampling = sv.make_sampling(inp["temperature"], inp["top_k"], inp["top_p"], max(k for _, k, _ in wl.mix))
         ws = torch.empty(sv.sv_workspace_bytes_batch(params, sampling), dtype=torch.uint8, device=dev)
@@ -203,7 +226,7 @@ def main():
             draft = src["draft_probs"] if wl.draft_probs else src["draft_logits"]
             layout = sv.SvLayout(sv.SV_DRAFT_PROBS if wl.draft_probs else sv.SV_DRAFT_LOGITS, 0, wl.V, wl.V,
                                  sv._ptr(src["cu_draft"]) if wl.lengths else None)
-            padded = inp
+            dense_inp = inp
             inp = dict(inp, target_logits=src["target_logits"], draft_logits=draft,
                        draft_tokens=src["draft_tokens"], cu_draft=src.get("cu_draft"))
             torch.cuda.synchronize()
@@ -263,6 +286,75 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 copies of 1 GiB done")
 
+    # What the method did on this batch (untimed): the law of n from the
+    # last timed call, and beta = sum min(p, q) per position from one more
+    # call of the same inputs with beta requested (a uniform batch call is
+    # bit-identical to the single-setting entry points).
+    import numpy as np
+    n_gpu = nacc.cpu().numpy()
+    g_req = wl.draft_lengths if wl.has_settings else np.full(B, G)
+    beta_t = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    o2 = [torch.empty_like(out), torch.empty_like(nacc), torch.empty_like(pd), torch.empty_like(qd)]
+    if wl.has_settings:
+        pn2 = torch.empty_like(pn) if pn is not None else None
+        sv.spec_verify_batch(params, sampling, layout, lt, ld, x,
+                             sv.make_outputs(*o2, beta=beta_t, path_nodes=pn2), ws, stream)
+    else:
+        bparams = sv.make_params(B, G, wl.V, wl.torch_dtype, wl.temperature if wl.entry != "greedy" else 0.0,
+                                 wl.top_k, wl.verify_seed)
+        bws = torch.empty(sv.sv_workspace_bytes_batch(bparams, None), dtype=torch.uint8, device=dev)
+        bdraft = ld if wl.entry == "prob" else None
+        blay = sv.SvLayout(sv.SV_DRAFT_LOGITS if bdraft is not None else sv.SV_DRAFT_ONEHOT, 0, wl.V,
+                           wl.V if bdraft is not None else 0, None, None)
+        sv.spec_verify_batch(bparams, None, blay, lt, bdraft, x, sv.make_outputs(*o2, beta=beta_t), bws, stream)
+    torch.cuda.synchronize()
+    beta_flat = beta_t.cpu().numpy()
+    beta_pad = np.full((B, G), np.nan)
+    if wl.lengths or beta_flat.ndim == 1:
+        off = 0
+        for b in range(B):
+            beta_pad[b, :g_req[b]] = beta_flat[off:off + g_req[b]]
+            off += g_req[b]
+    else:
+        beta_pad[:] = beta_flat
+    bmean = np.nanmean(beta_pad, axis=0)
+    reach = np.array([(n_gpu >= j).sum() for j in range(G + 1)], dtype=np.float64)
+    outcome = {"n_histogram": np.bincount(n_gpu, minlength=G + 1).tolist(),
+               "tokens_per_round": float((n_gpu + 1).mean()),
+               "acceptance_by_position": [float((n_gpu > j).sum() / reach[j]) if reach[j] else None
+                                          for j in range(G)],
+               "beta_by_position": [float(v) for v in bmean],
+               "mean_beta": float(np.nanmean(beta_pad)),
+               "beta_call_same_n": bool((o2[1].cpu().numpy() == n_gpu).all())}
+    if not wl.parents:
+        # Eq. 1 of the draft-model page with each request's own per-position
+        # rates: given its rows, position j of request b accepts with
+        # probability beta[b, j], independently of the others, so
+        # E[n_b + 1] = sum over i <= g_b of prod_{j < i} beta[b, j].  (The
+        # same sum over the batch-mean rates is lower whenever a request's
+        # rates rise and fall together, as they do with a per-request draft
+        # noise.)
+        cp = np.cumprod(np.nan_to_num(beta_pad, nan=0.0), axis=1)
+        per_req = 1.0 + np.array([cp[b, :g_req[b]].sum() for b in range(B)])
+        outcome["tokens_per_round_eq1"] = float(per_req.mean())
+
+    # The GPU's outputs per request, for the oracle check of the CPU leg.
+    got = {"out_tokens": out.cpu().numpy(), "num_accepted": n_gpu}
+    if wl.entry == "greedy" and not wl.has_settings:
+        got["target_argmax"] = ta.cpu().numpy()
+    elif wl.entry != "greedy":
+        for key, t in (("p_draft", pd), ("q_draft", qd)):
+            if key == "q_draft" and wl.entry == "onehot" and not wl.has_settings:
+                continue
+            flat = t.cpu().numpy()
+            if flat.ndim == 1:  # packed ragged rows back to [B, G]
+                dense, off = np.full((B, G), np.nan, np.float32), 0
+                for b in range(B):
+                    dense[b, :g_req[b]] = flat[off:off + g_req[b]]
+                    off += g_req[b]
+                flat = dense
+            got[key] = flat
+
     sec = wall / args.steps
     positions = int(wl.draft_lengths.sum()) if wl.has_settings else B * G
     rows = wl.target_rows + wl.draft_rows
@@ -276,7 +368,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(wl, padded, args.cpu_seconds)
+        cpu = cpu_baseline(wl, dense_inp, args.cpu_seconds, got=got)
     res = {
         "metric": "verified draft positions/sec and HBM GB/s (% of peak) at B=1024,gamma=8,V=256k",
         "value": positions / sec,
@@ -310,6 +402,7 @@ def main():
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic},
         "cpu_baseline": cpu,
+        "outcome": outcome,
     }
     if args.rounds:
         log(f"[bench] multi-round driver: {args.rounds} rounds")
