@@ -43,6 +43,10 @@ struct Plan {
   size_t off_err, off_part, off_cand, off_desc, off_slots, off_info, off_cut, total;
   int Srr, segrr;                           // row-race splits (sampler-match)
   size_t off_rdesc, off_rslots, off_samples;  // per-row race descriptors, slots, samples
+  // Nucleus of few rows split across workgroups: plan, row list, chunk
+  // histograms, per-row state, collected keys (batch calls with top-p).
+  size_t off_nplan = 0, off_nlist = 0, off_nhist = 0, off_nstate = 0, off_nkeys = 0;
+  int nuc_rows = 0, nuc_items = 0;  // grids of the per-row and per-chunk passes
   sv::Layout L;   // rows, tokens, outputs (dense: rows V apart, every request G positions)
   bool big_k;     // batch plans: a top-k above kcap is possible (full-row cut)
 };
@@ -169,6 +173,22 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   off = align_up(off + (size_t)pl->rows_t * 3 * 8, kWsAlign);
   pl->off_samples = off;
   off = align_up(off + (size_t)pl->rows_t * 4, kWsAlign);
+  if (sm && sm->top_p) {
+    const int nr = pl->rows_t + pl->rows_d;
+    pl->nuc_rows = nr < sv::kNucSplitRows ? nr : sv::kNucSplitRows;
+    const int64_t items = (int64_t)pl->nuc_rows * sv::kNucMaxSplit;
+    pl->nuc_items = items < sv::kNucItems ? (int)items : sv::kNucItems;
+    pl->off_nplan = off;
+    off = align_up(off + 4 * sizeof(int), kWsAlign);
+    pl->off_nlist = off;
+    off = align_up(off + (size_t)nr * sizeof(int), kWsAlign);
+    pl->off_nhist = off;
+    off = align_up(off + (size_t)pl->nuc_items * sv::kNucPartStride * sizeof(double), kWsAlign);
+    pl->off_nstate = off;
+    off = align_up(off + (size_t)pl->nuc_rows * sizeof(sv::NucState), kWsAlign);
+    pl->off_nkeys = off;
+    off = align_up(off + (size_t)pl->nuc_rows * sv::kNucCap * sizeof(uint64_t), kWsAlign);
+  }
   pl->total = off;
   return SV_OK;
 }
@@ -462,8 +482,9 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     TimedLaunch t(0, st);
     hipLaunchKernelGGL(sv::classify_kernel, dim3(1), dim3(1024), 0, st, ba.T, ba.K, ba.P, ba.T0, ba.K0, pl.B, pl.G,
                        pl.V, ba.max_top_k, pl.kcap, pl.L, MODE == 3 ? ba.parents : (const int32_t*)nullptr, info,
-                       err, out,
-                       nacc, p_draft, q_draft, beta);
+                       err, out, nacc, p_draft, q_draft, beta, MODE == 0 ? 1 : 0,
+                       nuc ? (int*)(ws + pl.off_nplan) : (int*)nullptr,
+                       nuc ? (int*)(ws + pl.off_nlist) : (int*)nullptr);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
@@ -499,10 +520,32 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       hipLaunchKernelGGL((sv::kcut_full_kernel<ET>), dim3(nrows), dim3(sv::kCutThreads), 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
                          (const ReqInfo*)info, cut, pl.L);
-    if (rs == SV_OK && nuc)
-      hipLaunchKernelGGL((sv::nucleus_full_kernel<ET>), dim3(nrows), dim3(sv::NucShape::NT), 0, st, (const ET*)lt,
-                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, (const float2*)(ws + pl.off_part),
-                         (const ReqInfo*)info, cut, pl.L);
+    if (rs == SV_OK && nuc) {
+      // The classify pass listed the top-p rows and picked one workgroup per
+      // row or, for few rows, rows split across workgroups (the part pass's
+      // grid covers both); the passes of the other path exit at once.
+      int* nplan = (int*)(ws + pl.off_nplan);
+      int* nlist = (int*)(ws + pl.off_nlist);
+      double* nhist = (double*)(ws + pl.off_nhist);
+      sv::NucState* nstate = (sv::NucState*)(ws + pl.off_nstate);
+      uint64_t* nkeys = (uint64_t*)(ws + pl.off_nkeys);
+      const float2* sp = (const float2*)(ws + pl.off_part);
+      const dim3 nt(sv::NucShape::NT);
+      hipLaunchKernelGGL((sv::nucleus_part_kernel<ET>), dim3(pl.nuc_items > nrows ? pl.nuc_items : nrows), nt, 0,
+                         st, (const ET*)lt,
+                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, sp, (const ReqInfo*)info, cut, pl.L,
+                         (const int*)nplan, (const int*)nlist, nhist);
+      hipLaunchKernelGGL(sv::nucleus_scan_kernel, dim3(pl.nuc_rows), nt, 0, st, pl.rows_t, pl.G, pl.S, sp,
+                         (const ReqInfo*)info, cut, (const int*)nplan, (const int*)nlist, (const double*)nhist,
+                         nstate);
+      hipLaunchKernelGGL((sv::nucleus_collect_kernel<ET>), dim3(pl.nuc_items), nt, 0, st, (const ET*)lt,
+                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, sp, (const ReqInfo*)info, pl.L,
+                         (const int*)nplan, (const int*)nlist, nstate, nkeys);
+      hipLaunchKernelGGL((sv::nucleus_finish_kernel<ET>), dim3(pl.nuc_rows), nt, 0, st, (const ET*)lt,
+                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, sp, (const ReqInfo*)info, cut, pl.L,
+                         (const int*)nplan, (const int*)nlist, (const sv::NucState*)nstate,
+                         (const uint64_t*)nkeys);
+    }
     if (rs == SV_OK) rs = check_launch();
     if (s_topk != st) {
       // Join (also after a failed launch): the caller's stream waits for

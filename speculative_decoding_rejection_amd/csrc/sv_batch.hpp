@@ -83,6 +83,18 @@ __device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, in
   return ok ? e : 0.0;
 }
 
+// Paths of the nucleus passes over full rows (below): with at most
+// kNucSplitRows rows with top-p in a call, each row is cut into NS =
+// min(kNucMaxSplit, kNucItems / rows) chunks; with more, one workgroup per
+// row.  plan = {rows, NS} (NS = 1: one workgroup per row).
+constexpr int kNucSplitRows = 512, kNucItems = 1024, kNucMaxSplit = 16;
+__device__ __forceinline__ void plan_nucleus(int n, int* plan) {
+  int ns = 1;
+  if (n > 0 && n <= kNucSplitRows) ns = kNucItems / n < kNucMaxSplit ? kNucItems / n : kNucMaxSplit;
+  plan[0] = n;
+  plan[1] = ns;
+}
+
 // ===========================================================================
 // Classify pass: one workgroup reads the per-request settings (or, where an
 // array is null, the call's single setting T0 / K0 / top_p 1), validates
@@ -100,11 +112,13 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
                                                         ReqInfo* __restrict__ info, int* __restrict__ err,
                                                         int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                                         float* __restrict__ p_draft, float* __restrict__ q_draft,
-                                                        float* __restrict__ beta) {
-  __shared__ int bad_layout;
+                                                        float* __restrict__ beta, int draft_rows,
+                                                        int* __restrict__ nplan, int* __restrict__ nlist) {
+  __shared__ int bad_layout, nlisted;
   if (threadIdx.x == 0) {
     atomicExch(err, 0);
     bad_layout = 0;
+    nlisted = 0;
   }
   __syncthreads();
   if (L.cu) {
@@ -154,6 +168,15 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
       }
     }
     info[b] = r;
+    if (nlist && r.kind == kReqFull && r.top_p < 1.f) {
+      // The request's rows that take a nucleus (any order: rows are
+      // independent): target rows 0..g, and its draft logit rows.
+      const int g = L.len(b, G), nr = g + 1 + (draft_rows ? g : 0);
+      const int at = atomicAdd(&nlisted, nr);
+      for (int j = 0; j <= g; ++j) nlist[at + j] = b * (G + 1) + j;
+      if (draft_rows)
+        for (int j = 0; j < g; ++j) nlist[at + g + 1 + j] = B * (G + 1) + b * G + j;
+    }
     if (!ok) {
       if (!all_bad) atomicOr(err, kErrBadParam);
       for (int j = 0; j <= G; ++j) out[(size_t)b * (G + 1) + j] = -1;
@@ -166,6 +189,13 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
           if (beta) beta[L.tok(b, G, j)] = 0.f;
         }
       }
+    }
+  }
+  if (nplan) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int n = nlisted;
+      plan_nucleus(n, nplan);
     }
   }
 }
@@ -308,10 +338,11 @@ __device__ __forceinline__ int nucleus_bin(double lm, float l, double it) {
 // scalar head and tail.  Chunks of U vectors per thread; the next chunk's
 // loads are issued before the current one is processed, so a wave's memory
 // requests stay in flight while it computes.
+// Elements [a, e) of the row (indices as in the whole row).
 template <typename ET, int NT, int U, typename FV, typename FS>
-__device__ __forceinline__ void row_stream(const ET* rp, int V, FV&& fv, FS&& fs) {
+__device__ __forceinline__ void row_stream(const ET* rp, int a, int e, FV&& fv, FS&& fs) {
   constexpr int EPV = Elem<ET>::kPerVec, STEP = NT * U;
-  Slice<ET> sl(rp, 0, V);
+  Slice<ET> sl(rp, a, e);
   const int tid = threadIdx.x;
   if (tid < sl.nscalar()) {
     const int y = sl.scalar_index(tid);
@@ -357,6 +388,11 @@ __device__ __forceinline__ void row_stream(const ET* rp, int V, FV&& fv, FS&& fs
     if (i0 + u * NT < nv) proc(v[u], i0 + u * NT);
 }
 
+template <typename ET, int NT, int U, typename FV, typename FS>
+__device__ __forceinline__ void row_stream(const ET* rp, int V, FV&& fv, FS&& fs) {
+  row_stream<ET, NT, U>(rp, 0, V, fv, fs);
+}
+
 // Calls f(logit, index) for every element of the row this thread owns.
 template <typename ET, int NT, int U, typename F>
 __device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
@@ -370,16 +406,142 @@ __device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
       f);
 }
 
+// The gap histogram of the nucleus passes (+ the spare slot of tokens
+// without a bin), one LDS array per kernel; dead once the cut bin is chosen,
+// it then holds the collected keys of that bin.
+__device__ __forceinline__ double* nucleus_hist_lds() {
+  __shared__ double hm[kNucBins + 1];
+  return hm;
+}
+
+// Largest logit of a row, from the softmax pass's partials (every lane of
+// every wave gets it).
+__device__ __forceinline__ float nucleus_lmax(const float2* part, int row, int S) {
+  float lmax = -INFINITY;
+  for (int k = lane_id(); k < S; k += kWave) lmax = fmaxf(lmax, part[(size_t)row * S + k].x);
+  return wave_max_f(lmax);
+}
+
+// Pass 1 over elements [a, e) of a row: adds each token's mass
+// exp((l - lm) * it) to the LDS histogram of its gap bin (hm[kNucBins]: the
+// spare slot of tokens without a bin) and returns this thread's sum of the
+// masses.  The gap is the negated exponent, so mass and bin come from one
+// product.  Branch-free: with FLOOR, a token whose key is below kfloor adds 0.
+template <typename ET, int NT, int U, bool FLOOR>
+__device__ __forceinline__ double nucleus_pass1(const ET* rp, int a, int e, double lm, double it, uint64_t kfloor,
+                                                const double* tab, double* hm) {
+  double zt = 0.0;
+  auto mass_bin = [&](float l, int y, uint32_t& bin) -> double {
+    int k;
+    double m = exp_nonpos_f64(((double)l - lm) * it, tab, &k);
+    if (FLOOR) m = make_key(l, (uint32_t)y) < kfloor ? 0.0 : m;
+    bin = min((uint32_t)(-k), (uint32_t)kNucBins);
+    return m;
+  };
+  row_stream<ET, NT, U>(
+      rp, a, e,
+      [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
+        // Masses and bins of the vector's tokens first (independent chains
+        // the scheduler interleaves), then the histogram adds.
+        constexpr int EPV = Elem<ET>::kPerVec;
+        double m[EPV];
+        uint32_t bin[EPV];
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) m[k] = mass_bin(fv[k], y0 + k, bin[k]);
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) atomicAdd(&hm[bin[k]], m[k]);
+#pragma unroll
+        for (int w2 = 1; w2 < EPV; w2 *= 2)
+#pragma unroll
+          for (int k = 0; k + w2 < EPV; k += 2 * w2) m[k] += m[k + w2];
+        zt += m[0];
+      },
+      [&](float l, int y) {
+        uint32_t bin;
+        const double m = mass_bin(l, y, bin);
+        atomicAdd(&hm[bin], m);
+        zt += m;
+      });
+  return zt;
+}
+
+// Scan of the gap histogram by a workgroup of NT threads: thread t owns bins
+// [t * PER, (t + 1) * PER); its interval of running mass is (incl[t - 1],
+// incl[t]], so the intervals tile [0, total].  Writes the first non-empty bin
+// where the running mass reaches target to *bin_out (-1 if none) and the mass
+// of the bins before it to *A_out.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void nucleus_pick(const double* hm, double target, double* incl_sh, double* red_s,
+                                             int* bin_out, double* A_out) {
+  constexpr int PER = kNucBins / NT, NW = NT / kWave;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  if (tid == 0) *bin_out = -1;
+  double loc = 0.0;
+  for (int k = 0; k < PER; ++k) loc += hm[tid * PER + k];
+  double inc = wave_incl_scan_d(loc);
+  if (lane == kWave - 1) red_s[w] = inc;
+  __syncthreads();
+  for (int k = 0; k < w && k < NW; ++k) inc += red_s[k];
+  incl_sh[tid] = inc;
+  __syncthreads();
+  const double start = tid == 0 ? 0.0 : incl_sh[tid - 1];
+  if (start < target && target <= inc) {
+    double cum = start;
+    int pick = -1;
+    double pickA = start;
+    for (int k = 0; k < PER; ++k) {
+      const int bin = tid * PER + k;
+      if (!(hm[bin] > 0.0)) continue;
+      pick = bin;  // last non-empty bin so far: the choice if rounding leaves the target unreached
+      pickA = cum;
+      const double nxt = cum + hm[bin];
+      if (nxt >= target) break;
+      cum = nxt;
+    }
+    *bin_out = pick;
+    *A_out = pickA;
+  }
+  __syncthreads();
+}
+
+// Pass 2 over elements [a, e): push(l, y) for every token of gap bin bstar.
+// The bins of a vector's tokens first (branch-free), then the rare tokens of
+// the chosen bin.
+template <typename ET, int NT, int U, typename P>
+__device__ __forceinline__ void nucleus_collect(const ET* rp, int a, int e, double lm, double it, int bstar,
+                                                P&& push) {
+  row_stream<ET, NT, U>(
+      rp, a, e,
+      [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
+        constexpr int EPV = Elem<ET>::kPerVec;
+        bool m[EPV];
+        bool any = false;
+#pragma unroll
+        for (int k = 0; k < EPV; ++k) {
+          m[k] = nucleus_bin(lm, fv[k], it) == bstar;
+          any |= m[k];
+        }
+        if (any) {
+#pragma unroll
+          for (int k = 0; k < EPV; ++k)
+            if (m[k]) push(fv[k], y0 + k);
+        }
+      },
+      [&](float l, int y) {
+        if (nucleus_bin(lm, l, it) == bstar) push(l, y);
+      });
+}
+
+// The whole nucleus of one row by one workgroup (every step above in one
+// pass each; refinement of an over-full bin included).
 template <typename ET>
-__global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
-                                                           int rows_t, int G, int V, int S,
-                                                           const float2* __restrict__ part,
-                                                           const ReqInfo* __restrict__ info,
-                                                           RowCut* __restrict__ cut, Layout L) {
-  constexpr int NT = NucShape::NT, U = NucShape::U, NW = NT / kWave, PER = kNucBins / NT;
+__device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, const ET* __restrict__ ld, int rows_t,
+                                            int G, int V, int S, const float2* __restrict__ part,
+                                            const ReqInfo* __restrict__ info, RowCut* __restrict__ cut,
+                                            const Layout& L) {
+  constexpr int NT = NucShape::NT, U = NucShape::U, NW = NT / kWave;
   static_assert(kNucBins % NT == 0, "bins per thread");
   static_assert(kNucCap * sizeof(uint64_t) <= kNucBins * sizeof(double), "keys alias the histogram");
-  const int row = blockIdx.x;
   const ReqInfo ri = info[row_request(row, rows_t, G)];
   if (ri.kind != kReqFull || !(ri.top_p < 1.f)) return;  // uniform over the workgroup
   const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
@@ -388,9 +550,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
   // the k-cut (written by kcut_full_kernel) have no mass here.
   const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
   auto below = [&](float l, int y) { return kfloor != 0ull && make_key(l, (uint32_t)y) < kfloor; };
-  // The gap histogram is dead once its bin is chosen; the collected keys of
-  // that bin then take its storage.
-  __shared__ double hm[kNucBins + 1];  // + the spare slot of tokens without a bin
+  double* hm = nucleus_hist_lds();
   uint64_t* keys = reinterpret_cast<uint64_t*>(hm);
   __shared__ double tab[64];
   __shared__ double red_d[NW], red_s[NW];
@@ -403,7 +563,6 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
       uint32_t c[256];
     } dig;
   } scr;
-  double* incl_sh = scr.incl;
   double* dm = scr.dig.m;
   uint32_t* dc = scr.dig.c;
   __shared__ uint64_t red_k[2][NW];
@@ -414,10 +573,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
   __shared__ int sh_plen;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
 
-  // Largest logit of the row, from the softmax partials.
-  float lmax = -INFINITY;
-  for (int k = lane; k < S; k += kWave) lmax = fmaxf(lmax, part[(size_t)row * S + k].x);
-  lmax = wave_max_f(lmax);
+  const float lmax = nucleus_lmax(part, row, S);
   const double lm = (double)lmax, it = 1.0 / (double)ri.T;
 
   for (int i = tid; i <= kNucBins; i += NT) hm[i] = 0.0;
@@ -428,54 +584,16 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
     return exp_nonpos_f64(((double)l - lm) * it, tab, &k);
   };
   if (tid == 0) {
-    sh_bin = -1;
     sh_prefix = 0ull;  // fixed top bits of the cut key (refinement)
     sh_plen = 0;
+    sh_n = 0;
   }
 
   __syncthreads();
 
-  // Pass 1: masses, Z and the mass histogram of the gap.  The gap is the
-  // negated exponent, so mass and bin come from one product.  Branch-free:
-  // a token without a bin adds to the spare slot hm[kNucBins], a token below
-  // the k-floor adds 0.
-  double zt = 0.0;
-  auto pass1 = [&](auto floor_tag) {
-    constexpr bool FLOOR = decltype(floor_tag)::value;
-    auto mass_bin = [&](float l, int y, uint32_t& bin) -> double {
-      int k;
-      double e = exp_nonpos_f64(((double)l - lm) * it, tab, &k);
-      if (FLOOR) e = make_key(l, (uint32_t)y) < kfloor ? 0.0 : e;
-      bin = min((uint32_t)(-k), (uint32_t)kNucBins);
-      return e;
-    };
-    row_stream<ET, NT, U>(
-        rp, V,
-        [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
-          // Masses and bins of the vector's tokens first (independent
-          // chains the scheduler interleaves), then the histogram adds.
-          constexpr int EPV = Elem<ET>::kPerVec;
-          double e[EPV];
-          uint32_t bin[EPV];
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) e[k] = mass_bin(fv[k], y0 + k, bin[k]);
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) atomicAdd(&hm[bin[k]], e[k]);
-#pragma unroll
-          for (int w2 = 1; w2 < EPV; w2 *= 2)
-#pragma unroll
-            for (int k = 0; k + w2 < EPV; k += 2 * w2) e[k] += e[k + w2];
-          zt += e[0];
-        },
-        [&](float l, int y) {
-          uint32_t bin;
-          const double e = mass_bin(l, y, bin);
-          atomicAdd(&hm[bin], e);
-          zt += e;
-        });
-  };
-  if (kfloor != 0ull) pass1(std::true_type{});
-  else pass1(std::false_type{});
+  // Pass 1: masses, Z and the mass histogram of the gap.
+  double zt = kfloor != 0ull ? nucleus_pass1<ET, NT, U, true>(rp, 0, V, lm, it, kfloor, tab, hm)
+                             : nucleus_pass1<ET, NT, U, false>(rp, 0, V, lm, it, kfloor, tab, hm);
   zt = wave_sum_d(zt);
   if (lane == 0) red_d[w] = zt;
   __syncthreads();
@@ -483,37 +601,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
   for (int k = 0; k < NW; ++k) Z += red_d[k];
   const double target = (double)ri.top_p * Z;
 
-  // Scan: thread t owns bins [t * PER, (t + 1) * PER).  Its interval of
-  // running mass is (incl[t - 1], incl[t]], so the intervals tile [0, total].
-  double loc = 0.0;
-  for (int k = 0; k < PER; ++k) loc += hm[tid * PER + k];
-  double inc = wave_incl_scan_d(loc);
-  if (lane == kWave - 1) red_s[w] = inc;
-  __syncthreads();
-  for (int k = 0; k < w; ++k) inc += red_s[k];
-  incl_sh[tid] = inc;
-  __syncthreads();
-  {
-    const double start = tid == 0 ? 0.0 : incl_sh[tid - 1];
-    if (start < target && target <= inc) {
-      double cum = start;
-      int pick = -1;
-      double pickA = start;
-      for (int k = 0; k < PER; ++k) {
-        const int bin = tid * PER + k;
-        if (!(hm[bin] > 0.0)) continue;
-        pick = bin;  // last non-empty bin so far: the choice if rounding leaves the target unreached
-        pickA = cum;
-        const double nxt = cum + hm[bin];
-        if (nxt >= target) break;
-        cum = nxt;
-      }
-      sh_bin = pick;
-      sh_A = pickA;
-    }
-    if (tid == 0) sh_n = 0;
-  }
-  __syncthreads();
+  nucleus_pick<NT>(hm, target, scr.incl, red_s, &sh_bin, &sh_A);
   const int bstar = sh_bin;
   if (bstar < 0) {
     // No finite mass (degenerate row): no cut.
@@ -524,39 +612,16 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
   // Pass 2: collect the keys of the bin (at most kNucCap are kept; the count
   // tells whether the bin needs refining).  filter_key: bin and key prefix.
   auto collect = [&](int plen, uint64_t prefix) {
-    auto push = [&](float l, int y) {
+    nucleus_collect<ET, NT, U>(rp, 0, V, lm, it, bstar, [&](float l, int y) {
       if (below(l, y)) return;
       const uint64_t k = make_key(l, (uint32_t)y);
       if (plen > 0 && (plen == 64 ? k != prefix : (k >> (64 - plen)) != (prefix >> (64 - plen)))) return;
       const int pos = atomicAdd(&sh_n, 1);
       if (pos < kNucCap) keys[pos] = k;
-    };
-    // The bins of a vector's tokens first (branch-free), then the rare
-    // tokens of the chosen bin.
-    row_stream<ET, NT, U>(
-        rp, V,
-        [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
-          constexpr int EPV = Elem<ET>::kPerVec;
-          bool m[EPV];
-          bool any = false;
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) {
-            m[k] = nucleus_bin(lm, fv[k], it) == bstar;
-            any |= m[k];
-          }
-          if (any) {
-#pragma unroll
-            for (int k = 0; k < EPV; ++k)
-              if (m[k]) push(fv[k], y0 + k);
-          }
-        },
-        [&](float l, int y) {
-          if (nucleus_bin(lm, l, it) == bstar) push(l, y);
-        });
+    });
   };
   collect(0, 0ull);
   __syncthreads();
-
   // Refinement of an over-full bin: radix over the keys below their common
   // prefix, 8 bits at a time, keeping the digit that holds the cut.
   if (sh_n > kNucCap) {
@@ -653,6 +718,222 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
   }
 }
 
+
+// ===========================================================================
+// Nucleus passes over full rows.  classify_kernel lists the rows with top-p
+// (how many there are is known only on the device).  With more than
+// kNucSplitRows of them, nucleus_part_kernel runs nucleus_row on each, one
+// workgroup per row.  With fewer, one workgroup per row would leave most of
+// the chip idle (a row then streams at the rate of one workgroup's loads in
+// flight), so each row is cut into NS contiguous chunks (NS =
+// min(kNucMaxSplit, kNucItems / rows)) and the steps of nucleus_row run as
+// separate passes:
+//   part     per chunk: pass 1 (Z and the gap histogram of its tokens) into
+//            the workspace;
+//   scan     per row: the chunks' histograms and Z summed in chunk order;
+//            the bin where the running mass reaches top_p Z, and the mass A
+//            of the bins before it;
+//   collect  per chunk: the keys of that bin, appended to the row's buffer;
+//   finish   per row: sort and walk the keys from A.  A bin of more than
+//            kNucCap keys is resolved by nucleus_row (with its refinement).
+// The passes of the path not taken exit at once.
+// ===========================================================================
+constexpr int kNucPartStride = kNucBins + 2;  // histogram, spare slot, Z
+
+struct NucState {
+  double A, Z;      // mass of the bins before the cut bin; the row's mass
+  uint64_t kfloor;  // the row's large top-k cut key (0: none)
+  int32_t bin;      // cut bin (-1: no cut, the row's RowCut is written)
+  uint32_t n;       // keys of the cut bin found by the collect pass
+};
+
+__device__ __forceinline__ int nucleus_splits(const int* plan) { return plan[1]; }
+
+// Chunk s of NS over a row of V tokens: boundaries on multiples of 64
+// elements (16-byte alignment relative to the row start is kept).
+__device__ __forceinline__ void nucleus_chunk(int V, int NS, int s, int* a, int* e) {
+  const int c = (((V + NS - 1) / NS) + 63) & ~63;
+  const int lo = s * c < V ? s * c : V;
+  *a = lo;
+  *e = lo + c < V ? lo + c : V;
+}
+
+// part: one workgroup per (listed row, chunk); with NS = 1, nucleus_row per
+// listed row.
+template <typename ET>
+__global__ __launch_bounds__(NucShape::NT) void nucleus_part_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                           int rows_t, int G, int V, int S,
+                                                           const float2* __restrict__ part,
+                                                           const ReqInfo* __restrict__ info,
+                                                           RowCut* __restrict__ cut, Layout L,
+                                                           const int* __restrict__ plan,
+                                                           const int* __restrict__ list,
+                                                           double* __restrict__ hpart) {
+  constexpr int NT = NucShape::NT, U = NucShape::U, NW = NT / kWave;
+  const int NS = nucleus_splits(plan);
+  const int item = blockIdx.x;
+  if (item >= plan[0] * NS) return;
+  if (NS == 1) {
+    nucleus_row<ET>(list[item], lt, ld, rows_t, G, V, S, part, info, cut, L);
+    return;
+  }
+  const int r = item / NS, s = item - r * NS;
+  const int row = list[r];
+  const ReqInfo ri = info[row_request(row, rows_t, G)];
+  const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
+  const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
+  double* hm = nucleus_hist_lds();
+  __shared__ double tab[64];
+  __shared__ double red_d[NW];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const double lm = (double)nucleus_lmax(part, row, S), it = 1.0 / (double)ri.T;
+  for (int i = tid; i <= kNucBins; i += NT) hm[i] = 0.0;
+  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  __syncthreads();
+  int a, e;
+  nucleus_chunk(V, NS, s, &a, &e);
+  double zt = kfloor != 0ull ? nucleus_pass1<ET, NT, U, true>(rp, a, e, lm, it, kfloor, tab, hm)
+                             : nucleus_pass1<ET, NT, U, false>(rp, a, e, lm, it, kfloor, tab, hm);
+  zt = wave_sum_d(zt);
+  if (lane == 0) red_d[w] = zt;
+  __syncthreads();
+  double* out = hpart + (size_t)item * kNucPartStride;
+  for (int i = tid; i <= kNucBins; i += NT) out[i] = hm[i];
+  if (tid == 0) {
+    double Z = 0.0;
+    for (int k = 0; k < NW; ++k) Z += red_d[k];
+    out[kNucBins + 1] = Z;
+  }
+}
+
+// scan: one workgroup per listed row.
+__global__ __launch_bounds__(NucShape::NT) void nucleus_scan_kernel(int rows_t, int G, int S,
+                                                                   const float2* __restrict__ part,
+                                                                   const ReqInfo* __restrict__ info,
+                                                                   RowCut* __restrict__ cut,
+                                                                   const int* __restrict__ plan,
+                                                                   const int* __restrict__ list,
+                                                                   const double* __restrict__ hpart,
+                                                                   NucState* __restrict__ state) {
+  constexpr int NT = NucShape::NT, NW = NT / kWave;
+  const int NS = nucleus_splits(plan);
+  const int r = blockIdx.x;
+  if (NS < 2 || r >= plan[0]) return;
+  const int row = list[r];
+  const ReqInfo ri = info[row_request(row, rows_t, G)];
+  const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
+  __shared__ double hm[kNucBins];
+  __shared__ double incl[NT], red_s[NW];
+  __shared__ double sh_A;
+  __shared__ int sh_bin;
+  const int tid = threadIdx.x;
+  const double* src = hpart + (size_t)r * NS * kNucPartStride;
+  for (int i = tid; i < kNucBins; i += NT) {
+    double v = 0.0;
+    for (int c = 0; c < NS; ++c) v += src[(size_t)c * kNucPartStride + i];
+    hm[i] = v;
+  }
+  double Z = 0.0;
+  for (int c = 0; c < NS; ++c) Z += src[(size_t)c * kNucPartStride + kNucBins + 1];
+  __syncthreads();
+  const double target = (double)ri.top_p * Z;
+  nucleus_pick<NT>(hm, target, incl, red_s, &sh_bin, &sh_A);
+  const float lmax = nucleus_lmax(part, row, S);  // by every wave (a wave reduction)
+  if (tid == 0) {
+    const int bstar = sh_bin;
+    if (bstar < 0) cut[row] = RowCut{kfloor, lmax, (float)(1.0 / Z)};  // no finite mass: no cut
+    state[r] = NucState{sh_A, Z, kfloor, bstar, 0u};
+  }
+}
+
+// collect: one workgroup per (listed row, chunk); keys of the cut bin are
+// appended to the row's buffer (the first kNucCap of them are stored).
+template <typename ET>
+__global__ __launch_bounds__(NucShape::NT) void nucleus_collect_kernel(const ET* __restrict__ lt,
+                                                              const ET* __restrict__ ld, int rows_t, int G,
+                                                              int V, int S, const float2* __restrict__ part,
+                                                              const ReqInfo* __restrict__ info, Layout L,
+                                                              const int* __restrict__ plan,
+                                                              const int* __restrict__ list,
+                                                              NucState* __restrict__ state,
+                                                              uint64_t* __restrict__ gkeys) {
+  constexpr int NT = NucShape::NT, U = NucShape::U;
+  const int NS = nucleus_splits(plan);
+  const int item = blockIdx.x;
+  if (NS < 2 || item >= plan[0] * NS) return;
+  const int r = item / NS, s = item - r * NS;
+  const int bstar = state[r].bin;
+  if (bstar < 0) return;
+  const uint64_t kfloor = state[r].kfloor;
+  const int row = list[r];
+  const ReqInfo ri = info[row_request(row, rows_t, G)];
+  const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
+  const double lm = (double)nucleus_lmax(part, row, S), it = 1.0 / (double)ri.T;
+  int a, e;
+  nucleus_chunk(V, NS, s, &a, &e);
+  uint32_t* cnt = &state[r].n;
+  uint64_t* dst = gkeys + (size_t)r * kNucCap;
+  nucleus_collect<ET, NT, U>(rp, a, e, lm, it, bstar, [&](float l, int y) {
+    const uint64_t k = make_key(l, (uint32_t)y);
+    if (kfloor != 0ull && k < kfloor) return;
+    const uint32_t pos = atomicAdd(cnt, 1u);
+    if (pos < (uint32_t)kNucCap) dst[pos] = k;
+  });
+}
+
+// finish: one workgroup per listed row.
+template <typename ET>
+__global__ __launch_bounds__(NucShape::NT) void nucleus_finish_kernel(const ET* __restrict__ lt,
+                                                             const ET* __restrict__ ld, int rows_t, int G, int V,
+                                                             int S, const float2* __restrict__ part,
+                                                             const ReqInfo* __restrict__ info,
+                                                             RowCut* __restrict__ cut, Layout L,
+                                                             const int* __restrict__ plan,
+                                                             const int* __restrict__ list,
+                                                             const NucState* __restrict__ state,
+                                                             const uint64_t* __restrict__ gkeys) {
+  constexpr int NT = NucShape::NT;
+  const int NS = nucleus_splits(plan);
+  const int r = blockIdx.x;
+  if (NS < 2 || r >= plan[0]) return;
+  const NucState st = state[r];
+  if (st.bin < 0) return;  // the scan wrote the row's cut
+  const int row = list[r];
+  if (st.n > (uint32_t)kNucCap) {
+    // Over-full bin (many equal or near-equal logits): the one-workgroup
+    // pass, which refines it.
+    nucleus_row<ET>(row, lt, ld, rows_t, G, V, S, part, info, cut, L);
+    return;
+  }
+  const ReqInfo ri = info[row_request(row, rows_t, G)];
+  uint64_t* keys = reinterpret_cast<uint64_t*>(nucleus_hist_lds());
+  __shared__ double tab[64];
+  const int tid = threadIdx.x;
+  const float lmax = nucleus_lmax(part, row, S);
+  const double lm = (double)lmax, it = 1.0 / (double)ri.T;
+  const int n = (int)st.n;
+  int n2 = 2;
+  while (n2 < n) n2 <<= 1;
+  const uint64_t* src = gkeys + (size_t)r * kNucCap;
+  for (int i = tid; i < n2; i += NT) keys[i] = i < n ? src[i] : 0ull;
+  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  __syncthreads();
+  block_sort_desc<NT>(keys, n2);
+  if (tid < kWave) {
+    auto mass = [&](float l) {
+      int k;
+      return exp_nonpos_f64(((double)l - lm) * it, tab, &k);
+    };
+    const double target = (double)ri.top_p * st.Z;
+    double zk;
+    const int t = n > 0 ? wave_walk(keys, n, st.A, target, mass, &zk) : -1;
+    if (tid == 0) {
+      if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / zk)};
+      else cut[row] = RowCut{st.kfloor, lmax, (float)(1.0 / st.Z)};
+    }
+  }
+}
+
 // ===========================================================================
 // Top-k above the candidate capacity, over a full row: the kept set is the k
 // largest keys (logit desc, index asc), so it is one cut key kappa, the k-th
@@ -666,7 +947,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_full_kernel(const ET* __
 // exp2((l - max) c), fp32 terms summed in fp64).  Keys are distinct, so at
 // most six passes (12, 24, ..., 60, 64 bits) reach a bucket of one key; rows
 // of N(0, 9) logits need two.  A nucleus over this law is cut afterwards by
-// nucleus_full_kernel, which reads kappa as its floor.
+// the nucleus passes, which read kappa as their floor.
 // ===========================================================================
 constexpr int kCutBits = 12, kCutBins = 1 << kCutBits;
 

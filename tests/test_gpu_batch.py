@@ -217,3 +217,16 @@ def test_full_size_batch_every_request(sv, name):
     gsub = {k: v[ids] for k, v in got.items() if isinstance(v, np.ndarray) and v.ndim >= 1 and v.shape[0] == wl.B}
     rep = assert_parity_batch(gsub, ref)
     print(f"[full] {name}: {rep}", flush=True)
+
+
+@pytest.mark.parametrize("B,G,V,onehot", [(1, 1, 5003, True), (3, 2, 97, False), (102, 2, 5003, False),
+                                          (103, 2, 5003, False), (40, 6, 20011, False)])
+def test_top_p_row_counts(sv, B, G, V, onehot):
+    """Top-p rows without top-k, as many as select each path of the nucleus
+    pass: up to 512 rows split across workgroups (2 rows: 16 chunks each; 510
+    rows: 2), 515 and 520 rows one workgroup each; a vocabulary of 97 leaves
+    most chunks empty."""
+    inp = mixed(B, G, V, "f32", mix=((1.0, 0, 0.9), (0.8, 0, 0.6)), seed=B)
+    rows = B * (G + 1) + (0 if onehot else B * G)
+    print(f"[batch] top-p rows {rows}", flush=True)
+    check_batch(sv, inp, onehot=onehot)
