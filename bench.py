@@ -170,6 +170,85 @@ def rounds_driver(sv, wl, rounds: int, device, seed_offset: int = 1000) -> dict:
             "_n": n, "_counters": counters.cpu().numpy()}
 
 
+def outcome_stats(sv, wl, params, sampling, layout, lt, ld, x, out, nacc, pd, qd, ta, pn, ws, stream):
+    """What the method did on the batch (untimed, after the timed region):
+    the law of n from the last timed call, and beta = sum min(p, q) per
+    position from one more call of the same inputs with beta requested (a
+    uniform batch call is bit-identical to the single-setting entry points).
+    Returns (outcome, got): the statistics, and the timed call's outputs per
+    request as host arrays for the oracle check."""
+    import numpy as np
+    import torch
+
+    B, G, dev = wl.B, wl.G, out.device
+    n_gpu = nacc.cpu().numpy()
+
+    g_req = wl.draft_lengths if wl.has_settings else np.full(B, G)
+    beta_t = torch.empty(x.shape, dtype=torch.float32, device=dev)
+    o2 = [torch.empty_like(out), torch.empty_like(nacc), torch.empty_like(pd), torch.empty_like(qd)]
+    if wl.has_settings:
+        pn2 = torch.empty_like(pn) if pn is not None else None
+        sv.spec_verify_batch(params, sampling, layout, lt, ld, x,
+                             sv.make_outputs(*o2, beta=beta_t, path_nodes=pn2), ws, stream)
+    else:
+        bparams = sv.make_params(B, G, wl.V, wl.torch_dtype, wl.temperature if wl.entry != "greedy" else 0.0,
+                                 wl.top_k, wl.verify_seed)
+        bws = torch.empty(sv.sv_workspace_bytes_batch(bparams, None), dtype=torch.uint8, device=dev)
+        bdraft = ld if wl.entry == "prob" else None
+        blay = sv.SvLayout(sv.SV_DRAFT_LOGITS if bdraft is not None else sv.SV_DRAFT_ONEHOT, 0, wl.V,
+                           wl.V if bdraft is not None else 0, None, None)
+        sv.spec_verify_batch(bparams, None, blay, lt, bdraft, x, sv.make_outputs(*o2, beta=beta_t), bws, stream)
+    torch.cuda.synchronize()
+    beta_flat = beta_t.cpu().numpy()
+    beta_pad = np.full((B, G), np.nan)
+    if wl.lengths or beta_flat.ndim == 1:
+        off = 0
+        for b in range(B):
+            beta_pad[b, :g_req[b]] = beta_flat[off:off + g_req[b]]
+            off += g_req[b]
+    else:
+        beta_pad[:] = beta_flat
+    bmean = np.nanmean(beta_pad, axis=0)
+    reach = np.array([(n_gpu >= j).sum() for j in range(G + 1)], dtype=np.float64)
+    outcome = {"n_histogram": np.bincount(n_gpu, minlength=G + 1).tolist(),
+               "tokens_per_round": float((n_gpu + 1).mean()),
+               "acceptance_by_position": [float((n_gpu > j).sum() / reach[j]) if reach[j] else None
+                                          for j in range(G)],
+               "beta_by_position": [float(v) for v in bmean],
+               "mean_beta": float(np.nanmean(beta_pad)),
+               "beta_call_same_n": bool((o2[1].cpu().numpy() == n_gpu).all())}
+    if not wl.parents:
+        # Eq. 1 of the draft-model page with each request's own per-position
+        # rates: given its rows, position j of request b accepts with
+        # probability beta[b, j], independently of the others, so
+        # E[n_b + 1] = sum over i <= g_b of prod_{j < i} beta[b, j].  (The
+        # same sum over the batch-mean rates is lower whenever a request's
+        # rates rise and fall together, as they do with a per-request draft
+        # noise.)
+        cp = np.cumprod(np.nan_to_num(beta_pad, nan=0.0), axis=1)
+        per_req = 1.0 + np.array([cp[b, :g_req[b]].sum() for b in range(B)])
+        outcome["tokens_per_round_eq1"] = float(per_req.mean())
+
+    # The GPU's outputs per request, for the oracle check of the CPU leg.
+    got = {"out_tokens": out.cpu().numpy(), "num_accepted": n_gpu}
+    if wl.entry == "greedy" and not wl.has_settings:
+        got["target_argmax"] = ta.cpu().numpy()
+    elif wl.entry != "greedy":
+        for key, t in (("p_draft", pd), ("q_draft", qd)):
+            if key == "q_draft" and wl.entry == "onehot" and not wl.has_settings:
+                continue
+            flat = t.cpu().numpy()
+            if flat.ndim == 1:  # packed ragged rows back to [B, G]
+                dense, off = np.full((B, G), np.nan, np.float32), 0
+                for b in range(B):
+                    dense[b, :g_req[b]] = flat[off:off + g_req[b]]
+                    off += g_req[b]
+                flat = dense
+            got[key] = flat
+
+    return outcome, got
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +259,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--rounds", type=int, default=0,
                     help="also run the multi-round driver for this many rounds and report its statistics")
+    ap.add_argument("--no-outcome", action="store_true",
+                    help="skip the untimed outcome statistics and the oracle check (profiling runs: only the "
+                         "warm-up and timed calls run)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -286,74 +368,10 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 3 copies of 1 GiB done")
 
-    # What the method did on this batch (untimed): the law of n from the
-    # last timed call, and beta = sum min(p, q) per position from one more
-    # call of the same inputs with beta requested (a uniform batch call is
-    # bit-identical to the single-setting entry points).
-    import numpy as np
-    n_gpu = nacc.cpu().numpy()
-    g_req = wl.draft_lengths if wl.has_settings else np.full(B, G)
-    beta_t = torch.empty(x.shape, dtype=torch.float32, device=dev)
-    o2 = [torch.empty_like(out), torch.empty_like(nacc), torch.empty_like(pd), torch.empty_like(qd)]
-    if wl.has_settings:
-        pn2 = torch.empty_like(pn) if pn is not None else None
-        sv.spec_verify_batch(params, sampling, layout, lt, ld, x,
-                             sv.make_outputs(*o2, beta=beta_t, path_nodes=pn2), ws, stream)
-    else:
-        bparams = sv.make_params(B, G, wl.V, wl.torch_dtype, wl.temperature if wl.entry != "greedy" else 0.0,
-                                 wl.top_k, wl.verify_seed)
-        bws = torch.empty(sv.sv_workspace_bytes_batch(bparams, None), dtype=torch.uint8, device=dev)
-        bdraft = ld if wl.entry == "prob" else None
-        blay = sv.SvLayout(sv.SV_DRAFT_LOGITS if bdraft is not None else sv.SV_DRAFT_ONEHOT, 0, wl.V,
-                           wl.V if bdraft is not None else 0, None, None)
-        sv.spec_verify_batch(bparams, None, blay, lt, bdraft, x, sv.make_outputs(*o2, beta=beta_t), bws, stream)
-    torch.cuda.synchronize()
-    beta_flat = beta_t.cpu().numpy()
-    beta_pad = np.full((B, G), np.nan)
-    if wl.lengths or beta_flat.ndim == 1:
-        off = 0
-        for b in range(B):
-            beta_pad[b, :g_req[b]] = beta_flat[off:off + g_req[b]]
-            off += g_req[b]
-    else:
-        beta_pad[:] = beta_flat
-    bmean = np.nanmean(beta_pad, axis=0)
-    reach = np.array([(n_gpu >= j).sum() for j in range(G + 1)], dtype=np.float64)
-    outcome = {"n_histogram": np.bincount(n_gpu, minlength=G + 1).tolist(),
-               "tokens_per_round": float((n_gpu + 1).mean()),
-               "acceptance_by_position": [float((n_gpu > j).sum() / reach[j]) if reach[j] else None
-                                          for j in range(G)],
-               "beta_by_position": [float(v) for v in bmean],
-               "mean_beta": float(np.nanmean(beta_pad)),
-               "beta_call_same_n": bool((o2[1].cpu().numpy() == n_gpu).all())}
-    if not wl.parents:
-        # Eq. 1 of the draft-model page with each request's own per-position
-        # rates: given its rows, position j of request b accepts with
-        # probability beta[b, j], independently of the others, so
-        # E[n_b + 1] = sum over i <= g_b of prod_{j < i} beta[b, j].  (The
-        # same sum over the batch-mean rates is lower whenever a request's
-        # rates rise and fall together, as they do with a per-request draft
-        # noise.)
-        cp = np.cumprod(np.nan_to_num(beta_pad, nan=0.0), axis=1)
-        per_req = 1.0 + np.array([cp[b, :g_req[b]].sum() for b in range(B)])
-        outcome["tokens_per_round_eq1"] = float(per_req.mean())
-
-    # The GPU's outputs per request, for the oracle check of the CPU leg.
-    got = {"out_tokens": out.cpu().numpy(), "num_accepted": n_gpu}
-    if wl.entry == "greedy" and not wl.has_settings:
-        got["target_argmax"] = ta.cpu().numpy()
-    elif wl.entry != "greedy":
-        for key, t in (("p_draft", pd), ("q_draft", qd)):
-            if key == "q_draft" and wl.entry == "onehot" and not wl.has_settings:
-                continue
-            flat = t.cpu().numpy()
-            if flat.ndim == 1:  # packed ragged rows back to [B, G]
-                dense, off = np.full((B, G), np.nan, np.float32), 0
-                for b in range(B):
-                    dense[b, :g_req[b]] = flat[off:off + g_req[b]]
-                    off += g_req[b]
-                flat = dense
-            got[key] = flat
+    outcome = got = None
+    if not args.no_outcome:
+        outcome, got = outcome_stats(sv, wl, params, sampling, layout, lt, ld, x, out, nacc, pd, qd, ta, pn, ws,
+                                     stream)
 
     sec = wall / args.steps
     positions = int(wl.draft_lengths.sum()) if wl.has_settings else B * G
