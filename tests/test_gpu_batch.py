@@ -230,3 +230,11 @@ def test_top_p_row_counts(sv, B, G, V, onehot):
     rows = B * (G + 1) + (0 if onehot else B * G)
     print(f"[batch] top-p rows {rows}", flush=True)
     check_batch(sv, inp, onehot=onehot)
+
+
+@pytest.mark.parametrize("rows", ["flat", "integers", "band"])
+def test_top_p_hard_rows_one_workgroup_each(sv, rows):
+    """The hard rows above, 560 of them (more than the split path takes): the
+    one-workgroup-per-row path with its refinement of over-full bins."""
+    inp = _rows_case(ROWS[rows], 112, 2, 4099, "f32", 1.0, [0.3, 0.5, 0.9, 0.97])
+    check_batch(sv, inp, max_top_k=0)
