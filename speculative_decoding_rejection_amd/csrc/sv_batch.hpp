@@ -294,8 +294,11 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 }
 
 // ===========================================================================
-// Nucleus of a full row (no top-k): one workgroup per row (NucShape below),
-// after the softmax row pass (whose partials give the row's largest logit).
+// Nucleus of a full row (no top-k), after the softmax row pass (whose
+// partials give the row's largest logit).  The steps below, as nucleus_row
+// runs them with one workgroup per row; with few such rows in a call, the
+// same steps are split over chunks of each row (the nucleus passes further
+// below).
 //
 //   pass 1  fp64 mass of every token; the total Z; a histogram of mass over
 //           bins of the gap d = (l_max - l) / T, ln2 / 64 nats per bin over
@@ -314,8 +317,9 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 // Each pass streams the row from HBM.
 // ===========================================================================
 constexpr int kNucBins = 4096;  // ln2 / 64 nats each: gaps below 44.4 nats
-// One workgroup per row: 512 threads, two vectors per thread and chunk.
-// Measured on MI355X with the row passes of the kinds running side by side:
+// A workgroup per row (or per chunk): 512 threads, two vectors per thread in
+// flight.  Measured on MI355X (one workgroup per row, before the split
+// passes) with the row passes of the kinds running side by side:
 // against 256 / 512 / 1024 threads and 1 / 2 / 4 vectors (by logit type, and
 // with a larger shape for calls with few rows), this one shape was the
 // fastest or within 1% on the mixed, ragged and sampler-match workloads.
