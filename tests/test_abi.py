@@ -198,3 +198,21 @@ def test_batch_match_layout_errors(sv):
     outs = sv.SvOutputs(1 << 20, 1 << 20, None, None, None, None, (1 << 20) + 2)
     assert lib.spec_verify_batch(ctypes.byref(p), ctypes.byref(ok), ctypes.byref(L(M, 0, 0, 0, None, None)),
                                  d, None, d, ctypes.byref(outs), d, 1 << 20, None) == sv.SV_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("B,G", [(1, 1), (3, 2), (256, 7)])
+def test_batch_workspace_holds_the_split_nucleus(sv, B, G):
+    """With top-p settings the workspace also holds the split nucleus passes'
+    buffers: the row list, chunk histograms for min(1024, 16 x rows) chunks
+    (4098 doubles each, rows capped at 512), and a 2048-key buffer per split
+    row; calls without top-p carry none of it."""
+    fake = 1 << 21
+    p = sv.make_params(B, G, 5003, sv.SV_F32, 1.0, 0, 1)
+    topk = sv.sv_workspace_bytes_batch(p, sv.SvSampling(fake, fake, None, 64, 0))
+    nuc = sv.sv_workspace_bytes_batch(p, sv.SvSampling(fake, fake, fake, 64, 0))
+    rows = B * (2 * G + 1)
+    split_rows = min(rows, 512)
+    items = min(1024, 16 * split_rows)
+    need = rows * 16 + rows * 4 + items * 4098 * 8 + split_rows * 2048 * 8
+    assert nuc - topk >= need
+    assert nuc - topk <= need + split_rows * 64 + 16 * 4096  # state records and alignment
