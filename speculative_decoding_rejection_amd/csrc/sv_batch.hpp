@@ -85,12 +85,16 @@ __device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, in
 
 // Paths of the nucleus passes over full rows (below): with at most
 // kNucSplitRows rows with top-p in a call, each row is cut into NS =
-// min(kNucMaxSplit, kNucItems / rows) chunks; with more, one workgroup per
-// row.  plan = {rows, NS} (NS = 1: one workgroup per row).
-constexpr int kNucSplitRows = 512, kNucItems = 1024, kNucMaxSplit = 16;
+// max(2, min(kNucMaxSplit, kNucItemTarget / rows)) chunks, about one wave of
+// workgroups over the chip (rows x NS <= kNucItems); with more, one
+// workgroup per row.  plan = {rows, NS} (NS = 1: one workgroup per row).
+constexpr int kNucSplitRows = 512, kNucItems = 1024, kNucMaxSplit = 16, kNucItemTarget = 512;
 __device__ __forceinline__ void plan_nucleus(int n, int* plan) {
   int ns = 1;
-  if (n > 0 && n <= kNucSplitRows) ns = kNucItems / n < kNucMaxSplit ? kNucItems / n : kNucMaxSplit;
+  if (n > 0 && n <= kNucSplitRows) {
+    ns = kNucItemTarget / n < kNucMaxSplit ? kNucItemTarget / n : kNucMaxSplit;
+    ns = ns < 2 ? 2 : ns;  // n * ns <= kNucItems
+  }
   plan[0] = n;
   plan[1] = ns;
 }
@@ -729,9 +733,8 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
 // kNucSplitRows of them, nucleus_part_kernel runs nucleus_row on each, one
 // workgroup per row.  With fewer, one workgroup per row would leave most of
 // the chip idle (a row then streams at the rate of one workgroup's loads in
-// flight), so each row is cut into NS contiguous chunks (NS =
-// min(kNucMaxSplit, kNucItems / rows)) and the steps of nucleus_row run as
-// separate passes:
+// flight), so each row is cut into NS contiguous chunks (plan_nucleus) and
+// the steps of nucleus_row run as separate passes:
 //   part     per chunk: pass 1 (Z and the gap histogram of its tokens) into
 //            the workspace;
 //   scan     per row: the chunks' histograms and Z summed in chunk order;
