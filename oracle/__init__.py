@@ -13,6 +13,11 @@ Pinned functions and their pins (see tests/test_oracle_pins.py):
       nucleus sets on hand-computed laws, index ties on flat rows, the
       temperature-before-top-p and top-k-before-top-p orders);
   race -- chi-square against w / sum(w);
+  accept_margin, race_margin, nucleus_margin, near_tie_position and
+      oracle.parity.near_tie_rows -- hand-computed values (equal scores give
+      0, one candidate 1, a planted relative gap of 5e-5 is flagged, a top-p
+      stop at the first token has only the C_1 - top_p side), and planted
+      near-ties in whole verifier calls;
   verify (prob / onehot / greedy / naive) -- the worked 5-token example and
       Monte Carlo table of the vLLM rejection-resampling page, Eq. 1 of the
       draft-model page, brute-force enumeration at V <= 4, and exact
@@ -80,8 +85,12 @@ def _load():
     lib.sv_ref_race.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint32,
                                 ctypes.c_uint32, ctypes.POINTER(ctypes.c_double)]
     lib.sv_ref_race.restype = ctypes.c_int
-    lib.sv_ref_block_race.argtypes = lib.sv_ref_race.argtypes
-    lib.sv_ref_block_race.restype = ctypes.c_int
+    lib.sv_ref_accept_margin.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_int]
+    lib.sv_ref_accept_margin.restype = ctypes.c_double
+    lib.sv_ref_race_margin.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double]
+    lib.sv_ref_race_margin.restype = ctypes.c_double
+    lib.sv_ref_nucleus_margin.argtypes = [ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double]
+    lib.sv_ref_nucleus_margin.restype = ctypes.c_double
     lib.sv_ref_verify.argtypes = ([ctypes.c_int] * 5 + [ctypes.c_double, ctypes.c_int, ctypes.c_uint64]
                                   + [ctypes.c_void_p] * 13 + [ctypes.c_int])
     lib.sv_ref_verify.restype = ctypes.c_int
@@ -150,13 +159,20 @@ def race(w, seed: int, b: int, j: int) -> tuple[int, float]:
     return tok, m.value
 
 
-def block_race(w, seed: int, b: int, j: int) -> tuple[int, float]:
-    """The two-stage race (blocks of 64 tokens, then tokens): the sampler of
-    full-vocabulary laws under sampler-match."""
-    wv = np.ascontiguousarray(w, dtype=np.float64)
-    m = ctypes.c_double(0.0)
-    tok = _load().sv_ref_block_race(_ptr(wv), wv.shape[0], seed, b, j, ctypes.byref(m))
-    return tok, m.value
+def accept_margin(u: float, px: float, qx: float, valid: bool = True) -> float:
+    """Relative distance of the accept test u q(x) <= p(x) from its boundary."""
+    return _load().sv_ref_accept_margin(float(u), float(px), float(qx), int(bool(valid)))
+
+
+def race_margin(ncand: int, s1: float, s2: float) -> float:
+    """Relative gap of a race winner's score s1 over the runner-up's s2."""
+    return _load().sv_ref_race_margin(int(ncand), float(s1), float(s2))
+
+
+def nucleus_margin(s: int, C: float, Cprev: float, top_p: float) -> float:
+    """Distance of top_p from the nucleus decision that stops at rank s with
+    running masses C (through rank s) and Cprev (through rank s - 1)."""
+    return _load().sv_ref_nucleus_margin(int(s), float(C), float(Cprev), float(top_p))
 
 
 def max_threads() -> int:

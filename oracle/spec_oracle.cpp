@@ -34,10 +34,8 @@
 //     0..g and positions 0..g-1; its uniforms are those of the same (b, j);
 //   * sampler-match ([P3] "mlxcel의 프롬프트 조회"): every node of the draft
 //     (a chain, or a tree given by parent indices) gets a fresh sample from
-//     its row's adjusted law, drawn by the Exp(1) race on the stream of
-//     (b, node) (a law over the whole vocabulary or a top-k above 1024
-//     tokens: first over blocks of 64 tokens by their mass, then within the
-//     winning block; the same law);
+//     its row's adjusted law, drawn by the same Exp(1) race over the whole
+//     law as the recovered and bonus draws, on the race stream of (b, node);
 //     from the root, the walk follows the child whose token equals
 //     the sample (the lowest-indexed child if several do) and emits the
 //     sample where no child matches.
@@ -49,6 +47,11 @@
 //   * Exp(1) variate E = -ln(u); E == 0 gives an infinite race score;
 //   * a residual of zero total mass falls back to w = p;
 //   * an out-of-range draft token counts as rejected and raises a flag.
+//
+// Decision margins (diagnostics; they decide which results a comparison may
+// exempt as near ties, [P3] "정확성 기준": a different reduction order can
+// flip near-equal tokens): accept_margin, race_margin and nucleus_margin
+// below, each pinned on hand-computed values.
 //
 // Parity unpinned by the pages: the tie rules at exact equality (race ties,
 // accept at u == p/q) are events of probability ~2^-53 that no sampling test
@@ -153,13 +156,46 @@ double decode_logit(const void* row, int dtype, int64_t y) {
 
 size_t elem_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
 
+// ---------------------------------------------------------------------------
+// Decision margins.  Each is the relative (or, for the nucleus, absolute
+// probability) distance of a decision from its boundary; 1 where no decision
+// could flip.
+// ---------------------------------------------------------------------------
+
+// The accept test u <= p(x) / q(x), written u q(x) <= p(x): relative gap
+// |u q - p| / max(u q, p).  An invalid token or q(x) = 0 rejects whatever u
+// is (no boundary); p = u q = 0 cannot occur since u > 0 and q > 0 there.
+double accept_margin(double u, double px, double qx, bool valid) {
+  if (!valid || !(qx > 0.0)) return 1.0;
+  const double lhs = u * qx, rhs = px;
+  const double den = std::max(lhs, rhs);
+  return den > 0.0 ? std::fabs(lhs - rhs) / den : 0.0;
+}
+
+// The race winner against the runner-up: (s1 - s2) / s1 for the two largest
+// scores.  One candidate (s2 absent): 1.  An infinite winner (E = 0) is
+// flipped only by another infinite score.
+double race_margin(int ncand, double s1, double s2) {
+  if (ncand < 2) return 1.0;
+  if (std::isinf(s1)) return std::isinf(s2) ? 0.0 : 1.0;
+  return (s1 - s2) / s1;
+}
+
+// The nucleus stops at the s-th kept token (rank order) because the running
+// mass C_s reaches top_p while C_(s-1) did not: the decision has the two
+// sides C_s - top_p and top_p - C_(s-1).  At s = 1 only the first exists (at
+// least one token is always kept, so nothing is decided below it).
+double nucleus_margin(int s, double C, double Cprev, double top_p) {
+  if (s <= 1) return C - top_p;
+  return std::min(C - top_p, top_p - Cprev);
+}
+
 // The adjusted distribution of one position: temperature, then top-k, then
 // top-p, then softmax ([P4] "vLLM 커널은 이 규칙을 어떻게 옮겼나": the sampling
 // constraints are applied to the logits before the test, so p is the adjusted
 // law; the page lists them as temperature, top_k, top_p).  top_p >= 1 is off.
-// *cut_margin (if not NULL) receives the distance of top_p from the nearest
-// cumulative mass of the nucleus decision, min(C_s - top_p, top_p - C_{s-1}),
-// or 1 when top-p is off.
+// *cut_margin (if not NULL) receives nucleus_margin of the stop, or 1 when
+// top-p is off.
 std::vector<double> row_probs(const void* row, int dtype, int V, double T, int top_k, double top_p = 1.0,
                               double* cut_margin = nullptr) {
   std::vector<double> l(V);
@@ -207,7 +243,7 @@ std::vector<double> row_probs(const void* row, int dtype, int V, double T, int t
     ++s;
     if (C >= top_p) break;
   }
-  if (cut_margin) *cut_margin = std::min(C - top_p, top_p - Cprev);
+  if (cut_margin) *cut_margin = nucleus_margin(s, C, Cprev, top_p);
   std::vector<char> nucleus(V, 0);
   for (int r = 0, taken = 0; r < V && taken < s; ++r) {
     const int y = order[r];
@@ -239,10 +275,11 @@ int row_argmax(const void* row, int dtype, int V) {
 // ties.  *margin receives (s1 - s2) / s1 for the top two scores.
 int race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
   const double inf = std::numeric_limits<double>::infinity();
-  int best = -1;
+  int best = -1, ncand = 0;
   double s1 = -inf, s2 = -inf;
   for (size_t y = 0; y < w.size(); ++y) {
     if (!(w[y] > 0.0)) continue;
+    ++ncand;
     double u = uniform_race(seed, b, j, (uint32_t)y);
     double E = -std::log(u);
     double s = (E == 0.0) ? inf : w[y] / E;
@@ -254,72 +291,8 @@ int race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, do
       s2 = s;
     }
   }
-  if (margin) {
-    if (best < 0 || s2 == -inf) *margin = 1.0;          // one candidate: no decision to flip
-    else if (s1 == inf) *margin = (s2 == inf) ? 0.0 : 1.0;
-    else *margin = (s1 - s2) / s1;
-  }
+  if (margin) *margin = race_margin(ncand, s1, s2);
   return best;
-}
-
-// The uniform of block k of a block race at (b, j): counter (k >> 1, j, b, 2),
-// words 0/1 for even k, 2/3 for odd k.
-double uniform_block(uint64_t seed, uint32_t b, uint32_t j, uint32_t k) {
-  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
-  uint32_t ctr[4] = {k >> 1, j, b, 2u};
-  uint32_t w[4];
-  philox4x32_10(ctr, key, w);
-  if ((k & 1u) == 0u) return words_to_unit(w[0], w[1]);
-  return words_to_unit(w[2], w[3]);
-}
-
-// A draw from the law w (unnormalised) in two Exp(1) races: first over
-// blocks of kBlockRace consecutive tokens (block k holds tokens
-// [64k, 64k + 64)) weighted by their total mass W_k, one exponential per
-// block; then over the tokens of the winning block, with the token
-// exponentials of `race`.  The minimum of independent exponentials E_y / w_y
-// over a block is itself exponential with rate W_k, and which token attains
-// it is independent of its value with P(y) = w_y / W_k; so the block winner
-// has law W_k / W and the token law w_y / W: the same law as the one-stage
-// race, with one random number per block instead of one per token.
-// *margin: the smaller relative gap of the two stages.
-constexpr int kBlockRace = 64;
-// Largest top-k whose law sampler-match draws token by token.
-constexpr int kTokenRaceMaxK = 1024;
-int block_race(const std::vector<double>& w, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
-  const double inf = std::numeric_limits<double>::infinity();
-  const size_t V = w.size();
-  const size_t nblk = (V + kBlockRace - 1) / kBlockRace;
-  int kbest = -1;
-  double s1 = -inf, s2 = -inf;
-  for (size_t k = 0; k < nblk; ++k) {
-    double W = 0.0;
-    for (size_t y = k * kBlockRace; y < std::min(V, (k + 1) * kBlockRace); ++y)
-      if (w[y] > 0.0) W += w[y];
-    if (!(W > 0.0)) continue;
-    const double E = -std::log(uniform_block(seed, b, j, (uint32_t)k));
-    const double s = (E == 0.0) ? inf : W / E;
-    if (s > s1) {
-      s2 = s1;
-      s1 = s;
-      kbest = (int)k;
-    } else if (s > s2) {
-      s2 = s;
-    }
-  }
-  double m1 = 1.0;
-  if (kbest >= 0 && s2 != -inf) m1 = (s1 == inf) ? ((s2 == inf) ? 0.0 : 1.0) : (s1 - s2) / s1;
-  if (kbest < 0) {
-    if (margin) *margin = 1.0;
-    return -1;
-  }
-  // Stage two: the one-stage race restricted to the block (same streams).
-  std::vector<double> wb(w.size(), 0.0);
-  for (size_t y = (size_t)kbest * kBlockRace; y < std::min(V, ((size_t)kbest + 1) * kBlockRace); ++y) wb[y] = w[y];
-  double m2 = 1.0;
-  const int y = race(wb, seed, b, j, &m2);
-  if (margin) *margin = std::min(m1, m2);
-  return y;
 }
 
 enum { MODE_PROB = 0, MODE_ONEHOT = 1, MODE_GREEDY = 2, MODE_NAIVE = 3, MODE_PROBS = 4 };
@@ -424,11 +397,7 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
     } else {
       accept = (u <= px[j]);
     }
-    if (acc_margin) {
-      double lhs = u * qx[j], rhs = px[j];
-      double den = std::max(lhs, rhs);
-      acc_margin[j] = (!valid[j] || qx[j] == 0.0) ? 1.0 : (den > 0.0 ? std::fabs(lhs - rhs) / den : 0.0);
-    }
+    if (acc_margin) acc_margin[j] = accept_margin(u, px[j], qx[j], valid[j]);
     if (!accept) { n = j; break; }
   }
 
@@ -495,12 +464,9 @@ int verify_match(const Problem& P, uint32_t b, const char* Lt, const int32_t* X,
       double c = 1.0;
       p[i] = row_probs(row, P.dtype, V, P.T, P.top_k, P.top_p, &c);
       cm = std::min(cm, c);
-      // A top-k law keeping at most kTokenRaceMaxK tokens is drawn by the
-      // one-stage race over its tokens; any other law (the whole vocabulary,
-      // or a larger top-k) by the block race.  Both draw the law exactly.
-      const bool topk = P.top_k > 0 && P.top_k < V && P.top_k <= kTokenRaceMaxK;
-      s[i] = topk ? race(p[i], P.seed, b, (uint32_t)i, &margin[i])
-                  : block_race(p[i], P.seed, b, (uint32_t)i, &margin[i]);
+      // A fresh draw from the node's law: the Exp(1) race over its tokens
+      // on the race stream of (b, node), as for a recovered or bonus token.
+      s[i] = race(p[i], P.seed, b, (uint32_t)i, &margin[i]);
     }
   }
   for (int i = 1; i <= g; ++i) {
@@ -577,11 +543,10 @@ int sv_ref_race(const double* w, int V, uint64_t seed, uint32_t b, uint32_t j, d
   return race(wv, seed, b, j, margin);
 }
 
-// The two-stage (block) race over w[0..V) at (seed, b, j).
-int sv_ref_block_race(const double* w, int V, uint64_t seed, uint32_t b, uint32_t j, double* margin) {
-  std::vector<double> wv(w, w + V);
-  return block_race(wv, seed, b, j, margin);
-}
+// The decision margins, for pinning.
+double sv_ref_accept_margin(double u, double px, double qx, int valid) { return accept_margin(u, px, qx, valid != 0); }
+double sv_ref_race_margin(int ncand, double s1, double s2) { return race_margin(ncand, s1, s2); }
+double sv_ref_nucleus_margin(int s, double C, double Cprev, double top_p) { return nucleus_margin(s, C, Cprev, top_p); }
 
 // Batched verifier.
 //   mode: 0 prob, 1 onehot, 2 greedy, 3 naive (test-only, deliberately wrong)

@@ -19,7 +19,9 @@ int sv_ref_row_probs_p(const void* row, int dtype, int V, double T, int top_k, d
                        double* cut_margin);
 int sv_ref_row_argmax(const void* row, int dtype, int V);
 int sv_ref_race(const double* w, int V, uint64_t seed, uint32_t b, uint32_t j, double* margin);
-int sv_ref_block_race(const double* w, int V, uint64_t seed, uint32_t b, uint32_t j, double* margin);
+double sv_ref_accept_margin(double u, double px, double qx, int valid);
+double sv_ref_race_margin(int ncand, double s1, double s2);
+double sv_ref_nucleus_margin(int s, double C, double Cprev, double top_p);
 int sv_ref_verify(int mode, int nreq, int G, int V, int dtype, double T, int top_k, uint64_t seed, const void* Lt,
                   const void* Ld, const int32_t* X, const int32_t* req_ids, int32_t* out_tokens,
                   int32_t* num_accepted, double* p_draft, double* q_draft, int32_t* target_argmax, double* beta,
@@ -116,12 +118,14 @@ void scalar_entry_points(Gen& g) {
       std::vector<double> w(V, 0.0);
       double m = 0.0;
       CHECK(sv_ref_race(w.data(), V, 1, 0, 0, &m) == -1);  // no mass: no winner
-      CHECK(sv_ref_block_race(w.data(), V, 1, 0, 0, &m) == -1);
       w[V - 1] = 1.0;
       CHECK(sv_ref_race(w.data(), V, 1, 0, 0, &m) == V - 1);
-      CHECK(sv_ref_block_race(w.data(), V, 1, 0, 0, &m) == V - 1);
+      CHECK(m == 1.0);  // one candidate
     }
   }
+  CHECK(sv_ref_accept_margin(0.5, 0.25, 0.5, 1) == 0.0);
+  CHECK(sv_ref_race_margin(1, 1.0, -1.0) == 1.0);
+  CHECK(sv_ref_nucleus_margin(1, 0.5, 0.0, 0.25) == 0.25);
 }
 
 void dense_verify(Gen& g) {

@@ -3,7 +3,10 @@
 Bar: p(x_j), q(x_j) within 1e-5 absolute; accepted lengths and every
 emitted token bit-identical on every request whose decisions all had a
 relative margin above 1e-4 (oracle margins), identical before the near-tie
-position otherwise; greedy results identical everywhere.
+position otherwise; exemptions used on at most 1e-4 of the rows (so none on
+calls of fewer than 10,000 rows, and none at all on the full-size
+workloads); greedy results identical everywhere.  Near-tie rows are counted
+and must be under 0.01% of each full-size workload's rows.
 """
 
 import numpy as np
@@ -221,17 +224,17 @@ FULL_CONFIGS = ["prob_f32_b8_g4_v32000", "greedy_bf16_b64_g5_v128256", "prob_f32
                 "onehot_bf16_b512_g3_v262144", "prob_topk64_bf16_b1024_g8_v256000"]
 
 
+# Near-tie rows of each full-size workload, filled by the test below (the
+# oracle's diagnostics pass over every request) for the fraction test.
+_NEAR_TIE = {}
+
+
 @pytest.mark.parametrize("name", FULL_CONFIGS)
 def test_full_size_every_request(sv, name):
     """The five workloads at their full sizes, in the launch configuration the
     benchmark times: p(x_j), q(x_j) within 1e-5 and accepted lengths and
-    tokens identical on every request outside flagged near-ties (the greedy
-    path, including the argmax, everywhere).  The near-tie exemption may be
-    used on fewer than 0.01% of the B (G + 1) rows: requests that differ from
-    the oracle after a near-tie decision are counted against that bar.  The
-    rows holding a near-tie decision (oracle margin <= 1e-4) are counted and
-    reported: one of 9216 on the headline workload, on which the GPU agrees
-    as well."""
+    tokens identical to the oracle's on every request, near-tie rows
+    included (no exemption is used); on the greedy path the argmax too."""
     wl = W[name]
     dev = torch.device("cuda:0")
     print(f"[full] {name}: generating on the GPU", flush=True)
@@ -251,12 +254,29 @@ def test_full_size_every_request(sv, name):
     torch.cuda.empty_cache()
     print(f"[full] {name}: oracle over all {wl.B} requests", flush=True)
     ref = oracle_run(wl.entry, host, wl.temperature, wl.top_k, wl.verify_seed)
-    rep = assert_parity(wl.entry, got, ref)
-    rows = wl.B * (wl.G + 1)
-    ties = near_tie_rows(ref)
-    rep["near_tie_rows"] = ties
+    rep = assert_parity(wl.entry, got, ref, max_exempt_fraction=0.0)
+    _NEAR_TIE[name] = (near_tie_rows(ref), wl.B * (wl.G + 1))
     print(f"[full] {name}: {rep}", flush=True)
-    assert rep["mismatch_tie"] < 1e-4 * rows, f"near-tie exemptions used on {rep['mismatch_tie']} of {rows} rows"
+    assert rep["mismatch_tie"] == 0
+
+
+# The committed seeds put one near-tie row (an oracle decision margin <=
+# 1e-4) in the 9216 rows of the B=1024, gamma=8 top-64 workload: 0.0109%,
+# above the 0.01% bar.  The expected count there is about 0.14 rows; the
+# GPU agrees with the oracle on that row as well (the test above).
+_NEAR_TIE_MISS = {"prob_topk64_bf16_b1024_g8_v256000": "1 near-tie row of 9216 (0.0109%) on the committed seeds"}
+
+
+@pytest.mark.parametrize("name", [pytest.param(n, marks=pytest.mark.xfail(reason=_NEAR_TIE_MISS[n], strict=True))
+                                  if n in _NEAR_TIE_MISS else n for n in FULL_CONFIGS])
+def test_full_size_near_tie_fraction(name):
+    """Near-tie rows (a decision the oracle took with a relative margin <=
+    1e-4) must be under 0.01% of the B (G + 1) rows of each workload."""
+    if name not in _NEAR_TIE:
+        pytest.skip("needs test_full_size_every_request of the same workload in this session")
+    ties, rows = _NEAR_TIE[name]
+    print(f"[near-tie] {name}: {ties} of {rows} rows ({100.0 * ties / rows:.4f}%)", flush=True)
+    assert ties < 1e-4 * rows
 
 
 @pytest.mark.parametrize("G", [1, 8])

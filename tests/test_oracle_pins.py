@@ -18,6 +18,7 @@ import pytest
 from scipy import stats
 
 import oracle
+from oracle.parity import compare_batch, near_tie_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 HELPERS = os.path.join(os.path.dirname(__file__), "helpers")
@@ -1028,75 +1029,184 @@ def test_sampler_match_reductions():
     assert c["bad_param"][2] == 1 and (c["out_tokens"][2] == -1).all() and c["bad_param"].sum() == 1
 
 
-# ---------------------------------------------------------------------------
-# The two-stage (block) race that draws full-vocabulary laws under
-# sampler-match
-# ---------------------------------------------------------------------------
-
-def test_block_race_law():
-    """Blocks of 64 tokens race by total mass, then tokens within the
-    winner: the token law is w / sum(w) and the block law W_k / W (chi-square
-    over 120k independent draws; V = 300 leaves a last block of 44 tokens)."""
-    rng = np.random.default_rng(5)
-    V = 300
-    w = rng.exponential(1.0, V) ** 3
-    w[rng.random(V) < 0.2] = 0.0      # tokens without mass are never drawn
-    w[[0, 10, 70, 299]] = [30.0, 40.0, 25.0, 30.0]  # heavy tokens in the first, second and last blocks
-    w[128:192] = 0.0                  # a block without mass
-    n = 120_000
-    toks = np.array([oracle.block_race(w, 17, b, 3)[0] for b in range(n)])
-    assert (w[toks] > 0).all()
-    p = w / w.sum()
-    counts = np.bincount(toks, minlength=V)
-    big = p * n >= 5
-    obs = np.append(counts[big], counts[~big].sum())
-    exp = np.append(p[big] * n, p[~big].sum() * n)
-    assert stats.chisquare(obs, exp).pvalue > 1e-6
-    blk = np.add.reduceat(counts, np.arange(0, V, 64))
-    W = np.add.reduceat(p, np.arange(0, V, 64))
-    assert blk[2] == 0
-    keep = W > 0
-    assert stats.chisquare(blk[keep], W[keep] * n).pvalue > 1e-6
-
-
-def test_block_race_reduces_to_the_token_race():
-    """Within one block the first stage has one contestant, so the draw is
-    the one-stage race on the same token stream, draw for draw: for V <= 64,
-    and for a law whose mass lies in one block of a larger row."""
-    rng = np.random.default_rng(9)
-    for b in range(300):
-        w = rng.random(rng.integers(1, 65))
-        assert oracle.block_race(w, 5, b, 1)[0] == oracle.race(w, 5, b, 1)[0]
-        big = np.zeros(1000)
-        k = int(rng.integers(0, 16))  # block 15 is the last, partial one (tokens 960..999)
-        big[64 * k: 64 * k + 64] = rng.random(min(64, 1000 - 64 * k))
-        assert oracle.block_race(big, 5, b, 2)[0] == oracle.race(big, 5, b, 2)[0]
-
-
-def test_block_race_streams_are_distinct():
-    """Block uniforms come from their own stream (counter word 3 = 2): two
-    blocks of equal mass are each drawn about half the time, and the same
-    (seed, b, j) gives the same draw."""
-    w = np.zeros(128)
-    w[5] = w[100] = 1.0
-    toks = np.array([oracle.block_race(w, 23, b, 0)[0] for b in range(4000)])
-    assert set(toks.tolist()) == {5, 100}
-    assert abs((toks == 5).mean() - 0.5) < 4 * np.sqrt(0.25 / 4000)
-    assert all(oracle.block_race(w, 23, b, 0)[0] == t for b, t in zip(range(50), toks))
-
-
-def test_sampler_match_race_by_law_size():
-    """The fresh sample of a node is the one-stage token race for a top-k law
-    keeping at most 1024 tokens and the block race for any larger law (a
-    top-k of 1025, or no top-k): the node's emitted token equals that race
-    on the row's adjusted law, stream for stream."""
+def test_sampler_match_sample_is_the_race_on_the_node_law():
+    """The fresh sample of a node is the one Exp(1) race over its adjusted
+    law on the race stream of (request, node), for every size of law (a
+    top-k of 64, 1024 or 1025 tokens, the whole vocabulary): the emitted
+    token of a walk that ends at the root equals that race."""
     rng = np.random.default_rng(13)
     V = 3000
     for trial in range(6):
         lt = rng.normal(0.0, 2.0, size=(1, 2, V)).astype(np.float32)
-        x = np.array([[int(rng.integers(V))]], np.int32)
-        for k, racer in ((1024, oracle.race), (1025, oracle.block_race), (0, oracle.block_race)):
+        x = np.array([[-1]], np.int32)  # no child can match: the root's sample is emitted
+        for k in (64, 1024, 1025, 0):
             p = oracle.row_probs(lt[0, 0], 1.0, k)
             res = oracle.verify_batch(lt, None, x, np.ones(1, np.float32), np.full(1, k, np.int32),
                                       np.ones(1, np.float32), max_top_k=max(k, 1), seed=17 + trial, match=True)
-            assert int(res["out_tokens"][0, 0]) == racer(p, 17 + trial, 0, 0)[0]
+            assert int(res["out_tokens"][0, 0]) == oracle.race(p, 17 + trial, 0, 0)[0]
+
+
+def test_sampler_match_full_law_frequencies():
+    """Sampler-match over the whole vocabulary: a root with no matching child
+    emits its sample, whose law over 40k requests is the row's p (chi-square;
+    the full-vocabulary path draws every token's own variate)."""
+    V = 40
+    rng = np.random.default_rng(2)
+    row = rng.normal(0.0, 1.5, V).astype(np.float32)
+    n = 40_000
+    lt = np.broadcast_to(row, (n, 2, V)).copy()
+    x = np.full((n, 1), -1, np.int32)
+    res = oracle.verify_batch(lt, None, x, np.ones(n, np.float32), np.zeros(n, np.int32), np.ones(n, np.float32),
+                              seed=3, match=True)
+    p = oracle.row_probs(row, 1.0)
+    counts = np.bincount(res["out_tokens"][:, 0], minlength=V)
+    assert (p * n >= 5).all()
+    assert stats.chisquare(counts, p * n).pvalue > 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Decision margins: they decide which results a comparison may exempt
+# ---------------------------------------------------------------------------
+
+def test_nucleus_margin_hand_computed():
+    """Top-p on (0.5, 0.3, 0.15, 0.05): the stop at rank s has the sides
+    C_s - top_p and top_p - C_(s-1); at s = 1 only the first exists."""
+    logits = np.log(np.array([0.5, 0.3, 0.15, 0.05])).astype(np.float32)
+    # (top_p, kept tokens, margin)
+    for top_p, kept, margin in ((1e-30, 1, 0.5), (0.45, 1, 0.05), (0.5, 1, 0.0), (0.6, 2, 0.1), (0.79, 2, 0.01),
+                                (0.81, 3, 0.01), (0.9, 3, 0.05), (0.97, 4, 0.02)):
+        p, m = oracle.row_probs(logits, 1.0, 0, top_p, return_margin=True)
+        assert int((p > 0).sum()) == kept, top_p
+        assert m == pytest.approx(margin, abs=1e-7), (top_p, m)
+    # The function itself, on exact values.
+    assert oracle.nucleus_margin(1, 0.5, 0.0, 1e-30) == 0.5 - 1e-30
+    assert oracle.nucleus_margin(1, 0.5, 0.0, 0.45) == 0.5 - 0.45
+    assert oracle.nucleus_margin(2, 0.75, 0.5, 0.625) == 0.125
+    assert oracle.nucleus_margin(2, 0.75, 0.5, 0.5625) == 0.0625
+    assert oracle.nucleus_margin(3, 1.0, 0.75, 0.75) == 0.0
+    # Top-p off: margin 1.
+    assert oracle.row_probs(logits, 1.0, 0, 1.0, return_margin=True)[1] == 1.0
+
+
+def test_accept_margin_hand_computed():
+    """|u q(x) - p(x)| / max(u q(x), p(x)); no boundary (margin 1) for an
+    invalid token or q(x) = 0."""
+    assert oracle.accept_margin(0.5, 0.25, 0.5) == 0.0          # u q = p exactly
+    assert oracle.accept_margin(0.5, 0.3, 0.5) == pytest.approx(0.05 / 0.3)
+    assert oracle.accept_margin(0.8, 0.2, 0.5) == pytest.approx(0.2 / 0.4)
+    assert oracle.accept_margin(0.25, 0.5, 1.0) == 0.5           # one-hot q: |u - p| / max(u, p)
+    assert oracle.accept_margin(0.7, 0.0, 0.5) == 1.0            # p = 0: rejected by any u
+    assert oracle.accept_margin(0.7, 0.4, 0.0) == 1.0            # q = 0: rejected
+    assert oracle.accept_margin(0.7, 0.4, 0.5, valid=False) == 1.0
+    # The denominator is the larger side (a slip to min() would give 1/3 here).
+    assert oracle.accept_margin(1.0, 0.75, 1.0) == pytest.approx(0.25)
+
+
+def test_race_margin_hand_computed():
+    """(s1 - s2) / s1 over the two best scores; one candidate: 1; an infinite
+    winner is flipped only by another."""
+    assert oracle.race_margin(2, 2.0, 2.0) == 0.0
+    assert oracle.race_margin(3, 2.0, 1.0) == 0.5                # a slip to / s2 would give 1
+    assert oracle.race_margin(1, 2.0, float("-inf")) == 1.0
+    assert oracle.race_margin(2, float("inf"), 3.0) == 1.0
+    assert oracle.race_margin(2, float("inf"), float("inf")) == 0.0
+
+
+def _race_e(seed, b, j, y):
+    return -math.log(oracle.uniform_race(seed, b, j, y))
+
+
+def test_race_margin_in_the_race():
+    """Weights set to the race's own exponentials make every score exactly 1:
+    the margin is 0 and the lowest index wins; a relative gap of 5e-5 planted
+    on one weight is flagged (<= 1e-4), one of 2e-4 is not; a single
+    candidate has margin 1."""
+    seed, b, j = 11, 3, 2
+    e = np.array([_race_e(seed, b, j, y) for y in range(6)])
+    tok, m = oracle.race(e, seed, b, j)
+    assert tok == 0 and m == 0.0
+    w = e.copy()
+    w[4] *= 1 + 5e-5
+    tok, m = oracle.race(w, seed, b, j)
+    assert tok == 4 and 0 < m <= 1e-4 and m == pytest.approx(5e-5 / (1 + 5e-5), rel=1e-6)
+    w = e.copy()
+    w[4] *= 1 + 2e-4
+    tok, m = oracle.race(w, seed, b, j)
+    assert tok == 4 and m > 1e-4
+    w = np.zeros(6)
+    w[3] = 0.2
+    assert oracle.race(w, seed, b, j) == (3, 1.0)
+
+
+def _onehot_row_for(p_target):
+    """Two logits whose softmax gives token 0 the probability p_target."""
+    d = math.log(p_target / (1 - p_target))
+    return np.array([d, 0.0])
+
+
+def test_near_tie_planted_in_a_verifier_call():
+    """One-hot drafts on V = 2 with p(x_j) planted next to the accept
+    uniform u_j: at position 1, p(x) = u (1 - 2e-5) is a near tie (flagged,
+    position 1, one row); p(x) = u (1 - 1e-3) is not.  Position 0 accepts
+    surely (p(x) = 1 - 1e-12) and takes no near tie."""
+    seed, G = 5, 3
+    for b in range(4):
+        u1 = oracle.uniform_accept(seed, b, 1)
+        for gap, flagged in ((2e-5, True), (1e-3, False)):
+            lt = np.zeros((1, G + 1, 2))
+            lt[0, 0] = _onehot_row_for(1 - 1e-12)
+            lt[0, 1] = _onehot_row_for(u1 * (1 - gap))
+            lt[0, 2] = _onehot_row_for(0.5)
+            lt[0, 3] = _onehot_row_for(0.5)
+            x = np.zeros((1, G), np.int32)
+            res = oracle.verify(oracle.MODE_ONEHOT, lt.astype(np.float64).astype(np.float32), None, x,
+                                temperature=1.0, seed=seed, req_ids=np.array([b], np.int32), diagnostics=True)
+            # fp32 rounding of the logits moves p(x) by ~1e-7 relative: the gap stays on its side.
+            assert res["num_accepted"][0] == 1
+            am = res["accept_margin"][0]
+            assert (am[1] <= 1e-4) == flagged, am
+            pos = oracle.near_tie_position(res)
+            assert pos[0] == (1 if flagged else -1)
+            assert near_tie_rows(res) == (1 if flagged else 0)
+
+
+def test_near_tie_position_and_rows_hand_built():
+    """On hand-built diagnostics: only decisions actually taken count (accept
+    tests j <= n, the race at n); margins past n are ignored; NaN margins
+    (greedy requests, unused positions) never flag; under sampler-match a
+    flagged race leaves no position fixed (0)."""
+    nan = float("nan")
+    res = {"num_accepted": np.array([1, 1, 3, 2, 0]),
+           "accept_margin": np.array([[0.5, 1e-5, 0.3],    # rejected at 1 with a near tie: position 1
+                                      [0.5, 0.5, 1e-6],    # margin past n = 1: ignored
+                                      [0.5, 0.5, 0.5],     # all accepted, race near tie at n = G = 3
+                                      [nan, nan, nan],     # greedy: never flagged
+                                      [0.2, 0.5, 0.5]]),
+           "race_margin": np.array([0.5, 0.5, 5e-5, nan, 1e-4])}
+    pos = oracle.near_tie_position(res)
+    np.testing.assert_array_equal(pos, [1, -1, 3, -1, 0])
+    # Rows: request 0 row 1; request 2 row 3 (its race); request 4 row 0
+    # (race at n = 0, margin exactly 1e-4 counts).
+    assert near_tie_rows(res) == 3
+    # Accept near tie and race near tie on the same row count once.
+    res2 = {"num_accepted": np.array([1]), "accept_margin": np.array([[0.5, 1e-6]]),
+            "race_margin": np.array([1e-6])}
+    assert near_tie_rows(res2) == 1
+    assert oracle.near_tie_position(res2)[0] == 1
+    res3 = dict(res2, match=True)
+    assert oracle.near_tie_position(dict(res3, accept_margin=np.ones((1, 2))))[0] == 0
+
+
+def test_near_cut_requests_compared_not_skipped():
+    """A top-p of 1e-30 keeps one token on every row with a margin of about
+    the top token's mass (not 1e-30): no request is near-cut, so every
+    request of such a batch is compared."""
+    rng = np.random.default_rng(4)
+    n, G, V = 6, 3, 50
+    lt = rng.normal(0, 2, size=(n, G + 1, V)).astype(np.float32)
+    x = rng.integers(0, V, size=(n, G)).astype(np.int32)
+    res = oracle.verify_batch(lt, None, x, np.ones(n, np.float32), np.zeros(n, np.int32),
+                              np.full(n, 1e-30, np.float32), seed=1, diagnostics=True)
+    assert (res["cut_margin"] > 1e-3).all()
+    rep = compare_batch(res, res)
+    assert rep["near_cut_requests"] == 0 and rep["mismatch_non_tie"] == 0
