@@ -142,7 +142,7 @@ typedef enum {
  * out_tokens stays [B][gamma+1].  With cu_draft NULL every request has gamma
  * positions, rows [B][gamma+1] and [B][gamma].  A cu_draft array that breaks
  * these rules makes every request invalid: out_tokens -1, num_accepted 0,
- * p_draft / q_draft not written, error bit 4. */
+ * p_draft / q_draft not written; the sticky error word gets bit 2 (value 4). */
 typedef struct {
   int32_t draft_kind;      /* sv_draft_kind */
   int32_t reserved;        /* 0 */
@@ -156,7 +156,8 @@ typedef struct {
                               parents[.] of node i is its parent node, in
                               0..i-1.  Target row i is the law after node i's
                               path.  A request whose parents break this rule
-                              emits nothing (error bit 2). */
+                              emits nothing; the sticky error word gets bit 1
+                              (value 2). */
 } sv_layout;
 
 /* Per-request sampling settings of spec_verify_batch: DEVICE arrays of
@@ -180,7 +181,7 @@ typedef struct {
  * A request whose settings break these rules (T negative, NaN or infinite;
  * top_k negative or in (max_top_k, vocab); top_p NaN, <= 0 or > 1) emits
  * nothing: out_tokens all -1, num_accepted 0, p_draft and q_draft 0; the
- * sticky error word gets bit 2.  Other requests are unaffected. */
+ * sticky error word gets bit 1 (value 2).  Other requests are unaffected. */
 typedef struct {
   const float* temperature;
   const int32_t* top_k;
@@ -244,13 +245,10 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  *   draft_tokens: as described by layout;
  *   outputs: see sv_outputs.
  * Sampler-match (layout->draft_kind SV_DRAFT_MATCH): every node gets a fresh
- * sample from its row's adjusted law (temperature 0: the argmax).  A top-k
- * law keeping at most 1024 tokens is drawn by the Exp(1) race over its kept
- * tokens on the stream of (request, node); any other law by two races: over the
- * blocks of 64 consecutive tokens weighted by their mass (block k's variate
- * from counter (k >> 1, node, request, 2), words 0/1 for even k, 2/3 for odd
- * k), then over the tokens of the winning block (the token streams of the
- * one-stage race).  Both give the law exactly.  From the root the walk follows
+ * sample from its row's adjusted law (temperature 0: the argmax), drawn by
+ * the Exp(1) race over the law's kept tokens on the race stream of (request,
+ * node): the draw of the recovered and bonus tokens, with the node in place
+ * of the position.  From the root the walk follows
  * the child whose token equals the sample (the lowest-indexed one if several
  * do) and emits the sample where no child matches: out_tokens holds the
  * accepted tokens and that sample, num_accepted the accepted depth.  Lossless
@@ -273,9 +271,10 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
                             const sv_outputs* outputs, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronises `stream`, then copies the sticky device error word of the
- * last call that used `workspace` to *host_code: bit 0 (1) = a draft token
- * was out of range; bit 1 (2) = a request of spec_verify_batch had invalid
- * settings; bit 2 (4) = its cu_draft array broke the layout rules. */
+ * last call that used `workspace` to *host_code: bit 0 (value 1) = a draft
+ * token was out of range; bit 1 (value 2) = a request of spec_verify_batch
+ * had invalid settings or tree parents; bit 2 (value 4) = its cu_draft array
+ * broke the layout rules. */
 sv_status sv_read_device_error(const void* workspace, int32_t* host_code, void* stream);
 
 /* Per-kernel timing for measurement.  While enabled, every launch of the

@@ -162,9 +162,9 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
   pl->big_k = mk > pl->kcap && pl->V > 1;  // some request may take a full-row top-k cut
   if ((sm && sm->top_p) || pl->big_k)
     off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * sizeof(RowCut), kWsAlign);
-  // Sampler-match: one sample per target row; the block race splits rows
-  // like the softmax pass (a quarter of the rows taken as its own).
-  pl->Srr = splits_for((pl->rows_t + 3) / 4, pl->V, 2048, 8192);
+  // Sampler-match: one sample per target row; the full-row race over rows
+  // is ALU-bound, so it splits rows finely (at least 2048 tokens a split).
+  pl->Srr = splits_for(pl->rows_t, pl->V, 8192, 2048);
   pl->segrr = seg_for(pl->V, pl->Srr);
   pl->Srr = (pl->V + pl->segrr - 1) / pl->segrr;
   pl->off_rdesc = off;
@@ -356,17 +356,18 @@ sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, 
 }
 
 // One sample per target row of a full-row request (sampler-match): the
-// two-stage block race, descriptors and slots per row, winners to `samples`.
+// full-row race over every such row (descriptors and slots per row), then
+// the winners to `samples`.
 template <typename ET, bool CUT>
-sv_status run_block_race(const Plan& pl, const void* lt, uint32_t k0, uint32_t k1, char* ws, hipStream_t st) {
+sv_status run_row_race(const Plan& pl, const void* lt, uint32_t k0, uint32_t k1, char* ws, hipStream_t st) {
   TimedLaunch t(2, st);
   const RaceDesc* rdesc = (const RaceDesc*)(ws + pl.off_rdesc);
   unsigned long long* rslots = (unsigned long long*)(ws + pl.off_rslots);
-  hipLaunchKernelGGL((sv::block_race_kernel<ET, 256, CUT>), dim3(pl.rows_t * pl.Srr), dim3(256), 0, st,
-                     (const ET*)lt, pl.V, pl.Srr, pl.segrr, k0, k1, rdesc, rslots);
-  hipLaunchKernelGGL((sv::block_finish_kernel<ET, CUT>), dim3((pl.rows_t + 3) / 4), dim3(256), 0, st, (const ET*)lt,
-                     pl.rows_t, pl.V, k0, k1, rdesc, (const unsigned long long*)rslots,
-                     (int32_t*)(ws + pl.off_samples));
+  hipLaunchKernelGGL((sv::race_full_kernel<ET, 256, CUT, false>), dim3(pl.rows_t * pl.Srr), dim3(256), 0, st,
+                     (const ET*)lt, (const ET*)nullptr, (const float*)nullptr, pl.V, pl.Srr, pl.segrr, k0, k1, rdesc,
+                     rslots);
+  hipLaunchKernelGGL(sv::match_samples_kernel, dim3((pl.rows_t + 255) / 256), dim3(256), 0, st, pl.rows_t, rdesc,
+                     (const unsigned long long*)rslots, (int32_t*)(ws + pl.off_samples));
   t.done();
   return check_launch();
 }
@@ -574,7 +575,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       t.done();
       if ((s = check_launch()) != SV_OK) return s;
     }
-    s = use_cut ? run_block_race<ET, true>(pl, lt, k0, k1, ws, st) : run_block_race<ET, false>(pl, lt, k0, k1, ws, st);
+    s = use_cut ? run_row_race<ET, true>(pl, lt, k0, k1, ws, st) : run_row_race<ET, false>(pl, lt, k0, k1, ws, st);
     if (s != SV_OK) return s;
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::match_walk_kernel<ET>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,

@@ -1331,137 +1331,18 @@ __global__ __launch_bounds__(256) void sample_topk_kernel(const uint64_t* __rest
   if (lane == 0) samples[row] = best ? (int32_t)key_index(best) : -1;
 }
 
-// Samples of full rows by the two-stage race.  Stage one races the blocks of
-// 64 consecutive tokens (block k: tokens [64k, 64k + 64)) weighted by their
-// kept mass W_k, one Exp(1) variate per block from counter (k >> 1, node,
-// request, 2), words 0/1 for even k and 2/3 for odd k; stage two races the
-// tokens of the winning block with the token streams of the one-stage race.
-// The smallest of independent exponentials E_y / w_y over a block is
-// exponential with rate W_k, independent of which token attains it, so the
-// token law is w_y / W as for the one-stage race, with one random number per
-// 64 tokens: the pass is a plain re-read of each row.
-//
-// Stage one, (row, vocabulary split): splits start on multiples of 64
-// tokens, so a block never straddles two workgroups.  The split is taken in
-// chunks of kBlockChunk blocks: a group of 64 / EPV lanes holds one block
-// (one 16-byte vector per lane) and sums its masses with shuffles into LDS;
-// then every thread scores whole blocks (one Philox block each), so the
-// random numbers are drawn with all lanes busy.  The row's workgroups merge
-// (score, block) keys with a 64-bit atomic max.
-constexpr int kRaceBlock = 64;
-constexpr int kBlockChunk = 1024;
-
-__device__ __forceinline__ uint4 block_race_words(uint32_t k0, uint32_t k1, uint32_t b, uint32_t j, uint32_t k) {
-  return philox10(make_uint4(k >> 1, j, b, 2u), k0, k1);
-}
-
-template <typename ET, int NT, bool CUT>
-__global__ __launch_bounds__(NT) void block_race_kernel(const ET* __restrict__ lt, int V, int S, int seg,
-                                                        uint32_t k0, uint32_t k1, const RaceDesc* __restrict__ desc,
-                                                        unsigned long long* __restrict__ slots) {
-  constexpr int EPV = Elem<ET>::kPerVec;
-  constexpr int LPB = kRaceBlock / EPV;  // lanes per block
-  constexpr int BPS = NT / LPB;           // blocks per workgroup step
-  constexpr int U = 4;                    // steps in flight
-  __shared__ float wsh[kBlockChunk];
-  __shared__ uint64_t red[NT / kWave];
-  const int row = blockIdx.x / S, s = blockIdx.x - row * S;
-  const RaceDesc d = desc[row];
-  if (d.n < 0) return;
-  const ET* rp = lt + d.prow;
-  const int a = s * seg;
-  const int e = min(V, a + seg);
-  const int tid = threadIdx.x, li = tid % LPB;
-  const bool vec_ok = (((uintptr_t)rp) & 15u) == 0u;  // a is a multiple of 64 elements
-  const int kb0 = a / kRaceBlock, nblk = (e - a + kRaceBlock - 1) / kRaceBlock;
-  const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)d.n;
-  // The nucleus cut as a float compare (see race_full_kernel).
-  const bool cut = CUT && d.kp != 0ull;
-  const float kv = cut ? key_value(d.kp) : 0.f;
-  const int ki = cut ? (int)key_index(d.kp) : 0;
-  uint64_t best = 0ull;
-  for (int c0 = 0; c0 < nblk; c0 += kBlockChunk) {
-    const int cn = min(kBlockChunk, nblk - c0);
-    for (int q0 = tid / LPB; q0 < cn; q0 += U * BPS) {
-      float f[U][EPV];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = q0 + u * BPS;
-        const int y0 = (kb0 + c0 + q) * kRaceBlock + li * EPV;
-        if (q < cn && vec_ok && y0 + EPV <= e) {
-          Elem<ET>::unpack(load_stream((const uint4*)(rp + y0)), f[u]);
-        } else {
-#pragma unroll
-          for (int k = 0; k < EPV; ++k) f[u][k] = (q < cn && y0 + k < e) ? Elem<ET>::load1(rp + y0 + k) : -INFINITY;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = q0 + u * BPS;
-        const int y0 = (kb0 + c0 + q) * kRaceBlock + li * EPV;
-        float w = 0.f;
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-          const float p = __builtin_amdgcn_exp2f((f[u][k] - d.mp) * d.c);
-          w += (!cut || f[u][k] > kv || (f[u][k] == kv && y0 + k <= ki)) ? p : 0.f;
-        }
-#pragma unroll
-        for (int m = LPB / 2; m >= 1; m >>= 1) w += __shfl_xor(w, m);
-        if (li == 0 && q < cn) wsh[q] = w;
-      }
-    }
-    __syncthreads();
-    for (int q = tid; q < cn; q += NT) {
-      const float w = wsh[q];
-      if (w > 0.f) {
-        const uint32_t kb = (uint32_t)(kb0 + c0 + q);
-        const uint4 r = block_race_words(k0, k1, ub, un, kb);
-        const float E = (kb & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
-        const uint64_t key = make_key(w * d.inv_zp * __builtin_amdgcn_rcpf(E), kb);
-        best = key > best ? key : best;
-      }
-    }
-    __syncthreads();  // wsh is refilled by the next chunk
-  }
-  best = wave_max_u64(best);
-  if (lane_id() == 0) red[tid / kWave] = best;
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t bk = red[0];
-    for (int k = 1; k < NT / kWave; ++k) bk = red[k] > bk ? red[k] : bk;
-    if (bk) atomicMax(&slots[3 * row], (unsigned long long)bk);
-  }
-}
-
-// Stage two, one wave per row: the one-stage race over the 64 tokens of the
-// winning block; the winner is the row's sample (-1 if no block had mass).
-template <typename ET, bool CUT>
-__global__ __launch_bounds__(256) void block_finish_kernel(const ET* __restrict__ lt, int rows_t, int V, uint32_t k0,
-                                                           uint32_t k1, const RaceDesc* __restrict__ desc,
-                                                           const unsigned long long* __restrict__ slots,
-                                                           int32_t* __restrict__ samples) {
-  const int row = blockIdx.x * 4 + threadIdx.x / kWave, lane = lane_id();
-  if (row >= rows_t) return;
-  const RaceDesc d = desc[row];
-  if (d.n < 0) return;
-  const unsigned long long win = slots[3 * row];
-  uint64_t best = 0ull;
-  if (win) {
-    const int y = (int)key_index(win) * kRaceBlock + lane;
-    if (y < V) {
-      // The same mass expression as stage one (a block with mass keeps it).
-      const float l = Elem<ET>::load1(lt + d.prow + y);
-      float p = __builtin_amdgcn_exp2f((l - d.mp) * d.c) * d.inv_zp;
-      if (CUT && make_key(l, (uint32_t)y) < d.kp) p = 0.f;
-      if (p > 0.f) {
-        const uint4 r = race_block(k0, k1, (uint32_t)d.rb, (uint32_t)d.n, (uint32_t)y);
-        const float E = (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
-        best = make_key(p * __builtin_amdgcn_rcpf(E), (uint32_t)y);
-      }
-    }
-  }
-  best = wave_max_u64(best);
-  if (lane == 0) samples[row] = best ? (int32_t)key_index(best) : -1;
+// Samples of full rows: race_full_kernel runs over (row, vocabulary split)
+// with one descriptor per row (match_prep_kernel), the one-stage Exp(1) race
+// over the row's kept tokens on the race stream of (request, node); this
+// pass moves each row's winning key into its sample (-1 if no token had
+// mass, which a row's own maximum rules out).  One thread per row.
+__global__ __launch_bounds__(256) void match_samples_kernel(int rows_t, const RaceDesc* __restrict__ desc,
+                                                            const unsigned long long* __restrict__ slots,
+                                                            int32_t* __restrict__ samples) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows_t || desc[row].n < 0) return;
+  const unsigned long long win = slots[3 * (size_t)row];
+  samples[row] = win ? (int32_t)key_index(win) : -1;
 }
 
 // The walk, one wave per request: p_parent(x) of every node (its acceptance
