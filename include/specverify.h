@@ -65,7 +65,9 @@ typedef enum {
   SV_ERR_DTYPE = 2,        /* dtype not SV_F32 / SV_BF16, or misaligned logits */
   SV_ERR_WORKSPACE = 3,    /* workspace null, misaligned or too small */
   SV_ERR_HIP = 4,          /* a HIP runtime call or kernel launch failed */
-  SV_ERR_UNSUPPORTED = 5   /* gamma > 16384: not implemented */
+  SV_ERR_UNSUPPORTED = 5,  /* gamma > 16384; spec_verify_prob_noalloc: top_k > 1024 */
+  SV_ERR_SCRATCH = 6       /* spec_verify_prob_noalloc: the call needs more than
+                              SV_NOALLOC_SCRATCH_BYTES of device scratch */
 } sv_status;
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -118,6 +120,29 @@ sv_status spec_verify_onehot(const sv_params* params, const void* target_logits,
 sv_status spec_verify_greedy(const sv_params* params, const void* target_logits, const int32_t* draft_tokens,
                              int32_t* out_tokens, int32_t* num_accepted, int32_t* target_argmax,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* spec_verify_prob for callers that cannot allocate device memory or pass a
+ * workspace: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and Philox
+ * streams as spec_verify_prob (bit-identical outputs), with the library's
+ * own device scratch in place of `workspace`: a static device array of
+ * SV_NOALLOC_SCRATCH_BYTES in the library's code object, one per GPU, held
+ * until the process ends.  Its address is looked up on the first call on
+ * each device; no call allocates or frees anything.
+ *   error_word: DEVICE int32 (may be NULL) that receives the call's error
+ *     word, bits as sv_read_device_error.
+ * Limits: the call must need at most SV_NOALLOC_SCRATCH_BYTES of scratch
+ * (sv_workspace_bytes(params) bytes; the B=1024, gamma=8, V=256000 top-64
+ * call needs about 9 MB), else SV_ERR_SCRATCH; a top_k above 1024 (below
+ * vocab) returns SV_ERR_UNSUPPORTED.  Nothing is enqueued after an error.
+ * Every call on one GPU uses that GPU's single scratch array: calls that
+ * overlap on one GPU (different streams, or host threads) race and must be
+ * ordered by the caller.  The kernels clear what must start at zero, so the
+ * array's contents left by an earlier call do not matter. */
+#define SV_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+sv_status spec_verify_prob_noalloc(const sv_params* params, const void* target_logits, const void* draft_logits,
+                                   const int32_t* draft_tokens, int32_t* out_tokens, int32_t* num_accepted,
+                                   float* p_draft, float* q_draft, int32_t* error_word, void* stream);
 
 /* Form of the draft in spec_verify_batch. */
 typedef enum {

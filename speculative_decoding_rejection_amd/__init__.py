@@ -7,9 +7,9 @@ memory.  There is no fallback: if the library is not built, importing a
 function raises.
 
 Same names as the C ABI: sv_workspace_bytes, sv_workspace_bytes_batch,
-sv_status_string, spec_verify_prob, spec_verify_onehot, spec_verify_greedy,
-spec_verify_batch, sv_read_device_error, sv_kernel_timing_enable / _reset /
-_read.  ``verify`` and ``verify_batch`` are convenience wrappers that
+sv_status_string, spec_verify_prob, spec_verify_prob_noalloc,
+spec_verify_onehot, spec_verify_greedy, spec_verify_batch,
+sv_read_device_error, sv_kernel_timing_enable / _reset / _read.  ``verify`` and ``verify_batch`` are convenience wrappers that
 allocate the outputs and the workspace.
 """
 
@@ -25,7 +25,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # build variants); by default the in-tree build is loaded.
 LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_PKG, "libspecverify.so")
 
-SV_OK, SV_ERR_INVALID_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED = range(6)
+SV_OK, SV_ERR_INVALID_ARG, SV_ERR_DTYPE, SV_ERR_WORKSPACE, SV_ERR_HIP, SV_ERR_UNSUPPORTED, SV_ERR_SCRATCH = range(7)
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 SV_F32, SV_BF16 = 0, 1
 SV_DRAFT_LOGITS, SV_DRAFT_ONEHOT, SV_DRAFT_PROBS, SV_DRAFT_MATCH = 0, 1, 2, 3
 FAMILY_ROWS, FAMILY_ACCEPT, FAMILY_RACE = 0, 1, 2
@@ -102,6 +103,8 @@ def load_library():
     lib.sv_status_string.restype = ctypes.c_char_p
     lib.spec_verify_prob.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_prob.restype = ctypes.c_int
+    lib.spec_verify_prob_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.spec_verify_prob_noalloc.restype = ctypes.c_int
     lib.spec_verify_onehot.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_onehot.restype = ctypes.c_int
     lib.spec_verify_greedy.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -170,6 +173,14 @@ def spec_verify_prob(params, target_logits, draft_logits, draft_tokens, out_toke
                                          _ptr(draft_tokens), _ptr(out_tokens), _ptr(num_accepted), _ptr(p_draft),
                                          _ptr(q_draft), _ptr(workspace), workspace.numel(), _stream(stream))
     _check(st, "spec_verify_prob")
+
+
+def spec_verify_prob_noalloc(params, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted, p_draft,
+                             q_draft, error_word=None, stream=None):
+    st = load_library().spec_verify_prob_noalloc(ctypes.byref(params), _ptr(target_logits), _ptr(draft_logits),
+                                                 _ptr(draft_tokens), _ptr(out_tokens), _ptr(num_accepted),
+                                                 _ptr(p_draft), _ptr(q_draft), _ptr(error_word), _stream(stream))
+    _check(st, "spec_verify_prob_noalloc")
 
 
 def spec_verify_onehot(params, target_logits, draft_tokens, out_tokens, num_accepted, p_draft, workspace,

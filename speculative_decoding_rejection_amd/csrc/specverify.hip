@@ -633,6 +633,60 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
 // top-k is a cut over each full row.
 bool large_top_k(const sv_params* p) { return p && p->top_k > kMaxTopK && p->top_k < p->vocab; }
 
+// The probabilistic-draft call once planned: argument checks against the
+// plan, then the kernels on `workspace`.
+sv_status prob_planned(const Plan& pl, uint64_t seed, const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, int32_t* out_tokens, int32_t* num_accepted, float* p_draft,
+                       float* q_draft, void* workspace, size_t workspace_bytes, void* stream) {
+  sv_status s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
+  if (s != SV_OK) return s;
+  if (!draft_logits) return SV_ERR_INVALID_ARG;
+  if (!aligned(draft_logits, (size_t)pl.esize)) return SV_ERR_DTYPE;
+  if ((p_draft && !aligned(p_draft, 4)) || (q_draft && !aligned(q_draft, 4))) return SV_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (pl.dtype == SV_F32)
+    return verify_sampled<float, 0>(pl, seed, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted,
+                                    p_draft, q_draft, ws, st);
+  return verify_sampled<uint16_t, 0>(pl, seed, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted,
+                                     p_draft, q_draft, ws, st);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of spec_verify_prob_noalloc: a device array in the library's code
+// object (each GPU that loads it holds its own copy until the process ends).
+// Host code never uses the array's name as an address: its device address
+// is looked up once per device with hipGetSymbolAddress (with that device
+// current) and kept in g_noalloc_ptr.  Calls on one GPU share its copy.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = SV_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+char* g_noalloc_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+sv_status noalloc_scratch(char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return SV_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return SV_ERR_HIP;
+    }
+    g_noalloc_ptr[dev] = (char*)p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return SV_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -654,7 +708,8 @@ const char* sv_status_string(sv_status s) {
     case SV_ERR_DTYPE: return "unsupported dtype or misaligned logits";
     case SV_ERR_WORKSPACE: return "workspace missing, misaligned (256 B) or smaller than sv_workspace_bytes()";
     case SV_ERR_HIP: return "HIP runtime or kernel launch failure";
-    case SV_ERR_UNSUPPORTED: return "gamma above 16384 is not supported";
+    case SV_ERR_UNSUPPORTED: return "unsupported: gamma above 16384, or (no-alloc entry) a top_k above 1024";
+    case SV_ERR_SCRATCH: return "the call needs more device scratch than spec_verify_prob_noalloc holds (16 MiB)";
   }
   return "unknown status";
 }
@@ -672,18 +727,27 @@ sv_status spec_verify_prob(const sv_params* params, const void* target_logits, c
   Plan pl;
   sv_status s = make_plan(params, kEntryProb, &pl);
   if (s != SV_OK) return s;
-  s = check_common(pl, target_logits, draft_tokens, out_tokens, num_accepted, workspace, workspace_bytes);
+  return prob_planned(pl, params->seed, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted,
+                      p_draft, q_draft, workspace, workspace_bytes, stream);
+}
+
+sv_status spec_verify_prob_noalloc(const sv_params* params, const void* target_logits, const void* draft_logits,
+                                   const int32_t* draft_tokens, int32_t* out_tokens, int32_t* num_accepted,
+                                   float* p_draft, float* q_draft, int32_t* error_word, void* stream) {
+  if (large_top_k(params)) return SV_ERR_UNSUPPORTED;  // the full-row cut runs as a batch call (side streams)
+  Plan pl;
+  sv_status s = make_plan(params, kEntryProb, &pl);
   if (s != SV_OK) return s;
-  if (!draft_logits) return SV_ERR_INVALID_ARG;
-  if (!aligned(draft_logits, (size_t)pl.esize)) return SV_ERR_DTYPE;
-  if ((p_draft && !aligned(p_draft, 4)) || (q_draft && !aligned(q_draft, 4))) return SV_ERR_INVALID_ARG;
-  hipStream_t st = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  if (pl.dtype == SV_F32)
-    return verify_sampled<float, 0>(pl, params->seed, target_logits, draft_logits, draft_tokens, out_tokens,
-                                    num_accepted, p_draft, q_draft, ws, st);
-  return verify_sampled<uint16_t, 0>(pl, params->seed, target_logits, draft_logits, draft_tokens, out_tokens,
-                                     num_accepted, p_draft, q_draft, ws, st);
+  if (pl.total > kNoAllocScratchBytes) return SV_ERR_SCRATCH;
+  if (error_word && !aligned(error_word, 4)) return SV_ERR_INVALID_ARG;
+  char* ws = nullptr;
+  if ((s = noalloc_scratch(&ws)) != SV_OK) return s;
+  s = prob_planned(pl, params->seed, target_logits, draft_logits, draft_tokens, out_tokens, num_accepted, p_draft,
+                   q_draft, ws, kNoAllocScratchBytes, stream);
+  if (s != SV_OK || !error_word) return s;
+  hipLaunchKernelGGL(sv::copy_word_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream,
+                     (const int32_t*)(ws + pl.off_err), error_word);
+  return check_launch();
 }
 
 sv_status spec_verify_onehot(const sv_params* params, const void* target_logits, const int32_t* draft_tokens,

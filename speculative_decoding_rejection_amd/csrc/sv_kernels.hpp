@@ -1593,4 +1593,9 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
   }
 }
 
+// Copies the error word of a call into a caller's device word.
+__global__ __launch_bounds__(64) void copy_word_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst) {
+  if (threadIdx.x == 0) *dst = *src;
+}
+
 }  // namespace sv

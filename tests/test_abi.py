@@ -216,3 +216,25 @@ def test_batch_workspace_holds_the_split_nucleus(sv, B, G):
     need = rows * 16 + rows * 4 + items * 4098 * 8 + split_rows * 2048 * 8
     assert nuc - topk >= need
     assert nuc - topk <= need + split_rows * 64 + 16 * 4096  # state records and alignment
+
+
+def test_noalloc_limits_before_any_gpu_call(sv):
+    """spec_verify_prob_noalloc checks its parameters and its scratch limit
+    before any HIP call: an oversized call, a top-k above 1024 and bad sizes
+    are refused on a machine without a GPU."""
+    lib = sv.load_library()
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced
+
+    def call(p):
+        return lib.spec_verify_prob_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, None, None)
+
+    big = sv.make_params(4096, 8, 256000, sv.SV_BF16, 0.7, 1024, 1)
+    assert sv.sv_workspace_bytes(big) > sv.SV_NOALLOC_SCRATCH_BYTES
+    assert call(big) == sv.SV_ERR_SCRATCH
+    assert call(sv.make_params(4, 2, 5000, sv.SV_BF16, 0.7, 2000, 1)) == sv.SV_ERR_UNSUPPORTED
+    assert call(sv.make_params(0, 2, 5000, sv.SV_BF16, 0.7, 0, 1)) == sv.SV_ERR_INVALID_ARG
+    assert call(sv.make_params(4, 2, 5000, sv.SV_BF16, 0.0, 0, 1)) == sv.SV_ERR_INVALID_ARG
+    # The headline call fits.
+    head = sv.make_params(1024, 8, 256000, sv.SV_BF16, 0.7, 64, 42)
+    assert sv.sv_workspace_bytes(head) <= sv.SV_NOALLOC_SCRATCH_BYTES
+    assert "16 MiB" in sv.sv_status_string(sv.SV_ERR_SCRATCH)
