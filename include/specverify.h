@@ -317,6 +317,14 @@ sv_status sv_kernel_timing_enable(int enable);
 sv_status sv_kernel_timing_reset(void);
 sv_status sv_kernel_timing_read(int family, double* total_ms, int64_t* launches);
 
+/* Measurement only: enqueues one read of `bytes` (a multiple of 16) of the
+ * DEVICE buffer `buf` (16-byte aligned), with the 16-byte nontemporal loads
+ * of the row passes and nothing else, one workgroup per 512 KB: the
+ * streaming-read ceiling the row passes' bandwidth is compared with.  `sink`
+ * (DEVICE, 256 uint32, 4-byte aligned) is written only by a data-dependent
+ * test that keeps the loads alive.  Asynchronous on `stream`. */
+sv_status sv_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,8 @@ function raises.
 Same names as the C ABI: sv_workspace_bytes, sv_workspace_bytes_batch,
 sv_status_string, spec_verify_prob, spec_verify_prob_noalloc,
 spec_verify_onehot, spec_verify_greedy, spec_verify_batch,
-sv_read_device_error, sv_kernel_timing_enable / _reset / _read.  ``verify`` and ``verify_batch`` are convenience wrappers that
+sv_read_device_error, sv_kernel_timing_enable / _reset / _read,
+sv_stream_read.  ``verify`` and ``verify_batch`` are convenience wrappers that
 allocate the outputs and the workspace.
 """
 
@@ -125,6 +126,8 @@ def load_library():
     lib.sv_kernel_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                           ctypes.POINTER(ctypes.c_int64)]
     lib.sv_kernel_timing_read.restype = ctypes.c_int
+    lib.sv_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.sv_stream_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -262,6 +265,12 @@ def sv_kernel_timing_read(family: int) -> tuple[float, int]:
     _check(load_library().sv_kernel_timing_read(int(family), ctypes.byref(ms), ctypes.byref(n)),
            "sv_kernel_timing_read")
     return float(ms.value), int(n.value)
+
+
+def sv_stream_read(buf, sink, stream=None) -> None:
+    """One streaming read of the whole device tensor `buf` (measurement)."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().sv_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "sv_stream_read")
 
 
 def alloc_workspace(params: SvParams, device) -> torch.Tensor:

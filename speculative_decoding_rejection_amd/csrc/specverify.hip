@@ -891,4 +891,15 @@ sv_status sv_kernel_timing_read(int family, double* total_ms, int64_t* launches)
   return SV_OK;
 }
 
+sv_status sv_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes < 16 || bytes % 16 || !aligned(buf, 16) || !aligned(sink, 4)) return SV_ERR_INVALID_ARG;
+  const int64_t nvec = (int64_t)(bytes / 16);
+  const int64_t chunk = 32768;  // 512 KB per workgroup, the size of a headline logit row
+  const int64_t nblk = (nvec + chunk - 1) / chunk;
+  if (nblk > INT32_MAX) return SV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(sv::stream_read_kernel<8>, dim3((unsigned)nblk), dim3(256), 0, (hipStream_t)stream,
+                     (const uint4*)buf, nvec, chunk, sink);
+  return check_launch();
+}
+
 }  // extern "C"

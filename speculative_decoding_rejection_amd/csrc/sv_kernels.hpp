@@ -1593,6 +1593,30 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
   }
 }
 
+// Measurement only: the streaming-read ceiling the row passes are compared
+// with.  One workgroup per chunk of `chunk` 16-byte vectors, read with the
+// row passes' nontemporal loads, U in flight per thread; nothing is written
+// unless the xor of a workgroup's words hits one fixed value (which keeps
+// the loads alive and is otherwise never true in practice).
+template <int U>
+__global__ __launch_bounds__(256) void stream_read_kernel(const uint4* __restrict__ p, int64_t nvec, int64_t chunk,
+                                                          uint32_t* __restrict__ sink) {
+  const int64_t c0 = (int64_t)blockIdx.x * chunk;
+  const int64_t c1 = c0 + chunk < nvec ? c0 + chunk : nvec;
+  uint32_t acc = 0u;
+  for (int64_t i0 = c0 + threadIdx.x; i0 < c1; i0 += 256 * U) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = i0 + (int64_t)u * 256;
+      v[u] = i < c1 ? load_stream(p + i) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x & 255] = acc;
+}
+
 // Copies the error word of a call into a caller's device word.
 __global__ __launch_bounds__(64) void copy_word_kernel(const int32_t* __restrict__ src, int32_t* __restrict__ dst) {
   if (threadIdx.x == 0) *dst = *src;
