@@ -28,6 +28,14 @@ constexpr int kMaxTopK = 1024;
 constexpr int kMaxGamma = 16384;  // the top-k accept pass keeps one byte per position in LDS
 constexpr size_t kWsAlign = 256;
 constexpr int kEntryProb = 0, kEntryOnehot = 1, kEntryGreedy = 2;
+// A call whose logits total at most this many bytes splits its rows into
+// pieces of at least kSmallMinSeg elements (else 8192 / 2048).
+constexpr size_t kSmallCallBytes = (size_t)64 << 20;
+#ifndef SV_SMALL_MIN_SEG
+#define SV_SMALL_MIN_SEG 2048
+#endif
+constexpr int kSmallMinSeg = SV_SMALL_MIN_SEG;
+constexpr size_t kFusedLdsBytes = 32768;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -41,6 +49,8 @@ struct Plan {
   int S, seg;     // row-pass splits of the vocabulary (softmax / argmax)
   int Sr, segr;   // race-pass splits
   size_t off_err, off_part, off_cand, off_desc, off_slots, off_info, off_cut, total;
+  size_t off_gath;  // gathered draft-token logits, one float per row (full-row single-setting calls)
+  bool fused;       // full rows, G < 64: accept and race in one launch (accept_race_kernel)
   int Srr, segrr;                           // row-race splits (sampler-match)
   size_t off_rdesc, off_rslots, off_samples;  // per-row race descriptors, slots, samples
   // Nucleus of few rows split across workgroups: plan, row list, chunk
@@ -51,8 +61,11 @@ struct Plan {
   bool big_k;     // batch plans: a top-k above kcap is possible (full-row cut)
 };
 
+// Splits per row so that rows x splits stays within target_blocks (one
+// round of workgroups at full occupancy: 256 CUs x 8 workgroups of 256
+// threads = 2048), each split at least min_seg elements.
 int splits_for(int rows, int V, int target_blocks, int min_seg) {
-  int s = (target_blocks + rows - 1) / rows;
+  int s = target_blocks / rows;
   int smax = V / min_seg;
   if (smax < 1) smax = 1;
   if (s > smax) s = smax;
@@ -90,13 +103,20 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   q.c = entry == kEntryGreedy ? 0.f : (float)(1.4426950408889634 / (double)p->temperature);
   q.rows_t = (int)(B * (G + 1));
   q.rows_d = (int)(B * G);  // sized for the prob entry; unused by the others
-  q.S = splits_for(q.rows_t + q.rows_d, q.V, 2048, 8192);
+  const size_t nrows = (size_t)q.rows_t + (size_t)q.rows_d;
+  // Few rows: shorter splits, so that the row pass still spreads over the
+  // chip and each workgroup's share is one or two rounds of loads.
+  const bool small = nrows * (size_t)q.V * (size_t)q.esize <= kSmallCallBytes;
+  q.S = splits_for(q.rows_t + q.rows_d, q.V, 2048, small ? kSmallMinSeg : 8192);
   q.seg = seg_for(q.V, q.S);
   q.S = (q.V + q.seg - 1) / q.seg;
-  q.Sr = splits_for(q.B, q.V, 4096, 2048);
+  q.Sr = splits_for(q.B, q.V, 4096, small ? kSmallMinSeg : 2048);
   q.segr = seg_for(q.V, q.Sr);
   q.Sr = (q.V + q.segr - 1) / q.segr;
-  const size_t nrows = (size_t)q.rows_t + (size_t)q.rows_d;
+  // Accept and race in one launch when the request's row partials fit the
+  // fused kernel's LDS staging.
+  q.fused = entry != kEntryGreedy && q.K == 0 && q.G < 64 &&
+            (size_t)(2 * q.G + 1) * (size_t)q.S * 8 <= kFusedLdsBytes;
   size_t off = 0;
   q.off_err = off;
   off = align_up(off + sizeof(int), kWsAlign);
@@ -109,6 +129,8 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   off = align_up(off + (size_t)q.B * sizeof(RaceDesc), kWsAlign);
   q.off_slots = off;
   off = align_up(off + (size_t)q.B * 3 * 8, kWsAlign);
+  q.off_gath = off;
+  off = align_up(off + nrows * sizeof(float), kWsAlign);
   q.off_info = q.off_cut = off;
   q.total = off;
   q.L = sv::Layout{nullptr, (int64_t)q.V, (int64_t)q.V};
@@ -292,11 +314,13 @@ sv_status check_common(const Plan& pl, const void* target_logits, const int32_t*
 
 template <typename ET>
 sv_status run_rows_softmax(const Plan& pl, const void* lt, const void* ld, int nrows, char* ws, hipStream_t st,
-                           const ReqInfo* info = nullptr, int fam = 0) {
+                           const ReqInfo* info = nullptr, int fam = 0, const int32_t* X = nullptr) {
   TimedLaunch t(fam, st);
+  float* gath = X ? (float*)(ws + pl.off_gath) : nullptr;
+  unsigned long long* slots = X ? (unsigned long long*)(ws + pl.off_slots) : nullptr;
   hipLaunchKernelGGL((sv::rows_softmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(nrows * pl.S),
                      dim3(kRowThreads), 0, st, (const ET*)lt, (const ET*)ld, pl.rows_t, pl.V, pl.S, pl.seg, pl.c,
-                     (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err), info, pl.G, pl.L);
+                     (float2*)(ws + pl.off_part), (int*)(ws + pl.off_err), info, pl.G, pl.L, X, gath, slots);
   t.done();
   return check_launch();
 }
@@ -406,10 +430,26 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     t.done();
     return check_launch();
   }
-  s = run_rows_softmax<ET>(pl, lt, ld, nrows, ws, st);
-  if (s != SV_OK) return s;
   RaceDesc* desc = (RaceDesc*)(ws + pl.off_desc);
   unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
+  if (pl.fused) {
+    // Row pass (with the draft tokens' logits and the race slots cleared),
+    // then accept and race in one launch, then the finish.
+    s = run_rows_softmax<ET>(pl, lt, ld, nrows, ws, st, nullptr, 0, X);
+    if (s != SV_OK) return s;
+    TimedLaunch t(2, st);
+    const size_t lds = (size_t)(pl.G + 1 + (MODE == 0 ? pl.G : 0)) * pl.S * sizeof(float2);
+    hipLaunchKernelGGL((sv::accept_race_kernel<ET, MODE>), dim3(pl.B * pl.Sr), dim3(256), lds, st, (const ET*)lt,
+                       (const ET*)ld, (const float2*)(ws + pl.off_part), (const float*)(ws + pl.off_gath), X, pl.G,
+                       pl.V, pl.S, pl.rows_t, pl.c, k0, k1, pl.Sr, pl.segr, out, nacc, p_draft, q_draft, desc, slots,
+                       err);
+    hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, false>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
+                       pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
+    t.done();
+    return check_launch();
+  }
+  s = run_rows_softmax<ET>(pl, lt, ld, nrows, ws, st);
+  if (s != SV_OK) return s;
   {
     TimedLaunch t(1, st);
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,

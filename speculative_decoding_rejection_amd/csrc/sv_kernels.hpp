@@ -179,11 +179,20 @@ struct Slice {
 // Row pass 1: online softmax partials.  For each (row, split): m = max logit,
 // s = sum_y exp2((l_y - m) * c) with c = log2(e) / T.
 // ===========================================================================
+//
+// Single-setting calls on dense rows may also pass `gath` and `slots`: the
+// workgroup whose split holds the draft token x_j of its row stores that
+// row's logit l(x_j) in gath[row] (the accept decisions then need no gather
+// of their own), and split 0 of target row (b, 0) clears request b's race
+// slot for the race that follows.
 template <typename ET, int NT, int U>
 __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                           int rows_t, int V, int S, int seg, float c,
                                                           float2* __restrict__ part, int* __restrict__ err,
-                                                          const ReqInfo* __restrict__ info, int G, Layout L) {
+                                                          const ReqInfo* __restrict__ info, int G, Layout L,
+                                                          const int32_t* __restrict__ X = nullptr,
+                                                          float* __restrict__ gath = nullptr,
+                                                          unsigned long long* __restrict__ slots = nullptr) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int blk = blockIdx.x;
   const int row = blk / S, s = blk - row * S;
@@ -199,6 +208,15 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
   if (!rp) return;  // past the request's draft length
   const int a = s * seg;
   const int e = min(V, a + seg);
+  // The row's draft token (one wave-uniform load, issued before the stream
+  // and used after it).
+  int xg = -1;
+  if (gath) {
+    const int b = row < rows_t ? row / (G + 1) : (row - rows_t) / G;
+    const int j = row < rows_t ? row - b * (G + 1) : (row - rows_t) - b * G;
+    if (j < G) xg = X[(size_t)b * G + j];
+    if (slots && threadIdx.x == 0 && s == 0 && row < rows_t && j == 0) slots[3 * (size_t)b] = 0ull;
+  }
   Slice<ET> sl(rp, a, e);
   float m = -INFINITY, sum = 0.f;
   const int tid = threadIdx.x;
@@ -235,6 +253,7 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
       }
     }
   }
+  if (tid == NT - 1 && xg >= a && xg < e) gath[row] = Elem<ET>::load1(rp + xg);
   wave_lse(m, sum, c);
   __shared__ float2 red[NT / kWave];
   const int w = tid / kWave;
@@ -1169,10 +1188,19 @@ __device__ __forceinline__ void merge_partials(const float2* part, int S, float 
   Z = s;
 }
 
-// Merge of one row's S partials by one lane.
+// Merge of one row's S partials by one lane, in order; the loads run four
+// ahead of the merges.
 __device__ __forceinline__ void merge_row_lane(const float2* part, int S, float c, float& M, float& Z) {
   float m = -INFINITY, s = 0.f;
-  for (int k = 0; k < S; ++k) {
+  int k = 0;
+  for (; k + 4 <= S; k += 4) {
+    const float2 v0 = part[k], v1 = part[k + 1], v2 = part[k + 2], v3 = part[k + 3];
+    lse_merge(m, s, v0.x, v0.y, c);
+    lse_merge(m, s, v1.x, v1.y, c);
+    lse_merge(m, s, v2.x, v2.y, c);
+    lse_merge(m, s, v3.x, v3.y, c);
+  }
+  for (; k < S; ++k) {
     const float2 v = part[k];
     lse_merge(m, s, v.x, v.y, c);
   }
@@ -1432,15 +1460,13 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   return key;
 }
 
+// The race over split s of the row a descriptor names: this workgroup's best
+// (score, index) key, 0 if no token of the split has weight (every thread
+// gets the workgroup's key).
 template <typename ET, int NT, bool CUT, bool QP>
-__global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
-                                                       const float* __restrict__ qp, int V, int S, int seg,
-                                                       uint32_t k0, uint32_t k1, const RaceDesc* __restrict__ desc,
-                                                       unsigned long long* __restrict__ slots) {
-  const int b = blockIdx.x / S, s = blockIdx.x - b * S;
-  const RaceDesc d = desc[b];
-  const int n = d.n;
-  if (n < 0) return;
+__device__ __forceinline__ uint64_t race_split(const RaceDesc& d, const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                               const float* __restrict__ qp, int V, int s, int seg, uint32_t k0,
+                                               uint32_t k1) {
   const ET* rp = lt + d.prow;
   const ET* rq = (!QP && d.resid) ? ld + d.qrow : nullptr;
   const float* rqp = (QP && d.resid) ? qp + d.qrow : nullptr;
@@ -1459,7 +1485,7 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   r.kvq = r.cut_q ? key_value(d.kq) : 0.f;
   r.kip = r.cut_p ? (int)key_index(d.kp) : 0;
   r.kiq = r.cut_q ? (int)key_index(d.kq) : 0;
-  const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)n;
+  const uint32_t ub = (uint32_t)d.rb, un = (uint32_t)d.n;
   Slice<ET> sl(rp, a, e);
   // The draft row is read with 16-byte vectors only if it shares the target
   // row's alignment (rows start at different offsets when V * size is not a
@@ -1484,12 +1510,127 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
   __shared__ uint64_t red[NT / kWave];
   if (lane_id() == 0) red[tid / kWave] = key;
   __syncthreads();
-  if (tid == 0) {
-    uint64_t bk = red[0];
-    for (int k = 1; k < NT / kWave; ++k) bk = red[k] > bk ? red[k] : bk;
-    // Device-scope atomic max: coherent across XCDs; read by the next launch.
-    if (bk) atomicMax(&slots[3 * b], (unsigned long long)bk);
+  uint64_t bk = red[0];
+  for (int k = 1; k < NT / kWave; ++k) bk = red[k] > bk ? red[k] : bk;
+  return bk;
+}
+
+template <typename ET, int NT, bool CUT, bool QP>
+__global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                       const float* __restrict__ qp, int V, int S, int seg,
+                                                       uint32_t k0, uint32_t k1, const RaceDesc* __restrict__ desc,
+                                                       unsigned long long* __restrict__ slots) {
+  const int b = blockIdx.x / S, s = blockIdx.x - b * S;
+  const RaceDesc d = desc[b];
+  if (d.n < 0) return;
+  const uint64_t bk = race_split<ET, NT, CUT, QP>(d, lt, ld, qp, V, s, seg, k0, k1);
+  // Device-scope atomic max: coherent across XCDs; read by the next launch.
+  if (threadIdx.x == 0 && bk) atomicMax(&slots[3 * b], (unsigned long long)bk);
+}
+
+// Accept pass and race in one launch (single-setting calls over full rows,
+// dense rows, G < 64): workgroup (b, s) first takes request b's accept
+// decisions itself, then races split s of row n.  The request's row partials
+// are staged in LDS with one coalesced load (dynamic LDS: (2G+1) S float2,
+// G+1 rows without draft logits); wave 0 then takes the decisions (lane j =
+// position j: p(x_j), q(x_j) from the logits the row pass gathered, the fp64
+// test, the first rejection by one ballot).  Every workgroup of a request reaches the same n from the
+// same inputs; workgroup 0 writes the outputs and the descriptor
+// race_finish_kernel reads.  The row pass has cleared the race slots.
+template <typename ET, int MODE>
+__global__ __launch_bounds__(256) void accept_race_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
+                                                          const float2* __restrict__ part,
+                                                          const float* __restrict__ gath,
+                                                          const int32_t* __restrict__ X, int G, int V, int S,
+                                                          int rows_t, float c, uint32_t k0, uint32_t k1, int Sr,
+                                                          int segr, int32_t* __restrict__ out,
+                                                          int32_t* __restrict__ nacc, float* __restrict__ p_draft,
+                                                          float* __restrict__ q_draft, RaceDesc* __restrict__ desc,
+                                                          unsigned long long* __restrict__ slots,
+                                                          int* __restrict__ err) {
+  extern __shared__ float2 psh[];  // [rows of the request][S]
+  __shared__ RaceDesc dsh;
+  const int b = blockIdx.x / Sr, s = blockIdx.x - b * Sr;
+  const int tid = threadIdx.x, w = tid / kWave, lane = lane_id();
+  const int nt = G + 1, nrq = nt + (MODE == 0 ? G : 0);
+  const float2* pt = part + (size_t)b * nt * S;                            // target rows 0..G
+  const float2* pd = part + ((size_t)rows_t + (size_t)b * G) * S;          // draft rows 0..G-1
+  // Wave 0's per-position inputs are loaded first, so that their latency
+  // overlaps the staging of the partials (a gathered value is used only
+  // where the token is valid).
+  int x = -1;
+  float gp = 0.f, gq = 0.f;
+  if (w == 0 && lane < G) {
+    x = X[(size_t)b * G + lane];
+    gp = gath[(size_t)b * nt + lane];
+    if (MODE == 0) gq = gath[(size_t)rows_t + (size_t)b * G + lane];
   }
+  for (int e = tid; e < nrq * S; e += 256) psh[e] = e < nt * S ? pt[e] : pd[e - nt * S];
+  __syncthreads();
+  if (w == 0) {
+    // The arithmetic of accept_full_kernel: each lane merges its rows'
+    // partials in order (p(x_j), q(x_j)); the race rows n are merged by the
+    // wave.  The results are bit-identical to that kernel's.
+    const int j = lane;
+    bool rej = false;
+    float px = 0.f, qx = 0.f;
+    bool valid = false;
+    if (j < G) {
+      valid = x >= 0 && x < V;
+      if (valid) {
+        float M, Z;
+        merge_row_lane(psh + j * S, S, c, M, Z);
+        px = __builtin_amdgcn_exp2f((gp - M) * c) / Z;
+        qx = 1.f;
+        if (MODE == 0) {
+          merge_row_lane(psh + (nt + j) * S, S, c, M, Z);
+          qx = __builtin_amdgcn_exp2f((gq - M) * c) / Z;
+        }
+      }
+      const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
+      const double u = unit_from_words(r.x, r.y);
+      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      rej = !acc;
+    }
+    const uint64_t m = ballot(rej);
+    const int n = m ? (int)__builtin_ctzll(m) : G;
+    RaceDesc d;
+    d.n = n;
+    d.mask_tok = (MODE == 1 && n < G) ? __shfl(x, n) : -1;
+    d.resid = (MODE == 0 && n < G) ? 1 : 0;
+    d.rb = b;
+    float Z;
+    merge_partials(psh + n * S, S, c, d.mp, Z);
+    d.inv_zp = 1.f / Z;
+    d.mq = 0.f;
+    d.inv_zq = 0.f;
+    if (d.resid) {
+      merge_partials(psh + (nt + n) * S, S, c, d.mq, Z);
+      d.inv_zq = 1.f / Z;
+    }
+    d.c = c;
+    d.pad2[0] = d.pad2[1] = d.pad2[2] = 0;
+    d.kp = d.kq = 0ull;
+    d.prow = (int64_t)(((size_t)b * nt + n) * (size_t)V);
+    d.qrow = d.resid ? (int64_t)(((size_t)b * G + n) * (size_t)V) : 0;
+    if (lane == 0) dsh = d;
+    if (s == 0) {
+      if (j < G) {
+        if (p_draft) p_draft[(size_t)b * G + j] = px;
+        if (q_draft) q_draft[(size_t)b * G + j] = MODE == 1 ? (valid ? 1.f : 0.f) : qx;
+        if (!valid) atomicOr(err, kErrBadToken);
+      }
+      if (j <= G) out[(size_t)b * nt + j] = j < n ? x : -1;
+      if (lane == 0) {
+        nacc[b] = n;
+        desc[b] = d;
+      }
+    }
+  }
+  __syncthreads();
+  const RaceDesc d = dsh;
+  const uint64_t bk = race_split<ET, 256, false, false>(d, lt, ld, (const float*)nullptr, V, s, segr, k0, k1);
+  if (threadIdx.x == 0 && bk) atomicMax(&slots[3 * b], (unsigned long long)bk);
 }
 
 // Writes each request's race winner to out[request][n].  If the residual had
