@@ -19,7 +19,10 @@ using sv::ReqInfo;
 using sv::RowCut;
 
 constexpr int kRowThreads = 256;
-constexpr int kRowUnroll = 4;
+#ifndef SV_ROW_UNROLL
+#define SV_ROW_UNROLL 4
+#endif
+constexpr int kRowUnroll = SV_ROW_UNROLL;  // vectors per thread in flight in the softmax and argmax row passes
 #ifndef SV_TOPK_UNROLL
 #define SV_TOPK_UNROLL 12
 #endif

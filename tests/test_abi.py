@@ -238,3 +238,15 @@ def test_noalloc_limits_before_any_gpu_call(sv):
     head = sv.make_params(1024, 8, 256000, sv.SV_BF16, 0.7, 64, 42)
     assert sv.sv_workspace_bytes(head) <= sv.SV_NOALLOC_SCRATCH_BYTES
     assert "16 MiB" in sv.sv_status_string(sv.SV_ERR_SCRATCH)
+
+
+def test_stream_read_rejects_bad_arguments(sv):
+    """The read-ceiling measurement hook validates before enqueueing."""
+    lib = sv.load_library()
+    fake = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 8)
+    assert lib.sv_stream_read(None, 1 << 20, fake, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_stream_read(fake, 1 << 20, None, None) == sv.SV_ERR_INVALID_ARG
+    assert lib.sv_stream_read(fake, 24, fake, None) == sv.SV_ERR_INVALID_ARG   # not a multiple of 16
+    assert lib.sv_stream_read(odd, 1 << 20, fake, None) == sv.SV_ERR_INVALID_ARG  # not 16-byte aligned
+    assert lib.sv_stream_read(fake, 0, fake, None) == sv.SV_ERR_INVALID_ARG

@@ -102,9 +102,13 @@ def test_small_parity(sv, name, over, k):
 
 
 @pytest.mark.parametrize("entry,G,k", [("prob", 70, 0), ("onehot", 130, 0), ("greedy", 129, 0),
-                                       ("prob", 100, 16), ("onehot", 65, 64)])
+                                       ("prob", 100, 16), ("onehot", 65, 64), ("prob", 63, 0), ("onehot", 63, 0),
+                                       ("prob", 64, 0)])
 def test_long_drafts(sv, entry, G, k):
     # More than 64 positions: the accept passes walk positions in chunks.
+    # G = 63 is the largest draft the fused accept-and-race kernel takes
+    # (lane j = position j, out[0..G] in one wave); G = 64 the smallest the
+    # separate accept pass takes.
     base = {"prob": "prob_f32_b8_g4_v32000", "onehot": "onehot_bf16_b512_g3_v262144",
             "greedy": "greedy_bf16_b64_g5_v128256"}[entry]
     wl = W[base].scaled(B=3, G=G, V=777, chunk=3)

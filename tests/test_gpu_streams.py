@@ -76,3 +76,14 @@ def test_null_stream(sv, inp):
     torch.cuda.synchronize()
     for k in KEYS:
         assert torch.equal(got[k], ref[k]), k
+
+
+def test_stream_read_hook(sv):
+    """The read-ceiling measurement hook streams a buffer and writes its sink
+    only through a data-dependent test (never for an all-zero buffer)."""
+    buf = torch.zeros(1 << 24, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda:0")
+    for _ in range(3):
+        sv.sv_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum().item()) == 0
