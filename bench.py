@@ -104,13 +104,14 @@ def cpu_baseline(wl, inp, target_seconds: float, got: dict | None = None, check_
         lt = workloads.to_host_arrays(inp["target_logits"][sub])
         ld = workloads.to_host_arrays(inp["draft_logits"][sub]) if wl.has_draft_logits else None
         x = workloads.to_host_arrays(inp["draft_tokens"][sub])
-        t0 = time.perf_counter()
         if wl.has_settings:
             probs = inp["draft_probs"][sub].cpu().numpy() if wl.draft_probs else None
             lens = inp["lengths"][sub].cpu().numpy() if wl.lengths else None
             par = inp["parents"][sub].cpu().numpy() if inp.get("parents") is not None else None
-            ref = oracle.verify_batch(lt, None if wl.draft_probs else ld, x, inp["temperature"][sub].cpu().numpy(),
-                                      inp["top_k"][sub].cpu().numpy(), inp["top_p"][sub].cpu().numpy(),
+            tt, kk, pp = (inp[k][sub].cpu().numpy() for k in ("temperature", "top_k", "top_p"))
+        t0 = time.perf_counter()
+        if wl.has_settings:
+            ref = oracle.verify_batch(lt, None if wl.draft_probs else ld, x, tt, kk, pp,
                                       max_top_k=max(k for _, k, _ in wl.mix), seed=wl.verify_seed,
                                       draft_probs=probs, lengths=lens, match=wl.entry == "match", parents=par,
                                       diagnostics=diagnostics)
@@ -125,6 +126,12 @@ def cpu_baseline(wl, inp, target_seconds: float, got: dict | None = None, check_
     if t < target_seconds / 3 and n < wl.B:
         n = int(min(wl.B, max(n + 1, n * target_seconds / max(t, 1e-3))))
         t, _ = run(n)
+    reps = 1
+    if t < target_seconds / 3 and n == wl.B:
+        # The whole workload is a short sample: time it repeated (the same
+        # call, every request each time) for a bounded total.
+        reps = int(min(10000, max(2, target_seconds / 2 / max(t, 1e-4))))
+        t = sum(run(n)[0] for _ in range(reps)) / reps  # oracle time only, per call
     check = None
     if got is not None:
         m = wl.B if check_requests is None else min(wl.B, check_requests)
@@ -146,8 +153,10 @@ def cpu_baseline(wl, inp, target_seconds: float, got: dict | None = None, check_
         "unit": "verified draft positions/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"first {n} of {wl.B} requests of the same workload (fp64 oracle, OpenMP over requests), "
-                  f"{t:.2f} s wall",
+        "sample": (f"first {n} of {wl.B} requests of the same workload (fp64 oracle, OpenMP over requests), "
+                   f"{t:.2f} s wall" if reps == 1 else
+                   f"all {n} requests of the same workload (fp64 oracle, OpenMP over requests), the call timed "
+                   f"{reps} times, {t * 1e3:.2f} ms wall per call"),
         "check": check,
     }
 

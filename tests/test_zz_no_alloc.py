@@ -80,3 +80,48 @@ def test_noalloc_limits(sv):
     assert lib.spec_verify_prob_noalloc(ctypes.byref(p), f, f, f, f, f, None, None, None, None) == sv.SV_ERR_SCRATCH
     p2 = sv.make_params(4, 2, 5000, sv.SV_BF16, 0.7, 2000, 1)
     assert lib.spec_verify_prob_noalloc(ctypes.byref(p2), f, f, f, f, f, None, None, None, None) == sv.SV_ERR_UNSUPPORTED
+
+
+def test_noalloc_captured_in_graph(sv):
+    """The no-alloc call captured into a HIP graph (no workspace to allocate
+    during capture) and replayed three times, with eager calls of other
+    seeds on the same scratch between the replays: every replay equals the
+    eager result bit for bit."""
+    wl = workloads.WORKLOADS["prob_topk64_bf16_b1024_g8_v256000"].scaled(B=12, V=20011)
+    inp = workloads.generate(wl)
+    lt, ld, x = inp["target_logits"].to(DEV), inp["draft_logits"].to(DEV), inp["draft_tokens"].to(DEV)
+    B, G = x.shape
+
+    def call(seed):
+        params = sv.make_params(B, G, wl.V, wl.torch_dtype, wl.temperature, wl.top_k, seed)
+        r = {"out_tokens": torch.empty((B, G + 1), dtype=torch.int32, device=DEV),
+             "num_accepted": torch.empty((B,), dtype=torch.int32, device=DEV),
+             "p_draft": torch.empty((B, G), dtype=torch.float32, device=DEV),
+             "q_draft": torch.empty((B, G), dtype=torch.float32, device=DEV)}
+        sv.spec_verify_prob_noalloc(params, lt, ld, x, r["out_tokens"], r["num_accepted"], r["p_draft"],
+                                    r["q_draft"])
+        return r
+
+    keys = ("out_tokens", "num_accepted", "p_draft", "q_draft")
+    eager = {k: v.clone() for k, v in call(42).items()}
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(42)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        res = call(42)
+    for rep in range(3):
+        other = call(1000 + rep)
+        torch.cuda.synchronize()
+        for k in keys:
+            res[k].fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        print(f"[noalloc-graph] replay {rep}", flush=True)
+        for k in keys:
+            assert torch.equal(res[k], eager[k]), (rep, k)
+        assert not torch.equal(other["out_tokens"], eager["out_tokens"])
