@@ -410,7 +410,9 @@ int verify_one(const Problem& P, uint32_t b, const char* Lt, const char* Ld, con
         w[y] = std::max(p[n][y] - q[n][y], 0.0);
         mass += w[y];
       }
-      if (!(mass > 0.0)) w = p[n];  // unreachable in exact arithmetic
+      // Zero mass needs p = q at row n: reached when an out-of-range draft
+      // token forces the rejection of a position whose two laws agree.
+      if (!(mass > 0.0)) w = p[n];
     } else if (P.mode == MODE_ONEHOT) {
       // One-hot q: the residual is p with the draft token masked ([P4]
       // "기본값 greedy 드래프트에서도 분포가 지켜질까").

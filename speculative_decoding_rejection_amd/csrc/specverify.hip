@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point: include/specverify.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstddef>
 #include <cstdint>
@@ -107,12 +108,25 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   q.rows_t = (int)(B * (G + 1));
   q.rows_d = (int)(B * G);  // sized for the prob entry; unused by the others
   const size_t nrows = (size_t)q.rows_t + (size_t)q.rows_d;
-  // Few rows: shorter splits, so that the row pass still spreads over the
-  // chip and each workgroup's share is one or two rounds of loads.
+  // Splits of the row pass over `rows` rows.  Few rows: shorter splits, so
+  // that the pass still spreads over the chip and each workgroup's share is
+  // one or two rounds of loads.
+  auto row_splits = [&](size_t rows, int* seg) {
+    const bool sm = rows * (size_t)q.V * (size_t)q.esize <= kSmallCallBytes;
+    *seg = seg_for(q.V, splits_for((int)rows, q.V, 2048, sm ? kSmallMinSeg : 8192));
+    return (q.V + *seg - 1) / *seg;
+  };
+  // The sampled entries plan the splits over target and draft rows (the
+  // plan a batch call with the same settings starts from, so that its row
+  // sums merge alike); greedy reads only the target rows and takes an
+  // argmax, which no split changes.  The partials area fits either, so one
+  // workspace size serves every entry.
+  int seg_all = 0, seg_t = 0;
+  const int S_all = row_splits(nrows, &seg_all), S_t = row_splits((size_t)q.rows_t, &seg_t);
+  const size_t part_slots = std::max(nrows * (size_t)S_all, (size_t)q.rows_t * (size_t)S_t);
+  q.S = entry == kEntryGreedy ? S_t : S_all;
+  q.seg = entry == kEntryGreedy ? seg_t : seg_all;
   const bool small = nrows * (size_t)q.V * (size_t)q.esize <= kSmallCallBytes;
-  q.S = splits_for(q.rows_t + q.rows_d, q.V, 2048, small ? kSmallMinSeg : 8192);
-  q.seg = seg_for(q.V, q.S);
-  q.S = (q.V + q.seg - 1) / q.seg;
   q.Sr = splits_for(q.B, q.V, 4096, small ? kSmallMinSeg : 2048);
   q.segr = seg_for(q.V, q.Sr);
   q.Sr = (q.V + q.segr - 1) / q.segr;
@@ -125,7 +139,7 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   off = align_up(off + sizeof(int), kWsAlign);
   q.off_part = off;
   // Row-pass partials: float2 (softmax) or uint64 (argmax), both 8 bytes.
-  off = align_up(off + nrows * (size_t)q.S * 8, kWsAlign);
+  off = align_up(off + part_slots * 8, kWsAlign);
   q.off_cand = off;
   off = align_up(off + (q.K ? nrows * (size_t)q.kcap * 8 : 0), kWsAlign);
   q.off_desc = off;
@@ -174,10 +188,11 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
     pl->S = (pl->V + pl->seg - 1) / pl->seg;
     size_t off = pl->off_part;
     off = align_up(off + ((size_t)pl->rows_t + (size_t)pl->rows_d) * (size_t)pl->S * 8, kWsAlign);
-    const size_t shift = off - pl->off_cand;  // later sections move up
+    const size_t shift = off > pl->off_cand ? off - pl->off_cand : 0;  // later sections move up
     pl->off_cand += shift;
     pl->off_desc += shift;
     pl->off_slots += shift;
+    pl->off_gath += shift;
     pl->total += shift;
   }
   size_t off = pl->total;

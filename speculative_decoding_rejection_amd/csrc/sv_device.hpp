@@ -235,6 +235,19 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   return v;
 }
 
+// Sums of exponentials t in [0, 1] that do not depend on the order of the
+// terms: each term is truncated to a multiple of 2^-52 (NaN counts as 0) and
+// the integers are added exactly; at most 1024 terms keep the total below
+// 2^62.  Two kept sets that hold the same logits in different orders then
+// get the same normaliser, so their laws agree token by token (and p - q is
+// exactly 0 where the logits agree).
+__device__ __forceinline__ uint64_t unit_fixed(float t) { return t > 0.f ? (uint64_t)(t * 0x1.0p52f) : 0ull; }
+__device__ __forceinline__ float wave_sum_fixed(uint64_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
+  return (float)v * 0x1.0p-52f;
+}
+
 // Online softmax pair (m = max logit, s = sum exp2((l - m) * c)) merge.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2, float c) {
   const float M = fmaxf(m, m2);

@@ -309,13 +309,19 @@ __global__ __launch_bounds__(NT) void rows_argmax_kernel(const ET* __restrict__ 
       if (i < sl.nvec) {
         float f[EPV];
         Elem<ET>::unpack(v[u], f);
-        // Strict '>' in ascending index order keeps the first maximum.
+        float vm = f[0];
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) {
-          if (f[k] > bv || bi < 0) {
-            bv = f[k];
-            bi = sl.vec_index0(i) + k;
-          }
+        for (int k = 1; k < EPV; ++k) vm = fmaxf(vm, f[k]);
+        // Strict '>' in ascending index order keeps the first maximum: a
+        // vector only matters if its largest value beats the running one,
+        // and then through the first of its elements that holds it.
+        if (vm > bv || bi < 0) {
+          int kk = 0;  // the lowest k with f[k] == vm
+#pragma unroll
+          for (int k = EPV - 1; k >= 0; --k)
+            if (f[k] == vm) kk = k;
+          bv = vm;
+          bi = sl.vec_index0(i) + kk;
         }
       }
     }
@@ -893,13 +899,21 @@ __device__ __forceinline__ CandStats cand_stats(const uint64_t* ck, int K, float
     if (k) m = fmaxf(m, key_value(k));
   }
   m = wave_max_f(m);
-  float z = 0.f;
+  uint64_t z = 0ull;
   for (int i = lane; i < K; i += kWave) {
     const uint64_t k = ck[i];
-    if (k) z += __builtin_amdgcn_exp2f((key_value(k) - m) * c);
+    if (k) z += unit_fixed(__builtin_amdgcn_exp2f((key_value(k) - m) * c));
   }
-  z = wave_sum_f(z);
-  return CandStats{m, 1.f / z};
+  return CandStats{m, 1.f / wave_sum_fixed(z)};
+}
+
+// Probability of a kept token of logit v under stats st, rounded as a
+// product of its own: with contraction off here, the compiler cannot fold the
+// product into a later p - q (that fma would leave q's rounding error where
+// two equal laws give exactly 0).
+__device__ __forceinline__ float cand_p(float v, CandStats st, float c) {
+#pragma clang fp contract(off)
+  return __builtin_amdgcn_exp2f((v - st.m) * c) * st.inv_z;
 }
 
 // Probability of token x under a kept set (0 if x is not kept).
@@ -1000,14 +1014,14 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     const uint64_t k = cp[i];
     if (!k) continue;
     const uint32_t y = key_index(k);
-    const float p = __builtin_amdgcn_exp2f((key_value(k) - sp.m) * c) * sp.inv_z;
+    const float p = cand_p(key_value(k), sp, c);
     float wgt = p;
     if (n < g) {
       if (MODE == 0) {
         float q = 0.f;
         for (int t = 0; t < K; ++t) {
           const uint64_t kq = qkeys[t];
-          if (kq && key_index(kq) == y) q = __builtin_amdgcn_exp2f((key_value(kq) - sq.m) * c) * sq.inv_z;
+          if (kq && key_index(kq) == y) q = cand_p(key_value(kq), sq, c);
         }
         wgt = fmaxf(p - q, 0.f);
       } else if (MODE == 2) {
@@ -1085,7 +1099,7 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
   // Softmax over a kept set held one key per lane: (m, 1 / z) as cand_stats.
   auto stats_of = [&](uint64_t k) -> CandStats {
     const float m = wave_max_f(k ? key_value(k) : -INFINITY);
-    const float z = wave_sum_f(k ? __builtin_amdgcn_exp2f((key_value(k) - m) * c) : 0.f);
+    const float z = wave_sum_fixed(k ? unit_fixed(__builtin_amdgcn_exp2f((key_value(k) - m) * c)) : 0ull);
     return CandStats{m, 1.f / z};
   };
   auto prob_of = [&](uint64_t k, CandStats st, int x) -> float {
@@ -1132,7 +1146,7 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
   if (MODE == 0 && n < g) {
     const uint64_t kq = keys[nt + n][lane];
     const CandStats sq = stats_of(kq);
-    const float myq = kq ? __builtin_amdgcn_exp2f((key_value(kq) - sq.m) * c) * sq.inv_z : 0.f;
+    const float myq = kq ? cand_p(key_value(kq), sq, c) : 0.f;
     const uint32_t myqi = kq ? key_index(kq) : 0xFFFFFFFFu;
     const uint32_t y = key_index(kp);
     for (int t = 0; t < K; ++t) {
@@ -1146,7 +1160,7 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
   uint64_t best_w = 0ull, best_p = 0ull;
   if (kp) {
     const uint32_t y = key_index(kp);
-    const float p = __builtin_amdgcn_exp2f((key_value(kp) - sp.m) * c) * sp.inv_z;
+    const float p = cand_p(key_value(kp), sp, c);
     float wgt = p;
     if (n < g) {
       if (MODE == 0 || MODE == 2) wgt = fmaxf(p - q, 0.f);
@@ -1534,9 +1548,10 @@ __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt
 // are staged in LDS with one coalesced load (dynamic LDS: (2G+1) S float2,
 // G+1 rows without draft logits); wave 0 then takes the decisions (lane j =
 // position j: p(x_j), q(x_j) from the logits the row pass gathered, the fp64
-// test, the first rejection by one ballot).  Every workgroup of a request reaches the same n from the
-// same inputs; workgroup 0 writes the outputs and the descriptor
-// race_finish_kernel reads.  The row pass has cleared the race slots.
+// test, the first rejection by one ballot).  Every workgroup of a request
+// reaches the same n from the same inputs; workgroup 0 writes the outputs and
+// the descriptor race_finish_kernel reads.  The row pass has cleared the race
+// slots.
 template <typename ET, int MODE>
 __global__ __launch_bounds__(256) void accept_race_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                           const float2* __restrict__ part,

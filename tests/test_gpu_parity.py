@@ -126,6 +126,75 @@ def test_long_drafts(sv, entry, G, k):
         assert got["num_accepted"][0] == 100 and got["num_accepted"][1] == G
 
 
+def _greedy_tie_rows(B, G, V, seed):
+    """Target rows whose maximum is held several times: flat rows, integer
+    logits, a planted maximum at two lanes of one 16-byte vector and in two
+    splits (V odd: rows after the first start off a 16-byte boundary), the
+    maximum only in a row's last element, -0.0 before +0.0, and rows of
+    -inf.  The greedy rule takes the lowest index holding the maximum."""
+    rng = np.random.default_rng(seed)
+    lt = rng.standard_normal((B, G + 1, V))
+    for b in range(B):
+        for j in range(G + 1):
+            kind = (b * (G + 1) + j) % 7
+            r = lt[b, j]
+            if kind == 0:
+                r[:] = 0.0
+            elif kind == 1:
+                r[:] = np.round(r * 2.0)
+            elif kind == 2:
+                q = int(rng.integers(1, V // 16)) * 8
+                r[[q + 5, q + 3, V - 2 - (q % 997)]] = 9.0
+            elif kind == 3:
+                r[[V - 1, V // 2 + 1]] = [7.5, 7.25]
+            elif kind == 4:
+                r[:] = -np.abs(r) - 1.0
+                r[[int(rng.integers(V // 2, V)), int(rng.integers(1, V // 2))]] = [0.0, -0.0]
+            elif kind == 5:
+                r[:] = -np.inf
+            else:
+                r[:] = -np.inf
+                r[int(rng.integers(0, V))] = -3.0
+    return lt
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [20011, 131071])
+def test_greedy_ties(sv, dtype, V):
+    B, G = 7, 3
+    lt = _greedy_tie_rows(B, G, V, seed=V)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    t = torch.from_numpy(lt).to(tdt)
+    # Drafts that follow the target argmax (lowest index) except at a few
+    # positions, so that acceptance runs deep.
+    x = torch.argmax(t[:, :G].float(), dim=-1).to(torch.int32)
+    x[1, 1] = (x[1, 1] + 1) % V
+    x[4, 0] = (x[4, 0] + 7) % V
+    inp = {"target_logits": t, "draft_tokens": x}
+    got, ref, _ = check(sv, "greedy", inp, T=0.0, k=0, seed=5)
+    np.testing.assert_array_equal(got["target_argmax"], ref["target_argmax"])
+
+
+@pytest.mark.parametrize("G,k,dtype", [(4, 0, "f32"), (4, 0, "bf16"), (64, 0, "f32"), (4, 50, "bf16")])
+def test_zero_residual_falls_back_to_p(sv, G, k, dtype):
+    """Draft rows equal to the target rows, and one out-of-range draft token
+    per request: every valid token is accepted (p(x) / q(x) = 1), the invalid
+    one forces the rejection, and max(p - q, 0) is zero at every token, so
+    the recovered token is drawn from p at that position.  G = 4 runs the
+    accept-and-race kernel whose last workgroup draws it, G = 64 the
+    separate race and finish passes, k = 50 the candidate race."""
+    wl = W["prob_f32_b8_g4_v32000"].scaled(B=8, G=G, V=20011, dtype=dtype)
+    inp = workloads.generate(wl)
+    inp["draft_logits"] = inp["target_logits"][:, :G].clone()
+    x = torch.argmax(inp["target_logits"][:, :G].float(), dim=-1).to(torch.int32)
+    for b in range(x.shape[0]):
+        x[b, (3 * b) % G] = -1 if b % 2 else wl.V
+    inp["draft_tokens"] = x
+    got, ref, _ = check(sv, "prob", inp, T=0.8, k=k, seed=31)
+    assert (ref["num_accepted"] == np.array([(3 * b) % G for b in range(x.shape[0])])).all()
+    assert (got["out_tokens"][np.arange(x.shape[0]), ref["num_accepted"]] >= 0).all()
+
+
 def test_topk1_matches_greedy_on_gpu(sv):
     wl = W["prob_f32_b256_g7_v151936"].scaled(B=16, V=4099, G=4)
     inp = workloads.generate(wl)
