@@ -88,6 +88,24 @@ def test_mixed_parity(sv, dtype, V, onehot):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_zero_residual_batch(sv, dtype):
+    """Draft rows equal to the target rows and one out-of-range draft token
+    per request, over every kind of request (and a top-k above the
+    candidate capacity): valid tokens are accepted (p(x) = q(x)), the
+    invalid one forces the rejection, and max(p - q, 0) is 0 at every token,
+    so the recovered token is drawn from p (the zero-mass reading)."""
+    G, V = 4, 20011
+    inp = mixed(36, G, V, dtype, mix=MIX_ALL + ((0.8, 1500, 1.0),), seed=5)
+    inp["draft_logits"] = inp["target_logits"][:, :G].clone()
+    x = torch.argmax(inp["target_logits"][:, :G].float(), dim=-1).to(torch.int32)
+    for b in range(x.shape[0]):
+        x[b, (3 * b) % G] = -1 if b % 2 else V
+    inp["draft_tokens"] = x
+    got, ref, rep = check_batch(sv, inp, max_top_k=1500)
+    assert (ref["num_accepted"] == np.array([(3 * b) % G for b in range(x.shape[0])])).all()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_uniform_settings_equal_single_entries(sv, dtype):
     """A batch whose requests share one setting is bit-identical to the
     single-setting entry point (same kernels' arithmetic, same streams)."""
