@@ -1713,19 +1713,29 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
   const int lane = lane_id();
   int32_t* o = out + (size_t)b * (G + 1);
   int n = g;
+  int x0 = -1;  // this lane's draft token in the first chunk of positions
   for (int j0 = 0; j0 <= g; j0 += kWave) {
     const int j = j0 + lane;
     bool mis = false;
     if (j <= g) {
+      // The draft token and the row's partial keys are loaded together,
+      // eight partials in flight at a time.
+      const size_t xj = j < g ? L.tok(b, G, j) : 0;
+      const int x = j < g ? X[xj] : -1;
+      if (j0 == 0) x0 = x;
       const uint64_t* pj = part + ((size_t)b * (G + 1) + j) * S;
       uint64_t m = 0ull;
-      for (int k = 0; k < S; ++k) m = pj[k] > m ? pj[k] : m;
+      for (int k0 = 0; k0 < S; k0 += 8) {
+        uint64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = k0 + u < S ? pj[k0 + u] : 0ull;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = v[u] > m ? v[u] : m;
+      }
       const int a = (int)key_index(m);
       o[j] = a;
       if (targ) targ[(size_t)b * (G + 1) + j] = a;
       if (j < g) {
-        const size_t xj = L.tok(b, G, j);
-        const int x = X[xj];
         const bool valid = x >= 0 && x < V;
         if (!valid) atomicOr(err, kErrBadToken);
         mis = !valid || x != a;
@@ -1740,7 +1750,7 @@ __global__ __launch_bounds__(64) void accept_greedy_kernel(const uint64_t* __res
   // Accepted drafts before n, the target argmax (already in place) at n,
   // padding after: each lane rewrites only positions of its own lane.
   for (int j = lane; j <= G; j += kWave) {
-    if (j < n) o[j] = X[L.tok(b, G, j)];
+    if (j < n) o[j] = j < kWave ? x0 : X[L.tok(b, G, j)];
     else if (j > n) o[j] = -1;
   }
   if (lane == 0) {
