@@ -304,11 +304,13 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 // same steps are split over chunks of each row (the nucleus passes further
 // below).
 //
-//   pass 1  fp64 mass of every token; the total Z; a histogram of mass over
-//           bins of the gap d = (l_max - l) / T, ln2 / 64 nats per bin over
-//           [0, 44.4).  Tokens further below the maximum carry less than
-//           2^31 e^-44 < 2e-10 of Z in total, so the cut (top_p <= 1 - 2^-24)
-//           always falls inside the histogram.
+//   pass 1  a histogram of fp64 mass over bins of the gap d = (l_max - l) /
+//           T, ln2 / 64 nats per bin over [0, 44.4) (each bin sums its
+//           tokens' masses divided by the bin's common power of two, which
+//           is applied once per bin afterwards), and the total Z.  Tokens
+//           further below the maximum carry less than 2^31 e^-44 < 2e-10 of
+//           Z in total, so the cut (top_p <= 1 - 2^-24) always falls inside
+//           the histogram.
 //   scan    the bin where the running mass reaches top_p * Z, and the mass A
 //           of the bins before it.
 //   pass 2  the bin's tokens are collected into LDS (at most kNucCap; the
@@ -322,13 +324,20 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 // ===========================================================================
 constexpr int kNucBins = 4096;  // ln2 / 64 nats each: gaps below 44.4 nats
 // A workgroup per row (or per chunk): 512 threads, two vectors per thread in
-// flight.  Measured on MI355X (one workgroup per row, before the split
-// passes) with the row passes of the kinds running side by side:
-// against 256 / 512 / 1024 threads and 1 / 2 / 4 vectors (by logit type, and
-// with a larger shape for calls with few rows), this one shape was the
-// fastest or within 1% on the mixed, ragged and sampler-match workloads.
+// flight (build knobs SV_NUC_NT, SV_NUC_U).  Measured on MI355X with pass 1
+// as below, against 256 x 2, 256 x 4, 512 x 3, 1024 x 1 and 1024 x 2: the
+// fastest or within 1% on the mixed, ragged and sampler-match workloads
+// (256 x 2 is 2% faster on a batch of top-p rows only and 5 to 6% slower on
+// the ragged and sampler-match ones).  The 32 KB fp64 histogram holds a CU
+// to two such workgroups.
+#ifndef SV_NUC_NT
+#define SV_NUC_NT 512
+#endif
+#ifndef SV_NUC_U
+#define SV_NUC_U 2
+#endif
 struct NucShape {
-  static constexpr int NT = 512, U = 2;
+  static constexpr int NT = SV_NUC_NT, U = SV_NUC_U;
 };
 constexpr int kCutThreads = 512;  // kcut_full_kernel
 constexpr int kNucCap = 2048;
@@ -430,47 +439,78 @@ __device__ __forceinline__ float nucleus_lmax(const float2* part, int row, int S
   return wave_max_f(lmax);
 }
 
-// Pass 1 over elements [a, e) of a row: adds each token's mass
-// exp((l - lm) * it) to the LDS histogram of its gap bin (hm[kNucBins]: the
-// spare slot of tokens without a bin) and returns this thread's sum of the
-// masses.  The gap is the negated exponent, so mass and bin come from one
-// product.  Branch-free: with FLOOR, a token whose key is below kfloor adds 0.
+// 2^(f/64) for |f| <= 1/2: exp(c f), c = ln2 / 64, by its Taylor polynomial
+// of degree 5 (|c f| <= 0.0055, truncation below 4e-17 relative).
+__device__ __forceinline__ double exp2_frac64(double f) {
+  constexpr double c = 0.6931471805599453 / 64.0;
+  constexpr double a2 = c * c / 2.0, a3 = a2 * c / 3.0, a4 = a3 * c / 4.0, a5 = a4 * c / 5.0;
+  double q = fma(f, a5, a4);
+  q = fma(f, q, a3);
+  q = fma(f, q, a2);
+  q = fma(f, q, c);
+  return fma(f, q, 1.0);
+}
+
+// Pass 1 over elements [a, e) of a row, into the LDS gap histogram.  A
+// token's mass exp(x), x = (l - lm) / T <= 0, is 2^(k/64) 2^(f/64) with
+// k = round(64 x / ln2) (the token's gap bin is -k, the rounding of
+// nucleus_bin) and |f| <= 1/2.  Every token of a bin shares the factor
+// 2^(k/64), so a bin adds up only the tokens' 2^(f/64); nucleus_unfactor
+// multiplies each bin by its factor once.  A token beyond the last bin (a
+// gap over 44.4 nats: rare) adds its whole mass, by the table-driven exp, to
+// the spare slot hm[kNucBins].  With FLOOR, a token whose key is below
+// kfloor adds 0.
 template <typename ET, int NT, int U, bool FLOOR>
-__device__ __forceinline__ double nucleus_pass1(const ET* rp, int a, int e, double lm, double it, uint64_t kfloor,
-                                                const double* tab, double* hm) {
-  double zt = 0.0;
-  auto mass_bin = [&](float l, int y, uint32_t& bin) -> double {
-    int k;
-    double m = exp_nonpos_f64(((double)l - lm) * it, tab, &k);
-    if (FLOOR) m = make_key(l, (uint32_t)y) < kfloor ? 0.0 : m;
-    bin = min((uint32_t)(-k), (uint32_t)kNucBins);
-    return m;
+__device__ __forceinline__ void nucleus_pass1(const ET* rp, int a, int e, double lm, double it, uint64_t kfloor,
+                                              const double* tab, double* hm) {
+  auto add = [&](float l, int y) {
+    const double x = ((double)l - lm) * it;
+    const double t = fma(fmax(x, -700.0), kNucInvStep, kNucRound);
+    const double kd = t - kNucRound;
+    const int bin = -__double2loint(t);
+    const bool in = bin < kNucBins;
+    double v = exp2_frac64(fma(fmax(x, -700.0), kNucInvStep, -kd));
+    if (!in) {
+      int k;
+      v = exp_nonpos_f64(x, tab, &k);
+    }
+    if (FLOOR && make_key(l, (uint32_t)y) < kfloor) v = 0.0;
+    atomicAdd(&hm[in ? bin : kNucBins], v);
   };
   row_stream<ET, NT, U>(
       rp, a, e,
       [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
-        // Masses and bins of the vector's tokens first (independent chains
-        // the scheduler interleaves), then the histogram adds.
-        constexpr int EPV = Elem<ET>::kPerVec;
-        double m[EPV];
-        uint32_t bin[EPV];
 #pragma unroll
-        for (int k = 0; k < EPV; ++k) m[k] = mass_bin(fv[k], y0 + k, bin[k]);
-#pragma unroll
-        for (int k = 0; k < EPV; ++k) atomicAdd(&hm[bin[k]], m[k]);
-#pragma unroll
-        for (int w2 = 1; w2 < EPV; w2 *= 2)
-#pragma unroll
-          for (int k = 0; k + w2 < EPV; k += 2 * w2) m[k] += m[k + w2];
-        zt += m[0];
+        for (int k = 0; k < Elem<ET>::kPerVec; ++k) add(fv[k], y0 + k);
       },
-      [&](float l, int y) {
-        uint32_t bin;
-        const double m = mass_bin(l, y, bin);
-        atomicAdd(&hm[bin], m);
-        zt += m;
-      });
-  return zt;
+      add);
+}
+
+// Bin b of a pass-1 histogram times its factor 2^(-b/64): the masses of the
+// gap bins, in place (the spare slot already holds masses).  Returns the
+// row's total mass Z (bins and spare slot) to every thread.  Starts after a
+// barrier and ends with one.
+template <int NT>
+__device__ __forceinline__ double nucleus_unfactor(double* hm, double spare, const double* tab, double* red) {
+  constexpr int NW = NT / kWave;
+  const int tid = threadIdx.x;
+  double z = tid == 0 ? spare : 0.0;
+  for (int i = tid; i < kNucBins; i += NT) {
+    const double v = hm[i];
+    if (v != 0.0) {
+      const int k = -i;
+      const double m = v * ldexp(tab[k & 63], k >> 6);
+      hm[i] = m;
+      z += m;
+    }
+  }
+  z = wave_sum_d(z);
+  if (lane_id() == 0) red[tid / kWave] = z;
+  __syncthreads();
+  double Z = 0.0;
+  for (int k = 0; k < NW; ++k) Z += red[k];
+  __syncthreads();
+  return Z;
 }
 
 // Scan of the gap histogram by a workgroup of NT threads: thread t owns bins
@@ -599,14 +639,11 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
 
   __syncthreads();
 
-  // Pass 1: masses, Z and the mass histogram of the gap.
-  double zt = kfloor != 0ull ? nucleus_pass1<ET, NT, U, true>(rp, 0, V, lm, it, kfloor, tab, hm)
-                             : nucleus_pass1<ET, NT, U, false>(rp, 0, V, lm, it, kfloor, tab, hm);
-  zt = wave_sum_d(zt);
-  if (lane == 0) red_d[w] = zt;
+  // Pass 1: the mass histogram of the gap, and Z.
+  if (kfloor != 0ull) nucleus_pass1<ET, NT, U, true>(rp, 0, V, lm, it, kfloor, tab, hm);
+  else nucleus_pass1<ET, NT, U, false>(rp, 0, V, lm, it, kfloor, tab, hm);
   __syncthreads();
-  double Z = 0.0;
-  for (int k = 0; k < NW; ++k) Z += red_d[k];
+  const double Z = nucleus_unfactor<NT>(hm, hm[kNucBins], tab, red_d);
   const double target = (double)ri.top_p * Z;
 
   nucleus_pick<NT>(hm, target, scr.incl, red_s, &sh_bin, &sh_A);
@@ -745,7 +782,7 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
 //            kNucCap keys is resolved by nucleus_row (with its refinement).
 // The passes of the path not taken exit at once.
 // ===========================================================================
-constexpr int kNucPartStride = kNucBins + 2;  // histogram, spare slot, Z
+constexpr int kNucPartStride = kNucBins + 2;  // histogram, spare slot (one slot of padding)
 
 struct NucState {
   double A, Z;      // mass of the bins before the cut bin; the row's mass
@@ -799,18 +836,13 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_part_kernel(const ET* __
   __syncthreads();
   int a, e;
   nucleus_chunk(V, NS, s, &a, &e);
-  double zt = kfloor != 0ull ? nucleus_pass1<ET, NT, U, true>(rp, a, e, lm, it, kfloor, tab, hm)
-                             : nucleus_pass1<ET, NT, U, false>(rp, a, e, lm, it, kfloor, tab, hm);
-  zt = wave_sum_d(zt);
-  if (lane == 0) red_d[w] = zt;
+  if (kfloor != 0ull) nucleus_pass1<ET, NT, U, true>(rp, a, e, lm, it, kfloor, tab, hm);
+  else nucleus_pass1<ET, NT, U, false>(rp, a, e, lm, it, kfloor, tab, hm);
   __syncthreads();
+  // The chunk's bins as accumulated (factors applied after the chunks are
+  // summed) and its spare slot.
   double* out = hpart + (size_t)item * kNucPartStride;
   for (int i = tid; i <= kNucBins; i += NT) out[i] = hm[i];
-  if (tid == 0) {
-    double Z = 0.0;
-    for (int k = 0; k < NW; ++k) Z += red_d[k];
-    out[kNucBins + 1] = Z;
-  }
 }
 
 // scan: one workgroup per listed row.
@@ -830,19 +862,23 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_scan_kernel(int rows_t, 
   const ReqInfo ri = info[row_request(row, rows_t, G)];
   const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
   __shared__ double hm[kNucBins];
-  __shared__ double incl[NT], red_s[NW];
+  __shared__ double incl[NT], red_s[NW], tab[64];
   __shared__ double sh_A;
   __shared__ int sh_bin;
   const int tid = threadIdx.x;
   const double* src = hpart + (size_t)r * NS * kNucPartStride;
+  // The chunks' bins summed in chunk order (every chunk's bin b carries the
+  // same factor), then the factors.
   for (int i = tid; i < kNucBins; i += NT) {
     double v = 0.0;
     for (int c = 0; c < NS; ++c) v += src[(size_t)c * kNucPartStride + i];
     hm[i] = v;
   }
-  double Z = 0.0;
-  for (int c = 0; c < NS; ++c) Z += src[(size_t)c * kNucPartStride + kNucBins + 1];
+  double spare = 0.0;
+  for (int c = 0; c < NS; ++c) spare += src[(size_t)c * kNucPartStride + kNucBins];
+  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
   __syncthreads();
+  const double Z = nucleus_unfactor<NT>(hm, spare, tab, red_s);
   const double target = (double)ri.top_p * Z;
   nucleus_pick<NT>(hm, target, incl, red_s, &sh_bin, &sh_A);
   const float lmax = nucleus_lmax(part, row, S);  // by every wave (a wave reduction)
