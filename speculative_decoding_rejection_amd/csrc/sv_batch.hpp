@@ -813,7 +813,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_part_kernel(const ET* __
                                                            const int* __restrict__ plan,
                                                            const int* __restrict__ list,
                                                            double* __restrict__ hpart) {
-  constexpr int NT = NucShape::NT, U = NucShape::U, NW = NT / kWave;
+  constexpr int NT = NucShape::NT, U = NucShape::U;
   const int NS = nucleus_splits(plan);
   const int item = blockIdx.x;
   if (item >= plan[0] * NS) return;
@@ -828,8 +828,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_part_kernel(const ET* __
   const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
   double* hm = nucleus_hist_lds();
   __shared__ double tab[64];
-  __shared__ double red_d[NW];
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int tid = threadIdx.x;
   const double lm = (double)nucleus_lmax(part, row, S), it = 1.0 / (double)ri.T;
   for (int i = tid; i <= kNucBins; i += NT) hm[i] = 0.0;
   if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
