@@ -83,6 +83,28 @@ def test_single_setting_call_in_graph(sv):
     _capture_and_replay(call, ("out_tokens", "num_accepted", "p_draft", "q_draft"))
 
 
+def test_match_tree_call_in_graph_shared_workspace(sv):
+    """A sampler-match tree batch (per-row races, the tree walk) captured and
+    replayed, with the eager calls between the replays made on the captured
+    call's own workspace: a replay depends on nothing that earlier calls
+    left there."""
+    wl = workloads.MATCH_WORKLOADS["match_tree_bf16_b256_g7_v151936"].scaled(B=16, V=9001, data_seed=4)
+    inp = workloads.generate(wl)
+    lt, x = inp["target_logits"].to(DEV), inp["draft_tokens"].to(DEV)
+    t, k, p = inp["temperature"].to(DEV), inp["top_k"].to(DEV), inp["top_p"].to(DEV)
+    par = inp["parents"].to(DEV).contiguous()
+    ws = {}
+
+    def call(seed):
+        r = sv.verify_batch(lt, x, None, draft_kind=sv.SV_DRAFT_MATCH, parents=par, temperature=t, top_k=k,
+                            top_p=p, max_top_k=int(inp["top_k"].max()), seed=seed, workspace=ws.get(0))
+        ws.setdefault(0, r["workspace"])
+        return r
+
+    print(f"[graph] match tree B={wl.B} V={wl.V}", flush=True)
+    _capture_and_replay(call, ("out_tokens", "num_accepted", "p_draft", "q_draft", "path_nodes"))
+
+
 def test_first_batch_call_under_capture():
     """A process whose first batch call is captured: the library does not
     create its side streams during the capture (the row passes then run on
