@@ -24,8 +24,10 @@ Pinned functions and their pins (see tests/test_oracle_pins.py):
       reductions between the three modes;
   verify_batch -- per-request settings reduce exactly to single-setting
       calls; temperature-0 requests follow numpy's argmax.
+  The zero-mass fallback (equal laws at a forced rejection) is pinned by its
+  law: the token drawn there follows p.
 Parity unpinned by the pages (pinned only by this oracle's own definition):
-  the tie rules, the Philox keying and bit mapping, the zero-mass fallback.
+  the tie rules, the Philox keying and bit mapping.
 """
 
 from __future__ import annotations

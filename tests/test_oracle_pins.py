@@ -186,6 +186,27 @@ def test_race_law_chi_square():
     assert chi.pvalue > 1e-6
 
 
+def test_zero_residual_fallback_law():
+    """Equal target and draft laws at a position rejected only because its
+    draft token is out of range: max(p - q, 0) is 0 everywhere, and the
+    token drawn there must follow p itself (the zero-mass reading).  Over
+    40,000 requests its frequencies match p (chi-square); emitting nothing
+    (-1) or racing on the masked or uniform law would fail."""
+    p = np.array([0.5, 0.3, 0.15, 0.05])
+    n = 40_000
+    row = np.log(p).astype(np.float32)
+    lt = np.ascontiguousarray(np.broadcast_to(row, (n, 2, 4)))
+    ld = np.ascontiguousarray(np.broadcast_to(row, (n, 1, 4)))
+    x = np.full((n, 1), 4, np.int32)  # out of range: rejected at position 0
+    ref = oracle.verify(oracle.MODE_PROB, lt, ld, x, temperature=1.0, seed=17)
+    assert (ref["num_accepted"] == 0).all() and ref["bad_token"].all()
+    tok = ref["out_tokens"][:, 0]
+    assert (tok >= 0).all() and (ref["out_tokens"][:, 1] == -1).all()
+    counts = np.bincount(tok, minlength=4)
+    assert stats.chisquare(counts, n * p).pvalue > 1e-6
+    assert stats.chisquare(counts, n * np.full(4, 0.25)).pvalue < 1e-12
+
+
 def test_race_wrong_law_is_detected():
     """Power check: a plausible slip (racing on p instead of the residual)
     is far outside the chi-square acceptance region used above."""
