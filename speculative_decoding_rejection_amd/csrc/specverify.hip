@@ -548,10 +548,12 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     if ((s = check_launch()) != SV_OK) return s;
   }
   {
-    // Row phase: top-k rows (candidates, then their nucleus) on side stream
-    // 0, temperature-0 rows (argmax) on side stream 1, full rows (softmax
+    // Row phase: top-k rows (candidates, then their nucleus, then the
+    // top-k requests' accept pass) on side stream 0, temperature-0 rows
+    // (argmax, then their accept pass) on side stream 1, full rows (softmax
     // partials, then a large top-k's cut and the nucleus) on the caller's
-    // stream.  The three write disjoint parts of the workspace.
+    // stream.  The three write disjoint parts of the workspace and of the
+    // outputs.
     TimedLaunch t(0, st);
     std::unique_lock<std::mutex> lock(g_side_mu);
     SideStreams* side = side_streams(st);
@@ -574,6 +576,26 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       hipLaunchKernelGGL((sv::rows_argmax_kernel<ET, kRowThreads, kRowUnroll>), dim3(pl.rows_t * pl.S),
                          dim3(kRowThreads), 0, s_arg, (const ET*)lt, pl.V, pl.S, pl.seg, part64, err,
                          (const ReqInfo*)info, pl.G, pl.L);
+    if constexpr (MODE != 3) {
+      // The accept passes of top-k and temperature-0 requests (and the
+      // former's beta) depend only on their own row passes: they run on
+      // those passes' streams, beside the full rows' softmax and nucleus
+      // passes.  Each writes only its own requests' outputs.
+      if (rs == SV_OK) {
+        const sv::Stats stats{beta, counters};
+        if (pl.K > 0) {
+          launch_accept_topk<MODE>(pl, (const uint64_t*)(ws + pl.off_cand), X, pl.kcap, 0.f, k0, k1, out, nacc,
+                                   p_draft, q_draft, err, (const ReqInfo*)info, qp, stats, s_topk);
+          if (beta && MODE != 1)
+            hipLaunchKernelGGL((sv::beta_topk_kernel<MODE>), dim3((pl.B * pl.G + 3) / 4), dim3(256), 0, s_topk,
+                               (const uint64_t*)(ws + pl.off_cand), qp, pl.B, pl.G, pl.kcap, pl.rows_t,
+                               (const ReqInfo*)info, pl.L, beta);
+        }
+        hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, s_arg, (const uint64_t*)part64, X,
+                           pl.G, pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft,
+                           q_draft, pl.L, stats);
+      }
+    }
     if (rs == SV_OK) rs = run_rows_softmax<ET>(pl, lt, ldl, nrows, ws, st, info, -1);
     if (rs == SV_OK && pl.big_k)  // top-k above the candidate capacity: the k-th key of the full row, before any nucleus
       hipLaunchKernelGGL((sv::kcut_full_kernel<ET>), dim3(nrows), dim3(sv::kCutThreads), 0, st, (const ET*)lt,
@@ -648,26 +670,14 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
   RaceDesc* desc = (RaceDesc*)(ws + pl.off_desc);
   unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
   {
+    // Full-row requests (the top-k and temperature-0 ones were accepted on
+    // the side streams, before the join).
     TimedLaunch t(1, st);
     const sv::Stats stats{beta, counters};
-    if (pl.K > 0)
-      launch_accept_topk<MODE>(pl, (const uint64_t*)(ws + pl.off_cand), X, pl.kcap, 0.f, k0, k1, out, nacc,
-                               p_draft, q_draft, err, (const ReqInfo*)info, qp, stats, st);
     hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
                        (const ET*)ldl, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0,
                        k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
                        (const RowCut*)(use_cut ? cut : nullptr), pl.L, qp, stats);
-    hipLaunchKernelGGL(sv::accept_greedy_kernel, dim3(pl.B), dim3(64), 0, st, (const uint64_t*)part64, X, pl.G,
-                       pl.V, pl.S, out, nacc, (int32_t*)nullptr, err, (const ReqInfo*)info, p_draft, q_draft, pl.L,
-                       stats);
-    t.done();
-    if ((s = check_launch()) != SV_OK) return s;
-  }
-  if (beta && MODE != 1 && pl.K > 0) {
-    TimedLaunch t(1, st);
-    hipLaunchKernelGGL((sv::beta_topk_kernel<MODE>), dim3((pl.B * pl.G + 3) / 4), dim3(256), 0, st,
-                       (const uint64_t*)(ws + pl.off_cand), qp, pl.B, pl.G, pl.kcap, pl.rows_t, (const ReqInfo*)info,
-                       pl.L, beta);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
