@@ -1,0 +1,83 @@
+"""Seeded random configurations of spec_verify_batch against the fp64
+oracle: shapes (B, G and V from 1 up), logit types, draft kinds (logits,
+one-hot, probabilities, token-only under sampler-match with random trees),
+dense and ragged layouts with zero-length drafts, row strides, random
+per-request settings (temperature 0 to 2.5, top-k from 1 to past the
+candidate capacity and V, top-p from 1e-6 to 1) and some out-of-range draft
+tokens.  Each case prints its configuration before it runs.  Bar: as in
+test_gpu_batch.py (oracle/parity.py, compare_batch)."""
+
+import numpy as np
+import pytest
+
+from test_gpu_layout import check, make, sv  # noqa: F401  (sv: the module fixture)
+from test_gpu_match import check as match_check
+from test_gpu_match import make as match_make
+from test_gpu_match import random_tree
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 48
+N_MATCH_CASES = 24
+_T = (0.0, 0.05, 0.3, 0.7, 1.0, 2.5)
+_K = (0, 1, 2, 20, 64, 65, 300, 1000, 1025)
+_P = (1.0, 0.999999, 0.9, 0.5, 0.1, 1e-6)
+
+
+def fuzz_case(i: int) -> dict:
+    rng = np.random.default_rng(7000 + i)
+    V = int(rng.choice([1, 2, 3, 17, 63, 64, 65, 511, 1000, 4097, 9001, 20011]))
+    G = int(rng.integers(1, 13))
+    mix = tuple((float(rng.choice(_T)), int(min(int(rng.choice(_K)), V)), float(rng.choice(_P)))
+                for _ in range(int(rng.integers(1, 5))))
+    return dict(B=int(rng.integers(1, 34)), G=G, V=V, dtype=str(rng.choice(["f32", "bf16"])),
+                kind=str(rng.choice(["logits", "onehot", "probs"])), ragged=bool(rng.integers(0, 2)),
+                pad_t=int(rng.choice([0, 0, 3, 64])), pad_d=int(rng.choice([0, 0, 5])), mix=mix,
+                bad=int(rng.integers(0, 3)), seed=int(rng.integers(0, 1 << 30)))
+
+
+def fuzz_inputs(c: dict) -> dict:
+    inp = make(c["B"], c["G"], c["V"], c["dtype"], lengths=(0, c["G"]) if c["ragged"] else None,
+               probs=c["kind"] == "probs", seed=c["seed"] % 1000, mix=c["mix"])
+    x = inp["draft_tokens"].clone()
+    rng = np.random.default_rng(c["seed"])
+    for _ in range(c["bad"]):  # out-of-range draft tokens
+        b, j = int(rng.integers(0, c["B"])), int(rng.integers(0, c["G"]))
+        x[b, j] = -1 if rng.random() < 0.5 else c["V"]
+    inp["draft_tokens"] = x
+    return inp
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_fuzz(sv, i):  # noqa: F811
+    c = fuzz_case(i)
+    print(f"[fuzz] case {i}: {c}", flush=True)
+    check(sv, fuzz_inputs(c), c["kind"], c["ragged"], pad_t=c["pad_t"], pad_d=c["pad_d"], seed=c["seed"])
+
+
+def match_case(i: int) -> dict:
+    rng = np.random.default_rng(9000 + i)
+    V = int(rng.choice([1, 2, 5, 64, 65, 1000, 4097, 9001]))
+    G = int(rng.integers(1, 12))
+    mix = tuple((float(rng.choice(_T)), int(min(int(rng.choice(_K)), V)), float(rng.choice(_P)))
+                for _ in range(int(rng.integers(1, 5))))
+    shape = str(rng.choice(["chain", "tree"]))
+    return dict(B=int(rng.integers(1, 30)), G=G, V=V, dtype=str(rng.choice(["f32", "bf16"])), mix=mix,
+                parents=random_tree(G, 9000 + i) if shape == "tree" else (), ragged=bool(rng.integers(0, 2)),
+                peak=float(rng.choice([6.0, 18.0])), bad=int(rng.integers(0, 3)), seed=int(rng.integers(0, 1 << 30)))
+
+
+@pytest.mark.parametrize("i", range(N_MATCH_CASES))
+def test_fuzz_match(sv, i):  # noqa: F811
+    c = match_case(i)
+    print(f"[fuzz-match] case {i}: {c}", flush=True)
+    inp = match_make(c["B"], c["G"], c["V"], c["dtype"], parents=c["parents"],
+                     lengths=(0, c["G"]) if c["ragged"] else (), peak=c["peak"], seed=c["seed"] % 1000,
+                     mix=c["mix"])
+    x = inp["draft_tokens"].clone()
+    rng = np.random.default_rng(c["seed"])
+    for _ in range(c["bad"]):
+        b, j = int(rng.integers(0, c["B"])), int(rng.integers(0, c["G"]))
+        x[b, j] = -1 if rng.random() < 0.5 else c["V"]
+    inp["draft_tokens"] = x
+    match_check(sv, inp, ragged=c["ragged"], seed=c["seed"])

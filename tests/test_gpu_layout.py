@@ -86,7 +86,7 @@ def check(sv, inp, kind, ragged, **kw):
     print(f"[layout] kind={kind} ragged={ragged} shape={tuple(inp['target_logits'].shape)} "
           f"dtype={inp['target_logits'].dtype} {kw}", flush=True)
     got = run_gpu(sv, inp, kind, ragged=ragged, **kw)
-    ref = run_oracle(inp, kind, ragged=ragged)
+    ref = run_oracle(inp, kind, ragged=ragged, seed=kw.get("seed", 42))
     rep = assert_parity_batch(got, ref)
     want = (1 if ref["bad_token"].any() else 0) | (2 if ref["bad_param"].any() else 0)
     assert got["error_code"] == want
