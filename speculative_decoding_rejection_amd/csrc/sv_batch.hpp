@@ -22,11 +22,6 @@
 
 namespace sv {
 
-__device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
-  return v;
-}
 // Inclusive prefix sum over the lanes of a wave, in lane order.
 __device__ __forceinline__ double wave_incl_scan_d(double v) {
   const int lane = lane_id();

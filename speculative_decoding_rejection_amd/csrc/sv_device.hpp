@@ -234,6 +234,22 @@ __device__ __forceinline__ float wave_sum_f(float v) {
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
   return v;
 }
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// A probability as the accept test compares it: exp2((l - m) c) inv_z from
+// the fp32 row statistics, evaluated in fp64.  A draft token's q(x) can lie
+// below fp32's smallest normal, 2^-126, at low temperatures while p(x) / q(x)
+// is large; in fp64 it reaches 2^-1074, as in the oracle's arithmetic.
+// Contraction off: the product is rounded on its own, so that a later
+// p - q of two equal laws is exactly 0.
+__device__ __forceinline__ double test_prob(float l, float m, float c, double inv_z) {
+#pragma clang fp contract(off)
+  return exp2(((double)l - (double)m) * (double)c) * inv_z;
+}
 
 // Sums of exponentials t in [0, 1] that do not depend on the order of the
 // terms: each term is truncated to a multiple of 2^-52 (NaN counts as 0) and
@@ -242,11 +258,12 @@ __device__ __forceinline__ float wave_sum_f(float v) {
 // get the same normaliser, so their laws agree token by token (and p - q is
 // exactly 0 where the logits agree).
 __device__ __forceinline__ uint64_t unit_fixed(float t) { return t > 0.f ? (uint64_t)(t * 0x1.0p52f) : 0ull; }
-__device__ __forceinline__ float wave_sum_fixed(uint64_t v) {
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_u64(v, m);
-  return (float)v * 0x1.0p-52f;
+  return v;
 }
+__device__ __forceinline__ float wave_sum_fixed(uint64_t v) { return (float)wave_sum_u64(v) * 0x1.0p-52f; }
 
 // Online softmax pair (m = max logit, s = sum exp2((l - m) * c)) merge.
 __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2, float c) {

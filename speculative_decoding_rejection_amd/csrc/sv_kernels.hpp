@@ -887,8 +887,9 @@ __global__ __launch_bounds__(WPR * RPB * kWave) void rows_topk_kernel(const ET* 
 // Accept pass, top-k rows: one wave per request.
 // ===========================================================================
 struct CandStats {
-  float m;      // max kept logit
-  float inv_z;  // 1 / sum exp2((l - m) c) over the kept tokens
+  float m;        // max kept logit
+  float inv_z;    // 1 / sum exp2((l - m) c) over the kept tokens
+  double inv_zd;  // the same in fp64 (the sum itself is exact, unit_fixed)
 };
 
 __device__ __forceinline__ CandStats cand_stats(const uint64_t* ck, int K, float c) {
@@ -904,27 +905,35 @@ __device__ __forceinline__ CandStats cand_stats(const uint64_t* ck, int K, float
     const uint64_t k = ck[i];
     if (k) z += unit_fixed(__builtin_amdgcn_exp2f((key_value(k) - m) * c));
   }
-  return CandStats{m, 1.f / wave_sum_fixed(z)};
+  z = wave_sum_u64(z);
+  return CandStats{m, 1.f / ((float)z * 0x1.0p-52f), 1.0 / ((double)z * 0x1.0p-52)};
 }
 
-// Probability of a kept token of logit v under stats st, rounded as a
-// product of its own: with contraction off here, the compiler cannot fold the
-// product into a later p - q (that fma would leave q's rounding error where
-// two equal laws give exactly 0).
+// Probability of a kept token of logit v under stats st (fp32): the weight
+// of a race on p.  Residual weights are taken in fp64 (test_prob).
 __device__ __forceinline__ float cand_p(float v, CandStats st, float c) {
-#pragma clang fp contract(off)
   return __builtin_amdgcn_exp2f((v - st.m) * c) * st.inv_z;
 }
 
-// Probability of token x under a kept set (0 if x is not kept).
-__device__ __forceinline__ float cand_prob(const uint64_t* ck, int K, CandStats st, float c, int x) {
+// Probability of token x under a kept set (0 if x is not kept), and in *pd
+// the same for the accept test (test_prob).
+__device__ __forceinline__ float cand_prob(const uint64_t* ck, int K, CandStats st, float c, int x, double* pd) {
   const int lane = lane_id();
   float p = 0.f;
+  double d = 0.0;
   for (int i = lane; i < K; i += kWave) {
     const uint64_t k = ck[i];
-    if (k && (int)key_index(k) == x) p = __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z;
+    if (k && (int)key_index(k) == x) {
+      p = __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z;
+      d = test_prob(key_value(k), st.m, c, (double)st.inv_z);
+    }
   }
+  *pd = wave_sum_d(d);
   return wave_sum_f(p);
+}
+__device__ __forceinline__ float cand_prob(const uint64_t* ck, int K, CandStats st, float c, int x) {
+  double unused;
+  return cand_prob(ck, K, st, c, x, &unused);
 }
 
 // MODE 0: prob (q from draft candidates), 1: onehot, 2: q given as
@@ -962,13 +971,15 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     const int x = X[xj];
     const bool valid = x >= 0 && x < V;
     const CandStats sp = cand_stats(ct + (size_t)j * kstride, K, c);
-    const float px = valid ? cand_prob(ct + (size_t)j * kstride, K, sp, c, x) : 0.f;
+    double pd = 0.0, qd = valid ? 1.0 : 0.0;
+    const float px = valid ? cand_prob(ct + (size_t)j * kstride, K, sp, c, x, &pd) : 0.f;
     float qx = valid ? 1.f : 0.f;
     if (MODE == 0) {
       const CandStats sq = cand_stats(cd + (size_t)j * kstride, K, c);
-      qx = valid ? cand_prob(cd + (size_t)j * kstride, K, sq, c, x) : 0.f;
+      qx = valid ? cand_prob(cd + (size_t)j * kstride, K, sq, c, x, &qd) : 0.f;
     } else if (MODE == 2) {
       qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
+      qd = qx;
     }
     if (lane == 0) {
       if (p_draft) p_draft[xj] = px;
@@ -977,7 +988,7 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
-      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      const bool acc = valid && (MODE != 1 ? (qd > 0.0 && u <= pd / qd) : (u <= pd));
       rejected[j] = acc ? 0 : 1;
     }
   }
@@ -1005,7 +1016,7 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
   // kept tokens of target row n.
   const uint64_t* cp = ct + (size_t)n * kstride;
   const CandStats sp = cand_stats(cp, K, c);
-  CandStats sq{0.f, 0.f};
+  CandStats sq{0.f, 0.f, 0.0};
   if (MODE == 0 && n < g) sq = cand_stats(qkeys, K, c);
   const int xn = n < g ? X[L.tok(b, G, n)] : -1;
   const float* qrow = (MODE == 2 && n < g) ? qp + L.tok(b, G, n) * (size_t)L.ds : nullptr;
@@ -1017,15 +1028,17 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     const float p = cand_p(key_value(k), sp, c);
     float wgt = p;
     if (n < g) {
+      // The residual in fp64 from the exact kept-set sums: where the two
+      // laws nearly agree it is a small difference of numbers near 1.
       if (MODE == 0) {
-        float q = 0.f;
+        double q = 0.0;
         for (int t = 0; t < K; ++t) {
           const uint64_t kq = qkeys[t];
-          if (kq && key_index(kq) == y) q = cand_p(key_value(kq), sq, c);
+          if (kq && key_index(kq) == y) q = test_prob(key_value(kq), sq.m, c, sq.inv_zd);
         }
-        wgt = fmaxf(p - q, 0.f);
+        wgt = (float)fmax(test_prob(key_value(k), sp.m, c, sp.inv_zd) - q, 0.0);
       } else if (MODE == 2) {
-        wgt = fmaxf(p - qrow[y], 0.f);
+        wgt = (float)fmax(test_prob(key_value(k), sp.m, c, sp.inv_zd) - (double)qrow[y], 0.0);
       } else if ((int)y == xn) {
         wgt = 0.f;
       }
@@ -1099,25 +1112,28 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
   // Softmax over a kept set held one key per lane: (m, 1 / z) as cand_stats.
   auto stats_of = [&](uint64_t k) -> CandStats {
     const float m = wave_max_f(k ? key_value(k) : -INFINITY);
-    const float z = wave_sum_fixed(k ? unit_fixed(__builtin_amdgcn_exp2f((key_value(k) - m) * c)) : 0ull);
-    return CandStats{m, 1.f / z};
+    const uint64_t z = wave_sum_u64(k ? unit_fixed(__builtin_amdgcn_exp2f((key_value(k) - m) * c)) : 0ull);
+    return CandStats{m, 1.f / ((float)z * 0x1.0p-52f), 1.0 / ((double)z * 0x1.0p-52)};
   };
-  auto prob_of = [&](uint64_t k, CandStats st, int x) -> float {
-    return wave_sum_f((k && (int)key_index(k) == x) ? __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z
-                                                   : 0.f);
+  auto prob_of = [&](uint64_t k, CandStats st, int x, double* pd) -> float {
+    const bool hit = k && (int)key_index(k) == x;
+    *pd = wave_sum_d(hit ? test_prob(key_value(k), st.m, c, (double)st.inv_z) : 0.0);
+    return wave_sum_f(hit ? __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z : 0.f);
   };
   for (int j = w; j < g; j += NW) {
     const size_t xj = L.tok(b, G, j);
     const int x = X[xj];
     const bool valid = x >= 0 && x < V;
     const uint64_t kp = keys[j][lane];
-    const float px = valid ? prob_of(kp, stats_of(kp), x) : 0.f;
+    double pd = 0.0, qd = valid ? 1.0 : 0.0;
+    const float px = valid ? prob_of(kp, stats_of(kp), x, &pd) : 0.f;
     float qx = valid ? 1.f : 0.f;
     if (MODE == 0) {
       const uint64_t kq = keys[nt + j][lane];
-      qx = valid ? prob_of(kq, stats_of(kq), x) : 0.f;
+      qx = valid ? prob_of(kq, stats_of(kq), x, &qd) : 0.f;
     } else if (MODE == 2) {
       qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
+      qd = qx;
     }
     if (lane == 0) {
       if (p_draft) p_draft[xj] = px;
@@ -1126,7 +1142,7 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
-      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      const bool acc = valid && (MODE != 1 ? (qd > 0.0 && u <= pd / qd) : (u <= pd));
       rejected[j] = acc ? 0 : 1;
     }
   }
@@ -1142,20 +1158,24 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
   const uint64_t kp = keys[n][lane];
   const CandStats sp = stats_of(kp);
   const int xn = n < g ? X[L.tok(b, G, n)] : -1;
-  float q = 0.f;
+  // q(y) of the residual in fp64 (as accept_topk_kernel), looked up among
+  // draft row n's keys by broadcasting them one lane at a time.
+  double q = 0.0;
   if (MODE == 0 && n < g) {
     const uint64_t kq = keys[nt + n][lane];
     const CandStats sq = stats_of(kq);
-    const float myq = kq ? cand_p(key_value(kq), sq, c) : 0.f;
+    const double myq = kq ? test_prob(key_value(kq), sq.m, c, sq.inv_zd) : 0.0;
     const uint32_t myqi = kq ? key_index(kq) : 0xFFFFFFFFu;
     const uint32_t y = key_index(kp);
+    const uint64_t myqb = (uint64_t)__double_as_longlong(myq);
     for (int t = 0; t < K; ++t) {
       const uint32_t yt = (uint32_t)__builtin_amdgcn_readlane((int)myqi, t);
-      const float qt = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(myq), t));
-      if (kp && yt == y) q = qt;
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)myqb, t);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(myqb >> 32), t);
+      if (kp && yt == y) q = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
     }
   } else if (MODE == 2 && n < g && kp) {
-    q = qp[L.tok(b, G, n) * (size_t)L.ds + key_index(kp)];
+    q = (double)qp[L.tok(b, G, n) * (size_t)L.ds + key_index(kp)];
   }
   uint64_t best_w = 0ull, best_p = 0ull;
   if (kp) {
@@ -1163,7 +1183,7 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
     const float p = cand_p(key_value(kp), sp, c);
     float wgt = p;
     if (n < g) {
-      if (MODE == 0 || MODE == 2) wgt = fmaxf(p - q, 0.f);
+      if (MODE == 0 || MODE == 2) wgt = (float)fmax(test_prob(key_value(kp), sp.m, c, sp.inv_zd) - q, 0.0);
       else if ((int)y == xn) wgt = 0.f;
     }
     const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
@@ -1254,14 +1274,20 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
   }
   const int g = L.len(b, G);  // this request's draft positions
   // Probability of token x (logit l) in padded row r, merged by one lane.
-  auto prob_lane = [&](size_t r, float l, int x) -> float {
+  // *pd: the same for the accept test (test_prob).
+  auto prob_lane = [&](size_t r, float l, int x, double* pd) -> float {
     if (nuc) {
       const RowCut rc = cut[r];
-      if (make_key(l, (uint32_t)x) < rc.kappa) return 0.f;
+      if (make_key(l, (uint32_t)x) < rc.kappa) {
+        *pd = 0.0;
+        return 0.f;
+      }
+      *pd = test_prob(l, rc.m, c, (double)rc.inv_z);
       return __builtin_amdgcn_exp2f((l - rc.m) * c) * rc.inv_z;
     }
     float M, Z;
     merge_row_lane(part + r * S, S, c, M, Z);
+    *pd = test_prob(l, M, c, 1.0 / (double)Z);
     return __builtin_amdgcn_exp2f((l - M) * c) / Z;
   };
   int n = g;
@@ -1273,13 +1299,16 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
       const int x = X[xj];
       const bool valid = x >= 0 && x < V;
       const size_t rt = (size_t)b * (G + 1) + j;
-      const float px = valid ? prob_lane(rt, Elem<ET>::load1(lt + L.trow(b, G, j) * (size_t)L.ts + x), x) : 0.f;
+      double pd = 0.0, qd = valid ? 1.0 : 0.0;
+      const float px =
+          valid ? prob_lane(rt, Elem<ET>::load1(lt + L.trow(b, G, j) * (size_t)L.ts + x), x, &pd) : 0.f;
       float qx = valid ? 1.f : 0.f;
       if (MODE == 0) {
         const size_t rd = (size_t)b * G + j;
-        qx = valid ? prob_lane((size_t)rows_t + rd, Elem<ET>::load1(ld + xj * (size_t)L.ds + x), x) : 0.f;
+        qx = valid ? prob_lane((size_t)rows_t + rd, Elem<ET>::load1(ld + xj * (size_t)L.ds + x), x, &qd) : 0.f;
       } else if (MODE == 2) {
         qx = valid ? qp[xj * (size_t)L.ds + x] : 0.f;
+        qd = qx;
       }
       if (q_draft) q_draft[xj] = qx;
       if (p_draft) p_draft[xj] = px;
@@ -1287,7 +1316,7 @@ __global__ __launch_bounds__(64) void accept_full_kernel(const ET* __restrict__ 
       if (!valid) atomicOr(err, kErrBadToken);
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
-      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      const bool acc = valid && (MODE != 1 ? (qd > 0.0 && u <= pd / qd) : (u <= pd));
       rej = !acc;
     }
     const uint64_t m = ballot(rej);
@@ -1589,6 +1618,7 @@ __global__ __launch_bounds__(256) void accept_race_kernel(const ET* __restrict__
     const int j = lane;
     bool rej = false;
     float px = 0.f, qx = 0.f;
+    double pdt = 0.0, qdt = 0.0;  // the same for the accept test (test_prob)
     bool valid = false;
     if (j < G) {
       valid = x >= 0 && x < V;
@@ -1596,15 +1626,18 @@ __global__ __launch_bounds__(256) void accept_race_kernel(const ET* __restrict__
         float M, Z;
         merge_row_lane(psh + j * S, S, c, M, Z);
         px = __builtin_amdgcn_exp2f((gp - M) * c) / Z;
+        pdt = test_prob(gp, M, c, 1.0 / (double)Z);
         qx = 1.f;
+        qdt = 1.0;
         if (MODE == 0) {
           merge_row_lane(psh + (nt + j) * S, S, c, M, Z);
           qx = __builtin_amdgcn_exp2f((gq - M) * c) / Z;
+          qdt = test_prob(gq, M, c, 1.0 / (double)Z);
         }
       }
       const uint4 r = accept_block(k0, k1, (uint32_t)b, (uint32_t)j);
       const double u = unit_from_words(r.x, r.y);
-      const bool acc = valid && (MODE != 1 ? (qx > 0.f && u <= (double)px / (double)qx) : (u <= (double)px));
+      const bool acc = valid && (MODE != 1 ? (qdt > 0.0 && u <= pdt / qdt) : (u <= pdt));
       rej = !acc;
     }
     const uint64_t m = ballot(rej);

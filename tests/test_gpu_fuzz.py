@@ -1,5 +1,5 @@
-"""Seeded random configurations of spec_verify_batch against the fp64
-oracle: shapes (B, G and V from 1 up), logit types, draft kinds (logits,
+"""Seeded random configurations of spec_verify_batch (and of the
+single-setting entry points) against the fp64 oracle: shapes (B, G and V from 1 up), logit types, draft kinds (logits,
 one-hot, probabilities, token-only under sampler-match with random trees),
 dense and ragged layouts with zero-length drafts, row strides, random
 per-request settings (temperature 0 to 2.5, top-k from 1 to past the
@@ -14,11 +14,15 @@ from test_gpu_layout import check, make, sv  # noqa: F401  (sv: the module fixtu
 from test_gpu_match import check as match_check
 from test_gpu_match import make as match_make
 from test_gpu_match import random_tree
+from test_gpu_parity import check as single_check
+
+import workloads
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
-N_MATCH_CASES = 24
+N_CASES = 64
+N_MATCH_CASES = 32
+N_SINGLE_CASES = 64
 _T = (0.0, 0.05, 0.3, 0.7, 1.0, 2.5)
 _K = (0, 1, 2, 20, 64, 65, 300, 1000, 1025)
 _P = (1.0, 0.999999, 0.9, 0.5, 0.1, 1e-6)
@@ -81,3 +85,34 @@ def test_fuzz_match(sv, i):  # noqa: F811
         x[b, j] = -1 if rng.random() < 0.5 else c["V"]
     inp["draft_tokens"] = x
     match_check(sv, inp, ragged=c["ragged"], seed=c["seed"])
+
+
+_SINGLE_BASE = {"prob": "prob_f32_b256_g7_v151936", "onehot": "onehot_bf16_b512_g3_v262144",
+                "greedy": "greedy_bf16_b64_g5_v128256"}
+
+
+def single_case(i: int) -> dict:
+    rng = np.random.default_rng(11000 + i)
+    entry = str(rng.choice(["prob", "onehot", "greedy"], p=[0.45, 0.35, 0.2]))
+    V = int(rng.choice([1, 2, 7, 64, 65, 777, 4097, 20011]))
+    G = int(rng.choice([1, 3, 8, 16, 63, 64, 70]))
+    T = 0.0 if entry == "greedy" else float(rng.choice([0.05, 0.3, 0.8, 1.0, 2.5]))
+    k = 0 if entry == "greedy" else int(min(int(rng.choice([0, 1, 20, 64, 65, 300, 1000, 1025])), V))
+    return dict(entry=entry, B=int(rng.integers(1, 25)), G=G, V=V, dtype=str(rng.choice(["f32", "bf16"])), T=T,
+                k=k, bad=int(rng.integers(0, 3)), seed=int(rng.integers(0, 1 << 30)))
+
+
+@pytest.mark.parametrize("i", range(N_SINGLE_CASES))
+def test_fuzz_single(sv, i):  # noqa: F811
+    c = single_case(i)
+    print(f"[fuzz-single] case {i}: {c}", flush=True)
+    wl = workloads.WORKLOADS[_SINGLE_BASE[c["entry"]]].scaled(B=c["B"], G=c["G"], V=c["V"], dtype=c["dtype"],
+                                                              data_seed=c["seed"] % 1000)
+    inp = workloads.generate(wl)
+    x = inp["draft_tokens"].clone()
+    rng = np.random.default_rng(c["seed"])
+    for _ in range(c["bad"]):
+        b, j = int(rng.integers(0, c["B"])), int(rng.integers(0, c["G"]))
+        x[b, j] = -1 if rng.random() < 0.5 else c["V"]
+    inp["draft_tokens"] = x
+    single_check(sv, c["entry"], inp, T=c["T"], k=c["k"], seed=c["seed"])
