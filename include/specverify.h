@@ -167,7 +167,10 @@ typedef enum {
  * out_tokens stays [B][gamma+1].  With cu_draft NULL every request has gamma
  * positions, rows [B][gamma+1] and [B][gamma].  A cu_draft array that breaks
  * these rules makes every request invalid: out_tokens -1, num_accepted 0,
- * p_draft / q_draft not written; the sticky error word gets bit 2 (value 4). */
+ * p_draft / q_draft not written; the sticky error word gets bit 2 (value 4).
+ * A ragged call whose every draft length is 0 (cu_draft[B] = 0) has no draft
+ * tokens or draft rows: draft_tokens and draft may then be NULL (if they are
+ * NULL and cu_draft[B] != 0, the layout is invalid as above). */
 typedef struct {
   int32_t draft_kind;      /* sv_draft_kind */
   int32_t reserved;        /* 0 */

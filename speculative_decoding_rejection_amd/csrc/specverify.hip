@@ -321,9 +321,11 @@ SideStreams* side_streams(hipStream_t st) {
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
 
+// null_tokens: a ragged batch call may pass no draft tokens (every draft
+// length 0, checked on the device).
 sv_status check_common(const Plan& pl, const void* target_logits, const int32_t* draft_tokens, int32_t* out_tokens,
-                       int32_t* num_accepted, void* workspace, size_t workspace_bytes) {
-  if (!target_logits || !draft_tokens || !out_tokens || !num_accepted) return SV_ERR_INVALID_ARG;
+                       int32_t* num_accepted, void* workspace, size_t workspace_bytes, bool null_tokens = false) {
+  if (!target_logits || (!draft_tokens && !null_tokens) || !out_tokens || !num_accepted) return SV_ERR_INVALID_ARG;
   if (!aligned(target_logits, (size_t)pl.esize)) return SV_ERR_DTYPE;
   if (!aligned(draft_tokens, 4) || !aligned(out_tokens, 4) || !aligned(num_accepted, 4)) return SV_ERR_INVALID_ARG;
   if (!workspace || !aligned(workspace, kWsAlign) || workspace_bytes < pl.total) return SV_ERR_WORKSPACE;
@@ -515,6 +517,7 @@ struct BatchArgs {
   float T0;
   int K0, max_top_k;
   const int32_t* parents;  // sampler-match trees (null: chains)
+  int no_drafts;           // ragged call without draft tokens or draft rows: every length must be 0
 };
 
 template <typename ET, int MODE>
@@ -543,7 +546,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
                        pl.V, ba.max_top_k, pl.kcap, pl.L, MODE == 3 ? ba.parents : (const int32_t*)nullptr, info,
                        err, out, nacc, p_draft, q_draft, beta, MODE == 0 ? 1 : 0,
                        nuc ? (int*)(ws + pl.off_nplan) : (int*)nullptr,
-                       nuc ? (int*)(ws + pl.off_nlist) : (int*)nullptr);
+                       nuc ? (int*)(ws + pl.off_nlist) : (int*)nullptr, ba.no_drafts);
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
@@ -872,14 +875,18 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
   if (s != SV_OK) return s;
   if (!outputs) return SV_ERR_INVALID_ARG;
   const sv_outputs o = *outputs;
-  s = check_common(pl, target_logits, draft_tokens, o.out_tokens, o.num_accepted, workspace, workspace_bytes);
+  // A ragged call whose every draft length is 0 has no draft tokens or rows
+  // to pass; their pointers may then be null (the classify pass checks that
+  // the offsets end at 0).
+  const bool ragged = layout && layout->cu_draft;
+  s = check_common(pl, target_logits, draft_tokens, o.out_tokens, o.num_accepted, workspace, workspace_bytes, ragged);
   if (s != SV_OK) return s;
   int kind = draft ? SV_DRAFT_LOGITS : SV_DRAFT_ONEHOT;
   if (layout) {
     kind = layout->draft_kind;
     if (kind != SV_DRAFT_LOGITS && kind != SV_DRAFT_ONEHOT && kind != SV_DRAFT_PROBS && kind != SV_DRAFT_MATCH)
       return SV_ERR_INVALID_ARG;
-    if ((kind == SV_DRAFT_LOGITS || kind == SV_DRAFT_PROBS) && !draft) return SV_ERR_INVALID_ARG;
+    if ((kind == SV_DRAFT_LOGITS || kind == SV_DRAFT_PROBS) && !draft && !ragged) return SV_ERR_INVALID_ARG;
     if (layout->parents && (kind != SV_DRAFT_MATCH || !aligned(layout->parents, 4))) return SV_ERR_INVALID_ARG;
     const int64_t ts = layout->target_stride ? layout->target_stride : pl.V;
     const int64_t ds = layout->draft_stride ? layout->draft_stride : pl.V;
@@ -903,6 +910,7 @@ sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling
   ba.K0 = params->top_k;
   ba.max_top_k = batch_max_top_k(params, sampling);
   ba.parents = layout ? layout->parents : nullptr;
+  ba.no_drafts = !draft_tokens || ((kind == SV_DRAFT_LOGITS || kind == SV_DRAFT_PROBS) && !draft);
   if (o.path_nodes && !aligned(o.path_nodes, 4)) return SV_ERR_INVALID_ARG;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;

@@ -99,7 +99,8 @@ __device__ __forceinline__ void plan_nucleus(int n, int* plan) {
 // array is null, the call's single setting T0 / K0 / top_p 1), validates
 // them, and writes one ReqInfo per request.  An invalid request emits
 // nothing (tokens -1, n = 0, p(x) = q(x) = 0) and sets kErrBadParam.  A
-// ragged layout is checked first (cu[0] = 0, 0 <= cu[b+1] - cu[b] <= G):
+// ragged layout is checked first (cu[0] = 0, 0 <= cu[b+1] - cu[b] <= G, and
+// cu[B] = 0 when the call passed no draft tokens or draft rows):
 // if it fails anywhere, every request is invalid, no per-position output is
 // written (their positions are unknown) and kErrBadLayout is set.  The pass
 // also clears the call's error word before any other kernel can set a bit.
@@ -112,7 +113,8 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
                                                         int32_t* __restrict__ out, int32_t* __restrict__ nacc,
                                                         float* __restrict__ p_draft, float* __restrict__ q_draft,
                                                         float* __restrict__ beta, int draft_rows,
-                                                        int* __restrict__ nplan, int* __restrict__ nlist) {
+                                                        int* __restrict__ nplan, int* __restrict__ nlist,
+                                                        int no_drafts) {
   __shared__ int bad_layout, nlisted;
   if (threadIdx.x == 0) {
     atomicExch(err, 0);
@@ -125,6 +127,9 @@ __global__ __launch_bounds__(1024) void classify_kernel(const float* __restrict_
       const int64_t c0 = L.cu[b], c1 = L.cu[b + 1];
       if ((b == 0 && c0 != 0) || c1 - c0 < 0 || c1 - c0 > G) bad_layout = 1;
     }
+    // A call that passed no draft tokens (or no draft rows) has no draft
+    // position to read: every length must be 0.
+    if (no_drafts && threadIdx.x == 0 && L.cu[B] != 0) bad_layout = 1;
   }
   __syncthreads();
   const bool all_bad = bad_layout != 0;

@@ -200,3 +200,28 @@ def test_full_size_ragged_probs_every_request(sv, name):
     got = {"out_tokens": out[ids], "num_accepted": n[ids], "p_draft": pd_pad, "q_draft": qd_pad}
     rep = assert_parity_batch(got, ref)
     print(f"[full] {name}: {rep}", flush=True)
+
+
+@pytest.mark.parametrize("kind", ["logits", "onehot", "probs"])
+def test_ragged_no_draft_positions(sv, kind):
+    """Every draft length 0 in a ragged call: there are no draft tokens or
+    draft rows, and the empty arrays are passed as null pointers; each request
+    draws its one token from p_0."""
+    inp = make(12, 3, 4097, "f32", lengths=(0, 0), probs=kind == "probs", seed=4)
+    assert int(inp["lengths"].sum()) == 0
+    got, ref, _ = check(sv, inp, kind, True)
+    assert (got["num_accepted"] == 0).all() and (got["out_tokens"][:, 0] >= 0).all()
+
+
+def test_null_draft_tokens_with_positions_are_invalid(sv):
+    """Null draft tokens where the offsets give draft positions: every request
+    is invalid (tokens -1, n = 0) and the error word gets the layout bit."""
+    inp = make(6, 3, 1001, "f32", lengths=(1, 3), seed=6)
+    pk = workloads.pack_ragged(inp, inp["lengths"])
+    empty = torch.empty(0, dtype=torch.int32, device=DEV)
+    res = sv.verify_batch(pk["target_logits"].to(DEV), empty, pk["draft_logits"].to(DEV),
+                          cu_draft=pk["cu_draft"].to(DEV), gamma=3, temperature=inp["temperature"].to(DEV),
+                          top_k=inp["top_k"].to(DEV), top_p=inp["top_p"].to(DEV), max_top_k=64, seed=3)
+    torch.cuda.synchronize()
+    assert sv.sv_read_device_error(res["workspace"]) & 4
+    assert (res["num_accepted"] == 0).all() and (res["out_tokens"] == -1).all()
