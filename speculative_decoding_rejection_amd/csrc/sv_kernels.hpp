@@ -915,21 +915,31 @@ __device__ __forceinline__ float cand_p(float v, CandStats st, float c) {
   return __builtin_amdgcn_exp2f((v - st.m) * c) * st.inv_z;
 }
 
+// Below this an fp32 probability may have lost digits to underflow; the
+// accept test then takes it again in fp64 (test_prob).
+constexpr float kTestProbFloor = 0x1.0p-100f;
+
 // Probability of token x under a kept set (0 if x is not kept), and in *pd
-// the same for the accept test (test_prob).
+// the same for the accept test: the fp32 value, or test_prob's below
+// kTestProbFloor (a wave-uniform branch, almost never taken).
 __device__ __forceinline__ float cand_prob(const uint64_t* ck, int K, CandStats st, float c, int x, double* pd) {
   const int lane = lane_id();
   float p = 0.f;
-  double d = 0.0;
+  float v = -INFINITY;
   for (int i = lane; i < K; i += kWave) {
     const uint64_t k = ck[i];
     if (k && (int)key_index(k) == x) {
       p = __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z;
-      d = test_prob(key_value(k), st.m, c, (double)st.inv_z);
+      v = key_value(k);
     }
   }
-  *pd = wave_sum_d(d);
-  return wave_sum_f(p);
+  p = wave_sum_f(p);
+  *pd = p;
+  if (p < kTestProbFloor) {
+    v = wave_max_f(v);
+    *pd = v == -INFINITY ? 0.0 : test_prob(v, st.m, c, (double)st.inv_z);
+  }
+  return p;
 }
 __device__ __forceinline__ float cand_prob(const uint64_t* ck, int K, CandStats st, float c, int x) {
   double unused;
@@ -1117,8 +1127,13 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
   };
   auto prob_of = [&](uint64_t k, CandStats st, int x, double* pd) -> float {
     const bool hit = k && (int)key_index(k) == x;
-    *pd = wave_sum_d(hit ? test_prob(key_value(k), st.m, c, (double)st.inv_z) : 0.0);
-    return wave_sum_f(hit ? __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z : 0.f);
+    const float p = wave_sum_f(hit ? __builtin_amdgcn_exp2f((key_value(k) - st.m) * c) * st.inv_z : 0.f);
+    *pd = p;
+    if (p < kTestProbFloor) {  // as cand_prob
+      const float v = wave_max_f(hit ? key_value(k) : -INFINITY);
+      *pd = v == -INFINITY ? 0.0 : test_prob(v, st.m, c, (double)st.inv_z);
+    }
+    return p;
   };
   for (int j = w; j < g; j += NW) {
     const size_t xj = L.tok(b, G, j);
