@@ -54,6 +54,7 @@ struct Plan {
   int Sr, segr;   // race-pass splits
   size_t off_err, off_part, off_cand, off_desc, off_slots, off_info, off_cut, total;
   size_t off_gath;  // gathered draft-token logits, one float per row (full-row single-setting calls)
+  size_t off_tpart, off_tkey;  // per race split: tails and set-aside key of a peaked residual race
   bool fused;       // full rows, G < 64: accept and race in one launch (accept_race_kernel)
   int Srr, segrr;                           // row-race splits (sampler-match)
   size_t off_rdesc, off_rslots, off_samples;  // per-row race descriptors, slots, samples
@@ -148,6 +149,10 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   off = align_up(off + (size_t)q.B * 3 * 8, kWsAlign);
   q.off_gath = off;
   off = align_up(off + nrows * sizeof(float), kWsAlign);
+  q.off_tpart = off;
+  off = align_up(off + (size_t)q.B * (size_t)q.Sr * 16, kWsAlign);
+  q.off_tkey = off;
+  off = align_up(off + (size_t)q.B * (size_t)q.Sr * 8, kWsAlign);
   q.off_info = q.off_cut = off;
   q.total = off;
   q.L = sv::Layout{nullptr, (int64_t)q.V, (int64_t)q.V};
@@ -193,6 +198,8 @@ sv_status make_batch_plan(const sv_params* p, const sv_sampling* sm, Plan* pl) {
     pl->off_desc += shift;
     pl->off_slots += shift;
     pl->off_gath += shift;
+    pl->off_tpart += shift;
+    pl->off_tkey += shift;
     pl->total += shift;
   }
   size_t off = pl->total;
@@ -387,14 +394,19 @@ sv_status run_rows_topk(const Plan& pl, const void* lt, const void* ld, int nrow
 }
 
 template <typename ET, bool CUT, bool QP>
-sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, uint32_t k1, RaceDesc* desc,
-                   unsigned long long* slots, int32_t* out, hipStream_t st) {
+sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, uint32_t k1, char* ws, int32_t* out,
+                   hipStream_t st) {
   TimedLaunch t(2, st);
+  RaceDesc* desc = (RaceDesc*)(ws + pl.off_desc);
+  unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
+  float4* tpart = (float4*)(ws + pl.off_tpart);
+  unsigned long long* tkey = (unsigned long long*)(ws + pl.off_tkey);
   hipLaunchKernelGGL((sv::race_full_kernel<ET, 256, CUT, QP>), dim3(pl.B * pl.Sr), dim3(256), 0, st,
                      (const ET*)lt, QP ? (const ET*)nullptr : (const ET*)ld, QP ? (const float*)ld : nullptr, pl.V,
-                     pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots);
+                     pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots, tpart, tkey);
   hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
-                     pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
+                     pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out,
+                     (const float4*)tpart, (const unsigned long long*)tkey, pl.Sr);
   t.done();
   return check_launch();
 }
@@ -462,9 +474,10 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     hipLaunchKernelGGL((sv::accept_race_kernel<ET, MODE>), dim3(pl.B * pl.Sr), dim3(256), lds, st, (const ET*)lt,
                        (const ET*)ld, (const float2*)(ws + pl.off_part), (const float*)(ws + pl.off_gath), X, pl.G,
                        pl.V, pl.S, pl.rows_t, pl.c, k0, k1, pl.Sr, pl.segr, out, nacc, p_draft, q_draft, desc, slots,
-                       err);
+                       err, (float4*)(ws + pl.off_tpart), (unsigned long long*)(ws + pl.off_tkey));
     hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, false>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
-                       pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out);
+                       pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out,
+                       (const float4*)(ws + pl.off_tpart), (const unsigned long long*)(ws + pl.off_tkey), pl.Sr);
     t.done();
     return check_launch();
   }
@@ -480,7 +493,7 @@ sv_status verify_sampled(const Plan& pl, uint64_t seed, const void* lt, const vo
     s = check_launch();
     if (s != SV_OK) return s;
   }
-  return run_race<ET, false, false>(pl, lt, ld, k0, k1, desc, slots, out, st);
+  return run_race<ET, false, false>(pl, lt, ld, k0, k1, ws, out, st);
 }
 
 template <typename ET>
@@ -695,8 +708,8 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     if ((s = check_launch()) != SV_OK) return s;
   }
   constexpr bool QP = MODE == 2;
-  if (use_cut) return run_race<ET, true, QP>(pl, lt, ld, k0, k1, desc, slots, out, st);
-  return run_race<ET, false, QP>(pl, lt, ld, k0, k1, desc, slots, out, st);
+  if (use_cut) return run_race<ET, true, QP>(pl, lt, ld, k0, k1, ws, out, st);
+  return run_race<ET, false, QP>(pl, lt, ld, k0, k1, ws, out, st);
 }
 
 // A single-setting call whose top-k exceeds the candidate capacity (and is

@@ -1402,9 +1402,28 @@ struct RaceRow {
   bool cut_p, cut_q;
 };
 
-template <typename ET, int NT, int RES, bool QV, bool EVEN>
+// A residual race over two peaked rows (both normalisers below 1 + 1/16, in
+// units of the rows' largest exponential): a token at the maximum of both
+// rows has weight 1 - Zp / Zq, which fp32 rounds to 0 once the rows' masses
+// off their maxima are below 2^-24 (at low temperature), while the other
+// weights stay representable.  For such rows the scan (TAIL) sets those
+// tokens aside and sums, per split, the two rows' masses off their maxima
+// (tails tp, tq, exact of the 1s) and the counts of maximal tokens (np, nq);
+// the finish weighs the set-aside tokens with ((nq - np) + (tq - tp)) / Zq,
+// Zq = nq + tq, each with its own variate (ukey: largest 1 / E, lowest index).
+constexpr float kTailInvZ = 1.0f / 1.0625f;
+struct TailAcc {
+  float tp, tq, np, nq;
+  uint64_t ukey;
+};
+__device__ __forceinline__ bool tail_race(const RaceDesc& d) {
+  return d.resid == 1 && d.inv_zp > kTailInvZ && d.inv_zq > kTailInvZ;
+}
+
+template <typename ET, int NT, int RES, bool QV, bool EVEN, bool TAIL = false>
 __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq, const float* rqp, const RaceRow& r,
-                                              float inv_zp, uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un) {
+                                              float inv_zp, uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un,
+                                              TailAcc* ta = nullptr) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int tid = threadIdx.x;
   float best = 0.f;  // scores are positive; best_y < 0 until a token scores
@@ -1419,6 +1438,14 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
     if (RES == 1) {
       q = __builtin_amdgcn_exp2f((lq - r.mq) * r.c);
       if (r.cut_q && !(lq > r.kvq || (lq == r.kvq && y <= r.kiq))) q = 0.f;
+      if constexpr (TAIL) {
+        const bool ip = lp == r.mp, iq = lq == r.mq;
+        ta->tp += ip ? 0.f : p;
+        ta->np += ip ? 1.f : 0.f;
+        ta->tq += iq ? 0.f : q;
+        ta->nq += iq ? 1.f : 0.f;
+        if (ip && iq) return -1.f;  // weighed by the finish
+      }
       return fmaxf(fmaf(-q, r.ratio, p), 0.f);
     }
     return fmaxf(fmaf(-lq, 1.f / inv_zp, p), 0.f);  // RES 2: q given as a probability
@@ -1433,6 +1460,13 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   constexpr float kBarScale = kRaceSkip * 0x1.0p-32f;
   float bar = 0.f;
   auto consider = [&](float w, uint32_t lo, uint32_t hi, int y) {
+    if constexpr (TAIL) {
+      if (w < 0.f) {
+        const uint64_t k = make_key(__builtin_amdgcn_rcpf(exp1_from_words(lo, hi)), (uint32_t)y);
+        ta->ukey = k > ta->ukey ? k : ta->ukey;
+        return;
+      }
+    }
     if (!(w <= bar * (float)(~hi))) {
       const float sc = w * __builtin_amdgcn_rcpf(exp1_from_words(lo, hi));  // E = 0 gives +inf
       if (sc > best) {
@@ -1514,17 +1548,27 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
       const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), (uint32_t)y);
       key = kk > key ? kk : key;
     }
+    if constexpr (TAIL) {
+      if (w < 0.f) {
+        const float E = (y & 1) ? exp1_from_words(rr.z, rr.w) : exp1_from_words(rr.x, rr.y);
+        const uint64_t kk = make_key(__builtin_amdgcn_rcpf(E), (uint32_t)y);
+        ta->ukey = kk > ta->ukey ? kk : ta->ukey;
+      }
+    }
   }
   return key;
 }
 
 // The race over split s of the row a descriptor names: this workgroup's best
 // (score, index) key, 0 if no token of the split has weight (every thread
-// gets the workgroup's key).
+// gets the workgroup's key).  A residual race over two peaked rows
+// (tail_race) also stores the split's tails, counts and set-aside key in
+// tpart[slot] and tkey[slot] (tpart null: never).
 template <typename ET, int NT, bool CUT, bool QP>
 __device__ __forceinline__ uint64_t race_split(const RaceDesc& d, const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                const float* __restrict__ qp, int V, int s, int seg, uint32_t k0,
-                                               uint32_t k1) {
+                                               uint32_t k1, float4* __restrict__ tpart = nullptr,
+                                               unsigned long long* __restrict__ tkey = nullptr, size_t slot = 0) {
   const ET* rp = lt + d.prow;
   const ET* rq = (!QP && d.resid) ? ld + d.qrow : nullptr;
   const float* rqp = (QP && d.resid) ? qp + d.qrow : nullptr;
@@ -1557,6 +1601,40 @@ __device__ __forceinline__ uint64_t race_split(const RaceDesc& d, const ET* __re
   } else if (QP) {
     key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
                : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
+  } else if (tpart && tail_race(d)) {
+    TailAcc ta{0.f, 0.f, 0.f, 0.f, 0ull};
+    if (q_vec)
+      key = even ? race_scan<ET, NT, 1, true, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta)
+                 : race_scan<ET, NT, 1, true, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta);
+    else
+      key = even ? race_scan<ET, NT, 1, false, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta)
+                 : race_scan<ET, NT, 1, false, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta);
+    // The split's tails and counts in a fixed order (waves, then lanes).
+    ta.tp = wave_sum_f(ta.tp);
+    ta.tq = wave_sum_f(ta.tq);
+    ta.np = wave_sum_f(ta.np);
+    ta.nq = wave_sum_f(ta.nq);
+    ta.ukey = wave_max_u64(ta.ukey);
+    __shared__ float4 tred[NT / kWave];
+    __shared__ uint64_t ured[NT / kWave];
+    if (lane_id() == 0) {
+      tred[tid / kWave] = make_float4(ta.tp, ta.tq, ta.np, ta.nq);
+      ured[tid / kWave] = ta.ukey;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float4 t = tred[0];
+      uint64_t u = ured[0];
+      for (int k = 1; k < NT / kWave; ++k) {
+        t.x += tred[k].x;
+        t.y += tred[k].y;
+        t.z += tred[k].z;
+        t.w += tred[k].w;
+        u = ured[k] > u ? ured[k] : u;
+      }
+      tpart[slot] = t;
+      tkey[slot] = u;
+    }
   } else if (q_vec) {
     key = even ? race_scan<ET, NT, 1, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
                : race_scan<ET, NT, 1, true, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
@@ -1577,11 +1655,13 @@ template <typename ET, int NT, bool CUT, bool QP>
 __global__ __launch_bounds__(NT) void race_full_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                        const float* __restrict__ qp, int V, int S, int seg,
                                                        uint32_t k0, uint32_t k1, const RaceDesc* __restrict__ desc,
-                                                       unsigned long long* __restrict__ slots) {
+                                                       unsigned long long* __restrict__ slots,
+                                                       float4* __restrict__ tpart = nullptr,
+                                                       unsigned long long* __restrict__ tkey = nullptr) {
   const int b = blockIdx.x / S, s = blockIdx.x - b * S;
   const RaceDesc d = desc[b];
   if (d.n < 0) return;
-  const uint64_t bk = race_split<ET, NT, CUT, QP>(d, lt, ld, qp, V, s, seg, k0, k1);
+  const uint64_t bk = race_split<ET, NT, CUT, QP>(d, lt, ld, qp, V, s, seg, k0, k1, tpart, tkey, blockIdx.x);
   // Device-scope atomic max: coherent across XCDs; read by the next launch.
   if (threadIdx.x == 0 && bk) atomicMax(&slots[3 * b], (unsigned long long)bk);
 }
@@ -1606,7 +1686,8 @@ __global__ __launch_bounds__(256) void accept_race_kernel(const ET* __restrict__
                                                           int32_t* __restrict__ nacc, float* __restrict__ p_draft,
                                                           float* __restrict__ q_draft, RaceDesc* __restrict__ desc,
                                                           unsigned long long* __restrict__ slots,
-                                                          int* __restrict__ err) {
+                                                          int* __restrict__ err, float4* __restrict__ tpart,
+                                                          unsigned long long* __restrict__ tkey) {
   extern __shared__ float2 psh[];  // [rows of the request][S]
   __shared__ RaceDesc dsh;
   const int b = blockIdx.x / Sr, s = blockIdx.x - b * Sr;
@@ -1692,25 +1773,49 @@ __global__ __launch_bounds__(256) void accept_race_kernel(const ET* __restrict__
   }
   __syncthreads();
   const RaceDesc d = dsh;
-  const uint64_t bk = race_split<ET, 256, false, false>(d, lt, ld, (const float*)nullptr, V, s, segr, k0, k1);
+  const uint64_t bk = race_split<ET, 256, false, false>(d, lt, ld, (const float*)nullptr, V, s, segr, k0, k1, tpart,
+                                                        tkey, blockIdx.x);
   if (threadIdx.x == 0 && bk) atomicMax(&slots[3 * b], (unsigned long long)bk);
 }
 
-// Writes each request's race winner to out[request][n].  If the residual had
+// Writes each request's race winner to out[request][n].  A residual race
+// over two peaked rows first weighs the tokens its splits set aside (the
+// tails and counts of splits 0..Sr-1 summed in order).  If the residual had
 // no positive weight (possible only when p and q agree to rounding) the draw
 // is taken from p_n instead, by the whole workgroup over the row (rare).
 template <typename ET, int NT, bool CUT>
 __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ lt, int G, int V, uint32_t k0,
                                                          uint32_t k1, const RaceDesc* __restrict__ desc,
                                                          const unsigned long long* __restrict__ slots,
-                                                         int32_t* __restrict__ out) {
+                                                         int32_t* __restrict__ out,
+                                                         const float4* __restrict__ tpart = nullptr,
+                                                         const unsigned long long* __restrict__ tkey = nullptr,
+                                                         int Sr = 0) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const RaceDesc d = desc[b];
   const int n = d.n;
   if (n < 0) return;
   const float c = d.c;
   int32_t* dst = out + (size_t)b * (G + 1) + n;
-  const unsigned long long win = slots[3 * b];
+  unsigned long long win = slots[3 * b];
+  if (tpart && tail_race(d)) {
+    float tp = 0.f, tq = 0.f, np = 0.f, nq = 0.f;
+    uint64_t u = 0ull;
+    for (int s = 0; s < Sr; ++s) {
+      const float4 t = tpart[(size_t)b * Sr + s];
+      tp += t.x;
+      tq += t.y;
+      np += t.z;
+      nq += t.w;
+      const uint64_t k = tkey[(size_t)b * Sr + s];
+      u = k > u ? k : u;
+    }
+    const float wt = ((nq - np) + (tq - tp)) / (nq + tq);
+    if (u && wt > 0.f) {
+      const uint64_t kk = make_key(wt * key_value(u), key_index(u));
+      win = kk > win ? kk : win;
+    }
+  }
   if (win) {
     if (tid == 0) *dst = (int32_t)key_index(win);
     return;

@@ -102,10 +102,7 @@ def single_case(i: int) -> dict:
                 k=k, bad=int(rng.integers(0, 3)), seed=int(rng.integers(0, 1 << 30)))
 
 
-@pytest.mark.parametrize("i", range(N_SINGLE_CASES))
-def test_fuzz_single(sv, i):  # noqa: F811
-    c = single_case(i)
-    print(f"[fuzz-single] case {i}: {c}", flush=True)
+def single_inputs(c: dict) -> dict:
     wl = workloads.WORKLOADS[_SINGLE_BASE[c["entry"]]].scaled(B=c["B"], G=c["G"], V=c["V"], dtype=c["dtype"],
                                                               data_seed=c["seed"] % 1000)
     inp = workloads.generate(wl)
@@ -115,4 +112,42 @@ def test_fuzz_single(sv, i):  # noqa: F811
         b, j = int(rng.integers(0, c["B"])), int(rng.integers(0, c["G"]))
         x[b, j] = -1 if rng.random() < 0.5 else c["V"]
     inp["draft_tokens"] = x
-    single_check(sv, c["entry"], inp, T=c["T"], k=c["k"], seed=c["seed"])
+    return inp
+
+
+@pytest.mark.parametrize("i", range(N_SINGLE_CASES))
+def test_fuzz_single(sv, i):  # noqa: F811
+    c = single_case(i)
+    print(f"[fuzz-single] case {i}: {c}", flush=True)
+    single_check(sv, c["entry"], single_inputs(c), T=c["T"], k=c["k"], seed=c["seed"])
+
+
+# Configurations of single_case (prob entry, full rows, T = 0.05) in which a
+# rejection falls where p and q both hold nearly all their mass on the same
+# token, so that the residual is carried by that token alone, with weight
+# 1 - Zp / Zq of 1e-15 to 1e-8, which fp32 rounds to 0 (the draft tokens
+# there were not drawn from q, so such rejections are common).  The race
+# weighs that token from the rows' masses off their maxima.  The single
+# entry (accept and race in one launch) and the batch entry with the same
+# setting (separate accept, race and finish) both run the race; they must
+# agree bit for bit, and with the oracle.
+PEAKED = (5000, 5033, 5255, 5289, 5511, 5541)
+
+
+@pytest.mark.parametrize("i", PEAKED)
+def test_peaked_residual_races(sv, i):  # noqa: F811
+    import torch
+    c = single_case(i)
+    assert c["entry"] == "prob" and c["T"] == 0.05 and c["k"] in (0, c["V"])
+    print(f"[peaked] case {i}: {c}", flush=True)
+    inp = single_inputs(c)
+    got, _, _ = single_check(sv, "prob", inp, T=c["T"], k=c["k"], seed=c["seed"])
+    dev = torch.device("cuda:0")
+    B = c["B"]
+    a = sv.verify_batch(inp["target_logits"].to(dev), inp["draft_tokens"].to(dev), inp["draft_logits"].to(dev),
+                        temperature=torch.full((B,), c["T"], dtype=torch.float32, device=dev),
+                        top_k=torch.full((B,), c["k"], dtype=torch.int32, device=dev), max_top_k=max(c["k"], 1),
+                        seed=c["seed"])
+    torch.cuda.synchronize()
+    assert np.array_equal(a["out_tokens"].cpu().numpy(), got["out_tokens"])
+    assert np.array_equal(a["num_accepted"].cpu().numpy(), got["num_accepted"])
