@@ -919,6 +919,12 @@ __device__ __forceinline__ float cand_p(float v, CandStats st, float c) {
 // accept test then takes it again in fp64 (test_prob).
 constexpr float kTestProbFloor = 0x1.0p-100f;
 
+// A candidate's residual weight max(p - q, 0) (fp64) as the race's fp32
+// weight, times 2^64: every residual weight of a race carries the same
+// factor, which leaves the winner unchanged, and masses down to 2^-190 keep
+// their value (scores w / E stay below 2^(64 + 53)).
+__device__ __forceinline__ float resid_weight(double d) { return (float)(fmax(d, 0.0) * 0x1.0p64); }
+
 // Probability of token x under a kept set (0 if x is not kept), and in *pd
 // the same for the accept test: the fp32 value, or test_prob's below
 // kTestProbFloor (a wave-uniform branch, almost never taken).
@@ -1046,9 +1052,9 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
           const uint64_t kq = qkeys[t];
           if (kq && key_index(kq) == y) q = test_prob(key_value(kq), sq.m, c, sq.inv_zd);
         }
-        wgt = (float)fmax(test_prob(key_value(k), sp.m, c, sp.inv_zd) - q, 0.0);
+        wgt = resid_weight(test_prob(key_value(k), sp.m, c, sp.inv_zd) - q);
       } else if (MODE == 2) {
-        wgt = (float)fmax(test_prob(key_value(k), sp.m, c, sp.inv_zd) - (double)qrow[y], 0.0);
+        wgt = resid_weight(test_prob(key_value(k), sp.m, c, sp.inv_zd) - (double)qrow[y]);
       } else if ((int)y == xn) {
         wgt = 0.f;
       }
@@ -1198,7 +1204,7 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
     const float p = cand_p(key_value(kp), sp, c);
     float wgt = p;
     if (n < g) {
-      if (MODE == 0 || MODE == 2) wgt = (float)fmax(test_prob(key_value(kp), sp.m, c, sp.inv_zd) - q, 0.0);
+      if (MODE == 0 || MODE == 2) wgt = resid_weight(test_prob(key_value(kp), sp.m, c, sp.inv_zd) - q);
       else if ((int)y == xn) wgt = 0.f;
     }
     const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
@@ -1408,10 +1414,15 @@ struct RaceRow {
 // off their maxima are below 2^-24 (at low temperature), while the other
 // weights stay representable.  For such rows the scan (TAIL) sets those
 // tokens aside and sums, per split, the two rows' masses off their maxima
-// (tails tp, tq, exact of the 1s) and the counts of maximal tokens (np, nq);
-// the finish weighs the set-aside tokens with ((nq - np) + (tq - tp)) / Zq,
-// Zq = nq + tq, each with its own variate (ukey: largest 1 / E, lowest index).
+// (tails tp, tq, kept apart from the 1s) and the counts of maximal tokens
+// (np, nq); the finish weighs the set-aside tokens with p - q = 1 / Zp -
+// 1 / Zq taken in fp64 from Z = n + tail, each with its own variate (ukey:
+// largest 1 / E, lowest index).
+// The scan of such rows also takes its exponentials times 2^64 (the race is
+// unchanged by a common factor; scores w / E stay below 2^(64 + 53)), so
+// that masses down to 2^-190 keep their value instead of flushing to 0.
 constexpr float kTailInvZ = 1.0f / 1.0625f;
+constexpr float kTailShift = 64.f;
 struct TailAcc {
   float tp, tq, np, nq;
   uint64_t ukey;
@@ -1431,12 +1442,12 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   // Nucleus cuts as float compares: key(l, y) >= kappa iff l > value(kappa),
   // or l equals it and y <= index(kappa); kappa = 0 keeps every token.
   auto weight = [&](float lp, float lq, int y) -> float {
-    float p = __builtin_amdgcn_exp2f((lp - r.mp) * r.c);
+    float p = TAIL ? __builtin_amdgcn_exp2f((lp - r.mp) * r.c + kTailShift) : __builtin_amdgcn_exp2f((lp - r.mp) * r.c);
     if (r.cut_p && !(lp > r.kvp || (lp == r.kvp && y <= r.kip))) p = 0.f;
     if (RES == 0) return p;  // the one-hot draft token is masked per vector
     float q;
     if (RES == 1) {
-      q = __builtin_amdgcn_exp2f((lq - r.mq) * r.c);
+      q = TAIL ? __builtin_amdgcn_exp2f((lq - r.mq) * r.c + kTailShift) : __builtin_amdgcn_exp2f((lq - r.mq) * r.c);
       if (r.cut_q && !(lq > r.kvq || (lq == r.kvq && y <= r.kiq))) q = 0.f;
       if constexpr (TAIL) {
         const bool ip = lp == r.mp, iq = lq == r.mq;
@@ -1525,15 +1536,28 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   // Two vectors per iteration (more independent Philox chains in flight);
   // the trip count is the same for every lane, so the whole wave takes part
   // in the exchange of the bar.
-  for (int base = 0; base < sl.nvec; base += 2 * NT) {
-    const int i0 = base + tid, i1 = i0 + NT;
-    const bool h0 = i0 < sl.nvec, h1 = i1 < sl.nvec;
-    const uint4 p0 = h0 ? load_stream(vp + i0) : zero4, p1 = h1 ? load_stream(vp + i1) : zero4;
-    const uint4 q0 = (QV && h0) ? load_stream(vq + i0) : zero4;
-    const uint4 q1 = (QV && h1) ? load_stream(vq + i1) : zero4;
-    if (h0) race_vec(p0, q0, i0);
-    if (h1) race_vec(p1, q1, i1);
-    bar = wave_max_f(bar);
+  if constexpr (TAIL) {
+    // Rare rows: one vector at a time, so that this path needs no more
+    // registers than the one below.
+    for (int base = 0; base < sl.nvec; base += NT) {
+      const int i0 = base + tid;
+      const bool h0 = i0 < sl.nvec;
+      const uint4 p0 = h0 ? load_stream(vp + i0) : zero4;
+      const uint4 q0 = (QV && h0) ? load_stream(vq + i0) : zero4;
+      if (h0) race_vec(p0, q0, i0);
+      bar = wave_max_f(bar);
+    }
+  } else {
+    for (int base = 0; base < sl.nvec; base += 2 * NT) {
+      const int i0 = base + tid, i1 = i0 + NT;
+      const bool h0 = i0 < sl.nvec, h1 = i1 < sl.nvec;
+      const uint4 p0 = h0 ? load_stream(vp + i0) : zero4, p1 = h1 ? load_stream(vp + i1) : zero4;
+      const uint4 q0 = (QV && h0) ? load_stream(vq + i0) : zero4;
+      const uint4 q1 = (QV && h1) ? load_stream(vq + i1) : zero4;
+      if (h0) race_vec(p0, q0, i0);
+      if (h1) race_vec(p1, q1, i1);
+      bar = wave_max_f(bar);
+    }
   }
   uint64_t key = best_y >= 0 ? make_key(best, (uint32_t)best_y) : 0ull;
   // Scalar head and tail: keyed directly, so index order does not matter.
@@ -1602,13 +1626,11 @@ __device__ __forceinline__ uint64_t race_split(const RaceDesc& d, const ET* __re
     key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
                : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   } else if (tpart && tail_race(d)) {
+    // Rare rows: the draft row is read element by element (two instances of
+    // this path instead of four keep the kernel's common paths as fast).
     TailAcc ta{0.f, 0.f, 0.f, 0.f, 0ull};
-    if (q_vec)
-      key = even ? race_scan<ET, NT, 1, true, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta)
-                 : race_scan<ET, NT, 1, true, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta);
-    else
-      key = even ? race_scan<ET, NT, 1, false, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta)
-                 : race_scan<ET, NT, 1, false, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta);
+    key = even ? race_scan<ET, NT, 1, false, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta)
+               : race_scan<ET, NT, 1, false, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta);
     // The split's tails and counts in a fixed order (waves, then lanes).
     ta.tp = wave_sum_f(ta.tp);
     ta.tq = wave_sum_f(ta.tq);
@@ -1810,7 +1832,11 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
       const uint64_t k = tkey[(size_t)b * Sr + s];
       u = k > u ? k : u;
     }
-    const float wt = ((nq - np) + (tq - tp)) / (nq + tq);
+    // p - q of a token at both maxima, 1 / Zp - 1 / Zq, taken in fp64 (the
+    // precision of the residual's definition) from Z = n + tail (the tails
+    // carry the scan's factor 2^64), in the scan's units (times Zp 2^64).
+    const double zp = (double)np + 0x1.0p-64 * (double)tp, zq = (double)nq + 0x1.0p-64 * (double)tq;
+    const float wt = (float)((1.0 / zp - 1.0 / zq) * zp * 0x1.0p64);
     if (u && wt > 0.f) {
       const uint64_t kk = make_key(wt * key_value(u), key_index(u));
       win = kk > win ? kk : win;

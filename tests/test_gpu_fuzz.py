@@ -124,14 +124,17 @@ def test_fuzz_single(sv, i):  # noqa: F811
 
 # Configurations of single_case (prob entry, full rows, T = 0.05) in which a
 # rejection falls where p and q both hold nearly all their mass on the same
-# token, so that the residual is carried by that token alone, with weight
-# 1 - Zp / Zq of 1e-15 to 1e-8, which fp32 rounds to 0 (the draft tokens
-# there were not drawn from q, so such rejections are common).  The race
-# weighs that token from the rows' masses off their maxima.  The single
-# entry (accept and race in one launch) and the batch entry with the same
-# setting (separate accept, race and finish) both run the race; they must
-# agree bit for bit, and with the oracle.
-PEAKED = (5000, 5033, 5255, 5289, 5511, 5541)
+# token (the draft tokens there were not drawn from q, so such rejections
+# are common).  In 5000 ... 5541 the residual is carried by that token, with
+# p - q of 1e-15 to 1e-8, which fp32 rounds to 0; in 5160, 5211 and 5421 its
+# p - q is below fp64's resolution at 1 (1e-19), as in the oracle, so the
+# residual is carried by tokens far below the maximum (down to 3e-40, below
+# fp32's normal range).  The race takes that token's p - q in fp64 from the
+# rows' masses off their maxima and scales the other weights of such rows by
+# 2^64.  The single entry (accept and race in one launch) and the batch
+# entry with the same setting (separate accept, race and finish) both run
+# the race; they must agree bit for bit, and with the oracle.
+PEAKED = (5000, 5033, 5160, 5211, 5255, 5289, 5421, 5511, 5541)
 
 
 @pytest.mark.parametrize("i", PEAKED)
