@@ -54,7 +54,7 @@ struct Plan {
   int Sr, segr;   // race-pass splits
   size_t off_err, off_part, off_cand, off_desc, off_slots, off_info, off_cut, total;
   size_t off_gath;  // gathered draft-token logits, one float per row (full-row single-setting calls)
-  size_t off_tpart, off_tkey;  // per race split: tails and set-aside key of a peaked residual race
+  size_t off_tpart, off_tkey;  // per race split: masses, counts and set-aside key of a peaked residual race
   bool fused;       // full rows, G < 64: accept and race in one launch (accept_race_kernel)
   int Srr, segrr;                           // row-race splits (sampler-match)
   size_t off_rdesc, off_rslots, off_samples;  // per-row race descriptors, slots, samples
@@ -150,7 +150,7 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   q.off_gath = off;
   off = align_up(off + nrows * sizeof(float), kWsAlign);
   q.off_tpart = off;
-  off = align_up(off + (size_t)q.B * (size_t)q.Sr * 16, kWsAlign);
+  off = align_up(off + (size_t)q.B * (size_t)q.Sr * 32, kWsAlign);
   q.off_tkey = off;
   off = align_up(off + (size_t)q.B * (size_t)q.Sr * 8, kWsAlign);
   q.off_info = q.off_cut = off;

@@ -919,11 +919,15 @@ __device__ __forceinline__ float cand_p(float v, CandStats st, float c) {
 // accept test then takes it again in fp64 (test_prob).
 constexpr float kTestProbFloor = 0x1.0p-100f;
 
-// A candidate's residual weight max(p - q, 0) (fp64) as the race's fp32
-// weight, times 2^64: every residual weight of a race carries the same
-// factor, which leaves the winner unchanged, and masses down to 2^-190 keep
-// their value (scores w / E stay below 2^(64 + 53)).
-__device__ __forceinline__ float resid_weight(double d) { return (float)(fmax(d, 0.0) * 0x1.0p64); }
+// Race key of a candidate whose residual d = p - q (fp64) is positive, with
+// variate E: the score w / E in the log domain, log2(d) - log2(E), so that
+// residuals far below fp32's range (down to fp64's) keep their order.  Every
+// residual race over candidates takes its keys this way.
+__device__ __forceinline__ uint64_t resid_key(double d, float E, uint32_t y) {
+  int ex;
+  const double m = frexp(d, &ex);  // d = m 2^ex, m in [1/2, 1)
+  return make_key((float)ex + __builtin_amdgcn_logf((float)m) - __builtin_amdgcn_logf(E), y);
+}
 
 // Probability of token x under a kept set (0 if x is not kept), and in *pd
 // the same for the accept test: the fp32 value, or test_prob's below
@@ -1043,6 +1047,7 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
     const uint32_t y = key_index(k);
     const float p = cand_p(key_value(k), sp, c);
     float wgt = p;
+    double wd = 0.0;  // the residual (MODE 0 / 2, n < g)
     if (n < g) {
       // The residual in fp64 from the exact kept-set sums: where the two
       // laws nearly agree it is a small difference of numbers near 1.
@@ -1052,16 +1057,21 @@ __global__ __launch_bounds__(256) void accept_topk_kernel(const uint64_t* __rest
           const uint64_t kq = qkeys[t];
           if (kq && key_index(kq) == y) q = test_prob(key_value(kq), sq.m, c, sq.inv_zd);
         }
-        wgt = resid_weight(test_prob(key_value(k), sp.m, c, sp.inv_zd) - q);
+        wd = test_prob(key_value(k), sp.m, c, sp.inv_zd) - q;
       } else if (MODE == 2) {
-        wgt = resid_weight(test_prob(key_value(k), sp.m, c, sp.inv_zd) - (double)qrow[y]);
+        wd = test_prob(key_value(k), sp.m, c, sp.inv_zd) - (double)qrow[y];
       } else if ((int)y == xn) {
         wgt = 0.f;
       }
     }
     const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
     const float E = (y & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
-    if (wgt > 0.f) {
+    if ((MODE == 0 || MODE == 2) && n < g) {
+      if (wd > 0.0) {
+        const uint64_t kk = resid_key(wd, E, y);
+        best_w = kk > best_w ? kk : best_w;
+      }
+    } else if (wgt > 0.f) {
       const uint64_t kk = make_key(wgt * __builtin_amdgcn_rcpf(E), y);
       best_w = kk > best_w ? kk : best_w;
     }
@@ -1203,13 +1213,15 @@ __global__ __launch_bounds__(512) void accept_topk_small_kernel(const uint64_t* 
     const uint32_t y = key_index(kp);
     const float p = cand_p(key_value(kp), sp, c);
     float wgt = p;
-    if (n < g) {
-      if (MODE == 0 || MODE == 2) wgt = resid_weight(test_prob(key_value(kp), sp.m, c, sp.inv_zd) - q);
-      else if ((int)y == xn) wgt = 0.f;
-    }
+    if (n < g && MODE == 1 && (int)y == xn) wgt = 0.f;
     const uint4 r = race_block(k0, k1, (uint32_t)b, (uint32_t)n, y);
     const float E = (y & 1u) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
-    if (wgt > 0.f) best_w = make_key(wgt * __builtin_amdgcn_rcpf(E), y);
+    if ((MODE == 0 || MODE == 2) && n < g) {
+      const double wd = test_prob(key_value(kp), sp.m, c, sp.inv_zd) - q;  // the residual, log-domain key
+      if (wd > 0.0) best_w = resid_key(wd, E, y);
+    } else if (wgt > 0.f) {
+      best_w = make_key(wgt * __builtin_amdgcn_rcpf(E), y);
+    }
     if (p > 0.f) best_p = make_key(p * __builtin_amdgcn_rcpf(E), y);
   }
   best_w = wave_max_u64(best_w);
@@ -1409,32 +1421,30 @@ struct RaceRow {
 };
 
 // A residual race over two peaked rows (both normalisers below 1 + 1/16, in
-// units of the rows' largest exponential): a token at the maximum of both
-// rows has weight 1 - Zp / Zq, which fp32 rounds to 0 once the rows' masses
-// off their maxima are below 2^-24 (at low temperature), while the other
-// weights stay representable.  For such rows the scan (TAIL) sets those
-// tokens aside and sums, per split, the two rows' masses off their maxima
-// (tails tp, tq, kept apart from the 1s) and the counts of maximal tokens
-// (np, nq); the finish weighs the set-aside tokens with p - q = 1 / Zp -
-// 1 / Zq taken in fp64 from Z = n + tail, each with its own variate (ukey:
-// largest 1 / E, lowest index).
-// The scan of such rows also takes its exponentials times 2^64 (the race is
-// unchanged by a common factor; scores w / E stay below 2^(64 + 53)), so
-// that masses down to 2^-190 keep their value instead of flushing to 0.
+// units of the rows' largest exponential; low temperature): a token at the
+// maximum of both rows has weight 1 - Zp / Zq, which fp32 rounds to 0 once
+// the rows' masses off their maxima are below 2^-24, and the other tokens'
+// residuals can lie below fp32's range.  Such rows take race_scan_tail:
+// log-domain scores, and the tokens whose two exponentials are equal (the
+// same gap below each row's maximum: the tokens at both maxima, and others)
+// set aside, since their residual e (1 / Zp - 1 / Zq) shares one factor that
+// the finish takes in fp64 from Z = n + c + t: n the count of maximal
+// tokens, c the mass of the other set-aside tokens (the same in both rows),
+// t the rest of the row's mass off its maximum (per-split sums, times 2^64
+// so that they do not flush).
 constexpr float kTailInvZ = 1.0f / 1.0625f;
 constexpr float kTailShift = 64.f;
 struct TailAcc {
-  float tp, tq, np, nq;
+  float tp, tq, np, nq, tc;
   uint64_t ukey;
 };
 __device__ __forceinline__ bool tail_race(const RaceDesc& d) {
   return d.resid == 1 && d.inv_zp > kTailInvZ && d.inv_zq > kTailInvZ;
 }
 
-template <typename ET, int NT, int RES, bool QV, bool EVEN, bool TAIL = false>
+template <typename ET, int NT, int RES, bool QV, bool EVEN>
 __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq, const float* rqp, const RaceRow& r,
-                                              float inv_zp, uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un,
-                                              TailAcc* ta = nullptr) {
+                                              float inv_zp, uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un) {
   constexpr int EPV = Elem<ET>::kPerVec;
   const int tid = threadIdx.x;
   float best = 0.f;  // scores are positive; best_y < 0 until a token scores
@@ -1442,21 +1452,13 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   // Nucleus cuts as float compares: key(l, y) >= kappa iff l > value(kappa),
   // or l equals it and y <= index(kappa); kappa = 0 keeps every token.
   auto weight = [&](float lp, float lq, int y) -> float {
-    float p = TAIL ? __builtin_amdgcn_exp2f((lp - r.mp) * r.c + kTailShift) : __builtin_amdgcn_exp2f((lp - r.mp) * r.c);
+    float p = __builtin_amdgcn_exp2f((lp - r.mp) * r.c);
     if (r.cut_p && !(lp > r.kvp || (lp == r.kvp && y <= r.kip))) p = 0.f;
     if (RES == 0) return p;  // the one-hot draft token is masked per vector
     float q;
     if (RES == 1) {
-      q = TAIL ? __builtin_amdgcn_exp2f((lq - r.mq) * r.c + kTailShift) : __builtin_amdgcn_exp2f((lq - r.mq) * r.c);
+      q = __builtin_amdgcn_exp2f((lq - r.mq) * r.c);
       if (r.cut_q && !(lq > r.kvq || (lq == r.kvq && y <= r.kiq))) q = 0.f;
-      if constexpr (TAIL) {
-        const bool ip = lp == r.mp, iq = lq == r.mq;
-        ta->tp += ip ? 0.f : p;
-        ta->np += ip ? 1.f : 0.f;
-        ta->tq += iq ? 0.f : q;
-        ta->nq += iq ? 1.f : 0.f;
-        if (ip && iq) return -1.f;  // weighed by the finish
-      }
       return fmaxf(fmaf(-q, r.ratio, p), 0.f);
     }
     return fmaxf(fmaf(-lq, 1.f / inv_zp, p), 0.f);  // RES 2: q given as a probability
@@ -1471,13 +1473,6 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   constexpr float kBarScale = kRaceSkip * 0x1.0p-32f;
   float bar = 0.f;
   auto consider = [&](float w, uint32_t lo, uint32_t hi, int y) {
-    if constexpr (TAIL) {
-      if (w < 0.f) {
-        const uint64_t k = make_key(__builtin_amdgcn_rcpf(exp1_from_words(lo, hi)), (uint32_t)y);
-        ta->ukey = k > ta->ukey ? k : ta->ukey;
-        return;
-      }
-    }
     if (!(w <= bar * (float)(~hi))) {
       const float sc = w * __builtin_amdgcn_rcpf(exp1_from_words(lo, hi));  // E = 0 gives +inf
       if (sc > best) {
@@ -1536,28 +1531,15 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
   // Two vectors per iteration (more independent Philox chains in flight);
   // the trip count is the same for every lane, so the whole wave takes part
   // in the exchange of the bar.
-  if constexpr (TAIL) {
-    // Rare rows: one vector at a time, so that this path needs no more
-    // registers than the one below.
-    for (int base = 0; base < sl.nvec; base += NT) {
-      const int i0 = base + tid;
-      const bool h0 = i0 < sl.nvec;
-      const uint4 p0 = h0 ? load_stream(vp + i0) : zero4;
-      const uint4 q0 = (QV && h0) ? load_stream(vq + i0) : zero4;
-      if (h0) race_vec(p0, q0, i0);
-      bar = wave_max_f(bar);
-    }
-  } else {
-    for (int base = 0; base < sl.nvec; base += 2 * NT) {
-      const int i0 = base + tid, i1 = i0 + NT;
-      const bool h0 = i0 < sl.nvec, h1 = i1 < sl.nvec;
-      const uint4 p0 = h0 ? load_stream(vp + i0) : zero4, p1 = h1 ? load_stream(vp + i1) : zero4;
-      const uint4 q0 = (QV && h0) ? load_stream(vq + i0) : zero4;
-      const uint4 q1 = (QV && h1) ? load_stream(vq + i1) : zero4;
-      if (h0) race_vec(p0, q0, i0);
-      if (h1) race_vec(p1, q1, i1);
-      bar = wave_max_f(bar);
-    }
+  for (int base = 0; base < sl.nvec; base += 2 * NT) {
+    const int i0 = base + tid, i1 = i0 + NT;
+    const bool h0 = i0 < sl.nvec, h1 = i1 < sl.nvec;
+    const uint4 p0 = h0 ? load_stream(vp + i0) : zero4, p1 = h1 ? load_stream(vp + i1) : zero4;
+    const uint4 q0 = (QV && h0) ? load_stream(vq + i0) : zero4;
+    const uint4 q1 = (QV && h1) ? load_stream(vq + i1) : zero4;
+    if (h0) race_vec(p0, q0, i0);
+    if (h1) race_vec(p1, q1, i1);
+    bar = wave_max_f(bar);
   }
   uint64_t key = best_y >= 0 ? make_key(best, (uint32_t)best_y) : 0ull;
   // Scalar head and tail: keyed directly, so index order does not matter.
@@ -1572,13 +1554,57 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
       const uint64_t kk = make_key(w * __builtin_amdgcn_rcpf(E), (uint32_t)y);
       key = kk > key ? kk : key;
     }
-    if constexpr (TAIL) {
-      if (w < 0.f) {
-        const float E = (y & 1) ? exp1_from_words(rr.z, rr.w) : exp1_from_words(rr.x, rr.y);
-        const uint64_t kk = make_key(__builtin_amdgcn_rcpf(E), (uint32_t)y);
-        ta->ukey = kk > ta->ukey ? kk : ta->ukey;
-      }
+  }
+  return key;
+}
+
+// The scan of a residual race over two peaked rows (tail_race), element by
+// element over [a, e) (a rare path: plain loads, one Philox block per
+// token).  Scores are taken in the log domain, log2(w) - log2(E) with w in
+// units of the target row's largest exponential, so that no residual mass
+// the oracle's fp64 keeps (down to 2^-1074) is lost: w = 2^gp (1 - 2^(gq -
+// gp) Zp / Zq), g = (l - m) c.  Tokens kept in both rows with gp == gq are
+// set aside (ukey: largest gp - log2(E), lowest index) for the finish; the
+// counts of maximal tokens and the masses c, tp, tq (times 2^64) are summed
+// into *ta.
+template <typename ET>
+__device__ __forceinline__ uint64_t race_scan_tail(const ET* rp, const ET* rq, int a, int e, const RaceRow& r,
+                                                   uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un, int nt,
+                                                   TailAcc* ta) {
+  uint64_t key = 0ull;
+#pragma unroll 1
+  for (int y = a + (int)threadIdx.x; y < e; y += nt) {
+    const float lp = Elem<ET>::load1(rp + y), lq = Elem<ET>::load1(rq + y);
+    const bool kp = !r.cut_p || lp > r.kvp || (lp == r.kvp && y <= r.kip);
+    const bool kq = !r.cut_q || lq > r.kvq || (lq == r.kvq && y <= r.kiq);
+    const float gp = (lp - r.mp) * r.c, gq = (lq - r.mq) * r.c;
+    const bool ip = lp == r.mp, iq = lq == r.mq;
+    const bool common = kp && kq && gp == gq;  // equal exponentials (both maxima: gp = gq = 0)
+    const float ep = kp ? __builtin_amdgcn_exp2f(gp + kTailShift) : 0.f;
+    const float eq = kq ? __builtin_amdgcn_exp2f(gq + kTailShift) : 0.f;
+    ta->np += ip ? 1.f : 0.f;
+    ta->nq += iq ? 1.f : 0.f;
+    if (common) {
+      ta->tc += ip ? 0.f : ep;
+    } else {
+      ta->tp += ip ? 0.f : ep;
+      ta->tq += iq ? 0.f : eq;
     }
+    if (!kp) continue;  // p = 0: no residual
+    const uint4 rr = race_block(k0, k1, ub, un, (uint32_t)y);
+    const float E = (y & 1) ? exp1_from_words(rr.z, rr.w) : exp1_from_words(rr.x, rr.y);
+    const float nle = -__builtin_amdgcn_logf(E);  // E = 0: +inf
+    if (common) {
+      const uint64_t k = make_key(gp + nle, (uint32_t)y);
+      ta->ukey = k > ta->ukey ? k : ta->ukey;
+      continue;
+    }
+    const float f = kq ? __builtin_amdgcn_exp2f(gq - gp) * r.ratio : 0.f;
+    if (!(f < 1.f)) continue;  // q >= p: no residual
+    const float lw = gp + __builtin_amdgcn_logf(1.f - f);
+    if (!(lw > -1074.f)) continue;  // below fp64's range, as in the oracle
+    const uint64_t k = make_key(lw + nle, (uint32_t)y);
+    key = k > key ? k : key;
   }
   return key;
 }
@@ -1626,35 +1652,38 @@ __device__ __forceinline__ uint64_t race_split(const RaceDesc& d, const ET* __re
     key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
                : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   } else if (tpart && tail_race(d)) {
-    // Rare rows: the draft row is read element by element (two instances of
-    // this path instead of four keep the kernel's common paths as fast).
-    TailAcc ta{0.f, 0.f, 0.f, 0.f, 0ull};
-    key = even ? race_scan<ET, NT, 1, false, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta)
-               : race_scan<ET, NT, 1, false, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un, &ta);
-    // The split's tails and counts in a fixed order (waves, then lanes).
+    TailAcc ta{0.f, 0.f, 0.f, 0.f, 0.f, 0ull};
+    key = race_scan_tail<ET>(rp, rq, a, e, r, k0, k1, ub, un, NT, &ta);
+    // The split's sums in a fixed order (waves, then lanes).
     ta.tp = wave_sum_f(ta.tp);
     ta.tq = wave_sum_f(ta.tq);
     ta.np = wave_sum_f(ta.np);
     ta.nq = wave_sum_f(ta.nq);
+    ta.tc = wave_sum_f(ta.tc);
     ta.ukey = wave_max_u64(ta.ukey);
     __shared__ float4 tred[NT / kWave];
+    __shared__ float cred[NT / kWave];
     __shared__ uint64_t ured[NT / kWave];
     if (lane_id() == 0) {
       tred[tid / kWave] = make_float4(ta.tp, ta.tq, ta.np, ta.nq);
+      cred[tid / kWave] = ta.tc;
       ured[tid / kWave] = ta.ukey;
     }
     __syncthreads();
     if (tid == 0) {
       float4 t = tred[0];
+      float tc = cred[0];
       uint64_t u = ured[0];
       for (int k = 1; k < NT / kWave; ++k) {
         t.x += tred[k].x;
         t.y += tred[k].y;
         t.z += tred[k].z;
         t.w += tred[k].w;
+        tc += cred[k];
         u = ured[k] > u ? ured[k] : u;
       }
-      tpart[slot] = t;
+      tpart[2 * slot] = t;
+      tpart[2 * slot + 1] = make_float4(tc, 0.f, 0.f, 0.f);
       tkey[slot] = u;
     }
   } else if (q_vec) {
@@ -1821,24 +1850,27 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
   int32_t* dst = out + (size_t)b * (G + 1) + n;
   unsigned long long win = slots[3 * b];
   if (tpart && tail_race(d)) {
-    float tp = 0.f, tq = 0.f, np = 0.f, nq = 0.f;
+    double tp = 0.0, tq = 0.0, np = 0.0, nq = 0.0, tc = 0.0;
     uint64_t u = 0ull;
     for (int s = 0; s < Sr; ++s) {
-      const float4 t = tpart[(size_t)b * Sr + s];
+      const size_t slot = (size_t)b * Sr + s;
+      const float4 t = tpart[2 * slot];
       tp += t.x;
       tq += t.y;
       np += t.z;
       nq += t.w;
-      const uint64_t k = tkey[(size_t)b * Sr + s];
+      tc += tpart[2 * slot + 1].x;
+      const uint64_t k = tkey[slot];
       u = k > u ? k : u;
     }
-    // p - q of a token at both maxima, 1 / Zp - 1 / Zq, taken in fp64 (the
-    // precision of the residual's definition) from Z = n + tail (the tails
-    // carry the scan's factor 2^64), in the scan's units (times Zp 2^64).
-    const double zp = (double)np + 0x1.0p-64 * (double)tp, zq = (double)nq + 0x1.0p-64 * (double)tq;
-    const float wt = (float)((1.0 / zp - 1.0 / zq) * zp * 0x1.0p64);
-    if (u && wt > 0.f) {
-      const uint64_t kk = make_key(wt * key_value(u), key_index(u));
+    // The set-aside tokens' factor 1 / Zp - 1 / Zq, taken in fp64 (the
+    // precision of the residual's definition) from Z = n + c + t (the sums
+    // carry the scan's factor 2^64), in units of the target row's largest
+    // exponential (times Zp); their best score gp - log2(E) plus its log2.
+    const double zp = np + 0x1.0p-64 * (tc + tp), zq = nq + 0x1.0p-64 * (tc + tq);
+    const double wt = (1.0 / zp - 1.0 / zq) * zp;
+    if (u && wt > 0.0) {
+      const uint64_t kk = make_key((float)log2(wt) + key_value(u), key_index(u));
       win = kk > win ? kk : win;
     }
   }
