@@ -101,6 +101,32 @@ def test_small_parity(sv, name, over, k):
     check(sv, wl.entry, inp, T=wl.temperature, k=wl.top_k if k is None else k, seed=wl.verify_seed)
 
 
+@pytest.mark.parametrize("dtype,k", [("f32", 0), ("bf16", 0), ("f32", 1500), ("bf16", 64)])
+def test_low_temperature_misdrawn_drafts(sv, dtype, k):
+    """Verification at T = 0.05 of draft tokens drawn at T = 1 (not from q):
+    rejections fall where p and q are both peaked, so the residual races take
+    their peaked-row forms at a full vocabulary (full rows: log-domain scores
+    and the set-aside tokens weighed from masses summed over 16 vocabulary
+    splits; top-64: log-domain keys over the candidates; top-1500: a cut over
+    the full row).  The masses off the maxima here are large enough for the
+    plain fp32 race as well (the sweep configurations in test_gpu_fuzz.py
+    are the ones it fails); this checks the peaked-row forms at scale.  The
+    single entry and the batch entry with the same setting agree bit for
+    bit."""
+    wl = W["prob_f32_b256_g7_v151936"].scaled(B=16, V=151936, dtype=dtype, temperature=1.0)
+    inp = workloads.generate(wl)
+    got, ref, rep = check(sv, "prob", inp, T=0.05, k=k, seed=77)
+    assert (ref["num_accepted"] < wl.G).sum() >= 8  # most requests reject
+    dev = torch.device("cuda:0")
+    B = wl.B
+    a = sv.verify_batch(inp["target_logits"].to(dev), inp["draft_tokens"].to(dev), inp["draft_logits"].to(dev),
+                        temperature=torch.full((B,), 0.05, dtype=torch.float32, device=dev),
+                        top_k=torch.full((B,), k, dtype=torch.int32, device=dev), max_top_k=max(k, 1), seed=77)
+    torch.cuda.synchronize()
+    assert np.array_equal(a["out_tokens"].cpu().numpy(), got["out_tokens"])
+    assert np.array_equal(a["num_accepted"].cpu().numpy(), got["num_accepted"])
+
+
 @pytest.mark.parametrize("entry,G,k", [("prob", 70, 0), ("onehot", 130, 0), ("greedy", 129, 0),
                                        ("prob", 100, 16), ("onehot", 65, 64), ("prob", 63, 0), ("onehot", 63, 0),
                                        ("prob", 64, 0)])
