@@ -106,8 +106,8 @@ def test_low_temperature_misdrawn_drafts(sv, dtype, k):
     """Verification at T = 0.05 of draft tokens drawn at T = 1 (not from q):
     rejections fall where p and q are both peaked, so the residual races take
     their peaked-row forms at a full vocabulary (full rows: log-domain scores
-    and the set-aside tokens weighed from masses summed over 16 vocabulary
-    splits; top-64: log-domain keys over the candidates; top-1500: a cut over
+    and the set-aside tokens weighed from masses summed over some 70
+    vocabulary splits; top-64: log-domain keys over the candidates; top-1500: a cut over
     the full row).  The masses off the maxima here are large enough for the
     plain fp32 race as well (the sweep configurations in test_gpu_fuzz.py
     are the ones it fails); this checks the peaked-row forms at scale.  The
