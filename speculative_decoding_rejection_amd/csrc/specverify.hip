@@ -406,7 +406,8 @@ sv_status run_race(const Plan& pl, const void* lt, const void* ld, uint32_t k0, 
                      pl.Sr, pl.segr, k0, k1, (const RaceDesc*)desc, slots, tpart, tkey);
   hipLaunchKernelGGL((sv::race_finish_kernel<ET, 256, CUT>), dim3(pl.B), dim3(256), 0, st, (const ET*)lt, pl.G,
                      pl.V, k0, k1, (const RaceDesc*)desc, (const unsigned long long*)slots, out,
-                     (const float4*)tpart, (const unsigned long long*)tkey, pl.Sr);
+                     (const float4*)tpart, (const unsigned long long*)tkey, pl.Sr,
+                     QP ? (const float*)ld : (const float*)nullptr);
   t.done();
   return check_launch();
 }

@@ -1438,8 +1438,9 @@ struct TailAcc {
   float tp, tq, np, nq, tc;
   uint64_t ukey;
 };
+// (Draft probabilities given: a peaked target row suffices.)
 __device__ __forceinline__ bool tail_race(const RaceDesc& d) {
-  return d.resid == 1 && d.inv_zp > kTailInvZ && d.inv_zq > kTailInvZ;
+  return (d.resid == 1 && d.inv_zp > kTailInvZ && d.inv_zq > kTailInvZ) || (d.resid == 2 && d.inv_zp > kTailInvZ);
 }
 
 template <typename ET, int NT, int RES, bool QV, bool EVEN>
@@ -1567,18 +1568,56 @@ __device__ __forceinline__ uint64_t race_scan(const Slice<ET>& sl, const ET* rq,
 // set aside (ukey: largest gp - log2(E), lowest index) for the finish; the
 // counts of maximal tokens and the masses c, tp, tq (times 2^64) are summed
 // into *ta.
-template <typename ET>
-__device__ __forceinline__ uint64_t race_scan_tail(const ET* rp, const ET* rq, int a, int e, const RaceRow& r,
-                                                   uint32_t k0, uint32_t k1, uint32_t ub, uint32_t un, int nt,
-                                                   TailAcc* ta) {
+//
+// log2 of a positive fp32 value, its denormals included (the hardware log
+// takes them as 0): a denormal's bits are its value in units of 2^-149.
+__device__ __forceinline__ float log2_pos(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return b < 0x00800000u ? __builtin_amdgcn_logf((float)b) - 149.f : __builtin_amdgcn_logf(v);
+}
+
+// With the draft given as probabilities (RES 2: q(y) = qp[y]), w = 2^gp -
+// q(y) Zp, taken as gp + log2(1 - 2^(log2 q(y) + log2 Zp - gp)); the target
+// row's maximal tokens are left to the finish, which weighs each with
+// p - q = 1 / Zp - q(y) in fp64 (Zp = np + tp).
+template <typename ET, int RES>
+__device__ __forceinline__ uint64_t race_scan_tail(const ET* rp, const ET* rq, const float* rqp, int a, int e,
+                                                   const RaceRow& r, float inv_zp, uint32_t k0, uint32_t k1,
+                                                   uint32_t ub, uint32_t un, int nt, TailAcc* ta) {
   uint64_t key = 0ull;
+  if constexpr (RES == 2) {
+    const float lzp = -__builtin_amdgcn_logf(inv_zp);  // log2 Zp
+#pragma unroll 1
+    for (int y = a + (int)threadIdx.x; y < e; y += nt) {
+      const float lp = Elem<ET>::load1(rp + y);
+      const bool kp = !r.cut_p || lp > r.kvp || (lp == r.kvp && y <= r.kip);
+      const float gp = (lp - r.mp) * r.c;
+      const bool ip = kp && lp == r.mp;  // a kept maximal token (a tie past a cut is not kept)
+      ta->tp += (kp && !ip) ? __builtin_amdgcn_exp2f(gp + kTailShift) : 0.f;
+      ta->np += ip ? 1.f : 0.f;
+      if (!kp || ip) continue;  // p = 0, or a maximal token (the finish)
+      const float qy = rqp[y];
+      float lw = gp;
+      if ((__float_as_uint(qy) & 0x7FFFFFFFu) != 0u) {
+        const float lf = log2_pos(qy) + lzp - gp;
+        if (!(lf < 0.f)) continue;  // q >= p: no residual
+        lw = gp + __builtin_amdgcn_logf(1.f - __builtin_amdgcn_exp2f(lf));
+      }
+      if (!(lw > -1074.f)) continue;  // below fp64's range, as in the oracle
+      const uint4 rr = race_block(k0, k1, ub, un, (uint32_t)y);
+      const float E = (y & 1) ? exp1_from_words(rr.z, rr.w) : exp1_from_words(rr.x, rr.y);
+      const uint64_t k = make_key(lw - __builtin_amdgcn_logf(E), (uint32_t)y);
+      key = k > key ? k : key;
+    }
+    return key;
+  }
 #pragma unroll 1
   for (int y = a + (int)threadIdx.x; y < e; y += nt) {
     const float lp = Elem<ET>::load1(rp + y), lq = Elem<ET>::load1(rq + y);
     const bool kp = !r.cut_p || lp > r.kvp || (lp == r.kvp && y <= r.kip);
     const bool kq = !r.cut_q || lq > r.kvq || (lq == r.kvq && y <= r.kiq);
     const float gp = (lp - r.mp) * r.c, gq = (lq - r.mq) * r.c;
-    const bool ip = lp == r.mp, iq = lq == r.mq;
+    const bool ip = kp && lp == r.mp, iq = kq && lq == r.mq;  // kept maximal tokens
     const bool common = kp && kq && gp == gq;  // equal exponentials (both maxima: gp = gq = 0)
     const float ep = kp ? __builtin_amdgcn_exp2f(gp + kTailShift) : 0.f;
     const float eq = kq ? __builtin_amdgcn_exp2f(gq + kTailShift) : 0.f;
@@ -1648,12 +1687,10 @@ __device__ __forceinline__ uint64_t race_split(const RaceDesc& d, const ET* __re
   if (!d.resid) {
     key = even ? race_scan<ET, NT, 0, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
                : race_scan<ET, NT, 0, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
-  } else if (QP) {
-    key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
-               : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   } else if (tpart && tail_race(d)) {
     TailAcc ta{0.f, 0.f, 0.f, 0.f, 0.f, 0ull};
-    key = race_scan_tail<ET>(rp, rq, a, e, r, k0, k1, ub, un, NT, &ta);
+    if constexpr (QP) key = race_scan_tail<ET, 2>(rp, rq, rqp, a, e, r, d.inv_zp, k0, k1, ub, un, NT, &ta);
+    else key = race_scan_tail<ET, 1>(rp, rq, rqp, a, e, r, d.inv_zp, k0, k1, ub, un, NT, &ta);
     // The split's sums in a fixed order (waves, then lanes).
     ta.tp = wave_sum_f(ta.tp);
     ta.tq = wave_sum_f(ta.tq);
@@ -1686,6 +1723,9 @@ __device__ __forceinline__ uint64_t race_split(const RaceDesc& d, const ET* __re
       tpart[2 * slot + 1] = make_float4(tc, 0.f, 0.f, 0.f);
       tkey[slot] = u;
     }
+  } else if (QP) {
+    key = even ? race_scan<ET, NT, 2, false, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
+               : race_scan<ET, NT, 2, false, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
   } else if (q_vec) {
     key = even ? race_scan<ET, NT, 1, true, true>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un)
                : race_scan<ET, NT, 1, true, false>(sl, rq, rqp, r, d.inv_zp, k0, k1, ub, un);
@@ -1841,7 +1881,7 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
                                                          int32_t* __restrict__ out,
                                                          const float4* __restrict__ tpart = nullptr,
                                                          const unsigned long long* __restrict__ tkey = nullptr,
-                                                         int Sr = 0) {
+                                                         int Sr = 0, const float* __restrict__ qp = nullptr) {
   const int b = blockIdx.x, tid = threadIdx.x;
   const RaceDesc d = desc[b];
   const int n = d.n;
@@ -1849,7 +1889,37 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
   const float c = d.c;
   int32_t* dst = out + (size_t)b * (G + 1) + n;
   unsigned long long win = slots[3 * b];
-  if (tpart && tail_race(d)) {
+  __shared__ uint64_t red[NT / kWave];
+  if (tpart && qp && d.resid == 2 && tail_race(d)) {
+    // Draft probabilities given: the target row's maximal tokens, each with
+    // p - q = 1 / Zp - q(y) in fp64 (Zp = np + tp, the scan's sums), found
+    // by one more pass over the row (rare rows only).
+    double tp = 0.0, np = 0.0;
+    for (int s = 0; s < Sr; ++s) {
+      const float4 t = tpart[2 * ((size_t)b * Sr + s)];
+      tp += t.x;
+      np += t.z;
+    }
+    const double zp = np + 0x1.0p-64 * tp;
+    const ET* rp = lt + d.prow;
+    const float* rq = qp + d.qrow;
+    uint64_t km = 0ull;
+    for (int y = tid; y < V; y += NT) {
+      const float l = Elem<ET>::load1(rp + y);
+      if (l != d.mp || (CUT && make_key(l, (uint32_t)y) < d.kp)) continue;  // kept maximal tokens
+      const double w = (1.0 / zp - (double)rq[y]) * zp;
+      if (!(w > 0.0)) continue;
+      const uint4 r = race_block(k0, k1, (uint32_t)d.rb, (uint32_t)n, (uint32_t)y);
+      const float E = (y & 1) ? exp1_from_words(r.z, r.w) : exp1_from_words(r.x, r.y);
+      const uint64_t kk = make_key((float)log2(w) - __builtin_amdgcn_logf(E), (uint32_t)y);
+      km = kk > km ? kk : km;
+    }
+    km = wave_max_u64(km);
+    if (lane_id() == 0) red[tid / kWave] = km;
+    __syncthreads();
+    for (int k = 0; k < NT / kWave; ++k) win = red[k] > win ? red[k] : win;
+    __syncthreads();
+  } else if (tpart && tail_race(d)) {
     double tp = 0.0, tq = 0.0, np = 0.0, nq = 0.0, tc = 0.0;
     uint64_t u = 0ull;
     for (int s = 0; s < Sr; ++s) {
@@ -1893,7 +1963,6 @@ __global__ __launch_bounds__(NT) void race_finish_kernel(const ET* __restrict__ 
     }
   }
   kp = wave_max_u64(kp);
-  __shared__ uint64_t red[NT / kWave];
   if (lane_id() == 0) red[tid / kWave] = kp;
   __syncthreads();
   if (tid == 0) {

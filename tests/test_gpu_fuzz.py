@@ -52,6 +52,24 @@ def fuzz_inputs(c: dict) -> dict:
     return inp
 
 
+# Batch configurations with the draft given as fp32 probabilities that
+# randomized sweeps found: 100684 and 100972, T = 0.05 on 3 tokens, a
+# rejection whose residual (1e-66) lies below fp32's range and a draft
+# probability that is an fp32 denormal (9.5e-44), which the hardware
+# logarithm would take as 0; 101291 and 103609, a nucleus cut (top-p 1e-6,
+# 0.1) that keeps one of two tokens tied at the maximum, so that the tied
+# token past the cut must count neither in the kept mass nor in the race.
+BATCH_RESIDUALS = (100684, 100972, 101291, 103609)
+
+
+@pytest.mark.parametrize("i", BATCH_RESIDUALS)
+def test_batch_residual_races(sv, i):  # noqa: F811
+    c = fuzz_case(i)
+    assert c["kind"] == "probs"
+    print(f"[batch residual] case {i}: {c}", flush=True)
+    check(sv, fuzz_inputs(c), c["kind"], c["ragged"], pad_t=c["pad_t"], pad_d=c["pad_d"], seed=c["seed"])
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_fuzz(sv, i):  # noqa: F811
     c = fuzz_case(i)
