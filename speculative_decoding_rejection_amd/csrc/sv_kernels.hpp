@@ -1438,9 +1438,14 @@ struct TailAcc {
   float tp, tq, np, nq, tc;
   uint64_t ukey;
 };
-// (Draft probabilities given: a peaked target row suffices.)
+// Draft logits: also two normalisers within 2^-10 of each other, where 1 -
+// Zp / Zq is as small and the rows' masses off their maxima, without the
+// tokens of equal gap, can still be small.  Draft probabilities given: a
+// peaked target row.
 __device__ __forceinline__ bool tail_race(const RaceDesc& d) {
-  return (d.resid == 1 && d.inv_zp > kTailInvZ && d.inv_zq > kTailInvZ) || (d.resid == 2 && d.inv_zp > kTailInvZ);
+  if (d.resid == 1)
+    return (d.inv_zp > kTailInvZ && d.inv_zq > kTailInvZ) || fabsf(d.inv_zp - d.inv_zq) < 0x1.0p-10f * d.inv_zq;
+  return d.resid == 2 && d.inv_zp > kTailInvZ;
 }
 
 template <typename ET, int NT, int RES, bool QV, bool EVEN>

@@ -151,12 +151,13 @@ def test_fuzz_single(sv, i):  # noqa: F811
 # below 2^-190 (down to 1e-85; 21735: bf16).  30514: a top-k of 1025 (a cut
 # over the full row) where a token with the same gap below both maxima carries
 # the rows' masses off their maxima.  40154: top-20 candidates with a
-# residual of 1e-109.  The single entry (for full rows, accept and race in
+# residual of 1e-109.  201617: a row that is not peaked (a token 0.125 below
+# both maxima holds 8% of the mass) with normalisers that agree to 6e-9.  The single entry (for full rows, accept and race in
 # one launch) and the batch entry with the same setting (separate accept,
 # race and finish) both run the race; they must agree bit for bit, and with
 # the oracle.
 LOW_T_RESIDUALS = (5000, 5033, 5160, 5211, 5255, 5289, 5421, 5511, 5541, 7768, 9270, 9366, 20867, 21735, 22450,
-                   30514, 40154)
+                   30514, 40154, 201617)
 
 
 @pytest.mark.parametrize("i", LOW_T_RESIDUALS)
