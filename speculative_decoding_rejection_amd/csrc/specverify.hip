@@ -564,6 +564,28 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     t.done();
     if ((s = check_launch()) != SV_OK) return s;
   }
+  // The side streams join the caller's stream after the row phase, or (when
+  // the kernels are not timed by family) at the end of the call: the
+  // full-row requests' accept and race read nothing the side streams write,
+  // so they run beside the top-k and temperature-0 row passes.  Sampler-match
+  // samples read the top-k candidates and join first.
+  const bool late_join = MODE != 3 && !g_timing;
+  std::unique_lock<std::mutex> lock(g_side_mu);
+  SideStreams* side = nullptr;
+  hipStream_t s_topk = st, s_arg = st;
+  // The caller's stream waits for both side streams (also after a failed
+  // launch); the lock is released once the join is enqueued.
+  auto join = [&]() -> sv_status {
+    sv_status r = SV_OK;
+    if (s_topk != st &&
+        (hipEventRecord(side->join[0], s_topk) != hipSuccess || hipEventRecord(side->join[1], s_arg) != hipSuccess ||
+         hipStreamWaitEvent(st, side->join[0], 0) != hipSuccess ||
+         hipStreamWaitEvent(st, side->join[1], 0) != hipSuccess))
+      r = SV_ERR_HIP;
+    s_topk = s_arg = st;
+    if (lock.owns_lock()) lock.unlock();
+    return r;
+  };
   {
     // Row phase: top-k rows (candidates, then their nucleus, then the
     // top-k requests' accept pass) on side stream 0, temperature-0 rows
@@ -572,9 +594,7 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
     // stream.  The three write disjoint parts of the workspace and of the
     // outputs.
     TimedLaunch t(0, st);
-    std::unique_lock<std::mutex> lock(g_side_mu);
-    SideStreams* side = side_streams(st);
-    hipStream_t s_topk = st, s_arg = st;
+    side = side_streams(st);
     if (side && hipEventRecord(side->fork, st) == hipSuccess &&
         hipStreamWaitEvent(side->s[0], side->fork, 0) == hipSuccess &&
         hipStreamWaitEvent(side->s[1], side->fork, 0) == hipSuccess) {
@@ -627,34 +647,28 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
       double* nhist = (double*)(ws + pl.off_nhist);
       sv::NucState* nstate = (sv::NucState*)(ws + pl.off_nstate);
       uint64_t* nkeys = (uint64_t*)(ws + pl.off_nkeys);
-      const float2* sp = (const float2*)(ws + pl.off_part);
+      float2* sp = (float2*)(ws + pl.off_part);
       const dim3 nt(sv::NucShape::NT);
       hipLaunchKernelGGL((sv::nucleus_part_kernel<ET>), dim3(pl.nuc_items > nrows ? pl.nuc_items : nrows), nt, 0,
-                         st, (const ET*)lt,
-                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, sp, (const ReqInfo*)info, cut, pl.L,
-                         (const int*)nplan, (const int*)nlist, nhist);
+                         st, (const ET*)lt, (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, sp, (const ReqInfo*)info,
+                         cut, pl.L, (const int*)nplan, (const int*)nlist, nhist);
       hipLaunchKernelGGL(sv::nucleus_scan_kernel, dim3(pl.nuc_rows), nt, 0, st, pl.rows_t, pl.G, pl.S, sp,
                          (const ReqInfo*)info, cut, (const int*)nplan, (const int*)nlist, (const double*)nhist,
                          nstate);
       hipLaunchKernelGGL((sv::nucleus_collect_kernel<ET>), dim3(pl.nuc_items), nt, 0, st, (const ET*)lt,
-                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, sp, (const ReqInfo*)info, pl.L,
-                         (const int*)nplan, (const int*)nlist, nstate, nkeys);
+                         (const ET*)ldl, pl.rows_t, pl.G, pl.V, (const ReqInfo*)info, pl.L, (const int*)nplan,
+                         (const int*)nlist, nstate, nkeys);
       hipLaunchKernelGGL((sv::nucleus_finish_kernel<ET>), dim3(pl.nuc_rows), nt, 0, st, (const ET*)lt,
                          (const ET*)ldl, pl.rows_t, pl.G, pl.V, pl.S, sp, (const ReqInfo*)info, cut, pl.L,
                          (const int*)nplan, (const int*)nlist, (const sv::NucState*)nstate,
                          (const uint64_t*)nkeys);
     }
     if (rs == SV_OK) rs = check_launch();
-    if (s_topk != st) {
-      // Join (also after a failed launch): the caller's stream waits for
-      // both side streams.
-      if (hipEventRecord(side->join[0], s_topk) != hipSuccess || hipEventRecord(side->join[1], s_arg) != hipSuccess ||
-          hipStreamWaitEvent(st, side->join[0], 0) != hipSuccess ||
-          hipStreamWaitEvent(st, side->join[1], 0) != hipSuccess)
-        rs = SV_ERR_HIP;
+    if (rs != SV_OK || !late_join) {
+      const sv_status js = join();
+      if (rs == SV_OK) rs = js;
     }
     if (rs != SV_OK) return rs;
-    lock.unlock();
     t.done();
   }
   if (MODE == 3) {
@@ -686,31 +700,38 @@ sv_status verify_batch(const Plan& pl, const BatchArgs& ba, uint64_t seed, const
   }
   RaceDesc* desc = (RaceDesc*)(ws + pl.off_desc);
   unsigned long long* slots = (unsigned long long*)(ws + pl.off_slots);
-  {
-    // Full-row requests (the top-k and temperature-0 ones were accepted on
-    // the side streams, before the join).
-    TimedLaunch t(1, st);
-    const sv::Stats stats{beta, counters};
-    hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
-                       (const ET*)ldl, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0,
-                       k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
-                       (const RowCut*)(use_cut ? cut : nullptr), pl.L, qp, stats);
-    t.done();
-    if ((s = check_launch()) != SV_OK) return s;
-  }
-  if (beta && MODE != 1) {
-    // Acceptance probability of every position of requests without top-k:
-    // one more read of their target and draft rows.
-    TimedLaunch t(1, st);
-    hipLaunchKernelGGL((sv::beta_full_kernel<ET, MODE == 2>), dim3(pl.B * pl.G), dim3(256), 0, st, (const ET*)lt,
-                       (const ET*)ldl, qp, (const float2*)(ws + pl.off_part), pl.G, pl.V, pl.S, pl.rows_t,
-                       (const ReqInfo*)info, (const RowCut*)(use_cut ? cut : nullptr), pl.L, beta);
-    t.done();
-    if ((s = check_launch()) != SV_OK) return s;
-  }
-  constexpr bool QP = MODE == 2;
-  if (use_cut) return run_race<ET, true, QP>(pl, lt, ld, k0, k1, ws, out, st);
-  return run_race<ET, false, QP>(pl, lt, ld, k0, k1, ws, out, st);
+  // Full-row requests (the top-k and temperature-0 ones are accepted on the
+  // side streams): accept, beta and race on the caller's stream, then the
+  // join if it is still pending.
+  auto tail = [&]() -> sv_status {
+    sv_status r;
+    {
+      TimedLaunch t(1, st);
+      const sv::Stats stats{beta, counters};
+      hipLaunchKernelGGL((sv::accept_full_kernel<ET, MODE>), dim3(pl.B), dim3(64), 0, st, (const ET*)lt,
+                         (const ET*)ldl, (const float2*)(ws + pl.off_part), X, pl.G, pl.V, pl.S, pl.rows_t, 0.f, k0,
+                         k1, out, nacc, p_draft, q_draft, desc, slots, err, (const ReqInfo*)info,
+                         (const RowCut*)(use_cut ? cut : nullptr), pl.L, qp, stats);
+      t.done();
+      if ((r = check_launch()) != SV_OK) return r;
+    }
+    if (beta && MODE != 1) {
+      // Acceptance probability of every position of requests without top-k:
+      // one more read of their target and draft rows.
+      TimedLaunch t(1, st);
+      hipLaunchKernelGGL((sv::beta_full_kernel<ET, MODE == 2>), dim3(pl.B * pl.G), dim3(256), 0, st,
+                         (const ET*)lt, (const ET*)ldl, qp, (const float2*)(ws + pl.off_part), pl.G, pl.V, pl.S,
+                         pl.rows_t, (const ReqInfo*)info, (const RowCut*)(use_cut ? cut : nullptr), pl.L, beta);
+      t.done();
+      if ((r = check_launch()) != SV_OK) return r;
+    }
+    constexpr bool QP = MODE == 2;
+    if (use_cut) return run_race<ET, true, QP>(pl, lt, ld, k0, k1, ws, out, st);
+    return run_race<ET, false, QP>(pl, lt, ld, k0, k1, ws, out, st);
+  };
+  const sv_status ts = tail();
+  const sv_status js = join();
+  return ts != SV_OK ? ts : js;
 }
 
 // A single-setting call whose top-k exceeds the candidate capacity (and is

@@ -298,38 +298,63 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 }
 
 // ===========================================================================
-// Nucleus of a full row (no top-k), after the softmax row pass (whose
-// partials give the row's largest logit).  The steps below, as nucleus_row
+// Nucleus of a full row (no top-k candidates).  The steps, as nucleus_row
 // runs them with one workgroup per row; with few such rows in a call, the
 // same steps are split over chunks of each row (the nucleus passes further
-// below).
+// below):
 //
-//   pass 1  a histogram of fp64 mass over bins of the gap d = (l_max - l) /
-//           T, ln2 / 64 nats per bin over [0, 44.4) (each bin sums its
-//           tokens' masses divided by the bin's common power of two, which
-//           is applied once per bin afterwards), and the total Z.  Tokens
-//           further below the maximum carry less than 2^31 e^-44 < 2e-10 of
-//           Z in total, so the cut (top_p <= 1 - 2^-24) always falls inside
-//           the histogram.
-//   scan    the bin where the running mass reaches top_p * Z, and the mass A
-//           of the bins before it.
+//   pass 1  a histogram of fp64 mass over bins ln2 / 64 nats wide, the row's
+//           largest logit and its total mass Z, in one read of the row (the
+//           softmax pass skips these rows).
+//   scan    the bin where the running mass, from the largest logit down,
+//           reaches top_p Z, and the mass A of the bins before it.
 //   pass 2  the bin's tokens are collected into LDS (at most kNucCap; the
 //           histogram's storage), sorted by key and walked from A: the first
-//           token that reaches top_p * Z is the cut.
+//           token that reaches top_p Z is the cut.
 //   refine  (a bin with more than kNucCap tokens, e.g. many equal logits)
 //           radix passes over the keys of that bin, 8 bits at a time below
 //           their common prefix, each keeping the digit that holds the cut,
 //           until at most kNucCap tokens remain.
-// Each pass streams the row from HBM.
+//
+// The grid.  With 1/T = it and C = 64 it / ln2, token l falls in bin
+// k(l) = round(y), y = (l - a) C (the exact product, rounded once by fma),
+// for an anchor a fixed before pass 1 reads the row: 0 for a row split over
+// chunks (every chunk bins alike), the largest logit of a first look for a
+// row read by one workgroup.  k is non-decreasing in l, so the bins cut the
+// row in key order.  With kmax the bin of the row's largest logit, every mass
+// of the nucleus passes is taken in the unit 2^((y - kmax) / 64) =
+// 2^((k - kmax) / 64) 2^(f / 64), f = y - k in [-1/2, 1/2]: a bin sums its
+// tokens' 2^(f / 64) and its power of two is applied once, and the walk and
+// the refinement take each token's mass the same way, so all of them agree
+// to rounding.  The row's masses exp((l - lmax) / T) are these times
+// g = 2^((kmax - y(lmax)) / 64), applied to the kept mass at the end.
+//
+// The window.  A workgroup holds kNucBins consecutive bins in LDS, bin k in
+// slot k mod kNucBins.  Before any token is added, the largest logit l0 of
+// the vectors the workgroup loads first places the window at bins
+// (k0 + R - kNucBins, k0 + R], k0 = k(l0), R = kNucRise.  A token below the
+// window adds its mass exp((l - l0) / T) to a spare sum; a token above it is
+// listed (at most kNucRiseCap) until the workgroup's maximum is known, and
+// the window then moves up to (kmax - kNucBins, kmax]: the bins it leaves go
+// into the spare sum, the listed tokens into their bins.  Either way every
+// bin within kNucBins - R bins (38.8 nats) of kmax holds its exact sum; the
+// tokens further below carry less than 2^31 e^-38.8 < 3.1e-8 of Z in total,
+// so the cut (top_p <= 1 - 2^-24) falls among the held bins.  A row whose
+// list overflows (e.g. ascending logits) or whose bins leave fp64's exact
+// integers is binned again with its maximum known (anchor and window at the
+// maximum): one more read, for that row only.  Rows under a large top-k take
+// that form from the start (the softmax pass before their top-k cut gives
+// the maximum).
 // ===========================================================================
-constexpr int kNucBins = 4096;  // ln2 / 64 nats each: gaps below 44.4 nats
+constexpr int kNucBins = 4096;      // slots of the window: ln2 / 64 nats each
+constexpr int kNucRise = 512;       // bins of the window above the first look's maximum
+constexpr int kNucRiseCap = 256;    // tokens listed above the window
+constexpr double kNucRange = 0x1.0p49;  // |y| bound of the window's bins (exact fp64 integers)
 // A workgroup per row (or per chunk): 512 threads, two vectors per thread in
-// flight (build knobs SV_NUC_NT, SV_NUC_U).  Measured on MI355X with pass 1
-// as below, against 256 x 2, 256 x 4, 512 x 3, 1024 x 1 and 1024 x 2: the
-// fastest or within 1% on the mixed, ragged and sampler-match workloads
-// (256 x 2 is 2% faster on a batch of top-p rows only and 5 to 6% slower on
-// the ragged and sampler-match ones).  The 32 KB fp64 histogram holds a CU
-// to two such workgroups.
+// flight (build knobs SV_NUC_NT, SV_NUC_U).  Measured on MI355X against
+// 256 x 2, 256 x 4, 512 x 3, 1024 x 1 and 1024 x 2 (with the earlier pass 1
+// that read the row after the softmax pass): the fastest or within 1% on the
+// mixed, ragged and sampler-match workloads.
 #ifndef SV_NUC_NT
 #define SV_NUC_NT 512
 #endif
@@ -341,14 +366,6 @@ struct NucShape {
 };
 constexpr int kCutThreads = 512;  // kcut_full_kernel
 constexpr int kNucCap = 2048;
-
-// Gap bin of logit l (-1: none), from the same rounding as the mass.
-// Branch-free: a gap beyond 700 nats (or an infinite one) rounds at 700,
-// which lies far past the last bin.
-__device__ __forceinline__ int nucleus_bin(double lm, float l, double it) {
-  const int b = -nucleus_k(fmax(((double)l - lm) * it, -700.0));
-  return b < kNucBins ? b : -1;
-}
 
 // Streams the row through the workgroup: fv(values, y0) for each 16-byte
 // vector this thread owns (elements y0 .. y0 + EPV - 1), fs(value, y) for the
@@ -423,12 +440,23 @@ __device__ __forceinline__ void row_foreach(const ET* rp, int V, F&& f) {
       f);
 }
 
-// The gap histogram of the nucleus passes (+ the spare slot of tokens
-// without a bin), one LDS array per kernel; dead once the cut bin is chosen,
-// it then holds the collected keys of that bin.
+// The window of the nucleus passes (kNucBins slots), one LDS array per
+// kernel; dead once the cut bin is chosen, it then holds the collected keys
+// of that bin.
 __device__ __forceinline__ double* nucleus_hist_lds() {
-  __shared__ double hm[kNucBins + 1];
+  __shared__ double hm[kNucBins];
   return hm;
+}
+
+// Tokens listed above the window, and a reduction buffer, for pass 1.
+struct NucRise {
+  float l[kNucRiseCap];
+  int n;
+  float red[NucShape::NT / kWave];
+};
+__device__ __forceinline__ NucRise* nucleus_rise_lds() {
+  __shared__ NucRise s;
+  return &s;
 }
 
 // Largest logit of a row, from the softmax pass's partials (every lane of
@@ -439,93 +467,279 @@ __device__ __forceinline__ float nucleus_lmax(const float2* part, int row, int S
   return wave_max_f(lmax);
 }
 
+// Writes a row's softmax partials as one split (max, mass) and empty ones,
+// for a row whose softmax pass was skipped.  By the whole workgroup.
+__device__ __forceinline__ void nucleus_write_part(float2* part, int row, int S, float lmax, float Z) {
+  for (int k = threadIdx.x; k < S; k += blockDim.x)
+    part[(size_t)row * S + k] = k == 0 ? make_float2(lmax, Z) : make_float2(-INFINITY, 0.f);
+}
+
+// Largest value over the workgroup (NT threads), to every thread.  Ends with
+// a barrier.
+template <int NT>
+__device__ __forceinline__ float block_max_f(float v, float* red) {
+  constexpr int NW = NT / kWave;
+  v = wave_max_f(v);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) m = fmaxf(m, red[k]);
+  __syncthreads();
+  return m;
+}
+
+// Sum over the workgroup (NT threads), to every thread.  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+  constexpr int NW = NT / kWave;
+  v = wave_sum_d(v);
+  if (lane_id() == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) s += red[k];
+  __syncthreads();
+  return s;
+}
+
 // 2^(f/64) for |f| <= 1/2: exp(c f), c = ln2 / 64, by its Taylor polynomial
-// of degree 5 (|c f| <= 0.0055, truncation below 4e-17 relative).
+// of degree 4 (|c f| <= 0.0055, truncation below 4e-14 relative).
 __device__ __forceinline__ double exp2_frac64(double f) {
   constexpr double c = 0.6931471805599453 / 64.0;
-  constexpr double a2 = c * c / 2.0, a3 = a2 * c / 3.0, a4 = a3 * c / 4.0, a5 = a4 * c / 5.0;
-  double q = fma(f, a5, a4);
-  q = fma(f, q, a3);
+  constexpr double a2 = c * c / 2.0, a3 = a2 * c / 3.0, a4 = a3 * c / 4.0;
+  double q = fma(f, a4, a3);
   q = fma(f, q, a2);
   q = fma(f, q, c);
   return fma(f, q, 1.0);
 }
 
-// Pass 1 over elements [a, e) of a row, into the LDS gap histogram.  A
-// token's mass exp(x), x = (l - lm) / T <= 0, is 2^(k/64) 2^(f/64) with
-// k = round(64 x / ln2) (the token's gap bin is -k, the rounding of
-// nucleus_bin) and |f| <= 1/2.  Every token of a bin shares the factor
-// 2^(k/64), so a bin adds up only the tokens' 2^(f/64); nucleus_unfactor
-// multiplies each bin by its factor once.  A token beyond the last bin (a
-// gap over 44.4 nats: rare) adds its whole mass, by the table-driven exp, to
-// the spare slot hm[kNucBins].  With FLOOR, a token whose key is below
-// kfloor adds 0.
-template <typename ET, int NT, int U, bool FLOOR>
-__device__ __forceinline__ void nucleus_pass1(const ET* rp, int a, int e, double lm, double it, uint64_t kfloor,
-                                              const double* tab, double* hm) {
-  auto add = [&](float l, int y) {
-    const double x = ((double)l - lm) * it;
-    const double t = fma(fmax(x, -700.0), kNucInvStep, kNucRound);
-    const double kd = t - kNucRound;
-    const int bin = -__double2loint(t);
-    const bool in = bin < kNucBins;
-    double v = exp2_frac64(fma(fmax(x, -700.0), kNucInvStep, -kd));
-    if (!in) {
-      int k;
-      v = exp_nonpos_f64(x, tab, &k);
-    }
-    if (FLOOR && make_key(l, (uint32_t)y) < kfloor) v = 0.0;
-    atomicAdd(&hm[in ? bin : kNucBins], v);
-  };
-  row_stream<ET, NT, U>(
-      rp, a, e,
-      [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
-#pragma unroll
-        for (int k = 0; k < Elem<ET>::kPerVec; ++k) add(fv[k], y0 + k);
-      },
-      add);
+// 2^(j/64) for an integer j <= 2^16 (tab[i] = 2^(i/64)); 0 below fp64's
+// range.
+__device__ __forceinline__ double exp2_64ths(double j, const double* tab) {
+  const int k = (int)fmin(fmax(j, -1048576.0), 65536.0);
+  return ldexp(tab[k & 63], k >> 6);
 }
 
-// Bin b of a pass-1 histogram times its factor 2^(-b/64): the masses of the
-// gap bins, in place (the spare slot already holds masses).  Returns the
-// row's total mass Z (bins and spare slot) to every thread.  Starts after a
+// 2^(e/64) for real e <= 2^16 (0 below fp64's range).
+__device__ __forceinline__ double exp2_64(double e, const double* tab) {
+  const double n = rint(e);
+  return e > -1048576.0 ? exp2_64ths(n, tab) * exp2_frac64(e - n) : 0.0;
+}
+
+// The bin grid of a row: t(l) = fma(l, C, B) rounds l C + B once to an
+// integer (B = kNucRound - rint(a C), an integer near kNucRound, for anchor
+// a), so token l is in bin k(l) = t(l) - kNucRound, with y = l C + B -
+// kNucRound and f = y - k = fma(l, C, B - t(l)) (an exact integer added to
+// the exact product, rounded once).  Exact while |y| < 2^51.
+struct NucGrid {
+  double B, C, kmax;  // offset, bins per unit of logit, bin of the largest logit
+};
+__device__ __forceinline__ double nuc_grid_B(double anchor, double C) { return kNucRound - rint(anchor * C); }
+__device__ __forceinline__ double nuc_t(float l, const NucGrid& g) { return fma((double)l, g.C, g.B); }
+
+// A token's mass in the grid's unit, 2^((y - kmax) / 64).
+__device__ __forceinline__ double nuc_mass(const NucGrid& g, float l, const double* tab) {
+  const double t = nuc_t(l, g);
+  const double m = exp2_64ths(t - kNucRound - g.kmax, tab) * exp2_frac64(fma((double)l, g.C, g.B - t));
+  return l == -INFINITY ? 0.0 : m;
+}
+
+// Result of pass 1 over a slice: the grid and window top kmax, the logit l0
+// that placed the window, the largest logit lmax (-inf: none finite), and
+// this thread's spare masses: sp in units of exp((l - l0) / T), sb in the
+// grid's unit.  ok false: the row must be binned again with its maximum
+// known.
+struct NucP1 {
+  NucGrid g;
+  float l0, lmax;
+  bool ok;
+  double sp, sb;
+};
+
+// Pass 1 over elements [a_, e_) of a row into the window hm (kNucBins slots,
+// zeroed by the caller, who also clears the rise list's count before a
+// barrier); tab[i] = 2^(i/64).  LOOK: the window is placed by a first look
+// at the vectors the workgroup loads first (the next ones while those hold
+// no finite logit), and the anchor is l0 when anchor_l0, else `anchor`.
+// !LOOK: the row's largest logit lm is known and is both anchor and l0; with
+// FLOOR a token whose key is below kfloor adds nothing.  Workgroup-uniform
+// result after a barrier.
+template <typename ET, int NT, int U, bool LOOK, bool FLOOR>
+__device__ NucP1 nucleus_pass1(const ET* rp, int a_, int e_, bool anchor_l0, double anchor, float lm, double it,
+                               uint64_t kfloor, const double* tab, double* hm) {
+  constexpr int EPV = Elem<ET>::kPerVec, STEP = NT * U, S = kNucBins;
+  NucRise* rl = nucleus_rise_lds();
+  const double C = it * kNucInvStep;
+  Slice<ET> sl(rp, a_, e_);
+  const int tid = threadIdx.x;
+  float sv = -INFINITY;
+  int sy = 0;
+  if (tid < sl.nscalar()) {
+    sy = sl.scalar_index(tid);
+    sv = Elem<ET>::load1(rp + sy);
+  }
+  const uint4* vp = sl.vecs();
+  const int nv = sl.nvec, nch = (nv + STEP - 1) / STEP;
+  const uint4 ninf = make_uint4(Elem<ET>::kNegInfWord, Elem<ET>::kNegInfWord, Elem<ET>::kNegInfWord,
+                                Elem<ET>::kNegInfWord);
+  // Chunk c's vectors of this thread; past the slice's end the load is
+  // clamped into it (unconditional) and the value replaced by -inf.
+  auto load = [&](int c, uint4(&v)[U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = c * STEP + u * NT + tid;
+      const uint4 x = load_stream(vp + (i < nv ? i : nv - 1));
+      v[u] = i < nv ? x : ninf;
+    }
+  };
+  uint4 cur[U];
+  int c = 0;
+  if (nch > 0) load(0, cur);
+  float l0 = lm;
+  if constexpr (LOOK) {
+    for (;;) {
+      float tm = c == 0 ? sv : -INFINITY;
+      if (c < nch) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          float f[EPV];
+          Elem<ET>::unpack(cur[u], f);
+#pragma unroll
+          for (int k = 0; k < EPV; ++k) tm = fmaxf(tm, f[k]);
+        }
+      }
+      l0 = block_max_f<NT>(tm, rl->red);
+      if (l0 != -INFINITY || c + 1 >= nch) break;  // uniform
+      ++c;  // chunks before c hold no finite logit (no mass)
+      load(c, cur);
+    }
+  }
+  NucP1 r;
+  r.g.B = kNucRound;
+  r.g.C = C;
+  r.g.kmax = 0.0;
+  r.l0 = l0;
+  r.lmax = -INFINITY;
+  r.ok = true;
+  r.sp = 0.0;
+  r.sb = 0.0;
+  if (l0 == -INFINITY) return r;  // no finite logit in the slice (uniform)
+  r.g.B = nuc_grid_B(LOOK ? (anchor_l0 ? (double)l0 : anchor) : (double)lm, C);
+  const double B = r.g.B;
+  // The window (lo, hi] in bins, as t values.
+  const double hi = nuc_t(l0, r.g) + (double)kNucRise, lo = hi - (double)S;
+  float tmax = -INFINITY;
+  double sp = 0.0;
+  // Below the window a token lies more than 38.8 nats under l0, and all of
+  // them carry less than 3.1e-8 of Z: their masses are taken in fp32 (about
+  // 1e-5 relative), so Z keeps about 1e-12 relative accuracy.
+  const float c2 = (float)(it * 1.4426950408889634);
+  auto add = [&](float l, int y) {
+    tmax = fmaxf(tmax, l);
+    if (FLOOR && make_key(l, (uint32_t)y) < kfloor) return;
+    const double t = fma((double)l, C, B);
+    if (t > lo && t <= hi) {
+      atomicAdd(&hm[__double2loint(t) & (S - 1)], exp2_frac64(fma((double)l, C, B - t)));
+    } else if (t > hi) {
+      const int pos = atomicAdd(&rl->n, 1);
+      if (pos < kNucRiseCap) rl->l[pos] = l;
+    } else {
+      const float m = __builtin_amdgcn_exp2f((l - l0) * c2);
+      sp += m > 0.f ? (double)m : 0.0;  // 0 for -inf and NaN
+    }
+  };
+  if (tid < sl.nscalar()) add(sv, sy);
+  for (; c < nch; ++c) {
+    uint4 nxt[U];
+    if (c + 1 < nch) load(c + 1, nxt);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float f[EPV];
+      Elem<ET>::unpack(cur[u], f);
+      const int y0 = sl.vec_index0(c * STEP + u * NT + tid);
+#pragma unroll
+      for (int k = 0; k < EPV; ++k) add(f[k], y0 + k);
+    }
+    if (c + 1 < nch) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+  }
+  r.sp = sp;
+  const float lmax = block_max_f<NT>(tmax, rl->red);  // its barrier also ends every add
+  r.lmax = lmax;
+  if (lmax == -INFINITY) return r;  // every token -inf (uniform)
+  const int nr = rl->n;
+  const double tmx = nuc_t(lmax, r.g);
+  const double kmax = tmx - kNucRound;
+  r.g.kmax = kmax;
+  r.ok = nr <= kNucRiseCap && fabs(fma((double)lmax, C, B - kNucRound)) < kNucRange &&
+         fabs(fma((double)l0, C, B - kNucRound)) < kNucRange;
+  if (r.ok && nr > 0) {
+    // The window moves up to (kmax - S, kmax]: bins (lo, kmax - S] leave it
+    // (slot i holds bin hi - dist, dist = (hi - i) mod S; t values).
+    const double shift = tmx - hi;  // > 0: a listed token lies above hi
+    const int top = __double2loint(hi);
+    double sb = 0.0;
+    for (int i = tid; i < S; i += NT) {
+      const int dist = (top - i) & (S - 1);
+      if ((double)dist >= (double)S - shift) {
+        const double v = hm[i];
+        if (v != 0.0) sb += v * exp2_64ths(-((double)dist + shift), tab);
+        hm[i] = 0.0;
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nr; i += NT) {
+      const float l = rl->l[i];
+      const double t = fma((double)l, C, B);
+      const double v = exp2_frac64(fma((double)l, C, B - t));
+      if (t > tmx - (double)S) atomicAdd(&hm[__double2loint(t) & (S - 1)], v);
+      else sb += v * exp2_64ths(t - tmx, tab);
+    }
+    __syncthreads();
+    r.sb = sb;
+  }
+  return r;
+}
+
+// Bin masses in the grid's unit, in place: slot i of a window with top bin
+// kmax (top = kmax mod 2^32) holds gap j = (top - i) mod kNucBins and is
+// multiplied by 2^(-j/64).  Returns the total, bins plus every thread's
+// spare (already in the grid's unit), to every thread.  Starts after a
 // barrier and ends with one.
 template <int NT>
-__device__ __forceinline__ double nucleus_unfactor(double* hm, double spare, const double* tab, double* red) {
-  constexpr int NW = NT / kWave;
-  const int tid = threadIdx.x;
-  double z = tid == 0 ? spare : 0.0;
-  for (int i = tid; i < kNucBins; i += NT) {
+__device__ __forceinline__ double nucleus_unfactor(double* hm, int top, double spare, const double* tab,
+                                                   double* red) {
+  double z = spare;
+  for (int i = threadIdx.x; i < kNucBins; i += NT) {
     const double v = hm[i];
     if (v != 0.0) {
-      const int k = -i;
-      const double m = v * ldexp(tab[k & 63], k >> 6);
+      const int j = (top - i) & (kNucBins - 1);
+      const double m = v * ldexp(tab[(-j) & 63], (-j) >> 6);
       hm[i] = m;
       z += m;
     }
   }
-  z = wave_sum_d(z);
-  if (lane_id() == 0) red[tid / kWave] = z;
-  __syncthreads();
-  double Z = 0.0;
-  for (int k = 0; k < NW; ++k) Z += red[k];
-  __syncthreads();
-  return Z;
+  return block_sum_d<NT>(z, red);
 }
 
-// Scan of the gap histogram by a workgroup of NT threads: thread t owns bins
-// [t * PER, (t + 1) * PER); its interval of running mass is (incl[t - 1],
-// incl[t]], so the intervals tile [0, total].  Writes the first non-empty bin
-// where the running mass reaches target to *bin_out (-1 if none) and the mass
-// of the bins before it to *A_out.  Ends with a barrier.
+// Scan of the window by a workgroup of NT threads in gap order (gap j in
+// slot (top - j) mod kNucBins): thread t owns gaps [t * PER, (t + 1) * PER);
+// its interval of running mass is (incl[t - 1], incl[t]], so the intervals
+// tile [0, total].  Writes the first non-empty gap where the running mass
+// reaches target to *bin_out (-1 if none) and the mass of the gaps before it
+// to *A_out.  Ends with a barrier.
 template <int NT>
-__device__ __forceinline__ void nucleus_pick(const double* hm, double target, double* incl_sh, double* red_s,
-                                             int* bin_out, double* A_out) {
+__device__ __forceinline__ void nucleus_pick(const double* hm, int top, double target, double* incl_sh,
+                                             double* red_s, int* bin_out, double* A_out) {
   constexpr int PER = kNucBins / NT, NW = NT / kWave;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  auto at = [&](int j) { return hm[(top - j) & (kNucBins - 1)]; };
   if (tid == 0) *bin_out = -1;
   double loc = 0.0;
-  for (int k = 0; k < PER; ++k) loc += hm[tid * PER + k];
+  for (int k = 0; k < PER; ++k) loc += at(tid * PER + k);
   double inc = wave_incl_scan_d(loc);
   if (lane == kWave - 1) red_s[w] = inc;
   __syncthreads();
@@ -538,11 +752,12 @@ __device__ __forceinline__ void nucleus_pick(const double* hm, double target, do
     int pick = -1;
     double pickA = start;
     for (int k = 0; k < PER; ++k) {
-      const int bin = tid * PER + k;
-      if (!(hm[bin] > 0.0)) continue;
-      pick = bin;  // last non-empty bin so far: the choice if rounding leaves the target unreached
+      const int j = tid * PER + k;
+      const double v = at(j);
+      if (!(v > 0.0)) continue;
+      pick = j;  // last non-empty gap so far: the choice if rounding leaves the target unreached
       pickA = cum;
-      const double nxt = cum + hm[bin];
+      const double nxt = cum + v;
       if (nxt >= target) break;
       cum = nxt;
     }
@@ -552,12 +767,11 @@ __device__ __forceinline__ void nucleus_pick(const double* hm, double target, do
   __syncthreads();
 }
 
-// Pass 2 over elements [a, e): push(l, y) for every token of gap bin bstar.
-// The bins of a vector's tokens first (branch-free), then the rare tokens of
+// Pass 2 over elements [a, e): push(l, y) for every token with in_bin(l).
+// The test of a vector's tokens first (branch-free), then the rare tokens of
 // the chosen bin.
-template <typename ET, int NT, int U, typename P>
-__device__ __forceinline__ void nucleus_collect(const ET* rp, int a, int e, double lm, double it, int bstar,
-                                                P&& push) {
+template <typename ET, int NT, int U, typename B, typename P>
+__device__ __forceinline__ void nucleus_collect(const ET* rp, int a, int e, B&& in_bin, P&& push) {
   row_stream<ET, NT, U>(
       rp, a, e,
       [&](const float (&fv)[Elem<ET>::kPerVec], int y0) {
@@ -566,7 +780,7 @@ __device__ __forceinline__ void nucleus_collect(const ET* rp, int a, int e, doub
         bool any = false;
 #pragma unroll
         for (int k = 0; k < EPV; ++k) {
-          m[k] = nucleus_bin(lm, fv[k], it) == bstar;
+          m[k] = in_bin(fv[k]);
           any |= m[k];
         }
         if (any) {
@@ -576,17 +790,20 @@ __device__ __forceinline__ void nucleus_collect(const ET* rp, int a, int e, doub
         }
       },
       [&](float l, int y) {
-        if (nucleus_bin(lm, l, it) == bstar) push(l, y);
+        if (in_bin(l)) push(l, y);
       });
 }
 
-// The whole nucleus of one row by one workgroup (every step above in one
-// pass each; refinement of an over-full bin included).
+// The whole nucleus of one row by one workgroup (every step above;
+// refinement of an over-full bin included).  known: the row's maximum is
+// read from the softmax partials (rows under a large top-k, whose softmax
+// pass ran, and rows the split passes send back), else pass 1 finds it.  A
+// row without top-k gets its softmax partials written here.
 template <typename ET>
 __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, const ET* __restrict__ ld, int rows_t,
-                                            int G, int V, int S, const float2* __restrict__ part,
+                                            int G, int V, int S, float2* __restrict__ part,
                                             const ReqInfo* __restrict__ info, RowCut* __restrict__ cut,
-                                            const Layout& L) {
+                                            const Layout& L, bool known) {
   constexpr int NT = NucShape::NT, U = NucShape::U, NW = NT / kWave;
   static_assert(kNucBins % NT == 0, "bins per thread");
   static_assert(kNucCap * sizeof(uint64_t) <= kNucBins * sizeof(double), "keys alias the histogram");
@@ -596,10 +813,12 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
   if (!rp) return;  // past the request's draft length
   // Under a large top-k the nucleus is taken over the top-k law: tokens below
   // the k-cut (written by kcut_full_kernel) have no mass here.
+  const bool own_part = ri.K == 0;  // the softmax pass skipped the row
   const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
   auto below = [&](float l, int y) { return kfloor != 0ull && make_key(l, (uint32_t)y) < kfloor; };
   double* hm = nucleus_hist_lds();
   uint64_t* keys = reinterpret_cast<uint64_t*>(hm);
+  NucRise* rl = nucleus_rise_lds();
   __shared__ double tab[64];
   __shared__ double red_d[NW], red_s[NW];
   // The scan's running sums and the refinement's digit counts live at
@@ -620,44 +839,66 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
   __shared__ uint64_t sh_prefix;
   __shared__ int sh_plen;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const double it = 1.0 / (double)ri.T;
 
-  const float lmax = nucleus_lmax(part, row, S);
-  const double lm = (double)lmax, it = 1.0 / (double)ri.T;
-
-  for (int i = tid; i <= kNucBins; i += NT) hm[i] = 0.0;
+  for (int i = tid; i < kNucBins; i += NT) hm[i] = 0.0;
   if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
-  // Every mass of this kernel: exp((l - lm) / T) by the table-driven exp.
-  auto mass = [&](float l) {
-    int k;
-    return exp_nonpos_f64(((double)l - lm) * it, tab, &k);
-  };
   if (tid == 0) {
+    rl->n = 0;
     sh_prefix = 0ull;  // fixed top bits of the cut key (refinement)
     sh_plen = 0;
     sh_n = 0;
   }
-
   __syncthreads();
 
-  // Pass 1: the mass histogram of the gap, and Z.
-  if (kfloor != 0ull) nucleus_pass1<ET, NT, U, true>(rp, 0, V, lm, it, kfloor, tab, hm);
-  else nucleus_pass1<ET, NT, U, false>(rp, 0, V, lm, it, kfloor, tab, hm);
-  __syncthreads();
-  const double Z = nucleus_unfactor<NT>(hm, hm[kNucBins], tab, red_d);
-  const double target = (double)ri.top_p * Z;
-
-  nucleus_pick<NT>(hm, target, scr.incl, red_s, &sh_bin, &sh_A);
-  const int bstar = sh_bin;
-  if (bstar < 0) {
-    // No finite mass (degenerate row): no cut.
-    if (tid == 0) cut[row] = RowCut{kfloor, lmax, (float)(1.0 / Z)};
+  // Pass 1: the window, the row's maximum and the spare masses.
+  NucP1 p;
+  if (known) {
+    const float lm = nucleus_lmax(part, row, S);
+    if (kfloor != 0ull) p = nucleus_pass1<ET, NT, U, false, true>(rp, 0, V, false, 0.0, lm, it, kfloor, tab, hm);
+    else p = nucleus_pass1<ET, NT, U, false, false>(rp, 0, V, false, 0.0, lm, it, 0ull, tab, hm);
+  } else {
+    p = nucleus_pass1<ET, NT, U, true, false>(rp, 0, V, true, 0.0, 0.f, it, 0ull, tab, hm);
+    if (!p.ok) {
+      // Binned again with the maximum known.
+      const float lm = p.lmax;
+      for (int i = tid; i < kNucBins; i += NT) hm[i] = 0.0;
+      if (tid == 0) rl->n = 0;
+      __syncthreads();
+      p = nucleus_pass1<ET, NT, U, false, false>(rp, 0, V, false, 0.0, lm, it, 0ull, tab, hm);
+    }
+  }
+  const float lmax = p.lmax;
+  if (lmax == -INFINITY) {
+    // No finite logit: no cut.
+    if (own_part) nucleus_write_part(part, row, S, lmax, 0.f);
+    if (tid == 0) cut[row] = RowCut{kfloor, lmax, INFINITY};
     return;
   }
+  const NucGrid g = p.g;
+  const int top = __double2loint(g.kmax + kNucRound);
+  const double sp = p.sp * exp2_64(fma((double)p.l0, g.C, g.B - kNucRound - g.kmax), tab);
+  const double Z = nucleus_unfactor<NT>(hm, top, sp + p.sb, tab, red_d);
+  // Grid unit -> exp((l - lmax) / T).
+  const double gf = exp2_frac64(-fma((double)lmax, g.C, g.B - kNucRound - g.kmax));
+  if (own_part) nucleus_write_part(part, row, S, lmax, (float)(Z * gf));
+  const double target = (double)ri.top_p * Z;
+
+  nucleus_pick<NT>(hm, top, target, scr.incl, red_s, &sh_bin, &sh_A);
+  const int jstar = sh_bin;
+  if (jstar < 0) {
+    // No mass (degenerate row): no cut.
+    if (tid == 0) cut[row] = RowCut{kfloor, lmax, (float)(1.0 / (Z * gf))};
+    return;
+  }
+  const double tstar = kNucRound + (g.kmax - (double)jstar);
+  auto in_bin = [&](float l) { return nuc_t(l, g) == tstar; };
+  auto mass = [&](float l) { return nuc_mass(g, l, tab); };
 
   // Pass 2: collect the keys of the bin (at most kNucCap are kept; the count
   // tells whether the bin needs refining).  filter_key: bin and key prefix.
   auto collect = [&](int plen, uint64_t prefix) {
-    nucleus_collect<ET, NT, U>(rp, 0, V, lm, it, bstar, [&](float l, int y) {
+    nucleus_collect<ET, NT, U>(rp, 0, V, in_bin, [&](float l, int y) {
       if (below(l, y)) return;
       const uint64_t k = make_key(l, (uint32_t)y);
       if (plen > 0 && (plen == 64 ? k != prefix : (k >> (64 - plen)) != (prefix >> (64 - plen)))) return;
@@ -673,7 +914,7 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
     if (tid == 0) sh_cnt = (uint32_t)sh_n;
     uint64_t kmin = ~0ull, kmax = 0ull;
     row_foreach<ET, NT, U>(rp, V, [&](float l, int y) {
-      if (nucleus_bin(lm, l, it) == bstar && !below(l, y)) {
+      if (in_bin(l) && !below(l, y)) {
         const uint64_t k = make_key(l, (uint32_t)y);
         kmin = k < kmin ? k : kmin;
         kmax = k > kmax ? k : kmax;
@@ -708,7 +949,7 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
       }
       __syncthreads();
       row_foreach<ET, NT, U>(rp, V, [&](float l, int y) {
-        if (nucleus_bin(lm, l, it) != bstar || below(l, y)) return;
+        if (!in_bin(l) || below(l, y)) return;
         const uint64_t k = make_key(l, (uint32_t)y);
         if (plen > 0 && (k >> (64 - plen)) != (prefix >> (64 - plen))) return;
         const int dig = (int)((k >> shift) & ((1ull << nb) - 1ull));
@@ -757,8 +998,8 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
     double zk;
     const int t = n > 0 ? wave_walk(keys, n, sh_A, target, mass, &zk) : -1;
     if (lane == 0) {
-      if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / zk)};
-      else cut[row] = RowCut{kfloor, lmax, (float)(1.0 / Z)};
+      if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / (zk * gf))};
+      else cut[row] = RowCut{kfloor, lmax, (float)(1.0 / (Z * gf))};
     }
   }
 }
@@ -772,23 +1013,32 @@ __device__ __forceinline__ void nucleus_row(int row, const ET* __restrict__ lt, 
 // the chip idle (a row then streams at the rate of one workgroup's loads in
 // flight), so each row is cut into NS contiguous chunks (plan_nucleus) and
 // the steps of nucleus_row run as separate passes:
-//   part     per chunk: pass 1 (Z and the gap histogram of its tokens) into
-//            the workspace;
-//   scan     per row: the chunks' histograms and Z summed in chunk order;
-//            the bin where the running mass reaches top_p Z, and the mass A
-//            of the bins before it;
+//   part     per chunk: pass 1 (its window on the row's common grid, anchor
+//            0, or the row's maximum under a large top-k) into the
+//            workspace;
+//   scan     per row: the chunks' windows merged at the row's largest
+//            logit (bins below the merged window join the spare mass); the
+//            bin where the running mass reaches top_p Z, and the mass A of
+//            the bins before it; the row's softmax partials;
 //   collect  per chunk: the keys of that bin, appended to the row's buffer;
 //   finish   per row: sort and walk the keys from A.  A bin of more than
-//            kNucCap keys is resolved by nucleus_row (with its refinement).
+//            kNucCap keys, or a row a chunk could not bin (see the window
+//            above), is resolved by nucleus_row with the maximum known.
 // The passes of the path not taken exit at once.
 // ===========================================================================
-constexpr int kNucPartStride = kNucBins + 2;  // histogram, spare slot (one slot of padding)
+// A chunk's record: its window's slots, then kmax, l0, the spare sums (units
+// of exp((l - l0) / T), and of the grid), lmax and ok.
+constexpr int kNucPartStride = kNucBins + 8;
+enum : int32_t { kNucNoCut = 0, kNucCutBin = 1, kNucRedo = 2 };
 
 struct NucState {
-  double A, Z;      // mass of the bins before the cut bin; the row's mass
-  uint64_t kfloor;  // the row's large top-k cut key (0: none)
-  int32_t bin;      // cut bin (-1: no cut, the row's RowCut is written)
-  uint32_t n;       // keys of the cut bin found by the collect pass
+  double A, Z;        // mass of the bins before the cut bin; the row's mass (grid unit)
+  double B, kmax;     // the grid's offset and the bin of the row's maximum
+  double tstar;       // kNucRound + the cut bin
+  double gf;          // grid unit -> exp((l - lmax) / T)
+  uint64_t kfloor;    // the row's large top-k cut key (0: none)
+  int32_t status;     // kNucNoCut (the row's RowCut is written), kNucCutBin, kNucRedo
+  uint32_t n;         // keys of the cut bin found by the collect pass
 };
 
 __device__ __forceinline__ int nucleus_splits(const int* plan) { return plan[1]; }
@@ -807,18 +1057,20 @@ __device__ __forceinline__ void nucleus_chunk(int V, int NS, int s, int* a, int*
 template <typename ET>
 __global__ __launch_bounds__(NucShape::NT) void nucleus_part_kernel(const ET* __restrict__ lt, const ET* __restrict__ ld,
                                                            int rows_t, int G, int V, int S,
-                                                           const float2* __restrict__ part,
+                                                           float2* __restrict__ part,
                                                            const ReqInfo* __restrict__ info,
                                                            RowCut* __restrict__ cut, Layout L,
                                                            const int* __restrict__ plan,
                                                            const int* __restrict__ list,
                                                            double* __restrict__ hpart) {
-  constexpr int NT = NucShape::NT, U = NucShape::U;
+  constexpr int NT = NucShape::NT, U = NucShape::U, NW = NT / kWave;
   const int NS = nucleus_splits(plan);
   const int item = blockIdx.x;
   if (item >= plan[0] * NS) return;
   if (NS == 1) {
-    nucleus_row<ET>(list[item], lt, ld, rows_t, G, V, S, part, info, cut, L);
+    const int row = list[item];
+    nucleus_row<ET>(row, lt, ld, rows_t, G, V, S, part, info, cut, L,
+                    info[row_request(row, rows_t, G)].K > 0);
     return;
   }
   const int r = item / NS, s = item - r * NS;
@@ -827,26 +1079,44 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_part_kernel(const ET* __
   const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
   const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
   double* hm = nucleus_hist_lds();
+  NucRise* rl = nucleus_rise_lds();
   __shared__ double tab[64];
+  __shared__ double red_d[NW];
   const int tid = threadIdx.x;
-  const double lm = (double)nucleus_lmax(part, row, S), it = 1.0 / (double)ri.T;
-  for (int i = tid; i <= kNucBins; i += NT) hm[i] = 0.0;
+  const double it = 1.0 / (double)ri.T;
+  for (int i = tid; i < kNucBins; i += NT) hm[i] = 0.0;
   if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  if (tid == 0) rl->n = 0;
   __syncthreads();
   int a, e;
   nucleus_chunk(V, NS, s, &a, &e);
-  if (kfloor != 0ull) nucleus_pass1<ET, NT, U, true>(rp, a, e, lm, it, kfloor, tab, hm);
-  else nucleus_pass1<ET, NT, U, false>(rp, a, e, lm, it, kfloor, tab, hm);
-  __syncthreads();
-  // The chunk's bins as accumulated (factors applied after the chunks are
-  // summed) and its spare slot.
+  NucP1 p;
+  if (ri.K > 0) {
+    // Under a large top-k: the maximum is known; the grid's anchor is it.
+    const float lm = nucleus_lmax(part, row, S);
+    p = nucleus_pass1<ET, NT, U, false, true>(rp, a, e, false, 0.0, lm, it, kfloor, tab, hm);
+  } else {
+    p = nucleus_pass1<ET, NT, U, true, false>(rp, a, e, false, 0.0, 0.f, it, 0ull, tab, hm);
+  }
+  const double sp = block_sum_d<NT>(p.sp, red_d);
+  const double sb = block_sum_d<NT>(p.sb, red_d);
+  // The chunk's slots as accumulated (each bin's power of two is applied
+  // after the merge), then its record.
   double* out = hpart + (size_t)item * kNucPartStride;
-  for (int i = tid; i <= kNucBins; i += NT) out[i] = hm[i];
+  for (int i = tid; i < kNucBins; i += NT) out[i] = hm[i];
+  if (tid == 0) {
+    out[kNucBins + 0] = p.g.kmax;
+    out[kNucBins + 1] = (double)p.l0;
+    out[kNucBins + 2] = sp;
+    out[kNucBins + 3] = sb;
+    out[kNucBins + 4] = (double)p.lmax;
+    out[kNucBins + 5] = p.ok ? 1.0 : 0.0;
+  }
 }
 
 // scan: one workgroup per listed row.
 __global__ __launch_bounds__(NucShape::NT) void nucleus_scan_kernel(int rows_t, int G, int S,
-                                                                   const float2* __restrict__ part,
+                                                                   float2* __restrict__ part,
                                                                    const ReqInfo* __restrict__ info,
                                                                    RowCut* __restrict__ cut,
                                                                    const int* __restrict__ plan,
@@ -860,31 +1130,93 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_scan_kernel(int rows_t, 
   const int row = list[r];
   const ReqInfo ri = info[row_request(row, rows_t, G)];
   const uint64_t kfloor = ri.K > 0 ? cut[row].kappa : 0ull;
+  const bool own_part = ri.K == 0;
   __shared__ double hm[kNucBins];
   __shared__ double incl[NT], red_s[NW], tab[64];
+  __shared__ double ck_kmax[kNucMaxSplit], ck_d[kNucMaxSplit];
+  __shared__ float ck_lmax[kNucMaxSplit];
   __shared__ double sh_A;
   __shared__ int sh_bin;
   const int tid = threadIdx.x;
   const double* src = hpart + (size_t)r * NS * kNucPartStride;
-  // The chunks' bins summed in chunk order (every chunk's bin b carries the
-  // same factor), then the factors.
+  const double it = 1.0 / (double)ri.T, C = it * kNucInvStep;
+  // The grid's anchor: 0, or the row's maximum under a large top-k.
+  const NucGrid g0{ri.K > 0 ? nuc_grid_B((double)nucleus_lmax(part, row, S), C) : kNucRound, C, 0.0};
+  const double B = g0.B;
+  float lmax = -INFINITY;
+  bool ok = true;
+  for (int c = 0; c < NS; ++c) {
+    const double* rec = src + (size_t)c * kNucPartStride + kNucBins;
+    const float lc = (float)rec[4];
+    lmax = fmaxf(lmax, lc);
+    ok = ok && (lc == -INFINITY || rec[5] != 0.0);
+  }
+  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  if (lmax == -INFINITY || !ok) {
+    // No finite logit (no cut), or a chunk that could not bin its tokens
+    // (the finish pass bins the row with this maximum).
+    if (own_part) nucleus_write_part(part, row, S, lmax, 0.f);
+    if (tid == 0) {
+      if (lmax == -INFINITY) cut[row] = RowCut{kfloor, lmax, INFINITY};
+      NucState st{};
+      st.kfloor = kfloor;
+      st.status = lmax == -INFINITY ? kNucNoCut : kNucRedo;
+      state[r] = st;
+    }
+    return;
+  }
+  const double kmax = nuc_t(lmax, g0) - kNucRound;
+  const int top = __double2loint(kmax + kNucRound);
+  if (tid < NS) {
+    const double* rec = src + (size_t)tid * kNucPartStride + kNucBins;
+    ck_kmax[tid] = rec[0];
+    ck_lmax[tid] = (float)rec[4];
+    ck_d[tid] = kmax - rec[0];  // >= 0: how far the chunk's window lies below the row's
+  }
+  __syncthreads();
+  // Slot i of every window holds a bin congruent to i: chunk c's bin at
+  // chunk gap jc = (top_c - i) mod kNucBins lies at the row's gap jc + d_c,
+  // in the row's window if that is below kNucBins, else below it (spare).
+  double sb = 0.0;
   for (int i = tid; i < kNucBins; i += NT) {
     double v = 0.0;
-    for (int c = 0; c < NS; ++c) v += src[(size_t)c * kNucPartStride + i];
+    for (int c = 0; c < NS; ++c) {
+      if (ck_lmax[c] == -INFINITY) continue;
+      const double x = src[(size_t)c * kNucPartStride + i];
+      if (x == 0.0) continue;
+      const int topc = __double2loint(ck_kmax[c] + kNucRound);
+      const double jr = (double)((topc - i) & (kNucBins - 1)) + ck_d[c];
+      if (jr < (double)kNucBins) v += x;
+      else sb += x * exp2_64ths(-jr, tab);
+    }
     hm[i] = v;
   }
-  double spare = 0.0;
-  for (int c = 0; c < NS; ++c) spare += src[(size_t)c * kNucPartStride + kNucBins];
-  if (tid < 64) tab[tid] = exp2((double)tid / 64.0);
+  if (tid < NS && ck_lmax[tid] != -INFINITY) {
+    // The chunk's spare sums in the row's grid unit.
+    const double* rec = src + (size_t)tid * kNucPartStride + kNucBins;
+    sb += rec[3] * exp2_64ths(-ck_d[tid], tab);
+    sb += rec[2] * exp2_64(fma(rec[1], C, B - kNucRound - kmax), tab);
+  }
   __syncthreads();
-  const double Z = nucleus_unfactor<NT>(hm, spare, tab, red_s);
+  const double Z = nucleus_unfactor<NT>(hm, top, sb, tab, red_s);
+  const double gf = exp2_frac64(-fma((double)lmax, C, B - kNucRound - kmax));
+  if (own_part) nucleus_write_part(part, row, S, lmax, (float)(Z * gf));
   const double target = (double)ri.top_p * Z;
-  nucleus_pick<NT>(hm, target, incl, red_s, &sh_bin, &sh_A);
-  const float lmax = nucleus_lmax(part, row, S);  // by every wave (a wave reduction)
+  nucleus_pick<NT>(hm, top, target, incl, red_s, &sh_bin, &sh_A);
   if (tid == 0) {
-    const int bstar = sh_bin;
-    if (bstar < 0) cut[row] = RowCut{kfloor, lmax, (float)(1.0 / Z)};  // no finite mass: no cut
-    state[r] = NucState{sh_A, Z, kfloor, bstar, 0u};
+    const int jstar = sh_bin;
+    if (jstar < 0) cut[row] = RowCut{kfloor, lmax, (float)(1.0 / (Z * gf))};  // no mass: no cut
+    NucState st;
+    st.A = sh_A;
+    st.Z = Z;
+    st.B = B;
+    st.kmax = kmax;
+    st.tstar = kNucRound + (kmax - (double)jstar);
+    st.gf = gf;
+    st.kfloor = kfloor;
+    st.status = jstar < 0 ? kNucNoCut : kNucCutBin;
+    st.n = 0u;
+    state[r] = st;
   }
 }
 
@@ -893,8 +1225,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_scan_kernel(int rows_t, 
 template <typename ET>
 __global__ __launch_bounds__(NucShape::NT) void nucleus_collect_kernel(const ET* __restrict__ lt,
                                                               const ET* __restrict__ ld, int rows_t, int G,
-                                                              int V, int S, const float2* __restrict__ part,
-                                                              const ReqInfo* __restrict__ info, Layout L,
+                                                              int V, const ReqInfo* __restrict__ info, Layout L,
                                                               const int* __restrict__ plan,
                                                               const int* __restrict__ list,
                                                               NucState* __restrict__ state,
@@ -904,30 +1235,32 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_collect_kernel(const ET*
   const int item = blockIdx.x;
   if (NS < 2 || item >= plan[0] * NS) return;
   const int r = item / NS, s = item - r * NS;
-  const int bstar = state[r].bin;
-  if (bstar < 0) return;
+  if (state[r].status != kNucCutBin) return;
+  const double tstar = state[r].tstar, gB = state[r].B;
   const uint64_t kfloor = state[r].kfloor;
   const int row = list[r];
   const ReqInfo ri = info[row_request(row, rows_t, G)];
   const ET* rp = row_ptr(L, lt, ld, rows_t, G, row);
-  const double lm = (double)nucleus_lmax(part, row, S), it = 1.0 / (double)ri.T;
+  const double C = (1.0 / (double)ri.T) * kNucInvStep;
   int a, e;
   nucleus_chunk(V, NS, s, &a, &e);
   uint32_t* cnt = &state[r].n;
   uint64_t* dst = gkeys + (size_t)r * kNucCap;
-  nucleus_collect<ET, NT, U>(rp, a, e, lm, it, bstar, [&](float l, int y) {
-    const uint64_t k = make_key(l, (uint32_t)y);
-    if (kfloor != 0ull && k < kfloor) return;
-    const uint32_t pos = atomicAdd(cnt, 1u);
-    if (pos < (uint32_t)kNucCap) dst[pos] = k;
-  });
+  nucleus_collect<ET, NT, U>(
+      rp, a, e, [&](float l) { return fma((double)l, C, gB) == tstar; },
+      [&](float l, int y) {
+        const uint64_t k = make_key(l, (uint32_t)y);
+        if (kfloor != 0ull && k < kfloor) return;
+        const uint32_t pos = atomicAdd(cnt, 1u);
+        if (pos < (uint32_t)kNucCap) dst[pos] = k;
+      });
 }
 
 // finish: one workgroup per listed row.
 template <typename ET>
 __global__ __launch_bounds__(NucShape::NT) void nucleus_finish_kernel(const ET* __restrict__ lt,
                                                              const ET* __restrict__ ld, int rows_t, int G, int V,
-                                                             int S, const float2* __restrict__ part,
+                                                             int S, float2* __restrict__ part,
                                                              const ReqInfo* __restrict__ info,
                                                              RowCut* __restrict__ cut, Layout L,
                                                              const int* __restrict__ plan,
@@ -939,12 +1272,12 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_finish_kernel(const ET* 
   const int r = blockIdx.x;
   if (NS < 2 || r >= plan[0]) return;
   const NucState st = state[r];
-  if (st.bin < 0) return;  // the scan wrote the row's cut
+  if (st.status == kNucNoCut) return;  // the scan wrote the row's cut
   const int row = list[r];
-  if (st.n > (uint32_t)kNucCap) {
-    // Over-full bin (many equal or near-equal logits): the one-workgroup
-    // pass, which refines it.
-    nucleus_row<ET>(row, lt, ld, rows_t, G, V, S, part, info, cut, L);
+  if (st.status == kNucRedo || st.n > (uint32_t)kNucCap) {
+    // A row a chunk could not bin, or an over-full bin (many equal or
+    // near-equal logits): the one-workgroup pass with the maximum known.
+    nucleus_row<ET>(row, lt, ld, rows_t, G, V, S, part, info, cut, L, true);
     return;
   }
   const ReqInfo ri = info[row_request(row, rows_t, G)];
@@ -952,7 +1285,7 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_finish_kernel(const ET* 
   __shared__ double tab[64];
   const int tid = threadIdx.x;
   const float lmax = nucleus_lmax(part, row, S);
-  const double lm = (double)lmax, it = 1.0 / (double)ri.T;
+  const NucGrid g{st.B, (1.0 / (double)ri.T) * kNucInvStep, st.kmax};
   const int n = (int)st.n;
   int n2 = 2;
   while (n2 < n) n2 <<= 1;
@@ -962,16 +1295,13 @@ __global__ __launch_bounds__(NucShape::NT) void nucleus_finish_kernel(const ET* 
   __syncthreads();
   block_sort_desc<NT>(keys, n2);
   if (tid < kWave) {
-    auto mass = [&](float l) {
-      int k;
-      return exp_nonpos_f64(((double)l - lm) * it, tab, &k);
-    };
     const double target = (double)ri.top_p * st.Z;
     double zk;
-    const int t = n > 0 ? wave_walk(keys, n, st.A, target, mass, &zk) : -1;
+    const int t =
+        n > 0 ? wave_walk(keys, n, st.A, target, [&](float l) { return nuc_mass(g, l, tab); }, &zk) : -1;
     if (tid == 0) {
-      if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / zk)};
-      else cut[row] = RowCut{st.kfloor, lmax, (float)(1.0 / st.Z)};
+      if (t >= 0) cut[row] = RowCut{keys[t], lmax, (float)(1.0 / (zk * st.gf))};
+      else cut[row] = RowCut{st.kfloor, lmax, (float)(1.0 / (st.Z * st.gf))};
     }
   }
 }

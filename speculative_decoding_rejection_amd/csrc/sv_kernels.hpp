@@ -197,9 +197,11 @@ __global__ __launch_bounds__(NT) void rows_softmax_kernel(const ET* __restrict__
   const int blk = blockIdx.x;
   const int row = blk / S, s = blk - row * S;
   if (info) {
-    // Batch call: only rows of requests without top-k; per-request T.
+    // Batch call: only rows of requests without top-k; per-request T.  Rows
+    // with top-p and no top-k are left to the nucleus pass, which finds
+    // their maximum and mass in the read that bins them.
     const ReqInfo ri = info[row_request(row, rows_t, G)];
-    if (ri.kind != kReqFull) return;
+    if (ri.kind != kReqFull || (ri.top_p < 1.f && ri.K == 0)) return;
     c = ri.c;
   } else if (blk == 0 && threadIdx.x == 0) {
     *err = 0;

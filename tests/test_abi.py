@@ -204,7 +204,7 @@ def test_batch_match_layout_errors(sv):
 def test_batch_workspace_holds_the_split_nucleus(sv, B, G):
     """With top-p settings the workspace also holds the split nucleus passes'
     buffers: the row list, chunk histograms for min(1024, 16 x rows) chunks
-    (4098 doubles each, rows capped at 512), and a 2048-key buffer per split
+    (4104 doubles each: a window of 4096 bins and its record; rows capped at 512), and a 2048-key buffer per split
     row; calls without top-p carry none of it."""
     fake = 1 << 21
     p = sv.make_params(B, G, 5003, sv.SV_F32, 1.0, 0, 1)
@@ -213,7 +213,7 @@ def test_batch_workspace_holds_the_split_nucleus(sv, B, G):
     rows = B * (2 * G + 1)
     split_rows = min(rows, 512)
     items = min(1024, 16 * split_rows)
-    need = rows * 16 + rows * 4 + items * 4098 * 8 + split_rows * 2048 * 8
+    need = rows * 16 + rows * 4 + items * 4104 * 8 + split_rows * 2048 * 8
     assert nuc - topk >= need
     assert nuc - topk <= need + split_rows * 64 + 16 * 4096  # state records and alignment
 

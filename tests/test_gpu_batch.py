@@ -168,6 +168,38 @@ def test_top_p_hard_rows(sv, rows, dtype):
     check_batch(sv, inp, max_top_k=0)
 
 
+# Rows that move the nucleus pass's bin window: ascending logits (every
+# token rises past the first look, so the row is binned again with its
+# maximum known), a masked prefix (the first looks find no finite logit;
+# whole chunks hold none), one token well above the rest near the row's end
+# (the window moves up by more than its headroom; at T 0.05 by more than its
+# width), and logits near 1e13 with tied maxima (bins past fp64's exact
+# integers on the split passes' common grid).
+WINDOW_ROWS = {
+    "ascending": (1.0, lambda rng, V: np.sort(rng.standard_normal(V) * 3.0)),
+    "masked_prefix": (1.0, lambda rng, V: np.where(np.arange(V) < (3 * V) // 5, -np.inf,
+                                                   rng.standard_normal(V) * 3.0)),
+    "late_spike": (1.0, lambda rng, V: np.where(np.arange(V) == V - 7, 11.0, rng.standard_normal(V))),
+    "far_spike": (0.05, lambda rng, V: np.where(np.arange(V) == V - 7, 40.0, rng.standard_normal(V))),
+    "huge_ties": (1.0, lambda rng, V: np.where(rng.random(V) < 0.01, 1e13,
+                                               1e13 - 2.0 ** 37 * rng.integers(1, 50, V))),
+}
+
+
+@pytest.mark.parametrize("rows", list(WINDOW_ROWS))
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,V", [(4, 100003), (112, 20011)])
+def test_top_p_window_rows(sv, rows, dtype, B, V):
+    """Rows that move the window of the nucleus pass, on the split passes
+    (20 rows, 16 chunks of 6272 tokens each) and one workgroup per row (560
+    rows).  No top_p is a binary fraction: over ~200 tied maxima a stop at
+    exactly top_p n of them is decided by the oracle's rounding alone, and
+    p(x) = 1/n then differs by far more than the p bar."""
+    T, fn = WINDOW_ROWS[rows]
+    inp = _rows_case(fn, B, 2, V, dtype, T, [0.3, 0.55, 0.9, 0.97])
+    check_batch(sv, inp, max_top_k=0)
+
+
 @pytest.mark.parametrize("top_p", [1e-30, 0.5, float(np.nextafter(np.float32(1), np.float32(0))), 1.0])
 def test_top_p_extremes(sv, top_p):
     inp = mixed(16, 4, 5003, "f32", mix=((0.9, 0, top_p), (0.8, 20, top_p)), seed=3)
