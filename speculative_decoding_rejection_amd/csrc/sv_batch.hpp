@@ -39,44 +39,11 @@ __device__ __forceinline__ double nucleus_mass(double lm, float l, double it) {
   return exp(((double)l - lm) * it);
 }
 
-// exp(x) for x <= 0 in fp64, table-driven (P. T. P. Tang, "Table-driven
-// implementation of the exponential function in IEEE floating-point
-// arithmetic", ACM TOMS 15(2), 1989): x = (64 m + j) ln2 / 64 + r with
-// |r| <= ln2 / 128, so exp(x) = 2^m * 2^(j/64) * exp(r).  k = 64 m + j is
-// x * 64 / ln2 rounded to the nearest integer by adding 1.5 * 2^52 (the
-// integer lands in the low mantissa bits); ln2 / 64 is split into a 32-bit
-// head (k times it is exact for |k| < 2^21) and a tail; exp(r) - 1 is its
-// Taylor polynomial of degree 6 (truncation below 1e-19); the factor 2^m is
-// an add to the exponent field (the result stays normal for x > -700, and
-// below that the mass, under 1e-304 of the row maximum's, is taken as 0).
-// tab[j] = 2^(j/64).  *k_out = k: -k is the token's gap bin (ln2 / 64 nats
-// per bin), a non-decreasing function of the gap -x.
-constexpr double kNucInvStep = 0x1.71547652b82fep+6;  // 64 / ln2
+// 64 / ln2 (bins of ln2 / 64 nats per unit exponent), and 1.5 * 2^52: an
+// fp64 value near it is rounded to an integer by its own precision (the
+// integer sits in the low mantissa bits).
+constexpr double kNucInvStep = 0x1.71547652b82fep+6;
 constexpr double kNucRound = 0x1.8p52;
-__device__ __forceinline__ int nucleus_k(double x) {
-  return __double2loint(fma(x, kNucInvStep, kNucRound));
-}
-__device__ __forceinline__ double exp_nonpos_f64(double x, const double* tab, int* k_out) {
-  // Branch-free, so that the masses of a vector's tokens are computed side by
-  // side: x <= -700 (and -inf) is evaluated at -700 and the result replaced.
-  const bool ok = x > -700.0;
-  const double xc = fmax(x, -700.0);
-  const double t = fma(xc, kNucInvStep, kNucRound);
-  const double kd = t - kNucRound;
-  const int k = __double2loint(t);
-  double r = fma(-kd, 0x1.62e42fee00000p-7, xc);  // head of ln2 / 64
-  r = fma(-kd, 0x1.a39ef35793c76p-39, r);          // tail
-  double q = fma(r, 1.0 / 720.0, 1.0 / 120.0);
-  q = fma(r, q, 1.0 / 24.0);
-  q = fma(r, q, 1.0 / 6.0);
-  q = fma(r, q, 0.5);
-  q = fma(r, q, 1.0);
-  const double tj = tab[k & 63];
-  const double v = fma(tj, q * r, tj);  // 2^(j/64) exp(r), in [0.99, 1.01]
-  const double e = __hiloint2double(__double2hiint(v) + (k >> 6) * (1 << 20), __double2loint(v));
-  *k_out = k;  // of max(x, -700): -k is past every gap bin when x <= -700
-  return ok ? e : 0.0;
-}
 
 // Paths of the nucleus passes over full rows (below): with at most
 // kNucSplitRows rows with top-p in a call, each row is cut into NS =
