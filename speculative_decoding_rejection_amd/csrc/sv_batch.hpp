@@ -284,11 +284,11 @@ __global__ __launch_bounds__(256) void nucleus_topk_kernel(uint64_t* __restrict_
 //           until at most kNucCap tokens remain.
 //
 // The grid.  With 1/T = it and C = 64 it / ln2, token l falls in bin
-// k(l) = round(y), y = (l - a) C (the exact product, rounded once by fma),
-// for an anchor a fixed before pass 1 reads the row: 0 for a row split over
-// chunks (every chunk bins alike), the largest logit of a first look for a
-// row read by one workgroup.  k is non-decreasing in l, so the bins cut the
-// row in key order.  With kmax the bin of the row's largest logit, every mass
+// k(l) = round(y), y = l C - rint(a C) (the exact product plus an integer,
+// rounded once by one fma), for an anchor a fixed before pass 1 reads the
+// row: 0 for a row split over chunks (every chunk bins alike), the largest
+// logit of a first look for a row read by one workgroup.  k is
+// non-decreasing in l, so the bins cut the row in key order.  With kmax the bin of the row's largest logit, every mass
 // of the nucleus passes is taken in the unit 2^((y - kmax) / 64) =
 // 2^((k - kmax) / 64) 2^(f / 64), f = y - k in [-1/2, 1/2]: a bin sums its
 // tokens' 2^(f / 64) and its power of two is applied once, and the walk and
