@@ -290,10 +290,11 @@ size_t sv_workspace_bytes_batch(const sv_params* params, const sv_sampling* samp
  * device that wait for it (created on the first batch call on that device
  * that is not being captured into a graph, non-blocking, default priority,
  * kept until the process ends; until then the row passes run on `stream`
- * one after another), and `stream`
- * waits for both before the accept passes: stream order is unchanged, and a
- * capture of `stream` takes the two streams in.  Calls from several host
- * threads are serialised while they enqueue this fork and join. */
+ * one after another), and `stream` waits for both at the end of the call
+ * (sampler-match calls, and calls while kernel timing is enabled, before
+ * their accept passes): stream order is unchanged, and a capture of
+ * `stream` takes the two streams in.  Calls from several host threads are
+ * serialised while they enqueue this fork and join. */
 sv_status spec_verify_batch(const sv_params* params, const sv_sampling* sampling, const sv_layout* layout,
                             const void* target_logits, const void* draft, const int32_t* draft_tokens,
                             const sv_outputs* outputs, void* workspace, size_t workspace_bytes, void* stream);
