@@ -200,6 +200,28 @@ def test_top_p_window_rows(sv, rows, dtype, B, V):
     check_batch(sv, inp, max_top_k=0)
 
 
+def _rising_rows(n_high, first):
+    """N(0, 0.01) logits with n_high tokens near 10 placed past index
+    `first`: every one of them rises more than the window's headroom (5.5
+    nats at T 1) above the largest logit a first look can see."""
+    def fn(rng, V):
+        r = rng.standard_normal(V) * 0.1
+        r[first + rng.choice(V - first, n_high, replace=False)] = 10.0 + 0.01 * np.arange(n_high)
+        return r
+    return fn
+
+
+@pytest.mark.parametrize("n_high", [256, 257])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_top_p_rise_list_capacity(sv, n_high, dtype):
+    """As many tokens rising above the nucleus pass's window as its list
+    holds (256), and one more (the row is then binned again with its
+    maximum known), one workgroup per row (560 rows of 20011; the first
+    look covers the first 4096 fp32 or 8192 bf16 elements)."""
+    inp = _rows_case(_rising_rows(n_high, 8192), 112, 2, 20011, dtype, 1.0, [0.3, 0.55, 0.9, 0.97])
+    check_batch(sv, inp, max_top_k=0)
+
+
 @pytest.mark.parametrize("top_p", [1e-30, 0.5, float(np.nextafter(np.float32(1), np.float32(0))), 1.0])
 def test_top_p_extremes(sv, top_p):
     inp = mixed(16, 4, 5003, "f32", mix=((0.9, 0, top_p), (0.8, 20, top_p)), seed=3)
