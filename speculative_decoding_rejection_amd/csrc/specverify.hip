@@ -40,6 +40,11 @@ constexpr size_t kSmallCallBytes = (size_t)64 << 20;
 #endif
 constexpr int kSmallMinSeg = SV_SMALL_MIN_SEG;
 constexpr size_t kFusedLdsBytes = 32768;
+// Measured on MI355X (race splits per request, us per call): fp32 full rows
+// (B 256, V 151936) 4 / 6 / 8 / 16 splits: 414 / 412.5 / 418 / 421.5; one-hot
+// bf16 (B 512, V 262144) 2 / 3 / 4 / 8: 317 / 316 / 312 / 312.5; bf16 full
+// rows (B 512, V 128256) 2 / 3 / 4 / 8: 276 / 252 / 241.5 / 244.
+constexpr int kFusedRaceMinSeg = 24576;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -128,13 +133,16 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   q.S = entry == kEntryGreedy ? S_t : S_all;
   q.seg = entry == kEntryGreedy ? seg_t : seg_all;
   const bool small = nrows * (size_t)q.V * (size_t)q.esize <= kSmallCallBytes;
-  q.Sr = splits_for(q.B, q.V, 4096, small ? kSmallMinSeg : 2048);
-  q.segr = seg_for(q.V, q.Sr);
-  q.Sr = (q.V + q.segr - 1) / q.segr;
   // Accept and race in one launch when the request's row partials fit the
   // fused kernel's LDS staging.
   q.fused = entry != kEntryGreedy && q.K == 0 && q.G < 64 &&
             (size_t)(2 * q.G + 1) * (size_t)q.S * 8 <= kFusedLdsBytes;
+  // Race splits.  Every workgroup of the fused kernel takes its request's
+  // accept decisions before it races, so large fused calls race longer
+  // splits (at least kFusedRaceMinSeg tokens).
+  q.Sr = splits_for(q.B, q.V, 4096, small ? kSmallMinSeg : (q.fused ? kFusedRaceMinSeg : 2048));
+  q.segr = seg_for(q.V, q.Sr);
+  q.Sr = (q.V + q.segr - 1) / q.segr;
   size_t off = 0;
   q.off_err = off;
   off = align_up(off + sizeof(int), kWsAlign);
