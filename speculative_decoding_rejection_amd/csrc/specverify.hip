@@ -139,10 +139,16 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
             (size_t)(2 * q.G + 1) * (size_t)q.S * 8 <= kFusedLdsBytes;
   // Race splits.  Every workgroup of the fused kernel takes its request's
   // accept decisions before it races, so large fused calls race longer
-  // splits (at least kFusedRaceMinSeg tokens).
-  q.Sr = splits_for(q.B, q.V, 4096, small ? kSmallMinSeg : (q.fused ? kFusedRaceMinSeg : 2048));
-  q.segr = seg_for(q.V, q.Sr);
-  q.Sr = (q.V + q.segr - 1) / q.segr;
+  // splits (at least kFusedRaceMinSeg tokens).  The race state is sized for
+  // the splits of the unfused rule, never fewer, so that one workspace size
+  // still serves every entry.
+  auto race_splits = [&](int min_seg, int* seg) {
+    *seg = seg_for(q.V, splits_for(q.B, q.V, 4096, min_seg));
+    return (q.V + *seg - 1) / *seg;
+  };
+  int seg_ws = 0;
+  const int Sr_ws = race_splits(small ? kSmallMinSeg : 2048, &seg_ws);
+  q.Sr = race_splits(small ? kSmallMinSeg : (q.fused ? kFusedRaceMinSeg : 2048), &q.segr);
   size_t off = 0;
   q.off_err = off;
   off = align_up(off + sizeof(int), kWsAlign);
@@ -158,9 +164,9 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
   q.off_gath = off;
   off = align_up(off + nrows * sizeof(float), kWsAlign);
   q.off_tpart = off;
-  off = align_up(off + (size_t)q.B * (size_t)q.Sr * 32, kWsAlign);
+  off = align_up(off + (size_t)q.B * (size_t)Sr_ws * 32, kWsAlign);
   q.off_tkey = off;
-  off = align_up(off + (size_t)q.B * (size_t)q.Sr * 8, kWsAlign);
+  off = align_up(off + (size_t)q.B * (size_t)Sr_ws * 8, kWsAlign);
   q.off_info = q.off_cut = off;
   q.total = off;
   q.L = sv::Layout{nullptr, (int64_t)q.V, (int64_t)q.V};

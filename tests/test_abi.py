@@ -48,6 +48,19 @@ def test_workspace_sizing(sv):
     assert sv.sv_workspace_bytes(sv.make_params(4, 2, 100, sv.SV_F32, 0.0)) > 0  # greedy parameters
 
 
+@pytest.mark.parametrize("B,G,V,bf16", [(8, 4, 32000, False), (64, 5, 128256, True), (256, 7, 151936, False),
+                                        (512, 3, 262144, True), (1024, 8, 256000, True)])
+def test_one_workspace_size_for_every_entry(sv, B, G, V, bf16):
+    """spec_verify_greedy ignores temperature and top_k, so a workspace
+    sized from sampled parameters must also fit a greedy call of the same
+    shape: never smaller than the size for temperature 0 (the greedy plan)."""
+    dt = sv.SV_BF16 if bf16 else sv.SV_F32
+    greedy = sv.sv_workspace_bytes(sv.make_params(B, G, V, dt, 0.0, 0, 1))
+    assert greedy > 0
+    for T, k in ((1.0, 0), (0.7, 64), (1.0, 1000), (1.0, 2000)):
+        assert sv.sv_workspace_bytes(sv.make_params(B, G, V, dt, T, k, 1)) >= greedy, (T, k)
+
+
 def _call_prob(sv, params, ws_bytes=1 << 20, null=None):
     lib = sv.load_library()
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: validation fails first

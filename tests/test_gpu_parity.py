@@ -232,6 +232,23 @@ def test_topk1_matches_greedy_on_gpu(sv):
     np.testing.assert_array_equal(a["num_accepted"], g["num_accepted"])
 
 
+@pytest.mark.parametrize("name", ["greedy_bf16_b64_g5_v128256", "prob_f32_b256_g7_v151936"])
+def test_greedy_ignores_sampling_params(sv, name):
+    """spec_verify_greedy ignores temperature and top_k: called with a
+    sampled temperature (and a top-k) and the workspace the library sizes for
+    those parameters, it runs and returns what the temperature-0 call does."""
+    wl = W[name]
+    dev = torch.device("cuda:0")
+    print(f"[greedy params] {name}", flush=True)
+    inp = workloads.generate(wl, device=dev)
+    ref = gpu_run(sv, "greedy", inp, 0.0, 0, 3)
+    for T, k in ((1.0, 0), (0.7, 64)):
+        got = gpu_run(sv, "greedy", inp, T, k, 3)
+        for key in ("out_tokens", "num_accepted", "target_argmax"):
+            np.testing.assert_array_equal(got[key], ref[key], err_msg=f"{key} T={T} k={k}")
+        assert got["error_code"] == 0
+
+
 # ---------------------------------------------------------------------------
 # Edge cases
 # ---------------------------------------------------------------------------
