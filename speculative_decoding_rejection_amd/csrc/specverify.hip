@@ -45,6 +45,10 @@ constexpr size_t kFusedLdsBytes = 32768;
 // bf16 (B 512, V 262144) 2 / 3 / 4 / 8: 317 / 316 / 312 / 312.5; bf16 full
 // rows (B 512, V 128256) 2 / 3 / 4 / 8: 276 / 252 / 241.5 / 244.
 constexpr int kFusedRaceMinSeg = 24576;
+// Calls of at most kSmallCallBytes (8 requests, gamma 4, V 32000, fp32: race
+// splits of at least 256 / 512 / 1024 / 2048 / 4096 tokens, us per call:
+// 21.5 / 18.8 / 18.1 / 18.8 / 20.6).
+constexpr int kSmallFusedRaceMinSeg = 1024;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -139,16 +143,18 @@ sv_status make_plan(const sv_params* p, int entry, Plan* pl) {
             (size_t)(2 * q.G + 1) * (size_t)q.S * 8 <= kFusedLdsBytes;
   // Race splits.  Every workgroup of the fused kernel takes its request's
   // accept decisions before it races, so large fused calls race longer
-  // splits (at least kFusedRaceMinSeg tokens).  The race state is sized for
-  // the splits of the unfused rule, never fewer, so that one workspace size
-  // still serves every entry.
+  // splits (at least kFusedRaceMinSeg tokens); small fused calls, bound by
+  // latency, race shorter ones (kSmallFusedRaceMinSeg).  The race state is
+  // sized for the most splits any entry takes (the shortest minimum), so
+  // that one workspace size serves every entry.
   auto race_splits = [&](int min_seg, int* seg) {
     *seg = seg_for(q.V, splits_for(q.B, q.V, 4096, min_seg));
     return (q.V + *seg - 1) / *seg;
   };
   int seg_ws = 0;
-  const int Sr_ws = race_splits(small ? kSmallMinSeg : 2048, &seg_ws);
-  q.Sr = race_splits(small ? kSmallMinSeg : (q.fused ? kFusedRaceMinSeg : 2048), &q.segr);
+  const int Sr_ws = race_splits(small ? std::min(kSmallMinSeg, kSmallFusedRaceMinSeg) : 2048, &seg_ws);
+  q.Sr = race_splits(small ? (q.fused ? kSmallFusedRaceMinSeg : kSmallMinSeg) : (q.fused ? kFusedRaceMinSeg : 2048),
+                     &q.segr);
   size_t off = 0;
   q.off_err = off;
   off = align_up(off + sizeof(int), kWsAlign);
